@@ -1,0 +1,497 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: hand-derived
+fixtures (tests/golden), closed forms, invariants stated on the pages, brute
+force over tiny inputs, or an independent library routine. The tests are
+chosen so that a dropped term, a wrong sign or index, a transposed operand or
+a swapped normalisation order fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.signal
+import scipy.special
+import torch
+
+import oracle as O
+from stream_residual_mixing_amd import synth
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _frac_matrix(d):
+    return np.array([[float(Fraction(n, q)) for n, q in zip(rn, rq)]
+                     for rn, rq in zip(d["num"], d["den"])])
+
+
+def _cfg_like_res_logits(rng, T, n, spread=0.03):
+    """Logits shaped like the workloads': identity bias plus small noise."""
+    return np.eye(n)[None] + spread * rng.standard_normal((T, n, n))
+
+
+# ---------------------------------------------------------------- sigmoid
+
+def test_sigmoid_closed_forms_and_library():
+    z = np.linspace(-30, 30, 1001)
+    assert O.sigmoid(0.0) == 0.5
+    np.testing.assert_allclose(O.sigmoid(z), scipy.special.expit(z), rtol=1e-15, atol=1e-300)
+    np.testing.assert_allclose(O.sigmoid(-z), 1.0 - O.sigmoid(z), atol=1e-15)
+    s = O.sigmoid(z)
+    assert np.all(s > 0) and np.all(s < 1)
+
+
+# ---------------------------------------------------------------- Sinkhorn
+
+def test_sinkhorn_hand_derived_2x2(golden_dir):
+    g = _load(golden_dir, "sinkhorn_2x2.json")
+    L = np.log(np.array(g["M0"], dtype=np.float64))
+    np.testing.assert_allclose(O.sinkhorn_knopp(L, 1), _frac_matrix(g["after_1_iteration"]),
+                               rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.sinkhorn_knopp(L, 2), _frac_matrix(g["after_2_iterations"]),
+                               rtol=0, atol=1e-15)
+
+
+def test_sinkhorn_2x2_limit_closed_form():
+    # Diagonal scaling keeps the cross ratio ad/bc, so the doubly stochastic limit
+    # of a positive 2x2 matrix is [[p, 1-p], [1-p, p]] with p = sqrt(ad)/(sqrt(ad)+sqrt(bc)).
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        a, b, c, d = rng.uniform(0.2, 5.0, 4)
+        p = math.sqrt(a * d) / (math.sqrt(a * d) + math.sqrt(b * c))
+        H = O.sinkhorn_knopp(np.log([[a, b], [c, d]]), 400)
+        np.testing.assert_allclose(H, [[p, 1 - p], [1 - p, p]], atol=1e-12)
+
+
+def test_sinkhorn_uniqueness_of_scaling():
+    # A doubly stochastic A: convex combination of permutation matrices (Birkhoff).
+    rng = np.random.default_rng(2)
+    n = 5
+    perms = [np.eye(n)[list(p)] for p in itertools.permutations(range(n))]
+    w = rng.dirichlet(np.ones(8))
+    A = sum(wi * perms[j] for wi, j in zip(w, rng.choice(len(perms), 8, replace=False)))
+    A = 0.9 * A + 0.1 / n  # strictly positive, still doubly stochastic
+    u, v = rng.standard_normal(n), rng.standard_normal(n)
+    L = np.log(A) + u[:, None] + v[None, :]
+    np.testing.assert_allclose(O.sinkhorn_knopp(L, 500), A, atol=1e-12)
+    # A constant offset is a global factor e^0.7: the first T_c removes it, so one
+    # iteration returns A itself.
+    L2 = np.log(A) + 0.7
+    np.testing.assert_allclose(O.sinkhorn_knopp(L2, 1), A, atol=1e-14)
+
+
+def test_sinkhorn_n1_is_identity():
+    for z in (-3.0, 0.0, 2.5):
+        assert O.sinkhorn_knopp(np.array([[z]]), 20)[0, 0] == 1.0
+
+
+def test_sinkhorn_permutation_equivariance():
+    rng = np.random.default_rng(3)
+    n = 4
+    L = rng.standard_normal((n, n))
+    P = np.eye(n)[[2, 0, 3, 1]]
+    Q = np.eye(n)[[1, 3, 0, 2]]
+    np.testing.assert_allclose(O.sinkhorn_knopp(P @ L @ Q, 20), P @ O.sinkhorn_knopp(L, 20) @ Q,
+                               atol=1e-14)
+
+
+def test_sinkhorn_rows_exact_columns_converged_at_workload_logits():
+    rng = np.random.default_rng(4)
+    H = O.sinkhorn_knopp(_cfg_like_res_logits(rng, 512, 4), 20)
+    assert np.all(H >= 0)
+    assert np.max(np.abs(H.sum(-1) - 1)) < 1e-13
+    assert np.max(np.abs(H.sum(-2) - 1)) < 1e-6
+
+
+def test_sinkhorn_order_rows_last():
+    # Wide logits are far from converged after 20 iterations. Because T_r runs
+    # last, rows sum to 1 to rounding while columns visibly do not.
+    rng = np.random.default_rng(5)
+    H = O.sinkhorn_knopp(4.0 * rng.standard_normal((64, 4, 4)), 20)
+    assert np.max(np.abs(H.sum(-1) - 1)) < 1e-13
+    assert np.max(np.abs(H.sum(-2) - 1)) > 1e-4
+
+
+def test_sinkhorn_norm_and_closure():
+    # Eq. 6 properties: ||H||_2 <= 1 (doubly stochastic), products stay doubly stochastic.
+    rng = np.random.default_rng(6)
+    Hs = O.sinkhorn_knopp(_cfg_like_res_logits(rng, 8, 4, spread=0.5), 60)
+    for H in Hs:
+        assert np.linalg.norm(H, 2) <= 1 + 1e-12
+    prod = np.eye(4)
+    for H in Hs:
+        prod = H @ prod
+    np.testing.assert_allclose(prod.sum(0), 1, atol=1e-12)
+    np.testing.assert_allclose(prod.sum(1), 1, atol=1e-12)
+    assert np.all(prod >= 0)
+    assert np.linalg.norm(prod, 2) <= 1 + 1e-12
+
+
+def test_sinkhorn_near_permutation_pins_mat_order():
+    # A large logit on (i, (i+1) % n) drives H_res to that permutation; mat() is
+    # row-major so z_res[i*n + j] lands on H_res[i, j].
+    n = 4
+    T = 1
+    bias = np.zeros(n * n + 2 * n)
+    for i in range(n):
+        bias[2 * n + i * n + (i + 1) % n] = 25.0
+    X = np.random.default_rng(7).standard_normal((T, n, 8))
+    phi = np.zeros((n * 8, n * n + 2 * n))
+    _, _, h_res = O.hc_coeffs(X, phi, bias, [0.01] * 3, 20)
+    target = np.zeros((n, n))
+    for i in range(n):
+        target[i, (i + 1) % n] = 1.0
+    np.testing.assert_allclose(h_res[0], target, atol=1e-9)
+
+
+# -------------------------------------------------- projection, norm and gates
+
+def test_phi_zero_closed_form(golden_dir):
+    g = _load(golden_dir, "sinkhorn_phi0_n4.json")
+    n, C, T = 4, 16, 5
+    X = np.random.default_rng(8).standard_normal((T, n, C))
+    h_pre, h_post, h_res = O.hc_coeffs(X, np.zeros((n * C, n * n + 2 * n)), synth.mhc_bias(n),
+                                       [0.01] * 3, 20)
+    np.testing.assert_allclose(h_pre, g["h_pre"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(h_post, g["h_post"], rtol=0, atol=1e-15)
+    expect = np.full((n, n), g["h_res_offdiag"]) + np.eye(n) * (g["h_res_diag"] - g["h_res_offdiag"])
+    np.testing.assert_allclose(h_res, np.broadcast_to(expect, h_res.shape), atol=1e-15)
+
+
+def test_single_entry_state_closed_form():
+    # One nonzero entry a at (stream i, channel c): r = |a|/sqrt(nC), so the
+    # normalised flat vector is sign(a)*sqrt(nC) at index i*C + c and 0 elsewhere.
+    # One-hot phi columns then make every logit a closed form; distinct gates per
+    # block pin which alpha multiplies which block, and the row of phi that is
+    # hit pins the stream-major flattening.
+    n, C = 3, 5
+    ncol = n * n + 2 * n
+    i0, c0, a = 2, 3, -0.37
+    X = np.zeros((1, n, C))
+    X[0, i0, c0] = a
+    flat = i0 * C + c0
+    phi = np.zeros((n * C, ncol))
+    phi[flat, :] = np.arange(1, ncol + 1) / ncol       # every column reads the entry
+    phi[(flat + 1) % (n * C), :] = 100.0                # a wrong flattening would read this row
+    alpha = np.array([0.011, 0.023, 0.037])
+    bias = np.linspace(-0.5, 0.5, ncol)
+    val = -math.sqrt(n * C)
+    P = val * np.arange(1, ncol + 1) / ncol
+    z = np.concatenate([alpha[0] * P[:n], alpha[1] * P[n:2 * n], alpha[2] * P[2 * n:]]) + bias
+    h_pre, h_post, h_res = O.hc_coeffs(X, phi, bias, alpha, 20)
+    np.testing.assert_allclose(h_pre[0], 1 / (1 + np.exp(-z[:n])), rtol=1e-14)
+    np.testing.assert_allclose(h_post[0], 2 / (1 + np.exp(-z[n:2 * n])), rtol=1e-14)
+    np.testing.assert_allclose(h_res[0], O.sinkhorn_knopp(z[2 * n:].reshape(n, n), 20), rtol=1e-14)
+
+
+def test_projection_brute_force_tiny():
+    rng = np.random.default_rng(9)
+    n, C, T = 2, 3, 4
+    X = rng.standard_normal((T, n, C))
+    phi = rng.standard_normal((n * C, n * n + 2 * n))
+    bias = rng.standard_normal(n * n + 2 * n)
+    alpha = [0.3, 0.5, 0.7]
+    z = O.mhc_logits(X, phi, bias, alpha)
+    for t in range(T):
+        ss = 0.0
+        for i in range(n):
+            for c in range(C):
+                ss += X[t, i, c] ** 2
+        r = math.sqrt(ss / (n * C))
+        for j in range(n * n + 2 * n):
+            acc = 0.0
+            for i in range(n):
+                for c in range(C):
+                    acc += X[t, i, c] / r * phi[i * C + c, j]
+            a = alpha[0] if j < n else alpha[1] if j < 2 * n else alpha[2]
+            assert abs(z[t, j] - (a * acc + bias[j])) < 1e-12
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((7, 96)) * 3.0
+    u, r = O.rms_normalise(x)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (96,), eps=0.0).numpy()
+    np.testing.assert_allclose(u, ref, rtol=1e-13)
+
+
+def test_coeffs_scale_invariant_and_zero_state():
+    rng = np.random.default_rng(11)
+    n, C = 4, 32
+    X = rng.standard_normal((6, n, C))
+    phi = 0.02 * rng.standard_normal((n * C, n * n + 2 * n))
+    bias = synth.mhc_bias(n)
+    a = [0.01] * 3
+    for got, ref in zip(O.hc_coeffs(3.7 * X, phi, bias, a), O.hc_coeffs(X, phi, bias, a)):
+        np.testing.assert_allclose(got, ref, rtol=1e-13)
+    h_pre, h_post, h_res = O.hc_coeffs(np.zeros((1, n, C)), phi, bias, a)
+    np.testing.assert_allclose(h_pre, 0.5)
+    np.testing.assert_allclose(h_post, 1.0)
+    np.testing.assert_allclose(h_res[0], O.sinkhorn_knopp(np.eye(n), 20))
+
+
+# ---------------------------------------------------------------- pre / post
+
+def test_pre_post_closed_forms_phi_zero():
+    rng = np.random.default_rng(12)
+    n, C, T = 4, 24, 3
+    X = rng.standard_normal((T, n, C))
+    F = rng.standard_normal((T, C))
+    out = O.mhc_sublayer(X, np.zeros((n * C, n * n + 2 * n)), synth.mhc_bias(n), [0.01] * 3, F)
+    np.testing.assert_allclose(out["F_in"], 0.5 * X.sum(1), rtol=1e-14)
+    H0 = O.sinkhorn_knopp(np.eye(n), 20)
+    np.testing.assert_allclose(out["X_next"], np.einsum("ij,tjc->tic", H0, X) + F[:, None, :],
+                               rtol=1e-13, atol=1e-14)
+
+
+def test_pre_picks_weighted_streams():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((2, 3, 5))
+    h = np.array([[0.0, 1.0, 0.0], [0.0, 0.0, 2.0]])
+    np.testing.assert_array_equal(O.hc_pre(X, h), np.stack([X[0, 1], 2 * X[1, 2]]))
+
+
+def test_post_n1_is_plain_residual():
+    # n = 1 with H_res = [1], H_pre = H_post = 1: x_{l+1} = x_l + F (Eq. 1).
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((4, 1, 9))
+    F = rng.standard_normal((4, 9))
+    np.testing.assert_array_equal(O.hc_post(x, np.ones((4, 1, 1)), np.ones((4, 1)), F),
+                                  x + F[:, None, :])
+    np.testing.assert_array_equal(O.hc_pre(x, np.ones((4, 1))), x[:, 0])
+
+
+def test_post_cyclic_permutation_pins_row_column_roles():
+    rng = np.random.default_rng(15)
+    n = 4
+    X = rng.standard_normal((2, n, 6))
+    H = np.zeros((2, n, n))
+    for i in range(n):
+        H[:, i, (i + 1) % n] = 1.0
+    Y = O.hc_post(X, H, np.zeros((2, n)), np.zeros((2, 6)))
+    np.testing.assert_array_equal(Y, X[:, [(i + 1) % n for i in range(n)]])
+    hp = np.array([[1.0, 2.0, 3.0, 4.0], [0.5, 0, 0, 0]])
+    F = rng.standard_normal((2, 6))
+    Y2 = O.hc_post(np.zeros_like(X), H, hp, F)
+    np.testing.assert_allclose(Y2, hp[:, :, None] * F[:, None, :], rtol=0, atol=0)
+
+
+def test_post_conserves_stream_sum():
+    # Column sums of a doubly stochastic H_res are 1, so sum_i X_next[i] =
+    # sum_i X[i] + (sum_i h_post_i) F_out (feature mean kept; mHC notes section 1).
+    rng = np.random.default_rng(16)
+    n, C, T = 4, 64, 32
+    X = rng.standard_normal((T, n, C))
+    phi = 0.02 * rng.standard_normal((n * C, n * n + 2 * n))
+    F = rng.standard_normal((T, C))
+    out = O.mhc_sublayer(X, phi, synth.mhc_bias(n), [0.01] * 3, F)
+    lhs = out["X_next"].sum(1)
+    rhs = X.sum(1) + out["h_post"].sum(1)[:, None] * F
+    assert np.max(np.abs(lhs - rhs)) < 1e-6 * np.max(np.abs(rhs))
+
+
+def test_post_linear_in_state_and_output():
+    rng = np.random.default_rng(17)
+    n, C, T = 3, 7, 2
+    H = rng.uniform(size=(T, n, n))
+    hp = rng.uniform(size=(T, n))
+    X1, X2 = rng.standard_normal((2, T, n, C))
+    F1, F2 = rng.standard_normal((2, T, C))
+    lhs = O.hc_post(2 * X1 - X2, H, hp, 2 * F1 - F2)
+    rhs = 2 * O.hc_post(X1, H, hp, F1) - O.hc_post(X2, H, hp, F2)
+    np.testing.assert_allclose(lhs, rhs, atol=1e-13)
+
+
+# ---------------------------------------------------------------- routing
+
+def test_select_brute_force_tiny():
+    # Brute force over every (k-m)-subset of the candidates: the routed set is the
+    # unique subset S in which every member beats every non-member, where j beats
+    # j' if s_j > s_j', or s_j == s_j' and j < j' (ties to the lower index).
+    rng = np.random.default_rng(18)
+    N, k, m = 7, 4, 1
+    s = np.round(rng.uniform(size=(200, N - m)), 2)  # coarse values: many exact ties
+    idx = O.xhc_select(s, k, m)
+
+    def beats(t, j, jj):
+        return s[t, j] > s[t, jj] or (s[t, j] == s[t, jj] and j < jj)
+
+    for t in range(s.shape[0]):
+        ok = [comb for comb in itertools.combinations(range(N - m), k - m)
+              if all(beats(t, j, jj) for j in comb for jj in range(N - m) if jj not in comb)]
+        assert len(ok) == 1
+        expect = sorted(list(range(m)) + [m + j for j in ok[0]])
+        assert list(idx[t]) == expect, (t, s[t], idx[t], expect)
+
+
+def test_select_fixed_only_and_candidate_offset():
+    s = np.random.default_rng(19).uniform(size=(10, 6))
+    np.testing.assert_array_equal(O.xhc_select(s, 3, 3), np.tile([0, 1, 2], (10, 1)))
+    s2 = np.zeros((1, 6))
+    s2[0, 4] = 1.0  # candidate column 4 is stream m + 4
+    assert list(O.xhc_select(s2, 3, 2)[0]) == [0, 1, 6]
+
+
+def test_router_duplicate_columns_tie_to_lower_index():
+    rng = np.random.default_rng(20)
+    N, C, m, k = 6, 4, 2, 3
+    X = rng.standard_normal((50, N, C))
+    W = rng.standard_normal((N * C, N - m))
+    W[:, 3] = W[:, 1]  # streams m+1 and m+3 always tie exactly
+    s = O.xhc_router_scores(X, W)
+    assert np.array_equal(s[:, 1], s[:, 3])
+    idx = O.xhc_select(s, k, m)  # one routed slot
+    hits = 0
+    for t in range(50):
+        if s[t, 1] == s[t].max():
+            hits += 1
+            assert m + 1 in idx[t] and m + 3 not in idx[t]
+    assert hits > 0
+
+
+def test_router_selection_independent_of_normalisation():
+    # No bias and r > 0: ordering of u @ W equals ordering of x @ W.
+    rng = np.random.default_rng(21)
+    N, C, m, k = 8, 6, 2, 4
+    X = rng.standard_normal((40, N, C))
+    W = rng.standard_normal((N * C, N - m))
+    raw = O.sigmoid(X.reshape(40, -1) @ W)
+    np.testing.assert_array_equal(O.xhc_select(raw, k, m),
+                                  O.xhc_select(O.xhc_router_scores(X, W), k, m))
+
+
+def test_route_k_equals_N_is_dense_mhc():
+    # With every stream active (k = N, any m), the sparse update is mHC's.
+    rng = np.random.default_rng(22)
+    N, C, T = 4, 16, 6
+    X = rng.standard_normal((T, N, C))
+    phi_pre = 0.3 * rng.standard_normal((N * C, N))
+    phi_act = 0.3 * rng.standard_normal((N * C, N + N * N))
+    b_pre = 0.1 * rng.standard_normal(N)
+    b_act = 0.1 * rng.standard_normal(N + N * N)
+    F = rng.standard_normal((T, C))
+    W = rng.standard_normal((N * C, N - 1))
+    a_pre, a_post, a_res = 0.2, 0.3, 0.4
+    pre = O.xhc_pre(X, phi_pre, b_pre, a_pre, W, k=N, m=1)
+    np.testing.assert_array_equal(pre["idx"], np.tile(np.arange(N), (T, 1)))
+    Xn, _, _ = O.xhc_route(X, pre["idx"], phi_act, b_act, a_post, a_res, F)
+    ref = O.mhc_sublayer(X, np.concatenate([phi_pre, phi_act], 1),
+                         np.concatenate([b_pre, b_act]), [a_pre, a_post, a_res], F)
+    np.testing.assert_allclose(pre["F_in"], ref["F_in"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(Xn, ref["X_next"], rtol=1e-13, atol=1e-13)
+
+
+def test_route_passes_inactive_streams_and_identity_maps():
+    rng = np.random.default_rng(23)
+    N, C, T, k = 8, 5, 9, 3
+    X = rng.standard_normal((T, N, C))
+    idx = np.array([sorted(rng.choice(N, k, replace=False)) for _ in range(T)])
+    phi_act = rng.standard_normal((k * C, k + k * k))
+    b_act = rng.standard_normal(k + k * k)
+    Xn, _, _ = O.xhc_route(X, idx, phi_act, b_act, 0.01, 0.01, rng.standard_normal((T, C)))
+    for t in range(T):
+        for i in range(N):
+            if i not in idx[t]:
+                assert np.array_equal(Xn[t, i], X[t, i])
+    # alpha = 0, res bias 40*I and post bias -40: H_res ~ I, H_post ~ 0 -> X unchanged.
+    b_id = np.concatenate([np.full(k, -40.0), (40.0 * np.eye(k)).reshape(-1)])
+    Xi, Hp, Hr = O.xhc_route(X, idx, phi_act, b_id, 0.0, 0.0, rng.standard_normal((T, C)))
+    np.testing.assert_allclose(Xi, X, atol=1e-15)
+
+
+def test_route_gather_order_and_slot_semantics():
+    # Slot a of the active set is stream idx[a]; a cyclic H_res_A moves slot a+1 into slot a.
+    rng = np.random.default_rng(24)
+    N, C, k = 6, 4, 3
+    X = rng.standard_normal((1, N, C))
+    idx = np.array([[1, 3, 4]])
+    b = np.concatenate([np.full(k, -60.0),
+                        (60.0 * np.eye(k)[[1, 2, 0]]).reshape(-1)])  # H[a, a+1] large
+    Xn, _, _ = O.xhc_route(X, idx, np.zeros((k * C, k + k * k)), b, 0.0, 0.0, np.zeros((1, C)))
+    np.testing.assert_allclose(Xn[0, 1], X[0, 3], atol=1e-12)
+    np.testing.assert_allclose(Xn[0, 3], X[0, 4], atol=1e-12)
+    np.testing.assert_allclose(Xn[0, 4], X[0, 1], atol=1e-12)
+
+
+# ---------------------------------------------------------------- augmentation
+
+def test_conv_one_hot_taps():
+    rng = np.random.default_rng(25)
+    B, S, C, kap = 2, 10, 3, 4
+    F = rng.standard_normal((B * S, C))
+    w_last = np.zeros((C, kap))
+    w_last[:, kap - 1] = 1.0
+    np.testing.assert_array_equal(O.causal_dwconv(F, w_last, B, S), F)
+    w_first = np.zeros((C, kap))
+    w_first[:, 0] = 1.0
+    g = O.causal_dwconv(F, w_first, B, S).reshape(B, S, C)
+    Fb = F.reshape(B, S, C)
+    np.testing.assert_array_equal(g[:, kap - 1:], Fb[:, :S - kap + 1])
+    assert np.all(g[:, :kap - 1] == 0)
+
+
+def test_conv_matches_fir_filter_per_sequence():
+    rng = np.random.default_rng(26)
+    B, S, C = 3, 40, 5
+    F = rng.standard_normal((B * S, C))
+    for kap in (4, 8, 12):
+        w = rng.standard_normal((C, kap))
+        g = O.causal_dwconv(F, w, B, S).reshape(B, S, C)
+        for b in range(B):
+            for c in range(C):
+                ref = scipy.signal.lfilter(w[c, ::-1], [1.0], F.reshape(B, S, C)[b, :, c])
+                np.testing.assert_allclose(g[b, :, c], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mgs_orthogonal_first_exact_and_qr():
+    rng = np.random.default_rng(27)
+    T, Kr, C = 6, 4, 50
+    G = rng.standard_normal((T, Kr, C))
+    G[:, 1:] += 0.8 * G[:, :1]  # correlated, as the conv outputs are
+    V = O.modified_gram_schmidt(G)
+    np.testing.assert_array_equal(V[:, 0], G[:, 0])
+    for t in range(T):
+        for i in range(Kr):
+            for j in range(i):
+                cos = V[t, i] @ V[t, j] / (np.linalg.norm(V[t, i]) * np.linalg.norm(V[t, j]))
+                assert abs(cos) < 1e-12
+        Q, R = np.linalg.qr(G[t].T)
+        for j in range(Kr):
+            np.testing.assert_allclose(V[t, j], Q[:, j] * R[j, j], rtol=1e-10, atol=1e-12)
+
+
+def test_mgs_keeps_orthogonal_components():
+    rng = np.random.default_rng(28)
+    Q, _ = np.linalg.qr(rng.standard_normal((30, 4)))
+    G = (Q * np.array([2.0, 0.5, 3.0, 1.5])).T[None]
+    np.testing.assert_allclose(O.modified_gram_schmidt(G), G, atol=1e-14)
+
+
+def test_augment_components_order():
+    # V[:, 0] is the raw output; V[:, 1] is the kappa_1 conv minus its projection.
+    rng = np.random.default_rng(29)
+    B, S, C = 1, 16, 6
+    F = rng.standard_normal((B * S, C))
+    ws = [rng.standard_normal((C, k)) for k in (4, 8, 12)]
+    V = O.xhc_augment(F, ws, B, S)
+    g1 = O.causal_dwconv(F, ws[0], B, S)
+    coef = np.sum(g1 * F, 1) / np.sum(F * F, 1)
+    np.testing.assert_allclose(V[:, 1], g1 - coef[:, None] * F, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(V[:, 0], F)
+
+
+# ------------------------------------------------------------ synth recipe
+
+def test_bf16_rounding_is_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e-3], np.float32)
+    r, bits = synth.round_to_bf16(vals)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(r, ref)
+    assert bits.dtype == np.uint16
