@@ -1,0 +1,210 @@
+/*
+ * hc.h - C ABI of the MI355X (gfx950) hyper-connection sublayer library (libhc.so).
+ *
+ * The library computes one forward hyper-connection sublayer per token:
+ * mHC's Sinkhorn-constrained n-stream residual mixing and xHC's routed,
+ * augmented extension. Sources of the definitions:
+ *   [mHC]   "mHC: Manifold-Constrained Hyper-Connections" (paper notes),
+ *           Eq. 3, Eq. 6, section 4.2 (Eq. 7-9), section 4.3.1 (Eq. 10-19 and
+ *           the F_pre / F_post,res kernels).
+ *   [xHC]   "xHC: Expanded Hyper-Connections" (paper summary), Method: temporal
+ *           feature augmentation; sparse residual stream architecture, steps
+ *           1-3; parameterisation and practical deployment.
+ *   [xHC-R] xHC repository README, default xHC configuration table.
+ *
+ * Conventions shared by every call:
+ *   - All tensor arguments are DEVICE pointers to caller-owned, C-contiguous,
+ *     row-major buffers. Scalars and the kappa array of xhc_augment are host
+ *     values. The library never allocates, frees or synchronises; every call
+ *     only enqueues kernels on `stream` (a hipStream_t; NULL = default stream)
+ *     and returns. Buffers must stay alive until that work completes.
+ *   - Stream tensors (X, F_out, F_in, Wb, V) have dtype HC_F32 or HC_BF16;
+ *     coefficient tensors, phi, biases and conv weights are always float32.
+ *     Accumulation is float32; every stored stream value is rounded once
+ *     (round-to-nearest-even for bfloat16).
+ *   - Token state X is [T, n, C] (stream-major within a token); the flattened
+ *     state vec(x) of a token is its contiguous n*C slice (index i*C + c).
+ *   - Return value: HC_OK (0) or a negative status. Argument errors are found
+ *     on the host before any HIP call; the outputs are then untouched.
+ *     HC_ERR_DEVICE means no usable GPU; HC_ERR_LAUNCH means a kernel launch
+ *     failed (outputs undefined). No call prints, aborts or throws.
+ *   - T == 0 (or B*S == 0) is valid and does nothing; pointers may then be NULL.
+ *   - Outputs must not overlap inputs, except where a call says otherwise.
+ *   - Calls keep no global mutable state and are safe to issue from several
+ *     host threads; calls that share output or workspace buffers must be
+ *     ordered by the caller (same stream or events).
+ *   - Workspaces: calls that take `workspace` need at least the bytes returned
+ *     by the matching *_workspace_bytes query (device memory, 256-byte
+ *     aligned, contents need not be initialised, reused freely between calls
+ *     on one stream).
+ */
+#ifndef HC_H_
+#define HC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HC_F32 0
+#define HC_BF16 1
+
+#define HC_OK 0
+#define HC_ERR_NULL (-1)      /* a required pointer is NULL */
+#define HC_ERR_SHAPE (-2)     /* a size or count is out of range */
+#define HC_ERR_DTYPE (-3)     /* unknown dtype code */
+#define HC_ERR_ALIGN (-4)     /* a pointer is not aligned to its element size */
+#define HC_ERR_ALIAS (-5)     /* an output overlaps an input it must not */
+#define HC_ERR_DEVICE (-6)    /* no usable HIP device */
+#define HC_ERR_LAUNCH (-7)    /* a kernel launch failed */
+#define HC_ERR_WORKSPACE (-8) /* workspace missing, misaligned or too small */
+
+/* Limits checked by every call. */
+#define HC_MAX_STREAMS 64     /* n (mHC) and N (xHC) */
+#define HC_MAX_MHC_STREAMS 16 /* n for the mHC calls */
+#define HC_MAX_ACTIVE 16      /* k (xHC) */
+#define HC_MAX_COMPONENTS 8   /* K = r + 1 write-back components */
+#define HC_MAX_KAPPA 32       /* causal conv kernel size */
+#define HC_MAX_ITERS 10000    /* Sinkhorn iterations */
+
+/* Human-readable text of a status code (static string, never NULL). */
+const char* hc_status_string(int status);
+
+/* ABI version (major*100 + minor). */
+int hc_version(void);
+
+/* ------------------------------------------------------------------ mHC -- */
+
+/* Workspace bytes needed by hc_coeffs / hc_coeffs_pre for these sizes. */
+int64_t hc_coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
+
+/*
+ * hc_coeffs - mHC coefficients of every token ([mHC] Eq. 7-9 and 14-19).
+ *   X      [T, n, C] stream dtype.       1 <= n <= 16, C >= 1.
+ *   phi    [n*C, n*n + 2n] float32, columns [pre n | post n | res n*n], the
+ *          RMSNorm gain folded in (Eq. 10, 14). Row i*C + c multiplies x[i, c].
+ *   bias   [n*n + 2n] float32, same column order (Eq. 13).
+ *   alpha_pre, alpha_post, alpha_res: the three gates (Eq. 12).
+ *   sinkhorn_iters >= 1: fixed iteration count (t_max; 20 on the pages).
+ * Per token: r = ||vec x||_2 / sqrt(nC) (Eq. 15; r = 0 gives a zero
+ * normalised state), z = alpha_block * (vec x @ phi) / r + bias (Eq. 16),
+ * h_pre = sigmoid(z_pre), h_post = 2 sigmoid(z_post), h_res = Sinkhorn-Knopp
+ * of exp(mat(z_res)) with columns then rows normalised per iteration (Eq. 9),
+ * mat row-major: h_res[i][j] = z_res[i*n + j].
+ * Outputs (float32): h_pre [T, n], h_post [T, n], h_res [T, n, n].
+ */
+int hc_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C,
+              const float* phi, const float* bias,
+              float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters,
+              float* h_pre, float* h_post, float* h_res,
+              void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * hc_pre - dense pre-read F_pre = H_pre x ([mHC] 4.3.1):
+ *   F_in[t, c] = sum_i h_pre[t, i] * X[t, i, c].
+ *   X [T, n, C] and F_in [T, C] in the stream dtype; h_pre [T, n] float32.
+ */
+int hc_pre(const void* X, int dtype, int64_t T, int n, int64_t C,
+           const float* h_pre, void* F_in, void* stream);
+
+/*
+ * hc_coeffs_pre - hc_coeffs followed by hc_pre, fused so that the state is
+ * read from HBM once where the shape allows it. Same arguments as hc_coeffs
+ * plus F_in [T, C] (stream dtype). h_pre may be NULL (then not stored).
+ */
+int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C,
+                  const float* phi, const float* bias,
+                  float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters,
+                  float* h_pre, float* h_post, float* h_res, void* F_in,
+                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * hc_post - fused post/res write F_post,res = H_res x + H_post^T F ([mHC] Eq. 3,
+ * 4.3.1), reading (n+1)C and writing nC elements per token:
+ *   X_next[t, i, c] = sum_j h_res[t, i, j] X[t, j, c] + h_post[t, i] F_out[t, c].
+ *   X, X_next [T, n, C] and F_out [T, C] in the stream dtype; h_res [T, n, n]
+ *   and h_post [T, n] float32. X_next may equal X (in place); any other
+ *   overlap with an input is HC_ERR_ALIAS.
+ */
+int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C,
+            const float* h_res, const float* h_post, const void* F_out, void* X_next,
+            void* stream);
+
+/* ------------------------------------------------------------------ xHC -- */
+
+/* Workspace bytes needed by xhc_pre (with_router != 0 when w_router is given). */
+int64_t xhc_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int with_router, int dtype);
+
+/*
+ * xhc_pre - full-state pass of an xHC sublayer ([xHC] steps 1 and 2):
+ *   dense read over all N streams: h_pre = sigmoid(alpha_pre * (vec X @ phi_pre)
+ *   / r + b_pre), F_in[t, c] = sum_{i<N} h_pre[t, i] X[t, i, c], and, when
+ *   w_router != NULL, the router: score[t, j] = sigmoid((vec X @ w_router)[j] / r)
+ *   for candidate stream m + j (j < N - m), and idx[t] = the m fixed streams
+ *   0..m-1 plus the k - m candidates with the highest score (equal scores go
+ *   to the lower stream index), listed in ascending stream order.
+ *   X [T, N, C], F_in [T, C] stream dtype; phi_pre [N*C, N], b_pre [N],
+ *   w_router [N*C, N - m] float32; outputs h_pre [T, N] float32 (may be NULL),
+ *   idx [T, k] int32, score [T, N - m] float32 (both required iff w_router).
+ *   1 <= m <= k <= N <= 64, k <= 16.
+ */
+int xhc_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+            const float* phi_pre, const float* b_pre, float alpha_pre, const float* w_router,
+            float* h_pre, void* F_in, int32_t* idx, float* score,
+            void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by xhc_route (with_router != 0 when idx_in is NULL). */
+int64_t xhc_route_workspace_bytes(int64_t T, int N, int64_t C, int k, int m, int K,
+                                  int with_router, int dtype);
+
+/*
+ * xhc_route - stream routing, gather, sparse mix and scatter, IN PLACE on X
+ * ([xHC] steps 1 and 3; parameterisation).
+ *   If idx_in is NULL the active set is selected here from the full state with
+ *   w_router exactly as in xhc_pre; otherwise idx_in [T, k] (int32, k distinct
+ *   stream indices in [0, N), ascending) is used and w_router is ignored.
+ *   Per token: X_A = X[t, idx[a], :] (a < k, slot order); r_A = ||vec X_A|| /
+ *   sqrt(kC); z = alpha * (vec X_A @ phi_act) / r_A + b_act with columns
+ *   [post k*K (a*K + j) | res k*k (a*k + b)] and alpha_post / alpha_res on the
+ *   two blocks; H_post_A = 2 sigmoid(z_post) [k, K]; H_res_A = Sinkhorn-Knopp
+ *   of exp(z_res) [k, k]; then X[t, idx[a], :] = sum_b H_res_A[a, b] X_A[b, :]
+ *   + sum_j H_post_A[a, j] Wb[t, j, :]. Streams not in idx are not written.
+ *   Wb [T, K, C] stream dtype: the K write-back components (K = 1: F_out;
+ *   K = r + 1: the output of xhc_augment). 1 <= K <= 8.
+ *   phi_act [k*C, k*K + k*k], b_act [k*K + k*k] float32.
+ *   Outputs: idx_out [T, k] int32 (required), score_out [T, N - m] float32
+ *   (optional, only written when selecting), h_post_out [T, k, K] and
+ *   h_res_out [T, k, k] float32 (optional).
+ *   Index entries outside [0, N) in idx_in leave the token unchanged.
+ */
+int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+              const float* w_router, const int32_t* idx_in,
+              const float* phi_act, const float* b_act, float alpha_post, float alpha_res,
+              int sinkhorn_iters, const void* Wb, int K,
+              int32_t* idx_out, float* score_out, float* h_post_out, float* h_res_out,
+              void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * xhc_augment - temporal feature augmentation ([xHC] temporal feature
+ * augmentation; kernel sizes {4, 8, 12} in [xHC-R]):
+ *   tokens are B sequences of S tokens ([B, S] row-major, T = B*S);
+ *   g_j[t, c] = sum_{s<kappa_j} w_j[c, s] * F_out[t - kappa_j + 1 + s, c], with
+ *   zeros before the start of each sequence (w_j[c, kappa_j - 1] weights the
+ *   current token); then Gram-Schmidt (modified form, no normalisation):
+ *   V[t, 0] = F_out[t]; V[t, j] = g_j minus its projections on V[t, 0..j-1],
+ *   removed one after another.
+ *   F_out [T, C] stream dtype `dtype`; conv_w = [C, kappa_1] then [C, kappa_2] ...
+ *   float32; kappa: HOST array of r kernel sizes (1..32); 0 <= r <= 7;
+ *   V [T, r + 1, C] in `v_dtype`.
+ */
+int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
+                const float* conv_w, const int* kappa, int r,
+                void* V, int v_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HC_H_ */

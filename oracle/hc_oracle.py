@@ -5,7 +5,7 @@ the cpu_baseline leg of bench.py may import or run this module. The product path
 (the HIP library and its Python binding) never calls it, and this module imports
 nothing from the product package: the two share no kernels, helpers, tables or
 constants. Inputs come from the seeded generators in
-stream_residual_mixing_amd/synth.py, which hold no arithmetic of the method.
+synth/__init__.py, which hold no arithmetic of the method.
 
 Everything is evaluated in float64 straight from the definitions on the pages:
 

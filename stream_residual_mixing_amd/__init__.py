@@ -1,0 +1,263 @@
+"""Python binding of libhc, the gfx950 hyper-connection sublayer library.
+
+Every function here has the name of a C entry point in include/hc.h and only
+marshals arguments: it checks tensor devices/dtypes/contiguity, allocates the
+outputs and the workspace with torch (device memory only), and calls the C ABI
+with raw device pointers and the current HIP stream. All arithmetic runs in the
+HIP kernels of libhc.so. If the library is missing, every call raises.
+
+Stream tensors are torch.float32 or torch.bfloat16 on a HIP device; coefficient
+tensors, phi, biases and conv weights are torch.float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhc.so")
+
+HC_F32, HC_BF16 = 0, 1
+_DT = {torch.float32: HC_F32, torch.bfloat16: HC_BF16}
+
+_c_i64, _c_int, _c_float, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+
+_SIGS = {
+    "hc_status_string": (ctypes.c_char_p, [_c_int]),
+    "hc_version": (_c_int, []),
+    "hc_coeffs_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int]),
+    "hc_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float,
+                           _c_int, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "hc_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp]),
+    "hc_coeffs_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float,
+                               _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "hc_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "xhc_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
+    "xhc_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _c_float, _vp,
+                         _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "xhc_route_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int,
+                                           _c_int]),
+    "xhc_route": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                           _c_float, _c_float, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64,
+                           _vp]),
+    "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp]),
+}
+
+_lib = None
+
+
+class HCError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libhc.so with argument types set (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m stream_residual_mixing_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().hc_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise HCError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(t, name, dtypes=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a tensor on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+def _f32(t, name):
+    return _dev_tensor(t, name, (torch.float32,))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if nbytes < 0:
+        raise ValueError("invalid sizes for the workspace query")
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------- mHC
+
+
+def hc_coeffs_workspace_bytes(T: int, n: int, C: int, dtype) -> int:
+    return int(lib().hc_coeffs_workspace_bytes(T, n, C, _DT[dtype]))
+
+
+def hc_coeffs(X, phi, bias, alpha, sinkhorn_iters=20, *, out=None, workspace=None, stream=None):
+    """(h_pre [T,n], h_post [T,n], h_res [T,n,n]) of X [T,n,C]; alpha = (pre, post, res)."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    phi, bias = _f32(phi, "phi"), _f32(bias, "bias")
+    if out is None:
+        out = (torch.empty(T, n, device=X.device), torch.empty(T, n, device=X.device),
+               torch.empty(T, n, n, device=X.device))
+    h_pre, h_post, h_res = out
+    ws = _workspace(hc_coeffs_workspace_bytes(T, n, C, X.dtype), X.device, workspace)
+    a = [float(v) for v in alpha]
+    _check("hc_coeffs", lib().hc_coeffs(_ptr(X), _DT[X.dtype], T, n, C, _ptr(phi), _ptr(bias), a[0], a[1],
+                                        a[2], int(sinkhorn_iters), _ptr(h_pre), _ptr(h_post), _ptr(h_res),
+                                        _ptr(ws), ws.numel(), _stream(X.device, stream)))
+    return h_pre, h_post, h_res
+
+
+def hc_pre(X, h_pre, *, out=None, stream=None):
+    """F_in [T,C] = sum_i h_pre[:, i] X[:, i, :]."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    h_pre = _f32(h_pre, "h_pre")
+    F_in = torch.empty(T, C, dtype=X.dtype, device=X.device) if out is None else out
+    _check("hc_pre", lib().hc_pre(_ptr(X), _DT[X.dtype], T, n, C, _ptr(h_pre), _ptr(F_in),
+                                  _stream(X.device, stream)))
+    return F_in
+
+
+def hc_coeffs_pre(X, phi, bias, alpha, sinkhorn_iters=20, *, out=None, workspace=None, stream=None,
+                  want_h_pre=True):
+    """Fused coefficients + pre-read: (h_pre or None, h_post, h_res, F_in)."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    phi, bias = _f32(phi, "phi"), _f32(bias, "bias")
+    if out is None:
+        out = (torch.empty(T, n, device=X.device) if want_h_pre else None,
+               torch.empty(T, n, device=X.device), torch.empty(T, n, n, device=X.device),
+               torch.empty(T, C, dtype=X.dtype, device=X.device))
+    h_pre, h_post, h_res, F_in = out
+    ws = _workspace(hc_coeffs_workspace_bytes(T, n, C, X.dtype), X.device, workspace)
+    a = [float(v) for v in alpha]
+    _check("hc_coeffs_pre", lib().hc_coeffs_pre(_ptr(X), _DT[X.dtype], T, n, C, _ptr(phi), _ptr(bias), a[0],
+                                                a[1], a[2], int(sinkhorn_iters), _ptr(h_pre), _ptr(h_post),
+                                                _ptr(h_res), _ptr(F_in), _ptr(ws), ws.numel(),
+                                                _stream(X.device, stream)))
+    return h_pre, h_post, h_res, F_in
+
+
+def hc_post(X, h_res, h_post, F_out, *, out=None, stream=None):
+    """X_next [T,n,C] = h_res @ X + h_post^T F_out (out may be X itself)."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
+    X_next = torch.empty_like(X) if out is None else out
+    _check("hc_post", lib().hc_post(_ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(h_res, "h_res")),
+                                    _ptr(_f32(h_post, "h_post")), _ptr(F_out), _ptr(X_next),
+                                    _stream(X.device, stream)))
+    return X_next
+
+
+# ------------------------------------------------------------------- xHC
+
+
+def xhc_pre_workspace_bytes(T, N, C, m, with_router, dtype) -> int:
+    return int(lib().xhc_pre_workspace_bytes(T, N, C, m, int(bool(with_router)), _DT[dtype]))
+
+
+def xhc_pre(X, phi_pre, b_pre, alpha_pre, w_router=None, k=4, m=2, *, want_h_pre=True, workspace=None,
+            stream=None):
+    """Full-state pass: dict(h_pre, F_in[, idx, score])."""
+    X = _dev_tensor(X, "X", _DT)
+    T, N, C = X.shape
+    dev = X.device
+    h_pre = torch.empty(T, N, device=dev) if want_h_pre else None
+    F_in = torch.empty(T, C, dtype=X.dtype, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev) if w_router is not None else None
+    score = torch.empty(T, N - m, device=dev) if w_router is not None else None
+    ws = _workspace(xhc_pre_workspace_bytes(T, N, C, m, w_router is not None, X.dtype), dev, workspace)
+    _check("xhc_pre", lib().xhc_pre(_ptr(X), _DT[X.dtype], T, N, C, k, m, _ptr(_f32(phi_pre, "phi_pre")),
+                                    _ptr(_f32(b_pre, "b_pre")), float(alpha_pre),
+                                    _ptr(None if w_router is None else _f32(w_router, "w_router")),
+                                    _ptr(h_pre), _ptr(F_in), _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
+                                    _stream(dev, stream)))
+    out = dict(h_pre=h_pre, F_in=F_in)
+    if w_router is not None:
+        out.update(idx=idx, score=score)
+    return out
+
+
+def xhc_route_workspace_bytes(T, N, C, k, m, K, with_router, dtype) -> int:
+    return int(lib().xhc_route_workspace_bytes(T, N, C, k, m, K, int(bool(with_router)), _DT[dtype]))
+
+
+def xhc_route(X, Wb, phi_act, b_act, alpha_post, alpha_res, *, k=4, m=2, idx=None, w_router=None,
+              sinkhorn_iters=20, want_coeffs=False, workspace=None, stream=None):
+    """In-place sparse update of X [T,N,C] with write-back components Wb [T,K,C] (or [T,C]).
+
+    Returns dict(idx[, score][, h_post, h_res])."""
+    X = _dev_tensor(X, "X", _DT)
+    T, N, C = X.shape
+    dev = X.device
+    Wb = _dev_tensor(Wb, "Wb", (X.dtype,))
+    K = 1 if Wb.dim() == 2 else Wb.shape[1]
+    idx_in = None if idx is None else _dev_tensor(idx, "idx", (torch.int32,))
+    idx_out = torch.empty(T, k, dtype=torch.int32, device=dev)
+    score = torch.empty(T, N - m, device=dev) if idx_in is None else None
+    hp = torch.empty(T, k, K, device=dev) if want_coeffs else None
+    hr = torch.empty(T, k, k, device=dev) if want_coeffs else None
+    ws = _workspace(xhc_route_workspace_bytes(T, N, C, k, m, K, idx_in is None, X.dtype), dev, workspace)
+    _check("xhc_route", lib().xhc_route(_ptr(X), _DT[X.dtype], T, N, C, k, m,
+                                        _ptr(None if w_router is None else _f32(w_router, "w_router")),
+                                        _ptr(idx_in), _ptr(_f32(phi_act, "phi_act")), _ptr(_f32(b_act, "b_act")),
+                                        float(alpha_post), float(alpha_res), int(sinkhorn_iters), _ptr(Wb), K,
+                                        _ptr(idx_out), _ptr(score), _ptr(hp), _ptr(hr), _ptr(ws), ws.numel(),
+                                        _stream(dev, stream)))
+    out = dict(idx=idx_out)
+    if score is not None:
+        out["score"] = score
+    if want_coeffs:
+        out.update(h_post=hp, h_res=hr)
+    return out
+
+
+def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, stream=None):
+    """V [T, r+1, C] = Gram-Schmidt([F_out; causal depthwise convs]); conv_w concatenated fp32."""
+    F_out = _dev_tensor(F_out, "F_out", _DT)
+    T, C = F_out.shape
+    if T != batch * seq:
+        raise ValueError("F_out rows must equal batch * seq")
+    r = len(kappas)
+    vdt = F_out.dtype if v_dtype is None else v_dtype
+    V = torch.empty(T, r + 1, C, dtype=vdt, device=F_out.device)
+    karr = (ctypes.c_int * max(r, 1))(*[int(x) for x in kappas])
+    w = _f32(conv_w, "conv_w") if r > 0 else None
+    _check("xhc_augment", lib().xhc_augment(_ptr(F_out), _DT[F_out.dtype], batch, seq, C, _ptr(w), karr, r,
+                                            _ptr(V), _DT[vdt], _stream(F_out.device, stream)))
+    return V
+
+
+__all__ = [
+    "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
+    "hc_coeffs_pre", "hc_post", "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
+    "xhc_route", "xhc_augment",
+]

@@ -1,0 +1,423 @@
+// extern "C" entry points of libhc (declared in include/hc.h): argument
+// validation on the host, workspace carving and kernel dispatch.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hc.h"
+#include "hc_launch.h"
+#include "hc_fast.h"
+
+namespace {
+
+inline int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+inline bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline size_t esize(int dtype) { return dtype == HC_F32 ? 4 : 2; }
+
+// True when [a, a+na) and [b, b+nb) share a byte.
+inline bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int device_status() {
+  static const int status = [] {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return HC_ERR_DEVICE;
+    return HC_OK;
+  }();
+  return status;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? HC_OK : HC_ERR_LAUNCH; }
+
+inline bool dtype_ok(int d) { return d == HC_F32 || d == HC_BF16; }
+
+// Vector (16-byte) paths need C % 8 == 0 and 16-byte aligned stream pointers.
+inline bool vec_ok(int64_t C, std::initializer_list<const void*> ps) {
+  if (C % 8 != 0) return false;
+  for (const void* p : ps)
+    if (p && !aligned_to(p, 16)) return false;
+  return true;
+}
+
+// Workspace of the mHC coefficient calls: projection rows P [T, n*n+2n],
+// squared norms ss [T], a private h_pre [T, n] (used when the caller passes
+// none) and the packed phi of the fast path.
+struct CoeffWs {
+  float* P;
+  float* ss;
+  float* h_pre;
+  void* packed;
+};
+
+int64_t mhc_ws_bytes(int64_t T, int n, int64_t C, int dtype) {
+  const int ncols = n * n + 2 * n;
+  int64_t b = align256(T * ncols * 4) + align256(T * 4) + align256(T * n * 4);
+  b += align256(hc::fast_coeffs_packed_bytes(n, C, dtype));
+  return b;
+}
+
+CoeffWs carve_mhc(void* ws, int64_t T, int n) {
+  const int ncols = n * n + 2 * n;
+  char* p = (char*)ws;
+  CoeffWs w;
+  w.P = (float*)p;
+  p += align256(T * ncols * 4);
+  w.ss = (float*)p;
+  p += align256(T * 4);
+  w.h_pre = (float*)p;
+  p += align256(T * n * 4);
+  w.packed = p;
+  return w;
+}
+
+int check_mhc_common(const void* X, int dtype, int64_t T, int n, int64_t C) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || n < 1 || n > HC_MAX_MHC_STREAMS) return HC_ERR_SHAPE;
+  if (T > 0 && !X) return HC_ERR_NULL;
+  if (X && !aligned_to(X, esize(dtype))) return HC_ERR_ALIGN;
+  return HC_OK;
+}
+
+int check_coeff_args(const void* X, int dtype, int64_t T, int n, int64_t C, const float* phi,
+                     const float* bias, int iters, const float* h_pre, const float* h_post,
+                     const float* h_res, bool h_pre_optional, void* ws, int64_t ws_bytes) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK) return s;
+  if (iters < 1 || iters > HC_MAX_ITERS) return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!phi || !bias || !h_post || !h_res || (!h_pre && !h_pre_optional)) return HC_ERR_NULL;
+  for (const void* p : {(const void*)phi, (const void*)bias, (const void*)h_pre, (const void*)h_post,
+                        (const void*)h_res})
+    if (p && !aligned_to(p, 4)) return HC_ERR_ALIGN;
+  if (!ws || !aligned_to(ws, 256) || ws_bytes < mhc_ws_bytes(T, n, C, dtype)) return HC_ERR_WORKSPACE;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype);
+  const int64_t wsb = mhc_ws_bytes(T, n, C, dtype);
+  const void* outs[3] = {h_pre, h_post, h_res};
+  const int64_t ob[3] = {T * n * 4, T * n * 4, T * n * n * 4};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], ob[i], X, xb) || overlaps(outs[i], ob[i], phi, (int64_t)n * C * (n * n + 2 * n) * 4) ||
+        overlaps(outs[i], ob[i], bias, (n * n + 2 * n) * 4) || overlaps(outs[i], ob[i], ws, wsb))
+      return HC_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  }
+  if (overlaps(ws, wsb, X, xb) || overlaps(ws, wsb, phi, (int64_t)n * C * (n * n + 2 * n) * 4) ||
+      overlaps(ws, wsb, bias, (n * n + 2 * n) * 4))
+    return HC_ERR_ALIAS;
+  return HC_OK;
+}
+
+// Generic coefficient path: projection, then the per-token epilogue.
+int run_coeffs_generic(const void* X, int dtype, int64_t T, int n, int64_t C, const float* phi,
+                       const float* bias, float a_pre, float a_post, float a_res, int iters,
+                       float* h_pre, float* h_post, float* h_res, const CoeffWs& w,
+                       hipStream_t st) {
+  const int ncols = n * n + 2 * n;
+  hipError_t e = hc::launch_proj_generic(dtype, X, (int64_t)n * C, T, C, n, nullptr, n, phi, ncols,
+                                         nullptr, 0, w.P, w.ss, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  e = hc::launch_coeff_epilogue(w.P, w.ss, (float)((double)n * (double)C), T, n, n, n, a_pre, a_post,
+                                a_res, bias, iters, h_pre, h_post, h_res, st);
+  return launch_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hc_status_string(int status) {
+  switch (status) {
+    case HC_OK: return "ok";
+    case HC_ERR_NULL: return "a required pointer is NULL";
+    case HC_ERR_SHAPE: return "a size or count is out of range";
+    case HC_ERR_DTYPE: return "unknown dtype code";
+    case HC_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case HC_ERR_ALIAS: return "an output overlaps an input it must not";
+    case HC_ERR_DEVICE: return "no usable HIP device";
+    case HC_ERR_LAUNCH: return "a kernel launch failed";
+    case HC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    default: return "unknown status";
+  }
+}
+
+int hc_version(void) { return 100; }
+
+int64_t hc_coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
+  if (T < 0 || n < 1 || n > HC_MAX_MHC_STREAMS || C < 1 || !dtype_ok(dtype)) return -1;
+  return mhc_ws_bytes(T, n, C, dtype);
+}
+
+int hc_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* phi,
+              const float* bias, float alpha_pre, float alpha_post, float alpha_res,
+              int sinkhorn_iters, float* h_pre, float* h_post, float* h_res, void* workspace,
+              int64_t workspace_bytes, void* stream) {
+  int s = check_coeff_args(X, dtype, T, n, C, phi, bias, sinkhorn_iters, h_pre, h_post, h_res,
+                           false, workspace, workspace_bytes);
+  if (s != HC_OK || T == 0) return s;
+  if ((s = device_status()) != HC_OK) return s;
+  const CoeffWs w = carve_mhc(workspace, T, n);
+  hipStream_t st = (hipStream_t)stream;
+  if (hc::fast_coeffs_supported(dtype, n, C, X)) {
+    return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
+                                                    alpha_res, sinkhorn_iters, h_pre, h_post,
+                                                    h_res, nullptr, w.packed, st));
+  }
+  return run_coeffs_generic(X, dtype, T, n, C, phi, bias, alpha_pre, alpha_post, alpha_res,
+                            sinkhorn_iters, h_pre, h_post, h_res, w, st);
+}
+
+int hc_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_pre, void* F_in,
+           void* stream) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!h_pre || !F_in) return HC_ERR_NULL;
+  if (!aligned_to(h_pre, 4) || !aligned_to(F_in, esize(dtype))) return HC_ERR_ALIGN;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+  if (overlaps(F_in, fb, X, xb) || overlaps(F_in, fb, h_pre, T * n * 4)) return HC_ERR_ALIAS;
+  if ((s = device_status()) != HC_OK) return s;
+  return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X, F_in}), X, T, n, C, h_pre, F_in,
+                                              (hipStream_t)stream));
+}
+
+int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* phi,
+                  const float* bias, float alpha_pre, float alpha_post, float alpha_res,
+                  int sinkhorn_iters, float* h_pre, float* h_post, float* h_res, void* F_in,
+                  void* workspace, int64_t workspace_bytes, void* stream) {
+  int s = check_coeff_args(X, dtype, T, n, C, phi, bias, sinkhorn_iters, h_pre, h_post, h_res,
+                           true, workspace, workspace_bytes);
+  if (s != HC_OK || T == 0) return s;
+  if (!F_in) return HC_ERR_NULL;
+  if (!aligned_to(F_in, esize(dtype))) return HC_ERR_ALIGN;
+  {
+    const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+    const int64_t wsb = mhc_ws_bytes(T, n, C, dtype);
+    if (overlaps(F_in, fb, X, xb) || overlaps(F_in, fb, workspace, wsb) ||
+        overlaps(F_in, fb, h_pre, T * n * 4) || overlaps(F_in, fb, h_post, T * n * 4) ||
+        overlaps(F_in, fb, h_res, T * n * n * 4) ||
+        overlaps(F_in, fb, phi, (int64_t)n * C * (n * n + 2 * n) * 4) ||
+        overlaps(F_in, fb, bias, (n * n + 2 * n) * 4))
+      return HC_ERR_ALIAS;
+  }
+  if ((s = device_status()) != HC_OK) return s;
+  const CoeffWs w = carve_mhc(workspace, T, n);
+  hipStream_t st = (hipStream_t)stream;
+  if (hc::fast_coeffs_supported(dtype, n, C, X) && aligned_to(F_in, 16)) {
+    return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
+                                                    alpha_res, sinkhorn_iters, h_pre, h_post,
+                                                    h_res, F_in, w.packed, st));
+  }
+  // Generic: the pre-read needs h_pre, kept in the workspace when the caller
+  // does not ask for it.
+  float* hp = h_pre ? h_pre : w.h_pre;
+  s = run_coeffs_generic(X, dtype, T, n, C, phi, bias, alpha_pre, alpha_post, alpha_res,
+                         sinkhorn_iters, hp, h_post, h_res, w, st);
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X, F_in}), X, T, n, C, hp, F_in, st));
+}
+
+int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+            const float* h_post, const void* F_out, void* X_next, void* stream) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!h_res || !h_post || !F_out || !X_next) return HC_ERR_NULL;
+  if (!aligned_to(h_res, 4) || !aligned_to(h_post, 4) || !aligned_to(F_out, esize(dtype)) ||
+      !aligned_to(X_next, esize(dtype)))
+    return HC_ERR_ALIGN;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+  if (X_next != X && overlaps(X_next, xb, X, xb)) return HC_ERR_ALIAS;
+  if (overlaps(X_next, xb, F_out, fb) || overlaps(X_next, xb, h_res, T * n * n * 4) ||
+      overlaps(X_next, xb, h_post, T * n * 4))
+    return HC_ERR_ALIAS;
+  if ((s = device_status()) != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (hc::fast_post_supported(dtype, n, C, X, F_out, X_next))
+    return launch_status(hc::launch_fast_post(X, T, C, h_res, h_post, F_out, X_next, st));
+  return launch_status(hc::launch_post_generic(dtype, vec_ok(C, {X, F_out, X_next}), X, T, n, C,
+                                               h_res, h_post, F_out, X_next, st));
+}
+
+// ------------------------------------------------------------------ xHC --
+
+static int64_t xhc_pre_ws(int64_t T, int N, int m, int with_router) {
+  const int pcols = N + (with_router ? N - m : 0);
+  return align256(T * pcols * 4) + align256(T * 4) + align256(T * N * 4);
+}
+
+int64_t xhc_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int with_router, int dtype) {
+  if (T < 0 || N < 1 || N > HC_MAX_STREAMS || m < 1 || m > N || C < 1 || !dtype_ok(dtype)) return -1;
+  return xhc_pre_ws(T, N, m, with_router);
+}
+
+int xhc_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+            const float* phi_pre, const float* b_pre, float alpha_pre, const float* w_router,
+            float* h_pre, void* F_in, int32_t* idx, float* score, void* workspace,
+            int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || m < 1 || k < m ||
+      k > N || k > HC_MAX_ACTIVE)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!X || !phi_pre || !b_pre || !F_in) return HC_ERR_NULL;
+  if (w_router && (!idx || !score)) return HC_ERR_NULL;
+  const size_t es = esize(dtype);
+  if (!aligned_to(X, es) || !aligned_to(F_in, es) || !aligned_to(phi_pre, 4) || !aligned_to(b_pre, 4) ||
+      (w_router && !aligned_to(w_router, 4)) || (h_pre && !aligned_to(h_pre, 4)) ||
+      (idx && !aligned_to(idx, 4)) || (score && !aligned_to(score, 4)))
+    return HC_ERR_ALIGN;
+  const int with_router = w_router != nullptr;
+  const int64_t wsb = xhc_pre_ws(T, N, m, with_router);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t xb = T * N * C * (int64_t)es, fb = T * C * (int64_t)es;
+  const void* outs[4] = {F_in, h_pre, with_router ? idx : nullptr, with_router ? score : nullptr};
+  const int64_t ob[4] = {fb, T * N * 4, T * k * 4, T * (N - m) * 4};
+  const void* ins[5] = {X, phi_pre, b_pre, w_router, workspace};
+  const int64_t ib[5] = {xb, (int64_t)N * C * N * 4, N * 4, (int64_t)N * C * (N - m) * 4, wsb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return HC_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  }
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* p = (char*)workspace;
+  const int pcols = N + (with_router ? N - m : 0);
+  float* P = (float*)p;
+  p += align256(T * pcols * 4);
+  float* ss = (float*)p;
+  p += align256(T * 4);
+  float* hp = h_pre ? h_pre : (float*)p;
+  hipError_t e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, phi_pre, N,
+                                         w_router, with_router ? N - m : 0, P, ss, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  e = hc::launch_xhc_select(P, pcols, 0, N, ss, (float)((double)N * (double)C), T, N, k, m, alpha_pre,
+                            b_pre, hp, with_router ? score : nullptr, with_router ? idx : nullptr, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X, F_in}), X, T, N, C, hp, F_in, st));
+}
+
+static int64_t xhc_route_ws(int64_t T, int N, int k, int m, int K, int with_router) {
+  const int acols = k * K + k * k;
+  int64_t b = align256(T * acols * 4) + align256(T * 4) + align256(T * k * K * 4) + align256(T * k * k * 4);
+  if (with_router) b += align256(T * (N - m) * 4) + align256(T * 4);
+  return b;
+}
+
+int64_t xhc_route_workspace_bytes(int64_t T, int N, int64_t C, int k, int m, int K, int with_router,
+                                  int dtype) {
+  if (T < 0 || N < 1 || N > HC_MAX_STREAMS || m < 1 || k < m || k > N || k > HC_MAX_ACTIVE || K < 1 ||
+      K > HC_MAX_COMPONENTS || C < 1 || !dtype_ok(dtype))
+    return -1;
+  return xhc_route_ws(T, N, k, m, K, with_router);
+}
+
+int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, const float* w_router,
+              const int32_t* idx_in, const float* phi_act, const float* b_act, float alpha_post,
+              float alpha_res, int sinkhorn_iters, const void* Wb, int K, int32_t* idx_out,
+              float* score_out, float* h_post_out, float* h_res_out, void* workspace,
+              int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || m < 1 || k < m || k > N ||
+      k > HC_MAX_ACTIVE || K < 1 || K > HC_MAX_COMPONENTS || sinkhorn_iters < 1 ||
+      sinkhorn_iters > HC_MAX_ITERS)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!X || !phi_act || !b_act || !Wb || !idx_out) return HC_ERR_NULL;
+  if (!idx_in && !w_router) return HC_ERR_NULL;
+  const size_t es = esize(dtype);
+  if (!aligned_to(X, es) || !aligned_to(Wb, es) || !aligned_to(phi_act, 4) || !aligned_to(b_act, 4) ||
+      !aligned_to(idx_out, 4) || (idx_in && !aligned_to(idx_in, 4)) ||
+      (w_router && !aligned_to(w_router, 4)) || (score_out && !aligned_to(score_out, 4)) ||
+      (h_post_out && !aligned_to(h_post_out, 4)) || (h_res_out && !aligned_to(h_res_out, 4)))
+    return HC_ERR_ALIGN;
+  const int with_router = idx_in == nullptr;
+  const int64_t wsb = xhc_route_ws(T, N, k, m, K, with_router);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int acols = k * K + k * k;
+  const int64_t xb = T * N * C * (int64_t)es;
+  // X is updated in place; the other outputs must not overlap anything.
+  const void* outs[5] = {X, idx_out, with_router ? score_out : nullptr, h_post_out, h_res_out};
+  const int64_t ob[5] = {xb, T * k * 4, T * (N - m) * 4, T * k * K * 4, T * k * k * 4};
+  const void* ins[6] = {Wb, phi_act, b_act, w_router, idx_in, workspace};
+  const int64_t ib[6] = {T * K * C * (int64_t)es, (int64_t)k * C * acols * 4, acols * 4,
+                         w_router ? (int64_t)N * C * (N - m) * 4 : 0, T * k * 4, wsb};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 6; ++j) {
+      if (i == 1 && j == 4 && outs[i] == ins[j]) continue;  // idx_out may equal idx_in
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return HC_ERR_ALIAS;
+    }
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  }
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* p = (char*)workspace;
+  float* P = (float*)p;
+  p += align256(T * acols * 4);
+  float* ss = (float*)p;
+  p += align256(T * 4);
+  float* Hp = h_post_out ? h_post_out : (float*)p;
+  p += align256(T * k * K * 4);
+  float* Hr = h_res_out ? h_res_out : (float*)p;
+  p += align256(T * k * k * 4);
+  hipError_t e;
+  if (with_router) {
+    float* Pr = (float*)p;
+    p += align256(T * (N - m) * 4);
+    float* ssf = (float*)p;
+    e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, w_router, N - m, nullptr, 0,
+                                Pr, ssf, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+    e = hc::launch_xhc_select(Pr, N - m, 0, 0, ssf, (float)((double)N * (double)C), T, N, k, m, 0.f,
+                              nullptr, nullptr, score_out, idx_out, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+  } else if (idx_out != idx_in) {
+    e = hipMemcpyAsync(idx_out, idx_in, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+  }
+  e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, k, idx_out, N, phi_act, acols, nullptr, 0,
+                              P, ss, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  e = hc::launch_coeff_epilogue(P, ss, (float)((double)k * (double)C), T, 0, k * K, k, 0.f, alpha_post,
+                                alpha_res, b_act, sinkhorn_iters, nullptr, Hp, Hr, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, Wb}), X, T, N, C, k, idx_out, Hr, Hp,
+                                              Wb, K, st));
+}
+
+int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, const float* conv_w,
+                const int* kappa, int r, void* V, int v_dtype, void* stream) {
+  if (!dtype_ok(dtype) || !dtype_ok(v_dtype)) return HC_ERR_DTYPE;
+  if (B < 0 || S < 0 || C < 1 || C > (1ll << 26) || r < 0 || r > HC_MAX_COMPONENTS - 1) return HC_ERR_SHAPE;
+  if (r > 0 && !kappa) return HC_ERR_NULL;
+  int64_t wtot = 0;
+  hc::ConvSpec spec{};
+  spec.r = r;
+  for (int j = 0; j < r; ++j) {
+    if (kappa[j] < 1 || kappa[j] > HC_MAX_KAPPA) return HC_ERR_SHAPE;
+    spec.kappa[j] = kappa[j];
+    spec.offset[j] = wtot;
+    wtot += C * kappa[j];
+  }
+  if (hc::augment_generic_lds_bytes(r, C) > 160 * 1024 - 1024) return HC_ERR_SHAPE;
+  const int64_t T = B * S;
+  if (T == 0) return HC_OK;
+  if (!F_out || !V || (r > 0 && !conv_w)) return HC_ERR_NULL;
+  if (!aligned_to(F_out, esize(dtype)) || !aligned_to(V, esize(v_dtype)) || (conv_w && !aligned_to(conv_w, 4)))
+    return HC_ERR_ALIGN;
+  const int64_t vb = T * (r + 1) * C * (int64_t)esize(v_dtype);
+  if (overlaps(V, vb, F_out, T * C * (int64_t)esize(dtype)) || overlaps(V, vb, conv_w, wtot * 4))
+    return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_augment_generic(dtype, v_dtype, F_out, B, S, C, conv_w, spec, V,
+                                                  (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Host-side launch functions of libhc's kernels (internal; the public ABI is include/hc.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define HC_MAX_COMPONENTS_DEV 8
+
+namespace hc {
+
+// Causal depthwise convolution set: r kernels of sizes kappa[j]; the weights of
+// kernel j start `offset[j]` floats into the concatenated weight array.
+struct ConvSpec {
+  int r;
+  int kappa[HC_MAX_COMPONENTS_DEV - 1];
+  int64_t offset[HC_MAX_COMPONENTS_DEV - 1];
+};
+
+// ---- generic kernels (hc_generic.hip)
+hipError_t launch_proj_generic(int dtype, const void* X, int64_t tok_stride, int64_t T, int64_t C,
+                               int nvec, const int32_t* idx, int Nstreams, const float* phiA,
+                               int colsA, const float* phiB, int colsB, float* P, float* ss,
+                               hipStream_t st);
+hipError_t launch_coeff_epilogue(const float* P, const float* ss, float len, int64_t T, int npre,
+                                 int npost, int nres, float a_pre, float a_post, float a_res,
+                                 const float* bias, int iters, float* h_pre, float* h_post,
+                                 float* h_res, hipStream_t st);
+hipError_t launch_xhc_select(const float* P, int pcols, int pre_off, int router_off, const float* ss,
+                             float len, int64_t T, int N, int k, int m, float a_pre,
+                             const float* b_pre, float* h_pre, float* score, int32_t* idx,
+                             hipStream_t st);
+hipError_t launch_pre_generic(int dtype, bool vec, const void* X, int64_t T, int n, int64_t C,
+                              const float* h, void* F_in, hipStream_t st);
+hipError_t launch_post_generic(int dtype, bool vec, const void* X, int64_t T, int n, int64_t C,
+                               const float* h_res, const float* h_post, const void* F, void* Y,
+                               hipStream_t st);
+hipError_t launch_mix_generic(int dtype, bool vec, void* X, int64_t T, int N, int64_t C, int k,
+                              const int32_t* idx, const float* H_res, const float* H_post,
+                              const void* Wb, int K, hipStream_t st);
+int64_t augment_generic_lds_bytes(int r, int64_t C);
+hipError_t launch_augment_generic(int dtype, int vdtype, const void* F, int64_t B, int64_t S,
+                                  int64_t C, const float* w, const ConvSpec& spec, void* V,
+                                  hipStream_t st);
+
+}  // namespace hc

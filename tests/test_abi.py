@@ -1,0 +1,136 @@
+"""CPU tests of the C-ABI boundary: libhc.so loads, exports every symbol that
+include/hc.h declares, and rejects bad arguments on the host before any device
+work (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hc_testutil import have_gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hc.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def hc():
+    import stream_residual_mixing_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libhc.so is not built (run __graft_entry__.build())")
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("hc_coeffs", "hc_pre", "hc_coeffs_pre", "hc_post", "xhc_pre", "xhc_route",
+                 "xhc_augment", "hc_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(hc):
+    raw = ctypes.CDLL(hc.LIB_PATH)
+    missing = [n for n in _declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_c_entry_points(hc):
+    for n in _declared_functions():
+        if n in ("hc_status_string", "hc_version"):
+            continue
+        assert hasattr(hc, n), n
+
+
+def test_status_strings(hc):
+    L = hc.lib()
+    for code in range(0, -9, -1):
+        assert L.hc_status_string(code)
+    assert L.hc_version() >= 100
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def test_validation_rejects_bad_arguments_before_device_work(hc):
+    L = hc.lib()
+    ws = hc.lib().hc_coeffs_workspace_bytes(8, 4, 64, 1)
+    assert ws > 0
+    args = lambda **kw: dict(dict(X=FAKE, dt=1, T=8, n=4, C=64), **kw)
+
+    def coeffs(X=FAKE, dt=1, T=8, n=4, C=64, phi=FAKE, bias=FAKE, iters=20, hpre=FAKE,
+               wsp=ctypes.c_void_p(0x20000), wsb=ws):
+        return L.hc_coeffs(X, dt, T, n, C, phi, bias, 0.01, 0.01, 0.01, iters, hpre,
+                           ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000), wsp, wsb, None)
+
+    assert coeffs(dt=7) == -3
+    assert coeffs(n=0) == -2
+    assert coeffs(n=17) == -2
+    assert coeffs(C=0) == -2
+    assert coeffs(T=-1) == -2
+    assert coeffs(iters=0) == -2
+    assert coeffs(X=None) == -1
+    assert coeffs(phi=None) == -1
+    assert coeffs(hpre=None) == -1
+    assert coeffs(X=ctypes.c_void_p(0x10001)) == -4
+    assert coeffs(wsb=ws - 1) == -8
+    assert coeffs(wsp=ctypes.c_void_p(0x20010)) == -8
+    # overlapping output and input
+    assert coeffs(hpre=ctypes.c_void_p(0x10000)) == -5
+    # empty input is valid and does nothing
+    assert coeffs(T=0, X=None, phi=None, hpre=None, wsp=None, wsb=0) == 0
+
+    post = lambda X=FAKE, Y=ctypes.c_void_p(0x90000), F=ctypes.c_void_p(0x50000): L.hc_post(
+        X, 1, 8, 4, 64, ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000), F, Y, None)
+    assert post(Y=None) == -1
+    assert post(Y=ctypes.c_void_p(0x10002)) == -5       # partial overlap with X
+    assert post(F=ctypes.c_void_p(0x90010)) == -5       # F_out inside X_next
+    assert L.hc_pre(FAKE, 1, 8, 4, 64, FAKE, ctypes.c_void_p(0x10010), None) == -5
+
+    # xHC shape rules: 1 <= m <= k <= N, k <= 16, K <= 8
+    def xpre(N=16, k=4, m=2):
+        return L.xhc_pre(FAKE, 1, 8, N, 64, k, m, FAKE, FAKE, 0.01, None, None,
+                         ctypes.c_void_p(0x80000), None, None, ctypes.c_void_p(0x100000), 1 << 20, None)
+    assert xpre(m=0) == -2
+    assert xpre(k=1, m=2) == -2
+    assert xpre(N=3, k=4) == -2
+    assert xpre(N=65) == -2
+    assert xpre(N=32, k=17) == -2
+
+    def xroute(K=1, idx=FAKE, w=None):
+        return L.xhc_route(ctypes.c_void_p(0x200000), 1, 8, 16, 64, 4, 2, w, idx, FAKE, FAKE, 0.01, 0.01,
+                           20, ctypes.c_void_p(0x300000), K, ctypes.c_void_p(0x400000), None, None, None,
+                           ctypes.c_void_p(0x500000), 1 << 20, None)
+    assert xroute(K=0) == -2
+    assert xroute(K=9) == -2
+    assert xroute(idx=None, w=None) == -1
+
+    karr = (ctypes.c_int * 3)(4, 8, 40)
+    assert L.xhc_augment(FAKE, 1, 2, 16, 64, FAKE, karr, 3, ctypes.c_void_p(0x600000), 1, None) == -2
+    karr = (ctypes.c_int * 3)(4, 8, 12)
+    assert L.xhc_augment(FAKE, 1, 2, 16, 64, FAKE, karr, 8, ctypes.c_void_p(0x600000), 1, None) == -2
+    assert L.xhc_augment(FAKE, 5, 2, 16, 64, FAKE, karr, 3, ctypes.c_void_p(0x600000), 1, None) == -3
+
+
+@pytest.mark.skipif(have_gpu(), reason="checks the no-device status; on a GPU box the call would run")
+def test_valid_call_without_device_reports_device_error(hc):
+    L = hc.lib()
+    ws = L.hc_coeffs_workspace_bytes(8, 4, 64, 1)
+    s = L.hc_coeffs(FAKE, 1, 8, 4, 64, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), 0.01, 0.01,
+                    0.01, 20, ctypes.c_void_p(0x300000), ctypes.c_void_p(0x310000),
+                    ctypes.c_void_p(0x320000), ctypes.c_void_p(0x400000), ws, None)
+    assert s == -6
+
+
+def test_workspace_queries(hc):
+    L = hc.lib()
+    assert L.hc_coeffs_workspace_bytes(0, 4, 64, 1) >= 0
+    assert L.hc_coeffs_workspace_bytes(8, 0, 64, 1) == -1
+    assert L.xhc_pre_workspace_bytes(8, 16, 64, 2, 1, 1) > L.xhc_pre_workspace_bytes(8, 16, 64, 2, 0, 1)
+    assert L.xhc_route_workspace_bytes(8, 16, 64, 4, 2, 4, 1, 1) > 0
+    assert L.xhc_route_workspace_bytes(8, 16, 64, 4, 2, 9, 1, 1) == -1

@@ -1,0 +1,222 @@
+"""GPU parity of the mHC calls (hc_coeffs, hc_pre, hc_coeffs_pre, hc_post) against
+the fp64 oracle, through the C ABI. Inputs come from the seeded synth recipe;
+the oracle always sees the same (stream-dtype rounded) values as the GPU."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from hc_testutil import (check_bf16, check_fp32, check_stream, dev, have_gpu, host64, note,
+                         rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+if have_gpu():
+    import torch
+    import stream_residual_mixing_amd as hc
+
+
+def _run_sublayer(inp, fused=True, iters=20):
+    X = dev(inp["X"])
+    phi, bias = dev(inp["phi"]), dev(inp["bias"])
+    alpha = [float(a) for a in inp["alpha"]]
+    if fused:
+        h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(X, phi, bias, alpha, iters)
+    else:
+        h_pre, h_post, h_res = hc.hc_coeffs(X, phi, bias, alpha, iters)
+        F_in = hc.hc_pre(X, h_pre)
+    X_next = hc.hc_post(X, h_res, h_post, dev(inp["F_out"]))
+    torch.cuda.synchronize()
+    return dict(h_pre=host64(h_pre), h_post=host64(h_post), h_res=host64(h_res), F_in=host64(F_in),
+                X_next=host64(X_next))
+
+
+def _compare_all(got, ref, dtype, literal=False):
+    for k in ("h_pre", "h_post", "h_res"):
+        check_fp32(k, got[k], ref[k])
+    check_stream("F_in", dtype, got["F_in"], ref["F_in"], literal)
+    check_stream("X_next", dtype, got["X_next"], ref["X_next"], literal)
+    # Sinkhorn sums of the GPU coefficients
+    assert np.max(np.abs(got["h_res"].sum(-1) - 1)) < 1e-6
+    assert np.max(np.abs(got["h_res"].sum(-2) - 1)) < 1e-6
+
+
+def _oracle(inp, iters=20):
+    return O.mhc_sublayer(inp["X"].values, inp["phi"], inp["bias"], inp["alpha"], inp["F_out"].values, iters)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_workload0_fp32_full(fused):
+    w = synth.WORKLOADS[0]
+    note(f"mHC workload 0 (n=4 C=256 T=512 fp32) fused={fused}")
+    inp = synth.mhc_layer(0, 0, w["T"], w["n"], w["C"], w["dtype"])
+    _compare_all(_run_sublayer(inp, fused), _oracle(inp), synth.F32)
+
+
+@pytest.mark.parametrize("T", [1, 7, 133])
+@pytest.mark.parametrize("fused", [True, False])
+def test_workload1_shape_ragged_T(T, fused):
+    note(f"mHC n=4 C=4096 bf16 T={T} fused={fused}")
+    inp = synth.mhc_layer(1, 0, T, 4, 4096, synth.BF16)
+    _compare_all(_run_sublayer(inp, fused), _oracle(inp), synth.BF16, literal=True)
+
+
+def test_workload1_full_size_sampled():
+    """Full-size run (T=8192, the benchmarked launch); oracle on sampled tokens,
+    invariants on every token."""
+    w = synth.WORKLOADS[1]
+    note("mHC workload 1 full size (n=4 C=4096 T=8192 bf16)")
+    inp = synth.mhc_layer(1, 0, w["T"], w["n"], w["C"], w["dtype"])
+    got = _run_sublayer(inp, fused=True)
+    rng = np.random.default_rng(101)
+    sample = np.unique(np.concatenate([[0, w["T"] - 1], rng.choice(w["T"], 254, replace=False)]))
+    sub = dict(inp)
+    sub["X"] = synth.Tensor(inp["X"].values[sample], synth.BF16)
+    sub["F_out"] = synth.Tensor(inp["F_out"].values[sample], synth.BF16)
+    ref = _oracle(sub)
+    _compare_all({k: v[sample] for k, v in got.items()}, ref, synth.BF16, literal=True)
+    h = got["h_res"]
+    assert np.all(h >= 0)
+    assert np.max(np.abs(h.sum(-1) - 1)) < 1e-6 and np.max(np.abs(h.sum(-2) - 1)) < 1e-6
+    assert np.all((got["h_pre"] > 0) & (got["h_pre"] < 1))
+    assert np.all((got["h_post"] > 0) & (got["h_post"] < 2))
+
+
+@pytest.mark.parametrize("n,C,dtype", [(1, 64, synth.F32), (2, 100, synth.BF16), (3, 40, synth.F32),
+                                       (4, 100, synth.BF16), (4, 24, synth.F32), (8, 96, synth.BF16),
+                                       (16, 33, synth.F32), (5, 512, synth.BF16)])
+def test_other_stream_counts_and_ragged_channels(n, C, dtype):
+    note(f"mHC n={n} C={C} {dtype} T=37")
+    inp = synth.mhc_layer(7, n, 37, n, C, dtype)
+    _compare_all(_run_sublayer(inp, fused=True), _oracle(inp), dtype)
+    _compare_all(_run_sublayer(inp, fused=False), _oracle(inp), dtype)
+
+
+def test_n1_is_plain_residual_bit_exact():
+    # n = 1: H_res = [1]; with supplied h_post = 1 the post write is x + F_out (Eq. 1).
+    note("mHC n=1 plain residual fp32")
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((9, 1, 64)).astype(np.float32)
+    F = rng.standard_normal((9, 64)).astype(np.float32)
+    Y = hc.hc_post(dev(X), dev(np.ones((9, 1, 1))), dev(np.ones((9, 1))), dev(F))
+    np.testing.assert_array_equal(Y.cpu().numpy(), (X.astype(np.float64) + F[:, None, :]).astype(np.float32))
+    inp = synth.mhc_layer(8, 0, 9, 1, 64, synth.F32)
+    _, _, h_res = hc.hc_coeffs(dev(inp["X"]), dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    assert np.all(h_res.cpu().numpy() == 1.0)
+
+
+def test_post_in_place():
+    note("mHC post in place bf16")
+    inp = synth.mhc_layer(9, 0, 21, 4, 4096, synth.BF16)
+    ref = _oracle(inp)
+    X = dev(inp["X"])
+    _, h_post, h_res, _ = hc.hc_coeffs_pre(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    hc.hc_post(X, h_res, h_post, dev(inp["F_out"]), out=X)
+    torch.cuda.synchronize()
+    check_bf16("X_next in place", host64(X), ref["X_next"])
+
+
+def test_empty_input():
+    note("mHC T=0")
+    X = torch.empty(0, 4, 64, dtype=torch.bfloat16, device="cuda")
+    phi = torch.zeros(256, 24, device="cuda")
+    out = hc.hc_coeffs_pre(X, phi, torch.zeros(24, device="cuda"), [0.01] * 3)
+    assert out[3].shape == (0, 64)
+    Y = hc.hc_post(X, out[2], out[1], torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"))
+    assert Y.shape == (0, 4, 64)
+
+
+def test_scale_invariance_power_of_two_bit_exact():
+    # coeffs(2^k X) == coeffs(X): sums and products scale exactly by powers of two
+    # and r = sqrt(ss/len) is correctly rounded, so the logits are bit-identical.
+    note("mHC scale invariance bf16 n=4 C=4096")
+    inp = synth.mhc_layer(10, 0, 40, 4, 4096, synth.BF16)
+    X = dev(inp["X"])
+    a = hc.hc_coeffs(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    b = hc.hc_coeffs(X * 4, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_phi_zero_closed_form_on_gpu(golden_dir):
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "sinkhorn_phi0_n4.json")))
+    note("mHC phi=0 closed form")
+    inp = synth.mhc_layer(11, 0, 16, 4, 4096, synth.BF16)
+    phi = torch.zeros(4 * 4096, 24, device="cuda")
+    h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(dev(inp["X"]), phi, dev(inp["bias"]), [0.01] * 3)
+    np.testing.assert_allclose(h_pre.cpu().numpy(), g["h_pre"], atol=1e-7)
+    np.testing.assert_allclose(h_post.cpu().numpy(), g["h_post"], atol=1e-7)
+    expect = np.full((4, 4), g["h_res_offdiag"]) + np.eye(4) * (g["h_res_diag"] - g["h_res_offdiag"])
+    np.testing.assert_allclose(h_res.cpu().numpy(), np.broadcast_to(expect, (16, 4, 4)), atol=1e-6)
+    check_bf16("F_in = sum/2", host64(F_in), 0.5 * inp["X"].values.astype(np.float64).sum(1))
+
+
+def test_wide_logits_follow_twenty_iterations():
+    # Far from convergence the output is M^(20), not the limit: compare with the
+    # oracle's 20-iteration result (rows exact, columns off by >1e-4).
+    note("mHC wide Sinkhorn logits")
+    inp = synth.mhc_layer(12, 0, 33, 4, 256, synth.F32)
+    inp["bias"] = inp["bias"].copy()
+    inp["bias"][8:] = np.random.default_rng(3).standard_normal(16).astype(np.float32) * 3.0
+    inp["alpha"] = np.array([0.5, 0.5, 2.0], np.float32)
+    got = _run_sublayer(inp, fused=True)
+    ref = _oracle(inp)
+    check_fp32("h_res wide", got["h_res"], ref["h_res"])
+    assert np.max(np.abs(ref["h_res"].sum(-2) - 1)) > 1e-4
+
+
+@pytest.mark.slow
+def test_workload2_chain_per_layer_and_conservation():
+    """8 chained sublayers at full size: per layer the oracle runs on the GPU's
+    bf16 X_l for sampled tokens; the stream-sum conservation holds on all tokens."""
+    w = synth.WORKLOADS[2]
+    T, n, C = w["T"], w["n"], w["C"]
+    rng = np.random.default_rng(202)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 62, replace=False)]))
+    first = synth.mhc_layer(2, 0, T, n, C, w["dtype"])
+    X = dev(first["X"])
+    del first["X"]
+    for layer in range(w["layers"]):
+        note(f"mHC workload 2 layer {layer} (n=4 C=7168 T=16384 bf16)")
+        inp = first if layer == 0 else synth.mhc_layer(2, layer, T, n, C, w["dtype"], draw_x=False)
+        F = dev(inp["F_out"])
+        h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+        Xn = hc.hc_post(X, h_res, h_post, F)
+        torch.cuda.synchronize()
+        Xs = host64(X[torch.from_numpy(sample).cuda()])
+        ref = O.mhc_sublayer(Xs, inp["phi"], inp["bias"], inp["alpha"], inp["F_out"].values[sample])
+        got = dict(h_pre=host64(h_pre)[sample], h_post=host64(h_post)[sample], h_res=host64(h_res)[sample],
+                   F_in=host64(F_in[torch.from_numpy(sample).cuda()]),
+                   X_next=host64(Xn[torch.from_numpy(sample).cuda()]))
+        _compare_all(got, ref, synth.BF16)
+        # conservation over every token: sum_i X_next = sum_i X + (sum_i h_post) F
+        lhs = Xn.float().sum(1)
+        rhs = X.float().sum(1) + h_post.sum(1, keepdim=True) * F.float()
+        e = (torch.linalg.vector_norm(lhs - rhs) / torch.linalg.vector_norm(rhs)).item()
+        assert e < 1e-2, f"layer {layer}: conservation rel err {e}"
+        X = Xn
+        del F, F_in
+
+
+def test_workload2_shape_chain_end_to_end():
+    """Reduced-T chain of 8 layers at C=7168: each layer against the oracle on the
+    GPU's input, and the independent oracle chain (bf16 rounding between layers)
+    against the GPU's last state."""
+    T, n, C = 45, 4, 7168
+    first = synth.mhc_layer(2, 0, T, n, C, synth.BF16)
+    X = dev(first["X"])
+    Xo = first["X"].values.astype(np.float64)
+    for layer in range(8):
+        note(f"mHC 8-layer chain C=7168 T=45 layer {layer}")
+        inp = first if layer == 0 else synth.mhc_layer(2, layer, T, n, C, synth.BF16, draw_x=False)
+        h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+        Xn = hc.hc_post(X, h_res, h_post, dev(inp["F_out"]))
+        torch.cuda.synchronize()
+        ref = O.mhc_sublayer(host64(X), inp["phi"], inp["bias"], inp["alpha"], inp["F_out"].values)
+        _compare_all(dict(h_pre=host64(h_pre), h_post=host64(h_post), h_res=host64(h_res),
+                          F_in=host64(F_in), X_next=host64(Xn)), ref, synth.BF16)
+        chain = O.mhc_sublayer(Xo, inp["phi"], inp["bias"], inp["alpha"], inp["F_out"].values)
+        Xo = synth.round_to_bf16(chain["X_next"].astype(np.float32))[0].astype(np.float64)
+        X = Xn
+    assert rel_l2(host64(X), Xo) < 1e-2

@@ -19,7 +19,7 @@ import scipy.special
 import torch
 
 import oracle as O
-from stream_residual_mixing_amd import synth
+import synth
 
 
 def _load(golden_dir, name):
