@@ -3,12 +3,19 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 One step is one forward hyper-connection sublayer over T = 8192 tokens
-(batch 4 x seq 2048) of a bfloat16 n=4, C=4096 stream state: the fused
-coefficient + pre-read call (hc_coeffs_pre: RMS factor, skinny projection,
-gates, sigmoid / 2*sigmoid, 20 Sinkhorn iterations, F_in) and the fused
-post/res write (hc_post), with F_out supplied. Inputs are seeded synthetic
-tensors already resident in HBM; three input sets are rotated so no step finds
-its inputs in the 256 MB Infinity Cache.
+(batch 4 x seq 2048) of a bfloat16 n=4, C=4096 stream state, F_out supplied:
+RMS factor, skinny projection nC -> 24, gates, sigmoid / 2*sigmoid, 20
+Sinkhorn iterations, pre-read F_in and post/res write X_next.
+
+Headline (steady state of a chain of sublayers): hc_pre (pre-read with the
+coefficients computed for this sublayer) + hc_post_coeffs (post/res write fused
+with the coefficients of the state it writes, for the next sublayer). Every step
+computes one sublayer's coefficients, pre-read and post write; the coefficients
+used by the first timed step come from the untimed warm-up steps. The state
+ping-pongs between two buffers; F_out rotates over three.
+
+Also reported: the isolated sublayer (hc_coeffs_pre + hc_post) on three rotated
+input sets, and the kernels' durations from HIP events.
 
 Prints one JSON line: tokens/s of the whole job, achieved algorithmic HBM
 bandwidth, a roofline entry for the dominant kernel (duration from HIP events
@@ -52,12 +59,18 @@ def algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
     hc_coeffs_pre: read X (nC per token), read phi and bias once, write F_in (C)
     and the n + n*n post/res coefficients (h_pre is not requested).
     hc_post: read X (nC), F_out (C) and the n*n + n coefficients, write X_next
-    (nC): the (n+1)C reads and nC writes of the fused post/res kernel."""
+    (nC): the (n+1)C reads and nC writes of the fused post/res kernel.
+    hc_pre: read X (nC) and h_pre (n), write F_in (C).
+    hc_post_coeffs: hc_post plus phi and bias once, and the n*n + 2n
+    coefficients of X_next written."""
     ncols = n * n + 2 * n
     coef = (n + n * n) * 4
-    cp = T * (n * C * esize + C * esize + coef) + n * C * ncols * 4 + ncols * 4
+    par = n * C * ncols * 4 + ncols * 4
+    cp = T * (n * C * esize + C * esize + coef) + par
     post = T * (n * C * esize + C * esize + coef + n * C * esize)
-    return {"hc_coeffs_pre": cp, "hc_post": post}
+    pre = T * (n * C * esize + n * 4 + C * esize)
+    pc = post + T * ncols * 4 + par
+    return {"hc_coeffs_pre": cp, "hc_post": post, "hc_pre": pre, "hc_post_coeffs": pc}
 
 
 def load_traffic(kernel: str, digest: str):
@@ -127,54 +140,73 @@ def main() -> int:
         return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
     X0, F0 = up_bf16(inp["X"]), up_bf16(inp["F_out"])
-    sets = [(X0, F0)] + [(X0.clone(), F0.clone()) for _ in range(2)]
     phi = torch.from_numpy(inp["phi"]).to(dev)
     bias = torch.from_numpy(inp["bias"]).to(dev)
     alpha = [float(a) for a in inp["alpha"]]
-    h_post = torch.empty(T, n, device=dev)
-    h_res = torch.empty(T, n, n, device=dev)
-    F_in = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
-    X_next = torch.empty(T, n, C, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(hc.hc_coeffs_workspace_bytes(T, n, C, torch.bfloat16), dtype=torch.uint8, device=dev)
-    out_cp = (None, h_post, h_res, F_in)
+    F_in = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
+    ab = algorithmic_bytes(T, n, C)
 
-    def step(i, evs=None):
-        X, F = sets[i % len(sets)]
+    def timed(step_fn, names, steps, warmup):
+        for i in range(warmup):
+            step_fn(i, None)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step_fn(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e-3 for j, nm in enumerate(names)}
+        return wall, kern
+
+    # --- chained sublayer (headline)
+    Xs = [X0.clone(), torch.empty_like(X0)]
+    Fs = [F0] + [F0.clone() for _ in range(2)]
+    coef = [(torch.empty(T, n, device=dev), torch.empty(T, n, device=dev), torch.empty(T, n, n, device=dev))
+            for _ in range(2)]
+    hc.hc_coeffs(Xs[0], phi, bias, alpha, SINKHORN_ITERS, out=coef[0], workspace=ws)
+
+    def chain_step(i, evs):
+        cur, nxt = i % 2, (i + 1) % 2
+        h_pre, h_post, h_res = coef[cur]
         if evs is not None:
             evs[0].record()
-        hc.hc_coeffs_pre(X, phi, bias, alpha, SINKHORN_ITERS, out=out_cp, workspace=ws)
+        hc.hc_pre(Xs[cur], h_pre, out=F_in)
         if evs is not None:
             evs[1].record()
-        hc.hc_post(X, h_res, h_post, F, out=X_next)
+        hc.hc_post_coeffs(Xs[cur], h_res, h_post, Fs[i % 3], phi, bias, alpha, SINKHORN_ITERS, out=Xs[nxt],
+                          coeffs_out=coef[nxt], workspace=ws)
         if evs is not None:
             evs[2].record()
 
-    if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    wall, kern = timed(chain_step, ["hc_pre", "hc_post_coeffs"], args.steps, args.warmup)
+    step_bytes = ab["hc_pre"] + ab["hc_post_coeffs"]
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # --- isolated sublayer on rotated input sets
+    h_post_i = torch.empty(T, n, device=dev)
+    h_res_i = torch.empty(T, n, n, device=dev)
+    X_next = torch.empty(T, n, C, dtype=torch.bfloat16, device=dev)
+    iso_sets = [(X0, F0)] + [(X0.clone(), F0.clone()) for _ in range(2)]
 
-    d_cp = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    d_post = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    def iso_step(i, evs):
+        X, F = iso_sets[i % 3]
+        if evs is not None:
+            evs[0].record()
+        hc.hc_coeffs_pre(X, phi, bias, alpha, SINKHORN_ITERS, out=(None, h_post_i, h_res_i, F_in), workspace=ws)
+        if evs is not None:
+            evs[1].record()
+        hc.hc_post(X, h_res_i, h_post_i, F, out=X_next)
+        if evs is not None:
+            evs[2].record()
+
+    iso_wall, iso_kern = timed(iso_step, ["hc_coeffs_pre", "hc_post"], args.steps, args.warmup)
+    iso_bytes = ab["hc_coeffs_pre"] + ab["hc_post"]
+
     ms_per_step = wall / args.steps * 1e3
     tokens_per_s = T * args.steps / wall
-    ab = algorithmic_bytes(T, n, C)
-    total_bytes = ab["hc_coeffs_pre"] + ab["hc_post"]
-    achieved = total_bytes / (wall / args.steps) / 1e9
-    kern = {"hc_coeffs_pre": float(d_cp.mean()), "hc_post": float(d_post.mean())}
+    achieved = step_bytes / (wall / args.steps) / 1e9
     dom = max(kern, key=kern.get)
     dom_gbps = ab[dom] / kern[dom] / 1e9
     digest = source_digest()
@@ -192,17 +224,25 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "mHC sublayer n=4 C=4096 T=8192 (batch 4 x seq 2048), bf16 streams, "
-                               "fp32 coefficients, 20 Sinkhorn iterations, forward",
+        "config": {"workload": "mHC sublayer n=4 C=4096 T=8192 (batch 4 x seq 2048), bf16 streams, fp32 "
+                               "coefficients, 20 Sinkhorn iterations, forward; steady state of a chain: pre-read + "
+                               "post/res write fused with the next sublayer's coefficients",
                    "n": n, "C": C, "T": T, "sinkhorn_iters": SINKHORN_ITERS, "parallelism": "single GPU"},
         "achieved_GBps": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
-        "algorithmic_bytes_per_step": total_bytes,
+        "algorithmic_bytes_per_step": step_bytes,
         "kernels_us": {k: v * 1e6 for k, v in kern.items()},
         "kernels_GBps": {k: ab[k] / kern[k] / 1e9 for k in kern},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom]},
+        "isolated_sublayer": {
+            "tokens_per_s": T * args.steps / iso_wall,
+            "ms_per_step": iso_wall / args.steps * 1e3,
+            "achieved_GBps": iso_bytes / (iso_wall / args.steps) / 1e9,
+            "pct_hbm_peak": 100.0 * iso_bytes / (iso_wall / args.steps) / 1e9 / HBM_PEAK_GBPS,
+            "kernels_us": {k: v * 1e6 for k, v in iso_kern.items()},
+            "algorithmic_bytes_per_step": iso_bytes},
         "source_digest": digest,
     }
     if not args.no_cpu_baseline:

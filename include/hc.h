@@ -132,6 +132,25 @@ int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C,
             const float* h_res, const float* h_post, const void* F_out, void* X_next,
             void* stream);
 
+/*
+ * hc_post_coeffs - hc_post followed by hc_coeffs on the state it writes, in one
+ * pass: the post/res write of sublayer l ([mHC] Eq. 3, 4.3.1) and the
+ * coefficients of sublayer l+1 ([mHC] Eq. 7-9, 14-19) computed from X_next
+ * while it is produced (so a chain of sublayers reads each state twice: once
+ * in the pre-read, once here).
+ *   X, h_res, h_post, F_out, X_next: as hc_post (X_next may equal X).
+ *   phi_next, bias_next, alpha_*, sinkhorn_iters: sublayer l+1's parameters,
+ *   as hc_coeffs. Outputs h_pre_next, h_post_next [T, n], h_res_next [T, n, n]
+ *   (float32; all required) are the coefficients of X_next.
+ *   Workspace: hc_coeffs_workspace_bytes(T, n, C, dtype).
+ */
+int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C,
+                   const float* h_res, const float* h_post, const void* F_out, void* X_next,
+                   const float* phi_next, const float* bias_next,
+                   float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters,
+                   float* h_pre_next, float* h_post_next, float* h_res_next,
+                   void* workspace, int64_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ xHC -- */
 
 /* Workspace bytes needed by xhc_pre (with_router != 0 when w_router is given). */

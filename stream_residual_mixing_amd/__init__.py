@@ -34,6 +34,8 @@ _SIGS = {
     "hc_coeffs_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float,
                                _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "hc_post_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _c_float,
+                                _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "xhc_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _c_float, _vp,
                          _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
@@ -177,6 +179,27 @@ def hc_post(X, h_res, h_post, F_out, *, out=None, stream=None):
     return X_next
 
 
+def hc_post_coeffs(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sinkhorn_iters=20, *, out=None,
+                   coeffs_out=None, workspace=None, stream=None):
+    """X_next = h_res @ X + h_post^T F_out, plus the coefficients of X_next under the next
+    sublayer's phi/bias/alpha. Returns (X_next, (h_pre', h_post', h_res'))."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
+    X_next = torch.empty_like(X) if out is None else out
+    if coeffs_out is None:
+        coeffs_out = (torch.empty(T, n, device=X.device), torch.empty(T, n, device=X.device),
+                      torch.empty(T, n, n, device=X.device))
+    hp, hq, hr = coeffs_out
+    ws = _workspace(hc_coeffs_workspace_bytes(T, n, C, X.dtype), X.device, workspace)
+    a = [float(v) for v in alpha_next]
+    _check("hc_post_coeffs", lib().hc_post_coeffs(
+        _ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(h_res, "h_res")), _ptr(_f32(h_post, "h_post")), _ptr(F_out),
+        _ptr(X_next), _ptr(_f32(phi_next, "phi_next")), _ptr(_f32(bias_next, "bias_next")), a[0], a[1], a[2],
+        int(sinkhorn_iters), _ptr(hp), _ptr(hq), _ptr(hr), _ptr(ws), ws.numel(), _stream(X.device, stream)))
+    return X_next, coeffs_out
+
+
 # ------------------------------------------------------------------- xHC
 
 
@@ -258,6 +281,6 @@ def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, stream=None)
 
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
-    "hc_coeffs_pre", "hc_post", "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
+    "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment",
 ]

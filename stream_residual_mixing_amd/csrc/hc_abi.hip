@@ -164,7 +164,7 @@ int hc_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float
   if (hc::fast_coeffs_supported(dtype, n, C, X)) {
     return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
                                                     alpha_res, sinkhorn_iters, h_pre, h_post,
-                                                    h_res, nullptr, w.packed, st));
+                                                    h_res, nullptr, w.packed, w.h_pre, st));
   }
   return run_coeffs_generic(X, dtype, T, n, C, phi, bias, alpha_pre, alpha_post, alpha_res,
                             sinkhorn_iters, h_pre, h_post, h_res, w, st);
@@ -179,6 +179,8 @@ int hc_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h
   const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
   if (overlaps(F_in, fb, X, xb) || overlaps(F_in, fb, h_pre, T * n * 4)) return HC_ERR_ALIAS;
   if ((s = device_status()) != HC_OK) return s;
+  if (dtype == HC_BF16 && n == 4 && vec_ok(C, {X, F_in}))
+    return launch_status(hc::launch_fast_pre(X, T, C, h_pre, F_in, (hipStream_t)stream));
   return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X, F_in}), X, T, n, C, h_pre, F_in,
                                               (hipStream_t)stream));
 }
@@ -208,7 +210,7 @@ int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const f
   if (hc::fast_coeffs_supported(dtype, n, C, X) && aligned_to(F_in, 16)) {
     return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
                                                     alpha_res, sinkhorn_iters, h_pre, h_post,
-                                                    h_res, F_in, w.packed, st));
+                                                    h_res, F_in, w.packed, w.h_pre, st));
   }
   // Generic: the pre-read needs h_pre, kept in the workspace when the caller
   // does not ask for it.
@@ -234,10 +236,52 @@ int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* 
     return HC_ERR_ALIAS;
   if ((s = device_status()) != HC_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (hc::fast_post_supported(dtype, n, C, X, F_out, X_next))
-    return launch_status(hc::launch_fast_post(X, T, C, h_res, h_post, F_out, X_next, st));
   return launch_status(hc::launch_post_generic(dtype, vec_ok(C, {X, F_out, X_next}), X, T, n, C,
                                                h_res, h_post, F_out, X_next, st));
+}
+
+int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                   const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                   const float* bias_next, float alpha_pre, float alpha_post, float alpha_res,
+                   int sinkhorn_iters, float* h_pre_next, float* h_post_next, float* h_res_next,
+                   void* workspace, int64_t workspace_bytes, void* stream) {
+  // validate as hc_post, then as hc_coeffs on X_next
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK) return s;
+  if (sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS) return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!h_res || !h_post || !F_out || !X_next) return HC_ERR_NULL;
+  if (!aligned_to(h_res, 4) || !aligned_to(h_post, 4) || !aligned_to(F_out, esize(dtype)) ||
+      !aligned_to(X_next, esize(dtype)))
+    return HC_ERR_ALIGN;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+  if (X_next != X && overlaps(X_next, xb, X, xb)) return HC_ERR_ALIAS;
+  if (overlaps(X_next, xb, F_out, fb) || overlaps(X_next, xb, h_res, T * n * n * 4) ||
+      overlaps(X_next, xb, h_post, T * n * 4))
+    return HC_ERR_ALIAS;
+  s = check_coeff_args(X_next, dtype, T, n, C, phi_next, bias_next, sinkhorn_iters, h_pre_next,
+                       h_post_next, h_res_next, false, workspace, workspace_bytes);
+  if (s != HC_OK) return s;
+  // the new coefficients must not overlap the coefficients being read
+  const void* outs[3] = {h_pre_next, h_post_next, h_res_next};
+  const int64_t ob[3] = {T * n * 4, T * n * 4, T * n * n * 4};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(outs[i], ob[i], h_res, T * n * n * 4) || overlaps(outs[i], ob[i], h_post, T * n * 4) ||
+        overlaps(outs[i], ob[i], F_out, fb) || overlaps(outs[i], ob[i], X, xb))
+      return HC_ERR_ALIAS;
+  if ((s = device_status()) != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const CoeffWs w = carve_mhc(workspace, T, n);
+  if (hc::fast_post_supported(dtype, n, C, X, F_out, X_next) && hc::fast_coeffs_supported(dtype, n, C, X_next))
+    return launch_status(hc::launch_fast_post_coeffs(X, T, C, h_res, h_post, F_out, X_next, phi_next,
+                                                     bias_next, alpha_pre, alpha_post, alpha_res,
+                                                     sinkhorn_iters, h_pre_next, h_post_next, h_res_next,
+                                                     w.packed, st));
+  hipError_t e = hc::launch_post_generic(dtype, vec_ok(C, {X, F_out, X_next}), X, T, n, C, h_res, h_post,
+                                         F_out, X_next, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  return run_coeffs_generic(X_next, dtype, T, n, C, phi_next, bias_next, alpha_pre, alpha_post, alpha_res,
+                            sinkhorn_iters, h_pre_next, h_post_next, h_res_next, w, st);
 }
 
 // ------------------------------------------------------------------ xHC --

@@ -220,3 +220,61 @@ def test_workload2_shape_chain_end_to_end():
         Xo = synth.round_to_bf16(chain["X_next"].astype(np.float32))[0].astype(np.float64)
         X = Xn
     assert rel_l2(host64(X), Xo) < 1e-2
+
+
+# ------------------------------------------------ post fused with next coefficients
+
+def _post_coeffs_case(T, C, seed, in_place=False):
+    inp = synth.mhc_layer(seed, 0, T, 4, C, synth.BF16)
+    nxt = synth.mhc_layer(seed, 1, T, 4, C, synth.BF16, draw_x=False)
+    X = dev(inp["X"])
+    h_pre, h_post, h_res = hc.hc_coeffs(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    ref = _oracle(inp)
+    out = X if in_place else None
+    Xn, (hp2, hq2, hr2) = hc.hc_post_coeffs(X, h_res, h_post, dev(inp["F_out"]), dev(nxt["phi"]), dev(nxt["bias"]),
+                                            [0.01] * 3, out=out)
+    torch.cuda.synchronize()
+    check_bf16("X_next", host64(Xn), ref["X_next"], literal_max_abs=True)
+    # coefficients of the state actually written (the GPU's bf16 X_next)
+    r2 = O.hc_coeffs(host64(Xn), nxt["phi"], nxt["bias"], nxt["alpha"])
+    for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (hp2, hq2, hr2), r2):
+        check_fp32(name, host64(g), r)
+
+
+@pytest.mark.parametrize("T", [1, 16, 133])
+def test_post_coeffs_matches_post_then_coeffs(T):
+    note(f"mHC hc_post_coeffs n=4 C=4096 bf16 T={T}")
+    _post_coeffs_case(T, 4096, 20 + T)
+
+
+def test_post_coeffs_in_place_and_small_C():
+    note("mHC hc_post_coeffs in place, C=64 and C=7168")
+    _post_coeffs_case(37, 64, 31, in_place=True)
+    _post_coeffs_case(19, 7168, 32)
+    note("mHC hc_post_coeffs generic shapes (C=40 bf16)")
+    _post_coeffs_case(11, 40, 33)
+
+
+def test_chain_with_post_coeffs_workload2_shape():
+    """The chained path (pre-read + post fused with the next coefficients) over 8
+    layers at C=7168: each layer against the oracle on the GPU's own input state."""
+    T, n, C = 45, 4, 7168
+    layers = [synth.mhc_layer(2, 0, T, n, C, synth.BF16)] + [
+        synth.mhc_layer(2, l, T, n, C, synth.BF16, draw_x=False) for l in range(1, 9)]
+    X = dev(layers[0]["X"])
+    h_pre, h_post, h_res = hc.hc_coeffs(X, dev(layers[0]["phi"]), dev(layers[0]["bias"]), [0.01] * 3)
+    for l in range(8):
+        note(f"mHC chained path C=7168 T=45 layer {l}")
+        inp = layers[l]
+        F_in = hc.hc_pre(X, h_pre)
+        Xn, (h_pre, h_post_n, h_res_n) = hc.hc_post_coeffs(X, h_res, h_post, dev(inp["F_out"]),
+                                                         dev(layers[l + 1]["phi"]), dev(layers[l + 1]["bias"]),
+                                                         [0.01] * 3)
+        torch.cuda.synchronize()
+        ref = O.mhc_sublayer(host64(X), inp["phi"], inp["bias"], inp["alpha"], inp["F_out"].values)
+        check_bf16("F_in", host64(F_in), ref["F_in"])
+        check_bf16("X_next", host64(Xn), ref["X_next"])
+        r2 = O.hc_coeffs(host64(Xn), layers[l + 1]["phi"], layers[l + 1]["bias"], layers[l + 1]["alpha"])
+        for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (h_pre, h_post_n, h_res_n), r2):
+            check_fp32(name, host64(g), r)
+        X, h_post, h_res = Xn, h_post_n, h_res_n
