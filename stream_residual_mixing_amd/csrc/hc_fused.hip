@@ -34,27 +34,27 @@ constexpr int TOK = 16;             // tokens per tile (MFMA M)
 
 __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__ phi, int64_t K,
                                                        uint16_t* __restrict__ packed) {
-  // one thread per (row group of 8, packed column)
+  // one thread per (row group of 8, column): writes the hi chunk (column c) and
+  // the lo chunk (column NCOL + c), 8 bf16 each
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t ngroups = K / 8;
-  if (g >= ngroups * NCP) return;
-  const int64_t rg = g / NCP;
-  const int col = (int)(g - rg * NCP);
-  const bool lo = col >= NCOL;
-  const int src = lo ? col - NCOL : col;
-  uint32_t w[4];
+  if (g >= ngroups * NCOL) return;
+  const int64_t rg = g / NCOL;
+  const int c = (int)(g - rg * NCOL);
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = phi[(rg * 8 + e) * NCOL + c];
+  uint32_t hi[4], lo[4];
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
-    float v[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float p = phi[(rg * 8 + e + u) * NCOL + src];
-      const float hi = bf2f(f2bf(p));
-      v[u] = lo ? (p - hi) : hi;  // p - hi is exact in float32
-    }
-    w[e / 2] = f2bf(v[0]) | (f2bf(v[1]) << 16);
+    const uint32_t h0 = f2bf(p[e]), h1 = f2bf(p[e + 1]);
+    hi[e / 2] = h0 | (h1 << 16);
+    // p - hi is exact in float32
+    lo[e / 2] = f2bf(p[e] - bf2f(h0)) | (f2bf(p[e + 1] - bf2f(h1)) << 16);
   }
-  reinterpret_cast<uint4*>(packed)[g] = make_uint4(w[0], w[1], w[2], w[3]);
+  uint4* out = reinterpret_cast<uint4*>(packed) + rg * NCP;
+  out[c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  out[NCOL + c] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
 // ---------------------------------------------------------- stream kernel
@@ -141,12 +141,13 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
     }
     __syncthreads();
   }
-  floatx4_t acc[2][3];
+  floatx4_t acc[2][3], gram[2];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
+  for (int tb = 0; tb < 2; ++tb) {
+    gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < 3; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float ss[2] = {0.f, 0.f};
+  }
 
   // Loads are unconditional: rows past T and channels past C are clamped to a
   // valid address and their values replaced by zeros, so no load sits behind a
@@ -215,13 +216,7 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
     }
     if (PROJ) {
 #pragma unroll
-      for (int i = 0; i < NS4; ++i) {
-        float v[8];
-        unpack8(a_frag[i], v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss[p] += v[e] * v[e];
-        *reinterpret_cast<uint4*>(buf + (i * TILE + m) * LROW + st_c8 * 2) = a_frag[i];
-      }
+      for (int i = 0; i < NS4; ++i) *reinterpret_cast<uint4*>(buf + (i * TILE + m) * LROW + st_c8 * 2) = a_frag[i];
     }
   };
 
@@ -264,6 +259,8 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
 #pragma unroll
           for (int b = 0; b < 3; ++b)
             acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pf[i][b]), acc[tb][b], 0, 0, 0);
+          // A times its own transpose: the diagonal accumulates each token's sum of squares.
+          gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
         }
       }
       // The next super-chunk writes the other buffer; the one after it writes this
@@ -282,8 +279,8 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
   __syncthreads();
   float* red = reinterpret_cast<float*>(lds);              // [SWAVE][TILE][NCP + 1]
   float* Pt = red + SWAVE * TILE * (NCP + 1);              // [TILE][NCOL]
-  float* ssr = Pt + TILE * NCOL;                           // [TILE][32]
-  float* sst = ssr + TILE * 32;                            // [TILE]
+  float* ssr = Pt + TILE * NCOL;                           // [SWAVE][TILE]
+  float* sst = ssr + SWAVE * TILE;                         // [TILE]
   // lane holds D[m = q*4 + e][n = tau] of each block b, for token block tb
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
@@ -292,8 +289,13 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         red[(wave * TILE + tb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
+  // gram[tb]: lane holds G[m = q*4 + e][n = tau]; the diagonal m == n sits in the
+  // lane with tau == q*4 + e.
 #pragma unroll
-  for (int p = 0; p < 2; ++p) ssr[(st_tok + 16 * p) * 32 + (tid & 31)] = ss[p];
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (tau == q * 4 + e) ssr[wave * TILE + tb * TOK + tau] = gram[tb][e];
   __syncthreads();
   for (int k = tid; k < TILE * NCOL; k += STHR) {
     const int m = k / NCOL, col = k - m * NCOL;
@@ -305,7 +307,8 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
   }
   if (tid < TILE) {
     float sum = 0.f;
-    for (int u = 0; u < 32; ++u) sum += ssr[tid * 32 + u];
+#pragma unroll
+    for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TILE + tid];
     sst[tid] = sum;
   }
   __syncthreads();
@@ -391,7 +394,7 @@ bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void*
 }
 
 static hipError_t launch_pack(const float* phi, int64_t K, void* packed, hipStream_t st) {
-  const int64_t work = K / 8 * NCP;
+  const int64_t work = K / 8 * NCOL;
   hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, phi, K,
                      (uint16_t*)packed);
   return hipGetLastError();
