@@ -28,7 +28,5 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
                                    hipStream_t st);
 
 bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y);
-hipError_t launch_fast_post(const void* X, int64_t T, int64_t C, const float* h_res,
-                            const float* h_post, const void* F, void* Y, hipStream_t st);
 
 }  // namespace hc

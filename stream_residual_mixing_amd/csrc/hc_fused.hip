@@ -104,6 +104,95 @@ __device__ __forceinline__ uint32_t pack_bf2_hw(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// v if keep, else zeros: per-component selects (a select between two uint4
+// objects can become a select of their addresses, which puts them in scratch).
+__device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
+  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+
+// Cross-wave reduction of a 32-token tile and the coefficient epilogue
+// ([mHC] Eq. 15-19). acc[tb][b] holds this wave's partial D = A * B for token
+// block tb and packed column block b (lane: D[m = q*4 + e][n = tau]); gram[tb]
+// holds its partial A * A^T, whose diagonal is the sum of squares. `red` is LDS
+// scratch of at least SWAVE * TILE * (NCP + 1) + TILE * (NCOL + SWAVE + 1)
+// floats; the caller has synchronised the workgroup before the call.
+__device__ __forceinline__ void tile_epilogue(float* red, const floatx4_t (&acc)[2][3], const floatx4_t (&gram)[2],
+                                              int64_t t0, int64_t T, int64_t C, const float* __restrict__ bias,
+                                              Gate gate, int iters, float* __restrict__ h_pre_out,
+                                              float* __restrict__ h_post_out, float* __restrict__ h_res_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tau = lane & 15, q = lane >> 4;
+  float* Pt = red + SWAVE * TILE * (NCP + 1);   // [TILE][NCOL]
+  float* ssr = Pt + TILE * NCOL;                // [SWAVE][TILE]
+  float* sst = ssr + SWAVE * TILE;              // [TILE]
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red[(wave * TILE + tb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
+  // the diagonal m == n of gram[tb] sits in the lane with tau == q*4 + e
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (tau == q * 4 + e) ssr[wave * TILE + tb * TOK + tau] = gram[tb][e];
+  __syncthreads();
+  for (int k = tid; k < TILE * NCOL; k += STHR) {
+    const int m = k / NCOL, col = k - m * NCOL;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < SWAVE; ++w)
+      sum += red[(w * TILE + m) * (NCP + 1) + col] + red[(w * TILE + m) * (NCP + 1) + NCOL + col];
+    Pt[m * NCOL + col] = sum;
+  }
+  if (tid < TILE) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TILE + tid];
+    sst[tid] = sum;
+  }
+  __syncthreads();
+  // thread (token m, entry e) for 32 tokens x 16 entries
+  const int m = tid >> 4, e = tid & 15;
+  const int64_t tt = t0 + m;
+  const float r = sqrtf(sst[m] / (float)(NS4 * C));
+  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  if (e < 8 && tt < T) {
+    const float a = e < 4 ? gate.a_pre : gate.a_post;
+    const float z = a * (Pt[m * NCOL + e] * invr) + bias[e];
+    if (e < 4) {
+      if (h_pre_out) h_pre_out[tt * 4 + e] = sigmoid(z);
+    } else {
+      h_post_out[tt * 4 + (e - 4)] = 2.0f * sigmoid(z);
+    }
+  }
+  // h_res: Sinkhorn on the 4x4 block held by 16 consecutive lanes (i = e>>2, j = e&3)
+  const float z = gate.a_res * (Pt[m * NCOL + 8 + e] * invr) + bias[8 + e];
+  float zm = z;
+  zm = fmaxf(zm, __shfl_xor(zm, 1, 64));
+  zm = fmaxf(zm, __shfl_xor(zm, 2, 64));
+  zm = fmaxf(zm, __shfl_xor(zm, 4, 64));
+  zm = fmaxf(zm, __shfl_xor(zm, 8, 64));
+  float M = expf(z - zm);
+  for (int it = 0; it < iters; ++it) {
+    float cs = M + __shfl_xor(M, 4, 64);  // column sum over i
+    cs += __shfl_xor(cs, 8, 64);
+    M = M / cs;
+    float rs = M + __shfl_xor(M, 1, 64);  // row sum over j
+    rs += __shfl_xor(rs, 2, 64);
+    M = M / rs;
+  }
+  if (tt < T) h_res_out[tt * 16 + e] = M;
+}
+
+// Buffer resource over [base, base + bytes): stores whose offset falls outside are
+// dropped by the hardware, so a guarded store needs no branch (a store behind a
+// branch makes the compiler's wait counts conservative at the merge).
+constexpr unsigned BUF_DW3 = 0x00020000u;
+constexpr uint32_t OOB = 0x80000000u;  // any offset >= the range is dropped
+
 template <bool POST, bool PROJ>
 __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
     const uint16_t* X, int64_t T, int64_t C,
@@ -131,6 +220,7 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
   const int q = lane >> 4;
   const int64_t nsc = (C + SC - 1) / SC;
 
+
   // per-token post coefficients of the tile, in LDS: [TILE][20] = h_res (16) | h_post (4)
   __shared__ float coef[POST ? TILE * 20 : 1];
   if (POST) {
@@ -152,6 +242,10 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
   // Loads are unconditional: rows past T and channels past C are clamped to a
   // valid address and their values replaced by zeros, so no load sits behind a
   // branch and consecutive loads stay in flight together.
+  // X_next of this tile through a buffer resource (rows t0 .. min(T, t0 + TILE))
+  const int64_t nrow = (T - t0) < TILE ? (T - t0) : TILE;
+  const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
+      POST ? Y + t0 * (NS4 * C) : nullptr, 0, POST ? (uint32_t)(nrow * NS4 * C * 2) : 0u, BUF_DW3);
   const uint16_t* xrow[2];
   const uint16_t* frow[2];
 #pragma unroll
@@ -204,15 +298,13 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
         o.y = pack_bf2_hw(y[2], y[3]);
         o.z = pack_bf2_hw(y[4], y[5]);
         o.w = pack_bf2_hw(y[6], y[7]);
-        if (!ok) o = make_uint4(0, 0, 0, 0);
-        a_frag[i] = o;
-        if (ok)
-          __builtin_nontemporal_store(u32x4_t{o.x, o.y, o.z, o.w},
-                                      reinterpret_cast<u32x4_t*>(Y + st_t[p] * (NS4 * C) + i * C + c));
+        a_frag[i] = o;  // positions past T or C are zeroed in the MFMA phase
+        const uint32_t yoff = ok ? (uint32_t)((((int64_t)m * NS4 + i) * C + c) * 2) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{o.x, o.y, o.z, o.w}, yres, yoff, 0, 2 /* nt */);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NS4; ++i) a_frag[i] = ok ? xc[i] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NS4; ++i) a_frag[i] = keep_or_zero(ok, xc[i]);
     }
     if (PROJ) {
 #pragma unroll
@@ -248,14 +340,20 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
     stream_half(s, H1{}, xB, fB, buf);
     if (PROJ) {
       __syncthreads();
-      // A wave whose group lies past C reads an all-zero A tile (a_frag was zeroed)
-      // against a clamped, valid B address: it adds nothing, with no branch.
+      // With POST, rows past T and channels past C hold values computed from
+      // clamped loads (zeroing them before the store would turn the store into
+      // a branch): their A fragments are replaced by zeros here. Without POST
+      // the tile already holds zeros there. Either way a group past C adds
+      // nothing against its clamped, valid B address.
+      const bool ch_ok = cg + q * 8 < C;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
+        const bool a_ok = ch_ok && (t0 + tb * TOK + tau < T);
 #pragma unroll
         for (int i = 0; i < NS4; ++i) {
-          const uint4 af =
+          uint4 af =
               *reinterpret_cast<const uint4*>(buf + (i * TILE + tb * TOK + tau) * LROW + (wave * 32 + q * 8) * 2);
+          if (POST) af = keep_or_zero(a_ok, af);
 #pragma unroll
           for (int b = 0; b < 3; ++b)
             acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pf[i][b]), acc[tb][b], 0, 0, 0);
@@ -275,77 +373,9 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
   body(nsc - 1, std::false_type{});
   if (!PROJ) return;
 
-  // ---- cross-wave reduction of the projection and of the squared norms
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);              // [SWAVE][TILE][NCP + 1]
-  float* Pt = red + SWAVE * TILE * (NCP + 1);              // [TILE][NCOL]
-  float* ssr = Pt + TILE * NCOL;                           // [SWAVE][TILE]
-  float* sst = ssr + SWAVE * TILE;                         // [TILE]
-  // lane holds D[m = q*4 + e][n = tau] of each block b, for token block tb
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[(wave * TILE + tb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
-  // gram[tb]: lane holds G[m = q*4 + e][n = tau]; the diagonal m == n sits in the
-  // lane with tau == q*4 + e.
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (tau == q * 4 + e) ssr[wave * TILE + tb * TOK + tau] = gram[tb][e];
-  __syncthreads();
-  for (int k = tid; k < TILE * NCOL; k += STHR) {
-    const int m = k / NCOL, col = k - m * NCOL;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < SWAVE; ++w)
-      sum += red[(w * TILE + m) * (NCP + 1) + col] + red[(w * TILE + m) * (NCP + 1) + NCOL + col];
-    Pt[m * NCOL + col] = sum;
-  }
-  if (tid < TILE) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TILE + tid];
-    sst[tid] = sum;
-  }
-  __syncthreads();
-
-  // ---- epilogue: thread (token m, entry e) for 32 tokens x 16 entries
-  {
-    const int m = tid >> 4, e = tid & 15;
-    const int64_t tt = t0 + m;
-    const float r = sqrtf(sst[m] / (float)(NS4 * C));
-    const float invr = (r > 0.f) ? 1.0f / r : 0.f;
-    if (e < 8 && tt < T) {
-      const float a = e < 4 ? gate.a_pre : gate.a_post;
-      const float z = a * (Pt[m * NCOL + e] * invr) + bias[e];
-      if (e < 4) {
-        if (h_pre_out) h_pre_out[tt * 4 + e] = sigmoid(z);
-      } else {
-        h_post_out[tt * 4 + (e - 4)] = 2.0f * sigmoid(z);
-      }
-    }
-    // h_res: Sinkhorn on the 4x4 block held by 16 consecutive lanes (i = e>>2, j = e&3)
-    const float z = gate.a_res * (Pt[m * NCOL + 8 + e] * invr) + bias[8 + e];
-    float zm = z;
-    zm = fmaxf(zm, __shfl_xor(zm, 1, 64));
-    zm = fmaxf(zm, __shfl_xor(zm, 2, 64));
-    zm = fmaxf(zm, __shfl_xor(zm, 4, 64));
-    zm = fmaxf(zm, __shfl_xor(zm, 8, 64));
-    float M = expf(z - zm);
-    for (int it = 0; it < iters; ++it) {
-      float cs = M + __shfl_xor(M, 4, 64);  // column sum over i
-      cs += __shfl_xor(cs, 8, 64);
-      M = M / cs;
-      float rs = M + __shfl_xor(M, 1, 64);  // row sum over j
-      rs += __shfl_xor(rs, 2, 64);
-      M = M / rs;
-    }
-    if (tt < T) h_res_out[tt * 16 + e] = M;
-  }
+  tile_epilogue(reinterpret_cast<float*>(lds), acc, gram, t0, T, C, bias, gate, iters, h_pre_out, h_post_out,
+                h_res_out);
 }
 
 // --------------------------------------------------------------- pre-read
@@ -423,15 +453,6 @@ hipError_t launch_fast_pre(const void* X, int64_t T, int64_t C, const float* h_p
   const int64_t work = T * (C / 8);
   hipLaunchKernelGGL(pre4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, (const uint16_t*)X, T,
                      C, h_pre, (uint16_t*)F_in);
-  return hipGetLastError();
-}
-
-hipError_t launch_fast_post(const void* X, int64_t T, int64_t C, const float* h_res,
-                            const float* h_post, const void* F, void* Y, hipStream_t st) {
-  const unsigned grid = (unsigned)((T + TILE - 1) / TILE);
-  hipLaunchKernelGGL((mhc_stream_kernel<true, false>), dim3(grid), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
-                     h_res, h_post, (const uint16_t*)F, (uint16_t*)Y, nullptr, nullptr, Gate{0.f, 0.f, 0.f}, 0,
-                     nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
