@@ -7,18 +7,20 @@ One step is one forward hyper-connection sublayer over T = 8192 tokens
 RMS factor, skinny projection nC -> 24, gates, sigmoid / 2*sigmoid, 20
 Sinkhorn iterations, pre-read F_in and post/res write X_next.
 
-Headline (steady state of a chain of sublayers): hc_pre (pre-read with the
-coefficients computed for this sublayer) + hc_post_coeffs (post/res write fused
-with the coefficients of the state it writes, for the next sublayer). Every step
-computes one sublayer's coefficients, pre-read and post write; the coefficients
-used by the first timed step come from the untimed warm-up steps. The state
+Headline (steady state of a chain of sublayers): one hc_post_pre call per step,
+the work between two sublayer functions: the post/res write of sublayer l, the
+coefficients of the state it writes under sublayer l+1's parameters, and sublayer
+l+1's pre-read. Every step thus computes one sublayer's coefficients, pre-read and
+post write. phi is a weight: it is packed once (hc_phi_pack) before timing; the
+same chain with phi packed inside every step is reported too. The state
 ping-pongs between two buffers; F_out rotates over three.
 
-Also reported: the isolated sublayer (hc_coeffs_pre + hc_post) on three rotated
-input sets, and the kernels' durations from HIP events.
+Also reported: the chain as two calls per step (hc_pre + hc_post_coeffs) with
+each call's duration, and the isolated sublayer (hc_coeffs_pre + hc_post) on
+three rotated input sets.
 
 Prints one JSON line: tokens/s of the whole job, achieved algorithmic HBM
-bandwidth, a roofline entry for the dominant kernel (duration from HIP events
+bandwidth, a roofline entry for the dominant call (duration from HIP events
 recorded around its launches inside the timed region) and the fp64 CPU oracle
 timed on the host cores over a bounded sample of the same workload.
 """
@@ -62,7 +64,10 @@ def algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
     (nC): the (n+1)C reads and nC writes of the fused post/res kernel.
     hc_pre: read X (nC) and h_pre (n), write F_in (C).
     hc_post_coeffs: hc_post plus phi and bias once, and the n*n + 2n
-    coefficients of X_next written."""
+    coefficients of X_next written.
+    hc_post_pre: hc_post plus phi and bias once, the n*n + n post/res
+    coefficients of X_next written, and the pre-read of X_next (read nC, write
+    C); h_pre of X_next is used on chip and not stored."""
     ncols = n * n + 2 * n
     coef = (n + n * n) * 4
     par = n * C * ncols * 4 + ncols * 4
@@ -70,7 +75,9 @@ def algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
     post = T * (n * C * esize + C * esize + coef + n * C * esize)
     pre = T * (n * C * esize + n * 4 + C * esize)
     pc = post + T * ncols * 4 + par
-    return {"hc_coeffs_pre": cp, "hc_post": post, "hc_pre": pre, "hc_post_coeffs": pc}
+    # hc_post_pre: hc_post_coeffs without storing h_pre, plus the pre-read of X_next
+    pp = post + T * (n + n * n) * 4 + par + T * (n * C * esize + C * esize)
+    return {"hc_coeffs_pre": cp, "hc_post": post, "hc_pre": pre, "hc_post_coeffs": pc, "hc_post_pre": pp}
 
 
 def load_traffic(kernel: str, digest: str):
@@ -118,8 +125,6 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -148,9 +153,9 @@ def main() -> int:
     ab = algorithmic_bytes(T, n, C)
 
     def timed(step_fn, names, steps, warmup):
-        """Warm up, then time `steps` steps twice: once bare (the headline: events
-        only at both ends, so no marker sits between kernels), once with HIP events
-        around every kernel on the launch stream (per-kernel durations)."""
+        """Warm up, then time `steps` steps twice: once bare (events only at both
+        ends, so no marker sits between kernels), once with HIP events around every
+        call on the launch stream (per-call durations)."""
         for i in range(warmup):
             step_fn(i, None)
         torch.cuda.synchronize()
@@ -171,28 +176,53 @@ def main() -> int:
         kern = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e-3 for j, nm in enumerate(names)}
         return wall, gpu, kern
 
-    # --- chained sublayer (headline)
-    Xs = [X0.clone(), torch.empty_like(X0)]
     Fs = [F0] + [F0.clone() for _ in range(2)]
-    coef = [(torch.empty(T, n, device=dev), torch.empty(T, n, device=dev), torch.empty(T, n, n, device=dev))
-            for _ in range(2)]
-    hc.hc_coeffs(Xs[0], phi, bias, alpha, SINKHORN_ITERS, out=coef[0], workspace=ws)
+    phi_packed = hc.hc_phi_pack(phi, n, C, torch.bfloat16)
 
-    def chain_step(i, evs):
+    # --- chained sublayer, one call per step (headline)
+    Xs = [X0.clone(), torch.empty_like(X0)]
+    coef = [(None, torch.empty(T, n, device=dev), torch.empty(T, n, n, device=dev)) for _ in range(2)]
+    F_ins = [torch.empty(T, C, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+
+    def make_chain_step(packed):
+        def step(i, evs):
+            cur, nxt = i % 2, (i + 1) % 2
+            _, h_post, h_res = coef[cur]
+            if evs is not None:
+                evs[0].record()
+            hc.hc_post_pre(Xs[cur], h_res, h_post, Fs[i % 3], phi, bias, alpha, SINKHORN_ITERS,
+                           phi_next_packed=packed, out=Xs[nxt], coeffs_out=coef[nxt], F_in_out=F_ins[nxt],
+                           workspace=ws)
+            if evs is not None:
+                evs[1].record()
+        return step
+
+    def chain_start():
+        _, h_post, h_res, _ = hc.hc_coeffs_pre(Xs[0], phi, bias, alpha, SINKHORN_ITERS,
+                                               out=(None, coef[0][1], coef[0][2], F_ins[0]), workspace=ws)
+
+    chain_start()
+    wall_pk, gpu_pk, kern_pk = timed(make_chain_step(None), ["hc_post_pre"], args.steps, args.warmup)
+
+    # --- the same chain as two calls per step: pre-read, then post fused with the next coefficients
+    coef2 = [(torch.empty(T, n, device=dev), torch.empty(T, n, device=dev), torch.empty(T, n, n, device=dev))
+             for _ in range(2)]
+    hc.hc_coeffs(Xs[0], phi, bias, alpha, SINKHORN_ITERS, out=coef2[0], workspace=ws)
+
+    def two_call_step(i, evs):
         cur, nxt = i % 2, (i + 1) % 2
-        h_pre, h_post, h_res = coef[cur]
+        h_pre, h_post, h_res = coef2[cur]
         if evs is not None:
             evs[0].record()
         hc.hc_pre(Xs[cur], h_pre, out=F_in)
         if evs is not None:
             evs[1].record()
         hc.hc_post_coeffs(Xs[cur], h_res, h_post, Fs[i % 3], phi, bias, alpha, SINKHORN_ITERS, out=Xs[nxt],
-                          coeffs_out=coef[nxt], workspace=ws)
+                          coeffs_out=coef2[nxt], workspace=ws)
         if evs is not None:
             evs[2].record()
 
-    wall, gpu_s, kern = timed(chain_step, ["hc_pre", "hc_post_coeffs"], args.steps, args.warmup)
-    step_bytes = ab["hc_pre"] + ab["hc_post_coeffs"]
+    wall2, gpu2, kern2 = timed(two_call_step, ["hc_pre", "hc_post_coeffs"], args.steps, args.warmup)
 
     # --- isolated sublayer on rotated input sets
     h_post_i = torch.empty(T, n, device=dev)
@@ -214,10 +244,20 @@ def main() -> int:
     iso_wall, iso_gpu, iso_kern = timed(iso_step, ["hc_coeffs_pre", "hc_post"], args.steps, args.warmup)
     iso_bytes = ab["hc_coeffs_pre"] + ab["hc_post"]
 
+    # headline last, once the clocks have settled under the variants above
+    chain_start()
+    wall, gpu_s, kern = timed(make_chain_step(phi_packed), ["hc_post_pre"], args.steps, args.warmup)
+    step_bytes = ab["hc_post_pre"]
+
+    def rate(wall_s, nbytes):
+        per = wall_s / args.steps
+        return {"tokens_per_s": T / per, "ms_per_step": per * 1e3, "achieved_GBps": nbytes / per / 1e9,
+                "pct_hbm_peak": 100.0 * nbytes / per / 1e9 / HBM_PEAK_GBPS}
+
     ms_per_step = wall / args.steps * 1e3
     tokens_per_s = T * args.steps / wall
     achieved = step_bytes / (wall / args.steps) / 1e9
-    dom = max(kern, key=kern.get)
+    dom = "hc_post_pre"
     dom_gbps = ab[dom] / kern[dom] / 1e9
     digest = source_digest()
     traffic = load_traffic(dom, digest)
@@ -235,25 +275,24 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "mHC sublayer n=4 C=4096 T=8192 (batch 4 x seq 2048), bf16 streams, fp32 "
-                               "coefficients, 20 Sinkhorn iterations, forward; steady state of a chain: pre-read + "
-                               "post/res write fused with the next sublayer's coefficients",
+                               "coefficients, 20 Sinkhorn iterations, forward; steady state of a chain: post/res "
+                               "write + next coefficients + next pre-read in one call per step, phi packed once",
                    "n": n, "C": C, "T": T, "sinkhorn_iters": SINKHORN_ITERS, "parallelism": "single GPU"},
         "achieved_GBps": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "gpu_ms_per_step": gpu_s / args.steps * 1e3,
-        "kernels_us": {k: v * 1e6 for k, v in kern.items()},
-        "kernels_GBps": {k: ab[k] / kern[k] / 1e9 for k in kern},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom]},
-        "isolated_sublayer": {
-            "tokens_per_s": T * args.steps / iso_wall,
-            "ms_per_step": iso_wall / args.steps * 1e3,
-            "achieved_GBps": iso_bytes / (iso_wall / args.steps) / 1e9,
-            "pct_hbm_peak": 100.0 * iso_bytes / (iso_wall / args.steps) / 1e9 / HBM_PEAK_GBPS,
-            "kernels_us": {k: v * 1e6 for k, v in iso_kern.items()},
-            "algorithmic_bytes_per_step": iso_bytes},
+        "roofline": {"kernel": "hc_post_pre (mhc_split_kernel<true> + coeffs_finish_kernel + pre4_kernel)",
+                     "bound": "hbm",
+                     "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom],
+                     "launch_us": kern[dom] * 1e6},
+        "chain_phi_packed_each_step": dict(rate(wall_pk, step_bytes), call_us=kern_pk[dom] * 1e6),
+        "chain_two_calls": dict(rate(wall2, ab["hc_pre"] + ab["hc_post_coeffs"]),
+                                calls_us={k: v * 1e6 for k, v in kern2.items()},
+                                calls_GBps={k: ab[k] / v / 1e9 for k, v in kern2.items()}),
+        "isolated_sublayer": dict(rate(iso_wall, iso_bytes), calls_us={k: v * 1e6 for k, v in iso_kern.items()},
+                                  algorithmic_bytes_per_step=iso_bytes),
         "source_digest": digest,
     }
     if not args.no_cpu_baseline:

@@ -151,6 +151,43 @@ int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C,
                    float* h_pre_next, float* h_post_next, float* h_res_next,
                    void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * hc_phi_packed_bytes - bytes of phi in the packed form the fast path of the
+ * coefficient calls multiplies with (n = 4, bfloat16 streams, C % 32 == 0);
+ * 0 when that form does not exist for (n, C, dtype); -1 for invalid sizes.
+ */
+int64_t hc_phi_packed_bytes(int n, int64_t C, int dtype);
+
+/*
+ * hc_phi_pack - phi [n*C, n*n+2n] float32 -> its packed form in `packed`
+ * (256-byte aligned, at least hc_phi_packed_bytes): per group of 8 rows, 48
+ * columns of 8 bfloat16: columns 0..23 hold hi = bf16(phi) (round to nearest
+ * even), columns 24..47 hold lo = bf16(phi - hi), so hi + lo carries about 16
+ * significant bits of phi ([mHC] Eq. 10 runs this product in tf32; see the
+ * notes in the source). A weight that is used many times is packed once. When
+ * no packed form exists the call does nothing and returns HC_OK.
+ */
+int hc_phi_pack(const float* phi, int n, int64_t C, int dtype, void* packed, int64_t packed_bytes,
+                void* stream);
+
+/*
+ * hc_post_pre - the whole step between sublayer l's function and sublayer
+ * l+1's: hc_post_coeffs (the post/res write of sublayer l, [mHC] Eq. 3, 4.3.1,
+ * and the coefficients of X_next under sublayer l+1's parameters, Eq. 7-9,
+ * 14-19) followed by hc_pre on X_next (F_in_next, the input of sublayer l+1's
+ * function, Eq. 3). Arguments as hc_post_coeffs, plus:
+ *   phi_next_packed: NULL, or hc_phi_pack(phi_next) (16-byte aligned); when
+ *     given and the fast path applies, phi_next is not packed again.
+ *   h_pre_next may be NULL (not stored); F_in_next [T, C] stream dtype.
+ *   Workspace: hc_coeffs_workspace_bytes(T, n, C, dtype).
+ */
+int hc_post_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                const void* phi_next_packed, const float* bias_next, float alpha_pre, float alpha_post,
+                float alpha_res, int sinkhorn_iters, float* h_pre_next, float* h_post_next,
+                float* h_res_next, void* F_in_next, void* workspace, int64_t workspace_bytes,
+                void* stream);
+
 /* ------------------------------------------------------------------ xHC -- */
 
 /* Workspace bytes needed by xhc_pre (with_router != 0 when w_router is given). */

@@ -36,6 +36,10 @@ _SIGS = {
     "hc_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "hc_post_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _c_float,
                                 _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "hc_phi_packed_bytes": (_c_i64, [_c_int, _c_i64, _c_int]),
+    "hc_phi_pack": (_c_int, [_vp, _c_int, _c_i64, _c_int, _vp, _c_i64, _vp]),
+    "hc_post_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_float,
+                             _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "xhc_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _c_float, _vp,
                          _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
@@ -200,6 +204,49 @@ def hc_post_coeffs(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sin
     return X_next, coeffs_out
 
 
+def hc_phi_packed_bytes(n: int, C: int, dtype) -> int:
+    return int(lib().hc_phi_packed_bytes(n, C, _DT[dtype]))
+
+
+def hc_phi_pack(phi, n, C, dtype=torch.bfloat16, *, out=None, stream=None):
+    """phi [n*C, n*n+2n] float32 in the packed form of the fast path (a uint8 tensor), or
+    None when (n, C, dtype) has no packed form."""
+    phi = _f32(phi, "phi")
+    nbytes = hc_phi_packed_bytes(n, C, dtype)
+    if nbytes < 0:
+        raise ValueError("invalid sizes for hc_phi_packed_bytes")
+    if nbytes == 0:
+        return None
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=phi.device) if out is None else out
+    _check("hc_phi_pack", lib().hc_phi_pack(_ptr(phi), n, C, _DT[dtype], _ptr(packed),
+                                            packed.numel() * packed.element_size(), _stream(phi.device, stream)))
+    return packed
+
+
+def hc_post_pre(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sinkhorn_iters=20, *,
+                phi_next_packed=None, out=None, coeffs_out=None, F_in_out=None, want_h_pre=True,
+                workspace=None, stream=None):
+    """hc_post_coeffs followed by the pre-read of X_next.
+    Returns (X_next, (h_pre' or None, h_post', h_res'), F_in')."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
+    X_next = torch.empty_like(X) if out is None else out
+    if coeffs_out is None:
+        coeffs_out = (torch.empty(T, n, device=X.device) if want_h_pre else None,
+                      torch.empty(T, n, device=X.device), torch.empty(T, n, n, device=X.device))
+    hp, hq, hr = coeffs_out
+    F_in = torch.empty(T, C, dtype=X.dtype, device=X.device) if F_in_out is None else F_in_out
+    ws = _workspace(hc_coeffs_workspace_bytes(T, n, C, X.dtype), X.device, workspace)
+    a = [float(v) for v in alpha_next]
+    _check("hc_post_pre", lib().hc_post_pre(
+        _ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(h_res, "h_res")), _ptr(_f32(h_post, "h_post")), _ptr(F_out),
+        _ptr(X_next), _ptr(_f32(phi_next, "phi_next")), _ptr(phi_next_packed),
+        _ptr(_f32(bias_next, "bias_next")), a[0], a[1], a[2], int(sinkhorn_iters), _ptr(hp), _ptr(hq), _ptr(hr),
+        _ptr(F_in), _ptr(ws), ws.numel(), _stream(X.device, stream)))
+    return X_next, coeffs_out, F_in
+
+
 # ------------------------------------------------------------------- xHC
 
 
@@ -281,6 +328,7 @@ def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, stream=None)
 
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
-    "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
+    "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
+    "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment",
 ]

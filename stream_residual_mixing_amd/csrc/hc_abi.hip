@@ -45,22 +45,25 @@ inline bool vec_ok(int64_t C, std::initializer_list<const void*> ps) {
 
 // Workspace of the mHC coefficient calls: projection rows P [T, n*n+2n],
 // squared norms ss [T], a private h_pre [T, n] (used when the caller passes
-// none) and the packed phi of the fast path.
+// none), and for the fast path the packed phi and the per-item partial
+// projections.
 struct CoeffWs {
   float* P;
   float* ss;
   float* h_pre;
   void* packed;
+  float* partial;
 };
 
 int64_t mhc_ws_bytes(int64_t T, int n, int64_t C, int dtype) {
   const int ncols = n * n + 2 * n;
   int64_t b = align256(T * ncols * 4) + align256(T * 4) + align256(T * n * 4);
   b += align256(hc::fast_coeffs_packed_bytes(n, C, dtype));
+  b += align256(hc::fast_coeffs_partial_bytes(T, n, C, dtype));
   return b;
 }
 
-CoeffWs carve_mhc(void* ws, int64_t T, int n) {
+CoeffWs carve_mhc(void* ws, int64_t T, int n, int64_t C, int dtype) {
   const int ncols = n * n + 2 * n;
   char* p = (char*)ws;
   CoeffWs w;
@@ -71,6 +74,8 @@ CoeffWs carve_mhc(void* ws, int64_t T, int n) {
   w.h_pre = (float*)p;
   p += align256(T * n * 4);
   w.packed = p;
+  p += align256(hc::fast_coeffs_packed_bytes(n, C, dtype));
+  w.partial = (float*)p;
   return w;
 }
 
@@ -159,12 +164,12 @@ int hc_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float
                            false, workspace, workspace_bytes);
   if (s != HC_OK || T == 0) return s;
   if ((s = device_status()) != HC_OK) return s;
-  const CoeffWs w = carve_mhc(workspace, T, n);
+  const CoeffWs w = carve_mhc(workspace, T, n, C, dtype);
   hipStream_t st = (hipStream_t)stream;
-  if (hc::fast_coeffs_supported(dtype, n, C, X)) {
+  if (hc::fast_coeffs_supported(dtype, n, T, C, X)) {
     return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
                                                     alpha_res, sinkhorn_iters, h_pre, h_post,
-                                                    h_res, nullptr, w.packed, w.h_pre, st));
+                                                    h_res, nullptr, w.packed, w.partial, st));
   }
   return run_coeffs_generic(X, dtype, T, n, C, phi, bias, alpha_pre, alpha_post, alpha_res,
                             sinkhorn_iters, h_pre, h_post, h_res, w, st);
@@ -205,12 +210,12 @@ int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const f
       return HC_ERR_ALIAS;
   }
   if ((s = device_status()) != HC_OK) return s;
-  const CoeffWs w = carve_mhc(workspace, T, n);
+  const CoeffWs w = carve_mhc(workspace, T, n, C, dtype);
   hipStream_t st = (hipStream_t)stream;
-  if (hc::fast_coeffs_supported(dtype, n, C, X) && aligned_to(F_in, 16)) {
+  if (hc::fast_coeffs_supported(dtype, n, T, C, X) && aligned_to(F_in, 16)) {
     return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
-                                                    alpha_res, sinkhorn_iters, h_pre, h_post,
-                                                    h_res, F_in, w.packed, w.h_pre, st));
+                                                    alpha_res, sinkhorn_iters, h_pre ? h_pre : w.h_pre, h_post,
+                                                    h_res, F_in, w.packed, w.partial, st));
   }
   // Generic: the pre-read needs h_pre, kept in the workspace when the caller
   // does not ask for it.
@@ -240,12 +245,16 @@ int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* 
                                                h_res, h_post, F_out, X_next, st));
 }
 
-int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
-                   const float* h_post, const void* F_out, void* X_next, const float* phi_next,
-                   const float* bias_next, float alpha_pre, float alpha_post, float alpha_res,
-                   int sinkhorn_iters, float* h_pre_next, float* h_post_next, float* h_res_next,
-                   void* workspace, int64_t workspace_bytes, void* stream) {
-  // validate as hc_post, then as hc_coeffs on X_next
+}  // extern "C"
+
+namespace {
+
+// Validation shared by hc_post_coeffs and hc_post_pre: hc_post's arguments, then
+// hc_coeffs' arguments on X_next, then the new coefficients against the inputs.
+int check_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                      const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                      const float* bias_next, int sinkhorn_iters, float* h_pre_next, bool h_pre_optional,
+                      float* h_post_next, float* h_res_next, void* workspace, int64_t workspace_bytes) {
   int s = check_mhc_common(X, dtype, T, n, C);
   if (s != HC_OK) return s;
   if (sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS) return HC_ERR_SHAPE;
@@ -260,7 +269,7 @@ int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const 
       overlaps(X_next, xb, h_post, T * n * 4))
     return HC_ERR_ALIAS;
   s = check_coeff_args(X_next, dtype, T, n, C, phi_next, bias_next, sinkhorn_iters, h_pre_next,
-                       h_post_next, h_res_next, false, workspace, workspace_bytes);
+                       h_post_next, h_res_next, h_pre_optional, workspace, workspace_bytes);
   if (s != HC_OK) return s;
   // the new coefficients must not overlap the coefficients being read
   const void* outs[3] = {h_pre_next, h_post_next, h_res_next};
@@ -269,19 +278,104 @@ int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const 
     if (overlaps(outs[i], ob[i], h_res, T * n * n * 4) || overlaps(outs[i], ob[i], h_post, T * n * 4) ||
         overlaps(outs[i], ob[i], F_out, fb) || overlaps(outs[i], ob[i], X, xb))
       return HC_ERR_ALIAS;
+  return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hc_post_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                   const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                   const float* bias_next, float alpha_pre, float alpha_post, float alpha_res,
+                   int sinkhorn_iters, float* h_pre_next, float* h_post_next, float* h_res_next,
+                   void* workspace, int64_t workspace_bytes, void* stream) {
+  int s = check_post_coeffs(X, dtype, T, n, C, h_res, h_post, F_out, X_next, phi_next, bias_next, sinkhorn_iters,
+                            h_pre_next, false, h_post_next, h_res_next, workspace, workspace_bytes);
+  if (s != HC_OK || T == 0) return s;
   if ((s = device_status()) != HC_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  const CoeffWs w = carve_mhc(workspace, T, n);
-  if (hc::fast_post_supported(dtype, n, C, X, F_out, X_next) && hc::fast_coeffs_supported(dtype, n, C, X_next))
-    return launch_status(hc::launch_fast_post_coeffs(X, T, C, h_res, h_post, F_out, X_next, phi_next,
-                                                     bias_next, alpha_pre, alpha_post, alpha_res,
-                                                     sinkhorn_iters, h_pre_next, h_post_next, h_res_next,
-                                                     w.packed, st));
+  const CoeffWs w = carve_mhc(workspace, T, n, C, dtype);
+  if (hc::fast_post_supported(dtype, n, C, X, F_out, X_next) && hc::fast_coeffs_supported(dtype, n, T, C, X_next))
+    return launch_status(hc::launch_fast_post_coeffs(X, T, C, h_res, h_post, F_out, X_next, phi_next, nullptr,
+                                                     bias_next, alpha_pre, alpha_post, alpha_res, sinkhorn_iters,
+                                                     h_pre_next, h_post_next, h_res_next, nullptr, w.packed,
+                                                     w.partial, st));
   hipError_t e = hc::launch_post_generic(dtype, vec_ok(C, {X, F_out, X_next}), X, T, n, C, h_res, h_post,
                                          F_out, X_next, st);
   if (e != hipSuccess) return HC_ERR_LAUNCH;
   return run_coeffs_generic(X_next, dtype, T, n, C, phi_next, bias_next, alpha_pre, alpha_post, alpha_res,
                             sinkhorn_iters, h_pre_next, h_post_next, h_res_next, w, st);
+}
+
+int64_t hc_phi_packed_bytes(int n, int64_t C, int dtype) {
+  if (n < 1 || n > HC_MAX_MHC_STREAMS || C < 1 || !dtype_ok(dtype)) return -1;
+  return hc::fast_coeffs_packed_bytes(n, C, dtype);
+}
+
+int hc_phi_pack(const float* phi, int n, int64_t C, int dtype, void* packed, int64_t packed_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (n < 1 || n > HC_MAX_MHC_STREAMS || C < 1 || C > (1ll << 26)) return HC_ERR_SHAPE;
+  const int64_t pb = hc::fast_coeffs_packed_bytes(n, C, dtype);
+  if (pb == 0) return HC_OK;  // no packed form for this shape: the calls use phi itself
+  if (!phi || !packed) return HC_ERR_NULL;
+  if (!aligned_to(phi, 4) || !aligned_to(packed, 256)) return HC_ERR_ALIGN;
+  if (packed_bytes < pb) return HC_ERR_SHAPE;
+  if (overlaps(packed, pb, phi, (int64_t)n * C * (n * n + 2 * n) * 4)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_fast_pack(phi, C, packed, (hipStream_t)stream));
+}
+
+int hc_post_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                const void* phi_next_packed, const float* bias_next, float alpha_pre, float alpha_post,
+                float alpha_res, int sinkhorn_iters, float* h_pre_next, float* h_post_next,
+                float* h_res_next, void* F_in_next, void* workspace, int64_t workspace_bytes,
+                void* stream) {
+  int s = check_post_coeffs(X, dtype, T, n, C, h_res, h_post, F_out, X_next, phi_next, bias_next, sinkhorn_iters,
+                            h_pre_next, true, h_post_next, h_res_next, workspace, workspace_bytes);
+  if (s != HC_OK || T == 0) return s;
+  if (!F_in_next) return HC_ERR_NULL;
+  if (!aligned_to(F_in_next, esize(dtype))) return HC_ERR_ALIGN;
+  {
+    const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+    const int64_t wsb = mhc_ws_bytes(T, n, C, dtype);
+    const int64_t pb = hc::fast_coeffs_packed_bytes(n, C, dtype);
+    if (overlaps(F_in_next, fb, X, xb) || overlaps(F_in_next, fb, X_next, xb) ||
+        overlaps(F_in_next, fb, F_out, fb) || overlaps(F_in_next, fb, workspace, wsb) ||
+        overlaps(F_in_next, fb, h_res, T * n * n * 4) || overlaps(F_in_next, fb, h_post, T * n * 4) ||
+        overlaps(F_in_next, fb, h_pre_next, T * n * 4) || overlaps(F_in_next, fb, h_post_next, T * n * 4) ||
+        overlaps(F_in_next, fb, h_res_next, T * n * n * 4) ||
+        overlaps(F_in_next, fb, phi_next, (int64_t)n * C * (n * n + 2 * n) * 4) ||
+        overlaps(F_in_next, fb, bias_next, (n * n + 2 * n) * 4) ||
+        (phi_next_packed && pb > 0 && overlaps(F_in_next, fb, phi_next_packed, pb)))
+      return HC_ERR_ALIAS;
+    if (phi_next_packed && pb > 0 &&
+        (!aligned_to(phi_next_packed, 16) || overlaps(phi_next_packed, pb, X_next, xb) ||
+         overlaps(phi_next_packed, pb, workspace, wsb)))
+      return phi_next_packed && !aligned_to(phi_next_packed, 16) ? HC_ERR_ALIGN : HC_ERR_ALIAS;
+  }
+  if ((s = device_status()) != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const CoeffWs w = carve_mhc(workspace, T, n, C, dtype);
+  if (hc::fast_post_supported(dtype, n, C, X, F_out, X_next) && hc::fast_coeffs_supported(dtype, n, T, C, X_next) &&
+      aligned_to(F_in_next, 16))
+    return launch_status(hc::launch_fast_post_coeffs(X, T, C, h_res, h_post, F_out, X_next, phi_next,
+                                                     phi_next_packed, bias_next, alpha_pre, alpha_post, alpha_res,
+                                                     sinkhorn_iters, h_pre_next ? h_pre_next : w.h_pre, h_post_next,
+                                                     h_res_next, F_in_next, w.packed, w.partial, st));
+  // generic: post, coefficients of X_next (h_pre kept in the workspace when not
+  // requested), pre-read of X_next
+  hipError_t e = hc::launch_post_generic(dtype, vec_ok(C, {X, F_out, X_next}), X, T, n, C, h_res, h_post,
+                                         F_out, X_next, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  float* hp = h_pre_next ? h_pre_next : w.h_pre;
+  s = run_coeffs_generic(X_next, dtype, T, n, C, phi_next, bias_next, alpha_pre, alpha_post, alpha_res,
+                         sinkhorn_iters, hp, h_post_next, h_res_next, w, st);
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X_next, F_in_next}), X_next, T, n, C, hp,
+                                              F_in_next, st));
 }
 
 // ------------------------------------------------------------------ xHC --

@@ -9,23 +9,29 @@ namespace hc {
 
 // Bytes of the packed phi used by the fused coefficient kernel (0 if unused).
 int64_t fast_coeffs_packed_bytes(int n, int64_t C, int dtype);
-bool fast_coeffs_supported(int dtype, int n, int64_t C, const void* X);
-// Coefficients (+ pre-read when F_in != nullptr) for n = 4 bfloat16 streams. When
-// h_pre is nullptr the pre-read takes h_pre from h_pre_tmp ([T, 4] floats).
+// Bytes of the per-item partial projections of the fused kernels (0 if unused).
+int64_t fast_coeffs_partial_bytes(int64_t T, int n, int64_t C, int dtype);
+bool fast_coeffs_supported(int dtype, int n, int64_t T, int64_t C, const void* X);
+// Coefficients (+ pre-read when F_in != nullptr) for n = 4 bfloat16 streams;
+// h_pre is required (the pre-read takes it from there).
 hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const float* phi,
                                   const float* bias, float a_pre, float a_post, float a_res,
                                   int iters, float* h_pre, float* h_post, float* h_res, void* F_in,
-                                  void* packed, float* h_pre_tmp, hipStream_t st);
+                                  void* packed, float* partial, hipStream_t st);
+// phi [4C, 24] float32 -> the packed bf16 hi/lo B-operand layout (fast_coeffs_packed_bytes).
+hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream_t st);
 // Pre-read for n = 4 bfloat16 streams (C % 8 == 0, 16-byte aligned).
 hipError_t launch_fast_pre(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in,
                            hipStream_t st);
 // Post/res write fused with the coefficients of the state it writes (phi, bias, gates of
-// the next sublayer).
+// the next sublayer) and, when F_in_n != nullptr, its pre-read (h_pre_n is then
+// required). phi_packed (may be nullptr) holds phi already packed; otherwise phi is
+// packed into `packed`.
 hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const float* h_res,
                                    const float* h_post, const void* F, void* Y, const float* phi,
-                                   const float* bias, float a_pre, float a_post, float a_res, int iters,
-                                   float* h_pre_n, float* h_post_n, float* h_res_n, void* packed,
-                                   hipStream_t st);
+                                   const void* phi_packed, const float* bias, float a_pre, float a_post,
+                                   float a_res, int iters, float* h_pre_n, float* h_post_n, float* h_res_n,
+                                   void* F_in_n, void* packed, float* partial, hipStream_t st);
 
 bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y);
 

@@ -1,14 +1,13 @@
 // Fast paths for n = 4 bfloat16 streams on gfx950.
 //
-// mhc_stream_kernel<POST, PROJ> walks a tile of 16 tokens through all C
-// channels of their 4 streams in 256-channel super-chunks:
+// mhc_split_kernel<POST> streams the state in 256-channel super-chunks of
+// 32-token tiles:
 //   POST: X_next = h_res X + h_post^T F_out  (mHC notes Eq. 3, F_post,res of 4.3.1)
-//   PROJ: the skinny projection of the tile it streams (the X_next it just
-//         produced when POST, else X) with MFMA, the sum of squares, and the
-//         coefficient epilogue (Eq. 15-19): RMS factor, gates, sigmoid,
-//         2*sigmoid and Sinkhorn-Knopp.
-// The projection uses v_mfma_f32_16x16x32_bf16 with the tile's 16 tokens as
-// the M rows. phi (float32) is split as phi = hi + lo with hi = bf16(phi) and
+//   always: the skinny projection of the state it streams (the X_next it just
+//         produced when POST, else X) with MFMA, and the sum of squares.
+// coeffs_finish_kernel turns the projections into the coefficients (Eq. 15-19):
+// RMS factor, gates, sigmoid, 2*sigmoid and Sinkhorn-Knopp.
+// The projection uses v_mfma_f32_16x16x32_bf16 with 16 tokens as the M rows. phi (float32) is split as phi = hi + lo with hi = bf16(phi) and
 // lo = bf16(phi - hi), so X (exact in bf16) times hi plus X times lo carries
 // about 16 significant bits of phi into an fp32 accumulator. phi is packed once
 // per call into the B-operand order [row/8][48][8] (hi columns 0..23, lo
@@ -32,18 +31,21 @@ constexpr int TOK = 16;             // tokens per tile (MFMA M)
 
 // ------------------------------------------------------------- phi packing
 
+// One workgroup per 64 rows of phi [K][24] (K = 4C is a multiple of 128 on the
+// fast path): the rows are read coalesced into LDS, then thread (row group g of
+// 8, column c) writes the hi chunk (column c) and the lo chunk (column 24 + c),
+// 8 bf16 each.
 __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__ phi, int64_t K,
                                                        uint16_t* __restrict__ packed) {
-  // one thread per (row group of 8, column): writes the hi chunk (column c) and
-  // the lo chunk (column NCOL + c), 8 bf16 each
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t ngroups = K / 8;
-  if (g >= ngroups * NCOL) return;
-  const int64_t rg = g / NCOL;
-  const int c = (int)(g - rg * NCOL);
+  __shared__ float rows[64 * NCOL];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * NCOL; i += 256) rows[i] = phi[r0 * NCOL + i];
+  __syncthreads();
+  if (threadIdx.x >= 8 * NCOL) return;
+  const int g = threadIdx.x / NCOL, c = threadIdx.x - g * NCOL;
   float p[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = phi[(rg * 8 + e) * NCOL + c];
+  for (int e = 0; e < 8; ++e) p[e] = rows[(g * 8 + e) * NCOL + c];
   uint32_t hi[4], lo[4];
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__
     // p - hi is exact in float32
     lo[e / 2] = f2bf(p[e] - bf2f(h0)) | (f2bf(p[e + 1] - bf2f(h1)) << 16);
   }
-  uint4* out = reinterpret_cast<uint4*>(packed) + rg * NCP;
+  uint4* out = reinterpret_cast<uint4*>(packed) + (r0 / 8 + g) * NCP;
   out[c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
   out[NCOL + c] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
@@ -78,7 +80,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& q) {
 }
 
 // Work split of one workgroup (32 tokens = two 16-row MFMA blocks, 512 threads
-// = 8 waves) per 256-channel super-chunk of all 4 streams:
+// = 8 waves) per 256-channel super-chunk of all 4 streams of a tile:
 //  * streaming phase: thread (token tid>>5 and tid>>5 + 16, 8 channels at
 //    (tid&31)*8) loads its 16-byte pieces of the 4 streams (and of F_out), so 32
 //    consecutive lanes read 512 contiguous bytes of one stream row; with POST it
@@ -110,82 +112,19 @@ __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
   return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
 
-// Cross-wave reduction of a 32-token tile and the coefficient epilogue
-// ([mHC] Eq. 15-19). acc[tb][b] holds this wave's partial D = A * B for token
-// block tb and packed column block b (lane: D[m = q*4 + e][n = tau]); gram[tb]
-// holds its partial A * A^T, whose diagonal is the sum of squares. `red` is LDS
-// scratch of at least SWAVE * TILE * (NCP + 1) + TILE * (NCOL + SWAVE + 1)
-// floats; the caller has synchronised the workgroup before the call.
-__device__ __forceinline__ void tile_epilogue(float* red, const floatx4_t (&acc)[2][3], const floatx4_t (&gram)[2],
-                                              int64_t t0, int64_t T, int64_t C, const float* __restrict__ bias,
-                                              Gate gate, int iters, float* __restrict__ h_pre_out,
-                                              float* __restrict__ h_post_out, float* __restrict__ h_res_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tau = lane & 15, q = lane >> 4;
-  float* Pt = red + SWAVE * TILE * (NCP + 1);   // [TILE][NCOL]
-  float* ssr = Pt + TILE * NCOL;                // [SWAVE][TILE]
-  float* sst = ssr + SWAVE * TILE;              // [TILE]
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int b = 0; b < 3; ++b)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[(wave * TILE + tb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
-  // the diagonal m == n of gram[tb] sits in the lane with tau == q*4 + e
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (tau == q * 4 + e) ssr[wave * TILE + tb * TOK + tau] = gram[tb][e];
-  __syncthreads();
-  for (int k = tid; k < TILE * NCOL; k += STHR) {
-    const int m = k / NCOL, col = k - m * NCOL;
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < SWAVE; ++w)
-      sum += red[(w * TILE + m) * (NCP + 1) + col] + red[(w * TILE + m) * (NCP + 1) + NCOL + col];
-    Pt[m * NCOL + col] = sum;
-  }
-  if (tid < TILE) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TILE + tid];
-    sst[tid] = sum;
-  }
-  __syncthreads();
-  // thread (token m, entry e) for 32 tokens x 16 entries
-  const int m = tid >> 4, e = tid & 15;
-  const int64_t tt = t0 + m;
-  const float r = sqrtf(sst[m] / (float)(NS4 * C));
-  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
-  if (e < 8 && tt < T) {
-    const float a = e < 4 ? gate.a_pre : gate.a_post;
-    const float z = a * (Pt[m * NCOL + e] * invr) + bias[e];
-    if (e < 4) {
-      if (h_pre_out) h_pre_out[tt * 4 + e] = sigmoid(z);
-    } else {
-      h_post_out[tt * 4 + (e - 4)] = 2.0f * sigmoid(z);
-    }
-  }
-  // h_res: Sinkhorn on the 4x4 block held by 16 consecutive lanes (i = e>>2, j = e&3)
-  const float z = gate.a_res * (Pt[m * NCOL + 8 + e] * invr) + bias[8 + e];
-  float zm = z;
-  zm = fmaxf(zm, __shfl_xor(zm, 1, 64));
-  zm = fmaxf(zm, __shfl_xor(zm, 2, 64));
-  zm = fmaxf(zm, __shfl_xor(zm, 4, 64));
-  zm = fmaxf(zm, __shfl_xor(zm, 8, 64));
-  float M = expf(z - zm);
-  for (int it = 0; it < iters; ++it) {
-    float cs = M + __shfl_xor(M, 4, 64);  // column sum over i
-    cs += __shfl_xor(cs, 8, 64);
-    M = M / cs;
-    float rs = M + __shfl_xor(M, 1, 64);  // row sum over j
-    rs += __shfl_xor(rs, 2, 64);
-    M = M / rs;
-  }
-  if (tt < T) h_res_out[tt * 16 + e] = M;
-}
+// Work items: a tile of 32 tokens times a slice of SPI super-chunks (SPI * 256
+// channels of all 4 streams). Items are numbered tile-major and a persistent
+// grid of one workgroup per CU takes items blockIdx.x, blockIdx.x + grid, ...,
+// so at any moment the running workgroups cover a few adjacent tiles entirely:
+// a compact window of HBM. (Giving each workgroup a whole tile instead puts
+// 256 strips of 512 bytes per 8 KB stream row in flight across the whole
+// state, which streams about 10% slower.) Each item leaves its partial
+// projection, [32 tokens][24 columns | sum of squares] in float, in a
+// workspace; coeffs_finish_kernel adds an item's slices in a fixed order.
+constexpr int SPI = 4;                   // super-chunks per item
+constexpr int PROW = NCOL + 1;           // floats per token of a partial
+constexpr int PART = TILE * PROW;        // floats per item partial
+constexpr int NCOEF = TILE * 20;         // h_res (16) | h_post (4) per token of a tile
 
 // Buffer resource over [base, base + bytes): stores whose offset falls outside are
 // dropped by the hardware, so a guarded store needs no branch (a store behind a
@@ -193,44 +132,26 @@ __device__ __forceinline__ void tile_epilogue(float* red, const floatx4_t (&acc)
 constexpr unsigned BUF_DW3 = 0x00020000u;
 constexpr uint32_t OOB = 0x80000000u;  // any offset >= the range is dropped
 
-template <bool POST, bool PROJ>
-__global__ __launch_bounds__(STHR) void mhc_stream_kernel(
-    const uint16_t* X, int64_t T, int64_t C,
+template <bool POST>
+__global__ __launch_bounds__(STHR) void mhc_split_kernel(
+    const uint16_t* X, int64_t T, int64_t C, int S, int nitem,
     const float* __restrict__ h_res_in, const float* __restrict__ h_post_in,
-    const uint16_t* __restrict__ F, uint16_t* Y,
-    const uint16_t* __restrict__ phi_p, const float* __restrict__ bias, Gate gate, int iters,
-    float* __restrict__ h_pre_out, float* __restrict__ h_post_out, float* __restrict__ h_res_out) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[PROJ ? 2 * LBUF : 16];
+    const uint16_t* __restrict__ F, uint16_t* Y, const uint16_t* __restrict__ phi_p, float* part) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * LBUF];
+  // coefficients of the tile being streamed and of the next item's tile
+  __shared__ float coef[POST ? 2 * NCOEF : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * TILE;
-  // streaming-phase role: tokens st_tok and st_tok + 16 of the tile
+  // streaming-phase role: tokens st_tok and st_tok + 16 of the tile, 8 channels
   const int st_tok = tid >> 5;
   const int st_c8 = (tid & 31) * 8;
-  int64_t st_t[2];
-  bool st_ok[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    st_t[p] = t0 + st_tok + 16 * p;
-    st_ok[p] = st_t[p] < T;
-  }
   // MFMA-phase role
   const int tau = lane & 15;
   const int q = lane >> 4;
-  const int64_t nsc = (C + SC - 1) / SC;
+  const int G = (int)gridDim.x;
+  const int nk = (nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
 
-
-  // per-token post coefficients of the tile, in LDS: [TILE][20] = h_res (16) | h_post (4)
-  __shared__ float coef[POST ? TILE * 20 : 1];
-  if (POST) {
-    for (int k = tid; k < TILE * 20; k += STHR) {
-      const int m = k / 20, e = k - m * 20;
-      const int64_t tt = t0 + m;
-      coef[k] = tt < T ? (e < 16 ? h_res_in[tt * 16 + e] : h_post_in[tt * 4 + (e - 16)]) : 0.f;
-    }
-    __syncthreads();
-  }
   floatx4_t acc[2][3], gram[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -238,58 +159,58 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
 #pragma unroll
     for (int b = 0; b < 3; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const __amdgpu_buffer_rsrc_t pres =
+      __builtin_amdgcn_make_buffer_rsrc(part, 0, (uint32_t)((int64_t)nitem * PART * 4), BUF_DW3);
+
+  // coefficient cidx (< NCOEF) of a tile; rows past T are clamped (never used)
+  auto coef_val = [&](int tile, int cidx) __attribute__((always_inline)) {
+    const int m = cidx / 20, e = cidx - m * 20;
+    int64_t tt = (int64_t)tile * TILE + m;
+    tt = tt < T ? tt : T - 1;
+    const float* src = e < 16 ? h_res_in + tt * 16 + e : h_post_in + tt * 4 + (e - 16);
+    return *src;
+  };
+  const int cidx1 = tid + STHR < NCOEF ? tid + STHR : NCOEF - 1;
 
   // Loads are unconditional: rows past T and channels past C are clamped to a
-  // valid address and their values replaced by zeros, so no load sits behind a
-  // branch and consecutive loads stay in flight together.
-  // X_next of this tile through a buffer resource (rows t0 .. min(T, t0 + TILE))
-  const int64_t nrow = (T - t0) < TILE ? (T - t0) : TILE;
-  const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
-      POST ? Y + t0 * (NS4 * C) : nullptr, 0, POST ? (uint32_t)(nrow * NS4 * C * 2) : 0u, BUF_DW3);
-  const uint16_t* xrow[2];
-  const uint16_t* frow[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int64_t tc = st_ok[p] ? st_t[p] : T - 1;
-    xrow[p] = X + tc * (NS4 * C);
-    frow[p] = POST ? F + tc * C : nullptr;
-  }
-
-  // Loads of one token half (p = 0: tokens 0..15, p = 1: tokens 16..31 of the
-  // tile) of super-chunk s.
-  auto load_half = [&](int64_t s, auto P, uint4 (&xv)[NS4], uint4& fv) __attribute__((always_inline)) {
+  // valid address and their values replaced by zeros (or their stores dropped),
+  // so no load sits behind a branch and consecutive loads stay in flight together.
+  auto load_half = [&](int tile, int64_t s, auto P, uint4 (&xv)[NS4], uint4& fv) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
+    int64_t t = (int64_t)tile * TILE + st_tok + 16 * p;
+    t = t < T ? t : T - 1;
     const int64_t c = s * SC + st_c8;
     const int64_t cc = c < C ? c : C - 8;
+    const uint16_t* xr = X + t * (NS4 * C) + cc;
 #pragma unroll
-    for (int i = 0; i < NS4; ++i) xv[i] = *reinterpret_cast<const uint4*>(xrow[p] + i * C + cc);
-    if (POST) fv = *reinterpret_cast<const uint4*>(frow[p] + cc);
+    for (int i = 0; i < NS4; ++i) xv[i] = *reinterpret_cast<const uint4*>(xr + i * C);
+    if (POST) fv = *reinterpret_cast<const uint4*>(F + t * C + cc);
   };
 
-  // Streaming work of one token half: X_next (POST), its squared norm and its
-  // bf16 tile in LDS (PROJ).
-  auto stream_half = [&](int64_t s, auto P, const uint4 (&xc)[NS4], const uint4& fc, unsigned char* buf)
-                         __attribute__((always_inline)) {
+  // Streaming work of one token half: X_next (POST) and the bf16 tile it
+  // projects, into LDS.
+  auto stream_half = [&](int tile, int64_t s, auto P, const uint4 (&xc)[NS4], const uint4& fc, unsigned char* buf,
+                         const float* cf, __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
-    const int64_t c = s * SC + st_c8;
-    const bool ok = st_ok[p] && c < C;
     const int m = st_tok + 16 * p;
+    const int64_t c = s * SC + st_c8;
+    const bool ok = ((int64_t)tile * TILE + m < T) && c < C;
     uint4 a_frag[NS4];
     if (POST) {
-      const float* cf = coef + m * 20;
+      const float* cm = cf + m * 20;
       float fv[8];
       unpack8(fc, fv);
 #pragma unroll
       for (int i = 0; i < NS4; ++i) {
         float y[8];
-        const float wp = cf[16 + i];
+        const float wp = cm[16 + i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = wp * fv[e];
 #pragma unroll
         for (int j = 0; j < NS4; ++j) {
           float xv[8];
           unpack8(xc[j], xv);
-          const float w = cf[i * 4 + j];
+          const float w = cm[i * 4 + j];
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] += w * xv[e];
         }
@@ -306,81 +227,244 @@ __global__ __launch_bounds__(STHR) void mhc_stream_kernel(
 #pragma unroll
       for (int i = 0; i < NS4; ++i) a_frag[i] = keep_or_zero(ok, xc[i]);
     }
-    if (PROJ) {
 #pragma unroll
-      for (int i = 0; i < NS4; ++i) *reinterpret_cast<uint4*>(buf + (i * TILE + m) * LROW + st_c8 * 2) = a_frag[i];
-    }
+    for (int i = 0; i < NS4; ++i) *reinterpret_cast<uint4*>(buf + (i * TILE + m) * LROW + st_c8 * 2) = a_frag[i];
   };
 
-  // One super-chunk. Issue order: B fragments of its MFMA phase, the second
-  // token half of this super-chunk, then (after the first half is computed) the
-  // first half of the next super-chunk. Waiting for the first half or for the
-  // B fragments thus never waits for loads issued later; the first-half
-  // register set is refilled for the next super-chunk while the second half
-  // is computed. prefetch: Pre (load the next super-chunk's first half) or NoPre.
+  // One super-chunk s of `tile`; (ptile, ps) is the super-chunk whose first
+  // token half is prefetched. Issue order: B fragments of the MFMA phase, the
+  // second token half, then (after the first half is computed) the prefetch, so
+  // waiting for the first half or for the B fragments never waits for loads
+  // issued later.
   uint4 xA[NS4], xB[NS4], fA = make_uint4(0, 0, 0, 0), fB = make_uint4(0, 0, 0, 0);
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  auto body = [&](int64_t s, auto prefetch) __attribute__((always_inline)) {
+  auto body = [&](int tile, int64_t s, int ptile, int64_t ps, unsigned char* buf, const float* cf,
+                  __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
     const int64_t cg = s * SC + wave * 32;
+    const int64_t cgc = cg < C ? cg : C - 32;
     uint4 pf[NS4][3];
-    if (PROJ) {
-      const int64_t cgc = cg < C ? cg : C - 32;
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      const uint4* pb = reinterpret_cast<const uint4*>(phi_p) + ((i * C + cgc) / 8 + q) * NCP + tau;
+#pragma unroll
+      for (int b = 0; b < 3; ++b) pf[i][b] = pb[b * 16];
+    }
+    load_half(tile, s, H1{}, xB, fB);
+    stream_half(tile, s, H0{}, xA, fA, buf, cf, yres);
+    load_half(ptile, ps, H0{}, xA, fA);
+    stream_half(tile, s, H1{}, xB, fB, buf, cf, yres);
+    __syncthreads();
+    // With POST, rows past T and channels past C hold values computed from
+    // clamped loads (zeroing them before the store would turn the store into a
+    // branch): their A fragments are replaced by zeros here. Without POST the
+    // tile already holds zeros there. Either way a group past C adds nothing
+    // against its clamped, valid B address.
+    const bool ch_ok = cg + q * 8 < C;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const bool a_ok = ch_ok && ((int64_t)tile * TILE + tb * TOK + tau < T);
 #pragma unroll
       for (int i = 0; i < NS4; ++i) {
-        const uint4* pb = reinterpret_cast<const uint4*>(phi_p) + ((i * C + cgc) / 8 + q) * NCP + tau;
+        uint4 af = *reinterpret_cast<const uint4*>(buf + (i * TILE + tb * TOK + tau) * LROW + (wave * 32 + q * 8) * 2);
+        if (POST) af = keep_or_zero(a_ok, af);
 #pragma unroll
-        for (int b = 0; b < 3; ++b) pf[i][b] = pb[b * 16];
+        for (int b = 0; b < 3; ++b)
+          acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pf[i][b]), acc[tb][b], 0, 0, 0);
+        // A times its own transpose: the diagonal accumulates each token's sum of squares.
+        gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
       }
     }
-    load_half(s, H1{}, xB, fB);
-    unsigned char* buf = lds + (s & 1) * LBUF;
-    stream_half(s, H0{}, xA, fA, buf);
-    if constexpr (decltype(prefetch)::value) load_half(s + 1, H0{}, xA, fA);
-    stream_half(s, H1{}, xB, fB, buf);
-    if (PROJ) {
-      __syncthreads();
-      // With POST, rows past T and channels past C hold values computed from
-      // clamped loads (zeroing them before the store would turn the store into
-      // a branch): their A fragments are replaced by zeros here. Without POST
-      // the tile already holds zeros there. Either way a group past C adds
-      // nothing against its clamped, valid B address.
-      const bool ch_ok = cg + q * 8 < C;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const bool a_ok = ch_ok && (t0 + tb * TOK + tau < T);
-#pragma unroll
-        for (int i = 0; i < NS4; ++i) {
-          uint4 af =
-              *reinterpret_cast<const uint4*>(buf + (i * TILE + tb * TOK + tau) * LROW + (wave * 32 + q * 8) * 2);
-          if (POST) af = keep_or_zero(a_ok, af);
-#pragma unroll
-          for (int b = 0; b < 3; ++b)
-            acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pf[i][b]), acc[tb][b], 0, 0, 0);
-          // A times its own transpose: the diagonal accumulates each token's sum of squares.
-          gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
-        }
-      }
-      // The next super-chunk writes the other buffer; the one after it writes this
-      // buffer only after passing the next barrier, i.e. after these reads.
-    }
+    // The next super-chunk writes the other buffer; the one after it writes this
+    // buffer only after passing the next barrier, i.e. after these reads.
   };
 
-  // The last super-chunk has nothing to prefetch; it is peeled so that the
-  // loop's prefetch is unconditional (branch-free wait counts).
-  load_half(0, H0{}, xA, fA);
-  for (int64_t s = 0; s + 1 < nsc; ++s) body(s, std::true_type{});
-  body(nsc - 1, std::false_type{});
-  if (!PROJ) return;
+  int item = (int)blockIdx.x;
+  int tile = item / S, slice = item - tile * S;
+  if (POST) {
+    coef[tid] = coef_val(tile, tid);
+    if (tid + STHR < NCOEF) coef[tid + STHR] = coef_val(tile, tid + STHR);
+  }
+  load_half(tile, (int64_t)slice * SPI, H0{}, xA, fA);
+  if (POST) __syncthreads();
+  // the partial sums this thread reduced for the previous item (pitem; -1: none)
+  float pend0 = 0.f, pend1 = 0.f;
+  int pitem = -1;
+  const bool two = tid + STHR < PART;
+  auto store_pending = [&]() __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)pitem * (uint32_t)(PART * 4);
+    const uint32_t off0 = pitem >= 0 ? base + (uint32_t)tid * 4 : OOB;
+    const uint32_t off1 = pitem >= 0 && two ? base + (uint32_t)(tid + STHR) * 4 : OOB;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend0), pres, off0, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend1), pres, off1, 0, 0);
+  };
+  int step = 0;
+  for (int k = 0; k < nk; ++k) {
+    // the next item of this workgroup (this one again after the last: its first
+    // super-chunk is then prefetched for nothing)
+    const int nitem_k = k + 1 < nk ? item + G : item;
+    const int ntile = nitem_k / S, nslice = nitem_k - ntile * S;
+    const float* cf = coef + (k & 1) * NCOEF;
+    const int64_t nrow = (T - (int64_t)tile * TILE) < TILE ? (T - (int64_t)tile * TILE) : TILE;
+    const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
+        POST ? Y + (int64_t)tile * TILE * (NS4 * C) : nullptr, 0, POST ? (uint32_t)(nrow * NS4 * C * 2) : 0u,
+        BUF_DW3);
+    const int64_t s0 = (int64_t)slice * SPI;
+    float cn0 = 0.f, cn1 = 0.f;
+    // SPI super-chunks, unrolled (past the last super-chunk of C they only add
+    // zeros): straight-line code keeps the compiler's wait counts exact.
+#pragma unroll
+    for (int j = 0; j < SPI; ++j) {
+      const bool last = j + 1 == SPI;
+      body(tile, s0 + j, last ? ntile : tile, last ? (int64_t)nslice * SPI : s0 + j + 1,
+           lds + ((step + j) & 1) * LBUF, cf, yres);
+      if (j == 0) {
+        // after the first prefetch: the previous item's partial sums and the
+        // next item's coefficients
+        store_pending();
+        if (POST) {
+          cn0 = coef_val(ntile, tid);
+          cn1 = coef_val(ntile, cidx1);
+        }
+      }
+    }
+    step += SPI;
+    // ---- item end: cross-wave reduction into this thread's partial sums,
+    // through the buffer the last super-chunk's MFMA phase read
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds + ((step - 1) & 1) * LBUF);  // [SWAVE][TILE][NCP + 1]
+    float* ssr = red + SWAVE * TILE * (NCP + 1);                           // [SWAVE][TILE]
+    // lane holds D[m = q*4 + e][n = tau] of each block b, for token block tb
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          red[(wave * TILE + tb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
+    // the diagonal m == n of gram[tb] sits in the lane with tau == q*4 + e
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (tau == q * 4 + e) ssr[wave * TILE + tb * TOK + tau] = gram[tb][e];
+    if (POST) {
+      float* cn = coef + ((k + 1) & 1) * NCOEF;
+      cn[tid] = cn0;
+      if (tid + STHR < NCOEF) cn[tid + STHR] = cn1;
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 3; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+    auto reduce = [&](int o) __attribute__((always_inline)) {
+      const int m = o / PROW, col = o - m * PROW;
+      float sum = 0.f;
+      if (col < NCOL) {
+#pragma unroll
+        for (int w = 0; w < SWAVE; ++w)
+          sum += red[(w * TILE + m) * (NCP + 1) + col] + red[(w * TILE + m) * (NCP + 1) + NCOL + col];
+      } else {
+#pragma unroll
+        for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TILE + m];
+      }
+      return sum;
+    };
+    pend0 = reduce(tid);
+    pend1 = reduce(two ? tid + STHR : tid);
+    pitem = item;
+    item = nitem_k;
+    tile = ntile;
+    slice = nslice;
+  }
+  store_pending();
+}
 
-  __syncthreads();
-  tile_epilogue(reinterpret_cast<float*>(lds), acc, gram, t0, T, C, bias, gate, iters, h_pre_out, h_post_out,
-                h_res_out);
+// Lane exchange within rows of 16 lanes (DPP): quad permutations and row rotations.
+constexpr int DPP_QXOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QXOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROR4 = 0x124;  // row_ror:4
+constexpr int DPP_ROR8 = 0x128;  // row_ror:8
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Coefficients of token tt (< T) from the partial projections ([mHC] Eq.
+// 15-19), computed by the 16 lanes of one DPP row (lane e = tid & 15). Each lane
+// adds the token's slices in slice order (the sum of squares, the h_res logit
+// of entry e = i*4 + j, and for e < 8 the pre/post logit), then r = sqrt(ss /
+// 4C), z = alpha * P / r + b, h_pre = sigmoid, h_post = 2 sigmoid, and
+// Sinkhorn-Knopp on the 4x4 block held by the 16 lanes. Returns h_pre[e] in
+// lanes e < 4; stores the coefficients when `store` (uniform over the row).
+__device__ __forceinline__ float token_coeffs(const float* __restrict__ part, int64_t tt, int e, int64_t C, int S,
+                                              const float* __restrict__ bias, Gate gate, int iters, bool store,
+                                              float* __restrict__ h_pre_out, float* __restrict__ h_post_out,
+                                              float* __restrict__ h_res_out) {
+  const int64_t tile = tt / TILE;
+  const int m = (int)(tt - tile * TILE);
+  const float* base = part + tile * S * PART + m * PROW;
+  float ss = 0.f, pr = 0.f, pe = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float* b = base + (int64_t)s * PART;
+    ss += b[NCOL];
+    pr += b[8 + e];
+    pe += b[e & 7];
+  }
+  const float r = sqrtf(ss / (float)(NS4 * C));
+  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  const float a = e < 4 ? gate.a_pre : gate.a_post;
+  const float sg = sigmoid(a * (pe * invr) + bias[e & 7]);
+  if (store && e < 8) {
+    if (e < 4) {
+      if (h_pre_out) h_pre_out[tt * 4 + e] = sg;
+    } else {
+      h_post_out[tt * 4 + (e - 4)] = 2.0f * sg;
+    }
+  }
+  // h_res: the per-token max logit is subtracted before exp (a common factor of
+  // M0, removed by the first normalisation). Cross-lane sums use DPP within the
+  // 16-lane row: a column (fixed j) is lanes j, j+4, j+8, j+12, summed as
+  // (M[e] + M[e+8]) + (M[e+4] + M[e+12]) by rotating 8 then 4, which gives the
+  // same operands, hence the same float, in all four lanes; a row (fixed i) is
+  // one quad, summed with the quad permutations xor 1, xor 2.
+  const float z = gate.a_res * (pr * invr) + bias[8 + e];
+  float zm = fmaxf(z, dpp<DPP_QXOR1>(z));
+  zm = fmaxf(zm, dpp<DPP_QXOR2>(zm));
+  zm = fmaxf(zm, dpp<DPP_ROR4>(zm));
+  zm = fmaxf(zm, dpp<DPP_ROR8>(zm));
+  float M = expf(z - zm);
+  for (int it = 0; it < iters; ++it) {
+    float cs = M + dpp<DPP_ROR8>(M);  // column sum over i
+    cs += dpp<DPP_ROR4>(cs);
+    M = M / cs;
+    float rs = M + dpp<DPP_QXOR1>(M);  // row sum over j
+    rs += dpp<DPP_QXOR2>(rs);
+    M = M / rs;
+  }
+  if (store) h_res_out[tt * 16 + e] = M;
+  return sg;
+}
+
+// Coefficients only: 16 threads per token (every lane of a row takes part in
+// the DPP exchanges; rows past T work on the last token and store nothing).
+__global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C,
+                                                            int S, const float* __restrict__ bias, Gate gate,
+                                                            int iters, float* __restrict__ h_pre_out,
+                                                            float* __restrict__ h_post_out,
+                                                            float* __restrict__ h_res_out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tt = g >> 4;
+  token_coeffs(part, tt < T ? tt : T - 1, (int)(g & 15), C, S, bias, gate, iters, tt < T, h_pre_out, h_post_out,
+               h_res_out);
 }
 
 // --------------------------------------------------------------- pre-read
 
-// F_in[t, c] = sum_i h_pre[t, i] X[t, i, c] for n = 4 bf16; 16 channels per thread.
+// F_in[t, c] = sum_i h_pre[t, i] X[t, i, c] for n = 4 bf16; 8 channels per thread.
 __global__ __launch_bounds__(256) void pre4_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t C,
                                                    const float* __restrict__ h_pre,
                                                    uint16_t* __restrict__ F_in) {
@@ -398,25 +482,53 @@ __global__ __launch_bounds__(256) void pre4_kernel(const uint16_t* __restrict__ 
   unpack8(*reinterpret_cast<const uint4*>(p + 3 * C), d);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = w0 * a[e] + w1 * b[e] + w2 * c[e] + w3 * d[e];
-  uint4 q;
-  q.x = pack_bf2(o[0], o[1]);
-  q.y = pack_bf2(o[2], o[3]);
-  q.z = pack_bf2(o[4], o[5]);
-  q.w = pack_bf2(o[6], o[7]);
-  *reinterpret_cast<uint4*>(F_in + t * C + c0) = q;
+  // F_in is not read again by this pass: a nontemporal store
+  __builtin_nontemporal_store(u32x4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                      pack_bf2_hw(o[6], o[7])},
+                              reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
 }
 
 // ----------------------------------------------------------------- hosts
 
 static inline bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+namespace {
+struct SplitGeom {
+  int S;      // items per tile
+  int nitem;  // tiles * S
+};
+SplitGeom split_geom(int64_t T, int64_t C) {
+  const int64_t nsc = (C + SC - 1) / SC;
+  const int64_t S = (nsc + SPI - 1) / SPI;
+  return SplitGeom{(int)S, (int)(((T + TILE - 1) / TILE) * S)};
+}
+// the shapes the split kernel addresses with 32-bit buffer offsets and int item ids
+bool split_shape_ok(int64_t T, int64_t C) {
+  if (C % 32 != 0 || C < 32 || C >= (1ll << 24)) return false;
+  const int64_t nsc = (C + SC - 1) / SC, S = (nsc + SPI - 1) / SPI;
+  return ((T + TILE - 1) / TILE) * S * PART * 4 < (1ll << 31);
+}
+int grid_for(int nitem) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+    ncu = 256;
+  return nitem < ncu ? nitem : ncu;
+}
+}  // namespace
+
 int64_t fast_coeffs_packed_bytes(int n, int64_t C, int dtype) {
   if (n != 4 || dtype != 1 || C % 32 != 0) return 0;
   return (int64_t)n * C / 8 * NCP * 16;
 }
 
-bool fast_coeffs_supported(int dtype, int n, int64_t C, const void* X) {
-  return dtype == 1 && n == 4 && C % 32 == 0 && C >= 32 && a16(X);
+int64_t fast_coeffs_partial_bytes(int64_t T, int n, int64_t C, int dtype) {
+  if (n != 4 || dtype != 1 || !split_shape_ok(T, C)) return 0;
+  return (int64_t)split_geom(T, C).nitem * PART * 4;
+}
+
+bool fast_coeffs_supported(int dtype, int n, int64_t T, int64_t C, const void* X) {
+  return dtype == 1 && n == 4 && split_shape_ok(T, C) && a16(X);
 }
 
 bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y) {
@@ -424,50 +536,66 @@ bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void*
 }
 
 static hipError_t launch_pack(const float* phi, int64_t K, void* packed, hipStream_t st) {
-  const int64_t work = K / 8 * NCOL;
-  hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, phi, K,
-                     (uint16_t*)packed);
+  hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)(K / 64)), dim3(256), 0, st, phi, K, (uint16_t*)packed);
   return hipGetLastError();
 }
 
-hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const float* phi,
-                                  const float* bias, float a_pre, float a_post, float a_res,
-                                  int iters, float* h_pre, float* h_post, float* h_res, void* F_in,
-                                  void* packed, float* h_pre_tmp, hipStream_t st) {
-  hipError_t e = launch_pack(phi, 4 * C, packed, st);
-  if (e != hipSuccess) return e;
-  float* hp = h_pre ? h_pre : h_pre_tmp;
-  const unsigned grid = (unsigned)((T + TILE - 1) / TILE);
-  hipLaunchKernelGGL((mhc_stream_kernel<false, true>), dim3(grid), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
-                     nullptr, nullptr, nullptr, nullptr, (const uint16_t*)packed, bias,
-                     Gate{a_pre, a_post, a_res}, iters, hp, h_post, h_res);
-  e = hipGetLastError();
-  if (e != hipSuccess || !F_in) return e;
-  const int64_t work = T * (C / 8);
-  hipLaunchKernelGGL(pre4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, (const uint16_t*)X, T,
-                     C, hp, (uint16_t*)F_in);
+static hipError_t launch_finish(const float* part, int64_t T, int64_t C, int S, const float* bias, Gate gate,
+                                int iters, float* h_pre, float* h_post, float* h_res, hipStream_t st) {
+  const int64_t threads = T * 16;
+  hipLaunchKernelGGL(coeffs_finish_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, T, C, S,
+                     bias, gate, iters, h_pre, h_post, h_res);
   return hipGetLastError();
 }
 
-hipError_t launch_fast_pre(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
+static hipError_t launch_pre4(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
   const int64_t work = T * (C / 8);
   hipLaunchKernelGGL(pre4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, (const uint16_t*)X, T,
                      C, h_pre, (uint16_t*)F_in);
   return hipGetLastError();
 }
 
-hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const float* h_res,
-                                   const float* h_post, const void* F, void* Y, const float* phi,
-                                   const float* bias, float a_pre, float a_post, float a_res, int iters,
-                                   float* h_pre_n, float* h_post_n, float* h_res_n, void* packed,
-                                   hipStream_t st) {
+hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const float* phi,
+                                  const float* bias, float a_pre, float a_post, float a_res,
+                                  int iters, float* h_pre, float* h_post, float* h_res, void* F_in,
+                                  void* packed, float* partial, hipStream_t st) {
   hipError_t e = launch_pack(phi, 4 * C, packed, st);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((T + TILE - 1) / TILE);
-  hipLaunchKernelGGL((mhc_stream_kernel<true, true>), dim3(grid), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
-                     h_res, h_post, (const uint16_t*)F, (uint16_t*)Y, (const uint16_t*)packed, bias,
-                     Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n, h_res_n);
-  return hipGetLastError();
+  const SplitGeom g = split_geom(T, C);
+  hipLaunchKernelGGL(mhc_split_kernel<false>, dim3(grid_for(g.nitem)), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
+                     g.S, g.nitem, nullptr, nullptr, nullptr, nullptr, (const uint16_t*)packed, partial);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, st);
+  if (e != hipSuccess || !F_in) return e;
+  return launch_pre4(X, T, C, h_pre, F_in, st);
+}
+
+hipError_t launch_fast_pre(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
+  return launch_pre4(X, T, C, h_pre, F_in, st);
+}
+
+hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const float* h_res,
+                                   const float* h_post, const void* F, void* Y, const float* phi,
+                                   const void* phi_packed, const float* bias, float a_pre, float a_post,
+                                   float a_res, int iters, float* h_pre_n, float* h_post_n, float* h_res_n,
+                                   void* F_in_n, void* packed, float* partial, hipStream_t st) {
+  hipError_t e;
+  if (!phi_packed) {
+    if ((e = launch_pack(phi, 4 * C, packed, st)) != hipSuccess) return e;
+    phi_packed = packed;
+  }
+  const SplitGeom g = split_geom(T, C);
+  hipLaunchKernelGGL(mhc_split_kernel<true>, dim3(grid_for(g.nitem)), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
+                     g.S, g.nitem, h_res, h_post, (const uint16_t*)F, (uint16_t*)Y, (const uint16_t*)phi_packed,
+                     partial);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n, h_res_n, st);
+  if (e != hipSuccess || !F_in_n) return e;
+  return launch_pre4(Y, T, C, h_pre_n, F_in_n, st);
+}
+
+hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream_t st) {
+  return launch_pack(phi, 4 * C, packed, st);
 }
 
 }  // namespace hc

@@ -29,8 +29,9 @@ def hc():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for want in ("hc_coeffs", "hc_pre", "hc_coeffs_pre", "hc_post", "xhc_pre", "xhc_route",
-                 "xhc_augment", "hc_status_string"):
+    for want in ("hc_coeffs", "hc_pre", "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_post_pre",
+                 "hc_phi_pack", "hc_phi_packed_bytes", "xhc_pre", "xhc_route", "xhc_augment",
+                 "hc_status_string"):
         assert want in names
 
 
@@ -91,6 +92,33 @@ def test_validation_rejects_bad_arguments_before_device_work(hc):
     assert post(Y=ctypes.c_void_p(0x10002)) == -5       # partial overlap with X
     assert post(F=ctypes.c_void_p(0x90010)) == -5       # F_out inside X_next
     assert L.hc_pre(FAKE, 1, 8, 4, 64, FAKE, ctypes.c_void_p(0x10010), None) == -5
+
+    # hc_post_pre: hc_post_coeffs' checks plus F_in_next
+    def post_pre(Fin=ctypes.c_void_p(0xA0000), Y=ctypes.c_void_p(0x90000), hpre=ctypes.c_void_p(0xB0000),
+                 packed=None, iters=20):
+        return L.hc_post_pre(FAKE, 1, 8, 4, 64, ctypes.c_void_p(0x60000), ctypes.c_void_p(0x70000),
+                             ctypes.c_void_p(0x50000), Y, ctypes.c_void_p(0xC0000), packed,
+                             ctypes.c_void_p(0xD0000), 0.01, 0.01, 0.01, iters, hpre, ctypes.c_void_p(0xB1000),
+                             ctypes.c_void_p(0xB2000), Fin, ctypes.c_void_p(0x100000), ws, None)
+    assert post_pre(Fin=None) == -1
+    assert post_pre(iters=0) == -2
+    assert post_pre(Fin=ctypes.c_void_p(0xA0001)) == -4   # misaligned for bf16
+    assert post_pre(Fin=ctypes.c_void_p(0x90010)) == -5   # F_in_next inside X_next
+    assert post_pre(Fin=ctypes.c_void_p(0x10020)) == -5   # F_in_next inside X
+    assert post_pre(Y=ctypes.c_void_p(0x10002)) == -5     # X_next partially over X
+    assert post_pre(packed=ctypes.c_void_p(0x90100)) == -5  # packed phi inside X_next
+    assert post_pre(packed=ctypes.c_void_p(0xE0008)) == -4  # packed phi not 16-byte aligned
+    # hc_phi_pack: packed form exists for n = 4 bf16 with C % 32 == 0 only
+    assert L.hc_phi_packed_bytes(4, 64, 1) == 4 * 64 // 8 * 48 * 16
+    assert L.hc_phi_packed_bytes(4, 40, 1) == 0
+    assert L.hc_phi_packed_bytes(4, 64, 0) == 0
+    assert L.hc_phi_packed_bytes(0, 64, 1) == -1
+    assert L.hc_phi_pack(FAKE, 4, 40, 1, None, 0, None) == 0  # nothing to pack
+    assert L.hc_phi_pack(None, 4, 64, 1, ctypes.c_void_p(0x200000), 1 << 20, None) == -1
+    assert L.hc_phi_pack(FAKE, 4, 64, 1, ctypes.c_void_p(0x200010), 1 << 20, None) == -4
+    assert L.hc_phi_pack(FAKE, 4, 64, 1, ctypes.c_void_p(0x200000), 100, None) == -2
+    assert L.hc_phi_pack(FAKE, 4, 64, 1, ctypes.c_void_p(0x10000), 1 << 20, None) == -5
+    assert L.hc_phi_pack(FAKE, 4, 64, 9, ctypes.c_void_p(0x200000), 1 << 20, None) == -3
 
     # xHC shape rules: 1 <= m <= k <= N, k <= 16, K <= 8
     def xpre(N=16, k=4, m=2):

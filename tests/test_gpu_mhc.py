@@ -278,3 +278,100 @@ def test_chain_with_post_coeffs_workload2_shape():
         for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (h_pre, h_post_n, h_res_n), r2):
             check_fp32(name, host64(g), r)
         X, h_post, h_res = Xn, h_post_n, h_res_n
+
+
+# ------------------------------------------- the whole step: post, next coefficients, next pre-read
+
+def _post_pre_case(T, C, seed, dtype=synth.BF16, in_place=False, packed=False, want_h_pre=True):
+    inp = synth.mhc_layer(seed, 0, T, 4, C, dtype)
+    nxt = synth.mhc_layer(seed, 1, T, 4, C, dtype, draw_x=False)
+    X = dev(inp["X"])
+    h_pre, h_post, h_res = hc.hc_coeffs(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    ref = _oracle(inp)
+    phi_n = dev(nxt["phi"])
+    pk = hc.hc_phi_pack(phi_n, 4, C, X.dtype) if packed else None
+    out = X if in_place else None
+    Xn, (hp2, hq2, hr2), F_in = hc.hc_post_pre(X, h_res, h_post, dev(inp["F_out"]), phi_n, dev(nxt["bias"]),
+                                               [0.01] * 3, phi_next_packed=pk, out=out, want_h_pre=want_h_pre)
+    torch.cuda.synchronize()
+    if dtype == synth.BF16:
+        check_bf16("X_next", host64(Xn), ref["X_next"], literal_max_abs=True)
+    else:
+        check_fp32("X_next", host64(Xn), ref["X_next"])
+    # coefficients and pre-read of the state actually written (the GPU's X_next)
+    r2 = O.hc_coeffs(host64(Xn), nxt["phi"], nxt["bias"], nxt["alpha"])
+    got = (hp2, hq2, hr2) if want_h_pre else (None, hq2, hr2)
+    for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), got, r2):
+        if g is not None:
+            check_fp32(name, host64(g), r)
+    F_ref = O.hc_pre(host64(Xn), r2[0])
+    if dtype == synth.BF16:
+        check_bf16("F_in'", host64(F_in), F_ref)
+    else:
+        check_fp32("F_in'", host64(F_in), F_ref)
+    return Xn, hq2, hr2, F_in
+
+
+@pytest.mark.parametrize("T", [1, 16, 133])
+def test_post_pre_matches_post_then_coeffs_pre(T):
+    note(f"mHC hc_post_pre n=4 C=4096 bf16 T={T}")
+    _post_pre_case(T, 4096, 40 + T)
+
+
+def test_post_pre_in_place_small_C_generic_and_no_h_pre():
+    note("mHC hc_post_pre in place C=64, C=7168 without h_pre, C=32")
+    _post_pre_case(37, 64, 51, in_place=True)
+    _post_pre_case(19, 7168, 52, want_h_pre=False)
+    _post_pre_case(70, 32, 53)
+    note("mHC hc_post_pre generic shapes (C=40 bf16, C=256 fp32)")
+    _post_pre_case(11, 40, 54)
+    _post_pre_case(23, 256, 55, dtype=synth.F32)
+
+
+def test_post_pre_packed_phi_is_identical():
+    """hc_phi_pack once + hc_post_pre(phi_next_packed) gives the same bits as
+    letting the call pack phi itself."""
+    note("mHC hc_post_pre with phi packed by hc_phi_pack, C=4096 T=77")
+    a = _post_pre_case(77, 4096, 61, packed=False)
+    b = _post_pre_case(77, 4096, 61, packed=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(host64(x), host64(y))
+
+
+def test_phi_pack_layout_pin():
+    """The packed form: per group of 8 rows, columns 0..23 hi = bf16(phi), 24..47
+    lo = bf16(phi - hi), 8 consecutive rows of one column contiguous."""
+    note("hc_phi_pack layout, C=64")
+    C = 64
+    rng = np.random.default_rng(7)
+    phi = rng.standard_normal((4 * C, 24)).astype(np.float32) * 0.02
+    pk = hc.hc_phi_pack(torch.from_numpy(phi).cuda(), 4, C, torch.bfloat16)
+    torch.cuda.synchronize()
+    got = pk.cpu().numpy().view(np.uint16).reshape(4 * C // 8, 48, 8)
+    hi, hi_bits = synth.round_to_bf16(phi)
+    _, lo_bits = synth.round_to_bf16(phi - hi)  # phi - hi is exact in float32
+    want = np.concatenate([hi_bits.reshape(4 * C // 8, 8, 24), lo_bits.reshape(4 * C // 8, 8, 24)], axis=2)
+    np.testing.assert_array_equal(got, want.transpose(0, 2, 1))
+
+
+def test_chain_with_post_pre_workload2_shape():
+    """The chained path as one call per step over 8 layers at C=7168, each layer
+    against the oracle on the GPU's own input state."""
+    T, n, C = 45, 4, 7168
+    layers = [synth.mhc_layer(2, 0, T, n, C, synth.BF16)] + [
+        synth.mhc_layer(2, l, T, n, C, synth.BF16, draw_x=False) for l in range(1, 9)]
+    X = dev(layers[0]["X"])
+    h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(X, dev(layers[0]["phi"]), dev(layers[0]["bias"]), [0.01] * 3)
+    for l in range(8):
+        note(f"mHC hc_post_pre chain C=7168 T=45 layer {l}")
+        inp = layers[l]
+        ref = O.mhc_sublayer(host64(X), inp["phi"], inp["bias"], inp["alpha"], inp["F_out"].values)
+        check_bf16("F_in", host64(F_in), ref["F_in"])
+        Xn, (h_pre, h_post_n, h_res_n), F_in = hc.hc_post_pre(
+            X, h_res, h_post, dev(inp["F_out"]), dev(layers[l + 1]["phi"]), dev(layers[l + 1]["bias"]), [0.01] * 3)
+        torch.cuda.synchronize()
+        check_bf16("X_next", host64(Xn), ref["X_next"])
+        r2 = O.hc_coeffs(host64(Xn), layers[l + 1]["phi"], layers[l + 1]["bias"], layers[l + 1]["alpha"])
+        for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (h_pre, h_post_n, h_res_n), r2):
+            check_fp32(name, host64(g), r)
+        X, h_post, h_res = Xn, h_post_n, h_res_n
