@@ -380,14 +380,18 @@ int hc_post_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const flo
 
 // ------------------------------------------------------------------ xHC --
 
-static int64_t xhc_pre_ws(int64_t T, int N, int m, int with_router) {
+// xhc_pre workspace: projection rows P [T, N + router columns], ss [T], a private
+// h_pre [T, N]; then the fast path's packed phi and per-item partials.
+static int64_t xhc_pre_ws(int64_t T, int N, int64_t C, int m, int with_router, int dtype) {
   const int pcols = N + (with_router ? N - m : 0);
-  return align256(T * pcols * 4) + align256(T * 4) + align256(T * N * 4);
+  const hc::XhcFastWs f = hc::xhc_pre_fast_ws(T, N, C, m, with_router, dtype);
+  return align256(T * pcols * 4) + align256(T * 4) + align256(T * N * 4) + align256(f.packed) +
+         align256(f.partial);
 }
 
 int64_t xhc_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int with_router, int dtype) {
   if (T < 0 || N < 1 || N > HC_MAX_STREAMS || m < 1 || m > N || C < 1 || !dtype_ok(dtype)) return -1;
-  return xhc_pre_ws(T, N, m, with_router);
+  return xhc_pre_ws(T, N, C, m, with_router, dtype);
 }
 
 int xhc_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
@@ -407,7 +411,7 @@ int xhc_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
       (idx && !aligned_to(idx, 4)) || (score && !aligned_to(score, 4)))
     return HC_ERR_ALIGN;
   const int with_router = w_router != nullptr;
-  const int64_t wsb = xhc_pre_ws(T, N, m, with_router);
+  const int64_t wsb = xhc_pre_ws(T, N, C, m, with_router, dtype);
   if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
   const int64_t xb = T * N * C * (int64_t)es, fb = T * C * (int64_t)es;
   const void* outs[4] = {F_in, h_pre, with_router ? idx : nullptr, with_router ? score : nullptr};
@@ -430,20 +434,46 @@ int xhc_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
   float* ss = (float*)p;
   p += align256(T * 4);
   float* hp = h_pre ? h_pre : (float*)p;
-  hipError_t e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, phi_pre, N,
-                                         w_router, with_router ? N - m : 0, P, ss, st);
-  if (e != hipSuccess) return HC_ERR_LAUNCH;
-  e = hc::launch_xhc_select(P, pcols, 0, N, ss, (float)((double)N * (double)C), T, N, k, m, alpha_pre,
-                            b_pre, hp, with_router ? score : nullptr, with_router ? idx : nullptr, st);
+  p += align256(T * N * 4);
+  hipError_t e;
+  const hc::XhcFastWs f = hc::xhc_pre_fast_ws(T, N, C, m, with_router, dtype);
+  if (f.packed > 0 && aligned_to(X, 16)) {
+    void* packed = p;
+    float* partial = (float*)(p + align256(f.packed));
+    e = hc::launch_fast_xhc_full(X, T, N, C, k, m, phi_pre, b_pre, alpha_pre, w_router, hp, score, idx, packed,
+                                 partial, st);
+  } else {
+    e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, phi_pre, N, w_router,
+                                with_router ? N - m : 0, P, ss, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+    e = hc::launch_xhc_select(P, pcols, 0, N, ss, (float)((double)N * (double)C), T, N, k, m, alpha_pre,
+                              b_pre, hp, with_router ? score : nullptr, with_router ? idx : nullptr, st);
+  }
   if (e != hipSuccess) return HC_ERR_LAUNCH;
   return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X, F_in}), X, T, N, C, hp, F_in, st));
 }
 
-static int64_t xhc_route_ws(int64_t T, int N, int k, int m, int K, int with_router) {
+// xhc_route workspace: projection rows P [T, k*K + k*k], ss [T], H_post, H_res, and
+// with the router its rows and ss; then the fast paths' packed phi and per-item
+// partials (the router pass and the active pass run one after the other and
+// share them).
+static hc::XhcFastWs xhc_route_fast(int64_t T, int N, int64_t C, int k, int m, int K, int with_router,
+                                    int dtype) {
+  hc::XhcFastWs f = hc::xhc_route_fast_ws(T, C, k, K, dtype);
+  if (with_router) {
+    const hc::XhcFastWs r = hc::xhc_router_fast_ws(T, N, C, m, dtype);
+    f.packed = f.packed > r.packed ? f.packed : r.packed;
+    f.partial = f.partial > r.partial ? f.partial : r.partial;
+  }
+  return f;
+}
+
+static int64_t xhc_route_ws(int64_t T, int N, int64_t C, int k, int m, int K, int with_router, int dtype) {
   const int acols = k * K + k * k;
   int64_t b = align256(T * acols * 4) + align256(T * 4) + align256(T * k * K * 4) + align256(T * k * k * 4);
   if (with_router) b += align256(T * (N - m) * 4) + align256(T * 4);
-  return b;
+  const hc::XhcFastWs f = xhc_route_fast(T, N, C, k, m, K, with_router, dtype);
+  return b + align256(f.packed) + align256(f.partial);
 }
 
 int64_t xhc_route_workspace_bytes(int64_t T, int N, int64_t C, int k, int m, int K, int with_router,
@@ -451,7 +481,7 @@ int64_t xhc_route_workspace_bytes(int64_t T, int N, int64_t C, int k, int m, int
   if (T < 0 || N < 1 || N > HC_MAX_STREAMS || m < 1 || k < m || k > N || k > HC_MAX_ACTIVE || K < 1 ||
       K > HC_MAX_COMPONENTS || C < 1 || !dtype_ok(dtype))
     return -1;
-  return xhc_route_ws(T, N, k, m, K, with_router);
+  return xhc_route_ws(T, N, C, k, m, K, with_router, dtype);
 }
 
 int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, const float* w_router,
@@ -474,7 +504,7 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
       (h_post_out && !aligned_to(h_post_out, 4)) || (h_res_out && !aligned_to(h_res_out, 4)))
     return HC_ERR_ALIGN;
   const int with_router = idx_in == nullptr;
-  const int64_t wsb = xhc_route_ws(T, N, k, m, K, with_router);
+  const int64_t wsb = xhc_route_ws(T, N, C, k, m, K, with_router, dtype);
   if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
   const int acols = k * K + k * k;
   const int64_t xb = T * N * C * (int64_t)es;
@@ -504,26 +534,45 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
   p += align256(T * k * K * 4);
   float* Hr = h_res_out ? h_res_out : (float*)p;
   p += align256(T * k * k * 4);
+  float* Pr = nullptr;
+  float* ssf = nullptr;
+  if (with_router) {
+    Pr = (float*)p;
+    p += align256(T * (N - m) * 4);
+    ssf = (float*)p;
+    p += align256(T * 4);
+  }
+  const hc::XhcFastWs fw = xhc_route_fast(T, N, C, k, m, K, with_router, dtype);
+  void* packed = p;
+  float* partial = (float*)(p + align256(fw.packed));
+  const bool x16 = aligned_to(X, 16);
   hipError_t e;
   if (with_router) {
-    float* Pr = (float*)p;
-    p += align256(T * (N - m) * 4);
-    float* ssf = (float*)p;
-    e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, w_router, N - m, nullptr, 0,
-                                Pr, ssf, st);
-    if (e != hipSuccess) return HC_ERR_LAUNCH;
-    e = hc::launch_xhc_select(Pr, N - m, 0, 0, ssf, (float)((double)N * (double)C), T, N, k, m, 0.f,
-                              nullptr, nullptr, score_out, idx_out, st);
+    if (x16 && hc::xhc_router_fast_ws(T, N, C, m, dtype).packed > 0) {
+      e = hc::launch_fast_xhc_full(X, T, N, C, k, m, nullptr, nullptr, 0.f, w_router, nullptr, score_out, idx_out,
+                                   packed, partial, st);
+    } else {
+      e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, w_router, N - m, nullptr, 0,
+                                  Pr, ssf, st);
+      if (e != hipSuccess) return HC_ERR_LAUNCH;
+      e = hc::launch_xhc_select(Pr, N - m, 0, 0, ssf, (float)((double)N * (double)C), T, N, k, m, 0.f,
+                                nullptr, nullptr, score_out, idx_out, st);
+    }
     if (e != hipSuccess) return HC_ERR_LAUNCH;
   } else if (idx_out != idx_in) {
     e = hipMemcpyAsync(idx_out, idx_in, (size_t)(T * k * 4), hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return HC_ERR_LAUNCH;
   }
-  e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, k, idx_out, N, phi_act, acols, nullptr, 0,
-                              P, ss, st);
-  if (e != hipSuccess) return HC_ERR_LAUNCH;
-  e = hc::launch_coeff_epilogue(P, ss, (float)((double)k * (double)C), T, 0, k * K, k, 0.f, alpha_post,
-                                alpha_res, b_act, sinkhorn_iters, nullptr, Hp, Hr, st);
+  if (x16 && hc::xhc_route_fast_ws(T, C, k, K, dtype).packed > 0) {
+    e = hc::launch_fast_xhc_active(X, T, N, C, idx_out, K, phi_act, b_act, alpha_post, alpha_res, sinkhorn_iters,
+                                   Hp, Hr, packed, partial, st);
+  } else {
+    e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, k, idx_out, N, phi_act, acols, nullptr, 0,
+                                P, ss, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+    e = hc::launch_coeff_epilogue(P, ss, (float)((double)k * (double)C), T, 0, k * K, k, 0.f, alpha_post,
+                                  alpha_res, b_act, sinkhorn_iters, nullptr, Hp, Hr, st);
+  }
   if (e != hipSuccess) return HC_ERR_LAUNCH;
   return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, Wb}), X, T, N, C, k, idx_out, Hr, Hp,
                                               Wb, K, st));

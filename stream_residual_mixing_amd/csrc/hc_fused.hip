@@ -31,21 +31,27 @@ constexpr int TOK = 16;             // tokens per tile (MFMA M)
 
 // ------------------------------------------------------------- phi packing
 
-// One workgroup per 64 rows of phi [K][24] (K = 4C is a multiple of 128 on the
-// fast path): the rows are read coalesced into LDS, then thread (row group g of
-// 8, column c) writes the hi chunk (column c) and the lo chunk (column 24 + c),
-// 8 bf16 each.
-__global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__ phi, int64_t K,
+// phi_a [K, na] | phi_b [K, nb] (nb may be 0) -> the packed B-operand form: per
+// group of 8 rows, 2 ncolp columns of 8 bf16, columns 0..ncolp-1 hi = bf16(phi)
+// and ncolp..2 ncolp-1 lo = bf16(phi - hi); columns past na + nb are zero. One
+// workgroup per 64 rows (K is a multiple of 64 on the fast paths): the rows are
+// read into LDS, then thread (row group g, column c) writes the two chunks.
+__global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__ phi_a, int na,
+                                                       const float* __restrict__ phi_b, int nb, int ncolp,
                                                        uint16_t* __restrict__ packed) {
-  __shared__ float rows[64 * NCOL];
+  __shared__ float rows[64 * 32];
   const int64_t r0 = (int64_t)blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * NCOL; i += 256) rows[i] = phi[r0 * NCOL + i];
+  const int nc = na + nb;
+  for (int i = threadIdx.x; i < 64 * nc; i += 256) {
+    const int r = i / nc, c = i - r * nc;
+    rows[r * 32 + c] = c < na ? phi_a[(r0 + r) * na + c] : phi_b[(r0 + r) * nb + (c - na)];
+  }
   __syncthreads();
-  if (threadIdx.x >= 8 * NCOL) return;
-  const int g = threadIdx.x / NCOL, c = threadIdx.x - g * NCOL;
+  if ((int)threadIdx.x >= 8 * ncolp) return;
+  const int g = threadIdx.x / ncolp, c = threadIdx.x - g * ncolp;
   float p[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = rows[(g * 8 + e) * NCOL + c];
+  for (int e = 0; e < 8; ++e) p[e] = c < nc ? rows[(g * 8 + e) * 32 + c] : 0.f;
   uint32_t hi[4], lo[4];
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
@@ -54,9 +60,9 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__
     // p - hi is exact in float32
     lo[e / 2] = f2bf(p[e] - bf2f(h0)) | (f2bf(p[e + 1] - bf2f(h1)) << 16);
   }
-  uint4* out = reinterpret_cast<uint4*>(packed) + (r0 / 8 + g) * NCP;
+  uint4* out = reinterpret_cast<uint4*>(packed) + (r0 / 8 + g) * (2 * ncolp);
   out[c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  out[NCOL + c] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  out[ncolp + c] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
 // ---------------------------------------------------------- stream kernel
@@ -112,19 +118,34 @@ __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
   return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
 }
 
-// Work items: a tile of 32 tokens times a slice of SPI super-chunks (SPI * 256
-// channels of all 4 streams). Items are numbered tile-major and a persistent
-// grid of one workgroup per CU takes items blockIdx.x, blockIdx.x + grid, ...,
-// so at any moment the running workgroups cover a few adjacent tiles entirely:
-// a compact window of HBM. (Giving each workgroup a whole tile instead puts
-// 256 strips of 512 bytes per 8 KB stream row in flight across the whole
-// state, which streams about 10% slower.) Each item leaves its partial
-// projection, [32 tokens][24 columns | sum of squares] in float, in a
-// workspace; coeffs_finish_kernel adds an item's slices in a fixed order.
+// Work items: a tile of 32 tokens times a group of 4 streams times a slice of
+// SPI super-chunks (SPI * 256 channels). Items are numbered tile-major and a
+// persistent grid of one workgroup per CU takes items blockIdx.x, blockIdx.x +
+// grid, ..., so at any moment the running workgroups cover a few adjacent tiles
+// entirely: a compact window of HBM. (Giving each workgroup a whole tile
+// instead puts 256 strips of 512 bytes per 8 KB stream row in flight across
+// the whole state, which streams about 10% slower.) Each item leaves its
+// partial projection, [32 tokens][NB*8 columns | sum of squares] in float, in a
+// workspace; the finish kernels add a tile's items in a fixed order.
+//
+// Which 4 streams an item reads (MODE):
+//   ROWS_CONTIG: the token row is the 4 streams (mHC state [T, 4, C]);
+//   ROWS_GROUPS: streams 4g..4g+3 of a wider row (xHC full state [T, N, C],
+//                N = 4 NG), with phi rows of those streams;
+//   ROWS_GATHER: the streams idx[t, 0..3] of a token row (xHC active set), with
+//                phi rows of slots 0..3.
 constexpr int SPI = 4;                   // super-chunks per item
-constexpr int PROW = NCOL + 1;           // floats per token of a partial
-constexpr int PART = TILE * PROW;        // floats per item partial
 constexpr int NCOEF = TILE * 20;         // h_res (16) | h_post (4) per token of a tile
+enum : int { ROWS_CONTIG = 0, ROWS_GROUPS = 1, ROWS_GATHER = 2 };
+
+template <int NB>
+struct PartGeom {
+  static constexpr int NCP = NB * 16;    // packed hi | lo columns
+  static constexpr int NCOLP = NB * 8;   // logical columns (padded)
+  static constexpr int PROW = NCOLP + 1; // floats per token of a partial
+  static constexpr int PART = TILE * PROW;
+  static constexpr int NPEND = (PART + STHR - 1) / STHR;
+};
 
 // Buffer resource over [base, base + bytes): stores whose offset falls outside are
 // dropped by the hardware, so a guarded store needs no branch (a store behind a
@@ -132,14 +153,34 @@ constexpr int NCOEF = TILE * 20;         // h_res (16) | h_post (4) per token of
 constexpr unsigned BUF_DW3 = 0x00020000u;
 constexpr uint32_t OOB = 0x80000000u;  // any offset >= the range is dropped
 
-template <bool POST>
-__global__ __launch_bounds__(STHR) void mhc_split_kernel(
-    const uint16_t* X, int64_t T, int64_t C, int S, int nitem,
-    const float* __restrict__ h_res_in, const float* __restrict__ h_post_in,
-    const uint16_t* __restrict__ F, uint16_t* Y, const uint16_t* __restrict__ phi_p, float* part) {
+struct SplitArgs {
+  const uint16_t* X;
+  int64_t T, C;
+  int64_t rowstride;  // elements per token row of X
+  int NG, S, nitem;   // stream groups, slices per group, items
+  const int32_t* idx; // ROWS_GATHER: [T, kidx] stream indices (slots 0..3 used)
+  int kidx, nstreams; // idx row length; streams per row (indices are clamped into range)
+  const float* h_res_in;   // POST: [T, 16]
+  const float* h_post_in;  // POST: [T, 4]
+  const uint16_t* F;       // POST: [T, C]
+  uint16_t* Y;             // POST: [T, 4, C]
+  const uint16_t* phi_p;   // packed phi, NB * 16 columns
+  float* part;             // [nitem][TILE][PROW]
+};
+
+template <bool POST, int NB, int MODE>
+__global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
+  static_assert(!POST || MODE == ROWS_CONTIG, "the post/res write is for the mHC state");
+  static_assert(SPI >= 3, "the next item's stream table is written after the second super-chunk");
+  using PG = PartGeom<NB>;
+  constexpr int NCP = PG::NCP;
+  const uint16_t* X = A.X;
+  const int64_t T = A.T, C = A.C;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * LBUF];
   // coefficients of the tile being streamed and of the next item's tile
   __shared__ float coef[POST ? 2 * NCOEF : 1];
+  // stream indices of the tile being streamed and of the next item's tile
+  __shared__ __attribute__((aligned(16))) int gtab[MODE == ROWS_GATHER ? 2 * TILE * 4 : 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -150,51 +191,84 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(
   const int tau = lane & 15;
   const int q = lane >> 4;
   const int G = (int)gridDim.x;
-  const int nk = (nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
+  const int nk = (A.nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
+  const int per_tile = A.NG * A.S;
 
-  floatx4_t acc[2][3], gram[2];
+  floatx4_t acc[2][NB], gram[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 3; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
   const __amdgpu_buffer_rsrc_t pres =
-      __builtin_amdgcn_make_buffer_rsrc(part, 0, (uint32_t)((int64_t)nitem * PART * 4), BUF_DW3);
+      __builtin_amdgcn_make_buffer_rsrc(A.part, 0, (uint32_t)((int64_t)A.nitem * PG::PART * 4), BUF_DW3);
 
   // coefficient cidx (< NCOEF) of a tile; rows past T are clamped (never used)
   auto coef_val = [&](int tile, int cidx) __attribute__((always_inline)) {
     const int m = cidx / 20, e = cidx - m * 20;
     int64_t tt = (int64_t)tile * TILE + m;
     tt = tt < T ? tt : T - 1;
-    const float* src = e < 16 ? h_res_in + tt * 16 + e : h_post_in + tt * 4 + (e - 16);
+    const float* src = e < 16 ? A.h_res_in + tt * 16 + e : A.h_post_in + tt * 4 + (e - 16);
     return *src;
   };
   const int cidx1 = tid + STHR < NCOEF ? tid + STHR : NCOEF - 1;
+  // stream index (slot tid & 3 of token tid >> 2, tid < 128) of a tile, clamped into range
+  auto gidx_val = [&](int tile) __attribute__((always_inline)) {
+    const int tt0 = tid < TILE * 4 ? tid : TILE * 4 - 1;
+    int64_t tt = (int64_t)tile * TILE + (tt0 >> 2);
+    tt = tt < T ? tt : T - 1;
+    const int v = A.idx[tt * A.kidx + (tt0 & 3)];
+    return v < 0 ? 0 : (v >= A.nstreams ? A.nstreams - 1 : v);
+  };
+
+  // Item geometry: tile, stream group, first super-chunk.
+  struct Item {
+    int tile, g;
+    int64_t s0;
+  };
+  auto item_of = [&](int item) __attribute__((always_inline)) {
+    const int tile = item / per_tile;
+    const int r = item - tile * per_tile;
+    const int g = r / A.S;
+    return Item{tile, g, (int64_t)(r - g * A.S) * SPI};
+  };
 
   // Loads are unconditional: rows past T and channels past C are clamped to a
   // valid address and their values replaced by zeros (or their stores dropped),
   // so no load sits behind a branch and consecutive loads stay in flight together.
-  auto load_half = [&](int tile, int64_t s, auto P, uint4 (&xv)[NS4], uint4& fv) __attribute__((always_inline)) {
+  auto load_half = [&](const Item& it, int64_t s, const int* gt, auto P, uint4 (&xv)[NS4], uint4& fv)
+                       __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
-    int64_t t = (int64_t)tile * TILE + st_tok + 16 * p;
+    const int m = st_tok + 16 * p;
+    int64_t t = (int64_t)it.tile * TILE + m;
     t = t < T ? t : T - 1;
     const int64_t c = s * SC + st_c8;
     const int64_t cc = c < C ? c : C - 8;
-    const uint16_t* xr = X + t * (NS4 * C) + cc;
+    const uint16_t* xr = X + t * A.rowstride + cc;
+    if (MODE == ROWS_GATHER) {
+      const int4 sv = *reinterpret_cast<const int4*>(gt + m * 4);
+      xv[0] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.x * C);
+      xv[1] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.y * C);
+      xv[2] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.z * C);
+      xv[3] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.w * C);
+    } else {
+      const uint16_t* xg = xr + (int64_t)(MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
 #pragma unroll
-    for (int i = 0; i < NS4; ++i) xv[i] = *reinterpret_cast<const uint4*>(xr + i * C);
-    if (POST) fv = *reinterpret_cast<const uint4*>(F + t * C + cc);
+      for (int i = 0; i < NS4; ++i) xv[i] = *reinterpret_cast<const uint4*>(xg + i * C);
+    }
+    if (POST) fv = *reinterpret_cast<const uint4*>(A.F + t * C + cc);
   };
 
   // Streaming work of one token half: X_next (POST) and the bf16 tile it
   // projects, into LDS.
-  auto stream_half = [&](int tile, int64_t s, auto P, const uint4 (&xc)[NS4], const uint4& fc, unsigned char* buf,
-                         const float* cf, __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
+  auto stream_half = [&](const Item& it, int64_t s, auto P, const uint4 (&xc)[NS4], const uint4& fc,
+                         unsigned char* buf, const float* cf, __amdgpu_buffer_rsrc_t yres)
+                         __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     const int m = st_tok + 16 * p;
     const int64_t c = s * SC + st_c8;
-    const bool ok = ((int64_t)tile * TILE + m < T) && c < C;
+    const bool ok = ((int64_t)it.tile * TILE + m < T) && c < C;
     uint4 a_frag[NS4];
     if (POST) {
       const float* cm = cf + m * 20;
@@ -231,29 +305,30 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(
     for (int i = 0; i < NS4; ++i) *reinterpret_cast<uint4*>(buf + (i * TILE + m) * LROW + st_c8 * 2) = a_frag[i];
   };
 
-  // One super-chunk s of `tile`; (ptile, ps) is the super-chunk whose first
-  // token half is prefetched. Issue order: B fragments of the MFMA phase, the
-  // second token half, then (after the first half is computed) the prefetch, so
-  // waiting for the first half or for the B fragments never waits for loads
-  // issued later.
+  // One super-chunk s of item `it`; (nx, ns, ngt) is the super-chunk whose
+  // first token half is prefetched. Issue order: B fragments of the MFMA phase,
+  // the second token half, then (after the first half is computed) the
+  // prefetch, so waiting for the first half or for the B fragments never waits
+  // for loads issued later.
   uint4 xA[NS4], xB[NS4], fA = make_uint4(0, 0, 0, 0), fB = make_uint4(0, 0, 0, 0);
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  auto body = [&](int tile, int64_t s, int ptile, int64_t ps, unsigned char* buf, const float* cf,
-                  __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
+  auto body = [&](const Item& it, int64_t s, const int* gt, const Item& nx, int64_t ns, const int* ngt,
+                  unsigned char* buf, const float* cf, __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
     const int64_t cg = s * SC + wave * 32;
     const int64_t cgc = cg < C ? cg : C - 32;
-    uint4 pf[NS4][3];
+    const int64_t prow0 = (MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;  // phi row of stream 0 of the item
+    uint4 pf[NS4][NB];
 #pragma unroll
     for (int i = 0; i < NS4; ++i) {
-      const uint4* pb = reinterpret_cast<const uint4*>(phi_p) + ((i * C + cgc) / 8 + q) * NCP + tau;
+      const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + i * C + cgc) / 8 + q) * NCP + tau;
 #pragma unroll
-      for (int b = 0; b < 3; ++b) pf[i][b] = pb[b * 16];
+      for (int b = 0; b < NB; ++b) pf[i][b] = pb[b * 16];
     }
-    load_half(tile, s, H1{}, xB, fB);
-    stream_half(tile, s, H0{}, xA, fA, buf, cf, yres);
-    load_half(ptile, ps, H0{}, xA, fA);
-    stream_half(tile, s, H1{}, xB, fB, buf, cf, yres);
+    load_half(it, s, gt, H1{}, xB, fB);
+    stream_half(it, s, H0{}, xA, fA, buf, cf, yres);
+    load_half(nx, ns, ngt, H0{}, xA, fA);
+    stream_half(it, s, H1{}, xB, fB, buf, cf, yres);
     __syncthreads();
     // With POST, rows past T and channels past C hold values computed from
     // clamped loads (zeroing them before the store would turn the store into a
@@ -263,13 +338,13 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(
     const bool ch_ok = cg + q * 8 < C;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const bool a_ok = ch_ok && ((int64_t)tile * TILE + tb * TOK + tau < T);
+      const bool a_ok = ch_ok && ((int64_t)it.tile * TILE + tb * TOK + tau < T);
 #pragma unroll
       for (int i = 0; i < NS4; ++i) {
         uint4 af = *reinterpret_cast<const uint4*>(buf + (i * TILE + tb * TOK + tau) * LROW + (wave * 32 + q * 8) * 2);
         if (POST) af = keep_or_zero(a_ok, af);
 #pragma unroll
-        for (int b = 0; b < 3; ++b)
+        for (int b = 0; b < NB; ++b)
           acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pf[i][b]), acc[tb][b], 0, 0, 0);
         // A times its own transpose: the diagonal accumulates each token's sum of squares.
         gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
@@ -280,52 +355,67 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(
   };
 
   int item = (int)blockIdx.x;
-  int tile = item / S, slice = item - tile * S;
+  Item it = item_of(item);
   if (POST) {
-    coef[tid] = coef_val(tile, tid);
-    if (tid + STHR < NCOEF) coef[tid + STHR] = coef_val(tile, tid + STHR);
+    coef[tid] = coef_val(it.tile, tid);
+    if (tid + STHR < NCOEF) coef[tid + STHR] = coef_val(it.tile, tid + STHR);
   }
-  load_half(tile, (int64_t)slice * SPI, H0{}, xA, fA);
-  if (POST) __syncthreads();
+  if (MODE == ROWS_GATHER) {
+    const int v = gidx_val(it.tile);
+    if (tid < TILE * 4) gtab[tid] = v;
+  }
+  if (POST || MODE == ROWS_GATHER) __syncthreads();
+  load_half(it, it.s0, gtab, H0{}, xA, fA);
   // the partial sums this thread reduced for the previous item (pitem; -1: none)
-  float pend0 = 0.f, pend1 = 0.f;
+  float pend[PG::NPEND];
+#pragma unroll
+  for (int u = 0; u < PG::NPEND; ++u) pend[u] = 0.f;
   int pitem = -1;
-  const bool two = tid + STHR < PART;
   auto store_pending = [&]() __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)pitem * (uint32_t)(PART * 4);
-    const uint32_t off0 = pitem >= 0 ? base + (uint32_t)tid * 4 : OOB;
-    const uint32_t off1 = pitem >= 0 && two ? base + (uint32_t)(tid + STHR) * 4 : OOB;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend0), pres, off0, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend1), pres, off1, 0, 0);
+    const uint32_t base = (uint32_t)pitem * (uint32_t)(PG::PART * 4);
+#pragma unroll
+    for (int u = 0; u < PG::NPEND; ++u) {
+      const int o = tid + u * STHR;
+      const uint32_t off = pitem >= 0 && o < PG::PART ? base + (uint32_t)o * 4 : OOB;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend[u]), pres, off, 0, 0);
+    }
   };
   int step = 0;
   for (int k = 0; k < nk; ++k) {
     // the next item of this workgroup (this one again after the last: its first
     // super-chunk is then prefetched for nothing)
     const int nitem_k = k + 1 < nk ? item + G : item;
-    const int ntile = nitem_k / S, nslice = nitem_k - ntile * S;
+    const Item nx = item_of(nitem_k);
     const float* cf = coef + (k & 1) * NCOEF;
-    const int64_t nrow = (T - (int64_t)tile * TILE) < TILE ? (T - (int64_t)tile * TILE) : TILE;
+    const int* gt = gtab + (k & 1) * (TILE * 4);
+    const int* ngt = gtab + ((k + 1) & 1) * (TILE * 4);
+    const int64_t nrow = (T - (int64_t)it.tile * TILE) < TILE ? (T - (int64_t)it.tile * TILE) : TILE;
     const __amdgpu_buffer_rsrc_t yres = __builtin_amdgcn_make_buffer_rsrc(
-        POST ? Y + (int64_t)tile * TILE * (NS4 * C) : nullptr, 0, POST ? (uint32_t)(nrow * NS4 * C * 2) : 0u,
+        POST ? A.Y + (int64_t)it.tile * TILE * (NS4 * C) : nullptr, 0, POST ? (uint32_t)(nrow * NS4 * C * 2) : 0u,
         BUF_DW3);
-    const int64_t s0 = (int64_t)slice * SPI;
     float cn0 = 0.f, cn1 = 0.f;
+    int gn = 0;
     // SPI super-chunks, unrolled (past the last super-chunk of C they only add
     // zeros): straight-line code keeps the compiler's wait counts exact.
 #pragma unroll
     for (int j = 0; j < SPI; ++j) {
       const bool last = j + 1 == SPI;
-      body(tile, s0 + j, last ? ntile : tile, last ? (int64_t)nslice * SPI : s0 + j + 1,
+      body(it, it.s0 + j, gt, last ? nx : it, last ? nx.s0 : it.s0 + j + 1, last ? ngt : gt,
            lds + ((step + j) & 1) * LBUF, cf, yres);
       if (j == 0) {
         // after the first prefetch: the previous item's partial sums and the
-        // next item's coefficients
+        // next item's coefficients and stream indices
         store_pending();
         if (POST) {
-          cn0 = coef_val(ntile, tid);
-          cn1 = coef_val(ntile, cidx1);
+          cn0 = coef_val(nx.tile, tid);
+          cn1 = coef_val(nx.tile, cidx1);
         }
+        if (MODE == ROWS_GATHER) gn = gidx_val(nx.tile);
+      }
+      if (j == 1 && MODE == ROWS_GATHER) {
+        // used by the last super-chunk's prefetch, after the next barrier; the
+        // previous item read this buffer before its end barriers
+        if (tid < TILE * 4) gtab[((k + 1) & 1) * (TILE * 4) + tid] = gn;
       }
     }
     step += SPI;
@@ -338,7 +428,7 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int b = 0; b < 3; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           red[(wave * TILE + tb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
@@ -357,28 +447,30 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(
     for (int tb = 0; tb < 2; ++tb) {
       gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 3; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < NB; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
     auto reduce = [&](int o) __attribute__((always_inline)) {
-      const int m = o / PROW, col = o - m * PROW;
+      const int m = o / PG::PROW, col = o - m * PG::PROW;
       float sum = 0.f;
-      if (col < NCOL) {
+      if (col < PG::NCOLP) {
 #pragma unroll
         for (int w = 0; w < SWAVE; ++w)
-          sum += red[(w * TILE + m) * (NCP + 1) + col] + red[(w * TILE + m) * (NCP + 1) + NCOL + col];
+          sum += red[(w * TILE + m) * (NCP + 1) + col] + red[(w * TILE + m) * (NCP + 1) + PG::NCOLP + col];
       } else {
 #pragma unroll
         for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TILE + m];
       }
       return sum;
     };
-    pend0 = reduce(tid);
-    pend1 = reduce(two ? tid + STHR : tid);
+#pragma unroll
+    for (int u = 0; u < PG::NPEND; ++u) {
+      const int o = tid + u * STHR;
+      pend[u] = reduce(o < PG::PART ? o : tid);
+    }
     pitem = item;
     item = nitem_k;
-    tile = ntile;
-    slice = nslice;
+    it = nx;
   }
   store_pending();
 }
@@ -404,13 +496,14 @@ __device__ __forceinline__ float token_coeffs(const float* __restrict__ part, in
                                               const float* __restrict__ bias, Gate gate, int iters, bool store,
                                               float* __restrict__ h_pre_out, float* __restrict__ h_post_out,
                                               float* __restrict__ h_res_out) {
+  using PG = PartGeom<3>;
   const int64_t tile = tt / TILE;
   const int m = (int)(tt - tile * TILE);
-  const float* base = part + tile * S * PART + m * PROW;
+  const float* base = part + tile * S * PG::PART + m * PG::PROW;
   float ss = 0.f, pr = 0.f, pe = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float* b = base + (int64_t)s * PART;
-    ss += b[NCOL];
+    const float* b = base + (int64_t)s * PG::PART;
+    ss += b[PG::NCOLP];
     pr += b[8 + e];
     pe += b[e & 7];
   }
@@ -462,6 +555,124 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
                h_res_out);
 }
 
+// ------------------------------------------------------- xHC finish kernels
+
+// xHC full-state pass ([xHC] steps 1 and 2, parameterisation): 32 lanes per
+// token, lane c owns column c of the projection [pre npre | router nr]. Each
+// lane adds the token's items in order (column c and the sum of squares), then
+// r = sqrt(ss / (N C)); pre lanes: h_pre = sigmoid(alpha_pre P / r + b_pre);
+// router lanes: score = sigmoid(P / r). Selection (when nr > 0): k - m rounds
+// of an arg-max over the candidate lanes (equal scores go to the lower stream),
+// then idx = the m fixed streams and the chosen ones in ascending order.
+template <int NB>
+__global__ __launch_bounds__(256) void xpre_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C, int N,
+                                                          int per_tile, int npre, int nr, int k, int m,
+                                                          const float* __restrict__ b_pre, float a_pre,
+                                                          float* __restrict__ h_pre, float* __restrict__ score,
+                                                          int32_t* __restrict__ idx) {
+  using PG = PartGeom<NB>;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tt = g >> 5;
+  const int c = (int)(g & 31);
+  const int64_t tc = tt < T ? tt : T - 1;
+  const int64_t tile = tc / TILE;
+  const int mrow = (int)(tc - tile * TILE);
+  const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
+  const int cc = c < PG::NCOLP ? c : 0;
+  float ss = 0.f, pc = 0.f;
+  for (int it = 0; it < per_tile; ++it) {
+    const float* b = base + (int64_t)it * PG::PART;
+    ss += b[PG::NCOLP];
+    pc += b[cc];
+  }
+  const float r = sqrtf(ss / (float)((double)N * (double)C));
+  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  const bool valid = tt < T;
+  const bool is_pre = c < npre, is_rt = c >= npre && c < npre + nr;
+  if (valid && is_pre && h_pre) h_pre[tt * npre + c] = sigmoid(a_pre * (pc * invr) + b_pre[c]);
+  if (nr == 0) return;  // uniform over the launch
+  const float sc = sigmoid(pc * invr);
+  if (valid && is_rt) score[tt * nr + (c - npre)] = sc;
+  // arg-max rounds within the 32-lane group: (key, candidate) ordered by key,
+  // then by the lower candidate; the butterfly leaves the winner in every lane
+  float key = is_rt ? sc : -1.f;
+  const int cand = is_rt ? c - npre : 64;
+  uint64_t chosen = 0;
+  for (int round = 0; round < k - m; ++round) {
+    float bv = key;
+    int bl = cand;
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d, 32);
+      const int ol = __shfl_xor(bl, d, 32);
+      if (ov > bv || (ov == bv && ol < bl)) {
+        bv = ov;
+        bl = ol;
+      }
+    }
+    chosen |= 1ull << (m + bl);  // candidate j is stream m + j
+    if (cand == bl) key = -2.f;
+  }
+  if (valid && c < k) {
+    const uint64_t mask = chosen | ((m >= 64 ? ~0ull : (1ull << m) - 1));
+    int cnt = 0, v = 0;
+    for (int sidx = 0; sidx < N; ++sidx)
+      if ((mask >> sidx) & 1ull) {
+        if (cnt == c) v = sidx;
+        ++cnt;
+      }
+    idx[tt * k + c] = v;
+  }
+}
+
+// xHC active coefficients ([xHC] step 3, parameterisation) for k = 4: 16 lanes
+// per token. Columns [post k*K (a*K + j) | res 16 (a*4 + b)]. Each lane adds the
+// token's items in order, r_A = sqrt(ss / (4 C)); post lanes e < 4K: H_post =
+// 2 sigmoid(alpha_post P / r + b); H_res = Sinkhorn-Knopp(exp(alpha_res P / r +
+// b)) on the 4x4 block held by the 16 lanes (DPP exchanges as in mHC).
+template <int NB>
+__global__ __launch_bounds__(256) void xroute_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C,
+                                                            int per_tile, int K, const float* __restrict__ b_act,
+                                                            float a_post, float a_res, int iters,
+                                                            float* __restrict__ Hp, float* __restrict__ Hr) {
+  using PG = PartGeom<NB>;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tt = g >> 4;
+  const int e = (int)(g & 15);
+  const int64_t tc = tt < T ? tt : T - 1;
+  const int64_t tile = tc / TILE;
+  const int mrow = (int)(tc - tile * TILE);
+  const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
+  const int kK = 4 * K;
+  const int cpost = e < kK ? e : 0;
+  float ss = 0.f, pr = 0.f, pp = 0.f;
+  for (int it = 0; it < per_tile; ++it) {
+    const float* b = base + (int64_t)it * PG::PART;
+    ss += b[PG::NCOLP];
+    pr += b[kK + e];
+    pp += b[cpost];
+  }
+  const float r = sqrtf(ss / (float)(4.0 * (double)C));
+  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  const bool valid = tt < T;
+  if (valid && e < kK) Hp[tt * kK + e] = 2.0f * sigmoid(a_post * (pp * invr) + b_act[e]);
+  const float z = a_res * (pr * invr) + b_act[kK + e];
+  float zm = fmaxf(z, dpp<DPP_QXOR1>(z));
+  zm = fmaxf(zm, dpp<DPP_QXOR2>(zm));
+  zm = fmaxf(zm, dpp<DPP_ROR4>(zm));
+  zm = fmaxf(zm, dpp<DPP_ROR8>(zm));
+  float M = expf(z - zm);
+  for (int it = 0; it < iters; ++it) {
+    float cs = M + dpp<DPP_ROR8>(M);  // column sum over a
+    cs += dpp<DPP_ROR4>(cs);
+    M = M / cs;
+    float rs = M + dpp<DPP_QXOR1>(M);  // row sum over b
+    rs += dpp<DPP_QXOR2>(rs);
+    M = M / rs;
+  }
+  if (valid) Hr[tt * 16 + e] = M;
+}
+
 // --------------------------------------------------------------- pre-read
 
 // F_in[t, c] = sum_i h_pre[t, i] X[t, i, c] for n = 4 bf16; 8 channels per thread.
@@ -493,21 +704,24 @@ __global__ __launch_bounds__(256) void pre4_kernel(const uint16_t* __restrict__ 
 static inline bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 namespace {
-struct SplitGeom {
-  int S;      // items per tile
-  int nitem;  // tiles * S
+struct Geom {
+  int NG, S, nitem;  // stream groups, channel slices per group, items
 };
-SplitGeom split_geom(int64_t T, int64_t C) {
+Geom geom(int64_t T, int64_t C, int NG) {
   const int64_t nsc = (C + SC - 1) / SC;
   const int64_t S = (nsc + SPI - 1) / SPI;
-  return SplitGeom{(int)S, (int)(((T + TILE - 1) / TILE) * S)};
+  return Geom{NG, (int)S, (int)(((T + TILE - 1) / TILE) * NG * S)};
 }
 // the shapes the split kernel addresses with 32-bit buffer offsets and int item ids
-bool split_shape_ok(int64_t T, int64_t C) {
+bool shape_ok(int64_t T, int64_t C, int NG, int NB) {
   if (C % 32 != 0 || C < 32 || C >= (1ll << 24)) return false;
   const int64_t nsc = (C + SC - 1) / SC, S = (nsc + SPI - 1) / SPI;
-  return ((T + TILE - 1) / TILE) * S * PART * 4 < (1ll << 31);
+  return ((T + TILE - 1) / TILE) * NG * S * (TILE * (NB * 8 + 1)) * 4 < (1ll << 31);
 }
+int64_t part_bytes(int64_t T, int64_t C, int NG, int NB) {
+  return (int64_t)geom(T, C, NG).nitem * TILE * (NB * 8 + 1) * 4;
+}
+int nb_for(int ncols) { return ncols <= 16 ? 2 : (ncols <= 24 ? 3 : 4); }
 int grid_for(int nitem) {
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -515,56 +729,88 @@ int grid_for(int nitem) {
     ncu = 256;
   return nitem < ncu ? nitem : ncu;
 }
-}  // namespace
 
-int64_t fast_coeffs_packed_bytes(int n, int64_t C, int dtype) {
-  if (n != 4 || dtype != 1 || C % 32 != 0) return 0;
-  return (int64_t)n * C / 8 * NCP * 16;
+SplitArgs args(const void* X, int64_t T, int64_t C, int64_t rowstride, const Geom& g, const void* phi_p,
+               float* part) {
+  SplitArgs A{};
+  A.X = (const uint16_t*)X;
+  A.T = T;
+  A.C = C;
+  A.rowstride = rowstride;
+  A.NG = g.NG;
+  A.S = g.S;
+  A.nitem = g.nitem;
+  A.phi_p = (const uint16_t*)phi_p;
+  A.part = part;
+  return A;
 }
 
-int64_t fast_coeffs_partial_bytes(int64_t T, int n, int64_t C, int dtype) {
-  if (n != 4 || dtype != 1 || !split_shape_ok(T, C)) return 0;
-  return (int64_t)split_geom(T, C).nitem * PART * 4;
-}
-
-bool fast_coeffs_supported(int dtype, int n, int64_t T, int64_t C, const void* X) {
-  return dtype == 1 && n == 4 && split_shape_ok(T, C) && a16(X);
-}
-
-bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y) {
-  return dtype == 1 && n == 4 && C % 32 == 0 && C >= 32 && a16(X) && a16(F) && a16(Y);
-}
-
-static hipError_t launch_pack(const float* phi, int64_t K, void* packed, hipStream_t st) {
-  hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)(K / 64)), dim3(256), 0, st, phi, K, (uint16_t*)packed);
+template <bool POST, int NB, int MODE>
+hipError_t launch_split(const SplitArgs& A, hipStream_t st) {
+  hipLaunchKernelGGL((mhc_split_kernel<POST, NB, MODE>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
   return hipGetLastError();
 }
 
-static hipError_t launch_finish(const float* part, int64_t T, int64_t C, int S, const float* bias, Gate gate,
-                                int iters, float* h_pre, float* h_post, float* h_res, hipStream_t st) {
+template <int MODE>
+hipError_t launch_split_nb(int nb, const SplitArgs& A, hipStream_t st) {
+  switch (nb) {
+    case 2: return launch_split<false, 2, MODE>(A, st);
+    case 3: return launch_split<false, 3, MODE>(A, st);
+    default: return launch_split<false, 4, MODE>(A, st);
+  }
+}
+
+hipError_t launch_pack(const float* phi_a, int na, const float* phi_b, int nb, int64_t K, int ncolp, void* packed,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)(K / 64)), dim3(256), 0, st, phi_a, na, phi_b, nb, ncolp,
+                     (uint16_t*)packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(const float* part, int64_t T, int64_t C, int S, const float* bias, Gate gate, int iters,
+                         float* h_pre, float* h_post, float* h_res, hipStream_t st) {
   const int64_t threads = T * 16;
   hipLaunchKernelGGL(coeffs_finish_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, T, C, S,
                      bias, gate, iters, h_pre, h_post, h_res);
   return hipGetLastError();
 }
 
-static hipError_t launch_pre4(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
+hipError_t launch_pre4(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
   const int64_t work = T * (C / 8);
   hipLaunchKernelGGL(pre4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, (const uint16_t*)X, T,
                      C, h_pre, (uint16_t*)F_in);
   return hipGetLastError();
+}
+}  // namespace
+
+// ------------------------------------------------------------------ mHC
+
+int64_t fast_coeffs_packed_bytes(int n, int64_t C, int dtype) {
+  if (n != 4 || dtype != 1 || C % 32 != 0) return 0;
+  return (int64_t)n * C / 8 * 48 * 16;
+}
+
+int64_t fast_coeffs_partial_bytes(int64_t T, int n, int64_t C, int dtype) {
+  if (n != 4 || dtype != 1 || !shape_ok(T, C, 1, 3)) return 0;
+  return part_bytes(T, C, 1, 3);
+}
+
+bool fast_coeffs_supported(int dtype, int n, int64_t T, int64_t C, const void* X) {
+  return dtype == 1 && n == 4 && shape_ok(T, C, 1, 3) && a16(X);
+}
+
+bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y) {
+  return dtype == 1 && n == 4 && C % 32 == 0 && C >= 32 && a16(X) && a16(F) && a16(Y);
 }
 
 hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const float* phi,
                                   const float* bias, float a_pre, float a_post, float a_res,
                                   int iters, float* h_pre, float* h_post, float* h_res, void* F_in,
                                   void* packed, float* partial, hipStream_t st) {
-  hipError_t e = launch_pack(phi, 4 * C, packed, st);
+  hipError_t e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st);
   if (e != hipSuccess) return e;
-  const SplitGeom g = split_geom(T, C);
-  hipLaunchKernelGGL(mhc_split_kernel<false>, dim3(grid_for(g.nitem)), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
-                     g.S, g.nitem, nullptr, nullptr, nullptr, nullptr, (const uint16_t*)packed, partial);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const Geom g = geom(T, C, 1);
+  if ((e = launch_split<false, 3, ROWS_CONTIG>(args(X, T, C, 4 * C, g, packed, partial), st)) != hipSuccess) return e;
   e = launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, st);
   if (e != hipSuccess || !F_in) return e;
   return launch_pre4(X, T, C, h_pre, F_in, st);
@@ -581,21 +827,101 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
                                    void* F_in_n, void* packed, float* partial, hipStream_t st) {
   hipError_t e;
   if (!phi_packed) {
-    if ((e = launch_pack(phi, 4 * C, packed, st)) != hipSuccess) return e;
+    if ((e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st)) != hipSuccess) return e;
     phi_packed = packed;
   }
-  const SplitGeom g = split_geom(T, C);
-  hipLaunchKernelGGL(mhc_split_kernel<true>, dim3(grid_for(g.nitem)), dim3(STHR), 0, st, (const uint16_t*)X, T, C,
-                     g.S, g.nitem, h_res, h_post, (const uint16_t*)F, (uint16_t*)Y, (const uint16_t*)phi_packed,
-                     partial);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const Geom g = geom(T, C, 1);
+  SplitArgs A = args(X, T, C, 4 * C, g, phi_packed, partial);
+  A.h_res_in = h_res;
+  A.h_post_in = h_post;
+  A.F = (const uint16_t*)F;
+  A.Y = (uint16_t*)Y;
+  if ((e = launch_split<true, 3, ROWS_CONTIG>(A, st)) != hipSuccess) return e;
   e = launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n, h_res_n, st);
   if (e != hipSuccess || !F_in_n) return e;
   return launch_pre4(Y, T, C, h_pre_n, F_in_n, st);
 }
 
 hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream_t st) {
-  return launch_pack(phi, 4 * C, packed, st);
+  return launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st);
+}
+
+// ------------------------------------------------------------------ xHC
+
+XhcFastWs xhc_pre_fast_ws(int64_t T, int N, int64_t C, int m, bool with_router, int dtype) {
+  const int ncols = N + (with_router ? N - m : 0);
+  if (dtype != 1 || N % 4 != 0 || N > 16 || ncols > 32 || !shape_ok(T, C, N / 4, nb_for(ncols))) return {0, 0};
+  const int nb = nb_for(ncols);
+  return {(int64_t)N * C / 8 * (nb * 16) * 16, part_bytes(T, C, N / 4, nb)};
+}
+
+XhcFastWs xhc_router_fast_ws(int64_t T, int N, int64_t C, int m, int dtype) {
+  const int nr = N - m;
+  if (dtype != 1 || N % 4 != 0 || N > 16 || nr > 32 || !shape_ok(T, C, N / 4, nb_for(nr))) return {0, 0};
+  const int nb = nb_for(nr);
+  return {(int64_t)N * C / 8 * (nb * 16) * 16, part_bytes(T, C, N / 4, nb)};
+}
+
+XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype) {
+  const int ncols = k * K + k * k;
+  if (dtype != 1 || k != 4 || ncols > 32 || !shape_ok(T, C, 1, nb_for(ncols))) return {0, 0};
+  const int nb = nb_for(ncols);
+  return {(int64_t)k * C / 8 * (nb * 16) * 16, part_bytes(T, C, 1, nb)};
+}
+
+hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int k, int m, const float* phi_pre,
+                                const float* b_pre, float a_pre, const float* w_router, float* h_pre, float* score,
+                                int32_t* idx, void* packed, float* partial, hipStream_t st) {
+  const int npre = phi_pre ? N : 0, nr = w_router ? N - m : 0;
+  const int nb = nb_for(npre + nr);
+  hipError_t e = phi_pre ? launch_pack(phi_pre, N, w_router, nr, (int64_t)N * C, nb * 8, packed, st)
+                         : launch_pack(w_router, nr, nullptr, 0, (int64_t)N * C, nb * 8, packed, st);
+  if (e != hipSuccess) return e;
+  const Geom g = geom(T, C, N / 4);
+  if ((e = launch_split_nb<ROWS_GROUPS>(nb, args(X, T, C, (int64_t)N * C, g, packed, partial), st)) != hipSuccess)
+    return e;
+  const int64_t threads = T * 32;
+  const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
+  const int per_tile = g.NG * g.S;
+  switch (nb) {
+    case 2:
+      hipLaunchKernelGGL(xpre_finish_kernel<2>, grid, blk, 0, st, partial, T, C, N, per_tile, npre, nr, k, m, b_pre,
+                         a_pre, h_pre, score, idx);
+      break;
+    case 3:
+      hipLaunchKernelGGL(xpre_finish_kernel<3>, grid, blk, 0, st, partial, T, C, N, per_tile, npre, nr, k, m, b_pre,
+                         a_pre, h_pre, score, idx);
+      break;
+    default:
+      hipLaunchKernelGGL(xpre_finish_kernel<4>, grid, blk, 0, st, partial, T, C, N, per_tile, npre, nr, k, m, b_pre,
+                         a_pre, h_pre, score, idx);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
+                                  const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
+                                  float* Hp, float* Hr, void* packed, float* partial, hipStream_t st) {
+  const int ncols = 4 * K + 16;
+  const int nb = nb_for(ncols);
+  hipError_t e = launch_pack(phi_act, ncols, nullptr, 0, 4 * C, nb * 8, packed, st);
+  if (e != hipSuccess) return e;
+  const Geom g = geom(T, C, 1);
+  SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);
+  A.idx = idx;
+  A.kidx = 4;
+  A.nstreams = N;
+  if ((e = launch_split_nb<ROWS_GATHER>(nb, A, st)) != hipSuccess) return e;
+  const int64_t threads = T * 16;
+  const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
+  if (nb == 3)
+    hipLaunchKernelGGL(xroute_finish_kernel<3>, grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, iters,
+                       Hp, Hr);
+  else
+    hipLaunchKernelGGL(xroute_finish_kernel<4>, grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, iters,
+                       Hp, Hr);
+  return hipGetLastError();
 }
 
 }  // namespace hc

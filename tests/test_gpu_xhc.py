@@ -286,3 +286,53 @@ def test_augment_one_hot_taps_pin_order_and_padding():
     torch.cuda.synchronize()
     ref = O.xhc_augment(F, [w], B, S)
     check_fp32("V one-hot", host64(V), ref)
+
+
+# ------------------------------------ shapes of the MFMA paths (bf16, C % 32 == 0)
+
+@pytest.mark.parametrize("N,m,C,T", [(8, 2, 96, 45), (12, 3, 288, 33), (16, 2, 1024, 70), (4, 1, 32, 64)])
+def test_fast_full_state_pass_shapes(N, m, C, T):
+    """xhc_pre over stream groups of 4: several N, ragged T, C not a multiple of the
+    256-channel super-chunk; h_pre, scores, indices (bit-exact) and F_in."""
+    k = min(4, N)
+    note(f"xHC xhc_pre N={N} k={k} m={m} C={C} T={T} bf16")
+    inp = _xhc_inputs(50 + N, T, N, k, m, C, 1)
+    X = dev(inp["X"])
+    pre = hc.xhc_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], dev(inp["w_router"]), k, m)
+    torch.cuda.synchronize()
+    _check_pre(inp, k, m, pre)
+    note(f"xHC xhc_pre N={N} without router")
+    pre2 = hc.xhc_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], None, k, m)
+    torch.cuda.synchronize()
+    assert torch.equal(pre2["h_pre"], pre["h_pre"]) and torch.equal(pre2["F_in"], pre["F_in"])
+
+
+@pytest.mark.parametrize("K,C,T", [(1, 96, 29), (2, 64, 40), (3, 320, 17), (4, 4096, 33)])
+def test_fast_route_shapes(K, C, T):
+    """xhc_route with k = 4 gathered streams for K = 1..4 write-back components, with
+    supplied indices and with the router inside."""
+    N, k, m = 8, 4, 1
+    note(f"xHC xhc_route N={N} k=4 K={K} C={C} T={T} bf16")
+    inp = _xhc_inputs(60 + K, T, N, k, m, C, 1)
+    rng = np.random.default_rng(70 + K)
+    Wb = synth.Tensor(rng.standard_normal((T, K, C)).astype(np.float32), synth.BF16)
+    phi_act = (0.02 * rng.standard_normal((k * C, k * K + k * k))).astype(np.float32)
+    b_act = np.concatenate([np.zeros(k * K), np.eye(k).reshape(-1)]).astype(np.float32)
+    inp = dict(inp, phi_act=phi_act, b_act=b_act)
+    idx = np.array([sorted(rng.choice(N, k, replace=False)) for _ in range(T)], np.int32)
+    X = dev(inp["X"])
+    out = hc.xhc_route(X, dev(Wb), dev(phi_act), dev(b_act), 0.01, 0.01, k=k, m=m, idx=dev(idx),
+                       want_coeffs=True)
+    torch.cuda.synchronize()
+    _check_route(inp["X"].values.astype(np.float64), inp, idx.astype(np.int64), Wb.values.astype(np.float64),
+                 X, out)
+    note(f"xHC xhc_route N={N} K={K} with the router inside")
+    X2 = dev(inp["X"])
+    out2 = hc.xhc_route(X2, dev(Wb), dev(phi_act), dev(b_act), 0.01, 0.01, k=k, m=m, w_router=dev(inp["w_router"]),
+                        want_coeffs=True)
+    torch.cuda.synchronize()
+    s_ref = O.xhc_router_scores(inp["X"].values, inp["w_router"])
+    np.testing.assert_array_equal(out2["idx"].cpu().numpy(), O.xhc_select(s_ref, k, m))
+    check_fp32("route score", host64(out2["score"]), s_ref)
+    _check_route(inp["X"].values.astype(np.float64), inp, out2["idx"].cpu().numpy().astype(np.int64),
+                 Wb.values.astype(np.float64), X2, out2)
