@@ -242,6 +242,10 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
               int32_t* idx_out, float* score_out, float* h_post_out, float* h_res_out,
               void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Workspace bytes needed by xhc_augment (0 when it needs none); -1 for invalid sizes. */
+int64_t xhc_augment_workspace_bytes(int64_t B, int64_t S, int64_t C, const int* kappa, int r, int dtype,
+                                    int v_dtype);
+
 /*
  * xhc_augment - temporal feature augmentation ([xHC] temporal feature
  * augmentation; kernel sizes {4, 8, 12} in [xHC-R]):
@@ -250,14 +254,18 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
  *   zeros before the start of each sequence (w_j[c, kappa_j - 1] weights the
  *   current token); then Gram-Schmidt (modified form, no normalisation):
  *   V[t, 0] = F_out[t]; V[t, j] = g_j minus its projections on V[t, 0..j-1],
- *   removed one after another.
+ *   removed one after another. (For kappa = {4, 8, 12} the projections are
+ *   formed from each token's 4x4 Gram matrix, which gives the same vectors in
+ *   exact arithmetic.)
  *   F_out [T, C] stream dtype `dtype`; conv_w = [C, kappa_1] then [C, kappa_2] ...
  *   float32; kappa: HOST array of r kernel sizes (1..32); 0 <= r <= 7;
  *   V [T, r + 1, C] in `v_dtype`.
+ *   Workspace: xhc_augment_workspace_bytes(B, S, C, kappa, r, dtype, v_dtype)
+ *   (may be NULL when that is 0).
  */
 int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
                 const float* conv_w, const int* kappa, int r,
-                void* V, int v_dtype, void* stream);
+                void* V, int v_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

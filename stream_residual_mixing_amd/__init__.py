@@ -48,7 +48,8 @@ _SIGS = {
     "xhc_route": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp,
                            _c_float, _c_float, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64,
                            _vp]),
-    "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp]),
+    "xhc_augment_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int, _c_int]),
+    "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
 }
 
 _lib = None
@@ -310,7 +311,13 @@ def xhc_route(X, Wb, phi_act, b_act, alpha_post, alpha_res, *, k=4, m=2, idx=Non
     return out
 
 
-def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, stream=None):
+def xhc_augment_workspace_bytes(batch, seq, C, kappas, dtype, v_dtype=None) -> int:
+    karr = (ctypes.c_int * max(len(kappas), 1))(*[int(x) for x in kappas])
+    vdt = dtype if v_dtype is None else v_dtype
+    return int(lib().xhc_augment_workspace_bytes(batch, seq, C, karr, len(kappas), _DT[dtype], _DT[vdt]))
+
+
+def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, workspace=None, stream=None):
     """V [T, r+1, C] = Gram-Schmidt([F_out; causal depthwise convs]); conv_w concatenated fp32."""
     F_out = _dev_tensor(F_out, "F_out", _DT)
     T, C = F_out.shape
@@ -321,8 +328,11 @@ def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, stream=None)
     V = torch.empty(T, r + 1, C, dtype=vdt, device=F_out.device)
     karr = (ctypes.c_int * max(r, 1))(*[int(x) for x in kappas])
     w = _f32(conv_w, "conv_w") if r > 0 else None
+    nbytes = int(lib().xhc_augment_workspace_bytes(batch, seq, C, karr, r, _DT[F_out.dtype], _DT[vdt]))
+    ws = _workspace(nbytes, F_out.device, workspace) if nbytes > 0 else None
     _check("xhc_augment", lib().xhc_augment(_ptr(F_out), _DT[F_out.dtype], batch, seq, C, _ptr(w), karr, r,
-                                            _ptr(V), _DT[vdt], _stream(F_out.device, stream)))
+                                            _ptr(V), _DT[vdt], _ptr(ws), 0 if ws is None else ws.numel(),
+                                            _stream(F_out.device, stream)))
     return V
 
 
@@ -330,5 +340,5 @@ __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
     "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
-    "xhc_route", "xhc_augment",
+    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment",
 ]

@@ -578,13 +578,12 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
                                               Wb, K, st));
 }
 
-int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, const float* conv_w,
-                const int* kappa, int r, void* V, int v_dtype, void* stream) {
-  if (!dtype_ok(dtype) || !dtype_ok(v_dtype)) return HC_ERR_DTYPE;
+static int augment_spec(int64_t B, int64_t S, int64_t C, const int* kappa, int r, hc::ConvSpec& spec,
+                        int64_t& wtot) {
   if (B < 0 || S < 0 || C < 1 || C > (1ll << 26) || r < 0 || r > HC_MAX_COMPONENTS - 1) return HC_ERR_SHAPE;
   if (r > 0 && !kappa) return HC_ERR_NULL;
-  int64_t wtot = 0;
-  hc::ConvSpec spec{};
+  wtot = 0;
+  spec = hc::ConvSpec{};
   spec.r = r;
   for (int j = 0; j < r; ++j) {
     if (kappa[j] < 1 || kappa[j] > HC_MAX_KAPPA) return HC_ERR_SHAPE;
@@ -592,17 +591,52 @@ int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, c
     spec.offset[j] = wtot;
     wtot += C * kappa[j];
   }
-  if (hc::augment_generic_lds_bytes(r, C) > 160 * 1024 - 1024) return HC_ERR_SHAPE;
+  return HC_OK;
+}
+
+static bool augment_fast_shape(int64_t C, const int* kappa, int r) {
+  return r == 3 && kappa[0] == 4 && kappa[1] == 8 && kappa[2] == 12 && C % 4 == 0;
+}
+
+int64_t xhc_augment_workspace_bytes(int64_t B, int64_t S, int64_t C, const int* kappa, int r, int dtype,
+                                    int v_dtype) {
+  if (!dtype_ok(dtype) || !dtype_ok(v_dtype)) return -1;
+  hc::ConvSpec spec;
+  int64_t wtot;
+  if (augment_spec(B, S, C, kappa, r, spec, wtot) != HC_OK) return -1;
+  return augment_fast_shape(C, kappa, r) ? hc::fast_augment_workspace_bytes(B, S, C) : 0;
+}
+
+int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, const float* conv_w,
+                const int* kappa, int r, void* V, int v_dtype, void* workspace, int64_t workspace_bytes,
+                void* stream) {
+  if (!dtype_ok(dtype) || !dtype_ok(v_dtype)) return HC_ERR_DTYPE;
+  hc::ConvSpec spec;
+  int64_t wtot;
+  int s = augment_spec(B, S, C, kappa, r, spec, wtot);
+  if (s != HC_OK) return s;
+  const bool fast_shape = augment_fast_shape(C, kappa, r);
+  if (!fast_shape && hc::augment_generic_lds_bytes(r, C) > 160 * 1024 - 1024) return HC_ERR_SHAPE;
   const int64_t T = B * S;
   if (T == 0) return HC_OK;
   if (!F_out || !V || (r > 0 && !conv_w)) return HC_ERR_NULL;
   if (!aligned_to(F_out, esize(dtype)) || !aligned_to(V, esize(v_dtype)) || (conv_w && !aligned_to(conv_w, 4)))
     return HC_ERR_ALIGN;
   const int64_t vb = T * (r + 1) * C * (int64_t)esize(v_dtype);
-  if (overlaps(V, vb, F_out, T * C * (int64_t)esize(dtype)) || overlaps(V, vb, conv_w, wtot * 4))
-    return HC_ERR_ALIAS;
-  int s = device_status();
-  if (s != HC_OK) return s;
+  const int64_t fb = T * C * (int64_t)esize(dtype);
+  if (overlaps(V, vb, F_out, fb) || overlaps(V, vb, conv_w, wtot * 4)) return HC_ERR_ALIAS;
+  const int64_t wsb = fast_shape ? hc::fast_augment_workspace_bytes(B, S, C) : 0;
+  if (wsb > 0) {
+    if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+    if (overlaps(workspace, wsb, V, vb) || overlaps(workspace, wsb, F_out, fb) ||
+        overlaps(workspace, wsb, conv_w, wtot * 4))
+      return HC_ERR_ALIAS;
+  }
+  if ((s = device_status()) != HC_OK) return s;
+  if (fast_shape && hc::fast_augment_supported(dtype, v_dtype, C, kappa, r, F_out, V))
+    return launch_status(hc::launch_fast_augment(dtype, v_dtype, F_out, B, S, C, conv_w, V, (float*)workspace,
+                                                 (hipStream_t)stream));
+  if (hc::augment_generic_lds_bytes(r, C) > 160 * 1024 - 1024) return HC_ERR_SHAPE;
   return launch_status(hc::launch_augment_generic(dtype, v_dtype, F_out, B, S, C, conv_w, spec, V,
                                                   (hipStream_t)stream));
 }

@@ -1,0 +1,317 @@
+// Temporal feature augmentation for the configuration of the xHC summary
+// (K_r = 4: F_out and causal depthwise convs with kappa = 4, 8, 12), in two
+// passes over F_out.
+//
+// [xHC] temporal feature augmentation: g_j[t, c] = sum_{s < kappa_j}
+// w_j[c, s] F[t - kappa_j + 1 + s, c] with zeros before each sequence start,
+// then Gram-Schmidt of a_0 = F, a_1..a_3 = g_1..g_3:
+//   v_0 = a_0,  v_j = a_j - sum_{i<j} (<a_j, v_i> / <v_i, v_i>) v_i.
+// The pages name the modified form, which equals this one in exact arithmetic.
+// Every inner product here is a combination of the entries of the 4x4 Gram
+// matrix G = [<a_i, a_j>] of the token: writing v_j = sum_k B[j][k] a_k,
+//   <a_j, v_i> = sum_k B[i][k] G[k][j],  <v_i, v_i> = B_i^T G B_i,
+// so the first pass only accumulates G (per token, per 1024-channel slice) and
+// the second pass rebuilds B (in float64) and writes V = B A. The full-C
+// reductions then need no workgroup to hold a token's whole row. (In float32
+// this matches float64 modified Gram-Schmidt to about 3e-8 relative L2 on
+// data of this shape, as the float32 modified form does.)
+//
+// Workgroup: 256 threads x 4 channels = a 1024-channel slice, over a strip of
+// 36 consecutive tokens of one sequence; each thread keeps its channels' 24
+// conv taps and the last 12 rows of F in registers, so F is read once per pass
+// (plus an 11-row halo per strip).
+#include <type_traits>
+
+#include "hc_device.h"
+#include "hc_fast.h"
+
+namespace hc {
+
+namespace {
+
+constexpr int K1 = 4, K2 = 8, K3 = 12;
+constexpr int ATT = 3 * K3;         // tokens per strip (a multiple of the ring length)
+constexpr int ACH = 4;              // channels per thread
+constexpr int ACS = 256 * ACH;      // channels per workgroup
+constexpr int NG10 = 10;            // upper triangle of the 4x4 Gram matrix
+constexpr int NB6 = 6;              // strictly lower part of B
+
+template <typename TF>
+__device__ __forceinline__ void ld4(const TF* p, float v[4]);
+template <>
+__device__ __forceinline__ void ld4<float>(const float* p, float v[4]) {
+  const float4 q = *reinterpret_cast<const float4*>(p);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+template <>
+__device__ __forceinline__ void ld4<bf16_t>(const bf16_t* p, float v[4]) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+template <typename TV>
+__device__ __forceinline__ void st4(TV* p, const float v[4]);
+template <>
+__device__ __forceinline__ void st4<float>(float* p, const float v[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const float v[4]) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+}
+
+// Sum over the 16 lanes of a DPP row (every lane gets it).
+__device__ __forceinline__ float row_sum16(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  v += dpp(v, std::integral_constant<int, 0x124>{});  // row_ror:4
+  v += dpp(v, std::integral_constant<int, 0x128>{});  // row_ror:8
+  return v;
+}
+
+// Where a workgroup works: sequence b, token positions [p0, p1), channels c0..c0+3
+// of its thread (cok: inside C; C % 4 == 0).
+struct Place {
+  int64_t b, p0, p1, c0;
+  bool cok;
+};
+__device__ __forceinline__ Place place(int64_t S, int64_t C, int nstrip, int nslice) {
+  const int slice = (int)(blockIdx.x % nslice);
+  const int64_t rest = blockIdx.x / nslice;
+  const int64_t strip = rest % nstrip;
+  Place pl;
+  pl.b = rest / nstrip;
+  pl.p0 = strip * ATT;
+  pl.p1 = pl.p0 + ATT < S ? pl.p0 + ATT : S;
+  const int64_t c = (int64_t)slice * ACS + threadIdx.x * ACH;
+  pl.cok = c < C;
+  pl.c0 = pl.cok ? c : 0;
+  return pl;
+}
+
+// The taps of the three convs for channels c0..c0+3 (w: [C, 4] | [C, 8] | [C, 12]).
+struct Taps {
+  float w1[K1][ACH], w2[K2][ACH], w3[K3][ACH];
+};
+__device__ __forceinline__ void load_taps(const float* __restrict__ w, int64_t C, int64_t c0, Taps& tp) {
+#pragma unroll
+  for (int ch = 0; ch < ACH; ++ch) {
+    const float* p1 = w + (c0 + ch) * K1;
+    const float* p2 = w + K1 * C + (c0 + ch) * K2;
+    const float* p3 = w + (K1 + K2) * C + (c0 + ch) * K3;
+#pragma unroll
+    for (int s = 0; s < K1; ++s) tp.w1[s][ch] = p1[s];
+#pragma unroll
+    for (int s = 0; s < K2; ++s) tp.w2[s][ch] = p2[s];
+#pragma unroll
+    for (int s = 0; s < K3; ++s) tp.w3[s][ch] = p3[s];
+  }
+}
+
+// Walks the strip's tokens in order with the last 12 rows of F (this thread's
+// channels) in a register ring: row p sits in slot (p - p0) mod 12 (p0 is a
+// multiple of 12), so with the walk unrolled by 12 every slot index is a
+// compile-time constant. Row p + 1 is loaded before token p is computed and
+// moved into the ring afterwards (its slot still holds row p - 11, the oldest
+// tap of token p). fn(p, u, a) receives a[0..3][ch] = F, g1, g2, g3 of token p
+// (zeros past C); u = (p - p0) mod 12.
+template <typename TF, typename Fn>
+__device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, int64_t C, const Place& pl,
+                                           const Taps& tp, Fn fn) {
+  const TF* base = F + pl.b * S * C + pl.c0;
+  auto row = [&](int64_t p, float v[ACH]) __attribute__((always_inline)) {
+    const int64_t pc = p < 0 ? 0 : (p < S ? p : S - 1);
+    ld4<TF>(base + pc * C, v);
+    if (p < 0) {
+#pragma unroll
+      for (int ch = 0; ch < ACH; ++ch) v[ch] = 0.f;
+    }
+  };
+  float ring[K3][ACH];
+#pragma unroll
+  for (int s = 1; s < K3; ++s) row(pl.p0 - K3 + s, ring[s]);  // rows p0-11 .. p0-1 in slots 1..11
+  row(pl.p0, ring[0]);
+  for (int64_t pb = pl.p0; pb < pl.p1; pb += K3) {
+#pragma unroll
+    for (int u = 0; u < K3; ++u) {
+      const int64_t p = pb + u;
+      if (p >= pl.p1) break;
+      float nxt[ACH];
+      row(p + 1, nxt);
+      float a[4][ACH];
+#pragma unroll
+      for (int ch = 0; ch < ACH; ++ch) {
+        // tap s of a kappa-wide conv reads row p - kappa + 1 + s, in slot (u + 1 + s + 12 - kappa) mod 12
+        float g1 = 0.f, g2 = 0.f, g3 = 0.f;
+#pragma unroll
+        for (int s = 0; s < K1; ++s) g1 += tp.w1[s][ch] * ring[(u + 1 + s + K3 - K1) % K3][ch];
+#pragma unroll
+        for (int s = 0; s < K2; ++s) g2 += tp.w2[s][ch] * ring[(u + 1 + s + K3 - K2) % K3][ch];
+#pragma unroll
+        for (int s = 0; s < K3; ++s) g3 += tp.w3[s][ch] * ring[(u + 1 + s) % K3][ch];
+        a[0][ch] = pl.cok ? ring[u][ch] : 0.f;
+        a[1][ch] = pl.cok ? g1 : 0.f;
+        a[2][ch] = pl.cok ? g2 : 0.f;
+        a[3][ch] = pl.cok ? g3 : 0.f;
+      }
+      fn(p, u, a);
+#pragma unroll
+      for (int ch = 0; ch < ACH; ++ch) ring[(u + 1) % K3][ch] = nxt[ch];
+    }
+  }
+}
+
+// Pass 1: partial Gram matrices gram[t][slice][10] (upper triangle, row-major).
+template <typename TF>
+__global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
+                                                       const float* __restrict__ w, int nstrip, int nslice,
+                                                       float* __restrict__ gram) {
+  __shared__ float red[ATT][NG10][16];  // [token][entry][row of 16 lanes]
+  const Place pl = place(S, C, nstrip, nslice);
+  Taps tp;
+  load_taps(w, C, pl.c0, tp);
+  const int lane = threadIdx.x & 63, rowid = threadIdx.x >> 4;
+  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, int, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+    int q = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = i; j < 4; ++j) {
+        float sacc = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < ACH; ++ch) sacc += a[i][ch] * a[j][ch];
+        sacc = row_sum16(sacc);
+        if ((lane & 15) == 0) red[p - pl.p0][q][rowid] = sacc;
+        ++q;
+      }
+  });
+  __syncthreads();
+  const int slice = (int)(blockIdx.x % nslice);
+  const int n = (int)(pl.p1 - pl.p0) * NG10;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int tk = i / NG10, k = i - tk * NG10;
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v += red[tk][k][r];
+    gram[((pl.b * S + pl.p0 + tk) * nslice + slice) * NG10 + k] = v;
+  }
+}
+
+// Pass 2: thread i < strip length builds B of token p0 + i from its Gram matrix
+// (slices added in order, float64) into LDS; then V[t, j] = a_j + sum_{k<j}
+// B[j][k] a_k.
+template <typename TF, typename TV>
+__global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
+                                                        const float* __restrict__ w, int nstrip, int nslice,
+                                                        const float* __restrict__ gram, TV* __restrict__ V) {
+  __shared__ float Bs[ATT][NB6];
+  const Place pl = place(S, C, nstrip, nslice);
+  if ((int64_t)threadIdx.x < pl.p1 - pl.p0) {
+    const int64_t t = pl.b * S + pl.p0 + threadIdx.x;
+    double G[4][4];
+    double gs[NG10];
+#pragma unroll
+    for (int k = 0; k < NG10; ++k) gs[k] = 0.0;
+    for (int sl = 0; sl < nslice; ++sl) {
+      const float* gp = gram + (t * nslice + sl) * NG10;
+#pragma unroll
+      for (int k = 0; k < NG10; ++k) gs[k] += (double)gp[k];
+    }
+    int q = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = i; j < 4; ++j) {
+        G[i][j] = gs[q];
+        G[j][i] = gs[q];
+        ++q;
+      }
+    // rows B_j of v_j = sum_k B[j][k] a_k; <a_j, v_i> = B_i . G[:, j], <v_i, v_i> = B_i^T G B_i
+    double Bm[4][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}};
+    double vv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int i = 0; i < j; ++i) {
+        double num = 0.0;
+#pragma unroll
+        for (int k = 0; k <= i; ++k) num += Bm[i][k] * G[k][j];
+        const double cji = num / vv[i];
+#pragma unroll
+        for (int k = 0; k <= i; ++k) Bm[j][k] -= cji * Bm[i][k];
+      }
+      double qf = 0.0;
+#pragma unroll
+      for (int k = 0; k <= j; ++k)
+#pragma unroll
+        for (int l = 0; l <= j; ++l) qf += Bm[j][k] * G[k][l] * Bm[j][l];
+      vv[j] = qf;
+    }
+    float* out = Bs[threadIdx.x];
+    out[0] = (float)Bm[1][0];
+    out[1] = (float)Bm[2][0];
+    out[2] = (float)Bm[2][1];
+    out[3] = (float)Bm[3][0];
+    out[4] = (float)Bm[3][1];
+    out[5] = (float)Bm[3][2];
+  }
+  __syncthreads();
+  Taps tp;
+  load_taps(w, C, pl.c0, tp);
+  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, int, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+    if (!pl.cok) return;
+    const float* bq = Bs[p - pl.p0];
+    const int64_t t = pl.b * S + p;
+    float v[ACH];
+    st4<TV>(V + (t * 4 + 0) * C + pl.c0, a[0]);
+#pragma unroll
+    for (int ch = 0; ch < ACH; ++ch) v[ch] = a[1][ch] + bq[0] * a[0][ch];
+    st4<TV>(V + (t * 4 + 1) * C + pl.c0, v);
+#pragma unroll
+    for (int ch = 0; ch < ACH; ++ch) v[ch] = a[2][ch] + bq[1] * a[0][ch] + bq[2] * a[1][ch];
+    st4<TV>(V + (t * 4 + 2) * C + pl.c0, v);
+#pragma unroll
+    for (int ch = 0; ch < ACH; ++ch) v[ch] = a[3][ch] + bq[3] * a[0][ch] + bq[4] * a[1][ch] + bq[5] * a[2][ch];
+    st4<TV>(V + (t * 4 + 3) * C + pl.c0, v);
+  });
+}
+
+template <typename TF, typename TV>
+hipError_t launch_aug(const void* F, int64_t B, int64_t S, int64_t C, const float* w, void* V, float* gram,
+                      hipStream_t st) {
+  const int nstrip = (int)((S + ATT - 1) / ATT);
+  const int nslice = (int)((C + ACS - 1) / ACS);
+  const dim3 grid((unsigned)(B * nstrip * nslice)), blk(256);
+  hipLaunchKernelGGL(aug_gram_kernel<TF>, grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((aug_apply_kernel<TF, TV>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice,
+                     (const float*)gram, (TV*)V);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fast_augment_supported(int dtype, int vdtype, int64_t C, const int* kappa, int r, const void* F,
+                            const void* V) {
+  if (r != 3 || kappa[0] != K1 || kappa[1] != K2 || kappa[2] != K3 || C % 4 != 0) return false;
+  const uintptr_t fa = dtype == 0 ? 16 : 8, va = vdtype == 0 ? 16 : 8;
+  return ((uintptr_t)F % fa) == 0 && ((uintptr_t)V % va) == 0;
+}
+
+int64_t fast_augment_workspace_bytes(int64_t B, int64_t S, int64_t C) {
+  return B * S * ((C + ACS - 1) / ACS) * NG10 * 4;
+}
+
+hipError_t launch_fast_augment(int dtype, int vdtype, const void* F, int64_t B, int64_t S, int64_t C,
+                               const float* w, void* V, float* gram, hipStream_t st) {
+  if (dtype == 0 && vdtype == 0) return launch_aug<float, float>(F, B, S, C, w, V, gram, st);
+  if (dtype == 0) return launch_aug<float, bf16_t>(F, B, S, C, w, V, gram, st);
+  if (vdtype == 0) return launch_aug<bf16_t, float>(F, B, S, C, w, V, gram, st);
+  return launch_aug<bf16_t, bf16_t>(F, B, S, C, w, V, gram, st);
+}
+
+}  // namespace hc

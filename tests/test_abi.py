@@ -139,10 +139,20 @@ def test_validation_rejects_bad_arguments_before_device_work(hc):
     assert xroute(idx=None, w=None) == -1
 
     karr = (ctypes.c_int * 3)(4, 8, 40)
-    assert L.xhc_augment(FAKE, 1, 2, 16, 64, FAKE, karr, 3, ctypes.c_void_p(0x600000), 1, None) == -2
+    aug = lambda karr, r, dt=1, ws=ctypes.c_void_p(0x700000), wsb=1 << 20: L.xhc_augment(
+        FAKE, dt, 2, 16, 64, FAKE, karr, r, ctypes.c_void_p(0x600000), 1, ws, wsb, None)
+    assert aug(karr, 3) == -2
     karr = (ctypes.c_int * 3)(4, 8, 12)
-    assert L.xhc_augment(FAKE, 1, 2, 16, 64, FAKE, karr, 8, ctypes.c_void_p(0x600000), 1, None) == -2
-    assert L.xhc_augment(FAKE, 5, 2, 16, 64, FAKE, karr, 3, ctypes.c_void_p(0x600000), 1, None) == -3
+    assert aug(karr, 8) == -2
+    assert aug(karr, 3, dt=5) == -3
+    # kappa = {4, 8, 12} takes a workspace of per-token Gram matrices
+    wsa = L.xhc_augment_workspace_bytes(2, 16, 64, karr, 3, 1, 1)
+    assert wsa == 2 * 16 * 1 * 10 * 4
+    assert aug(karr, 3, ws=None, wsb=0) == -8
+    assert aug(karr, 3, wsb=wsa - 1) == -8
+    assert aug(karr, 3, ws=ctypes.c_void_p(0x600100)) == -5  # workspace inside V
+    assert L.xhc_augment_workspace_bytes(2, 16, 64, karr, 2, 1, 1) == 0
+    assert L.xhc_augment_workspace_bytes(2, 16, 64, karr, 3, 9, 1) == -1
 
 
 @pytest.mark.skipif(have_gpu(), reason="checks the no-device status; on a GPU box the call would run")
