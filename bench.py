@@ -80,6 +80,107 @@ def algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
     return {"hc_coeffs_pre": cp, "hc_post": post, "hc_pre": pre, "hc_post_coeffs": pc, "hc_post_pre": pp}
 
 
+def xhc_algorithmic_bytes(T: int, N: int, C: int, k: int, m: int, K: int, esize: int = 2) -> dict:
+    """Minimum bytes of each xHC call (counted once per launch; weights once).
+
+    xhc_pre: read the full state X (N C per token) once, write F_in (C) and the
+    k indices + N - m scores; phi_pre and W_r once.
+    xhc_route (indices given): read the k active rows and the K write-back
+    components, write the k active rows back; the k indices; phi_act once.
+    xhc_augment: read F_out (C), write V (K C)."""
+    pre = T * (N * C * esize + C * esize + k * 4 + (N - m) * 4) + N * C * (N + N - m) * 4
+    route = T * (2 * k * C * esize + K * C * esize + k * 4) + k * C * (k * K + k * k) * 4
+    aug = T * (C * esize + K * C * esize) + C * (4 + 8 + 12) * 4
+    return {"xhc_pre": pre, "xhc_route": route, "xhc_augment": aug}
+
+
+def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
+    """Throughput of the xHC sublayer (N=16, k=4, m=2, C=4096, T=8192, bf16) on
+    seeded synthetic device data: the routed step xhc_pre + xhc_route (K=1, F_out
+    written back) and the augmented step xhc_pre + xhc_augment + xhc_route (K=4,
+    B=2 S=4096), three rotating state sets, HIP events around every call."""
+    N, k, m, C, T = 16, 4, 2, 4096, 8192
+    B, S = 2, 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(3000)
+    rn = lambda *shape, std=1.0: torch.randn(*shape, device=dev, generator=g) * std
+    Xs = [rn(T, N, C).to(torch.bfloat16) for _ in range(3)]
+    Fs = [rn(T, C).to(torch.bfloat16) for _ in range(3)]
+    phi_pre, b_pre = rn(N * C, N, std=0.02), torch.zeros(N, device=dev)
+    w_r = rn(N * C, N - m, std=(1.0 / (N * C)) ** 0.5)
+
+    def act(K):
+        b = torch.zeros(k * K + k * k, device=dev)
+        b[k * K:] = torch.eye(k, device=dev).flatten()
+        return rn(k * C, k * K + k * k, std=0.02), b
+
+    phi1, b1 = act(1)
+    phi4, b4 = act(4)
+    conv = torch.cat([rn(C, kk, std=(1.0 / kk) ** 0.5) for kk in (4, 8, 12)], 1).contiguous()
+    ab1 = xhc_algorithmic_bytes(T, N, C, k, m, 1)
+    ab4 = xhc_algorithmic_bytes(T, N, C, k, m, 4)
+    ws_pre = torch.empty(hc.xhc_pre_workspace_bytes(T, N, C, m, True, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(max(hc.xhc_route_workspace_bytes(T, N, C, k, m, K, False, torch.bfloat16) for K in (1, 4)),
+                       dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(hc.xhc_augment_workspace_bytes(B, S, C, (4, 8, 12), torch.bfloat16), dtype=torch.uint8,
+                       device=dev)
+
+    def run(step, names):
+        for i in range(warmup):
+            step(i, None)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        return wall, {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e-3 for j, nm in
+                      enumerate(names)}
+
+    def routed(i, evs):
+        X = Xs[i % 3]
+        if evs:
+            evs[0].record()
+        pre = hc.xhc_pre(X, phi_pre, b_pre, 0.01, w_r, k, m, want_h_pre=False, workspace=ws_pre)
+        if evs:
+            evs[1].record()
+        hc.xhc_route(X, Fs[i % 3], phi1, b1, 0.01, 0.01, k=k, m=m, idx=pre["idx"], workspace=ws_r)
+        if evs:
+            evs[2].record()
+
+    def augmented(i, evs):
+        X = Xs[i % 3]
+        if evs:
+            evs[0].record()
+        pre = hc.xhc_pre(X, phi_pre, b_pre, 0.01, w_r, k, m, want_h_pre=False, workspace=ws_pre)
+        if evs:
+            evs[1].record()
+        V = hc.xhc_augment(Fs[i % 3], conv, (4, 8, 12), B, S, workspace=ws_a)
+        if evs:
+            evs[2].record()
+        hc.xhc_route(X, V, phi4, b4, 0.01, 0.01, k=k, m=m, idx=pre["idx"], workspace=ws_r)
+        if evs:
+            evs[3].record()
+
+    out = {}
+    for name, fn, calls, ab in (("routed_K1", routed, ["xhc_pre", "xhc_route"], ab1),
+                                ("augmented_K4", augmented, ["xhc_pre", "xhc_augment", "xhc_route"], ab4)):
+        wall, kern = run(fn, calls)
+        step_bytes = sum(ab[c] for c in calls)
+        total = sum(kern.values())
+        out[name] = {
+            "tokens_per_s": T / total, "us_per_step": total * 1e6, "wall_us_per_step": wall * 1e6,
+            "algorithmic_bytes_per_step": step_bytes,
+            "achieved_GBps": step_bytes / total / 1e9, "pct_hbm_peak": 100.0 * step_bytes / total / 1e9 / HBM_PEAK_GBPS,
+            "calls": {c: {"us": kern[c] * 1e6, "algorithmic_bytes": ab[c], "achieved_GBps": ab[c] / kern[c] / 1e9,
+                          "pct_hbm_peak": 100.0 * ab[c] / kern[c] / 1e9 / HBM_PEAK_GBPS} for c in calls},
+        }
+    out["workload"] = ("xHC N=16 k=4 m=2 C=4096 T=8192 bf16 (K=1: F_out written back; K=4: B=2 S=4096 "
+                       "augmentation, kappa 4,8,12); seeded synthetic device data; durations from HIP events")
+    return out
+
+
 def load_traffic(kernel: str, digest: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -125,6 +226,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-xhc", action="store_true", help="skip the xHC measurements")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -295,6 +397,8 @@ def main() -> int:
                                   algorithmic_bytes_per_step=iso_bytes),
         "source_digest": digest,
     }
+    if not args.no_xhc:
+        result["xhc"] = xhc_bench(torch, hc, dev, max(3, min(args.steps, 20)), 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

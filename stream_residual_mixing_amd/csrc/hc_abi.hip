@@ -437,11 +437,12 @@ int xhc_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
   p += align256(T * N * 4);
   hipError_t e;
   const hc::XhcFastWs f = hc::xhc_pre_fast_ws(T, N, C, m, with_router, dtype);
-  if (f.packed > 0 && aligned_to(X, 16)) {
+  if (f.packed > 0 && aligned_to(X, 16) && aligned_to(F_in, 16)) {
     void* packed = p;
     float* partial = (float*)(p + align256(f.packed));
-    e = hc::launch_fast_xhc_full(X, T, N, C, k, m, phi_pre, b_pre, alpha_pre, w_router, hp, score, idx, packed,
-                                 partial, st);
+    e = hc::launch_fast_xhc_full(X, T, N, C, k, m, phi_pre, b_pre, alpha_pre, w_router, hp, score, idx, F_in,
+                                 packed, partial, st);
+    return launch_status(e);
   } else {
     e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, phi_pre, N, w_router,
                                 with_router ? N - m : 0, P, ss, st);
@@ -550,7 +551,7 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
   if (with_router) {
     if (x16 && hc::xhc_router_fast_ws(T, N, C, m, dtype).packed > 0) {
       e = hc::launch_fast_xhc_full(X, T, N, C, k, m, nullptr, nullptr, 0.f, w_router, nullptr, score_out, idx_out,
-                                   packed, partial, st);
+                                   nullptr, packed, partial, st);
     } else {
       e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, N, nullptr, N, w_router, N - m, nullptr, 0,
                                   Pr, ssf, st);

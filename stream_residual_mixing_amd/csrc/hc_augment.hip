@@ -114,13 +114,17 @@ __device__ __forceinline__ void load_taps(const float* __restrict__ w, int64_t C
 // Walks the strip's tokens in order with the last 12 rows of F (this thread's
 // channels) in a register ring: row p sits in slot (p - p0) mod 12 (p0 is a
 // multiple of 12), so with the walk unrolled by 12 every slot index is a
-// compile-time constant. Row p + 1 is loaded before token p is computed and
-// moved into the ring afterwards (its slot still holds row p - 11, the oldest
-// tap of token p). fn(p, u, a) receives a[0..3][ch] = F, g1, g2, g3 of token p
-// (zeros past C); u = (p - p0) mod 12.
+// compile-time constant. Rows are loaded PF tokens ahead into a small queue
+// (slot (p - p0) mod PF) and moved into the ring once the token PF - 1 places
+// earlier is done (the ring slot they take still holds row p - 11, the oldest
+// tap of that token). fn(p, a) receives a[0..3][ch] = F, g1, g2, g3 of token p
+// (zeros past C).
+constexpr int PF = 4;  // rows in flight (divides 12)
+
 template <typename TF, typename Fn>
 __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, int64_t C, const Place& pl,
                                            const Taps& tp, Fn fn) {
+  static_assert(K3 % PF == 0, "the queue slot of a row must be a compile-time constant");
   const TF* base = F + pl.b * S * C + pl.c0;
   auto row = [&](int64_t p, float v[ACH]) __attribute__((always_inline)) {
     const int64_t pc = p < 0 ? 0 : (p < S ? p : S - 1);
@@ -131,16 +135,18 @@ __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, 
     }
   };
   float ring[K3][ACH];
+  float q[PF][ACH];
 #pragma unroll
   for (int s = 1; s < K3; ++s) row(pl.p0 - K3 + s, ring[s]);  // rows p0-11 .. p0-1 in slots 1..11
   row(pl.p0, ring[0]);
+#pragma unroll
+  for (int d = 1; d < PF; ++d) row(pl.p0 + d, q[d]);  // rows p0+1 .. p0+PF-1
   for (int64_t pb = pl.p0; pb < pl.p1; pb += K3) {
 #pragma unroll
     for (int u = 0; u < K3; ++u) {
       const int64_t p = pb + u;
       if (p >= pl.p1) break;
-      float nxt[ACH];
-      row(p + 1, nxt);
+      row(p + PF, q[u % PF]);  // the slot of row p, already in the ring
       float a[4][ACH];
 #pragma unroll
       for (int ch = 0; ch < ACH; ++ch) {
@@ -157,9 +163,9 @@ __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, 
         a[2][ch] = pl.cok ? g2 : 0.f;
         a[3][ch] = pl.cok ? g3 : 0.f;
       }
-      fn(p, u, a);
+      fn(p, a);
 #pragma unroll
-      for (int ch = 0; ch < ACH; ++ch) ring[(u + 1) % K3][ch] = nxt[ch];
+      for (int ch = 0; ch < ACH; ++ch) ring[(u + 1) % K3][ch] = q[(u + 1) % PF][ch];
     }
   }
 }
@@ -174,7 +180,7 @@ __global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F,
   Taps tp;
   load_taps(w, C, pl.c0, tp);
   const int lane = threadIdx.x & 63, rowid = threadIdx.x >> 4;
-  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, int, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
     int q = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -261,7 +267,7 @@ __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F
   __syncthreads();
   Taps tp;
   load_taps(w, C, pl.c0, tp);
-  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, int, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
     if (!pl.cok) return;
     const float* bq = Bs[p - pl.p0];
     const int64_t t = pl.b * S + p;

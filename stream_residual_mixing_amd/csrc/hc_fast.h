@@ -46,10 +46,11 @@ XhcFastWs xhc_router_fast_ws(int64_t T, int N, int64_t C, int m, int dtype);
 // active-set projection: k == 4, k*K + k*k <= 32
 XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype);
 // Full-state pass: h_pre (phi_pre != nullptr) and/or router scores + selection
-// (w_router != nullptr) from one MFMA projection over all N streams.
+// (w_router != nullptr) from one MFMA projection over all N streams, and when
+// F_in != nullptr the pre-read (h_pre then required).
 hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int k, int m, const float* phi_pre,
                                 const float* b_pre, float a_pre, const float* w_router, float* h_pre, float* score,
-                                int32_t* idx, void* packed, float* partial, hipStream_t st);
+                                int32_t* idx, void* F_in, void* packed, float* partial, hipStream_t st);
 // Active coefficients H_post [T, 4, K], H_res [T, 4, 4] of the streams idx[t, 0..3].
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
                                   const float* phi_act, const float* b_act, float a_post, float a_res, int iters,

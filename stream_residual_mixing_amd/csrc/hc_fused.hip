@@ -17,6 +17,7 @@
 
 #include "hc_device.h"
 #include "hc_fast.h"
+#include "hc_launch.h"
 
 namespace hc {
 
@@ -869,15 +870,11 @@ XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype) {
   return {(int64_t)k * C / 8 * (nb * 16) * 16, part_bytes(T, C, 1, nb)};
 }
 
-hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int k, int m, const float* phi_pre,
-                                const float* b_pre, float a_pre, const float* w_router, float* h_pre, float* score,
-                                int32_t* idx, void* packed, float* partial, hipStream_t st) {
-  const int npre = phi_pre ? N : 0, nr = w_router ? N - m : 0;
-  const int nb = nb_for(npre + nr);
-  hipError_t e = phi_pre ? launch_pack(phi_pre, N, w_router, nr, (int64_t)N * C, nb * 8, packed, st)
-                         : launch_pack(w_router, nr, nullptr, 0, (int64_t)N * C, nb * 8, packed, st);
-  if (e != hipSuccess) return e;
+static hipError_t xhc_full_proj(const void* X, int64_t T, int N, int64_t C, int k, int m, int npre, int nr, int nb,
+                                 const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
+                                 const void* packed, float* partial, hipStream_t st) {
   const Geom g = geom(T, C, N / 4);
+  hipError_t e;
   if ((e = launch_split_nb<ROWS_GROUPS>(nb, args(X, T, C, (int64_t)N * C, g, packed, partial), st)) != hipSuccess)
     return e;
   const int64_t threads = T * 32;
@@ -898,6 +895,19 @@ hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int 
       break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int k, int m, const float* phi_pre,
+                                const float* b_pre, float a_pre, const float* w_router, float* h_pre, float* score,
+                                int32_t* idx, void* F_in, void* packed, float* partial, hipStream_t st) {
+  const int npre = phi_pre ? N : 0, nr = w_router ? N - m : 0;
+  const int nb = nb_for(npre + nr);
+  hipError_t e = phi_pre ? launch_pack(phi_pre, N, w_router, nr, (int64_t)N * C, nb * 8, packed, st)
+                         : launch_pack(w_router, nr, nullptr, 0, (int64_t)N * C, nb * 8, packed, st);
+  if (e != hipSuccess) return e;
+  e = xhc_full_proj(X, T, N, C, k, m, npre, nr, nb, b_pre, a_pre, h_pre, score, idx, packed, partial, st);
+  if (e != hipSuccess || !F_in) return e;
+  return launch_pre_generic(1, true, X, T, N, C, h_pre, F_in, st);
 }
 
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
