@@ -148,6 +148,15 @@ struct PartGeom {
   static constexpr int NPEND = (PART + STHR - 1) / STHR;
 };
 
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{})
+template <int N, typename Fn, int I = 0>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, Fn, I + 1>(static_cast<Fn&&>(f));
+  }
+}
+
 // Buffer resource over [base, base + bytes): stores whose offset falls outside are
 // dropped by the hardware, so a guarded store needs no branch (a store behind a
 // branch makes the compiler's wait counts conservative at the merge).
@@ -314,23 +323,10 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
   uint4 xA[NS4], xB[NS4], fA = make_uint4(0, 0, 0, 0), fB = make_uint4(0, 0, 0, 0);
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  auto body = [&](const Item& it, int64_t s, const int* gt, const Item& nx, int64_t ns, const int* ngt,
-                  unsigned char* buf, const float* cf, __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
+  // MFMA phase of super-chunk s from the tile in `buf`, B fragments pf.
+  auto mfma_phase = [&](const Item& it, int64_t s, const unsigned char* buf, const uint4 (&pf)[NS4][NB])
+                        __attribute__((always_inline)) {
     const int64_t cg = s * SC + wave * 32;
-    const int64_t cgc = cg < C ? cg : C - 32;
-    const int64_t prow0 = (MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;  // phi row of stream 0 of the item
-    uint4 pf[NS4][NB];
-#pragma unroll
-    for (int i = 0; i < NS4; ++i) {
-      const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + i * C + cgc) / 8 + q) * NCP + tau;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) pf[i][b] = pb[b * 16];
-    }
-    load_half(it, s, gt, H1{}, xB, fB);
-    stream_half(it, s, H0{}, xA, fA, buf, cf, yres);
-    load_half(nx, ns, ngt, H0{}, xA, fA);
-    stream_half(it, s, H1{}, xB, fB, buf, cf, yres);
-    __syncthreads();
     // With POST, rows past T and channels past C hold values computed from
     // clamped loads (zeroing them before the store would turn the store into a
     // branch): their A fragments are replaced by zeros here. Without POST the
@@ -355,6 +351,63 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     // buffer only after passing the next barrier, i.e. after these reads.
   };
 
+  auto body = [&](const Item& it, int64_t s, const int* gt, const Item& nx, int64_t ns, const int* ngt,
+                  unsigned char* buf, const float* cf, __amdgpu_buffer_rsrc_t yres) __attribute__((always_inline)) {
+    const int64_t cg = s * SC + wave * 32;
+    const int64_t cgc = cg < C ? cg : C - 32;
+    const int64_t prow0 = (MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;  // phi row of stream 0 of the item
+    uint4 pf[NS4][NB];
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + i * C + cgc) / 8 + q) * NCP + tau;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) pf[i][b] = pb[b * 16];
+    }
+    load_half(it, s, gt, H1{}, xB, fB);
+    stream_half(it, s, H0{}, xA, fA, buf, cf, yres);
+    load_half(nx, ns, ngt, H0{}, xA, fA);
+    stream_half(it, s, H1{}, xB, fB, buf, cf, yres);
+    __syncthreads();
+    mfma_phase(it, s, buf, pf);
+  };
+
+  // Without POST the streaming work is only the copy into LDS, so more of the
+  // state can be in flight: a queue of 4 token halves, filled 2 super-chunks
+  // ahead. Half h of an item (h = 2 j + p) uses queue slot h mod 4 (an item
+  // has 2 SPI halves, a multiple of 4, so the slot is a compile-time constant);
+  // once half h is in LDS its slot is refilled with half h + 4, which for the
+  // last 4 halves is one of the next item's first 4.
+  constexpr bool DEEP = !POST && !(MODE == ROWS_GATHER && NB >= 4);  // (the latter has no registers left)
+  static_assert(2 * SPI % 4 == 0, "queue slots of the deep prefetch");
+  uint4 xq[DEEP ? 4 : 1][NS4];
+  auto body_deep = [&](const Item& it, auto J, const int* gt, const Item& nx, const int* ngt, unsigned char* buf)
+                       __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    constexpr int h0 = 2 * j, h1 = 2 * j + 1;
+    constexpr int q0 = DEEP ? h0 % 4 : 0, q1 = DEEP ? h1 % 4 : 0;
+    const int64_t s = it.s0 + j;
+    const int64_t cg = s * SC + wave * 32;
+    const int64_t cgc = cg < C ? cg : C - 32;
+    const int64_t prow0 = (MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
+    uint4 pf[NS4][NB];
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + i * C + cgc) / 8 + q) * NCP + tau;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) pf[i][b] = pb[b * 16];
+    }
+    uint4 fz = make_uint4(0, 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t nores = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0u, BUF_DW3);
+    stream_half(it, s, H0{}, xq[q0], fz, buf, nullptr, nores);
+    if constexpr (h0 + 4 < 2 * SPI) load_half(it, it.s0 + (h0 + 4) / 2, gt, H0{}, xq[q0], fz);
+    else load_half(nx, nx.s0 + (h0 + 4 - 2 * SPI) / 2, ngt, H0{}, xq[q0], fz);
+    stream_half(it, s, H1{}, xq[q1], fz, buf, nullptr, nores);
+    if constexpr (h1 + 4 < 2 * SPI) load_half(it, it.s0 + (h1 + 4) / 2, gt, H1{}, xq[q1], fz);
+    else load_half(nx, nx.s0 + (h1 + 4 - 2 * SPI) / 2, ngt, H1{}, xq[q1], fz);
+    __syncthreads();
+    mfma_phase(it, s, buf, pf);
+  };
+
   int item = (int)blockIdx.x;
   Item it = item_of(item);
   if (POST) {
@@ -366,7 +419,15 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     if (tid < TILE * 4) gtab[tid] = v;
   }
   if (POST || MODE == ROWS_GATHER) __syncthreads();
-  load_half(it, it.s0, gtab, H0{}, xA, fA);
+  if constexpr (DEEP) {
+    uint4 fz = make_uint4(0, 0, 0, 0);
+    load_half(it, it.s0, gtab, H0{}, xq[0], fz);
+    load_half(it, it.s0, gtab, H1{}, xq[1], fz);
+    load_half(it, it.s0 + 1, gtab, H0{}, xq[2], fz);
+    load_half(it, it.s0 + 1, gtab, H1{}, xq[3], fz);
+  } else {
+    load_half(it, it.s0, gtab, H0{}, xA, fA);
+  }
   // the partial sums this thread reduced for the previous item (pitem; -1: none)
   float pend[PG::NPEND];
 #pragma unroll
@@ -395,14 +456,13 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
         POST ? A.Y + (int64_t)it.tile * TILE * (NS4 * C) : nullptr, 0, POST ? (uint32_t)(nrow * NS4 * C * 2) : 0u,
         BUF_DW3);
     float cn0 = 0.f, cn1 = 0.f;
+    // the next item's stream indices: the deep prefetch reads them from the
+    // third super-chunk on, the other one in the last super-chunk
     int gn = 0;
+    if (DEEP && MODE == ROWS_GATHER) gn = gidx_val(nx.tile);
     // SPI super-chunks, unrolled (past the last super-chunk of C they only add
     // zeros): straight-line code keeps the compiler's wait counts exact.
-#pragma unroll
-    for (int j = 0; j < SPI; ++j) {
-      const bool last = j + 1 == SPI;
-      body(it, it.s0 + j, gt, last ? nx : it, last ? nx.s0 : it.s0 + j + 1, last ? ngt : gt,
-           lds + ((step + j) & 1) * LBUF, cf, yres);
+    auto tail = [&](int j) __attribute__((always_inline)) {
       if (j == 0) {
         // after the first prefetch: the previous item's partial sums and the
         // next item's coefficients and stream indices
@@ -411,12 +471,26 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
           cn0 = coef_val(nx.tile, tid);
           cn1 = coef_val(nx.tile, cidx1);
         }
-        if (MODE == ROWS_GATHER) gn = gidx_val(nx.tile);
+        if (!DEEP && MODE == ROWS_GATHER) gn = gidx_val(nx.tile);
       }
-      if (j == 1 && MODE == ROWS_GATHER) {
-        // used by the last super-chunk's prefetch, after the next barrier; the
-        // previous item read this buffer before its end barriers
+      if (j == (DEEP ? 0 : 1) && MODE == ROWS_GATHER) {
+        // visible after the next barrier, before the first read for the next
+        // item; this item's reads of that buffer ended in the previous item
         if (tid < TILE * 4) gtab[((k + 1) & 1) * (TILE * 4) + tid] = gn;
+      }
+    };
+    if constexpr (DEEP) {
+      static_for<SPI>([&](auto J) __attribute__((always_inline)) {
+        body_deep(it, J, gt, nx, ngt, lds + ((step + decltype(J)::value) & 1) * LBUF);
+        tail(decltype(J)::value);
+      });
+    } else {
+#pragma unroll
+      for (int j = 0; j < SPI; ++j) {
+        const bool last = j + 1 == SPI;
+        body(it, it.s0 + j, gt, last ? nx : it, last ? nx.s0 : it.s0 + j + 1, last ? ngt : gt,
+             lds + ((step + j) & 1) * LBUF, cf, yres);
+        tail(j);
       }
     }
     step += SPI;
