@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "tokens/s + achieved HBM GB/s (% peak), fused mHC n=4 C=4096 sublayer, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
-WORKLOAD = 1
+WORKLOAD = "mhc_n4_C4096_T8192_bf16"
 SINKHORN_ITERS = 20
 
 
@@ -202,7 +202,7 @@ def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
 
     w = synth.WORKLOADS[WORKLOAD]
     T, n, C = w["T"], w["n"], w["C"]
-    inp = synth.mhc_layer(WORKLOAD, 0, T, n, C, w["dtype"])
+    inp = synth.mhc_layer(w["seed"], 0, T, n, C, w["dtype"])
     Xv, Fv = inp["X"].values, inp["F_out"].values
     done, start, chunk = 0, time.perf_counter(), 512
     elapsed = 0.0
@@ -241,7 +241,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     w = synth.WORKLOADS[WORKLOAD]
     T, n, C = w["T"], w["n"], w["C"]
-    inp = synth.mhc_layer(WORKLOAD, 0, T, n, C, w["dtype"])
+    inp = synth.mhc_layer(w["seed"], 0, T, n, C, w["dtype"])
 
     def up_bf16(t):
         return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)

@@ -4,7 +4,7 @@ This module only draws random numbers and rounds them to the stream dtype. It
 holds none of the method's arithmetic, so both the fp64 oracle and the HIP path
 can take their inputs from it without sharing any computation.
 
-Recipe (one numpy PCG64 generator per (workload, layer), seed 1000*workload +
+Recipe (one numpy PCG64 generator per (seed, layer), entropy 1000*seed +
 layer; draws are float32 standard normals scaled in float32, then rounded to the
 stream dtype with round-to-nearest-even when the stream is bfloat16):
 
@@ -28,14 +28,16 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-# The five workloads: shapes, dtypes and value distributions.
+# The workloads, by shape: sizes, dtypes, and the seed their draws start from.
 WORKLOADS = {
-    0: dict(kind="mhc", n=4, C=256, T=512, dtype=F32, layers=1),
-    1: dict(kind="mhc", n=4, C=4096, T=8192, dtype=BF16, layers=1, batch=4, seq=2048),
-    2: dict(kind="mhc", n=4, C=7168, T=16384, dtype=BF16, layers=8, batch=8, seq=2048),
-    3: dict(kind="xhc", N=16, k=4, m=2, C=4096, T=8192, dtype=BF16, K=1),
-    4: dict(kind="xhc", N=16, k=4, m=2, C=4096, T=8192, dtype=BF16, K=4,
-            batch=2, seq=4096, kappas=(4, 8, 12)),
+    "mhc_n4_C256_T512_f32": dict(seed=0, kind="mhc", n=4, C=256, T=512, dtype=F32, layers=1),
+    "mhc_n4_C4096_T8192_bf16": dict(seed=1, kind="mhc", n=4, C=4096, T=8192, dtype=BF16, layers=1, batch=4,
+                                    seq=2048),
+    "mhc_n4_C7168_T16384_bf16_8layers": dict(seed=2, kind="mhc", n=4, C=7168, T=16384, dtype=BF16, layers=8,
+                                             batch=8, seq=2048),
+    "xhc_N16_k4_m2_C4096_T8192_bf16_K1": dict(seed=3, kind="xhc", N=16, k=4, m=2, C=4096, T=8192, dtype=BF16, K=1),
+    "xhc_N16_k4_m2_C4096_T8192_bf16_K4": dict(seed=4, kind="xhc", N=16, k=4, m=2, C=4096, T=8192, dtype=BF16, K=4,
+                                              batch=2, seq=4096, kappas=(4, 8, 12)),
 }
 
 PHI_STD = 0.02
@@ -43,9 +45,9 @@ ALPHA = 0.01
 SINKHORN_ITERS = 20
 
 
-def make_rng(workload: int, layer: int = 0, stream: int = 0) -> np.random.Generator:
-    """Generator for (workload, layer); `stream` > 0 gives independent side streams."""
-    return np.random.Generator(np.random.PCG64([1000 * workload + layer, stream]))
+def make_rng(seed: int, layer: int = 0, stream: int = 0) -> np.random.Generator:
+    """Generator for (seed, layer); `stream` > 0 gives independent side streams."""
+    return np.random.Generator(np.random.PCG64([1000 * seed + layer, stream]))
 
 
 def round_to_bf16(a: np.ndarray):
@@ -95,10 +97,10 @@ def mhc_bias(n: int) -> np.ndarray:
     return b
 
 
-def mhc_layer(seed_workload: int, layer: int, T: int, n: int, C: int, dtype: str,
+def mhc_layer(seed: int, layer: int, T: int, n: int, C: int, dtype: str,
               draw_x: bool = True) -> dict:
     """Inputs of one mHC sublayer. With draw_x=False the X draw is skipped (chains)."""
-    rng = make_rng(seed_workload, layer)
+    rng = make_rng(seed, layer)
     out = {}
     if draw_x:
         out["X"] = Tensor(normal(rng, (T, n, C)), dtype)
@@ -109,10 +111,10 @@ def mhc_layer(seed_workload: int, layer: int, T: int, n: int, C: int, dtype: str
     return out
 
 
-def xhc_layer(seed_workload: int, layer: int, T: int, N: int, C: int, k: int, m: int,
+def xhc_layer(seed: int, layer: int, T: int, N: int, C: int, k: int, m: int,
               K: int, dtype: str, kappas=(4, 8, 12)) -> dict:
     """Inputs of one xHC sublayer (K=1: plain write-back; K>1: augmented)."""
-    rng = make_rng(seed_workload, layer)
+    rng = make_rng(seed, layer)
     out = {}
     out["X"] = Tensor(normal(rng, (T, N, C)), dtype)
     out["phi_pre"] = normal(rng, (N * C, N), PHI_STD)

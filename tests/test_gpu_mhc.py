@@ -46,26 +46,26 @@ def _oracle(inp, iters=20):
 
 
 @pytest.mark.parametrize("fused", [True, False])
-def test_workload0_fp32_full(fused):
-    w = synth.WORKLOADS[0]
-    note(f"mHC workload 0 (n=4 C=256 T=512 fp32) fused={fused}")
+def test_mhc_n4_C256_T512_fp32_full(fused):
+    w = synth.WORKLOADS["mhc_n4_C256_T512_f32"]
+    note(f"mHC n=4 C=256 T=512 fp32 fused={fused}")
     inp = synth.mhc_layer(0, 0, w["T"], w["n"], w["C"], w["dtype"])
     _compare_all(_run_sublayer(inp, fused), _oracle(inp), synth.F32)
 
 
 @pytest.mark.parametrize("T", [1, 7, 133])
 @pytest.mark.parametrize("fused", [True, False])
-def test_workload1_shape_ragged_T(T, fused):
+def test_mhc_n4_C4096_bf16_ragged_T(T, fused):
     note(f"mHC n=4 C=4096 bf16 T={T} fused={fused}")
     inp = synth.mhc_layer(1, 0, T, 4, 4096, synth.BF16)
     _compare_all(_run_sublayer(inp, fused), _oracle(inp), synth.BF16, literal=True)
 
 
-def test_workload1_full_size_sampled():
+def test_mhc_n4_C4096_T8192_bf16_full_size_sampled():
     """Full-size run (T=8192, the benchmarked launch); oracle on sampled tokens,
     invariants on every token."""
-    w = synth.WORKLOADS[1]
-    note("mHC workload 1 full size (n=4 C=4096 T=8192 bf16)")
+    w = synth.WORKLOADS["mhc_n4_C4096_T8192_bf16"]
+    note("mHC full size (n=4 C=4096 T=8192 bf16)")
     inp = synth.mhc_layer(1, 0, w["T"], w["n"], w["C"], w["dtype"])
     got = _run_sublayer(inp, fused=True)
     rng = np.random.default_rng(101)
@@ -167,10 +167,10 @@ def test_wide_logits_follow_twenty_iterations():
 
 
 @pytest.mark.slow
-def test_workload2_chain_per_layer_and_conservation():
+def test_mhc_n4_C7168_T16384_chain_per_layer_and_conservation():
     """8 chained sublayers at full size: per layer the oracle runs on the GPU's
     bf16 X_l for sampled tokens; the stream-sum conservation holds on all tokens."""
-    w = synth.WORKLOADS[2]
+    w = synth.WORKLOADS["mhc_n4_C7168_T16384_bf16_8layers"]
     T, n, C = w["T"], w["n"], w["C"]
     rng = np.random.default_rng(202)
     sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 62, replace=False)]))
@@ -178,7 +178,7 @@ def test_workload2_chain_per_layer_and_conservation():
     X = dev(first["X"])
     del first["X"]
     for layer in range(w["layers"]):
-        note(f"mHC workload 2 layer {layer} (n=4 C=7168 T=16384 bf16)")
+        note(f"mHC chain layer {layer} (n=4 C=7168 T=16384 bf16)")
         inp = first if layer == 0 else synth.mhc_layer(2, layer, T, n, C, w["dtype"], draw_x=False)
         F = dev(inp["F_out"])
         h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
@@ -199,7 +199,7 @@ def test_workload2_chain_per_layer_and_conservation():
         del F, F_in
 
 
-def test_workload2_shape_chain_end_to_end():
+def test_mhc_n4_C7168_chain_end_to_end():
     """Reduced-T chain of 8 layers at C=7168: each layer against the oracle on the
     GPU's input, and the independent oracle chain (bf16 rounding between layers)
     against the GPU's last state."""
@@ -255,7 +255,7 @@ def test_post_coeffs_in_place_and_small_C():
     _post_coeffs_case(11, 40, 33)
 
 
-def test_chain_with_post_coeffs_workload2_shape():
+def test_chain_with_post_coeffs_C7168():
     """The chained path (pre-read + post fused with the next coefficients) over 8
     layers at C=7168: each layer against the oracle on the GPU's own input state."""
     T, n, C = 45, 4, 7168
@@ -354,7 +354,7 @@ def test_phi_pack_layout_pin():
     np.testing.assert_array_equal(got, want.transpose(0, 2, 1))
 
 
-def test_chain_with_post_pre_workload2_shape():
+def test_chain_with_post_pre_C7168():
     """The chained path as one call per step over 8 layers at C=7168, each layer
     against the oracle on the GPU's own input state."""
     T, n, C = 45, 4, 7168

@@ -24,10 +24,10 @@ def _router_scores_chunked(Xv, w_router, chunk=256):
     return np.concatenate(out)
 
 
-def enforce_score_gaps(inp, k, m, workload):
+def enforce_score_gaps(inp, k, m, seed):
     """Redraw (seeded) every token whose top-(k-m+1) candidate scores are closer than
     1e-3 to each other, so the selection does not hinge on rounding."""
-    rng = synth.make_rng(workload, 0, stream=7)
+    rng = synth.make_rng(seed, 0, stream=7)
     X = inp["X"]
     todo = np.arange(X.shape[0])
     for _ in range(50):
@@ -41,10 +41,10 @@ def enforce_score_gaps(inp, k, m, workload):
     raise AssertionError("could not enforce score gaps")
 
 
-def _xhc_inputs(workload, T, N, k, m, C, K, batch=None, seq=None):
-    inp = synth.xhc_layer(workload, 0, T, N, C, k, m, K, synth.BF16,
+def _xhc_inputs(seed, T, N, k, m, C, K, batch=None, seq=None):
+    inp = synth.xhc_layer(seed, 0, T, N, C, k, m, K, synth.BF16,
                           kappas=(4, 8, 12)[: K - 1] if K > 1 else ())
-    enforce_score_gaps(inp, k, m, workload)
+    enforce_score_gaps(inp, k, m, seed)
     return inp
 
 
@@ -78,7 +78,7 @@ def _check_route(X_before, inp, idx, Wb_host, got_X, got_coeffs, sample=None):
 
 
 @pytest.mark.parametrize("T", [1, 77])
-def test_workload3_shape_pre_and_route(T):
+def test_xhc_N16_C4096_pre_and_route(T):
     N, k, m, C = 16, 4, 2, 4096
     note(f"xHC N=16 k=4 m=2 C=4096 bf16 K=1 T={T}")
     inp = _xhc_inputs(3, T, N, k, m, C, 1)
@@ -105,10 +105,10 @@ def test_workload3_shape_pre_and_route(T):
 
 
 @pytest.mark.slow
-def test_workload3_full_size():
-    w = synth.WORKLOADS[3]
+def test_xhc_N16_C4096_T8192_full_size():
+    w = synth.WORKLOADS["xhc_N16_k4_m2_C4096_T8192_bf16_K1"]
     T, N, k, m, C = w["T"], w["N"], w["k"], w["m"], w["C"]
-    note("xHC workload 3 full size (N=16 k=4 C=4096 T=8192 bf16)")
+    note("xHC full size (N=16 k=4 C=4096 T=8192 bf16)")
     inp = _xhc_inputs(3, T, N, k, m, C, 1)
     X = dev(inp["X"])
     pre = hc.xhc_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], dev(inp["w_router"]), k, m)
@@ -127,7 +127,7 @@ def test_workload3_full_size():
 
 
 @pytest.mark.parametrize("vdt", ["bf16", "f32"])
-def test_workload4_shape_augment_and_route(vdt):
+def test_xhc_N16_C4096_augment_and_route(vdt):
     B, S, N, k, m, C = 2, 40, 16, 4, 2, 4096
     note(f"xHC augmented K=4 B=2 S=40 C=4096 V={vdt}")
     inp = _xhc_inputs(4, B * S, N, k, m, C, 4)
@@ -155,11 +155,11 @@ def test_workload4_shape_augment_and_route(vdt):
 
 
 @pytest.mark.slow
-def test_workload4_full_size():
-    wl = synth.WORKLOADS[4]
+def test_xhc_N16_C4096_T8192_K4_full_size():
+    wl = synth.WORKLOADS["xhc_N16_k4_m2_C4096_T8192_bf16_K4"]
     B, S, N, k, m, C = wl["batch"], wl["seq"], wl["N"], wl["k"], wl["m"], wl["C"]
     T = B * S
-    note("xHC workload 4 full size (K=4, B=2 S=4096 C=4096 bf16)")
+    note("xHC full size (K=4, B=2 S=4096 C=4096 bf16)")
     inp = _xhc_inputs(4, T, N, k, m, C, 4)
     F = dev(inp["F_out"])
     w = dev(np.concatenate([wj.reshape(-1) for wj in inp["conv_w"]]))
