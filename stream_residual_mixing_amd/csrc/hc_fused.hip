@@ -576,6 +576,7 @@ __device__ __forceinline__ float token_coeffs(const float* __restrict__ part, in
   const int m = (int)(tt - tile * TILE);
   const float* base = part + tile * S * PG::PART + m * PG::PROW;
   float ss = 0.f, pr = 0.f, pe = 0.f;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float* b = base + (int64_t)s * PG::PART;
     ss += b[PG::NCOLP];
@@ -655,6 +656,7 @@ __global__ __launch_bounds__(256) void xpre_finish_kernel(const float* __restric
   const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
   const int cc = c < PG::NCOLP ? c : 0;
   float ss = 0.f, pc = 0.f;
+#pragma unroll 4
   for (int it = 0; it < per_tile; ++it) {
     const float* b = base + (int64_t)it * PG::PART;
     ss += b[PG::NCOLP];
@@ -721,6 +723,7 @@ __global__ __launch_bounds__(256) void xroute_finish_kernel(const float* __restr
   const int kK = 4 * K;
   const int cpost = e < kK ? e : 0;
   float ss = 0.f, pr = 0.f, pp = 0.f;
+#pragma unroll 4
   for (int it = 0; it < per_tile; ++it) {
     const float* b = base + (int64_t)it * PG::PART;
     ss += b[PG::NCOLP];
