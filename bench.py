@@ -181,6 +181,23 @@ def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     return out
 
 
+def copy_ceiling(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Read + write GB/s of a plain device-to-device copy of `nbytes` (three rotating
+    buffer pairs) on the same box: the practical bandwidth ceiling."""
+    src = [torch.full((nbytes // 4,), float(i), dtype=torch.float32, device=dev) for i in range(3)]
+    dst = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+    for i in range(3):
+        dst[i].copy_(src[i])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        dst[i % 3].copy_(src[i % 3])
+    b.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def load_traffic(kernel: str, digest: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -254,7 +271,7 @@ def main() -> int:
     F_in = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
     ab = algorithmic_bytes(T, n, C)
 
-    def timed(step_fn, names, steps, warmup):
+    def timed(step_fn, names, steps, warmup, label):
         """Warm up, then time `steps` steps twice: once bare (events only at both
         ends, so no marker sits between kernels), once with HIP events around every
         call on the launch stream (per-call durations)."""
@@ -276,7 +293,12 @@ def main() -> int:
             step_fn(warmup + steps + i, evs[i])
         torch.cuda.synchronize()
         kern = {nm: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) * 1e-3 for j, nm in enumerate(names)}
+        dist[label] = {
+            nm: {q: float(np.percentile([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs], p))
+                 for q, p in (("p10_us", 10), ("median_us", 50), ("p90_us", 90))} for j, nm in enumerate(names)}
         return wall, gpu, kern
+
+    dist = {}
 
     Fs = [F0] + [F0.clone() for _ in range(2)]
     phi_packed = hc.hc_phi_pack(phi, n, C, torch.bfloat16)
@@ -304,7 +326,8 @@ def main() -> int:
                                                out=(None, coef[0][1], coef[0][2], F_ins[0]), workspace=ws)
 
     chain_start()
-    wall_pk, gpu_pk, kern_pk = timed(make_chain_step(None), ["hc_post_pre"], args.steps, args.warmup)
+    wall_pk, gpu_pk, kern_pk = timed(make_chain_step(None), ["hc_post_pre"], args.steps, args.warmup,
+                                     "chain_phi_packed_each_step")
 
     # --- the same chain as two calls per step: pre-read, then post fused with the next coefficients
     coef2 = [(torch.empty(T, n, device=dev), torch.empty(T, n, device=dev), torch.empty(T, n, n, device=dev))
@@ -324,7 +347,8 @@ def main() -> int:
         if evs is not None:
             evs[2].record()
 
-    wall2, gpu2, kern2 = timed(two_call_step, ["hc_pre", "hc_post_coeffs"], args.steps, args.warmup)
+    wall2, gpu2, kern2 = timed(two_call_step, ["hc_pre", "hc_post_coeffs"], args.steps, args.warmup,
+                                "chain_two_calls")
 
     # --- isolated sublayer on rotated input sets
     h_post_i = torch.empty(T, n, device=dev)
@@ -343,12 +367,13 @@ def main() -> int:
         if evs is not None:
             evs[2].record()
 
-    iso_wall, iso_gpu, iso_kern = timed(iso_step, ["hc_coeffs_pre", "hc_post"], args.steps, args.warmup)
+    iso_wall, iso_gpu, iso_kern = timed(iso_step, ["hc_coeffs_pre", "hc_post"], args.steps, args.warmup,
+                                        "isolated_sublayer")
     iso_bytes = ab["hc_coeffs_pre"] + ab["hc_post"]
 
     # headline last, once the clocks have settled under the variants above
     chain_start()
-    wall, gpu_s, kern = timed(make_chain_step(phi_packed), ["hc_post_pre"], args.steps, args.warmup)
+    wall, gpu_s, kern = timed(make_chain_step(phi_packed), ["hc_post_pre"], args.steps, args.warmup, "headline")
     step_bytes = ab["hc_post_pre"]
 
     def rate(wall_s, nbytes):
@@ -395,6 +420,8 @@ def main() -> int:
                                 calls_GBps={k: ab[k] / v / 1e9 for k, v in kern2.items()}),
         "isolated_sublayer": dict(rate(iso_wall, iso_bytes), calls_us={k: v * 1e6 for k, v in iso_kern.items()},
                                   algorithmic_bytes_per_step=iso_bytes),
+        "call_durations": dist,
+        "device_copy_ceiling_GBps": copy_ceiling(torch, dev),
         "source_digest": digest,
     }
     if not args.no_xhc:
