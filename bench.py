@@ -409,7 +409,7 @@ def main() -> int:
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "gpu_ms_per_step": gpu_s / args.steps * 1e3,
-        "roofline": {"kernel": "hc_post_pre (mhc_split_kernel<true> + coeffs_finish_kernel + pre4_kernel)",
+        "roofline": {"kernel": "hc_post_pre (mhc_split_kernel<true> + finish_pre4_kernel)",
                      "bound": "hbm",
                      "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom],

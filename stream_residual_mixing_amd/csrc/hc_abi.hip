@@ -214,8 +214,8 @@ int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const f
   hipStream_t st = (hipStream_t)stream;
   if (hc::fast_coeffs_supported(dtype, n, T, C, X) && aligned_to(F_in, 16)) {
     return launch_status(hc::launch_fast_coeffs_pre(X, T, C, phi, bias, alpha_pre, alpha_post,
-                                                    alpha_res, sinkhorn_iters, h_pre ? h_pre : w.h_pre, h_post,
-                                                    h_res, F_in, w.packed, w.partial, st));
+                                                    alpha_res, sinkhorn_iters, h_pre, h_post, h_res, F_in,
+                                                    w.packed, w.partial, st));
   }
   // Generic: the pre-read needs h_pre, kept in the workspace when the caller
   // does not ask for it.
@@ -363,8 +363,8 @@ int hc_post_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const flo
       aligned_to(F_in_next, 16))
     return launch_status(hc::launch_fast_post_coeffs(X, T, C, h_res, h_post, F_out, X_next, phi_next,
                                                      phi_next_packed, bias_next, alpha_pre, alpha_post, alpha_res,
-                                                     sinkhorn_iters, h_pre_next ? h_pre_next : w.h_pre, h_post_next,
-                                                     h_res_next, F_in_next, w.packed, w.partial, st));
+                                                     sinkhorn_iters, h_pre_next, h_post_next, h_res_next, F_in_next,
+                                                     w.packed, w.partial, st));
   // generic: post, coefficients of X_next (h_pre kept in the workspace when not
   // requested), pre-read of X_next
   hipError_t e = hc::launch_post_generic(dtype, vec_ok(C, {X, F_out, X_next}), X, T, n, C, h_res, h_post,

@@ -12,8 +12,8 @@ int64_t fast_coeffs_packed_bytes(int n, int64_t C, int dtype);
 // Bytes of the per-item partial projections of the fused kernels (0 if unused).
 int64_t fast_coeffs_partial_bytes(int64_t T, int n, int64_t C, int dtype);
 bool fast_coeffs_supported(int dtype, int n, int64_t T, int64_t C, const void* X);
-// Coefficients (+ pre-read when F_in != nullptr) for n = 4 bfloat16 streams;
-// h_pre is required (the pre-read takes it from there).
+// Coefficients (+ pre-read when F_in != nullptr) for n = 4 bfloat16 streams.
+// h_pre may be nullptr when F_in is given (the pre-read forms h_pre itself).
 hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const float* phi,
                                   const float* bias, float a_pre, float a_post, float a_res,
                                   int iters, float* h_pre, float* h_post, float* h_res, void* F_in,
@@ -24,8 +24,8 @@ hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream
 hipError_t launch_fast_pre(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in,
                            hipStream_t st);
 // Post/res write fused with the coefficients of the state it writes (phi, bias, gates of
-// the next sublayer) and, when F_in_n != nullptr, its pre-read (h_pre_n is then
-// required). phi_packed (may be nullptr) holds phi already packed; otherwise phi is
+// the next sublayer) and, when F_in_n != nullptr, its pre-read (h_pre_n may then be
+// nullptr). phi_packed (may be nullptr) holds phi already packed; otherwise phi is
 // packed into `packed`.
 hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const float* h_res,
                                    const float* h_post, const void* F, void* Y, const float* phi,

@@ -106,6 +106,13 @@ constexpr int LROW = SC * 2 + 16;       // bytes per (stream, token) row in LDS,
 constexpr int LBUF = NS4 * TILE * LROW; // bytes per LDS buffer
 
 // Round-to-nearest-even pack of two floats into bf16x2 (v_cvt_pk_bf16_f32).
+// Loads of the streamed state (read once per pass): nontemporal, so they stream
+// through L2 without displacing the packed phi that every item re-reads.
+__device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t pack_bf2_hw(float a, float b) {
   typedef float f2_t __attribute__((ext_vector_type(2)));
   typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
@@ -258,16 +265,16 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     const uint16_t* xr = X + t * A.rowstride + cc;
     if (MODE == ROWS_GATHER) {
       const int4 sv = *reinterpret_cast<const int4*>(gt + m * 4);
-      xv[0] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.x * C);
-      xv[1] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.y * C);
-      xv[2] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.z * C);
-      xv[3] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.w * C);
+      xv[0] = ld_stream(xr + (int64_t)sv.x * C);
+      xv[1] = ld_stream(xr + (int64_t)sv.y * C);
+      xv[2] = ld_stream(xr + (int64_t)sv.z * C);
+      xv[3] = ld_stream(xr + (int64_t)sv.w * C);
     } else {
       const uint16_t* xg = xr + (int64_t)(MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
 #pragma unroll
-      for (int i = 0; i < NS4; ++i) xv[i] = *reinterpret_cast<const uint4*>(xg + i * C);
+      for (int i = 0; i < NS4; ++i) xv[i] = ld_stream(xg + i * C);
     }
-    if (POST) fv = *reinterpret_cast<const uint4*>(A.F + t * C + cc);
+    if (POST) fv = ld_stream(A.F + t * C + cc);
   };
 
   // Streaming work of one token half: X_next (POST) and the bf16 tile it
@@ -305,7 +312,10 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
         o.w = pack_bf2_hw(y[6], y[7]);
         a_frag[i] = o;  // positions past T or C are zeroed in the MFMA phase
         const uint32_t yoff = ok ? (uint32_t)((((int64_t)m * NS4 + i) * C + c) * 2) : OOB;
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{o.x, o.y, o.z, o.w}, yres, yoff, 0, 2 /* nt */);
+        // A cached store, not a nontemporal one: the pre-read that follows reads
+        // these rows back newest first and finds many of them in the last-level
+        // cache (on the 4 x 4096 state, about 9% off the whole call).
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{o.x, o.y, o.z, o.w}, yres, yoff, 0, 0);
       }
     } else {
 #pragma unroll
@@ -560,6 +570,15 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
+// 1 / r with r = sqrt(ss / 4C), the token's RMS over the flattened state
+// (0 for an all-zero state), and the gate logit alpha * P / r + b: shared by
+// every kernel that forms mHC gates, so they produce the same floats.
+__device__ __forceinline__ float inv_rms4(float ss, int64_t C) {
+  const float r = sqrtf(ss / (float)(NS4 * C));
+  return (r > 0.f) ? 1.0f / r : 0.f;
+}
+__device__ __forceinline__ float gate_logit(float a, float p, float invr, float b) { return a * (p * invr) + b; }
+
 // Coefficients of token tt (< T) from the partial projections ([mHC] Eq.
 // 15-19), computed by the 16 lanes of one DPP row (lane e = tid & 15). Each lane
 // adds the token's slices in slice order (the sum of squares, the h_res logit
@@ -583,10 +602,9 @@ __device__ __forceinline__ float token_coeffs(const float* __restrict__ part, in
     pr += b[8 + e];
     pe += b[e & 7];
   }
-  const float r = sqrtf(ss / (float)(NS4 * C));
-  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  const float invr = inv_rms4(ss, C);
   const float a = e < 4 ? gate.a_pre : gate.a_post;
-  const float sg = sigmoid(a * (pe * invr) + bias[e & 7]);
+  const float sg = sigmoid(gate_logit(a, pe, invr, bias[e & 7]));
   if (store && e < 8) {
     if (e < 4) {
       if (h_pre_out) h_pre_out[tt * 4 + e] = sg;
@@ -600,7 +618,7 @@ __device__ __forceinline__ float token_coeffs(const float* __restrict__ part, in
   // (M[e] + M[e+8]) + (M[e+4] + M[e+12]) by rotating 8 then 4, which gives the
   // same operands, hence the same float, in all four lanes; a row (fixed i) is
   // one quad, summed with the quad permutations xor 1, xor 2.
-  const float z = gate.a_res * (pr * invr) + bias[8 + e];
+  const float z = gate_logit(gate.a_res, pr, invr, bias[8 + e]);
   float zm = fmaxf(z, dpp<DPP_QXOR1>(z));
   zm = fmaxf(zm, dpp<DPP_QXOR2>(zm));
   zm = fmaxf(zm, dpp<DPP_ROR4>(zm));
@@ -765,13 +783,79 @@ __global__ __launch_bounds__(256) void pre4_kernel(const uint16_t* __restrict__ 
   const float w0 = h_pre[t * 4 + 0], w1 = h_pre[t * 4 + 1], w2 = h_pre[t * 4 + 2], w3 = h_pre[t * 4 + 3];
   const uint16_t* p = X + t * 4 * C + c0;
   float a[8], b[8], c[8], d[8], o[8];
-  unpack8(*reinterpret_cast<const uint4*>(p), a);
-  unpack8(*reinterpret_cast<const uint4*>(p + C), b);
-  unpack8(*reinterpret_cast<const uint4*>(p + 2 * C), c);
-  unpack8(*reinterpret_cast<const uint4*>(p + 3 * C), d);
+  unpack8(ld_stream(p), a);
+  unpack8(ld_stream(p + C), b);
+  unpack8(ld_stream(p + 2 * C), c);
+  unpack8(ld_stream(p + 3 * C), d);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = w0 * a[e] + w1 * b[e] + w2 * c[e] + w3 * d[e];
   // F_in is not read again by this pass: a nontemporal store
+  __builtin_nontemporal_store(u32x4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                      pack_bf2_hw(o[6], o[7])},
+                              reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
+}
+
+// h_pre of token tt ([mHC] Eq. 15-18) from the partial projections, with the
+// arithmetic of token_coeffs (slices added in order, the same gate helpers), so
+// both give the same floats.
+__device__ __forceinline__ void token_pre4(const float* __restrict__ part, int64_t tt, int64_t C, int S,
+                                           const float* __restrict__ bias, float a_pre, float (&w)[4]) {
+  using PG = PartGeom<3>;
+  const int64_t tile = tt / TILE;
+  const int m = (int)(tt - tile * TILE);
+  const float* base = part + tile * S * PG::PART + m * PG::PROW;
+  float ss = 0.f, pe[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const float* b = base + (int64_t)s * PG::PART;
+    ss += b[PG::NCOLP];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe[e] += b[e];
+  }
+  const float invr = inv_rms4(ss, C);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = sigmoid(gate_logit(a_pre, pe[e], invr, bias[e]));
+}
+
+// The finish and the pre-read in one launch. Blocks [0, ncb) are
+// coeffs_finish_kernel (16 threads per token); the others are pre4_kernel,
+// each thread forming its token's h_pre from the partials itself instead of
+// waiting for the finish blocks. The two kinds of block are independent, so
+// the latency-bound finish runs beside the bandwidth-bound pre-read. The
+// pre-read blocks take the tokens from the last to the first: the split pass
+// before wrote the state tile by tile from the first, so the rows it wrote
+// last (the likeliest to be still in the last-level cache) are read first,
+// and the pass ends on the first rows, where the next split pass begins.
+__global__ __launch_bounds__(256) void finish_pre4_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
+                                                          const float* __restrict__ bias, Gate gate, int iters,
+                                                          float* __restrict__ h_pre_out,
+                                                          float* __restrict__ h_post_out,
+                                                          float* __restrict__ h_res_out, int ncb,
+                                                          const uint16_t* __restrict__ X,
+                                                          uint16_t* __restrict__ F_in) {
+  if ((int)blockIdx.x < ncb) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tt = g >> 4;
+    token_coeffs(part, tt < T ? tt : T - 1, (int)(g & 15), C, S, bias, gate, iters, tt < T, h_pre_out, h_post_out,
+                 h_res_out);
+    return;
+  }
+  const int64_t nch = C / 8;
+  const int64_t g = (int64_t)((int)gridDim.x - 1 - (int)blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= T * nch) return;
+  const int64_t t = g / nch;
+  const int64_t c0 = (g - t * nch) * 8;
+  const uint16_t* p = X + t * 4 * C + c0;
+  const uint4 x0 = ld_stream(p), x1 = ld_stream(p + C), x2 = ld_stream(p + 2 * C), x3 = ld_stream(p + 3 * C);
+  float w[4];
+  token_pre4(part, t, C, S, bias, gate.a_pre, w);
+  float a[8], b[8], c[8], d[8], o[8];
+  unpack8(x0, a);
+  unpack8(x1, b);
+  unpack8(x2, c);
+  unpack8(x3, d);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = w[0] * a[e] + w[1] * b[e] + w[2] * c[e] + w[3] * d[e];
   __builtin_nontemporal_store(u32x4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
                                       pack_bf2_hw(o[6], o[7])},
                               reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
@@ -853,6 +937,15 @@ hipError_t launch_finish(const float* part, int64_t T, int64_t C, int S, const f
   return hipGetLastError();
 }
 
+hipError_t launch_finish_pre4(const float* part, int64_t T, int64_t C, int S, const float* bias, Gate gate,
+                              int iters, float* h_pre, float* h_post, float* h_res, const void* X, void* F_in,
+                              hipStream_t st) {
+  const int64_t ncb = (T * 16 + 255) / 256, npb = (T * (C / 8) + 255) / 256;
+  hipLaunchKernelGGL(finish_pre4_kernel, dim3((unsigned)(ncb + npb)), dim3(256), 0, st, part, T, C, S, bias, gate,
+                     iters, h_pre, h_post, h_res, (int)ncb, (const uint16_t*)X, (uint16_t*)F_in);
+  return hipGetLastError();
+}
+
 hipError_t launch_pre4(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
   const int64_t work = T * (C / 8);
   hipLaunchKernelGGL(pre4_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, st, (const uint16_t*)X, T,
@@ -889,9 +982,9 @@ hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const flo
   if (e != hipSuccess) return e;
   const Geom g = geom(T, C, 1);
   if ((e = launch_split<false, 3, ROWS_CONTIG>(args(X, T, C, 4 * C, g, packed, partial), st)) != hipSuccess) return e;
-  e = launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, st);
-  if (e != hipSuccess || !F_in) return e;
-  return launch_pre4(X, T, C, h_pre, F_in, st);
+  if (!F_in) return launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, st);
+  return launch_finish_pre4(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, X,
+                            F_in, st);
 }
 
 hipError_t launch_fast_pre(const void* X, int64_t T, int64_t C, const float* h_pre, void* F_in, hipStream_t st) {
@@ -915,9 +1008,10 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
   A.F = (const uint16_t*)F;
   A.Y = (uint16_t*)Y;
   if ((e = launch_split<true, 3, ROWS_CONTIG>(A, st)) != hipSuccess) return e;
-  e = launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n, h_res_n, st);
-  if (e != hipSuccess || !F_in_n) return e;
-  return launch_pre4(Y, T, C, h_pre_n, F_in_n, st);
+  if (!F_in_n)
+    return launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n, h_res_n, st);
+  return launch_finish_pre4(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n,
+                            h_res_n, Y, F_in_n, st);
 }
 
 hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream_t st) {

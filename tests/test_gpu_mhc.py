@@ -338,6 +338,31 @@ def test_post_pre_packed_phi_is_identical():
         np.testing.assert_array_equal(host64(x), host64(y))
 
 
+@pytest.mark.parametrize("T,C", [(133, 4096), (300, 7168), (40, 32)])
+def test_pre_read_h_pre_matches_returned_coefficients_bit_exact(T, C):
+    """The fused pre-read forms each token's h_pre from the partial projections
+    itself; its F_in must be exactly hc_pre(X_next, h_pre') with the h_pre' the
+    same call returns, and the same whether or not h_pre' is requested (also
+    for hc_coeffs_pre)."""
+    note(f"mHC pre-read h_pre consistency n=4 C={C} T={T}")
+    inp = synth.mhc_layer(80 + T, 0, T, 4, C, synth.BF16)
+    nxt = synth.mhc_layer(80 + T, 1, T, 4, C, synth.BF16, draw_x=False)
+    X = dev(inp["X"])
+    h_pre, h_post, h_res = hc.hc_coeffs(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    args = (X, h_res, h_post, dev(inp["F_out"]), dev(nxt["phi"]), dev(nxt["bias"]), [0.01] * 3)
+    Xn, (hp2, _, _), F_a = hc.hc_post_pre(*args)
+    _, (none, _, _), F_b = hc.hc_post_pre(*args, want_h_pre=False)
+    assert none is None
+    F_ref = hc.hc_pre(Xn, hp2)
+    hq, _, _, F_c = hc.hc_coeffs_pre(Xn, dev(nxt["phi"]), dev(nxt["bias"]), [0.01] * 3)
+    _, _, _, F_d = hc.hc_coeffs_pre(Xn, dev(nxt["phi"]), dev(nxt["bias"]), [0.01] * 3, want_h_pre=False)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu().numpy()
+    np.testing.assert_array_equal(hq.cpu().numpy(), hp2.cpu().numpy())
+    for F in (F_a, F_b, F_c, F_d):
+        np.testing.assert_array_equal(bits(F), bits(F_ref))
+
+
 def test_phi_pack_layout_pin():
     """The packed form: per group of 8 rows, columns 0..23 hi = bf16(phi), 24..47
     lo = bf16(phi - hi), 8 consecutive rows of one column contiguous."""
