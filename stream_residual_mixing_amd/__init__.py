@@ -255,14 +255,18 @@ def xhc_pre_workspace_bytes(T, N, C, m, with_router, dtype) -> int:
     return int(lib().xhc_pre_workspace_bytes(T, N, C, m, int(bool(with_router)), _DT[dtype]))
 
 
-def xhc_pre(X, phi_pre, b_pre, alpha_pre, w_router=None, k=4, m=2, *, want_h_pre=True, workspace=None,
-            stream=None):
-    """Full-state pass: dict(h_pre, F_in[, idx, score])."""
+def xhc_pre(X, phi_pre, b_pre, alpha_pre, w_router=None, k=4, m=2, *, want_h_pre=True, out=None,
+            workspace=None, stream=None):
+    """Full-state pass: dict(h_pre, F_in[, idx, score]). out = (h_pre or None, F_in)
+    writes into given tensors."""
     X = _dev_tensor(X, "X", _DT)
     T, N, C = X.shape
     dev = X.device
-    h_pre = torch.empty(T, N, device=dev) if want_h_pre else None
-    F_in = torch.empty(T, C, dtype=X.dtype, device=dev)
+    if out is not None:
+        h_pre, F_in = out
+    else:
+        h_pre = torch.empty(T, N, device=dev) if want_h_pre else None
+        F_in = torch.empty(T, C, dtype=X.dtype, device=dev)
     idx = torch.empty(T, k, dtype=torch.int32, device=dev) if w_router is not None else None
     score = torch.empty(T, N - m, device=dev) if w_router is not None else None
     ws = _workspace(xhc_pre_workspace_bytes(T, N, C, m, w_router is not None, X.dtype), dev, workspace)

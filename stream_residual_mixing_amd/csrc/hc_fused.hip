@@ -861,6 +861,51 @@ __global__ __launch_bounds__(256) void finish_pre4_kernel(const float* __restric
                               reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
 }
 
+// F_in[t, c] = sum_i h_pre[t, i] X[t, i, c] over NS bfloat16 streams (the xHC
+// full-state pre-read, [xHC] step 2); 8 channels per thread, all NS rows in
+// flight at once. Blocks take the tokens from the last to the first, so the
+// rows the projection pass read last are read first.
+template <int NS, bool H16>  // H16: h_pre is 16-byte aligned (read as float4)
+__global__ __launch_bounds__(256) void pre_wide_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t C,
+                                                       const float* __restrict__ h_pre,
+                                                       uint16_t* __restrict__ F_in) {
+  const int64_t nch = C / 8;
+  const int64_t g = (int64_t)((int)gridDim.x - 1 - (int)blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= T * nch) return;
+  const int64_t t = g / nch;
+  const int64_t c0 = (g - t * nch) * 8;
+  const uint16_t* p = X + t * NS * C + c0;
+  uint4 x[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) x[i] = ld_stream(p + i * C);
+  float w[NS];
+  if (H16) {
+    const float4* hp = reinterpret_cast<const float4*>(h_pre + t * NS);
+#pragma unroll
+    for (int i = 0; i < NS / 4; ++i) {
+      const float4 v = hp[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) w[i] = h_pre[t * NS + i];
+  }
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    float xv[8];
+    unpack8(x[i], xv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += w[i] * xv[e];
+  }
+  __builtin_nontemporal_store(u32x4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                      pack_bf2_hw(o[6], o[7])},
+                              reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
+}
+
 // ----------------------------------------------------------------- hosts
 
 static inline bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -943,6 +988,26 @@ hipError_t launch_finish_pre4(const float* part, int64_t T, int64_t C, int S, co
   const int64_t ncb = (T * 16 + 255) / 256, npb = (T * (C / 8) + 255) / 256;
   hipLaunchKernelGGL(finish_pre4_kernel, dim3((unsigned)(ncb + npb)), dim3(256), 0, st, part, T, C, S, bias, gate,
                      iters, h_pre, h_post, h_res, (int)ncb, (const uint16_t*)X, (uint16_t*)F_in);
+  return hipGetLastError();
+}
+
+// N % 4 == 0, 4 <= N <= 16, C % 8 == 0, X, F_in 16-byte aligned, h_pre [T, N]
+hipError_t launch_pre_wide(const void* X, int64_t T, int N, int64_t C, const float* h_pre, void* F_in,
+                           hipStream_t st) {
+  const dim3 grid((unsigned)((T * (C / 8) + 255) / 256)), blk(256);
+  const uint16_t* x = (const uint16_t*)X;
+  uint16_t* f = (uint16_t*)F_in;
+  const bool h16 = a16(h_pre);
+#define HC_PRE_WIDE(NS)                                                                                     \
+  if (h16) hipLaunchKernelGGL((pre_wide_kernel<NS, true>), grid, blk, 0, st, x, T, C, h_pre, f);          \
+  else hipLaunchKernelGGL((pre_wide_kernel<NS, false>), grid, blk, 0, st, x, T, C, h_pre, f);
+  switch (N) {
+    case 4: HC_PRE_WIDE(4) break;
+    case 8: HC_PRE_WIDE(8) break;
+    case 12: HC_PRE_WIDE(12) break;
+    default: HC_PRE_WIDE(16) break;
+  }
+#undef HC_PRE_WIDE
   return hipGetLastError();
 }
 
@@ -1078,7 +1143,7 @@ hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int 
   if (e != hipSuccess) return e;
   e = xhc_full_proj(X, T, N, C, k, m, npre, nr, nb, b_pre, a_pre, h_pre, score, idx, packed, partial, st);
   if (e != hipSuccess || !F_in) return e;
-  return launch_pre_generic(1, true, X, T, N, C, h_pre, F_in, st);
+  return launch_pre_wide(X, T, N, C, h_pre, F_in, st);
 }
 
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,

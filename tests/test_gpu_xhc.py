@@ -307,6 +307,27 @@ def test_fast_full_state_pass_shapes(N, m, C, T):
     assert torch.equal(pre2["h_pre"], pre["h_pre"]) and torch.equal(pre2["F_in"], pre["F_in"])
 
 
+@pytest.mark.parametrize("N", [4, 16])
+def test_fast_full_state_pre_read_h_pre_alignment(N):
+    """The pre-read reads h_pre as float4 when it is 16-byte aligned and one float at
+    a time otherwise: an h_pre given at a 4-byte offset gives the same bits."""
+    T, C, k, m = 70, 256, min(4, N), 1
+    note(f"xHC xhc_pre N={N} C={C} T={T} with h_pre at a 4-byte offset")
+    inp = _xhc_inputs(90 + N, T, N, k, m, C, 1)
+    X = dev(inp["X"])
+    a = hc.xhc_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], None, k, m)
+    buf = torch.empty(T * N + 1, device=X.device)
+    h_off = buf[1:].view(T, N)
+    F_off = torch.empty(T, C, dtype=X.dtype, device=X.device)
+    b = hc.xhc_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], None, k, m, out=(h_off, F_off))
+    torch.cuda.synchronize()
+    assert h_off.data_ptr() % 16 == 4
+    assert torch.equal(a["h_pre"], b["h_pre"]) and torch.equal(a["F_in"], b["F_in"])
+    ref = O.xhc_pre(inp["X"].values, inp["phi_pre"], inp["b_pre"], inp["alpha_pre"], inp["w_router"], k, m)
+    check_fp32("h_pre", host64(b["h_pre"]), ref["h_pre"])
+    check_bf16("F_in", host64(b["F_in"]), ref["F_in"])
+
+
 @pytest.mark.parametrize("K,C,T", [(1, 96, 29), (2, 64, 40), (3, 320, 17), (4, 4096, 33)])
 def test_fast_route_shapes(K, C, T):
     """xhc_route with k = 4 gathered streams for K = 1..4 write-back components, with
