@@ -575,6 +575,8 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
                                   alpha_res, b_act, sinkhorn_iters, nullptr, Hp, Hr, st);
   }
   if (e != hipSuccess) return HC_ERR_LAUNCH;
+  if (hc::fast_mix_supported(dtype, k, K, C, X, Wb))
+    return launch_status(hc::launch_fast_mix(X, T, N, C, idx_out, Hr, Hp, Wb, K, st));
   return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, Wb}), X, T, N, C, k, idx_out, Hr, Hp,
                                               Wb, K, st));
 }

@@ -264,11 +264,15 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     const int64_t cc = c < C ? c : C - 8;
     const uint16_t* xr = X + t * A.rowstride + cc;
     if (MODE == ROWS_GATHER) {
+      // Ordinary (cache-allocating) loads for the gathered rows: the mix pass that
+      // follows reads the same rows again and finds part of them in the
+      // last-level cache (207.8 against 235.5 us per K = 4 route call at
+      // N = 16, C = 4096, T = 8192 with nontemporal loads here).
       const int4 sv = *reinterpret_cast<const int4*>(gt + m * 4);
-      xv[0] = ld_stream(xr + (int64_t)sv.x * C);
-      xv[1] = ld_stream(xr + (int64_t)sv.y * C);
-      xv[2] = ld_stream(xr + (int64_t)sv.z * C);
-      xv[3] = ld_stream(xr + (int64_t)sv.w * C);
+      xv[0] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.x * C);
+      xv[1] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.y * C);
+      xv[2] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.z * C);
+      xv[3] = *reinterpret_cast<const uint4*>(xr + (int64_t)sv.w * C);
     } else {
       const uint16_t* xg = xr + (int64_t)(MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
 #pragma unroll
@@ -906,6 +910,77 @@ __global__ __launch_bounds__(256) void pre_wide_kernel(const uint16_t* __restric
                               reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
 }
 
+// xHC mix + scatter for k = 4 bfloat16 active streams and K <= 4 write-back
+// components, in place ([xHC] step 3): X[t, idx[a]] = sum_b H_res[t, a, b]
+// X[t, idx[b]] + sum_j H_post[t, a, j] Wb[t, j], 8 channels per thread, all
+// 4 + K rows in flight at once, nontemporal loads and stores (each row is read
+// and written once here). Tokens with an index outside [0, N) are left
+// unchanged. Blocks take the tokens from the last to the first: the projection
+// pass before read the gathered rows from the first token on, so the rows it
+// read last are read first here.
+template <int K>
+__global__ __launch_bounds__(256) void mix4_kernel(uint16_t* X, int64_t T, int N, int64_t C,
+                                                   const int32_t* __restrict__ idx,
+                                                   const float* __restrict__ H_res,
+                                                   const float* __restrict__ H_post,
+                                                   const uint16_t* __restrict__ Wb) {
+  const int64_t nch = C / 8;
+  const int64_t g = (int64_t)((int)gridDim.x - 1 - (int)blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= T * nch) return;
+  const int64_t t = g / nch;
+  const int64_t c0 = (g - t * nch) * 8;
+  int s[4];
+  bool ok = true;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    s[a] = idx[t * 4 + a];
+    ok = ok && s[a] >= 0 && s[a] < N;
+  }
+  if (!ok) return;
+  uint4 xr[4], wr[K];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) xr[a] = ld_stream(X + (t * N + s[a]) * C + c0);
+#pragma unroll
+  for (int j = 0; j < K; ++j) wr[j] = ld_stream(Wb + (t * K + j) * C + c0);
+  const float* hr = H_res + t * 16;
+  const float* hp = H_post + t * 4 * K;
+  float x[4][8], y[4][8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) unpack8(xr[b], x[b]);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[a][e] = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float w = hr[a * 4 + b];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[a][e] += w * x[b][e];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    float wv[8];
+    unpack8(wr[j], wv);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float w = hp[a * K + j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[a][e] += w * wv[e];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    uint4 o;
+    o.x = pack_bf2_hw(y[a][0], y[a][1]);
+    o.y = pack_bf2_hw(y[a][2], y[a][3]);
+    o.z = pack_bf2_hw(y[a][4], y[a][5]);
+    o.w = pack_bf2_hw(y[a][6], y[a][7]);
+    __builtin_nontemporal_store(u32x4_t{o.x, o.y, o.z, o.w},
+                                reinterpret_cast<u32x4_t*>(X + (t * N + s[a]) * C + c0));
+  }
+}
+
 // ----------------------------------------------------------------- hosts
 
 static inline bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -1144,6 +1219,25 @@ hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int 
   e = xhc_full_proj(X, T, N, C, k, m, npre, nr, nb, b_pre, a_pre, h_pre, score, idx, packed, partial, st);
   if (e != hipSuccess || !F_in) return e;
   return launch_pre_wide(X, T, N, C, h_pre, F_in, st);
+}
+
+bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const void* Wb) {
+  return dtype == 1 && k == 4 && K >= 1 && K <= 4 && C % 8 == 0 && a16(X) && a16(Wb);
+}
+
+hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* idx, const float* H_res,
+                           const float* H_post, const void* Wb, int K, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)((T * (C / 8) + 255) / 256)), blk(256);
+  uint16_t* x = (uint16_t*)X;
+  const uint16_t* w = (const uint16_t*)Wb;
+  switch (K) {
+    case 1: hipLaunchKernelGGL(mix4_kernel<1>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    case 2: hipLaunchKernelGGL(mix4_kernel<2>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    case 3: hipLaunchKernelGGL(mix4_kernel<3>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    default: hipLaunchKernelGGL(mix4_kernel<4>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,

@@ -237,6 +237,38 @@ def test_fixed_only_and_ties_and_invalid_indices():
     check_fp32("X valid tokens", Y[ok], ref_X)
 
 
+@pytest.mark.parametrize("K", [1, 4])
+def test_fast_mix_invalid_indices_leave_token_unchanged(K):
+    """k = 4 bf16 (the MFMA route path and its mix kernel): a token with an index
+    outside [0, N) keeps all its streams bit for bit; the other tokens follow the
+    oracle."""
+    N, k, C, T = 8, 4, 64, 40
+    note(f"xHC fast route k=4 K={K} with invalid supplied indices")
+    rng = np.random.default_rng(100 + K)
+    Xt = synth.Tensor(rng.standard_normal((T, N, C)).astype(np.float32), synth.BF16)
+    idx = np.array([sorted(rng.choice(N, k, replace=False)) for _ in range(T)], np.int32)
+    idx[3, 3] = 99
+    idx[7, 0] = -1
+    idx[T - 1, 2] = N
+    Wb = synth.Tensor(rng.standard_normal((T, K, C)).astype(np.float32), synth.BF16)
+    phi_act = (0.02 * rng.standard_normal((k * C, k * K + k * k))).astype(np.float32)
+    b_act = np.concatenate([np.zeros(k * K), np.eye(k).reshape(-1)]).astype(np.float32)
+    X = dev(Xt)
+    hc.xhc_route(X, dev(Wb), dev(phi_act), dev(b_act), 0.01, 0.01, k=k, m=1, idx=dev(idx))
+    torch.cuda.synchronize()
+    Y = host64(X)
+    bad = (3, 7, T - 1)
+    for t in bad:
+        np.testing.assert_array_equal(Y[t], Xt.values[t])
+    ok = [t for t in range(T) if t not in bad]
+    ref_X, _, _ = O.xhc_route(Xt.values[ok], idx[ok].astype(np.int64), phi_act, b_act, 0.01, 0.01,
+                              Wb.values[ok])
+    act = np.zeros((len(ok), N), bool)
+    act[np.arange(len(ok))[:, None], idx[ok]] = True
+    assert np.array_equal(Y[ok][~act], Xt.values[ok][~act])
+    check_bf16("X_active valid tokens", Y[ok][act], ref_X[act])
+
+
 @pytest.mark.parametrize("k,m,K,C,dtype", [(2, 1, 1, 100, synth.F32), (3, 2, 2, 64, synth.BF16),
                                            (4, 2, 3, 72, synth.F32), (5, 1, 4, 96, synth.BF16)])
 def test_route_other_active_counts(k, m, K, C, dtype):
