@@ -636,7 +636,7 @@ int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, c
       return HC_ERR_ALIAS;
   }
   if ((s = device_status()) != HC_OK) return s;
-  if (fast_shape && hc::fast_augment_supported(dtype, v_dtype, C, kappa, r, F_out, V))
+  if (fast_shape && hc::fast_augment_supported(dtype, v_dtype, S, C, kappa, r, F_out, V))
     return launch_status(hc::launch_fast_augment(dtype, v_dtype, F_out, B, S, C, conv_w, V, (float*)workspace,
                                                  (hipStream_t)stream));
   if (hc::augment_generic_lds_bytes(r, C) > 160 * 1024 - 1024) return HC_ERR_SHAPE;

@@ -49,15 +49,24 @@ __device__ __forceinline__ void ld4<bf16_t>(const bf16_t* p, float v[4]) {
   v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
   v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
 }
+// Buffer resource over [base, base + bytes): stores whose offset falls outside
+// are dropped by the hardware.
+constexpr unsigned BUF_DW3 = 0x00020000u;
+constexpr uint32_t OOB = 0x80000000u;  // any offset >= the range is dropped
+
 template <typename TV>
-__device__ __forceinline__ void st4(TV* p, const float v[4]);
+__device__ __forceinline__ void st4b(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[4]);
 template <>
-__device__ __forceinline__ void st4<float>(float* p, const float v[4]) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ void st4b<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[4]) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(
+      u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}, r, off, 0,
+      0);
 }
 template <>
-__device__ __forceinline__ void st4<bf16_t>(bf16_t* p, const float v[4]) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+__device__ __forceinline__ void st4b<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[4]) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2_hw(v[0], v[1]), pack_bf2_hw(v[2], v[3])}, r, off, 0, 0);
 }
 
 // Sum over the 16 lanes of a DPP row (every lane gets it).
@@ -111,42 +120,68 @@ __device__ __forceinline__ void load_taps(const float* __restrict__ w, int64_t C
   }
 }
 
-// Walks the strip's tokens in order with the last 12 rows of F (this thread's
-// channels) in a register ring: row p sits in slot (p - p0) mod 12 (p0 is a
-// multiple of 12), so with the walk unrolled by 12 every slot index is a
+// Walks the strip's ATT tokens in order with the last 12 rows of F (this
+// thread's channels) in a register ring: row p sits in slot (p - p0) mod 12 (p0
+// is a multiple of 12), so with the walk unrolled by 12 every slot index is a
 // compile-time constant. Rows are loaded PF tokens ahead into a small queue
-// (slot (p - p0) mod PF) and moved into the ring once the token PF - 1 places
-// earlier is done (the ring slot they take still holds row p - 11, the oldest
-// tap of that token). fn(p, a) receives a[0..3][ch] = F, g1, g2, g3 of token p
-// (zeros past C).
-constexpr int PF = 4;  // rows in flight (divides 12)
+// (slot (p - p0) mod PF) as loaded, and converted into the ring once the token
+// PF - 1 places earlier is done (the ring slot they take still holds row
+// p - 11, the oldest tap of that token). The walk always covers ATT tokens, past
+// the strip end too (rows clamped to the sequence, results discarded by the
+// caller), and every load is unconditional: the compiler can then count the
+// loads in flight exactly and waits only for the row it needs. fn(p, a)
+// receives a[0..3][ch] = F, g1, g2, g3 of token p (zeros past C).
+constexpr int PF = 4;  // rows in flight (divides 12; 4 measured faster than 6 or 12)
 
-template <typename TF, typename Fn>
+// A row of this thread's 4 channels as loaded (converted to float when it
+// enters the ring, so a load in the queue is not waited for before then).
+template <typename TF>
+struct RawRow;
+template <>
+struct RawRow<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void get(float o[4]) const { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
+};
+template <>
+struct RawRow<bf16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void get(float o[4]) const {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+
+template <bool FC, typename TF, typename Fn>  // FC: C is a multiple of the slice width
 __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, int64_t C, const Place& pl,
                                            const Taps& tp, Fn fn) {
-  static_assert(K3 % PF == 0, "the queue slot of a row must be a compile-time constant");
+  static_assert(K3 % PF == 0 && ATT % K3 == 0, "ring and queue slots must be compile-time constants");
   const TF* base = F + pl.b * S * C + pl.c0;
-  auto row = [&](int64_t p, float v[ACH]) __attribute__((always_inline)) {
-    const int64_t pc = p < 0 ? 0 : (p < S ? p : S - 1);
-    ld4<TF>(base + pc * C, v);
-    if (p < 0) {
-#pragma unroll
-      for (int ch = 0; ch < ACH; ++ch) v[ch] = 0.f;
-    }
-  };
+  auto at = [&](int64_t p) __attribute__((always_inline)) { return base + (p < 0 ? 0 : (p < S ? p : S - 1)) * C; };
   float ring[K3][ACH];
-  float q[PF][ACH];
+  RawRow<TF> q[PF];
+  {
+    // rows p0-11 .. p0-1 in slots 1..11 and p0 in slot 0, all loads issued first;
+    // rows before the sequence start are zeros (a mask, not a branch)
+    RawRow<TF> r0[K3];
 #pragma unroll
-  for (int s = 1; s < K3; ++s) row(pl.p0 - K3 + s, ring[s]);  // rows p0-11 .. p0-1 in slots 1..11
-  row(pl.p0, ring[0]);
+    for (int sl = 0; sl < K3; ++sl) r0[sl].load(at(sl == 0 ? pl.p0 : pl.p0 - K3 + sl));
 #pragma unroll
-  for (int d = 1; d < PF; ++d) row(pl.p0 + d, q[d]);  // rows p0+1 .. p0+PF-1
-  for (int64_t pb = pl.p0; pb < pl.p1; pb += K3) {
+    for (int d = 1; d < PF; ++d) q[d].load(at(pl.p0 + d));
+#pragma unroll
+    for (int sl = 0; sl < K3; ++sl) {
+      r0[sl].get(ring[sl]);
+      const uint32_t keep = (sl == 0 || pl.p0 - K3 + sl >= 0) ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int ch = 0; ch < ACH; ++ch) ring[sl][ch] = __uint_as_float(__float_as_uint(ring[sl][ch]) & keep);
+    }
+  }
+  for (int blk = 0; blk < ATT / K3; ++blk) {
 #pragma unroll
     for (int u = 0; u < K3; ++u) {
-      const int64_t p = pb + u;
-      if (p >= pl.p1) break;
-      row(p + PF, q[u % PF]);  // the slot of row p, already in the ring
+      const int64_t p = pl.p0 + blk * K3 + u;
+      q[u % PF].load(at(p + PF));  // the slot of row p, already in the ring
       float a[4][ACH];
 #pragma unroll
       for (int ch = 0; ch < ACH; ++ch) {
@@ -158,29 +193,29 @@ __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, 
         for (int s = 0; s < K2; ++s) g2 += tp.w2[s][ch] * ring[(u + 1 + s + K3 - K2) % K3][ch];
 #pragma unroll
         for (int s = 0; s < K3; ++s) g3 += tp.w3[s][ch] * ring[(u + 1 + s) % K3][ch];
-        a[0][ch] = pl.cok ? ring[u][ch] : 0.f;
-        a[1][ch] = pl.cok ? g1 : 0.f;
-        a[2][ch] = pl.cok ? g2 : 0.f;
-        a[3][ch] = pl.cok ? g3 : 0.f;
+        const bool cok = FC || pl.cok;
+        a[0][ch] = cok ? ring[u][ch] : 0.f;
+        a[1][ch] = cok ? g1 : 0.f;
+        a[2][ch] = cok ? g2 : 0.f;
+        a[3][ch] = cok ? g3 : 0.f;
       }
       fn(p, a);
-#pragma unroll
-      for (int ch = 0; ch < ACH; ++ch) ring[(u + 1) % K3][ch] = q[(u + 1) % PF][ch];
+      q[(u + 1) % PF].get(ring[(u + 1) % K3]);
     }
   }
 }
 
 // Pass 1: partial Gram matrices gram[t][slice][10] (upper triangle, row-major).
-template <typename TF>
+template <bool FC, typename TF>
 __global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
                                                        const float* __restrict__ w, int nstrip, int nslice,
                                                        float* __restrict__ gram) {
-  __shared__ float red[ATT][NG10][16];  // [token][entry][row of 16 lanes]
+  __shared__ float red[ATT][NG10][16];  // [token][entry][row of 16 lanes]; rows past the strip unused
   const Place pl = place(S, C, nstrip, nslice);
   Taps tp;
   load_taps(w, C, pl.c0, tp);
   const int lane = threadIdx.x & 63, rowid = threadIdx.x >> 4;
-  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+  walk_strip<FC, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
     int q = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -209,7 +244,7 @@ __global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F,
 // Pass 2: thread i < strip length builds B of token p0 + i from its Gram matrix
 // (slices added in order, float64) into LDS; then V[t, j] = a_j + sum_{k<j}
 // B[j][k] a_k.
-template <typename TF, typename TV>
+template <bool FC, typename TF, typename TV>
 __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
                                                         const float* __restrict__ w, int nstrip, int nslice,
                                                         const float* __restrict__ gram, TV* __restrict__ V) {
@@ -267,21 +302,28 @@ __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F
   __syncthreads();
   Taps tp;
   load_taps(w, C, pl.c0, tp);
-  walk_strip<TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
-    if (!pl.cok) return;
-    const float* bq = Bs[p - pl.p0];
-    const int64_t t = pl.b * S + p;
+  // V rows of this sequence through a buffer resource: a store of a token past
+  // the strip or of channels past C gets an out-of-range offset and is dropped
+  // (no branch around a store)
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      V + pl.b * S * 4 * C, 0, (uint32_t)(S * 4 * C * (int64_t)sizeof(TV)), BUF_DW3);
+  walk_strip<FC, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+    const float* bq = Bs[p - pl.p0];  // rows past the strip hold stale values (their stores are dropped)
+    const bool ok = (FC || pl.cok) && p < pl.p1;
+    auto off = [&](int j) __attribute__((always_inline)) {
+      return ok ? (uint32_t)(((p * 4 + j) * C + pl.c0) * (int64_t)sizeof(TV)) : OOB;
+    };
     float v[ACH];
-    st4<TV>(V + (t * 4 + 0) * C + pl.c0, a[0]);
+    st4b<TV>(vres, off(0), a[0]);
 #pragma unroll
     for (int ch = 0; ch < ACH; ++ch) v[ch] = a[1][ch] + bq[0] * a[0][ch];
-    st4<TV>(V + (t * 4 + 1) * C + pl.c0, v);
+    st4b<TV>(vres, off(1), v);
 #pragma unroll
     for (int ch = 0; ch < ACH; ++ch) v[ch] = a[2][ch] + bq[1] * a[0][ch] + bq[2] * a[1][ch];
-    st4<TV>(V + (t * 4 + 2) * C + pl.c0, v);
+    st4b<TV>(vres, off(2), v);
 #pragma unroll
     for (int ch = 0; ch < ACH; ++ch) v[ch] = a[3][ch] + bq[3] * a[0][ch] + bq[4] * a[1][ch] + bq[5] * a[2][ch];
-    st4<TV>(V + (t * 4 + 3) * C + pl.c0, v);
+    st4b<TV>(vres, off(3), v);
   });
 }
 
@@ -291,19 +333,27 @@ hipError_t launch_aug(const void* F, int64_t B, int64_t S, int64_t C, const floa
   const int nstrip = (int)((S + ATT - 1) / ATT);
   const int nslice = (int)((C + ACS - 1) / ACS);
   const dim3 grid((unsigned)(B * nstrip * nslice)), blk(256);
-  hipLaunchKernelGGL(aug_gram_kernel<TF>, grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
+  const bool fc = C % ACS == 0;
+  if (fc) hipLaunchKernelGGL((aug_gram_kernel<true, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
+  else hipLaunchKernelGGL((aug_gram_kernel<false, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((aug_apply_kernel<TF, TV>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice,
-                     (const float*)gram, (TV*)V);
+  if (fc)
+    hipLaunchKernelGGL((aug_apply_kernel<true, TF, TV>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice,
+                       (const float*)gram, (TV*)V);
+  else
+    hipLaunchKernelGGL((aug_apply_kernel<false, TF, TV>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice,
+                       (const float*)gram, (TV*)V);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool fast_augment_supported(int dtype, int vdtype, int64_t C, const int* kappa, int r, const void* F,
+bool fast_augment_supported(int dtype, int vdtype, int64_t S, int64_t C, const int* kappa, int r, const void* F,
                             const void* V) {
   if (r != 3 || kappa[0] != K1 || kappa[1] != K2 || kappa[2] != K3 || C % 4 != 0) return false;
+  // one sequence's V addressed with 32-bit buffer offsets
+  if (S * 4 * C * (vdtype == 0 ? 4 : 2) >= (1ll << 31)) return false;
   const uintptr_t fa = dtype == 0 ? 16 : 8, va = vdtype == 0 ? 16 : 8;
   return ((uintptr_t)F % fa) == 0 && ((uintptr_t)V % va) == 0;
 }

@@ -24,6 +24,15 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);
 }
 
+// The same rounding (to nearest even) in one instruction, v_cvt_pk_bf16_f32;
+// NaNs come out as the instruction's quiet NaN.
+__device__ __forceinline__ uint32_t pack_bf2_hw(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  const b2_t r = __builtin_convertvector((f2_t){lo, hi}, b2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // ------------------------------------------------------- element access
 
 template <typename T> struct Elem;

@@ -63,7 +63,7 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
 
 // Temporal augmentation for kappa = {4, 8, 12} (C % 4 == 0; F_out and V aligned to 4
 // elements): conv + Gram pass, then Gram-Schmidt from the Gram matrices.
-bool fast_augment_supported(int dtype, int vdtype, int64_t C, const int* kappa, int r, const void* F,
+bool fast_augment_supported(int dtype, int vdtype, int64_t S, int64_t C, const int* kappa, int r, const void* F,
                             const void* V);
 int64_t fast_augment_workspace_bytes(int64_t B, int64_t S, int64_t C);
 hipError_t launch_fast_augment(int dtype, int vdtype, const void* F, int64_t B, int64_t S, int64_t C,

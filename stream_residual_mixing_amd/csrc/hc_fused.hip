@@ -105,19 +105,11 @@ constexpr int TILE = 2 * TOK;           // tokens per workgroup
 constexpr int LROW = SC * 2 + 16;       // bytes per (stream, token) row in LDS, padded
 constexpr int LBUF = NS4 * TILE * LROW; // bytes per LDS buffer
 
-// Round-to-nearest-even pack of two floats into bf16x2 (v_cvt_pk_bf16_f32).
 // Loads of the streamed state (read once per pass): nontemporal, so they stream
 // through L2 without displacing the packed phi that every item re-reads.
 __device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t pack_bf2_hw(float a, float b) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
-  const b2_t r = __builtin_convertvector((f2_t){a, b}, b2_t);
-  return __builtin_bit_cast(uint32_t, r);
 }
 
 // v if keep, else zeros: per-component selects (a select between two uint4

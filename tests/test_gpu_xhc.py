@@ -6,7 +6,7 @@ import pytest
 
 import oracle as O
 import synth
-from hc_testutil import check_bf16, check_fp32, dev, have_gpu, host64, note
+from hc_testutil import check_bf16, check_fp32, check_stream, dev, have_gpu, host64, note
 
 pytestmark = pytest.mark.gpu
 
@@ -318,6 +318,30 @@ def test_augment_one_hot_taps_pin_order_and_padding():
     torch.cuda.synchronize()
     ref = O.xhc_augment(F, [w], B, S)
     check_fp32("V one-hot", host64(V), ref)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_augment_fast_strips_one_hot_delays(dtype):
+    """kappa = 4, 8, 12 (the strip-walking kernels): one-hot taps turn the three
+    convs into delays of 3, 7 and 11 rows, across 36-token strip boundaries, a
+    ragged last strip and two sequences (zero fill at each start); then random
+    taps on the same shape. With the delays, the first 11 positions of a
+    sequence have an all-zero component, which the unregularised Gram-Schmidt
+    turns into 0/0 on both sides, so those positions are left out of that case."""
+    B, S, C = 2, 80, 64
+    rng = np.random.default_rng(61)
+    F = synth.Tensor(rng.standard_normal((B * S, C)).astype(np.float32), dtype)
+    kap = (4, 8, 12)
+    one_hot = [np.zeros((C, kk), np.float32) for kk in kap]
+    for w in one_hot:
+        w[:, 0] = 1.0
+    rand = [rng.standard_normal((C, kk)).astype(np.float32) / np.sqrt(kk) for kk in kap]
+    pos = np.tile(np.arange(S), B)
+    for name, ws, keep in (("one-hot", one_hot, pos >= 11), ("random", rand, pos >= 0)):
+        note(f"xHC augment strips {name} taps B={B} S={S} C={C} dtype={dtype}")
+        V = hc.xhc_augment(dev(F), dev(np.concatenate([x.reshape(-1) for x in ws])), kap, B, S)
+        torch.cuda.synchronize()
+        check_stream(f"V {name}", dtype, host64(V)[keep], O.xhc_augment(F.values, ws, B, S)[keep])
 
 
 # ------------------------------------ shapes of the MFMA paths (bf16, C % 32 == 0)
