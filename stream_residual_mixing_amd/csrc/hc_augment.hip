@@ -16,10 +16,11 @@
 // this matches float64 modified Gram-Schmidt to about 3e-8 relative L2 on
 // data of this shape, as the float32 modified form does.)
 //
-// Workgroup: 256 threads x 4 channels = a 1024-channel slice, over a strip of
-// 36 consecutive tokens of one sequence; each thread keeps its channels' 24
-// conv taps and the last 12 rows of F in registers, so F is read once per pass
-// (plus an 11-row halo per strip).
+// Workgroup: 256 threads x CH channels (CH = 4 in the Gram pass, 2 in the apply
+// pass) = a slice of 1024 or 512 channels, over a strip of 36 consecutive
+// tokens of one sequence; each thread keeps its channels' 24 conv taps and the
+// last 12 rows of F in registers, so F is read once per pass (plus an 11-row
+// halo per strip).
 #include <type_traits>
 
 #include "hc_device.h"
@@ -31,42 +32,68 @@ namespace {
 
 constexpr int K1 = 4, K2 = 8, K3 = 12;
 constexpr int ATT = 3 * K3;         // tokens per strip (a multiple of the ring length)
-constexpr int ACH = 4;              // channels per thread
-constexpr int ACS = 256 * ACH;      // channels per workgroup
+// Channels per thread of the two passes (a workgroup of 256 threads covers 256 x
+// that many): the Gram pass reduces each token's products across the threads of
+// a slice, so 4 channels per thread halve that work per channel; the apply pass
+// has no such reduction and runs more waves per SIMD with 2 (half the registers
+// for taps and the ring).
+constexpr int CH_G = 4;
+constexpr int CH_A = 2;
 constexpr int NG10 = 10;            // upper triangle of the 4x4 Gram matrix
 constexpr int NB6 = 6;              // strictly lower part of B
 
-template <typename TF>
-__device__ __forceinline__ void ld4(const TF* p, float v[4]);
+// A row of CH channels of one thread, as loaded (converted to float when used).
+template <typename TF, int CH>
+struct RawRow;
 template <>
-__device__ __forceinline__ void ld4<float>(const float* p, float v[4]) {
-  const float4 q = *reinterpret_cast<const float4*>(p);
-  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-}
+struct RawRow<float, 4> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void get(float o[4]) const { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
+};
 template <>
-__device__ __forceinline__ void ld4<bf16_t>(const bf16_t* p, float v[4]) {
-  const uint2 q = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
-  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
-}
+struct RawRow<float, 2> {
+  float2 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ void get(float o[2]) const { o[0] = v.x; o[1] = v.y; }
+};
+template <>
+struct RawRow<bf16_t, 4> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void get(float o[4]) const {
+    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
+    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+template <>
+struct RawRow<bf16_t, 2> {
+  uint32_t v;
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void get(float o[2]) const {
+    o[0] = __uint_as_float(v << 16); o[1] = __uint_as_float(v & 0xffff0000u);
+  }
+};
 // Buffer resource over [base, base + bytes): stores whose offset falls outside
 // are dropped by the hardware.
 constexpr unsigned BUF_DW3 = 0x00020000u;
 constexpr uint32_t OOB = 0x80000000u;  // any offset >= the range is dropped
 
-template <typename TV>
-__device__ __forceinline__ void st4b(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[4]);
-template <>
-__device__ __forceinline__ void st4b<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[4]) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(
-      u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}, r, off, 0,
-      0);
-}
-template <>
-__device__ __forceinline__ void st4b<bf16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, const float v[4]) {
+// CH channels of one thread at byte offset off of a buffer resource
+template <typename TV, int CH>
+__device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2_hw(v[0], v[1]), pack_bf2_hw(v[2], v[3])}, r, off, 0, 0);
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (std::is_same<TV, float>::value && CH == 4)
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])}, r, off,
+        0, 0);
+  else if constexpr (std::is_same<TV, float>::value)
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v[0]), __float_as_uint(v[1])}, r, off, 0, 0);
+  else if constexpr (CH == 4)
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2_hw(v[0], v[1]), pack_bf2_hw(v[2], v[3])}, r, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf2_hw(v[0], v[1]), r, off, 0, 0);
 }
 
 // Sum over the 16 lanes of a DPP row (every lane gets it).
@@ -81,12 +108,13 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Where a workgroup works: sequence b, token positions [p0, p1), channels c0..c0+3
-// of its thread (cok: inside C; C % 4 == 0).
+// Where a workgroup works: sequence b, token positions [p0, p1), channels
+// c0..c0+CH-1 of its thread (cok: inside C; C % 4 == 0).
 struct Place {
   int64_t b, p0, p1, c0;
   bool cok;
 };
+template <int CH>
 __device__ __forceinline__ Place place(int64_t S, int64_t C, int nstrip, int nslice) {
   const int slice = (int)(blockIdx.x % nslice);
   const int64_t rest = blockIdx.x / nslice;
@@ -95,19 +123,21 @@ __device__ __forceinline__ Place place(int64_t S, int64_t C, int nstrip, int nsl
   pl.b = rest / nstrip;
   pl.p0 = strip * ATT;
   pl.p1 = pl.p0 + ATT < S ? pl.p0 + ATT : S;
-  const int64_t c = (int64_t)slice * ACS + threadIdx.x * ACH;
+  const int64_t c = (int64_t)slice * (256 * CH) + threadIdx.x * CH;
   pl.cok = c < C;
   pl.c0 = pl.cok ? c : 0;
   return pl;
 }
 
-// The taps of the three convs for channels c0..c0+3 (w: [C, 4] | [C, 8] | [C, 12]).
+// The taps of the three convs for channels c0..c0+CH-1 (w: [C, 4] | [C, 8] | [C, 12]).
+template <int CH>
 struct Taps {
-  float w1[K1][ACH], w2[K2][ACH], w3[K3][ACH];
+  float w1[K1][CH], w2[K2][CH], w3[K3][CH];
 };
-__device__ __forceinline__ void load_taps(const float* __restrict__ w, int64_t C, int64_t c0, Taps& tp) {
+template <int CH>
+__device__ __forceinline__ void load_taps(const float* __restrict__ w, int64_t C, int64_t c0, Taps<CH>& tp) {
 #pragma unroll
-  for (int ch = 0; ch < ACH; ++ch) {
+  for (int ch = 0; ch < CH; ++ch) {
     const float* p1 = w + (c0 + ch) * K1;
     const float* p2 = w + K1 * C + (c0 + ch) * K2;
     const float* p3 = w + (K1 + K2) * C + (c0 + ch) * K3;
@@ -133,38 +163,18 @@ __device__ __forceinline__ void load_taps(const float* __restrict__ w, int64_t C
 // receives a[0..3][ch] = F, g1, g2, g3 of token p (zeros past C).
 constexpr int PF = 4;  // rows in flight (divides 12; 4 measured faster than 6 or 12)
 
-// A row of this thread's 4 channels as loaded (converted to float when it
-// enters the ring, so a load in the queue is not waited for before then).
-template <typename TF>
-struct RawRow;
-template <>
-struct RawRow<float> {
-  float4 v;
-  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
-  __device__ __forceinline__ void get(float o[4]) const { o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; }
-};
-template <>
-struct RawRow<bf16_t> {
-  uint2 v;
-  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void get(float o[4]) const {
-    o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xffff0000u);
-    o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xffff0000u);
-  }
-};
-
-template <bool FC, typename TF, typename Fn>  // FC: C is a multiple of the slice width
+template <bool FC, int CH, typename TF, typename Fn>  // FC: C is a multiple of the slice width
 __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, int64_t C, const Place& pl,
-                                           const Taps& tp, Fn fn) {
+                                           const Taps<CH>& tp, Fn fn) {
   static_assert(K3 % PF == 0 && ATT % K3 == 0, "ring and queue slots must be compile-time constants");
   const TF* base = F + pl.b * S * C + pl.c0;
   auto at = [&](int64_t p) __attribute__((always_inline)) { return base + (p < 0 ? 0 : (p < S ? p : S - 1)) * C; };
-  float ring[K3][ACH];
-  RawRow<TF> q[PF];
+  float ring[K3][CH];
+  RawRow<TF, CH> q[PF];
   {
     // rows p0-11 .. p0-1 in slots 1..11 and p0 in slot 0, all loads issued first;
     // rows before the sequence start are zeros (a mask, not a branch)
-    RawRow<TF> r0[K3];
+    RawRow<TF, CH> r0[K3];
 #pragma unroll
     for (int sl = 0; sl < K3; ++sl) r0[sl].load(at(sl == 0 ? pl.p0 : pl.p0 - K3 + sl));
 #pragma unroll
@@ -174,7 +184,7 @@ __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, 
       r0[sl].get(ring[sl]);
       const uint32_t keep = (sl == 0 || pl.p0 - K3 + sl >= 0) ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int ch = 0; ch < ACH; ++ch) ring[sl][ch] = __uint_as_float(__float_as_uint(ring[sl][ch]) & keep);
+      for (int ch = 0; ch < CH; ++ch) ring[sl][ch] = __uint_as_float(__float_as_uint(ring[sl][ch]) & keep);
     }
   }
   for (int blk = 0; blk < ATT / K3; ++blk) {
@@ -182,9 +192,9 @@ __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, 
     for (int u = 0; u < K3; ++u) {
       const int64_t p = pl.p0 + blk * K3 + u;
       q[u % PF].load(at(p + PF));  // the slot of row p, already in the ring
-      float a[4][ACH];
+      float a[4][CH];
 #pragma unroll
-      for (int ch = 0; ch < ACH; ++ch) {
+      for (int ch = 0; ch < CH; ++ch) {
         // tap s of a kappa-wide conv reads row p - kappa + 1 + s, in slot (u + 1 + s + 12 - kappa) mod 12
         float g1 = 0.f, g2 = 0.f, g3 = 0.f;
 #pragma unroll
@@ -211,11 +221,11 @@ __global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F,
                                                        const float* __restrict__ w, int nstrip, int nslice,
                                                        float* __restrict__ gram) {
   __shared__ float red[ATT][NG10][16];  // [token][entry][row of 16 lanes]; rows past the strip unused
-  const Place pl = place(S, C, nstrip, nslice);
-  Taps tp;
+  const Place pl = place<CH_G>(S, C, nstrip, nslice);
+  Taps<CH_G> tp;
   load_taps(w, C, pl.c0, tp);
   const int lane = threadIdx.x & 63, rowid = threadIdx.x >> 4;
-  walk_strip<FC, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+  walk_strip<FC, CH_G, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][CH_G]) __attribute__((always_inline)) {
     int q = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F,
       for (int j = i; j < 4; ++j) {
         float sacc = 0.f;
 #pragma unroll
-        for (int ch = 0; ch < ACH; ++ch) sacc += a[i][ch] * a[j][ch];
+        for (int ch = 0; ch < CH_G; ++ch) sacc += a[i][ch] * a[j][ch];
         sacc = row_sum16(sacc);
         if ((lane & 15) == 0) red[p - pl.p0][q][rowid] = sacc;
         ++q;
@@ -246,10 +256,11 @@ __global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F,
 // B[j][k] a_k.
 template <bool FC, typename TF, typename TV>
 __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
-                                                        const float* __restrict__ w, int nstrip, int nslice,
-                                                        const float* __restrict__ gram, TV* __restrict__ V) {
+                                                        const float* __restrict__ w, int nstrip, int nslice_a,
+                                                        int nslice, const float* __restrict__ gram,
+                                                        TV* __restrict__ V) {
   __shared__ float Bs[ATT][NB6];
-  const Place pl = place(S, C, nstrip, nslice);
+  const Place pl = place<CH_A>(S, C, nstrip, nslice_a);
   if ((int64_t)threadIdx.x < pl.p1 - pl.p0) {
     const int64_t t = pl.b * S + pl.p0 + threadIdx.x;
     double G[4][4];
@@ -300,30 +311,30 @@ __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F
     out[5] = (float)Bm[3][2];
   }
   __syncthreads();
-  Taps tp;
+  Taps<CH_A> tp;
   load_taps(w, C, pl.c0, tp);
   // V rows of this sequence through a buffer resource: a store of a token past
   // the strip or of channels past C gets an out-of-range offset and is dropped
   // (no branch around a store)
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
       V + pl.b * S * 4 * C, 0, (uint32_t)(S * 4 * C * (int64_t)sizeof(TV)), BUF_DW3);
-  walk_strip<FC, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][ACH]) __attribute__((always_inline)) {
+  walk_strip<FC, CH_A, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][CH_A]) __attribute__((always_inline)) {
     const float* bq = Bs[p - pl.p0];  // rows past the strip hold stale values (their stores are dropped)
     const bool ok = (FC || pl.cok) && p < pl.p1;
     auto off = [&](int j) __attribute__((always_inline)) {
       return ok ? (uint32_t)(((p * 4 + j) * C + pl.c0) * (int64_t)sizeof(TV)) : OOB;
     };
-    float v[ACH];
-    st4b<TV>(vres, off(0), a[0]);
+    float v[CH_A];
+    stb<TV, CH_A>(vres, off(0), a[0]);
 #pragma unroll
-    for (int ch = 0; ch < ACH; ++ch) v[ch] = a[1][ch] + bq[0] * a[0][ch];
-    st4b<TV>(vres, off(1), v);
+    for (int ch = 0; ch < CH_A; ++ch) v[ch] = a[1][ch] + bq[0] * a[0][ch];
+    stb<TV, CH_A>(vres, off(1), v);
 #pragma unroll
-    for (int ch = 0; ch < ACH; ++ch) v[ch] = a[2][ch] + bq[1] * a[0][ch] + bq[2] * a[1][ch];
-    st4b<TV>(vres, off(2), v);
+    for (int ch = 0; ch < CH_A; ++ch) v[ch] = a[2][ch] + bq[1] * a[0][ch] + bq[2] * a[1][ch];
+    stb<TV, CH_A>(vres, off(2), v);
 #pragma unroll
-    for (int ch = 0; ch < ACH; ++ch) v[ch] = a[3][ch] + bq[3] * a[0][ch] + bq[4] * a[1][ch] + bq[5] * a[2][ch];
-    st4b<TV>(vres, off(3), v);
+    for (int ch = 0; ch < CH_A; ++ch) v[ch] = a[3][ch] + bq[3] * a[0][ch] + bq[4] * a[1][ch] + bq[5] * a[2][ch];
+    stb<TV, CH_A>(vres, off(3), v);
   });
 }
 
@@ -331,19 +342,21 @@ template <typename TF, typename TV>
 hipError_t launch_aug(const void* F, int64_t B, int64_t S, int64_t C, const float* w, void* V, float* gram,
                       hipStream_t st) {
   const int nstrip = (int)((S + ATT - 1) / ATT);
-  const int nslice = (int)((C + ACS - 1) / ACS);
-  const dim3 grid((unsigned)(B * nstrip * nslice)), blk(256);
-  const bool fc = C % ACS == 0;
-  if (fc) hipLaunchKernelGGL((aug_gram_kernel<true, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
-  else hipLaunchKernelGGL((aug_gram_kernel<false, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
+  const int nslice = (int)((C + 256 * CH_G - 1) / (256 * CH_G));
+  const int nslice_a = (int)((C + 256 * CH_A - 1) / (256 * CH_A));
+  const dim3 grid((unsigned)(B * nstrip * nslice)), grid_a((unsigned)(B * nstrip * nslice_a)), blk(256);
+  if (C % (256 * CH_G) == 0)
+    hipLaunchKernelGGL((aug_gram_kernel<true, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
+  else
+    hipLaunchKernelGGL((aug_gram_kernel<false, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (fc)
-    hipLaunchKernelGGL((aug_apply_kernel<true, TF, TV>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice,
-                       (const float*)gram, (TV*)V);
+  if (C % (256 * CH_A) == 0)
+    hipLaunchKernelGGL((aug_apply_kernel<true, TF, TV>), grid_a, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice_a,
+                       nslice, (const float*)gram, (TV*)V);
   else
-    hipLaunchKernelGGL((aug_apply_kernel<false, TF, TV>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice,
-                       (const float*)gram, (TV*)V);
+    hipLaunchKernelGGL((aug_apply_kernel<false, TF, TV>), grid_a, blk, 0, st, (const TF*)F, S, C, w, nstrip,
+                       nslice_a, nslice, (const float*)gram, (TV*)V);
   return hipGetLastError();
 }
 
@@ -359,7 +372,7 @@ bool fast_augment_supported(int dtype, int vdtype, int64_t S, int64_t C, const i
 }
 
 int64_t fast_augment_workspace_bytes(int64_t B, int64_t S, int64_t C) {
-  return B * S * ((C + ACS - 1) / ACS) * NG10 * 4;
+  return B * S * ((C + 256 * CH_G - 1) / (256 * CH_G)) * NG10 * 4;
 }
 
 hipError_t launch_fast_augment(int dtype, int vdtype, const void* F, int64_t B, int64_t S, int64_t C,
