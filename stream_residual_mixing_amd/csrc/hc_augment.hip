@@ -10,17 +10,18 @@
 // Every inner product here is a combination of the entries of the 4x4 Gram
 // matrix G = [<a_i, a_j>] of the token: writing v_j = sum_k B[j][k] a_k,
 //   <a_j, v_i> = sum_k B[i][k] G[k][j],  <v_i, v_i> = B_i^T G B_i,
-// so the first pass only accumulates G (per token, per 1024-channel slice) and
+// so the first pass only accumulates G (per token, per 512-channel slice) and
 // the second pass rebuilds B (in float64) and writes V = B A. The full-C
 // reductions then need no workgroup to hold a token's whole row. (In float32
 // this matches float64 modified Gram-Schmidt to about 3e-8 relative L2 on
 // data of this shape, as the float32 modified form does.)
 //
-// Workgroup: 256 threads x CH channels (CH = 4 in the Gram pass, 2 in the apply
-// pass) = a slice of 1024 or 512 channels, over a strip of 36 consecutive
-// tokens of one sequence; each thread keeps its channels' 24 conv taps and the
-// last 12 rows of F in registers, so F is read once per pass (plus an 11-row
-// halo per strip).
+// The Gram pass works one position per lane (below); the apply pass, whose
+// stores must run along the channels, works one channel pair per thread: a
+// workgroup of 256 threads x 2 channels = a 512-channel slice, over a strip of
+// 36 consecutive tokens of one sequence; each thread keeps its channels' 24 conv
+// taps and the last 12 rows of F in registers, so F is read once per pass (plus
+// an 11-row halo per strip).
 #include <type_traits>
 
 #include "hc_device.h"
@@ -32,12 +33,9 @@ namespace {
 
 constexpr int K1 = 4, K2 = 8, K3 = 12;
 constexpr int ATT = 3 * K3;         // tokens per strip (a multiple of the ring length)
-// Channels per thread of the two passes (a workgroup of 256 threads covers 256 x
-// that many): the Gram pass reduces each token's products across the threads of
-// a slice, so 4 channels per thread halve that work per channel; the apply pass
-// has no such reduction and runs more waves per SIMD with 2 (half the registers
-// for taps and the ring).
-constexpr int CH_G = 4;
+// Channels per thread of the apply pass (a workgroup of 256 threads covers 512):
+// 2 rather than 4 halves the registers for taps and the ring, for more waves
+// per SIMD.
 constexpr int CH_A = 2;
 constexpr int NG10 = 10;            // upper triangle of the 4x4 Gram matrix
 constexpr int NB6 = 6;              // strictly lower part of B
@@ -94,18 +92,6 @@ __device__ __forceinline__ void stb(__amdgpu_buffer_rsrc_t r, uint32_t off, cons
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2_hw(v[0], v[1]), pack_bf2_hw(v[2], v[3])}, r, off, 0, 0);
   else
     __builtin_amdgcn_raw_buffer_store_b32(pack_bf2_hw(v[0], v[1]), r, off, 0, 0);
-}
-
-// Sum over the 16 lanes of a DPP row (every lane gets it).
-__device__ __forceinline__ float row_sum16(float v) {
-  auto dpp = [](float x, auto ctrl) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, true));
-  };
-  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
-  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
-  v += dpp(v, std::integral_constant<int, 0x124>{});  // row_ror:4
-  v += dpp(v, std::integral_constant<int, 0x128>{});  // row_ror:8
-  return v;
 }
 
 // Where a workgroup works: sequence b, token positions [p0, p1), channels
@@ -215,39 +201,141 @@ __device__ __forceinline__ void walk_strip(const TF* __restrict__ F, int64_t S, 
   }
 }
 
-// Pass 1: partial Gram matrices gram[t][slice][10] (upper triangle, row-major).
-template <bool FC, typename TF>
-__global__ __launch_bounds__(256) void aug_gram_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
-                                                       const float* __restrict__ w, int nstrip, int nslice,
-                                                       float* __restrict__ gram) {
-  __shared__ float red[ATT][NG10][16];  // [token][entry][row of 16 lanes]; rows past the strip unused
-  const Place pl = place<CH_G>(S, C, nstrip, nslice);
-  Taps<CH_G> tp;
-  load_taps(w, C, pl.c0, tp);
-  const int lane = threadIdx.x & 63, rowid = threadIdx.x >> 4;
-  walk_strip<FC, CH_G, TF>(F, S, C, pl, tp, [&](int64_t p, const float (&a)[4][CH_G]) __attribute__((always_inline)) {
-    int q = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = i; j < 4; ++j) {
-        float sacc = 0.f;
-#pragma unroll
-        for (int ch = 0; ch < CH_G; ++ch) sacc += a[i][ch] * a[j][ch];
-        sacc = row_sum16(sacc);
-        if ((lane & 15) == 0) red[p - pl.p0][q][rowid] = sacc;
-        ++q;
-      }
-  });
-  __syncthreads();
+// Pass 1: partial Gram matrices gram[t][slice][10] (upper triangle, row-major),
+// one position per lane. A workgroup of 1024 threads (16 waves) takes a block of
+// GT = 256 consecutive positions of one sequence (lane l of every wave: positions
+// 4l..4l+3 of the block) and a slice of GCS channels, in chunks of 64 channels
+// staged through LDS as float columns [channel][row], row 0 = 11 positions before
+// the block (zeros before the sequence start and past C). Wave w takes channels
+// w, w + 16, w + 32, w + 48 of each chunk: the channel is the same across the
+// wave, so its 24 taps come by scalar loads, and each lane adds its 4 positions'
+// 10 products over its channels with no exchange between lanes. The 16 waves'
+// sums are added through LDS at the end, in wave order.
+constexpr int GW = 1024;               // threads per workgroup
+constexpr int GT = 256;                // positions per workgroup (4 per lane)
+constexpr int GCK = 64;                // channels per LDS chunk
+constexpr int GCS = 8 * GCK;           // channels per workgroup
+constexpr int GROWS = GT + K3 - 1;     // staged rows of a chunk
+// Column of one channel: 16-byte blocks of 4 rows; block b of channel c sits at
+// block position b ^ (c / 4 mod 16), so the staging writes (16 lanes, 16 channel
+// groups, one row) and the window reads (64 lanes, 64 consecutive blocks) both
+// hit distinct banks. 80 blocks = 320 rows cover every swizzled position.
+constexpr int GRS = 320;
+static_assert(((GROWS + 3) / 4 + 3 + 15) / 16 * 16 * 4 <= GRS, "swizzled blocks fit the column");
+constexpr int GUNITS = GROWS * (GCK / 4);  // staging units of 4 channels x 1 row per chunk
+constexpr int GUPT = (GUNITS + GW - 1) / GW;
+
+__device__ __forceinline__ int gswz(int cl, int row) {  // LDS float index of (channel cl, row)
+  return cl * GRS + ((((row >> 2) ^ ((cl >> 2) & 15))) << 2) + (row & 3);
+}
+
+template <typename TF>
+__global__ __launch_bounds__(GW) void aug_gram_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
+                                                      const float* __restrict__ w, int nblk, int nslice,
+                                                      float* __restrict__ gram) {
+  __shared__ __attribute__((aligned(16))) float tile[GCK * GRS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slice = (int)(blockIdx.x % nslice);
-  const int n = (int)(pl.p1 - pl.p0) * NG10;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int tk = i / NG10, k = i - tk * NG10;
-    float v = 0.f;
+  const int64_t rest = blockIdx.x / nslice;
+  const int64_t b = rest / nblk, p0 = (rest % nblk) * GT;
+  const int64_t cbase = (int64_t)slice * GCS;
+  const TF* Fb = F + b * S * C;
+  // staging: unit u = (row u / 16, channels 4 (u % 16) .. +3 of the chunk)
+  RawRow<TF, 4> st[GUPT];
+  auto stage_load = [&](int k) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v += red[tk][k][r];
-    gram[((pl.b * S + pl.p0 + tk) * nslice + slice) * NG10 + k] = v;
+    for (int i = 0; i < GUPT; ++i) {
+      const int u = i * GW + tid;
+      const int r = (u < GUNITS ? u : GUNITS - 1) >> 4;
+      const int64_t pos = p0 - (K3 - 1) + r;
+      const int64_t c = cbase + (int64_t)k * GCK + (u & 15) * 4;
+      st[i].load(Fb + (pos < 0 ? 0 : (pos < S ? pos : S - 1)) * C + (c < C ? c : 0));
+    }
+  };
+  auto stage_store = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < GUPT; ++i) {
+      const int u = i * GW + tid;
+      if (u < GUNITS) {
+        const int r = u >> 4, g = u & 15;
+        const int64_t pos = p0 - (K3 - 1) + r;
+        const bool ok = pos >= 0 && cbase + (int64_t)k * GCK + g * 4 < C;
+        float v[4];
+        st[i].get(v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[gswz(g * 4 + e, r)] = ok ? v[e] : 0.f;
+      }
+    }
+  };
+  float acc[4][NG10];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < NG10; ++q) acc[j][q] = 0.f;
+  const int nchunk = (int)((C - cbase + GCK - 1) / GCK < GCS / GCK ? (C - cbase + GCK - 1) / GCK : GCS / GCK);
+  stage_load(0);
+  for (int k = 0; k < nchunk; ++k) {
+    __syncthreads();  // the previous chunk's reads are done
+    stage_store(k);
+    __syncthreads();
+    if (k + 1 < nchunk) stage_load(k + 1);
+#pragma unroll
+    for (int cw = 0; cw < GCK / 16; ++cw) {
+      const int cl = wv + 16 * cw;  // channel within the chunk (uniform over the wave)
+      int64_t c = cbase + (int64_t)k * GCK + cl;
+      c = c < C ? c : 0;
+      const float* t1 = w + c * K1;
+      const float* t2 = w + K1 * C + c * K2;
+      const float* t3 = w + (K1 + K2) * C + c * K3;
+      float x[16];  // rows 4l .. 4l+15 of this channel
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&tile[gswz(cl, 4 * (lane + bi))]);
+        x[4 * bi] = q4.x;
+        x[4 * bi + 1] = q4.y;
+        x[4 * bi + 2] = q4.z;
+        x[4 * bi + 3] = q4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // position 4l + j of the block is row 4l + j + 11
+        float a[4];
+        a[0] = x[j + K3 - 1];
+        float g1 = 0.f, g2 = 0.f, g3 = 0.f;
+#pragma unroll
+        for (int s = 0; s < K1; ++s) g1 += t1[s] * x[j + K3 - K1 + s];
+#pragma unroll
+        for (int s = 0; s < K2; ++s) g2 += t2[s] * x[j + K3 - K2 + s];
+#pragma unroll
+        for (int s = 0; s < K3; ++s) g3 += t3[s] * x[j + s];
+        a[1] = g1;
+        a[2] = g2;
+        a[3] = g3;
+        int q = 0;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+#pragma unroll
+          for (int j2 = i2; j2 < 4; ++j2) acc[j][q++] += a[i2] * a[j2];
+      }
+    }
+  }
+  // the 16 waves' sums, in two rounds of 5 entries: [wave][entry][position]
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 5; ++q) tile[(wv * 5 + q) * GT + 4 * lane + j] = acc[j][half * 5 + q];
+    __syncthreads();
+    for (int i = tid; i < 5 * GT; i += GW) {
+      const int q = i / GT, pp = i - q * GT;
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < GW / 64; ++ww) v += tile[(ww * 5 + q) * GT + pp];
+      const int64_t pos = p0 + pp;
+      if (pos < S) gram[((b * S + pos) * nslice + slice) * NG10 + half * 5 + q] = v;
+    }
   }
 }
 
@@ -342,13 +430,11 @@ template <typename TF, typename TV>
 hipError_t launch_aug(const void* F, int64_t B, int64_t S, int64_t C, const float* w, void* V, float* gram,
                       hipStream_t st) {
   const int nstrip = (int)((S + ATT - 1) / ATT);
-  const int nslice = (int)((C + 256 * CH_G - 1) / (256 * CH_G));
+  const int nblk = (int)((S + GT - 1) / GT);
+  const int nslice = (int)((C + GCS - 1) / GCS);
   const int nslice_a = (int)((C + 256 * CH_A - 1) / (256 * CH_A));
-  const dim3 grid((unsigned)(B * nstrip * nslice)), grid_a((unsigned)(B * nstrip * nslice_a)), blk(256);
-  if (C % (256 * CH_G) == 0)
-    hipLaunchKernelGGL((aug_gram_kernel<true, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
-  else
-    hipLaunchKernelGGL((aug_gram_kernel<false, TF>), grid, blk, 0, st, (const TF*)F, S, C, w, nstrip, nslice, gram);
+  const dim3 grid((unsigned)(B * nblk * nslice)), grid_a((unsigned)(B * nstrip * nslice_a)), blk(256);
+  hipLaunchKernelGGL(aug_gram_kernel<TF>, grid, dim3(GW), 0, st, (const TF*)F, S, C, w, nblk, nslice, gram);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (C % (256 * CH_A) == 0)
@@ -372,7 +458,7 @@ bool fast_augment_supported(int dtype, int vdtype, int64_t S, int64_t C, const i
 }
 
 int64_t fast_augment_workspace_bytes(int64_t B, int64_t S, int64_t C) {
-  return B * S * ((C + 256 * CH_G - 1) / (256 * CH_G)) * NG10 * 4;
+  return B * S * ((C + GCS - 1) / GCS) * NG10 * 4;
 }
 
 hipError_t launch_fast_augment(int dtype, int vdtype, const void* F, int64_t B, int64_t S, int64_t C,
