@@ -63,6 +63,38 @@ __device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
   v[6] = bf2f(q.w & 0xffffu); v[7] = __uint_as_float(q.w & 0xffff0000u);
 }
 
+// Nontemporal forms for state streamed once per pass (it does not displace what
+// L2 holds for reuse).
+__device__ __forceinline__ void load8_nt(const float* p, float v[8]) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 a = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  const f4 b = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p) + 1);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void load8_nt(const bf16_t* p, float v[8]) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  const u4 q = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
+  v[0] = bf2f(q.x & 0xffffu); v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = bf2f(q.y & 0xffffu); v[3] = __uint_as_float(q.y & 0xffff0000u);
+  v[4] = bf2f(q.z & 0xffffu); v[5] = __uint_as_float(q.z & 0xffff0000u);
+  v[6] = bf2f(q.w & 0xffffu); v[7] = __uint_as_float(q.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ void store8_nt(float* p, const float v[8]) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(f4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4*>(p));
+  __builtin_nontemporal_store(f4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f4*>(p) + 1);
+}
+
+__device__ __forceinline__ void store8_nt(bf16_t* p, const float v[8]) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                                 pack_bf2(v[6], v[7])},
+                              reinterpret_cast<u4*>(p));
+}
+
 __device__ __forceinline__ void store8(float* p, const float v[8]) {
   reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);

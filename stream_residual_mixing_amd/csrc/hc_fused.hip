@@ -386,22 +386,41 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
   constexpr bool DEEP = !POST && !(MODE == ROWS_GATHER && NB >= 4);  // (the latter has no registers left)
   static_assert(2 * SPI % 4 == 0, "queue slots of the deep prefetch");
   uint4 xq[DEEP ? 4 : 1][NS4];
+  // DEEP: the B fragments of the super-chunk being multiplied. Each stream's are
+  // replaced by the next super-chunk's as soon as its MFMAs have issued, so that
+  // load has a whole super-chunk to arrive (the copy into LDS is too short to
+  // hide an L2 round trip).
+  uint4 pfq[DEEP ? NS4 : 1][NB];
+  auto load_pf = [&](const Item& it2, int64_t s2, int i, uint4 (&dst)[NB]) __attribute__((always_inline)) {
+    const int64_t cg = s2 * SC + wave * 32;
+    const int64_t cgc = cg < C ? cg : C - 32;
+    const int64_t prow0 = (MODE == ROWS_GROUPS ? 4 * it2.g : 0) * C;
+    const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + i * C + cgc) / 8 + q) * NCP + tau;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dst[b] = pb[b * 16];
+  };
+  // Without POST the tile holds zeros for rows past T and channels past C.
+  auto mfma_phase_deep = [&](const unsigned char* buf, const Item& nit, int64_t ns) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const uint4 af =
+            *reinterpret_cast<const uint4*>(buf + (i * TILE + tb * TOK + tau) * LROW + (wave * 32 + q * 8) * 2);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pfq[i][b]), acc[tb][b], 0, 0, 0);
+        gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
+      }
+      if constexpr (DEEP) load_pf(nit, ns, i, pfq[i]);
+    }
+  };
   auto body_deep = [&](const Item& it, auto J, const int* gt, const Item& nx, const int* ngt, unsigned char* buf)
                        __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     constexpr int h0 = 2 * j, h1 = 2 * j + 1;
     constexpr int q0 = DEEP ? h0 % 4 : 0, q1 = DEEP ? h1 % 4 : 0;
     const int64_t s = it.s0 + j;
-    const int64_t cg = s * SC + wave * 32;
-    const int64_t cgc = cg < C ? cg : C - 32;
-    const int64_t prow0 = (MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
-    uint4 pf[NS4][NB];
-#pragma unroll
-    for (int i = 0; i < NS4; ++i) {
-      const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + i * C + cgc) / 8 + q) * NCP + tau;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) pf[i][b] = pb[b * 16];
-    }
     uint4 fz = make_uint4(0, 0, 0, 0);
     const __amdgpu_buffer_rsrc_t nores = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0u, BUF_DW3);
     stream_half(it, s, H0{}, xq[q0], fz, buf, nullptr, nores);
@@ -411,7 +430,9 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     if constexpr (h1 + 4 < 2 * SPI) load_half(it, it.s0 + (h1 + 4) / 2, gt, H1{}, xq[q1], fz);
     else load_half(nx, nx.s0 + (h1 + 4 - 2 * SPI) / 2, ngt, H1{}, xq[q1], fz);
     __syncthreads();
-    mfma_phase(it, s, buf, pf);
+    // the next super-chunk: this item's next one, or the next item's first
+    if constexpr (j + 1 < SPI) mfma_phase_deep(buf, it, it.s0 + j + 1);
+    else mfma_phase_deep(buf, nx, nx.s0);
   };
 
   int item = (int)blockIdx.x;
@@ -431,6 +452,8 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     load_half(it, it.s0, gtab, H1{}, xq[1], fz);
     load_half(it, it.s0 + 1, gtab, H0{}, xq[2], fz);
     load_half(it, it.s0 + 1, gtab, H1{}, xq[3], fz);
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) load_pf(it, it.s0, i, pfq[i]);
   } else {
     load_half(it, it.s0, gtab, H0{}, xA, fA);
   }

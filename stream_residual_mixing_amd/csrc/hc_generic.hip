@@ -191,16 +191,26 @@ __global__ __launch_bounds__(256) void pre_generic_kernel(
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float w = h[t * n + i];
-    float x[8];
-    const T* p = X + (t * n + i) * C + c0;
-    if (VEC) load8(p, x); else load8_tail(p, cnt, x);
+  // rows 4 at a time, all 4 loads issued before use; past n the row index is
+  // clamped (no branch around a load) and the row is not added
+  for (int i0 = 0; i0 < n; i0 += 4) {
+    float x[4][8], w[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u < n ? i0 + u : n - 1;
+      w[u] = h[t * n + i];
+      const T* p = X + (t * n + i) * C + c0;
+      if (VEC) load8_nt(p, x[u]); else load8_tail(p, cnt, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u < n) {  // (a padded row times a zero weight could still give NaN)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w[u] * x[u][e];
+      }
   }
   T* q = F_in + t * C + c0;
-  if (VEC) store8(q, acc); else store8_tail(q, cnt, acc);
+  if (VEC) store8_nt(q, acc); else store8_tail(q, cnt, acc);
 }
 
 // --------------------------------------------------------------------------
@@ -222,9 +232,9 @@ __global__ __launch_bounds__(256) void post_generic_kernel(
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const T* p = X + (t * NS + j) * C + c0;
-    if (VEC) load8(p, x[j]); else load8_tail(p, cnt, x[j]);
+    if (VEC) load8_nt(p, x[j]); else load8_tail(p, cnt, x[j]);
   }
-  if (VEC) load8(F + t * C + c0, f); else load8_tail(F + t * C + c0, cnt, f);
+  if (VEC) load8_nt(F + t * C + c0, f); else load8_tail(F + t * C + c0, cnt, f);
   const float* hr = h_res + t * NS * NS;
   const float* hp = h_post + t * NS;
 #pragma unroll
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(256) void post_generic_kernel(
       for (int e = 0; e < 8; ++e) y[e] += w * x[j][e];
     }
     T* q = Y + (t * NS + i) * C + c0;
-    if (VEC) store8(q, y); else store8_tail(q, cnt, y);
+    if (VEC) store8_nt(q, y); else store8_tail(q, cnt, y);
   }
 }
 
