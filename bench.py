@@ -181,6 +181,24 @@ def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     return out
 
 
+def device_copy_rate(torch, hc, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Read + write GB/s of the library's streaming copy probe (16-byte nontemporal
+    loads and stores) over three rotating buffer pairs of `nbytes`: the practical
+    streaming ceiling of this device, measured on the same box."""
+    src = [torch.full((nbytes // 4,), float(i), dtype=torch.float32, device=dev) for i in range(3)]
+    dst = [torch.empty(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+    for i in range(3):
+        hc.hc_copy_probe(src[i], dst[i])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        hc.hc_copy_probe(src[i % 3], dst[i % 3])
+    b.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def torch_copy_rate(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Read + write GB/s of torch's own device-to-device copy of `nbytes` (three
     rotating buffer pairs) on the same box: context for the streaming rate of this
@@ -212,31 +230,41 @@ def load_traffic(kernel: str, digest: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
+def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0, single_seconds: float = 3.0) -> dict:
     """The fp64 oracle (as is) over 512-token chunks of the same workload, cycling
-    through the 8192 tokens until at least `min_seconds` of work has run."""
+    through the 8192 tokens until at least `min_seconds` of work has run with the
+    host's BLAS threads, then for `single_seconds` with one thread."""
     import synth
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     w = synth.WORKLOADS[WORKLOAD]
     T, n, C = w["T"], w["n"], w["C"]
     inp = synth.mhc_layer(w["seed"], 0, T, n, C, w["dtype"])
     Xv, Fv = inp["X"].values, inp["F_out"].values
-    done, start, chunk = 0, time.perf_counter(), 512
-    elapsed = 0.0
-    while elapsed < min_seconds:
-        s = done % T
-        O.mhc_sublayer(Xv[s:s + chunk], inp["phi"], inp["bias"], inp["alpha"], Fv[s:s + chunk],
-                       SINKHORN_ITERS)
-        done += chunk
-        elapsed = time.perf_counter() - start
-        if elapsed > max_seconds:
-            break
+    chunk = 512
+
+    def run(seconds, cap):
+        done, start, elapsed = 0, time.perf_counter(), 0.0
+        while elapsed < seconds:
+            s = done % T
+            O.mhc_sublayer(Xv[s:s + chunk], inp["phi"], inp["bias"], inp["alpha"], Fv[s:s + chunk],
+                           SINKHORN_ITERS)
+            done += chunk
+            elapsed = time.perf_counter() - start
+            if elapsed > cap:
+                break
+        return done, elapsed
+
+    done, elapsed = run(min_seconds, max_seconds)
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    with threadpool_limits(limits=1):
+        done1, elapsed1 = run(single_seconds, 3 * single_seconds)
     return {"value": done / elapsed, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} tokens ({done // chunk} chunks of {chunk}) of the n=4 C=4096 bf16 workload, "
-                      f"{elapsed:.1f} s, numpy fp64 with {threads} BLAS threads"}
+                      f"{elapsed:.1f} s, numpy fp64 with {threads} BLAS threads",
+            "single_thread": {"value": done1 / elapsed1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{done1} tokens, {elapsed1:.1f} s, one BLAS thread"}}
 
 
 def main() -> int:
@@ -423,6 +451,7 @@ def main() -> int:
         "isolated_sublayer": dict(rate(iso_wall, iso_bytes), calls_us={k: v * 1e6 for k, v in iso_kern.items()},
                                   algorithmic_bytes_per_step=iso_bytes),
         "call_durations": dist,
+        "device_copy_ceiling_GBps": device_copy_rate(torch, hc, dev),
         "torch_copy_GBps": torch_copy_rate(torch, dev),
         "source_digest": digest,
     }

@@ -267,6 +267,20 @@ int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
                 const float* conv_w, const int* kappa, int r,
                 void* V, int v_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ measurement -- */
+
+/*
+ * hc_copy_probe - not part of the method: a plain device-to-device copy of
+ * `bytes` bytes with 16-byte nontemporal loads and stores, the access pattern
+ * the streaming kernels use, so that a benchmark can measure the practical HBM
+ * streaming rate of the device it runs on next to the sublayer's rate.
+ *   src, dst: device pointers, 16-byte aligned, not overlapping; bytes >= 0 and
+ *   a multiple of 16 (bytes == 0 does nothing; pointers may then be NULL).
+ *   Errors: HC_ERR_NULL, HC_ERR_SHAPE (bytes < 0), HC_ERR_ALIGN (alignment or
+ *   bytes % 16), HC_ERR_ALIAS (overlap).
+ */
+int hc_copy_probe(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

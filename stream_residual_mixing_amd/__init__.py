@@ -50,6 +50,7 @@ _SIGS = {
                            _vp]),
     "xhc_augment_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int, _c_int]),
     "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
+    "hc_copy_probe": (_c_int, [_vp, _vp, _c_i64, _vp]),
 }
 
 _lib = None
@@ -340,9 +341,21 @@ def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, workspace=No
     return V
 
 
+def hc_copy_probe(src, dst, *, stream=None):
+    """Copy src into dst (same byte size, 16-byte aligned) with the library's streaming
+    copy: a measurement probe of the device's streaming rate, not part of the method."""
+    src = _dev_tensor(src, "src")
+    dst = _dev_tensor(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("hc_copy_probe needs contiguous tensors of the same byte size")
+    _check("hc_copy_probe", lib().hc_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device, stream)))
+    return dst
+
+
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
     "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
-    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment",
+    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_copy_probe",
 ]

@@ -644,4 +644,15 @@ int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, c
                                                   (hipStream_t)stream));
 }
 
+int hc_copy_probe(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0) return HC_ERR_SHAPE;
+  if (bytes == 0) return HC_OK;
+  if (!src || !dst) return HC_ERR_NULL;
+  if (bytes % 16 != 0 || !aligned_to(src, 16) || !aligned_to(dst, 16)) return HC_ERR_ALIGN;
+  if (overlaps(src, bytes, dst, bytes)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_copy_probe(src, dst, bytes, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -52,6 +52,8 @@ hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int 
                                 const float* b_pre, float a_pre, const float* w_router, float* h_pre, float* score,
                                 int32_t* idx, void* F_in, void* packed, float* partial, hipStream_t st);
 // Active coefficients H_post [T, 4, K], H_res [T, 4, 4] of the streams idx[t, 0..3].
+// Streaming copy of `bytes` (a multiple of 16; 16-byte aligned pointers).
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, hipStream_t st);
 // xHC mix + scatter in place for k = 4 bfloat16 active streams, 1 <= K <= 4
 // (C % 8 == 0, X and Wb 16-byte aligned).
 bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const void* Wb);

@@ -1236,6 +1236,33 @@ hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int 
   return launch_pre_wide(X, T, N, C, h_pre, F_in, st);
 }
 
+// Streaming copy of n16 16-byte words: 4 per thread, all loads issued before
+// the stores, nontemporal both ways (the probe of the streaming rate).
+__global__ __launch_bounds__(256) void copy_probe_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                         int64_t n16) {
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  u32x4_t v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int64_t i = base + k * 256;
+    i = i < n16 ? i : n16 - 1;
+    v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + i));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = base + k * 256;
+    if (i < n16) __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4_t*>(dst + i));
+  }
+}
+
+hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)((n16 + 1023) / 1024)), dim3(256), 0, st,
+                     (const uint4*)src, (uint4*)dst, n16);
+  return hipGetLastError();
+}
+
 bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const void* Wb) {
   return dtype == 1 && k == 4 && K >= 1 && K <= 4 && C % 8 == 0 && a16(X) && a16(Wb);
 }

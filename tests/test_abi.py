@@ -155,6 +155,18 @@ def test_validation_rejects_bad_arguments_before_device_work(hc):
     assert L.xhc_augment_workspace_bytes(2, 16, 64, karr, 3, 9, 1) == -1
 
 
+def test_copy_probe_validation(hc):
+    L = hc.lib()
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert L.hc_copy_probe(a, b, 0, None) == 0
+    assert L.hc_copy_probe(None, None, 0, None) == 0
+    assert L.hc_copy_probe(a, b, -16, None) == -2
+    assert L.hc_copy_probe(None, b, 64, None) == -1
+    assert L.hc_copy_probe(a, b, 24, None) == -4
+    assert L.hc_copy_probe(ctypes.c_void_p(0x100008), b, 64, None) == -4
+    assert L.hc_copy_probe(a, ctypes.c_void_p(0x100010), 64, None) == -5
+
+
 @pytest.mark.skipif(have_gpu(), reason="checks the no-device status; on a GPU box the call would run")
 def test_valid_call_without_device_reports_device_error(hc):
     L = hc.lib()
