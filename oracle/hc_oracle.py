@@ -306,3 +306,52 @@ def xhc_augment(F_out, conv_ws, batch: int, seq: int):
     F = _f64(F_out)
     comps = [F] + [causal_dwconv(F, w, batch, seq) for w in conv_ws]
     return modified_gram_schmidt(np.stack(comps, axis=1))
+
+
+# ---------------------------------------------------------------------------
+# The unconstrained HC baseline and the gain of a chain of residual maps
+# ---------------------------------------------------------------------------
+
+def hc_tanh_coeffs(X, theta, bias, alpha):
+    """Hyper-Connections' maps (mHC notes, section 3 Preliminary, Eq. 5).
+
+    Each stream row x_i (length C) of a token is RMS-normalised on its own (the
+    last dimension; reading: no learnable gain and no epsilon, and an all-zero
+    row gives x~ = 0), then
+        H_pre[i]     = a_pre  * tanh(theta_pre    . x~_i) + b_pre[i]
+        H_post[i]    = a_post * tanh(theta_post   . x~_i) + b_post[i]
+        H_res[j, i]  = a_res  * tanh(theta_res[j] . x~_i) + b_res[j, i]
+    (H_res = a tanh(theta_res x~^T) + b: row j, column i; row j is output stream j
+    of the residual update, as in the mHC calls).
+    theta: [n + 2, C] rows (pre, post, res_0 .. res_{n-1}); bias: [n*n + 2n]
+    (pre n | post n | res n*n row-major); alpha = (pre, post, res).
+    Returns h_pre [T, n], h_post [T, n], h_res [T, n, n].
+    """
+    X = _f64(X)
+    T, n, C = X.shape
+    th = _f64(theta)
+    b = _f64(bias)
+    r = np.sqrt(np.mean(X * X, axis=2, keepdims=True))
+    xt = np.divide(X, r, out=np.zeros_like(X), where=r > 0)
+    P = xt @ th.T  # [T, n, n + 2]: P[t, i, k] = theta_k . x~_i
+    h_pre = alpha[0] * np.tanh(P[:, :, 0]) + b[:n]
+    h_post = alpha[1] * np.tanh(P[:, :, 1]) + b[n:2 * n]
+    h_res = alpha[2] * np.tanh(np.transpose(P[:, :, 2:], (0, 2, 1))) + b[2 * n:].reshape(n, n)
+    return h_pre, h_post, h_res
+
+
+def amax_gain(h_res_layers):
+    """Amax gain magnitude of a chain of residual maps (mHC notes, section 3.1).
+
+    h_res_layers: [L, T, n, n], layer 0 first. Per token the composite map is
+    M = H_{L-1} ... H_1 H_0, the product that carries x_0 to x_L through the
+    residual terms of Eq. 3. The forward gain is the largest absolute row sum,
+    max_i |sum_j M[i, j]|; the backward gain the largest absolute column sum,
+    max_j |sum_i M[i, j]|. Returns (forward [T], backward [T]).
+    """
+    H = _f64(h_res_layers)
+    L, T, n, _ = H.shape
+    M = np.broadcast_to(np.eye(n), (T, n, n)).copy()
+    for layer in range(L):
+        M = H[layer] @ M
+    return np.abs(M.sum(axis=2)).max(axis=1), np.abs(M.sum(axis=1)).max(axis=1)

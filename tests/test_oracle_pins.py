@@ -495,3 +495,110 @@ def test_bf16_rounding_is_nearest_even():
     ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float32).numpy()
     np.testing.assert_array_equal(r, ref)
     assert bits.dtype == np.uint16
+
+
+# ----------------------------------- HC baseline (Eq. 5) and the Amax gain (section 3.1)
+
+def test_hc_tanh_zero_projection_gives_the_static_maps():
+    """theta = 0: every tanh is 0, so the maps are the biases (the static part)."""
+    rng = np.random.default_rng(200)
+    T, n, C = 3, 4, 16
+    X = rng.standard_normal((T, n, C))
+    b = rng.standard_normal(n * n + 2 * n)
+    hp, hq, hr = O.hc_tanh_coeffs(X, np.zeros((n + 2, C)), b, (0.7, -1.3, 2.0))
+    np.testing.assert_array_equal(hp, np.tile(b[:n], (T, 1)))
+    np.testing.assert_array_equal(hq, np.tile(b[n:2 * n], (T, 1)))
+    np.testing.assert_array_equal(hr, np.tile(b[2 * n:].reshape(n, n), (T, 1, 1)))
+
+
+def test_hc_tanh_single_nonzero_entry_closed_form():
+    """A stream row with one nonzero entry v at channel c normalises to
+    sign(v) sqrt(C) e_c, so theta_k . x~ = sign(v) sqrt(C) theta[k, c]; the row
+    index of H_res is the theta row, the column the stream."""
+    n, C = 3, 9
+    rng = np.random.default_rng(201)
+    theta = rng.standard_normal((n + 2, C)) * 0.3
+    b = rng.standard_normal(n * n + 2 * n)
+    a = (0.5, 1.5, -0.25)
+    X = np.zeros((1, n, C))
+    cols, vals = [2, 7, 0], [-3.0, 0.5, 11.0]
+    for i in range(n):
+        X[0, i, cols[i]] = vals[i]
+    hp, hq, hr = O.hc_tanh_coeffs(X, theta, b, a)
+    for i in range(n):
+        s = math.copysign(math.sqrt(C), vals[i])
+        assert math.isclose(hp[0, i], a[0] * math.tanh(s * theta[0, cols[i]]) + b[i], rel_tol=1e-14)
+        assert math.isclose(hq[0, i], a[1] * math.tanh(s * theta[1, cols[i]]) + b[n + i], rel_tol=1e-14)
+        for j in range(n):
+            want = a[2] * math.tanh(s * theta[2 + j, cols[i]]) + b[2 * n + j * n + i]
+            assert math.isclose(hr[0, j, i], want, rel_tol=1e-14, abs_tol=1e-15)
+
+
+def test_hc_tanh_brute_force_and_per_stream_scale_invariance():
+    rng = np.random.default_rng(202)
+    T, n, C = 2, 3, 5
+    X = rng.standard_normal((T, n, C))
+    X[1, 2] = 0.0  # an all-zero row: x~ = 0
+    theta = rng.standard_normal((n + 2, C))
+    b = rng.standard_normal(n * n + 2 * n)
+    a = (0.9, 0.4, 1.1)
+    hp, hq, hr = O.hc_tanh_coeffs(X, theta, b, a)
+    for t in range(T):
+        for i in range(n):
+            row = [float(v) for v in X[t, i]]
+            r = math.sqrt(sum(v * v for v in row) / C)
+            xt = [v / r if r > 0 else 0.0 for v in row]
+            dot = lambda k: sum(theta[k, c] * xt[c] for c in range(C))
+            assert math.isclose(hp[t, i], a[0] * math.tanh(dot(0)) + b[i], rel_tol=1e-12, abs_tol=1e-14)
+            assert math.isclose(hq[t, i], a[1] * math.tanh(dot(1)) + b[n + i], rel_tol=1e-12, abs_tol=1e-14)
+            for j in range(n):
+                assert math.isclose(hr[t, j, i], a[2] * math.tanh(dot(2 + j)) + b[2 * n + j * n + i],
+                                    rel_tol=1e-12, abs_tol=1e-14)
+    # each stream is normalised on its own: scaling one stream by 2^k changes nothing
+    Xs = X.copy()
+    Xs[:, 0] *= 8.0
+    Xs[:, 1] *= 0.25
+    for u, v in zip(O.hc_tanh_coeffs(Xs, theta, b, a), (hp, hq, hr)):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_amax_gain_closed_forms():
+    T, n = 4, 3
+    eye = np.broadcast_to(np.eye(n), (5, T, n, n))
+    f, g = O.amax_gain(eye)
+    np.testing.assert_array_equal(f, np.ones(T))
+    np.testing.assert_array_equal(g, np.ones(T))
+    # permutations keep every row and column sum at 1
+    perms = np.stack([np.stack([np.eye(n)[list(p)] for p in itertools.islice(itertools.permutations(range(n)),
+                                                                             T)]) for _ in range(3)])
+    f, g = O.amax_gain(perms)
+    np.testing.assert_array_equal(f, np.ones(T))
+    # diagonal maps multiply: gain = max_i |prod_l d_l[i]|
+    rng = np.random.default_rng(203)
+    d = rng.uniform(-2, 2, (4, T, n))
+    f, g = O.amax_gain(np.einsum("ltn,nm->ltnm", d, np.eye(n)))
+    want = np.abs(np.prod(d, axis=0)).max(axis=1)
+    np.testing.assert_allclose(f, want, rtol=1e-14)
+    np.testing.assert_allclose(g, want, rtol=1e-14)
+    # Sinkhorn outputs end with a row normalisation: a chain of them has row sums
+    # exactly 1 (to rounding), so the forward gain is 1
+    Hs = np.stack([O.sinkhorn_knopp(rng.standard_normal((T, n, n)), 20) for _ in range(6)])
+    f, _ = O.amax_gain(Hs)
+    np.testing.assert_allclose(f, 1.0, rtol=0, atol=1e-13)
+
+
+def test_amax_gain_brute_force_order():
+    """M = H_{L-1} ... H_0 (a transposed or reversed product fails this)."""
+    rng = np.random.default_rng(204)
+    L, T, n = 3, 2, 3
+    H = rng.standard_normal((L, T, n, n))
+    f, g = O.amax_gain(H)
+    for t in range(T):
+        M = [[1.0 if i == j else 0.0 for j in range(n)] for i in range(n)]
+        for layer in range(L):
+            A = H[layer, t]
+            M = [[sum(A[i][k] * M[k][j] for k in range(n)) for j in range(n)] for i in range(n)]
+        rows = [abs(sum(M[i][j] for j in range(n))) for i in range(n)]
+        cols = [abs(sum(M[i][j] for i in range(n))) for j in range(n)]
+        assert math.isclose(f[t], max(rows), rel_tol=1e-12)
+        assert math.isclose(g[t], max(cols), rel_tol=1e-12)
