@@ -267,6 +267,39 @@ int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
                 const float* conv_w, const int* kappa, int r,
                 void* V, int v_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ----------------------------------------- HC baseline and gain diagnostic -- */
+
+/*
+ * hc_tanh_coeffs - the maps of unconstrained Hyper-Connections ([mHC] section 3
+ * Preliminary, Eq. 5), for comparison with the mHC calls (apply them with
+ * hc_pre and hc_post):
+ *   per token t and stream i, x~_i = X[t, i] / r_i with r_i = sqrt(sum_c
+ *   X[t, i, c]^2 / C) (each stream normalised over its own C channels; no gain,
+ *   no epsilon; x~_i = 0 when r_i = 0);
+ *   h_pre[t, i]     = alpha_pre  * tanh(theta[0]     . x~_i) + bias[i]
+ *   h_post[t, i]    = alpha_post * tanh(theta[1]     . x~_i) + bias[n + i]
+ *   h_res[t, j, i]  = alpha_res  * tanh(theta[2 + j] . x~_i) + bias[2n + j*n + i]
+ *   X [T, n, C] stream dtype; theta [n + 2, C] float32 (rows pre, post, res_0 ..
+ *   res_{n-1}); bias [n*n + 2n] float32 as for hc_coeffs; outputs float32
+ *   h_pre [T, n], h_post [T, n], h_res [T, n, n] (row j = output stream j).
+ *   1 <= n <= 16. No workspace.
+ */
+int hc_tanh_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* theta,
+                   const float* bias, float alpha_pre, float alpha_post, float alpha_res, float* h_pre,
+                   float* h_post, float* h_res, void* stream);
+
+/*
+ * hc_amax_gain - Amax gain magnitude of a chain of residual maps ([mHC]
+ * section 3.1): per token t, M = H_{L-1} ... H_1 H_0 (float32) with
+ * H_l = h_res[l, t] (n x n, row = output stream), then
+ *   gain_fwd[t] = max_i |sum_j M[i, j]|   (largest absolute row sum: forward)
+ *   gain_bwd[t] = max_j |sum_i M[i, j]|   (largest absolute column sum: backward).
+ *   h_res [L, T, n, n] float32 (layer 0 first; may be NULL when L == 0, the
+ *   gains are then 1); gain_fwd, gain_bwd [T] float32. 1 <= n <= 16, L >= 0.
+ */
+int hc_amax_gain(const float* h_res, int64_t L, int64_t T, int n, float* gain_fwd, float* gain_bwd,
+                 void* stream);
+
 /* ------------------------------------------------------------ measurement -- */
 
 /*

@@ -51,6 +51,9 @@ _SIGS = {
     "xhc_augment_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int, _c_int]),
     "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
     "hc_copy_probe": (_c_int, [_vp, _vp, _c_i64, _vp]),
+    "hc_tanh_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float,
+                                _vp, _vp, _vp, _vp]),
+    "hc_amax_gain": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -341,6 +344,32 @@ def xhc_augment(F_out, conv_w, kappas, batch, seq, *, v_dtype=None, workspace=No
     return V
 
 
+def hc_tanh_coeffs(X, theta, bias, alpha, *, out=None, stream=None):
+    """HC's unconstrained maps (h_pre [T,n], h_post [T,n], h_res [T,n,n]) of X [T,n,C];
+    theta [n+2, C] float32, bias [n*n+2n], alpha = (pre, post, res)."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    if out is None:
+        out = (torch.empty(T, n, device=X.device), torch.empty(T, n, device=X.device),
+               torch.empty(T, n, n, device=X.device))
+    h_pre, h_post, h_res = out
+    a = [float(v) for v in alpha]
+    _check("hc_tanh_coeffs", lib().hc_tanh_coeffs(_ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(theta, "theta")),
+                                                  _ptr(_f32(bias, "bias")), a[0], a[1], a[2], _ptr(h_pre),
+                                                  _ptr(h_post), _ptr(h_res), _stream(X.device, stream)))
+    return h_pre, h_post, h_res
+
+
+def hc_amax_gain(h_res_layers, *, stream=None):
+    """(forward gain [T], backward gain [T]) of the chain h_res_layers [L, T, n, n] (layer 0 first)."""
+    H = _f32(h_res_layers, "h_res_layers")
+    L, T, n, _ = H.shape
+    fwd = torch.empty(T, device=H.device)
+    bwd = torch.empty(T, device=H.device)
+    _check("hc_amax_gain", lib().hc_amax_gain(_ptr(H), L, T, n, _ptr(fwd), _ptr(bwd), _stream(H.device, stream)))
+    return fwd, bwd
+
+
 def hc_copy_probe(src, dst, *, stream=None):
     """Copy src into dst (same byte size, 16-byte aligned) with the library's streaming
     copy: a measurement probe of the device's streaming rate, not part of the method."""
@@ -357,5 +386,6 @@ __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
     "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
-    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_copy_probe",
+    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
+    "hc_copy_probe",
 ]

@@ -644,6 +644,44 @@ int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, c
                                                   (hipStream_t)stream));
 }
 
+int hc_tanh_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const float* theta,
+                   const float* bias, float alpha_pre, float alpha_post, float alpha_res, float* h_pre,
+                   float* h_post, float* h_res, void* stream) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!theta || !bias || !h_pre || !h_post || !h_res) return HC_ERR_NULL;
+  for (const void* p : {(const void*)theta, (const void*)bias, (const void*)h_pre, (const void*)h_post,
+                        (const void*)h_res})
+    if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype), thb = (int64_t)(n + 2) * C * 4, bb = (n * n + 2 * n) * 4;
+  const void* outs[3] = {h_pre, h_post, h_res};
+  const int64_t ob[3] = {T * n * 4, T * n * 4, T * n * n * 4};
+  for (int a = 0; a < 3; ++a) {
+    if (overlaps(outs[a], ob[a], X, xb) || overlaps(outs[a], ob[a], theta, thb) || overlaps(outs[a], ob[a], bias, bb))
+      return HC_ERR_ALIAS;
+    for (int b = 0; b < a; ++b)
+      if (overlaps(outs[a], ob[a], outs[b], ob[b])) return HC_ERR_ALIAS;
+  }
+  if ((s = device_status()) != HC_OK) return s;
+  const bool vec = C % 8 == 0 && aligned_to(X, 16) && aligned_to(theta, 16);
+  return launch_status(hc::launch_hc_tanh(dtype, vec, X, T, n, C, theta, bias, alpha_pre, alpha_post, alpha_res,
+                                          h_pre, h_post, h_res, (hipStream_t)stream));
+}
+
+int hc_amax_gain(const float* h_res, int64_t L, int64_t T, int n, float* gain_fwd, float* gain_bwd, void* stream) {
+  if (L < 0 || T < 0 || n < 1 || n > HC_MAX_MHC_STREAMS) return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if ((L > 0 && !h_res) || !gain_fwd || !gain_bwd) return HC_ERR_NULL;
+  if (!aligned_to(h_res, 4) || !aligned_to(gain_fwd, 4) || !aligned_to(gain_bwd, 4)) return HC_ERR_ALIGN;
+  const int64_t hb = L * T * n * n * 4;
+  if (overlaps(gain_fwd, T * 4, gain_bwd, T * 4) || overlaps(gain_fwd, T * 4, h_res, hb) ||
+      overlaps(gain_bwd, T * 4, h_res, hb))
+    return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_amax_gain(h_res, L, T, n, gain_fwd, gain_bwd, (hipStream_t)stream));
+}
+
 int hc_copy_probe(const void* src, void* dst, int64_t bytes, void* stream) {
   if (bytes < 0) return HC_ERR_SHAPE;
   if (bytes == 0) return HC_OK;

@@ -42,4 +42,11 @@ hipError_t launch_augment_generic(int dtype, int vdtype, const void* F, int64_t 
                                   int64_t C, const float* w, const ConvSpec& spec, void* V,
                                   hipStream_t st);
 
+// ---- HC baseline and the gain diagnostic (hc_baseline.hip)
+// vec: C % 8 == 0 with X and theta 16-byte aligned.
+hipError_t launch_hc_tanh(int dtype, bool vec, const void* X, int64_t T, int n, int64_t C, const float* theta,
+                          const float* bias, float a_pre, float a_post, float a_res, float* h_pre, float* h_post,
+                          float* h_res, hipStream_t st);
+hipError_t launch_amax_gain(const float* H, int64_t L, int64_t T, int n, float* fwd, float* bwd, hipStream_t st);
+
 }  // namespace hc

@@ -155,6 +155,31 @@ def test_validation_rejects_bad_arguments_before_device_work(hc):
     assert L.xhc_augment_workspace_bytes(2, 16, 64, karr, 3, 9, 1) == -1
 
 
+def test_hc_tanh_and_gain_validation(hc):
+    L = hc.lib()
+    A, B, Cc = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    o1, o2, o3 = ctypes.c_void_p(0x400000), ctypes.c_void_p(0x410000), ctypes.c_void_p(0x420000)
+
+    def tanh(X=A, dt=1, T=8, n=4, C=64, th=B, b=Cc, p=o1, q=o2, r=o3):
+        return L.hc_tanh_coeffs(X, dt, T, n, C, th, b, 0.1, 0.1, 0.1, p, q, r, None)
+    assert tanh(dt=7) == -3
+    assert tanh(n=0) == -2 and tanh(n=17) == -2 and tanh(C=0) == -2 and tanh(T=-1) == -2
+    assert tanh(T=0, X=None, th=None) == 0
+    assert tanh(th=None) == -1 and tanh(r=None) == -1
+    assert tanh(p=ctypes.c_void_p(0x400002)) == -4
+    assert tanh(q=ctypes.c_void_p(0x400010)) == -5  # h_post inside h_pre
+    assert tanh(p=ctypes.c_void_p(0x100010)) == -5  # h_pre inside X
+
+    def gain(H=A, Ln=3, T=8, n=4, f=o1, g=o2):
+        return L.hc_amax_gain(H, Ln, T, n, f, g, None)
+    assert gain(n=0) == -2 and gain(n=17) == -2 and gain(Ln=-1) == -2 and gain(T=-1) == -2
+    assert gain(T=0, H=None, f=None, g=None) == 0
+    assert gain(H=None) == -1 and gain(f=None) == -1
+    assert gain(g=ctypes.c_void_p(0x410002)) == -4
+    assert gain(g=ctypes.c_void_p(0x400010)) == -5
+    assert gain(f=ctypes.c_void_p(0x100010)) == -5
+
+
 def test_copy_probe_validation(hc):
     L = hc.lib()
     a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
