@@ -355,3 +355,41 @@ def amax_gain(h_res_layers):
     for layer in range(L):
         M = H[layer] @ M
     return np.abs(M.sum(axis=2)).max(axis=1), np.abs(M.sum(axis=1)).max(axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Static mHC (the mHC-SSM abstract): per-layer maps that do not depend on the input
+# ---------------------------------------------------------------------------
+
+def softmax(z):
+    """exp(z_i) / sum_j exp(z_j) over the last axis (the max is subtracted first;
+    the result is the same in exact arithmetic)."""
+    z = _f64(z)
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def static_mhc_maps(logits, n: int, sinkhorn_iters: int = 20):
+    """Maps of static mHC ("mHC-SSM" abstract): one set per layer, shared by all
+    tokens. Pre-mixing and post-mixing are simplex-constrained; reading: each is
+    the softmax of its n logits (nonnegative, summing to 1). Residual mixing is
+    Sinkhorn-projected as in mHC (exp of the n x n logits, then sinkhorn_iters
+    alternating column / row normalisations, mHC notes Eq. 9).
+    logits: [n*n + 2n] (pre n | post n | res n*n row-major, the layout of the mHC
+    bias). Returns h_pre [n], h_post [n], h_res [n, n]."""
+    z = _f64(logits)
+    return (softmax(z[:n]), softmax(z[n:2 * n]),
+            sinkhorn_knopp(z[2 * n:].reshape(n, n), sinkhorn_iters))
+
+
+def static_pre(X, h_pre):
+    """F_in[t] = sum_i h_pre[i] X[t, i]: the mHC pre-read with one h_pre for every token."""
+    X = _f64(X)
+    return hc_pre(X, np.broadcast_to(_f64(h_pre), X.shape[:2]))
+
+
+def static_post(X, h_res, h_post, F_out):
+    """X_next[t] = h_res X[t] + h_post^T F_out[t]: the mHC post with maps shared by every token."""
+    X = _f64(X)
+    T, n, _ = X.shape
+    return hc_post(X, np.broadcast_to(_f64(h_res), (T, n, n)), np.broadcast_to(_f64(h_post), (T, n)), F_out)

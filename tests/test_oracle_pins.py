@@ -602,3 +602,40 @@ def test_amax_gain_brute_force_order():
         cols = [abs(sum(M[i][j] for i in range(n))) for j in range(n)]
         assert math.isclose(f[t], max(rows), rel_tol=1e-12)
         assert math.isclose(g[t], max(cols), rel_tol=1e-12)
+
+
+# ------------------------------------------------ static mHC (the mHC-SSM abstract)
+
+def test_static_maps_simplex_and_sinkhorn():
+    rng = np.random.default_rng(210)
+    n = 4
+    z = rng.standard_normal(n * n + 2 * n) * 2.0
+    hp, hq, hr = O.static_mhc_maps(z, n, 20)
+    np.testing.assert_allclose(hp, scipy.special.softmax(z[:n]), rtol=1e-14)
+    np.testing.assert_allclose(hq, scipy.special.softmax(z[n:2 * n]), rtol=1e-14)
+    np.testing.assert_allclose(hr, O.sinkhorn_knopp(z[2 * n:].reshape(n, n), 20), rtol=0, atol=0)
+    assert math.isclose(hp.sum(), 1.0, rel_tol=1e-15) and (hp > 0).all()
+    np.testing.assert_allclose(hr.sum(axis=1), 1.0, rtol=1e-14)  # rows normalised last
+    # equal logits: the uniform point of the simplex; a shift changes nothing
+    hp0, _, _ = O.static_mhc_maps(np.zeros(n * n + 2 * n), n)
+    np.testing.assert_array_equal(hp0, np.full(n, 0.25))
+    hp1, hq1, _ = O.static_mhc_maps(z + 3.0, n, 20)
+    np.testing.assert_allclose(hp1, hp, rtol=1e-14)
+
+
+def test_static_apply_is_the_broadcast_mhc_apply():
+    """The static maps applied to every token equal the per-token formulas written
+    out with explicit loops."""
+    rng = np.random.default_rng(211)
+    T, n, C = 3, 3, 5
+    X = rng.standard_normal((T, n, C))
+    F = rng.standard_normal((T, C))
+    hp, hq, hr = O.static_mhc_maps(rng.standard_normal(n * n + 2 * n), n, 20)
+    Fin = O.static_pre(X, hp)
+    Xn = O.static_post(X, hr, hq, F)
+    for t in range(T):
+        for c in range(C):
+            assert math.isclose(Fin[t, c], sum(hp[i] * X[t, i, c] for i in range(n)), rel_tol=1e-13, abs_tol=1e-14)
+            for i in range(n):
+                want = sum(hr[i, j] * X[t, j, c] for j in range(n)) + hq[i] * F[t, c]
+                assert math.isclose(Xn[t, i, c], want, rel_tol=1e-13, abs_tol=1e-14)
