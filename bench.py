@@ -94,6 +94,57 @@ def xhc_algorithmic_bytes(T: int, N: int, C: int, k: int, m: int, K: int, esize:
     return {"xhc_pre": pre, "xhc_route": route, "xhc_augment": aug}
 
 
+def hc_baseline_bench(torch, hc, dev, reps: int = 20) -> dict:
+    """The HC baseline maps (hc_tanh_coeffs) and the static mHC pre-read and post on
+    the n=4 C=4096 T=8192 bf16 state, three rotating state sets; and the Amax gain
+    of an 8-layer chain of n=4 maps over T=16384 tokens. HIP events around the
+    repeated calls."""
+    T, n, C = 8192, 4, 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000)
+    Xs = [torch.randn(T, n, C, device=dev, generator=g).to(torch.bfloat16) for _ in range(3)]
+    theta = torch.randn(n + 2, C, device=dev, generator=g) * 0.02
+    bias = torch.zeros(n * n + 2 * n, device=dev)
+    out = (torch.empty(T, n, device=dev), torch.empty(T, n, device=dev), torch.empty(T, n, n, device=dev))
+
+    def timeit(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    t_tanh = timeit(lambda i: hc.hc_tanh_coeffs(Xs[i % 3], theta, bias, (0.1, 0.1, 0.1), out=out))
+    tanh_bytes = T * n * C * 2 + T * (n * n + 2 * n) * 4
+    L, T2 = 8, 16384
+    H = (torch.eye(n, device=dev) + 0.1 * torch.randn(L, T2, n, n, device=dev, generator=g)).contiguous()
+    t_gain = timeit(lambda i: hc.hc_amax_gain(H))
+    gain_bytes = L * T2 * n * n * 4 + 2 * T2 * 4
+    Fs = [torch.randn(T, C, device=dev, generator=g).to(torch.bfloat16) for _ in range(3)]
+    z = torch.randn(n * n + 2 * n, device=dev, generator=g)
+    sp, sq, sr = hc.hc_static_maps(z, n, SINKHORN_ITERS)
+    F_in = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
+    Xn = torch.empty(T, n, C, dtype=torch.bfloat16, device=dev)
+    t_spre = timeit(lambda i: hc.hc_static_pre(Xs[i % 3], sp, out=F_in))
+    t_spost = timeit(lambda i: hc.hc_static_post(Xs[i % 3], sr, sq, Fs[i % 3], out=Xn))
+    spre_bytes = T * n * C * 2 + T * C * 2
+    spost_bytes = T * n * C * 2 * 2 + T * C * 2
+    stat = {name: {"workload": "static mHC n=4 C=4096 T=8192 bf16", "us": t * 1e6, "algorithmic_bytes": nb,
+                   "achieved_GBps": nb / t / 1e9, "pct_hbm_peak": 100.0 * nb / t / 1e9 / HBM_PEAK_GBPS}
+            for name, t, nb in (("hc_static_pre", t_spre, spre_bytes), ("hc_static_post", t_spost, spost_bytes))}
+    return {**stat,
+            "hc_tanh_coeffs": {"workload": "HC maps n=4 C=4096 T=8192 bf16", "us": t_tanh * 1e6,
+                               "algorithmic_bytes": tanh_bytes, "achieved_GBps": tanh_bytes / t_tanh / 1e9,
+                               "pct_hbm_peak": 100.0 * tanh_bytes / t_tanh / 1e9 / HBM_PEAK_GBPS},
+            "hc_amax_gain": {"workload": "8-layer chain of n=4 maps, T=16384", "us": t_gain * 1e6,
+                             "algorithmic_bytes": gain_bytes, "achieved_GBps": gain_bytes / t_gain / 1e9}}
+
+
 def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     """Throughput of the xHC sublayer (N=16, k=4, m=2, C=4096, T=8192, bf16) on
     seeded synthetic device data: the routed step xhc_pre + xhc_route (K=1, F_out
@@ -457,6 +508,7 @@ def main() -> int:
     }
     if not args.no_xhc:
         result["xhc"] = xhc_bench(torch, hc, dev, max(3, min(args.steps, 20)), 3)
+        result["hc_baseline"] = hc_baseline_bench(torch, hc, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

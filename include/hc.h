@@ -300,6 +300,31 @@ int hc_tanh_coeffs(const void* X, int dtype, int64_t T, int n, int64_t C, const 
 int hc_amax_gain(const float* h_res, int64_t L, int64_t T, int n, float* gain_fwd, float* gain_bwd,
                  void* stream);
 
+/* ------------------------------------------------------------- static mHC -- */
+
+/*
+ * Static mHC ("mHC-SSM" abstract: mHC around a state space model block with
+ * one set of maps per layer, shared by every token).
+ *
+ * hc_static_maps - the maps from their logits (device arrays):
+ *   logits [n*n + 2n] float32 (pre n | post n | res n*n row-major, the layout of
+ *   the mHC bias); h_pre [n] = softmax(pre logits) and h_post [n] =
+ *   softmax(post logits) (simplex-constrained pre- and post-mixing: nonnegative,
+ *   summing to 1); h_res [n, n] = Sinkhorn-Knopp of exp(res logits), as in
+ *   hc_coeffs ([mHC] Eq. 9). 1 <= n <= 16; 1 <= sinkhorn_iters <= HC_MAX_ITERS.
+ *
+ * hc_static_pre  - F_in[t] = sum_i h_pre[i] X[t, i]       ([mHC] F_pre, one h_pre for all tokens)
+ * hc_static_post - X_next[t] = h_res X[t] + h_post^T F_out[t]  ([mHC] Eq. 3, F_post,res)
+ *   X [T, n, C], F_in / F_out [T, C] stream dtype; h_pre, h_post [n], h_res [n, n]
+ *   float32 device arrays; X_next may equal X (not partially overlap it).
+ */
+int hc_static_maps(const float* logits, int n, int sinkhorn_iters, float* h_pre, float* h_post, float* h_res,
+                   void* stream);
+int hc_static_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_pre, void* F_in,
+                  void* stream);
+int hc_static_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res, const float* h_post,
+                   const void* F_out, void* X_next, void* stream);
+
 /* ------------------------------------------------------------ measurement -- */
 
 /*

@@ -54,6 +54,9 @@ _SIGS = {
     "hc_tanh_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float,
                                 _vp, _vp, _vp, _vp]),
     "hc_amax_gain": (_c_int, [_vp, _c_i64, _c_i64, _c_int, _vp, _vp, _vp]),
+    "hc_static_maps": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _vp, _vp]),
+    "hc_static_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp]),
+    "hc_static_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -370,6 +373,39 @@ def hc_amax_gain(h_res_layers, *, stream=None):
     return fwd, bwd
 
 
+def hc_static_maps(logits, n, sinkhorn_iters=20, *, stream=None):
+    """Static mHC maps (h_pre [n], h_post [n], h_res [n, n]) from logits [n*n + 2n] float32."""
+    z = _f32(logits, "logits")
+    h_pre = torch.empty(n, device=z.device)
+    h_post = torch.empty(n, device=z.device)
+    h_res = torch.empty(n, n, device=z.device)
+    _check("hc_static_maps", lib().hc_static_maps(_ptr(z), n, int(sinkhorn_iters), _ptr(h_pre), _ptr(h_post),
+                                                  _ptr(h_res), _stream(z.device, stream)))
+    return h_pre, h_post, h_res
+
+
+def hc_static_pre(X, h_pre, *, out=None, stream=None):
+    """F_in [T, C] = sum_i h_pre[i] X[:, i, :] with one h_pre [n] for every token."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    F_in = torch.empty(T, C, dtype=X.dtype, device=X.device) if out is None else out
+    _check("hc_static_pre", lib().hc_static_pre(_ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(h_pre, "h_pre")),
+                                                _ptr(F_in), _stream(X.device, stream)))
+    return F_in
+
+
+def hc_static_post(X, h_res, h_post, F_out, *, out=None, stream=None):
+    """X_next [T, n, C] = h_res X[t] + h_post^T F_out[t] with maps shared by every token."""
+    X = _dev_tensor(X, "X", _DT)
+    T, n, C = X.shape
+    Y = torch.empty_like(X) if out is None else out
+    _check("hc_static_post", lib().hc_static_post(_ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(h_res, "h_res")),
+                                                  _ptr(_f32(h_post, "h_post")),
+                                                  _ptr(_dev_tensor(F_out, "F_out", _DT)), _ptr(Y),
+                                                  _stream(X.device, stream)))
+    return Y
+
+
 def hc_copy_probe(src, dst, *, stream=None):
     """Copy src into dst (same byte size, 16-byte aligned) with the library's streaming
     copy: a measurement probe of the device's streaming rate, not part of the method."""
@@ -387,5 +423,5 @@ __all__ = [
     "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
-    "hc_copy_probe",
+    "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",
 ]

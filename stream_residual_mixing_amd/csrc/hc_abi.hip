@@ -682,6 +682,55 @@ int hc_amax_gain(const float* h_res, int64_t L, int64_t T, int n, float* gain_fw
   return launch_status(hc::launch_amax_gain(h_res, L, T, n, gain_fwd, gain_bwd, (hipStream_t)stream));
 }
 
+int hc_static_maps(const float* logits, int n, int sinkhorn_iters, float* h_pre, float* h_post, float* h_res,
+                   void* stream) {
+  if (n < 1 || n > HC_MAX_MHC_STREAMS || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS) return HC_ERR_SHAPE;
+  if (!logits || !h_pre || !h_post || !h_res) return HC_ERR_NULL;
+  for (const void* p : {(const void*)logits, (const void*)h_pre, (const void*)h_post, (const void*)h_res})
+    if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
+  const void* outs[3] = {h_pre, h_post, h_res};
+  const int64_t ob[3] = {(int64_t)n * 4, (int64_t)n * 4, (int64_t)n * n * 4};
+  for (int a = 0; a < 3; ++a) {
+    if (overlaps(outs[a], ob[a], logits, (int64_t)(n * n + 2 * n) * 4)) return HC_ERR_ALIAS;
+    for (int b = 0; b < a; ++b)
+      if (overlaps(outs[a], ob[a], outs[b], ob[b])) return HC_ERR_ALIAS;
+  }
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_static_maps(logits, n, sinkhorn_iters, h_pre, h_post, h_res, (hipStream_t)stream));
+}
+
+int hc_static_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_pre, void* F_in,
+                  void* stream) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!h_pre || !F_in) return HC_ERR_NULL;
+  if (!aligned_to(h_pre, 4) || !aligned_to(F_in, esize(dtype))) return HC_ERR_ALIGN;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+  if (overlaps(F_in, fb, X, xb) || overlaps(F_in, fb, h_pre, (int64_t)n * 4)) return HC_ERR_ALIAS;
+  if ((s = device_status()) != HC_OK) return s;
+  return launch_status(hc::launch_static_apply(dtype, false, vec_ok(C, {X, F_in}), X, T, n, C, h_pre, nullptr,
+                                               nullptr, F_in, (hipStream_t)stream));
+}
+
+int hc_static_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res, const float* h_post,
+                   const void* F_out, void* X_next, void* stream) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!h_res || !h_post || !F_out || !X_next) return HC_ERR_NULL;
+  if (!aligned_to(h_res, 4) || !aligned_to(h_post, 4) || !aligned_to(F_out, esize(dtype)) ||
+      !aligned_to(X_next, esize(dtype)))
+    return HC_ERR_ALIGN;
+  const int64_t xb = T * n * C * (int64_t)esize(dtype), fb = T * C * (int64_t)esize(dtype);
+  if (X_next != X && overlaps(X_next, xb, X, xb)) return HC_ERR_ALIAS;
+  if (overlaps(X_next, xb, F_out, fb) || overlaps(X_next, xb, h_res, (int64_t)n * n * 4) ||
+      overlaps(X_next, xb, h_post, (int64_t)n * 4))
+    return HC_ERR_ALIAS;
+  if ((s = device_status()) != HC_OK) return s;
+  return launch_status(hc::launch_static_apply(dtype, true, vec_ok(C, {X, F_out, X_next}), X, T, n, C, h_res, h_post,
+                                               F_out, X_next, (hipStream_t)stream));
+}
+
 int hc_copy_probe(const void* src, void* dst, int64_t bytes, void* stream) {
   if (bytes < 0) return HC_ERR_SHAPE;
   if (bytes == 0) return HC_OK;

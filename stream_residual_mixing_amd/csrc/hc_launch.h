@@ -49,4 +49,12 @@ hipError_t launch_hc_tanh(int dtype, bool vec, const void* X, int64_t T, int n, 
                           float* h_res, hipStream_t st);
 hipError_t launch_amax_gain(const float* H, int64_t L, int64_t T, int n, float* fwd, float* bwd, hipStream_t st);
 
+// ---- static mHC (hc_static.hip)
+hipError_t launch_static_maps(const float* logits, int n, int iters, float* h_pre, float* h_post, float* h_res,
+                              hipStream_t st);
+// post: X_next from (h_res = h1, h_post = h2, F); else F_in (into Y) from h_pre = h1.
+// vec: C % 8 == 0 with X, F and Y 16-byte aligned.
+hipError_t launch_static_apply(int dtype, bool post, bool vec, const void* X, int64_t T, int n, int64_t C,
+                               const float* h1, const float* h2, const void* F, void* Y, hipStream_t st);
+
 }  // namespace hc

@@ -180,6 +180,25 @@ def test_hc_tanh_and_gain_validation(hc):
     assert gain(f=ctypes.c_void_p(0x100010)) == -5
 
 
+def test_static_mhc_validation(hc):
+    L = hc.lib()
+    z, a, b, c = (ctypes.c_void_p(v) for v in (0x100000, 0x200000, 0x210000, 0x220000))
+    assert L.hc_static_maps(z, 0, 20, a, b, c, None) == -2
+    assert L.hc_static_maps(z, 4, 0, a, b, c, None) == -2
+    assert L.hc_static_maps(None, 4, 20, a, b, c, None) == -1
+    assert L.hc_static_maps(z, 4, 20, ctypes.c_void_p(0x200002), b, c, None) == -4
+    assert L.hc_static_maps(z, 4, 20, a, ctypes.c_void_p(0x200008), c, None) == -5
+    assert L.hc_static_maps(z, 4, 20, ctypes.c_void_p(0x100010), b, c, None) == -5
+    X, F, Y = ctypes.c_void_p(0x1000000), ctypes.c_void_p(0x2000000), ctypes.c_void_p(0x3000000)
+    assert L.hc_static_pre(X, 5, 8, 4, 64, a, F, None) == -3
+    assert L.hc_static_pre(X, 1, 8, 4, 64, None, F, None) == -1
+    assert L.hc_static_pre(X, 1, 8, 4, 64, a, ctypes.c_void_p(0x1000010), None) == -5
+    assert L.hc_static_pre(X, 1, 0, 4, 64, None, None, None) == 0
+    assert L.hc_static_post(X, 1, 8, 4, 64, a, b, F, ctypes.c_void_p(0x1000010), None) == -5
+    assert L.hc_static_post(X, 1, 8, 4, 64, a, b, None, Y, None) == -1
+    assert L.hc_static_post(X, 1, 8, 4, 64, a, b, F, ctypes.c_void_p(0x3000001), None) == -4
+
+
 def test_copy_probe_validation(hc):
     L = hc.lib()
     a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)

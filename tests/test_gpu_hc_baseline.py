@@ -1,6 +1,7 @@
-"""GPU parity of the HC baseline maps (mHC notes Eq. 5) and the Amax gain
-diagnostic (section 3.1) against the fp64 oracle, through the C ABI; the HC maps
-applied with the mHC pre-read and post calls."""
+"""GPU parity of the HC baseline maps (mHC notes Eq. 5), the Amax gain
+diagnostic (section 3.1) and static mHC (the mHC-SSM abstract) against the fp64
+oracle, through the C ABI; the HC maps applied with the mHC pre-read and post
+calls."""
 import numpy as np
 import pytest
 
@@ -83,3 +84,28 @@ def test_gain_of_mhc_chain_is_one_and_hc_chain_drifts():
     assert np.abs(host64(fm) - 1.0).max() < 1e-5
     note(f"HC forward gain: max {float(fh.max()):.3f}, mHC forward gain: max {float(fm.max()):.6f}")
     assert float(fh.max()) > 1.05
+
+
+@pytest.mark.parametrize("n,C,T,dtype", [(4, 4096, 133, synth.BF16), (4, 256, 512, synth.F32),
+                                         (1, 64, 9, synth.F32), (7, 100, 21, synth.BF16), (16, 64, 5, synth.F32)])
+def test_static_mhc_maps_and_apply(n, C, T, dtype):
+    note(f"static mHC n={n} C={C} T={T} dtype={dtype}")
+    rng = np.random.default_rng(700 + n)
+    z = (2.0 * rng.standard_normal(n * n + 2 * n)).astype(np.float32)
+    hp, hq, hr = hc.hc_static_maps(torch.from_numpy(z).cuda(), n, 20)
+    torch.cuda.synchronize()
+    rp, rq, rr = O.static_mhc_maps(z, n, 20)
+    check_fp32("static h_pre", host64(hp), rp)
+    check_fp32("static h_post", host64(hq), rq)
+    check_fp32("static h_res", host64(hr), rr)
+    X = synth.Tensor(rng.standard_normal((T, n, C)).astype(np.float32), dtype)
+    F = synth.Tensor(rng.standard_normal((T, C)).astype(np.float32), dtype)
+    F_in = hc.hc_static_pre(dev(X), hp)
+    Xn = hc.hc_static_post(dev(X), hr, hq, dev(F))
+    Xd = dev(X)
+    hc.hc_static_post(Xd, hr, hq, dev(F), out=Xd)  # in place
+    torch.cuda.synchronize()
+    check_stream("static F_in", dtype, host64(F_in), O.static_pre(X.values, host64(hp)))
+    ref = O.static_post(X.values, host64(hr), host64(hq), F.values)
+    check_stream("static X_next", dtype, host64(Xn), ref)
+    np.testing.assert_array_equal(host64(Xd), host64(Xn))
