@@ -14,7 +14,9 @@ namespace hc {
 
 namespace {
 
-constexpr int HROWS = 4;  // stream rows per wave: theta read once for 4 rows
+// stream rows per wave: theta is read from L2 once for that many rows
+template <int NS>
+constexpr int rows_per_wave() { return NS <= 8 ? 8 : 4; }
 
 // Sum over the 64 lanes of a wave (a fixed butterfly, every lane gets the sum).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -23,7 +25,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per HROWS consecutive stream rows (row = t * n + i). Each lane adds
+// One wave per RW consecutive stream rows (row = t * n + i). Each lane adds
 // its channels' products with the n + 2 theta rows and the row's sum of
 // squares; the wave sums them; lane r then forms row r's maps:
 // x~ . theta_k = (x . theta_k) / r with r = sqrt(sum x^2 / C) (0 for a zero row).
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(256) void hc_tanh_kernel(const T* __restrict__ X, i
                                                       const float* __restrict__ bias, float a_pre, float a_post,
                                                       float a_res, float* __restrict__ h_pre,
                                                       float* __restrict__ h_post, float* __restrict__ h_res) {
-  constexpr int NK = NS + 2;
+  constexpr int NK = NS + 2, HROWS = rows_per_wave<NS>();
   const int lane = threadIdx.x & 63;
   const int64_t nrows = T_ * NS;
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * HROWS;
@@ -154,7 +156,7 @@ template <typename T, int NS>
 void tanh_dispatch_vec(bool vec, const void* X, int64_t T_, int64_t C, const float* theta, const float* bias,
                        float a_pre, float a_post, float a_res, float* h_pre, float* h_post, float* h_res,
                        hipStream_t st) {
-  const int64_t waves = (T_ * NS + HROWS - 1) / HROWS;
+  const int64_t waves = (T_ * NS + rows_per_wave<NS>() - 1) / rows_per_wave<NS>();
   const dim3 g((unsigned)((waves + 3) / 4)), b(256);
   if (vec)
     hipLaunchKernelGGL((hc_tanh_kernel<T, NS, true>), g, b, 0, st, (const T*)X, T_, C, theta, bias, a_pre, a_post,
