@@ -5,6 +5,8 @@
 //   POST: X_next = h_res X + h_post^T F_out  (mHC notes Eq. 3, F_post,res of 4.3.1)
 //   always: the skinny projection of the state it streams (the X_next it just
 //         produced when POST, else X) with MFMA, and the sum of squares.
+// proj_wide_kernel is the projection alone on 64-token items (up to 24
+// columns): each phi fragment read from L2 serves twice the tokens.
 // coeffs_finish_kernel turns the projections into the coefficients (Eq. 15-19):
 // RMS factor, gates, sigmoid, 2*sigmoid and Sinkhorn-Knopp.
 // The projection uses v_mfma_f32_16x16x32_bf16 with 16 tokens as the M rows. phi (float32) is split as phi = hi + lo with hi = bf16(phi) and
@@ -138,12 +140,12 @@ constexpr int SPI = 4;                   // super-chunks per item
 constexpr int NCOEF = TILE * 20;         // h_res (16) | h_post (4) per token of a tile
 enum : int { ROWS_CONTIG = 0, ROWS_GROUPS = 1, ROWS_GATHER = 2 };
 
-template <int NB>
+template <int NB, int TT = TILE>  // TT: tokens per item
 struct PartGeom {
   static constexpr int NCP = NB * 16;    // packed hi | lo columns
   static constexpr int NCOLP = NB * 8;   // logical columns (padded)
   static constexpr int PROW = NCOLP + 1; // floats per token of a partial
-  static constexpr int PART = TILE * PROW;
+  static constexpr int PART = TT * PROW;
   static constexpr int NPEND = (PART + STHR - 1) / STHR;
 };
 
@@ -174,7 +176,7 @@ struct SplitArgs {
   const uint16_t* F;       // POST: [T, C]
   uint16_t* Y;             // POST: [T, 4, C]
   const uint16_t* phi_p;   // packed phi, NB * 16 columns
-  float* part;             // [nitem][TILE][PROW]
+  float* part;             // [nitem][tokens per item][PROW]
 };
 
 template <bool POST, int NB, int MODE>
@@ -579,6 +581,228 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
   store_pending();
 }
 
+// ---------------------------------------------------------- 64-token items
+// Projection only (no post/res write) with items of W_TOK = 64 tokens: each
+// packed-phi fragment taken from L2 serves 64 tokens instead of 32, half the L2
+// traffic per byte of state (measured: with every wave loading the same phi the
+// 32-token kernel runs 22% faster, so that traffic, not the MFMA work, is what
+// costs). Item = 64 tokens x a group of 4 streams x W_SPI super-chunks of W_SC
+// = 128 channels (1024 channels), numbered tile-major as in mhc_split_kernel;
+// per-item partials [64][NB*8 + 1] in float, added by the finish kernels.
+//  * streaming phase: thread (token tid >> 4, and + 32 for the second half; 8
+//    channels at (tid & 15) * 8) loads its 16-byte pieces of the 4 streams: 16
+//    consecutive lanes read 256 contiguous bytes of a stream row;
+//  * MFMA phase: wave w takes the 32-channel group w & 3 of the super-chunk for
+//    streams 2 (w >> 2) and 2 (w >> 2) + 1 and all 4 token blocks.
+// Four token halves (two super-chunks) are in flight; each stream's phi
+// fragments for the next super-chunk load right after its MFMAs.
+constexpr int W_TOK = 64;
+constexpr int W_SC = 128;
+constexpr int W_SPI = 8;
+constexpr int W_LROW = W_SC * 2 + 16;         // bytes per (stream, token) row in LDS, padded
+constexpr int W_LBUF = NS4 * W_TOK * W_LROW;  // bytes per LDS buffer
+
+template <int NB, int MODE>
+__global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
+  static_assert(MODE != ROWS_GATHER, "gathered rows use mhc_split_kernel");
+  // NB = 4 (4 token blocks x 4 accumulator sets) would exceed the registers
+  static_assert(NB <= 3, "more columns use the 32-token items of mhc_split_kernel");
+  using PG = PartGeom<NB, W_TOK>;
+  constexpr int NCP = PG::NCP;
+  constexpr int NPH = (32 * PG::PROW + STHR - 1) / STHR;  // partial floats per thread per 32-token half
+  static_assert(SWAVE * 32 * (NCP + 1) * 4 + SWAVE * 32 * 4 <= W_LBUF, "reduction buffer");
+  const uint16_t* X = A.X;
+  const int64_t T = A.T, C = A.C;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * W_LBUF];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int st_tok = tid >> 4;
+  const int st_c8 = (tid & 15) * 8;
+  const int tau = lane & 15;
+  const int q = lane >> 4;
+  const int cgw = wave & 3, sp = wave >> 2;
+  const int G = (int)gridDim.x;
+  const int nk = (A.nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
+  const int per_tile = A.NG * A.S;
+
+  floatx4_t acc[4][NB], gram[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const __amdgpu_buffer_rsrc_t pres =
+      __builtin_amdgcn_make_buffer_rsrc(A.part, 0, (uint32_t)((int64_t)A.nitem * PG::PART * 4), BUF_DW3);
+
+  struct Item {
+    int tile, g;
+    int64_t s0;
+  };
+  auto item_of = [&](int item) __attribute__((always_inline)) {
+    const int tile = item / per_tile;
+    const int r = item - tile * per_tile;
+    const int g = r / A.S;
+    return Item{tile, g, (int64_t)(r - g * A.S) * W_SPI};
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  // Loads are unconditional (clamped rows and channels), as in mhc_split_kernel.
+  auto load_half = [&](const Item& it, int64_t s, auto P, uint4 (&xv)[NS4]) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    int64_t t = (int64_t)it.tile * W_TOK + st_tok + 32 * p;
+    t = t < T ? t : T - 1;
+    const int64_t c = s * W_SC + st_c8;
+    const int64_t cc = c < C ? c : C - 8;
+    const uint16_t* xg = X + t * A.rowstride + cc + (int64_t)(MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) xv[i] = ld_stream(xg + i * C);
+  };
+  // the tile in LDS holds zeros for rows past T and channels past C
+  auto stream_half = [&](const Item& it, int64_t s, auto P, const uint4 (&xc)[NS4], unsigned char* buf)
+                         __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    const int m = st_tok + 32 * p;
+    const bool ok = ((int64_t)it.tile * W_TOK + m < T) && (s * W_SC + st_c8 < C);
+#pragma unroll
+    for (int i = 0; i < NS4; ++i)
+      *reinterpret_cast<uint4*>(buf + (i * W_TOK + m) * W_LROW + st_c8 * 2) = keep_or_zero(ok, xc[i]);
+  };
+  uint4 xq[4][NS4];
+  uint4 pfq[2][NB];
+  auto load_pf = [&](const Item& it2, int64_t s2, int si, uint4 (&dst)[NB]) __attribute__((always_inline)) {
+    const int64_t cg = s2 * W_SC + cgw * 32;
+    const int64_t cgc = cg < C ? cg : C - 32;
+    const int64_t prow0 = (int64_t)((MODE == ROWS_GROUPS ? 4 * it2.g : 0) + 2 * sp + si) * C;
+    const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + cgc) / 8 + q) * NCP + tau;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dst[b] = pb[b * 16];
+  };
+  auto mfma_phase = [&](const unsigned char* buf, const Item& nit, int64_t ns) __attribute__((always_inline)) {
+#pragma unroll
+    for (int si = 0; si < 2; ++si) {
+      const int stream = 2 * sp + si;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const uint4 af = *reinterpret_cast<const uint4*>(buf + (stream * W_TOK + tb * TOK + tau) * W_LROW +
+                                                         (cgw * 32 + q * 8) * 2);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pfq[si][b]), acc[tb][b], 0, 0, 0);
+        gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
+      }
+      load_pf(nit, ns, si, pfq[si]);
+    }
+  };
+  // Super-chunk j of item `it`: half h (= 2j + p) uses queue slot h mod 4 and is
+  // refilled with half h + 4 (for the last 4 halves: the next item's first 4).
+  static_assert(2 * W_SPI % 4 == 0, "queue slots");
+  auto body = [&](const Item& it, auto J, const Item& nx, unsigned char* buf) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
+    constexpr int h0 = 2 * j, h1 = 2 * j + 1;
+    constexpr int q0 = h0 % 4, q1 = h1 % 4;
+    const int64_t s = it.s0 + j;
+    stream_half(it, s, H0{}, xq[q0], buf);
+    if constexpr (h0 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h0 + 4) / 2, H0{}, xq[q0]);
+    else load_half(nx, nx.s0 + (h0 + 4 - 2 * W_SPI) / 2, H0{}, xq[q0]);
+    stream_half(it, s, H1{}, xq[q1], buf);
+    if constexpr (h1 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h1 + 4) / 2, H1{}, xq[q1]);
+    else load_half(nx, nx.s0 + (h1 + 4 - 2 * W_SPI) / 2, H1{}, xq[q1]);
+    __syncthreads();
+    if constexpr (j + 1 < W_SPI) mfma_phase(buf, it, it.s0 + j + 1);
+    else mfma_phase(buf, nx, nx.s0);
+  };
+
+  int item = (int)blockIdx.x;
+  Item it = item_of(item);
+  load_half(it, it.s0, H0{}, xq[0]);
+  load_half(it, it.s0, H1{}, xq[1]);
+  load_half(it, it.s0 + 1, H0{}, xq[2]);
+  load_half(it, it.s0 + 1, H1{}, xq[3]);
+  load_pf(it, it.s0, 0, pfq[0]);
+  load_pf(it, it.s0, 1, pfq[1]);
+  // the partial sums this thread reduced for the previous item (pitem; -1: none):
+  // pend[r][u] holds element tid + u * STHR of the item's token half r
+  float pend[2][NPH];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int u = 0; u < NPH; ++u) pend[r][u] = 0.f;
+  int pitem = -1;
+  auto store_pending = [&]() __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)pitem * (uint32_t)(PG::PART * 4);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int u = 0; u < NPH; ++u) {
+        const int o = tid + u * STHR;
+        const uint32_t off = pitem >= 0 && o < 32 * PG::PROW ? base + (uint32_t)(r * 32 * PG::PROW + o) * 4 : OOB;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend[r][u]), pres, off, 0, 0);
+      }
+  };
+  int step = 0;
+  for (int k = 0; k < nk; ++k) {
+    const int nitem_k = k + 1 < nk ? item + G : item;
+    const Item nx = item_of(nitem_k);
+    static_for<W_SPI>([&](auto J) __attribute__((always_inline)) {
+      body(it, J, nx, lds + ((step + decltype(J)::value) & 1) * W_LBUF);
+      if constexpr (decltype(J)::value == 0) store_pending();
+    });
+    step += W_SPI;
+    // item end: the 8 waves' sums, 32 tokens (two token blocks) per round,
+    // through the buffer the last MFMA phase read
+    float* red = reinterpret_cast<float*>(lds + ((step - 1) & 1) * W_LBUF);  // [SWAVE][32][NCP + 1]
+    float* ssr = red + SWAVE * 32 * (NCP + 1);                                // [SWAVE][32]
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      __syncthreads();
+#pragma unroll
+      for (int tbb = 0; tbb < 2; ++tbb) {
+        const int tb = 2 * r + tbb;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            red[(wave * 32 + tbb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (tau == q * 4 + e) ssr[wave * 32 + tbb * TOK + tau] = gram[tb][e];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NPH; ++u) {
+        int o = tid + u * STHR;
+        o = o < 32 * PG::PROW ? o : tid;
+        const int m = o / PG::PROW, col = o - m * PG::PROW;
+        float sum = 0.f;
+        if (col < PG::NCOLP) {
+#pragma unroll
+          for (int w = 0; w < SWAVE; ++w)
+            sum += red[(w * 32 + m) * (NCP + 1) + col] + red[(w * 32 + m) * (NCP + 1) + PG::NCOLP + col];
+        } else {
+#pragma unroll
+          for (int w = 0; w < SWAVE; ++w) sum += ssr[w * 32 + m];
+        }
+        pend[r][u] = sum;
+      }
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    pitem = item;
+    item = nitem_k;
+    it = nx;
+  }
+  store_pending();
+}
+
+// Partial sums of an item: W_TOK-token items (proj_wide_kernel) or TILE-token
+// items (mhc_split_kernel); the finish kernels take the item size TT.
+
 // Lane exchange within rows of 16 lanes (DPP): quad permutations and row rotations.
 constexpr int DPP_QXOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
 constexpr int DPP_QXOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
@@ -605,13 +829,15 @@ __device__ __forceinline__ float gate_logit(float a, float p, float invr, float 
 // 4C), z = alpha * P / r + b, h_pre = sigmoid, h_post = 2 sigmoid, and
 // Sinkhorn-Knopp on the 4x4 block held by the 16 lanes. Returns h_pre[e] in
 // lanes e < 4; stores the coefficients when `store` (uniform over the row).
+// TT: tokens per item of the partials.
+template <int TT>
 __device__ __forceinline__ float token_coeffs(const float* __restrict__ part, int64_t tt, int e, int64_t C, int S,
                                               const float* __restrict__ bias, Gate gate, int iters, bool store,
                                               float* __restrict__ h_pre_out, float* __restrict__ h_post_out,
                                               float* __restrict__ h_res_out) {
-  using PG = PartGeom<3>;
-  const int64_t tile = tt / TILE;
-  const int m = (int)(tt - tile * TILE);
+  using PG = PartGeom<3, TT>;
+  const int64_t tile = tt / TT;
+  const int m = (int)(tt - tile * TT);
   const float* base = part + tile * S * PG::PART + m * PG::PROW;
   float ss = 0.f, pr = 0.f, pe = 0.f;
 #pragma unroll 4
@@ -657,6 +883,7 @@ __device__ __forceinline__ float token_coeffs(const float* __restrict__ part, in
 
 // Coefficients only: 16 threads per token (every lane of a row takes part in
 // the DPP exchanges; rows past T work on the last token and store nothing).
+template <int TT>
 __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C,
                                                             int S, const float* __restrict__ bias, Gate gate,
                                                             int iters, float* __restrict__ h_pre_out,
@@ -664,8 +891,8 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
                                                             float* __restrict__ h_res_out) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tt = g >> 4;
-  token_coeffs(part, tt < T ? tt : T - 1, (int)(g & 15), C, S, bias, gate, iters, tt < T, h_pre_out, h_post_out,
-               h_res_out);
+  token_coeffs<TT>(part, tt < T ? tt : T - 1, (int)(g & 15), C, S, bias, gate, iters, tt < T, h_pre_out, h_post_out,
+                   h_res_out);
 }
 
 // ------------------------------------------------------- xHC finish kernels
@@ -677,19 +904,19 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
 // router lanes: score = sigmoid(P / r). Selection (when nr > 0): k - m rounds
 // of an arg-max over the candidate lanes (equal scores go to the lower stream),
 // then idx = the m fixed streams and the chosen ones in ascending order.
-template <int NB>
+template <int NB, int TT>
 __global__ __launch_bounds__(256) void xpre_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C, int N,
                                                           int per_tile, int npre, int nr, int k, int m,
                                                           const float* __restrict__ b_pre, float a_pre,
                                                           float* __restrict__ h_pre, float* __restrict__ score,
                                                           int32_t* __restrict__ idx) {
-  using PG = PartGeom<NB>;
+  using PG = PartGeom<NB, TT>;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tt = g >> 5;
   const int c = (int)(g & 31);
   const int64_t tc = tt < T ? tt : T - 1;
-  const int64_t tile = tc / TILE;
-  const int mrow = (int)(tc - tile * TILE);
+  const int64_t tile = tc / TT;
+  const int mrow = (int)(tc - tile * TT);
   const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
   const int cc = c < PG::NCOLP ? c : 0;
   float ss = 0.f, pc = 0.f;
@@ -817,11 +1044,12 @@ __global__ __launch_bounds__(256) void pre4_kernel(const uint16_t* __restrict__ 
 // h_pre of token tt ([mHC] Eq. 15-18) from the partial projections, with the
 // arithmetic of token_coeffs (slices added in order, the same gate helpers), so
 // both give the same floats.
+template <int TT>
 __device__ __forceinline__ void token_pre4(const float* __restrict__ part, int64_t tt, int64_t C, int S,
                                            const float* __restrict__ bias, float a_pre, float (&w)[4]) {
-  using PG = PartGeom<3>;
-  const int64_t tile = tt / TILE;
-  const int m = (int)(tt - tile * TILE);
+  using PG = PartGeom<3, TT>;
+  const int64_t tile = tt / TT;
+  const int m = (int)(tt - tile * TT);
   const float* base = part + tile * S * PG::PART + m * PG::PROW;
   float ss = 0.f, pe[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
@@ -845,6 +1073,7 @@ __device__ __forceinline__ void token_pre4(const float* __restrict__ part, int64
 // before wrote the state tile by tile from the first, so the rows it wrote
 // last (the likeliest to be still in the last-level cache) are read first,
 // and the pass ends on the first rows, where the next split pass begins.
+template <int TT>
 __global__ __launch_bounds__(256) void finish_pre4_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
                                                           const float* __restrict__ bias, Gate gate, int iters,
                                                           float* __restrict__ h_pre_out,
@@ -855,8 +1084,8 @@ __global__ __launch_bounds__(256) void finish_pre4_kernel(const float* __restric
   if ((int)blockIdx.x < ncb) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t tt = g >> 4;
-    token_coeffs(part, tt < T ? tt : T - 1, (int)(g & 15), C, S, bias, gate, iters, tt < T, h_pre_out, h_post_out,
-                 h_res_out);
+    token_coeffs<TT>(part, tt < T ? tt : T - 1, (int)(g & 15), C, S, bias, gate, iters, tt < T, h_pre_out,
+                     h_post_out, h_res_out);
     return;
   }
   const int64_t nch = C / 8;
@@ -867,7 +1096,7 @@ __global__ __launch_bounds__(256) void finish_pre4_kernel(const float* __restric
   const uint16_t* p = X + t * 4 * C + c0;
   const uint4 x0 = ld_stream(p), x1 = ld_stream(p + C), x2 = ld_stream(p + 2 * C), x3 = ld_stream(p + 3 * C);
   float w[4];
-  token_pre4(part, t, C, S, bias, gate.a_pre, w);
+  token_pre4<TT>(part, t, C, S, bias, gate.a_pre, w);
   float a[8], b[8], c[8], d[8], o[8];
   unpack8(x0, a);
   unpack8(x1, b);
@@ -1004,19 +1233,24 @@ namespace {
 struct Geom {
   int NG, S, nitem;  // stream groups, channel slices per group, items
 };
-Geom geom(int64_t T, int64_t C, int NG) {
-  const int64_t nsc = (C + SC - 1) / SC;
-  const int64_t S = (nsc + SPI - 1) / SPI;
-  return Geom{NG, (int)S, (int)(((T + TILE - 1) / TILE) * NG * S)};
+// Both item kinds cover SPI * SC = W_SPI * W_SC = 1024 channels of a stream
+// group, so a token's slices are the same for either; TT is the item's tokens.
+static_assert(SPI * SC == W_SPI * W_SC, "channels per item");
+int64_t slices(int64_t C) { return (C + SPI * SC - 1) / (SPI * SC); }
+Geom geom(int64_t T, int64_t C, int NG, int TT) {
+  const int64_t S = slices(C);
+  return Geom{NG, (int)S, (int)(((T + TT - 1) / TT) * NG * S)};
 }
-// the shapes the split kernel addresses with 32-bit buffer offsets and int item ids
+// Tokens rounded up to whole W_TOK-token items: the partial buffer sized for
+// them holds the partials of either item size.
+int64_t part_tokens(int64_t T) { return (T + W_TOK - 1) / W_TOK * W_TOK; }
+// the shapes the split kernels address with 32-bit buffer offsets and int item ids
 bool shape_ok(int64_t T, int64_t C, int NG, int NB) {
   if (C % 32 != 0 || C < 32 || C >= (1ll << 24)) return false;
-  const int64_t nsc = (C + SC - 1) / SC, S = (nsc + SPI - 1) / SPI;
-  return ((T + TILE - 1) / TILE) * NG * S * (TILE * (NB * 8 + 1)) * 4 < (1ll << 31);
+  return part_tokens(T) * NG * slices(C) * (NB * 8 + 1) * 4 < (1ll << 31);
 }
 int64_t part_bytes(int64_t T, int64_t C, int NG, int NB) {
-  return (int64_t)geom(T, C, NG).nitem * TILE * (NB * 8 + 1) * 4;
+  return part_tokens(T) * NG * slices(C) * (NB * 8 + 1) * 4;
 }
 int nb_for(int ncols) { return ncols <= 16 ? 2 : (ncols <= 24 ? 3 : 4); }
 int grid_for(int nitem) {
@@ -1057,6 +1291,13 @@ hipError_t launch_split_nb(int nb, const SplitArgs& A, hipStream_t st) {
   }
 }
 
+// projection only, W_TOK-token items (A from geom(..., W_TOK))
+template <int NB, int MODE>
+hipError_t launch_wide(const SplitArgs& A, hipStream_t st) {
+  hipLaunchKernelGGL((proj_wide_kernel<NB, MODE>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const float* phi_a, int na, const float* phi_b, int nb, int64_t K, int ncolp, void* packed,
                        hipStream_t st) {
   hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)(K / 64)), dim3(256), 0, st, phi_a, na, phi_b, nb, ncolp,
@@ -1064,19 +1305,21 @@ hipError_t launch_pack(const float* phi_a, int na, const float* phi_b, int nb, i
   return hipGetLastError();
 }
 
+template <int TT>
 hipError_t launch_finish(const float* part, int64_t T, int64_t C, int S, const float* bias, Gate gate, int iters,
                          float* h_pre, float* h_post, float* h_res, hipStream_t st) {
   const int64_t threads = T * 16;
-  hipLaunchKernelGGL(coeffs_finish_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, T, C, S,
+  hipLaunchKernelGGL(coeffs_finish_kernel<TT>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, part, T, C, S,
                      bias, gate, iters, h_pre, h_post, h_res);
   return hipGetLastError();
 }
 
+template <int TT>
 hipError_t launch_finish_pre4(const float* part, int64_t T, int64_t C, int S, const float* bias, Gate gate,
                               int iters, float* h_pre, float* h_post, float* h_res, const void* X, void* F_in,
                               hipStream_t st) {
   const int64_t ncb = (T * 16 + 255) / 256, npb = (T * (C / 8) + 255) / 256;
-  hipLaunchKernelGGL(finish_pre4_kernel, dim3((unsigned)(ncb + npb)), dim3(256), 0, st, part, T, C, S, bias, gate,
+  hipLaunchKernelGGL(finish_pre4_kernel<TT>, dim3((unsigned)(ncb + npb)), dim3(256), 0, st, part, T, C, S, bias, gate,
                      iters, h_pre, h_post, h_res, (int)ncb, (const uint16_t*)X, (uint16_t*)F_in);
   return hipGetLastError();
 }
@@ -1135,10 +1378,11 @@ hipError_t launch_fast_coeffs_pre(const void* X, int64_t T, int64_t C, const flo
                                   void* packed, float* partial, hipStream_t st) {
   hipError_t e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st);
   if (e != hipSuccess) return e;
-  const Geom g = geom(T, C, 1);
-  if ((e = launch_split<false, 3, ROWS_CONTIG>(args(X, T, C, 4 * C, g, packed, partial), st)) != hipSuccess) return e;
-  if (!F_in) return launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, st);
-  return launch_finish_pre4(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, X,
+  const Geom g = geom(T, C, 1, W_TOK);
+  if ((e = launch_wide<3, ROWS_CONTIG>(args(X, T, C, 4 * C, g, packed, partial), st)) != hipSuccess) return e;
+  if (!F_in)
+    return launch_finish<W_TOK>(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, st);
+  return launch_finish_pre4<W_TOK>(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre, h_post, h_res, X,
                             F_in, st);
 }
 
@@ -1156,7 +1400,7 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
     if ((e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st)) != hipSuccess) return e;
     phi_packed = packed;
   }
-  const Geom g = geom(T, C, 1);
+  const Geom g = geom(T, C, 1, TILE);
   SplitArgs A = args(X, T, C, 4 * C, g, phi_packed, partial);
   A.h_res_in = h_res;
   A.h_post_in = h_post;
@@ -1164,8 +1408,9 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
   A.Y = (uint16_t*)Y;
   if ((e = launch_split<true, 3, ROWS_CONTIG>(A, st)) != hipSuccess) return e;
   if (!F_in_n)
-    return launch_finish(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n, h_res_n, st);
-  return launch_finish_pre4(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n,
+    return launch_finish<TILE>(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n,
+                               h_res_n, st);
+  return launch_finish_pre4<TILE>(partial, T, C, g.S, bias, Gate{a_pre, a_post, a_res}, iters, h_pre_n, h_post_n,
                             h_res_n, Y, F_in_n, st);
 }
 
@@ -1196,31 +1441,43 @@ XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype) {
   return {(int64_t)k * C / 8 * (nb * 16) * 16, part_bytes(T, C, 1, nb)};
 }
 
+// Full-state projection and finish, on 64-token items (proj_wide_kernel, half
+// the phi traffic per byte of state) or 32-token items (mhc_split_kernel). The
+// item size follows from N and m alone, through the column count of the pass
+// with both maps (N + N - m): up to 24 columns the wide kernel, beyond it the
+// 32-token kernel, whose registers hold 32 columns (the wide kernel's 4 token
+// blocks of 4 accumulator sets do not fit, and measured slower at N = 16). So
+// the pre map, the router and both together add every column in one order
+// and give the same bits.
+template <int NB, int TT>
+static hipError_t xhc_full_nb(const void* X, int64_t T, int N, int64_t C, int k, int m, int npre, int nr,
+                              const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
+                              const void* packed, float* partial, hipStream_t st) {
+  const Geom g = geom(T, C, N / 4, TT);
+  const SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);
+  if constexpr (TT == W_TOK) hipLaunchKernelGGL((proj_wide_kernel<NB, ROWS_GROUPS>), dim3(grid_for(A.nitem)),
+                                                dim3(STHR), 0, st, A);
+  else hipLaunchKernelGGL((mhc_split_kernel<false, NB, ROWS_GROUPS>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = T * 32;
+  hipLaunchKernelGGL((xpre_finish_kernel<NB, TT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     partial, T, C, N, g.NG * g.S, npre, nr, k, m, b_pre, a_pre, h_pre, score, idx);
+  return hipGetLastError();
+}
+
 static hipError_t xhc_full_proj(const void* X, int64_t T, int N, int64_t C, int k, int m, int npre, int nr, int nb,
                                  const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
                                  const void* packed, float* partial, hipStream_t st) {
-  const Geom g = geom(T, C, N / 4);
-  hipError_t e;
-  if ((e = launch_split_nb<ROWS_GROUPS>(nb, args(X, T, C, (int64_t)N * C, g, packed, partial), st)) != hipSuccess)
-    return e;
-  const int64_t threads = T * 32;
-  const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
-  const int per_tile = g.NG * g.S;
+  const bool wide = nb_for(N + (N - m)) <= 3;
+#define HC_FULL(NB, TT) \
+  xhc_full_nb<NB, TT>(X, T, N, C, k, m, npre, nr, b_pre, a_pre, h_pre, score, idx, packed, partial, st)
   switch (nb) {
-    case 2:
-      hipLaunchKernelGGL(xpre_finish_kernel<2>, grid, blk, 0, st, partial, T, C, N, per_tile, npre, nr, k, m, b_pre,
-                         a_pre, h_pre, score, idx);
-      break;
-    case 3:
-      hipLaunchKernelGGL(xpre_finish_kernel<3>, grid, blk, 0, st, partial, T, C, N, per_tile, npre, nr, k, m, b_pre,
-                         a_pre, h_pre, score, idx);
-      break;
-    default:
-      hipLaunchKernelGGL(xpre_finish_kernel<4>, grid, blk, 0, st, partial, T, C, N, per_tile, npre, nr, k, m, b_pre,
-                         a_pre, h_pre, score, idx);
-      break;
+    case 2: return wide ? HC_FULL(2, W_TOK) : HC_FULL(2, TILE);
+    case 3: return wide ? HC_FULL(3, W_TOK) : HC_FULL(3, TILE);
+    default: return HC_FULL(4, TILE);
   }
-  return hipGetLastError();
+#undef HC_FULL
 }
 
 hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int k, int m, const float* phi_pre,
@@ -1289,7 +1546,7 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
   const int nb = nb_for(ncols);
   hipError_t e = launch_pack(phi_act, ncols, nullptr, 0, 4 * C, nb * 8, packed, st);
   if (e != hipSuccess) return e;
-  const Geom g = geom(T, C, 1);
+  const Geom g = geom(T, C, 1, TILE);
   SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);
   A.idx = idx;
   A.kidx = 4;

@@ -343,7 +343,8 @@ def test_pre_read_h_pre_matches_returned_coefficients_bit_exact(T, C):
     """The fused pre-read forms each token's h_pre from the partial projections
     itself; its F_in must be exactly hc_pre(X_next, h_pre') with the h_pre' the
     same call returns, and the same whether or not h_pre' is requested (also
-    for hc_coeffs_pre)."""
+    for hc_coeffs_pre, whose projection adds the channels in another order than
+    hc_post_pre's, so its h_pre' may differ from that one in the last bits)."""
     note(f"mHC pre-read h_pre consistency n=4 C={C} T={T}")
     inp = synth.mhc_layer(80 + T, 0, T, 4, C, synth.BF16)
     nxt = synth.mhc_layer(80 + T, 1, T, 4, C, synth.BF16, draw_x=False)
@@ -356,11 +357,14 @@ def test_pre_read_h_pre_matches_returned_coefficients_bit_exact(T, C):
     F_ref = hc.hc_pre(Xn, hp2)
     hq, _, _, F_c = hc.hc_coeffs_pre(Xn, dev(nxt["phi"]), dev(nxt["bias"]), [0.01] * 3)
     _, _, _, F_d = hc.hc_coeffs_pre(Xn, dev(nxt["phi"]), dev(nxt["bias"]), [0.01] * 3, want_h_pre=False)
+    F_q = hc.hc_pre(Xn, hq)
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int16).cpu().numpy()
-    np.testing.assert_array_equal(hq.cpu().numpy(), hp2.cpu().numpy())
-    for F in (F_a, F_b, F_c, F_d):
+    np.testing.assert_allclose(hq.cpu().numpy(), hp2.cpu().numpy(), rtol=1e-6, atol=0)
+    for F in (F_a, F_b):
         np.testing.assert_array_equal(bits(F), bits(F_ref))
+    for F in (F_c, F_d):
+        np.testing.assert_array_equal(bits(F), bits(F_q))
 
 
 def test_phi_pack_layout_pin():
