@@ -393,3 +393,105 @@ def static_post(X, h_res, h_post, F_out):
     X = _f64(X)
     T, n, _ = X.shape
     return hc_post(X, np.broadcast_to(_f64(h_res), (T, n, n)), np.broadcast_to(_f64(h_post), (T, n)), F_out)
+
+
+# ---------------------------------------------------------------------------
+# mHC backward (gradients of one sublayer)
+# ---------------------------------------------------------------------------
+
+def sinkhorn_knopp_backward(logits, grad, iters: int):
+    """Gradient of sum(grad * SK(logits)) with respect to the logits.
+
+    mHC notes 4.3.1, on Eq. 19: the backward recomputes the iterates and walks the
+    iterations in reverse. The forward is sinkhorn_knopp: M^(0) = exp(logits);
+    each iteration A = T_c(M) (A_ij = M_ij / s_j, s_j the column sum), then
+    B = T_r(A) (B_ij = A_ij / q_i, q_i the row sum). For Y = M / s with s the sum
+    along one axis and upstream G, dM = (G - sum_axis(G * Y)) / s. The last step is
+    the derivative of exp: d logits = dM^(0) * M^(0). Works on [..., n, n].
+    """
+    z = _f64(logits)
+    M = np.exp(z)
+    saved = []
+    for _ in range(int(iters)):
+        s = M.sum(axis=-2, keepdims=True)
+        A = M / s
+        q = A.sum(axis=-1, keepdims=True)
+        B = A / q
+        saved.append((s, A, q, B))
+        M = B
+    g = _f64(grad)
+    for s, A, q, B in reversed(saved):
+        g = (g - (g * B).sum(axis=-1, keepdims=True)) / q  # through T_r
+        g = (g - (g * A).sum(axis=-2, keepdims=True)) / s  # through T_c
+    return g * np.exp(z)
+
+
+def mhc_sublayer_backward(X, phi, bias, alpha, F_out, dX_next, dF_in, sinkhorn_iters: int = 20):
+    """Gradients of one mHC sublayer (mhc_sublayer) for the upstream gradients
+    dX_next [T, n, C] of X_next and dF_in [T, C] of F_in.
+
+    The forward is recomputed from X (mHC notes 4.3: the intermediates of the mHC
+    kernels are recomputed in the backward rather than kept), in the form of Eq.
+    14-16: P = vec(x) phi, r = ||vec x|| / sqrt(nC), z = alpha_block * P / r + b.
+    Then the chain rule in reverse order:
+      F_post,res (Eq. 3): dF_out = H_post dX_next, dH_res[i, j] = <dX_next_i, x_j>,
+        dH_post[i] = <dX_next_i, F_out>, dx_j += sum_i H_res[i, j] dX_next_i;
+      F_pre: dH_pre[i] = <dF_in, x_i>, dx_i += H_pre[i] dF_in;
+      Eq. 17-19: dz = dH_pre sigma', dH_post 2 sigma', Sinkhorn backward;
+      Eq. 16: db = dz, dalpha_block = sum over the block of dz P / r,
+        dP = alpha_block dz / r, d(1/r) = sum alpha_block dz P;
+      Eq. 15: with 1/r = (ss / nC)^(-1/2), ss = ||vec x||^2,
+        dss = -(1/2) d(1/r) (1/r)^3 / nC, and d vec x += 2 dss vec x;
+      Eq. 14: d vec x += dP phi^T, dphi = vec(x)^T dP.
+    Reading for the all-zero state: 1/r is taken as 0 there (as in the forward)
+    and contributes no gradient.
+    Returns dict(dX [T, n, C], dF_out [T, C], dphi [nC, n*n + 2n], dbias
+    [n*n + 2n], dalpha [3], dz [T, n*n + 2n]); dbias and dalpha sum over tokens.
+    """
+    X = _f64(X)
+    T, n, C = X.shape
+    N = n * C
+    x = X.reshape(T, N)
+    phi = _f64(phi)
+    assert phi.shape == (N, n * n + 2 * n)
+    a = _f64(alpha)
+    gate = np.concatenate([np.full(n, a[0]), np.full(n, a[1]), np.full(n * n, a[2])])
+    ss = np.sum(x * x, axis=-1)
+    r = np.sqrt(ss / N)
+    rho = np.where(r > 0.0, 1.0 / np.where(r > 0.0, r, 1.0), 0.0)
+    P = x @ phi
+    z = gate[None, :] * P * rho[:, None] + _f64(bias)[None, :]
+    h_pre = sigmoid(z[:, :n])
+    s_post = sigmoid(z[:, n:2 * n])
+    h_post = 2.0 * s_post
+    z_res = z[:, 2 * n:].reshape(T, n, n)
+    h_res = sinkhorn_knopp(z_res, sinkhorn_iters)
+
+    dXn = _f64(dX_next)
+    dFi = _f64(dF_in)
+    Fo = _f64(F_out)
+    # post/res write
+    dF_out = np.einsum("ti,tic->tc", h_post, dXn)
+    dh_res = np.einsum("tic,tjc->tij", dXn, X)
+    dh_post = np.einsum("tic,tc->ti", dXn, Fo)
+    dX = np.einsum("tij,tic->tjc", h_res, dXn)
+    # pre-read
+    dh_pre = np.einsum("tc,tic->ti", dFi, X)
+    dX = dX + h_pre[:, :, None] * dFi[:, None, :]
+    # activations and Sinkhorn
+    dz = np.empty_like(z)
+    dz[:, :n] = dh_pre * h_pre * (1.0 - h_pre)
+    dz[:, n:2 * n] = dh_post * 2.0 * s_post * (1.0 - s_post)
+    dz[:, 2 * n:] = sinkhorn_knopp_backward(z_res, dh_res, sinkhorn_iters).reshape(T, n * n)
+    # gates and bias
+    dbias = dz.sum(axis=0)
+    u = dz * P * rho[:, None]
+    dalpha = np.array([u[:, :n].sum(), u[:, n:2 * n].sum(), u[:, 2 * n:].sum()])
+    dP = dz * gate[None, :] * rho[:, None]
+    drho = np.sum(dz * gate[None, :] * P, axis=-1)
+    dss = np.where(ss > 0.0, -0.5 * drho * rho ** 3 / N, 0.0)
+    # RMS factor and projection
+    dx = dP @ phi.T + 2.0 * dss[:, None] * x
+    dphi = x.T @ dP
+    dX = dX + dx.reshape(T, n, C)
+    return dict(dX=dX, dF_out=dF_out, dphi=dphi, dbias=dbias, dalpha=dalpha, dz=dz)

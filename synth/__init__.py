@@ -16,6 +16,9 @@ stream dtype with round-to-nearest-even when the stream is bfloat16):
   F_out[T,C] ~ N(0,1), conv weights w_kappa[C, kappa] ~ N(0, 1/kappa) for the
   augmented (K > 1) case. b_pre = 0, b_act = [0]*(k*K) + vec(I_k), alpha = 0.01.
   Draw order: X, phi_pre, w_router, phi_act, F_out, conv weights.
+* mHC upstream gradients (the backward's inputs): dX_next[T,n,C] ~ N(0,1) and
+  dF_in[T,C] ~ N(0,1) in the stream dtype, from the side stream 1 of (seed,
+  layer). Draw order: dX_next, dF_in.
 
 Arrays are returned as host numpy float32 arrays whose values are exactly
 representable in the stream dtype, plus (for bfloat16 streams) the raw uint16
@@ -109,6 +112,12 @@ def mhc_layer(seed: int, layer: int, T: int, n: int, C: int, dtype: str,
     out["bias"] = mhc_bias(n)
     out["alpha"] = np.array([ALPHA, ALPHA, ALPHA], np.float32)
     return out
+
+
+def mhc_grads(seed: int, layer: int, T: int, n: int, C: int, dtype: str) -> dict:
+    """Upstream gradients of one mHC sublayer: dX_next [T, n, C] and dF_in [T, C]."""
+    rng = make_rng(seed, layer, stream=1)
+    return {"dX_next": Tensor(normal(rng, (T, n, C)), dtype), "dF_in": Tensor(normal(rng, (T, C)), dtype)}
 
 
 def xhc_layer(seed: int, layer: int, T: int, N: int, C: int, k: int, m: int,

@@ -639,3 +639,99 @@ def test_static_apply_is_the_broadcast_mhc_apply():
             for i in range(n):
                 want = sum(hr[i, j] * X[t, j, c] for j in range(n)) + hq[i] * F[t, c]
                 assert math.isclose(Xn[t, i, c], want, rel_tol=1e-13, abs_tol=1e-14)
+
+
+# ---------------------------------------------------------------- backward
+
+def _central_difference(f, arr, h=1e-6):
+    """Brute-force gradient of the scalar f at arr by central differences."""
+    out = np.zeros_like(arr)
+    for idx in np.ndindex(arr.shape):
+        a = arr.copy()
+        a[idx] += h
+        up = f(a)
+        a[idx] -= 2 * h
+        out[idx] = (up - f(a)) / (2 * h)
+    return out
+
+
+@pytest.mark.parametrize("n,iters", [(4, 20), (3, 5), (2, 1)])
+def test_sinkhorn_backward_finite_differences(n, iters):
+    """The Sinkhorn backward is the gradient of sum(G * SK(z)): central
+    differences of the forward oracle, entry by entry."""
+    rng = np.random.default_rng(300 + n)
+    z = rng.standard_normal((2, n, n))
+    G = rng.standard_normal((2, n, n))
+    got = O.sinkhorn_knopp_backward(z, G, iters)
+    want = _central_difference(lambda a: np.sum(G * O.sinkhorn_knopp(a, iters)), z)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-8 * np.abs(want).max())
+
+
+def test_sinkhorn_backward_invariances_and_zero_iterations():
+    """The first step normalises columns, so SK(exp(z + v_j)) = SK(exp(z)) for any
+    column shift v: the gradient sums to zero down every column, exactly. Row shifts
+    only cancel in the limit: row sums shrink as the iterations grow. With no
+    iteration SK is exp, whose gradient is G * exp(z)."""
+    rng = np.random.default_rng(310)
+    z = rng.standard_normal((3, 4, 4))
+    G = rng.standard_normal((3, 4, 4))
+    for iters in (1, 5, 20):
+        g = O.sinkhorn_knopp_backward(z, G, iters)
+        np.testing.assert_allclose(g.sum(axis=-2), 0.0, atol=1e-14)
+    row5 = np.abs(O.sinkhorn_knopp_backward(z, G, 5).sum(axis=-1)).max()
+    row40 = np.abs(O.sinkhorn_knopp_backward(z, G, 40).sum(axis=-1)).max()
+    assert row40 < 1e-3 * row5
+    np.testing.assert_allclose(O.sinkhorn_knopp_backward(z, G, 0), G * np.exp(z), rtol=1e-15)
+
+
+def _sublayer_loss(dXn, dFi, iters):
+    def L(X, phi, b, al, Fo):
+        o = O.mhc_sublayer(X, phi, b, al, Fo, iters)
+        return np.sum(dXn * o["X_next"]) + np.sum(dFi * o["F_in"])
+    return L
+
+
+@pytest.mark.parametrize("T,n,C,iters", [(2, 4, 3, 20), (3, 2, 5, 7), (1, 1, 4, 3)])
+def test_sublayer_backward_finite_differences(T, n, C, iters):
+    """Every gradient of mhc_sublayer_backward (state, phi, bias, the three gates,
+    F_out) against central differences of L = <dX_next, X_next> + <dF_in, F_in>
+    through the forward oracle. Gates and phi are large enough that no sigmoid
+    saturates and Sinkhorn is far from its fixed point."""
+    rng = np.random.default_rng(320 + 10 * n + C)
+    X = rng.standard_normal((T, n, C))
+    phi = 0.3 * rng.standard_normal((n * C, n * n + 2 * n))
+    b = 0.5 * rng.standard_normal(n * n + 2 * n)
+    al = np.array([0.7, 0.9, 1.3])
+    Fo = rng.standard_normal((T, C))
+    dXn = rng.standard_normal((T, n, C))
+    dFi = rng.standard_normal((T, C))
+    L = _sublayer_loss(dXn, dFi, iters)
+    g = O.mhc_sublayer_backward(X, phi, b, al, Fo, dXn, dFi, iters)
+    cases = [("dX", X, lambda a: L(a, phi, b, al, Fo)), ("dphi", phi, lambda a: L(X, a, b, al, Fo)),
+             ("dbias", b, lambda a: L(X, phi, a, al, Fo)), ("dalpha", al, lambda a: L(X, phi, b, a, Fo)),
+             ("dF_out", Fo, lambda a: L(X, phi, b, al, a))]
+    for name, arr, f in cases:
+        want = _central_difference(f, arr)
+        np.testing.assert_allclose(g[name], want, rtol=0, atol=1e-7 * np.abs(want).max(), err_msg=name)
+
+
+def test_sublayer_backward_zero_state_and_bias_gradient():
+    """The all-zero state: the forward's z is the bias alone (1/r taken as 0), so
+    the gradient reaching x is the plain transpose of the apply, H_res^T dX_next +
+    H_pre dF_in, with the maps of z = b; dphi is zero (vec x = 0) and the bias
+    gradient is the logit gradient itself."""
+    rng = np.random.default_rng(330)
+    T, n, C = 2, 4, 6
+    X = np.zeros((T, n, C))
+    phi = rng.standard_normal((n * C, n * n + 2 * n))
+    b = rng.standard_normal(n * n + 2 * n)
+    dXn = rng.standard_normal((T, n, C))
+    dFi = rng.standard_normal((T, C))
+    g = O.mhc_sublayer_backward(X, phi, b, (0.5, 0.5, 0.5), rng.standard_normal((T, C)), dXn, dFi, 20)
+    hp = 1.0 / (1.0 + np.exp(-b[:n]))
+    hr = O.sinkhorn_knopp(b[2 * n:].reshape(n, n), 20)
+    want = np.einsum("ij,tic->tjc", hr, dXn) + hp[None, :, None] * dFi[:, None, :]
+    np.testing.assert_allclose(g["dX"], want, rtol=1e-14, atol=1e-14)
+    np.testing.assert_array_equal(g["dphi"], 0.0)
+    np.testing.assert_allclose(g["dbias"], g["dz"].sum(axis=0), rtol=1e-15)
+    np.testing.assert_array_equal(g["dalpha"], 0.0)
