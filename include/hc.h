@@ -68,6 +68,7 @@ extern "C" {
 #define HC_MAX_COMPONENTS 8   /* K = r + 1 write-back components */
 #define HC_MAX_KAPPA 32       /* causal conv kernel size */
 #define HC_MAX_ITERS 10000    /* Sinkhorn iterations */
+#define HC_MAX_BWD_ITERS 64   /* Sinkhorn iterations of hc_backward (iterates kept on chip) */
 
 /* Human-readable text of a status code (static string, never NULL). */
 const char* hc_status_string(int status);
@@ -119,6 +120,38 @@ int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C,
                   float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters,
                   float* h_pre, float* h_post, float* h_res, void* F_in,
                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * hc_backward - gradients of one mHC sublayer ([mHC] 4.3.1 Kernel Fusion: the
+ * backward of the Eq. 14-15 projection, two products over the same x, and a
+ * Sinkhorn-Knopp backward that recomputes the iterates on chip; 4.3 recomputes
+ * the forward's intermediates from x in the backward).
+ *   Forward (hc_coeffs, hc_pre, hc_post with the same arguments):
+ *     F_in = H_pre x,  X_next = H_res x + H_post^T F_out.
+ *   Inputs: X [T, 4, C], F_out [T, C] (the forward's), dX_next [T, 4, C] and
+ *     dF_in [T, C] (upstream gradients of X_next and F_in), all bfloat16;
+ *     phi, bias, alpha_*, sinkhorn_iters as for hc_coeffs.
+ *   Outputs: dX [T, 4, C] and dF_out [T, C] bfloat16 (rounded once from float32),
+ *     dphi [4C, 24], dbias [24] (column order of phi), dalpha [3]
+ *     (pre, post, res) float32; dphi, dbias and dalpha are sums over the T tokens.
+ *   Covered: dtype HC_BF16 (HC_F32 -> HC_ERR_DTYPE), n = 4, C a multiple of 32,
+ *   1 <= sinkhorn_iters <= HC_MAX_BWD_ITERS (else HC_ERR_SHAPE). The all-zero
+ *   state takes 1/r = 0 (as the forward) and passes no gradient through r.
+ *   Alignment: X, F_out, dX_next, dF_in, dX, dF_out 16 bytes; the float arrays 4
+ *   bytes; workspace 256 bytes, at least hc_backward_workspace_bytes (the
+ *   recomputed coefficients, projection partials, per-token gradients and the
+ *   partial sums of dphi). No output may overlap an input, another output or the
+ *   workspace (HC_ERR_ALIAS). Deterministic: every sum runs in a fixed order.
+ *   hc_backward_workspace_bytes: 0 for T = 0, -1 for sizes or a dtype that
+ *   hc_backward does not cover.
+ */
+int64_t hc_backward_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
+int hc_backward(const void* X, int dtype, int64_t T, int n, int64_t C,
+                const float* phi, const float* bias,
+                float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters,
+                const void* F_out, const void* dX_next, const void* dF_in,
+                void* dX, void* dF_out, float* dphi, float* dbias, float* dalpha,
+                void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * hc_post - fused post/res write F_post,res = H_res x + H_post^T F ([mHC] Eq. 3,

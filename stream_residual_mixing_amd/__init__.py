@@ -34,6 +34,9 @@ _SIGS = {
     "hc_coeffs_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float,
                                _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "hc_backward_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int]),
+    "hc_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float, _c_int,
+                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_post_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _c_float,
                                 _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_phi_packed_bytes": (_c_i64, [_c_int, _c_i64, _c_int]),
@@ -189,6 +192,34 @@ def hc_post(X, h_res, h_post, F_out, *, out=None, stream=None):
                                     _ptr(_f32(h_post, "h_post")), _ptr(F_out), _ptr(X_next),
                                     _stream(X.device, stream)))
     return X_next
+
+
+def hc_backward_workspace_bytes(T: int, n: int, C: int, dtype) -> int:
+    return int(lib().hc_backward_workspace_bytes(T, n, C, _DT[dtype]))
+
+
+def hc_backward(X, phi, bias, alpha, F_out, dX_next, dF_in, sinkhorn_iters=20, *, out=None, workspace=None,
+                stream=None):
+    """Gradients of one mHC sublayer (n = 4, bfloat16): (dX, dF_out, dphi, dbias, dalpha)."""
+    X = _dev_tensor(X, "X", (torch.bfloat16,))
+    T, n, C = X.shape
+    F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
+    dX_next = _dev_tensor(dX_next, "dX_next", (X.dtype,))
+    dF_in = _dev_tensor(dF_in, "dF_in", (X.dtype,))
+    phi, bias = _f32(phi, "phi"), _f32(bias, "bias")
+    if out is None:
+        dev = X.device
+        out = (torch.empty_like(X), torch.empty(T, C, dtype=X.dtype, device=dev),
+               torch.empty(n * C, n * n + 2 * n, device=dev), torch.empty(n * n + 2 * n, device=dev),
+               torch.empty(3, device=dev))
+    dX, dF_out, dphi, dbias, dalpha = out
+    ws = _workspace(hc_backward_workspace_bytes(T, n, C, X.dtype), X.device, workspace)
+    a = [float(v) for v in alpha]
+    _check("hc_backward", lib().hc_backward(_ptr(X), _DT[X.dtype], T, n, C, _ptr(phi), _ptr(bias), a[0], a[1], a[2],
+                                            int(sinkhorn_iters), _ptr(F_out), _ptr(dX_next), _ptr(dF_in),
+                                            _ptr(dX), _ptr(dF_out), _ptr(dphi), _ptr(dbias), _ptr(dalpha),
+                                            _ptr(ws), ws.numel(), _stream(X.device, stream)))
+    return dX, dF_out, dphi, dbias, dalpha
 
 
 def hc_post_coeffs(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sinkhorn_iters=20, *, out=None,
@@ -420,7 +451,7 @@ def hc_copy_probe(src, dst, *, stream=None):
 
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
-    "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
+    "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
     "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",

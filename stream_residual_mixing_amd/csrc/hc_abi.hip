@@ -226,6 +226,51 @@ int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const f
   return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X, F_in}), X, T, n, C, hp, F_in, st));
 }
 
+int64_t hc_backward_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
+  if (T < 0) return -1;
+  if (T == 0) return 0;
+  if (!hc::fast_backward_supported(dtype, n, T, C, 1)) return -1;
+  return hc::fast_backward_ws_bytes(T, C);
+}
+
+int hc_backward(const void* X, int dtype, int64_t T, int n, int64_t C, const float* phi, const float* bias,
+                float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters, const void* F_out,
+                const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi, float* dbias,
+                float* dalpha, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (dtype != HC_BF16) return HC_ERR_DTYPE;
+  if (T < 0 || n != 4 || C < 32 || C % 32 != 0 || C > (1ll << 26) || sinkhorn_iters < 1 ||
+      sinkhorn_iters > HC_MAX_BWD_ITERS)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!hc::fast_backward_supported(dtype, n, T, C, sinkhorn_iters)) return HC_ERR_SHAPE;
+  if (!X || !phi || !bias || !F_out || !dX_next || !dF_in || !dX || !dF_out || !dphi || !dbias || !dalpha)
+    return HC_ERR_NULL;
+  for (const void* p : {X, F_out, dX_next, dF_in, (const void*)dX, (const void*)dF_out})
+    if (!aligned_to(p, 16)) return HC_ERR_ALIGN;
+  for (const void* p : {(const void*)phi, (const void*)bias, (const void*)dphi, (const void*)dbias,
+                        (const void*)dalpha})
+    if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
+  const int64_t wsb = hc::fast_backward_ws_bytes(T, C);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t xb = T * 4 * C * 2, fb = T * C * 2, pb = 4 * C * 24 * 4;
+  const void* ins[6] = {X, phi, bias, F_out, dX_next, dF_in};
+  const int64_t ib[6] = {xb, pb, 24 * 4, fb, xb, fb};
+  const void* outs[6] = {dX, dF_out, dphi, dbias, dalpha, workspace};
+  const int64_t ob[6] = {xb, fb, pb, 24 * 4, 3 * 4, wsb};
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return HC_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  }
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_fast_backward(X, T, C, phi, bias, alpha_pre, alpha_post, alpha_res,
+                                                sinkhorn_iters, F_out, dX_next, dF_in, dX, dF_out, dphi, dbias,
+                                                dalpha, workspace, (hipStream_t)stream));
+}
+
 int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
             const float* h_post, const void* F_out, void* X_next, void* stream) {
   int s = check_mhc_common(X, dtype, T, n, C);

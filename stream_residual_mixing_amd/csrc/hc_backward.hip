@@ -1,0 +1,501 @@
+// mHC sublayer backward for n = 4 bfloat16 streams on gfx950.
+//
+// "mHC: Manifold-Constrained Hyper-Connections" (paper notes), 4.3.1: the
+// backward of the Eq. 14-15 kernel holds two products over the same x, and the
+// Sinkhorn-Knopp backward recomputes the iterates on chip and walks the
+// iterations; 4.3 also recomputes the mHC kernels' intermediates in the
+// backward instead of keeping them. Here, from X, F_out and the upstream
+// gradients dX_next and dF_in:
+//  1. the projection partials and the coefficients of X, by the forward's
+//     kernels (hc_fused.hip);
+//  2. bwd_reduce_kernel: per token dh = [dH_pre | dH_post | dH_res] (sums over
+//     the channels) and dF_out = H_post dX_next;
+//  3. bwd_coeff_kernel (hc_fused.hip, beside the forward finish whose floats it
+//     recomputes): gates and Sinkhorn backward -> dP, g2, per-token sums;
+//  4. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
+//     dP phi^T product on MFMA;
+//  5. bwd_dphi_kernel: vec(x)^T dP over groups of token tiles on MFMA (the
+//     tokens are the K dimension);
+//  6. the group partials of dphi and the per-token sums of db and dalpha are
+//     added in a fixed order.
+#include "hc.h"
+#include "hc_device.h"
+#include "hc_fast.h"
+
+namespace hc {
+namespace {
+
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+
+constexpr int BS = 4;     // streams
+constexpr int BCOL = 24;  // n*n + 2n columns: [pre 4 | post 4 | res 16]
+constexpr int DPS = 32;   // floats per dP row (columns 24..31 zero)
+constexpr int RED = 28;   // floats per row of the per-token sums
+
+__device__ __forceinline__ bf8_t bf8(const uint4& q) { return __builtin_bit_cast(bf8_t, q); }
+
+__device__ __forceinline__ uint4 ld_nt16(const uint16_t* p) {
+  const u4_t v = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void unpack_bf8(const uint4& q, float v[8]) {
+  v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
+  v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xffff0000u);
+  v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xffff0000u);
+}
+
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact in float32),
+// each as 8 packed bfloat16: about 16 significant bits of v.
+__device__ __forceinline__ void split_bf8(const float v[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h[k] = pack_bf2_hw(v[2 * k], v[2 * k + 1]);
+    l[k] = pack_bf2_hw(v[2 * k] - __uint_as_float(h[k] << 16), v[2 * k + 1] - __uint_as_float(h[k] & 0xffff0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// ------------------------------------------------------------ phi rows
+
+// phi [R = 4C, 24] float32 -> per row 128 bytes: bf16 hi of columns 0..31 (24..31
+// zero), then bf16 lo = bf16(phi - hi). The B operand of dP phi^T: a lane takes
+// one row (channel) and 8 consecutive columns, 16 contiguous bytes.
+__global__ __launch_bounds__(256) void pack_phi_rows_kernel(const float* __restrict__ phi, int64_t R,
+                                                            uint4* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= R * 4) return;
+  const int64_t r = g >> 2;
+  const int q = (int)(g & 3);
+  float p[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int col = q * 8 + e;
+    p[e] = col < BCOL ? phi[r * BCOL + col] : 0.f;
+  }
+  uint4 hi, lo;
+  split_bf8(p, hi, lo);
+  out[r * 8 + q] = hi;
+  out[r * 8 + 4 + q] = lo;
+}
+
+// ------------------------------------------------------- per-token sums
+
+// One 256-thread workgroup per token t. Sums over the channels:
+//   dh[i]          = dH_pre[i]     = <dF_in, x_i>
+//   dh[4 + i]      = dH_post[i]    = <dX_next_i, F_out>
+//   dh[8 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>
+// and dF_out = sum_i H_post[i] dX_next_i (rounded once to bfloat16). Thread tid
+// takes the 8-channel chunks tid, tid + 256, ...; the threads' sums are added by
+// a butterfly in each wave and then the 4 waves in order.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const uint16_t* __restrict__ X,
+                                                         const uint16_t* __restrict__ dXn,
+                                                         const uint16_t* __restrict__ Fo,
+                                                         const uint16_t* __restrict__ dFi, int64_t C,
+                                                         const float* __restrict__ h_post, float* __restrict__ dh,
+                                                         uint16_t* __restrict__ dFo) {
+  __shared__ float wsum[4][BCOL];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  float acc[BCOL];
+#pragma unroll
+  for (int k = 0; k < BCOL; ++k) acc[k] = 0.f;
+  const float4 hq = *reinterpret_cast<const float4*>(h_post + t * 4);
+  const float hpost[4] = {hq.x, hq.y, hq.z, hq.w};
+  const int64_t nch = C / 8;
+  const uint16_t* xr = X + t * BS * C;
+  const uint16_t* dr = dXn + t * BS * C;
+  for (int64_t j = tid; j < nch; j += 256) {
+    const int64_t c = j * 8;
+    uint4 xq[BS], dq[BS];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      xq[i] = ld_nt16(xr + i * C + c);
+      dq[i] = ld_nt16(dr + i * C + c);
+    }
+    const uint4 fq = ld_nt16(Fo + t * C + c), gq = ld_nt16(dFi + t * C + c);
+    float x[BS][8], d[BS][8], f[8], gi[8], o[8];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      unpack_bf8(xq[i], x[i]);
+      unpack_bf8(dq[i], d[i]);
+    }
+    unpack_bf8(fq, f);
+    unpack_bf8(gq, gi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = hpost[0] * d[0][e] + hpost[1] * d[1][e] + hpost[2] * d[2][e] + hpost[3] * d[3][e];
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+        acc[i] += gi[e] * x[i][e];
+        acc[4 + i] += d[i][e] * f[e];
+#pragma unroll
+        for (int k = 0; k < BS; ++k) acc[8 + 4 * i + k] += d[i][e] * x[k][e];
+      }
+    }
+    __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                     pack_bf2_hw(o[6], o[7])},
+                                reinterpret_cast<u4_t*>(dFo + t * C + c));
+  }
+#pragma unroll
+  for (int k = 0; k < BCOL; ++k) acc[k] = wave_sum(acc[k]);
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < BCOL; ++k) wsum[tid >> 6][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid < BCOL) dh[t * BCOL + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+}
+
+// ------------------------------------------------------------------- dX
+
+constexpr int XT = 32;        // tokens per item
+constexpr int XCH = 128;      // channels per item
+constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product tile in LDS
+
+// dX of an item of 32 tokens x 128 channels x 4 streams (512 threads).
+// The streaming loads of thread (token tid >> 4, channels (tid & 15) * 8) are
+// issued first. MFMA phase: wave w forms dP phi^T for stream w >> 1, the four
+// 16-channel blocks (w & 1) * 4 .. + 3 and both 16-token blocks
+// (v_mfma_f32_16x16x32_bf16; A = the tokens' dP rows split hi/lo, B = the
+// channels' phi rows hi/lo; hi*hi + hi*lo + lo*hi into one float32
+// accumulator), and puts the tile in LDS. Then each thread forms, for its
+// token and channels,
+//   dX_j = sum_i H_res[i, j] dX_next_i + H_pre[j] dF_in + (dP phi^T)_j + g2 x_j
+// and stores it rounded once to bfloat16. Rows past T and channels past C are
+// computed on clamped addresses and not stored.
+__global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dXn,
+                                                     const uint16_t* __restrict__ dFi, int64_t T, int64_t C,
+                                                     const float* __restrict__ h_pre, const float* __restrict__ h_res,
+                                                     const float* __restrict__ dP, const float* __restrict__ g2,
+                                                     const uint4* __restrict__ phi_rows, uint16_t* __restrict__ dX) {
+  __shared__ __attribute__((aligned(16))) float prj[BS * XT * PRJ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t chunk = blockIdx.x, tile = blockIdx.y;
+  const int m = tid >> 4, c8 = (tid & 15) * 8;
+  const int64_t t = tile * XT + m, c = chunk * XCH + c8;
+  const bool ok = t < T && c < C;
+  const int64_t tl = t < T ? t : T - 1, cl = c < C ? c : C - 8;
+  uint4 xq[BS], dq[BS];
+#pragma unroll
+  for (int i = 0; i < BS; ++i) {
+    xq[i] = ld_nt16(X + (tl * BS + i) * C + cl);
+    dq[i] = ld_nt16(dXn + (tl * BS + i) * C + cl);
+  }
+  const uint4 fq = ld_nt16(dFi + tl * C + cl);
+
+  const int si = wave >> 1, cb0 = (wave & 1) * 4;
+  const int tau = lane & 15, q = lane >> 4;
+  uint4 ah[2], al[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    int64_t tok = tile * XT + tb * 16 + tau;
+    tok = tok < T ? tok : T - 1;
+    const float4* pp = reinterpret_cast<const float4*>(dP + tok * DPS + q * 8);
+    const float4 p0 = pp[0], p1 = pp[1];
+    const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    split_bf8(v, ah[tb], al[tb]);
+  }
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    int64_t ch = chunk * XCH + (cb0 + cb) * 16 + tau;
+    ch = ch < C ? ch : C - 1;
+    const uint4* pr = phi_rows + ((int64_t)si * C + ch) * 8;
+    const uint4 bh = pr[q], bl = pr[4 + q];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      f4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah[tb]), bf8(bh), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah[tb]), bf8(bl), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(al[tb]), bf8(bh), acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) prj[(si * XT + tb * 16 + q * 4 + e) * PRJ + (cb0 + cb) * 16 + tau] = acc[e];
+    }
+  }
+  __syncthreads();
+
+  const float4* hr4 = reinterpret_cast<const float4*>(h_res + tl * 16);
+  const float4 r0 = hr4[0], r1 = hr4[1], r2 = hr4[2], r3 = hr4[3];
+  // H[i][j] = h_res[t, i, j]
+  const float H[4][4] = {{r0.x, r0.y, r0.z, r0.w}, {r1.x, r1.y, r1.z, r1.w}, {r2.x, r2.y, r2.z, r2.w},
+                         {r3.x, r3.y, r3.z, r3.w}};
+  const float4 hp4 = *reinterpret_cast<const float4*>(h_pre + tl * 4);
+  const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w};
+  const float gx = g2[tl];
+  float x[BS][8], d[BS][8], f[8];
+#pragma unroll
+  for (int i = 0; i < BS; ++i) {
+    unpack_bf8(xq[i], x[i]);
+    unpack_bf8(dq[i], d[i]);
+  }
+  unpack_bf8(fq, f);
+#pragma unroll
+  for (int j = 0; j < BS; ++j) {
+    const float4* pj = reinterpret_cast<const float4*>(prj + (j * XT + m) * PRJ + c8);
+    const float4 p0 = pj[0], p1 = pj[1];
+    const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o[e] = H[0][j] * d[0][e] + H[1][j] * d[1][e] + H[2][j] * d[2][e] + H[3][j] * d[3][e] + hp[j] * f[e] + p[e] +
+             gx * x[j][e];
+    if (ok)
+      __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                       pack_bf2_hw(o[6], o[7])},
+                                  reinterpret_cast<u4_t*>(dX + (t * BS + j) * C + c));
+  }
+}
+
+// ----------------------------------------------------------------- dphi
+
+constexpr int FT = 32;          // tokens per tile
+constexpr int FCH = 128;        // channels per chunk
+constexpr int FROW = FCH * 2;   // bytes per (stream, token) row of the state tile
+constexpr int DPT = FT + 8;     // bfloat16 per column of the transposed dP tile (80 bytes)
+
+// Byte offset of (stream i, token m, channel c) in the state tile. The 16-byte
+// block c >> 3 of a row sits at block (c >> 3) ^ (((m >> 3) & 3) << 1): the
+// A-fragment reads (16 consecutive channels of tokens m, m + 8, m + 16, m + 24)
+// then fall in distinct banks.
+__device__ __forceinline__ int xoff(int i, int m, int c) {
+  return (i * FT + m) * FROW + (((c >> 3) ^ (((m >> 3) & 3) << 1)) << 4) + (c & 7) * 2;
+}
+
+// Partial dphi of a chunk of 128 channels x 4 streams over the token tiles g,
+// g + G, ... (g = blockIdx.y, G = gridDim.y <= the tile count):
+//   part[g][i*C + c][k] = sum_t x[t, i, c] dP[t, k]   (k < 24)
+// on MFMA with the tokens as K: A = x^T (lane: one channel, 8 tokens, read from
+// the LDS state tile one element at a time), B = dP (lane: one column, 8 tokens,
+// from the transposed hi/lo tile in LDS), D += A B_hi + A B_lo. Wave w owns
+// stream w >> 1, channel blocks (w & 1) * 4 .. + 3 and both 16-column blocks;
+// its accumulators stay in registers over the workgroup's tiles. The next
+// tile's state and dP are loaded while the MFMAs of the current one run.
+__global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restrict__ X, const float* __restrict__ dP,
+                                                       int64_t T, int64_t C, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char xt[BS * FT * FROW];
+  __shared__ __attribute__((aligned(16))) uint16_t dpt[2 * DPS * DPT];  // [hi | lo][column][token]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t chunk = blockIdx.x;
+  const int grp = blockIdx.y, G = gridDim.y;
+  const int64_t ntile = (T + FT - 1) / FT;
+  const int m = tid >> 4, c8 = (tid & 15) * 8;
+  const int64_t c = chunk * FCH + c8;
+  const bool cok = c < C;
+  const int64_t cl = cok ? c : C - 8;
+  // dP staging: threads tid < 256 take token tid >> 3, columns (tid & 7) * 4 .. + 3
+  const int pm = (tid & 255) >> 3, pc = (tid & 7) * 4;
+  const int si = wave >> 1, cb0 = (wave & 1) * 4;
+  const int tau = lane & 15, q = lane >> 4;
+
+  f4_t acc[4][2];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[cb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 xq[BS];
+  float4 pv;
+  auto load_tile = [&](int64_t tl) __attribute__((always_inline)) {
+    const int64_t t = tl * FT + m;
+    const bool ok = t < T && cok;
+    const int64_t tc = t < T ? t : T - 1;
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      const uint4 v = ld_nt16(X + (tc * BS + i) * C + cl);
+      xq[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+    const int64_t t2 = tl * FT + pm;
+    const float4 w = *reinterpret_cast<const float4*>(dP + (t2 < T ? t2 : T - 1) * DPS + pc);
+    pv = t2 < T ? w : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  int64_t tl = grp;
+  load_tile(tl);
+  for (; tl < ntile; tl += G) {
+#pragma unroll
+    for (int i = 0; i < BS; ++i) *reinterpret_cast<uint4*>(xt + xoff(i, m, c8)) = xq[i];
+    if (tid < 256) {
+      const float v[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t h = f2bf(v[k]);
+        const uint32_t l = f2bf(v[k] - bf2f(h));
+        dpt[(pc + k) * DPT + pm] = (uint16_t)h;
+        dpt[(DPS + pc + k) * DPT + pm] = (uint16_t)l;
+      }
+    }
+    __syncthreads();
+    if (tl + G < ntile) load_tile(tl + G);
+    uint4 bh[2], bl[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      bh[nb] = *reinterpret_cast<const uint4*>(dpt + (nb * 16 + tau) * DPT + q * 8);
+      bl[nb] = *reinterpret_cast<const uint4*>(dpt + (DPS + nb * 16 + tau) * DPT + q * 8);
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int chl = (cb0 + cb) * 16 + tau;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(xt + xoff(si, q * 8 + 2 * k, chl));
+        const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(xt + xoff(si, q * 8 + 2 * k + 1, chl));
+        w[k] = lo16 | (hi16 << 16);
+      }
+      const uint4 a = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(a), bf8(bh[nb]), acc[cb][nb], 0, 0, 0);
+        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(a), bf8(bl[nb]), acc[cb][nb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  float* out = part + (int64_t)grp * BS * C * BCOL;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ch = chunk * FCH + (cb0 + cb) * 16 + q * 4 + e;
+        const int col = nb * 16 + tau;
+        if (ch < C && col < BCOL) out[((int64_t)si * C + ch) * BCOL + col] = acc[cb][nb][e];
+      }
+}
+
+// dphi = the G group partials added in group order; one thread per entry.
+__global__ __launch_bounds__(256) void sum_groups_kernel(const float* __restrict__ part, int64_t n, int G,
+                                                         float* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < G; ++k) s += part[(int64_t)k * n + g];
+  out[g] = s;
+}
+
+// Column k of the per-token sums [T][28] added over the tokens: dbias[k] for
+// k < 24, dalpha[k - 24] for k = 24, 25, 26. One workgroup per column; each
+// thread adds the tokens tid, tid + 256, ... in order, then a tree in LDS.
+__global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ red, int64_t T,
+                                                      float* __restrict__ dbias, float* __restrict__ dalpha) {
+  __shared__ float s[256];
+  const int k = blockIdx.x, tid = threadIdx.x;
+  float v = 0.f;
+  for (int64_t t = tid; t < T; t += 256) v += red[t * RED + k];
+  s[tid] = v;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (tid < h) s[tid] += s[tid + h];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (k < BCOL) dbias[k] = s[0];
+    else dalpha[k - BCOL] = s[0];
+  }
+}
+
+int ncu_of_device() {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+    ncu = 256;
+  return ncu;
+}
+
+int64_t al256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// token groups of the dphi pass: about two workgroups per CU, at most the tile count
+int dphi_groups(int64_t T, int64_t C) {
+  const int64_t nchunk = (C + FCH - 1) / FCH, ntile = (T + FT - 1) / FT;
+  int64_t g = (2 * (int64_t)ncu_of_device() + nchunk - 1) / nchunk;
+  g = g < 1 ? 1 : g;
+  return (int)(g < ntile ? g : ntile);
+}
+
+struct BwdWs {
+  void* packed;
+  float* partial;
+  uint4* phi_rows;
+  float *h_pre, *h_post, *h_res, *dh, *dP, *g2, *red, *dphi_part;
+  int G;
+};
+
+// Workspace pieces in order; each 256-byte aligned.
+BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
+  BwdWs w{};
+  unsigned char* p = (unsigned char*)ws;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    unsigned char* q = p ? p + off : nullptr;
+    off += al256(bytes);
+    return q;
+  };
+  w.packed = take(fast_coeffs_packed_bytes(4, C, 1));
+  w.partial = (float*)take(fast_coeffs_partial_bytes(T, 4, C, 1));
+  w.phi_rows = (uint4*)take(BS * C * 128);
+  w.h_pre = (float*)take(T * 4 * 4);
+  w.h_post = (float*)take(T * 4 * 4);
+  w.h_res = (float*)take(T * 16 * 4);
+  w.dh = (float*)take(T * BCOL * 4);
+  w.dP = (float*)take(T * DPS * 4);
+  w.g2 = (float*)take(T * 4);
+  w.red = (float*)take(T * RED * 4);
+  w.G = dphi_groups(T, C);
+  w.dphi_part = (float*)take((int64_t)w.G * BS * C * BCOL * 4);
+  if (total) *total = off;
+  return w;
+}
+
+}  // namespace
+
+bool fast_backward_supported(int dtype, int n, int64_t T, int64_t C, int iters) {
+  return dtype == 1 && n == 4 && T >= 1 && iters >= 1 && iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 &&
+         fast_coeffs_partial_bytes(T, 4, C, 1) > 0 && (C + FCH - 1) / FCH <= 65535 && (T + XT - 1) / XT <= 65535;
+}
+
+int64_t fast_backward_ws_bytes(int64_t T, int64_t C) {
+  int64_t total = 0;
+  carve(nullptr, T, C, &total);
+  return total;
+}
+
+hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float* phi, const float* bias,
+                                float a_pre, float a_post, float a_res, int iters, const void* F_out,
+                                const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi,
+                                float* dbias, float* dalpha, void* ws, hipStream_t st) {
+  const BwdWs w = carve(ws, T, C, nullptr);
+  const uint16_t* x = (const uint16_t*)X;
+  hipError_t e = launch_fast_coeffs_pre(X, T, C, phi, bias, a_pre, a_post, a_res, iters, w.h_pre, w.h_post,
+                                        w.h_res, nullptr, w.packed, w.partial, st);
+  if (e != hipSuccess) return e;
+  const int64_t R = BS * C;
+  hipLaunchKernelGGL(pack_phi_rows_kernel, dim3((unsigned)((R * 4 + 255) / 256)), dim3(256), 0, st, phi, R,
+                     w.phi_rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dX_next,
+                     (const uint16_t*)F_out, (const uint16_t*)dF_in, C, w.h_post, w.dh, (uint16_t*)dF_out);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, w.dh, w.dP, w.g2, w.red,
+                                  st)) != hipSuccess)
+    return e;
+  const unsigned nchunk_x = (unsigned)((C + XCH - 1) / XCH), ntile_x = (unsigned)((T + XT - 1) / XT);
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(nchunk_x, ntile_x), dim3(512), 0, st, x, (const uint16_t*)dX_next,
+                     (const uint16_t*)dF_in, T, C, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dphi_kernel, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st, x,
+                     w.dP, T, C, w.dphi_part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nphi = R * BCOL;
+  hipLaunchKernelGGL(sum_groups_kernel, dim3((unsigned)((nphi + 255) / 256)), dim3(256), 0, st, w.dphi_part, nphi,
+                     w.G, dphi);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(col_sum_kernel, dim3(BCOL + 3), dim3(256), 0, st, w.red, T, dbias, dalpha);
+  return hipGetLastError();
+}
+
+}  // namespace hc

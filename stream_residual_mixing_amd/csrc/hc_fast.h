@@ -35,6 +35,22 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
 
 bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y);
 
+// mHC sublayer backward for n = 4 bfloat16 streams (hc_backward.hip): shapes it
+// covers, its workspace, and the launch sequence (all device pointers; X, F_out,
+// dX_next, dF_in, dX, dF_out 16-byte aligned).
+bool fast_backward_supported(int dtype, int n, int64_t T, int64_t C, int iters);
+int64_t fast_backward_ws_bytes(int64_t T, int64_t C);
+hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float* phi, const float* bias,
+                                float a_pre, float a_post, float a_res, int iters, const void* F_out,
+                                const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi,
+                                float* dbias, float* dalpha, void* ws, hipStream_t st);
+// Gates' and Sinkhorn's backward from the projection partials of
+// launch_fast_coeffs_pre (hc_fused.hip): dh [T, 24] in, dP [T, 32], g2 [T] and the
+// per-token sums red [T, 28] out; dynamic LDS of iters * 1 KB (iters <= 64).
+hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
+                                  float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
+                                  float* red, hipStream_t st);
+
 // xHC fast paths (bfloat16 streams, C % 32 == 0). Workspace needs of each (all zero
 // when the shape has no fast path): the packed phi and the per-item partials.
 struct XhcFastWs {

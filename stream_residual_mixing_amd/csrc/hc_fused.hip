@@ -895,6 +895,121 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
                    h_res_out);
 }
 
+// ------------------------------------------------- mHC coefficient backward
+
+// Backward of Eq. 15-19 for token tt, 16 lanes per token as in token_coeffs
+// (lane e: h_res entry e = i*4 + j; lanes e < 8 also gate column e: pre for
+// e < 4, post for 4 <= e < 8). The logits are recomputed from the partials with
+// token_coeffs' arithmetic, so they are the forward's floats. Sinkhorn-Knopp
+// is run forward again with each iterate M_k (before its column step) kept in
+// LDS (`it_lds`, iters x 256 floats), then walked in reverse: for an iterate,
+// A = T_c(M_k) and B = T_r(A) are recomputed from M_k and the gradient goes
+// through T_r (g = (g - rowsum(g B)) / q) and then T_c (g = (g - colsum(g A)) /
+// s); the logit gradient is g M_0 (the max subtracted before exp is a common
+// factor, which Sinkhorn's output does not depend on). Gates: dz = dh s (1 - s)
+// (pre) and 2 dh s (1 - s) (post) with s = sigmoid(z). Then with rho = 1/r:
+// dP = alpha dz rho, d rho = sum alpha dz P, and the factor of vec x in its
+// gradient, 2 dss = -d rho rho^3 / (4C) (0 for the all-zero state).
+// Outputs per token: dP [32] (columns 24..31 zero: the A operand of the dx
+// product), g2 (= 2 dss), and red [28] = dz [24] | sum over each gate of
+// dz P rho [3] | 0, which are summed over tokens for db and dalpha.
+template <int TT>
+__global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
+                                                        const float* __restrict__ bias, Gate gate, int iters,
+                                                        const float* __restrict__ dh, float* __restrict__ dP,
+                                                        float* __restrict__ g2, float* __restrict__ red) {
+  extern __shared__ float it_lds[];  // [iters][256]
+  using PG = PartGeom<3, TT>;
+  const int tid = threadIdx.x;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
+  const int64_t tt = g >> 4;
+  const int e = (int)(g & 15);
+  const bool valid = tt < T;
+  const int64_t tc = valid ? tt : T - 1;
+  const int64_t tile = tc / TT;
+  const int m = (int)(tc - tile * TT);
+  const float* base = part + tile * S * PG::PART + m * PG::PROW;
+  float ss = 0.f, pr = 0.f, pe = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const float* b = base + (int64_t)s * PG::PART;
+    ss += b[PG::NCOLP];
+    pr += b[8 + e];
+    pe += b[e & 7];
+  }
+  const float invr = inv_rms4(ss, C);
+  const float a = e < 4 ? gate.a_pre : gate.a_post;
+  const float sg = sigmoid(gate_logit(a, pe, invr, bias[e & 7]));
+  const float z = gate_logit(gate.a_res, pr, invr, bias[8 + e]);
+  float zm = fmaxf(z, dpp<DPP_QXOR1>(z));
+  zm = fmaxf(zm, dpp<DPP_QXOR2>(zm));
+  zm = fmaxf(zm, dpp<DPP_ROR4>(zm));
+  zm = fmaxf(zm, dpp<DPP_ROR8>(zm));
+  const float M0 = expf(z - zm);
+  float M = M0;
+  for (int it = 0; it < iters; ++it) {
+    it_lds[it * 256 + tid] = M;
+    float cs = M + dpp<DPP_ROR8>(M);
+    cs += dpp<DPP_ROR4>(cs);
+    M = M / cs;
+    float rs = M + dpp<DPP_QXOR1>(M);
+    rs += dpp<DPP_QXOR2>(rs);
+    M = M / rs;
+  }
+  // each lane reads back only the iterates it wrote: no barrier needed
+  float G = dh[tc * 24 + 8 + e];
+  for (int it = iters - 1; it >= 0; --it) {
+    const float Mk = it_lds[it * 256 + tid];
+    float cs = Mk + dpp<DPP_ROR8>(Mk);
+    cs += dpp<DPP_ROR4>(cs);
+    const float A = Mk / cs;
+    float rs = A + dpp<DPP_QXOR1>(A);
+    rs += dpp<DPP_QXOR2>(rs);
+    const float B = A / rs;
+    float u = G * B;  // through T_r: the row sum of G B
+    u += dpp<DPP_QXOR1>(u);
+    u += dpp<DPP_QXOR2>(u);
+    G = (G - u) / rs;
+    float v = G * A;  // through T_c: the column sum of G A
+    v += dpp<DPP_ROR8>(v);
+    v += dpp<DPP_ROR4>(v);
+    G = (G - v) / cs;
+  }
+  const float dz_res = G * M0;
+  float dz_pp = 0.f;
+  if (e < 8) {
+    const float d = dh[tc * 24 + e];
+    dz_pp = (e < 4 ? d : 2.0f * d) * sg * (1.0f - sg);
+  }
+  // sums over the 16 lanes: quads, then the four quads (every lane gets the total)
+  auto row16 = [](float x) __attribute__((always_inline)) {
+    x += dpp<DPP_QXOR1>(x);
+    x += dpp<DPP_QXOR2>(x);
+    x += dpp<DPP_ROR8>(x);
+    x += dpp<DPP_ROR4>(x);
+    return x;
+  };
+  const float drho = row16(gate.a_res * dz_res * pr + (e < 8 ? a * dz_pp * pe : 0.f));
+  const float u_pre = row16(e < 4 ? dz_pp * pe * invr : 0.f);
+  const float u_post = row16(e >= 4 && e < 8 ? dz_pp * pe * invr : 0.f);
+  const float u_res = row16(dz_res * pr * invr);
+  if (!valid) return;
+  dP[tt * 32 + 8 + e] = gate.a_res * dz_res * invr;
+  red[tt * 28 + 8 + e] = dz_res;
+  if (e < 8) {
+    dP[tt * 32 + e] = a * dz_pp * invr;
+    dP[tt * 32 + 24 + e] = 0.f;
+    red[tt * 28 + e] = dz_pp;
+  }
+  if (e == 0) {
+    red[tt * 28 + 24] = u_pre;
+    red[tt * 28 + 25] = u_post;
+    red[tt * 28 + 26] = u_res;
+    red[tt * 28 + 27] = 0.f;
+    g2[tt] = -drho * invr * invr * invr / (float)(NS4 * C);
+  }
+}
+
 // ------------------------------------------------------- xHC finish kernels
 
 // xHC full-state pass ([xHC] steps 1 and 2, parameterisation): 32 lanes per
@@ -1416,6 +1531,16 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
 
 hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream_t st) {
   return launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st);
+}
+
+hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
+                                  float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
+                                  float* red, hipStream_t st) {
+  const int64_t threads = T * 16;
+  hipLaunchKernelGGL(bwd_coeff_kernel<W_TOK>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), bias,
+                     Gate{a_pre, a_post, a_res}, iters, dh, dP, g2, red);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ xHC

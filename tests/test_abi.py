@@ -228,3 +228,37 @@ def test_workspace_queries(hc):
     assert L.xhc_pre_workspace_bytes(8, 16, 64, 2, 1, 1) > L.xhc_pre_workspace_bytes(8, 16, 64, 2, 0, 1)
     assert L.xhc_route_workspace_bytes(8, 16, 64, 4, 2, 4, 1, 1) > 0
     assert L.xhc_route_workspace_bytes(8, 16, 64, 4, 2, 9, 1, 1) == -1
+
+
+def test_backward_validation(hc):
+    L = hc.lib()
+    T, C = 8, 64
+    wsb = L.hc_backward_workspace_bytes(T, 4, C, 1)
+    assert wsb > 0
+    assert L.hc_backward_workspace_bytes(0, 4, C, 1) == 0
+    assert L.hc_backward_workspace_bytes(T, 3, C, 1) == -1
+    assert L.hc_backward_workspace_bytes(T, 4, 48, 1) == -1
+    assert L.hc_backward_workspace_bytes(T, 4, C, 0) == -1
+    assert L.hc_backward_workspace_bytes(-1, 4, C, 1) == -1
+    P = lambda k: ctypes.c_void_p(0x1000000 * (k + 1))  # distinct, far apart, 256-byte aligned
+    names = ["X", "phi", "bias", "Fo", "dXn", "dFi", "dX", "dFo", "dphi", "dbias", "dalpha", "ws"]
+
+    def bwd(dt=1, T=T, n=4, C=C, iters=20, wsb=wsb, **kw):
+        p = {nm: kw.get(nm, P(k)) for k, nm in enumerate(names)}
+        return L.hc_backward(p["X"], dt, T, n, C, p["phi"], p["bias"], 0.01, 0.01, 0.01, iters, p["Fo"],
+                             p["dXn"], p["dFi"], p["dX"], p["dFo"], p["dphi"], p["dbias"], p["dalpha"], p["ws"],
+                             wsb, None)
+    assert bwd(dt=7) == -3 and bwd(dt=0) == -3
+    assert bwd(n=3) == -2 and bwd(C=48) == -2 and bwd(C=0) == -2 and bwd(T=-1) == -2
+    assert bwd(iters=0) == -2 and bwd(iters=65) == -2
+    assert bwd(T=0, X=None, dX=None) == 0
+    for nm in names[:-1]:
+        assert bwd(**{nm: None}) == -1, nm
+    assert bwd(X=ctypes.c_void_p(0x1000008)) == -4
+    assert bwd(dX=ctypes.c_void_p(0x7000004)) == -4
+    assert bwd(dphi=ctypes.c_void_p(0x9000002)) == -4
+    assert bwd(ws=None) == -8 and bwd(wsb=wsb - 1) == -8 and bwd(ws=ctypes.c_void_p(0xc000010)) == -8
+    assert bwd(dX=ctypes.c_void_p(0x5000000)) == -5  # dX over dX_next
+    assert bwd(dFo=ctypes.c_void_p(0x4000000)) == -5  # dF_out over F_out
+    assert bwd(dbias=ctypes.c_void_p(0x9000010)) == -5  # dbias inside dphi
+    assert bwd(ws=ctypes.c_void_p(0x7000000)) == -5  # workspace over dX
