@@ -145,6 +145,55 @@ def hc_baseline_bench(torch, hc, dev, reps: int = 20) -> dict:
                              "algorithmic_bytes": gain_bytes, "achieved_GBps": gain_bytes / t_gain / 1e9}}
 
 
+def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
+    """The mHC sublayer backward (hc_backward, n=4 C=4096 T=8192 bf16) on three
+    rotating sets of state and upstream gradients; HIP events around the repeated
+    calls. algorithmic_bytes is the one-pass minimum per call (read X, F_out,
+    dX_next, dF_in; write dX, dF_out; phi read and dphi written once); pass_bytes
+    is what this kernel sequence moves by design (the state read by the
+    projection, the channel sums, the dX pass and the dphi pass; dX_next and dF_in
+    by the sums and the dX pass)."""
+    T, n, C = 8192, 4, 4096
+    g = torch.Generator(device=dev)
+    g.manual_seed(5000)
+    rn = lambda *shape, std=1.0: torch.randn(*shape, device=dev, generator=g) * std
+    Xs = [rn(T, n, C).to(torch.bfloat16) for _ in range(3)]
+    dXs = [rn(T, n, C).to(torch.bfloat16) for _ in range(3)]
+    Fs = [rn(T, C).to(torch.bfloat16) for _ in range(3)]
+    dFs = [rn(T, C).to(torch.bfloat16) for _ in range(3)]
+    phi = rn(n * C, n * n + 2 * n, std=0.02)
+    bias = torch.zeros(n * n + 2 * n, device=dev)
+    bias[2 * n:] = torch.eye(n, device=dev).flatten()
+    out = (torch.empty(T, n, C, dtype=torch.bfloat16, device=dev), torch.empty(T, C, dtype=torch.bfloat16, device=dev),
+           torch.empty(n * C, n * n + 2 * n, device=dev), torch.empty(n * n + 2 * n, device=dev),
+           torch.empty(3, device=dev))
+    ws = torch.empty(hc.hc_backward_workspace_bytes(T, n, C, torch.bfloat16), dtype=torch.uint8, device=dev)
+    fn = lambda i: hc.hc_backward(Xs[i % 3], phi, bias, (0.01, 0.01, 0.01), Fs[i % 3], dXs[i % 3], dFs[i % 3],
+                                  SINKHORN_ITERS, out=out, workspace=ws)
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    times = []
+    for r in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(r)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    s = n * C * 2
+    phi_b = n * C * (n * n + 2 * n) * 4
+    alg = T * (3 * s + 3 * C * 2) + 2 * phi_b
+    f = C * 2
+    # X 4 reads, dX_next 2, dF_in 2, F_out 1; dX and dF_out written once
+    pas = T * (4 * s + 2 * s + 2 * f + f + s + f) + 2 * phi_b
+    return {"workload": "mHC backward n=4 C=4096 T=8192 bf16 (20 Sinkhorn iterations recomputed)",
+            "median_us": t * 1e6, "tokens_per_s": T / t, "algorithmic_bytes": alg,
+            "achieved_GBps": alg / t / 1e9, "pct_hbm_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
+            "pass_bytes": pas, "pass_GBps": pas / t / 1e9}
+
+
 def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     """Throughput of the xHC sublayer (N=16, k=4, m=2, C=4096, T=8192, bf16) on
     seeded synthetic device data: the routed step xhc_pre + xhc_route (K=1, F_out
@@ -509,6 +558,7 @@ def main() -> int:
     if not args.no_xhc:
         result["xhc"] = xhc_bench(torch, hc, dev, max(3, min(args.steps, 20)), 3)
         result["hc_baseline"] = hc_baseline_bench(torch, hc, dev)
+        result["backward"] = backward_bench(torch, hc, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

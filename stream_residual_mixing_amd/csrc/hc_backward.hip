@@ -11,7 +11,8 @@
 //  2. bwd_reduce_kernel: per token dh = [dH_pre | dH_post | dH_res] (sums over
 //     the channels) and dF_out = H_post dX_next;
 //  3. bwd_coeff_kernel (hc_fused.hip, beside the forward finish whose floats it
-//     recomputes): gates and Sinkhorn backward -> dP, g2, per-token sums;
+//     recomputes): gates and Sinkhorn backward -> dP, g2, sums over groups of
+//     16 tokens;
 //  4. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
 //     dP phi^T product on MFMA;
 //  5. bwd_dphi_kernel: vec(x)^T dP over groups of token tiles on MFMA (the
@@ -158,96 +159,142 @@ constexpr int XT = 32;        // tokens per item
 constexpr int XCH = 128;      // channels per item
 constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product tile in LDS
 
-// dX of an item of 32 tokens x 128 channels x 4 streams (512 threads).
-// The streaming loads of thread (token tid >> 4, channels (tid & 15) * 8) are
-// issued first. MFMA phase: wave w forms dP phi^T for stream w >> 1, the four
-// 16-channel blocks (w & 1) * 4 .. + 3 and both 16-token blocks
-// (v_mfma_f32_16x16x32_bf16; A = the tokens' dP rows split hi/lo, B = the
-// channels' phi rows hi/lo; hi*hi + hi*lo + lo*hi into one float32
-// accumulator), and puts the tile in LDS. Then each thread forms, for its
-// token and channels,
-//   dX_j = sum_i H_res[i, j] dX_next_i + H_pre[j] dF_in + (dP phi^T)_j + g2 x_j
-// and stores it rounded once to bfloat16. Rows past T and channels past C are
-// computed on clamped addresses and not stored.
+// dX over items of 32 tokens x 128 channels x 4 streams, 512 threads. The grid
+// is (chunk, group): workgroup (c, j) keeps the channel chunk c and walks the
+// token tiles j, j + J, ... (J = gridDim.y), so its phi fragments load once.
+// Everything a tile needs from memory is loaded one tile ahead into a second
+// register set: thread (token tid >> 4, channels (tid & 15) * 8) takes its
+// 16-byte pieces of x and dX_next in the 4 streams and of dF_in; threads
+// tid < 192 one 16-byte piece of the tile's coefficients [h_res 16 | h_pre 4 |
+// g2 | 0 0 0] and threads tid < 256 one of its dP rows, both staged in LDS at
+// the start of the tile. Per tile:
+//  * MFMA phase: wave w forms dP phi^T for stream w >> 1, the four 16-channel
+//    blocks (w & 1) * 4 .. + 3 and both 16-token blocks
+//    (v_mfma_f32_16x16x32_bf16; A = the tokens' dP rows split hi/lo, B = the
+//    channels' phi rows hi/lo; hi*hi + hi*lo + lo*hi into one float32
+//    accumulator) into the LDS product tile; then the next tile's loads are
+//    issued;
+//  * streaming phase: dX_j = sum_i H_res[i, j] dX_next_i + H_pre[j] dF_in +
+//    (dP phi^T)_j + g2 x_j, rounded once to bfloat16 and stored.
+// Rows past T and channels past C are computed on clamped addresses and not
+// stored.
+constexpr int CFR = 24;  // floats per token of the staged coefficients
+constexpr int DPR = 36;  // floats per token row of the staged dP tile (padded)
+
 __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dXn,
                                                      const uint16_t* __restrict__ dFi, int64_t T, int64_t C,
                                                      const float* __restrict__ h_pre, const float* __restrict__ h_res,
                                                      const float* __restrict__ dP, const float* __restrict__ g2,
                                                      const uint4* __restrict__ phi_rows, uint16_t* __restrict__ dX) {
   __shared__ __attribute__((aligned(16))) float prj[BS * XT * PRJ];
+  __shared__ __attribute__((aligned(16))) float cf[XT * CFR];
+  __shared__ __attribute__((aligned(16))) float dpt[XT * DPR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t chunk = blockIdx.x, tile = blockIdx.y;
+  const int64_t chunk = blockIdx.x;
+  const int64_t J = gridDim.y, ntile = (T + XT - 1) / XT;
   const int m = tid >> 4, c8 = (tid & 15) * 8;
-  const int64_t t = tile * XT + m, c = chunk * XCH + c8;
-  const bool ok = t < T && c < C;
-  const int64_t tl = t < T ? t : T - 1, cl = c < C ? c : C - 8;
-  uint4 xq[BS], dq[BS];
-#pragma unroll
-  for (int i = 0; i < BS; ++i) {
-    xq[i] = ld_nt16(X + (tl * BS + i) * C + cl);
-    dq[i] = ld_nt16(dXn + (tl * BS + i) * C + cl);
-  }
-  const uint4 fq = ld_nt16(dFi + tl * C + cl);
-
+  const int64_t c = chunk * XCH + c8;
+  const bool cok = c < C;
+  const int64_t cl = cok ? c : C - 8;
   const int si = wave >> 1, cb0 = (wave & 1) * 4;
   const int tau = lane & 15, q = lane >> 4;
-  uint4 ah[2], al[2];
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    int64_t tok = tile * XT + tb * 16 + tau;
-    tok = tok < T ? tok : T - 1;
-    const float4* pp = reinterpret_cast<const float4*>(dP + tok * DPS + q * 8);
-    const float4 p0 = pp[0], p1 = pp[1];
-    const float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    split_bf8(v, ah[tb], al[tb]);
-  }
+  // staging roles: coefficient piece (token tid / 6, piece tid % 6), dP piece
+  // (token (tid & 255) >> 3, piece tid & 7)
+  const int ctok = tid < 192 ? tid / 6 : 0, cpc = tid < 192 ? tid - 6 * ctok : 0;
+  const int dtok = (tid & 255) >> 3, dpc = tid & 7;
+
+  uint4 bh[4], bl[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     int64_t ch = chunk * XCH + (cb0 + cb) * 16 + tau;
     ch = ch < C ? ch : C - 1;
     const uint4* pr = phi_rows + ((int64_t)si * C + ch) * 8;
-    const uint4 bh = pr[q], bl = pr[4 + q];
+    bh[cb] = pr[q];
+    bl[cb] = pr[4 + q];
+  }
+
+  struct In {
+    uint4 xq[BS], dq[BS], fq;
+    float4 cv, dv;
+  };
+  auto load = [&](int64_t tl, In& in) __attribute__((always_inline)) {
+    const int64_t t = tl * XT + m;
+    const int64_t tc = t < T ? t : T - 1;
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      in.xq[i] = ld_nt16(X + (tc * BS + i) * C + cl);
+      in.dq[i] = ld_nt16(dXn + (tc * BS + i) * C + cl);
+    }
+    in.fq = ld_nt16(dFi + tc * C + cl);
+    int64_t t1 = tl * XT + ctok;
+    t1 = t1 < T ? t1 : T - 1;
+    if (cpc < 4) in.cv = reinterpret_cast<const float4*>(h_res + t1 * 16)[cpc];
+    else if (cpc == 4) in.cv = *reinterpret_cast<const float4*>(h_pre + t1 * 4);
+    else in.cv = make_float4(g2[t1], 0.f, 0.f, 0.f);
+    int64_t t2 = tl * XT + dtok;
+    t2 = t2 < T ? t2 : T - 1;
+    in.dv = reinterpret_cast<const float4*>(dP + t2 * DPS)[dpc];
+  };
+  // one tile: returns false after the last
+  auto step = [&](int64_t& tl, In& cur, In& nxt) __attribute__((always_inline)) {
+    if (tid < 192) *reinterpret_cast<float4*>(cf + ctok * CFR + cpc * 4) = cur.cv;
+    if (tid < 256) *reinterpret_cast<float4*>(dpt + dtok * DPR + dpc * 4) = cur.dv;
+    __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      f4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah[tb]), bf8(bh), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah[tb]), bf8(bl), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(al[tb]), bf8(bh), acc, 0, 0, 0);
+      const float4* pa = reinterpret_cast<const float4*>(dpt + (tb * 16 + tau) * DPR + q * 8);
+      const float4 a0 = pa[0], a1 = pa[1];
+      const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      uint4 ah, al;
+      split_bf8(v, ah, al);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) prj[(si * XT + tb * 16 + q * 4 + e) * PRJ + (cb0 + cb) * 16 + tau] = acc[e];
+      for (int cb = 0; cb < 4; ++cb) {
+        f4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah), bf8(bh[cb]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah), bf8(bl[cb]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(al), bf8(bh[cb]), acc, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) prj[(si * XT + tb * 16 + q * 4 + e) * PRJ + (cb0 + cb) * 16 + tau] = acc[e];
+      }
     }
-  }
-  __syncthreads();
-
-  const float4* hr4 = reinterpret_cast<const float4*>(h_res + tl * 16);
-  const float4 r0 = hr4[0], r1 = hr4[1], r2 = hr4[2], r3 = hr4[3];
-  // H[i][j] = h_res[t, i, j]
-  const float H[4][4] = {{r0.x, r0.y, r0.z, r0.w}, {r1.x, r1.y, r1.z, r1.w}, {r2.x, r2.y, r2.z, r2.w},
-                         {r3.x, r3.y, r3.z, r3.w}};
-  const float4 hp4 = *reinterpret_cast<const float4*>(h_pre + tl * 4);
-  const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w};
-  const float gx = g2[tl];
-  float x[BS][8], d[BS][8], f[8];
+    const int64_t nt = tl + J;
+    if (nt < ntile) load(nt, nxt);
+    __syncthreads();
+    const float4* c4 = reinterpret_cast<const float4*>(cf + m * CFR);
+    const float4 r0 = c4[0], r1 = c4[1], r2 = c4[2], r3 = c4[3], hp4 = c4[4], g4 = c4[5];
+    const float H[4][4] = {{r0.x, r0.y, r0.z, r0.w}, {r1.x, r1.y, r1.z, r1.w}, {r2.x, r2.y, r2.z, r2.w},
+                           {r3.x, r3.y, r3.z, r3.w}};  // H[i][j] = h_res[t, i, j]
+    const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w};
+    float d[BS][8], f[8];
 #pragma unroll
-  for (int i = 0; i < BS; ++i) {
-    unpack_bf8(xq[i], x[i]);
-    unpack_bf8(dq[i], d[i]);
-  }
-  unpack_bf8(fq, f);
+    for (int i = 0; i < BS; ++i) unpack_bf8(cur.dq[i], d[i]);
+    unpack_bf8(cur.fq, f);
+    const int64_t t = tl * XT + m;
+    const bool ok = t < T && cok;
 #pragma unroll
-  for (int j = 0; j < BS; ++j) {
-    const float4* pj = reinterpret_cast<const float4*>(prj + (j * XT + m) * PRJ + c8);
-    const float4 p0 = pj[0], p1 = pj[1];
-    const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    float o[8];
+    for (int j = 0; j < BS; ++j) {
+      const float4* pj = reinterpret_cast<const float4*>(prj + (j * XT + m) * PRJ + c8);
+      const float4 p0 = pj[0], p1 = pj[1];
+      const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      float xj[8], o[8];
+      unpack_bf8(cur.xq[j], xj);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      o[e] = H[0][j] * d[0][e] + H[1][j] * d[1][e] + H[2][j] * d[2][e] + H[3][j] * d[3][e] + hp[j] * f[e] + p[e] +
-             gx * x[j][e];
-    if (ok)
-      __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
-                                       pack_bf2_hw(o[6], o[7])},
-                                  reinterpret_cast<u4_t*>(dX + (t * BS + j) * C + c));
+      for (int e = 0; e < 8; ++e)
+        o[e] = H[0][j] * d[0][e] + H[1][j] * d[1][e] + H[2][j] * d[2][e] + H[3][j] * d[3][e] + hp[j] * f[e] +
+               p[e] + g4.x * xj[e];
+      if (ok)
+        __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]),
+                                         pack_bf2_hw(o[4], o[5]), pack_bf2_hw(o[6], o[7])},
+                                    reinterpret_cast<u4_t*>(dX + (t * BS + j) * C + c));
+    }
+    __syncthreads();  // the LDS tiles are rewritten by the next tile
+    tl = nt;
+    return nt < ntile;
+  };
+  int64_t tl = blockIdx.y;
+  In a, b;
+  load(tl, a);
+  while (step(tl, a, b) && step(tl, b, a)) {
   }
 }
 
@@ -378,15 +425,16 @@ __global__ __launch_bounds__(256) void sum_groups_kernel(const float* __restrict
   out[g] = s;
 }
 
-// Column k of the per-token sums [T][28] added over the tokens: dbias[k] for
-// k < 24, dalpha[k - 24] for k = 24, 25, 26. One workgroup per column; each
-// thread adds the tokens tid, tid + 256, ... in order, then a tree in LDS.
-__global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ red, int64_t T,
+// Column k of the sums over groups of 16 tokens [nrow][28] added over the
+// groups: dbias[k] for k < 24, dalpha[k - 24] for k = 24, 25, 26. One workgroup
+// per column; each thread adds the rows tid, tid + 256, ... in order, then a
+// tree in LDS.
+__global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ red, int64_t nrow,
                                                       float* __restrict__ dbias, float* __restrict__ dalpha) {
   __shared__ float s[256];
   const int k = blockIdx.x, tid = threadIdx.x;
   float v = 0.f;
-  for (int64_t t = tid; t < T; t += 256) v += red[t * RED + k];
+  for (int64_t t = tid; t < nrow; t += 256) v += red[t * RED + k];
   s[tid] = v;
   __syncthreads();
   for (int h = 128; h > 0; h >>= 1) {
@@ -413,6 +461,15 @@ int64_t al256(int64_t b) { return (b + 255) / 256 * 256; }
 int dphi_groups(int64_t T, int64_t C) {
   const int64_t nchunk = (C + FCH - 1) / FCH, ntile = (T + FT - 1) / FT;
   int64_t g = (2 * (int64_t)ncu_of_device() + nchunk - 1) / nchunk;
+  g = g < 1 ? 1 : g;
+  return (int)(g < ntile ? g : ntile);
+}
+
+// token-tile groups of the dX pass: about one workgroup per CU over the chunks,
+// at most the tile count
+int dx_groups(int64_t T, int64_t C) {
+  const int64_t nchunk = (C + XCH - 1) / XCH, ntile = (T + XT - 1) / XT;
+  int64_t g = (int64_t)ncu_of_device() / nchunk;
   g = g < 1 ? 1 : g;
   return (int)(g < ntile ? g : ntile);
 }
@@ -444,7 +501,7 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
   w.dh = (float*)take(T * BCOL * 4);
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
-  w.red = (float*)take(T * RED * 4);
+  w.red = (float*)take((T + 15) / 16 * RED * 4);
   w.G = dphi_groups(T, C);
   w.dphi_part = (float*)take((int64_t)w.G * BS * C * BCOL * 4);
   if (total) *total = off;
@@ -455,7 +512,7 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
 
 bool fast_backward_supported(int dtype, int n, int64_t T, int64_t C, int iters) {
   return dtype == 1 && n == 4 && T >= 1 && iters >= 1 && iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 &&
-         fast_coeffs_partial_bytes(T, 4, C, 1) > 0 && (C + FCH - 1) / FCH <= 65535 && (T + XT - 1) / XT <= 65535;
+         fast_coeffs_partial_bytes(T, 4, C, 1) > 0 && (C + FCH - 1) / FCH <= 65535;
 }
 
 int64_t fast_backward_ws_bytes(int64_t T, int64_t C) {
@@ -483,8 +540,8 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
   if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, w.dh, w.dP, w.g2, w.red,
                                   st)) != hipSuccess)
     return e;
-  const unsigned nchunk_x = (unsigned)((C + XCH - 1) / XCH), ntile_x = (unsigned)((T + XT - 1) / XT);
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3(nchunk_x, ntile_x), dim3(512), 0, st, x, (const uint16_t*)dX_next,
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)), dim3(512), 0,
+                     st, x, (const uint16_t*)dX_next,
                      (const uint16_t*)dF_in, T, C, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dphi_kernel, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st, x,
@@ -494,7 +551,7 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
   hipLaunchKernelGGL(sum_groups_kernel, dim3((unsigned)((nphi + 255) / 256)), dim3(256), 0, st, w.dphi_part, nphi,
                      w.G, dphi);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(col_sum_kernel, dim3(BCOL + 3), dim3(256), 0, st, w.red, T, dbias, dalpha);
+  hipLaunchKernelGGL(col_sum_kernel, dim3(BCOL + 3), dim3(256), 0, st, w.red, (T + 15) / 16, dbias, dalpha);
   return hipGetLastError();
 }
 

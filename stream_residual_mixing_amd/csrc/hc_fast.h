@@ -46,7 +46,8 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
                                 float* dbias, float* dalpha, void* ws, hipStream_t st);
 // Gates' and Sinkhorn's backward from the projection partials of
 // launch_fast_coeffs_pre (hc_fused.hip): dh [T, 24] in, dP [T, 32], g2 [T] and the
-// per-token sums red [T, 28] out; dynamic LDS of iters * 1 KB (iters <= 64).
+// sums red [ceil(T / 16), 28] over groups of 16 tokens out; dynamic LDS of
+// iters * 1 KB (iters <= 64).
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                   float* red, hipStream_t st);

@@ -911,8 +911,9 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
 // dP = alpha dz rho, d rho = sum alpha dz P, and the factor of vec x in its
 // gradient, 2 dss = -d rho rho^3 / (4C) (0 for the all-zero state).
 // Outputs per token: dP [32] (columns 24..31 zero: the A operand of the dx
-// product), g2 (= 2 dss), and red [28] = dz [24] | sum over each gate of
-// dz P rho [3] | 0, which are summed over tokens for db and dalpha.
+// product) and g2 (= 2 dss); per workgroup of 16 tokens, red [28] = the sums
+// over its tokens of dz [24] | dz P rho over each gate [3] | 0, which are then
+// added over the workgroups for db and dalpha.
 template <int TT>
 __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
                                                         const float* __restrict__ bias, Gate gate, int iters,
@@ -959,21 +960,24 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   // each lane reads back only the iterates it wrote: no barrier needed
   float G = dh[tc * 24 + 8 + e];
   for (int it = iters - 1; it >= 0; --it) {
+    // (the reverse walk divides by one reciprocal per sum, v_rcp_f32 to 1 ulp)
     const float Mk = it_lds[it * 256 + tid];
     float cs = Mk + dpp<DPP_ROR8>(Mk);
     cs += dpp<DPP_ROR4>(cs);
-    const float A = Mk / cs;
+    const float rcs = __builtin_amdgcn_rcpf(cs);
+    const float A = Mk * rcs;
     float rs = A + dpp<DPP_QXOR1>(A);
     rs += dpp<DPP_QXOR2>(rs);
-    const float B = A / rs;
+    const float rrs = __builtin_amdgcn_rcpf(rs);
+    const float B = A * rrs;
     float u = G * B;  // through T_r: the row sum of G B
     u += dpp<DPP_QXOR1>(u);
     u += dpp<DPP_QXOR2>(u);
-    G = (G - u) / rs;
+    G = (G - u) * rrs;
     float v = G * A;  // through T_c: the column sum of G A
     v += dpp<DPP_ROR8>(v);
     v += dpp<DPP_ROR4>(v);
-    G = (G - v) / cs;
+    G = (G - v) * rcs;
   }
   const float dz_res = G * M0;
   float dz_pp = 0.f;
@@ -993,20 +997,26 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   const float u_pre = row16(e < 4 ? dz_pp * pe * invr : 0.f);
   const float u_post = row16(e >= 4 && e < 8 ? dz_pp * pe * invr : 0.f);
   const float u_res = row16(dz_res * pr * invr);
-  if (!valid) return;
-  dP[tt * 32 + 8 + e] = gate.a_res * dz_res * invr;
-  red[tt * 28 + 8 + e] = dz_res;
-  if (e < 8) {
-    dP[tt * 32 + e] = a * dz_pp * invr;
-    dP[tt * 32 + 24 + e] = 0.f;
-    red[tt * 28 + e] = dz_pp;
+  if (valid) {
+    dP[tt * 32 + 8 + e] = gate.a_res * dz_res * invr;
+    if (e < 8) {
+      dP[tt * 32 + e] = a * dz_pp * invr;
+      dP[tt * 32 + 24 + e] = 0.f;
+    }
+    if (e == 0) g2[tt] = -drho * invr * invr * invr / (float)(NS4 * C);
   }
-  if (e == 0) {
-    red[tt * 28 + 24] = u_pre;
-    red[tt * 28 + 25] = u_post;
-    red[tt * 28 + 26] = u_res;
-    red[tt * 28 + 27] = 0.f;
-    g2[tt] = -drho * invr * invr * invr / (float)(NS4 * C);
+  // the workgroup's 16 tokens added in token order (rows past T add zero)
+  __shared__ float bsum[16][28];
+  const int tk = tid >> 4;
+  bsum[tk][8 + e] = valid ? dz_res : 0.f;
+  if (e < 8) bsum[tk][e] = valid ? dz_pp : 0.f;
+  if (e < 4) bsum[tk][24 + e] = !valid || e == 3 ? 0.f : (e == 0 ? u_pre : (e == 1 ? u_post : u_res));
+  __syncthreads();
+  if (tid < 28) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sum += bsum[k][tid];
+    red[(int64_t)blockIdx.x * 28 + tid] = sum;
   }
 }
 
