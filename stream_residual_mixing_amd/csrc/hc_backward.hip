@@ -6,18 +6,18 @@
 // iterations; 4.3 also recomputes the mHC kernels' intermediates in the
 // backward instead of keeping them. Here, from X, F_out and the upstream
 // gradients dX_next and dF_in:
-//  1. the projection partials and the coefficients of X, by the forward's
-//     kernels (hc_fused.hip);
-//  2. bwd_reduce_kernel: per token dh = [dH_pre | dH_post | dH_res] (sums over
-//     the channels) and dF_out = H_post dX_next;
+//  1. phi packed in two forms (projection and dP phi^T operands) and the
+//     projection partials of X by the forward's kernel (hc_fused.hip);
+//  2. bwd_reduce_kernel (hc_fused.hip): per token dh = [dH_pre | dH_post |
+//     dH_res] (sums over the channels) and dF_out = H_post dX_next;
 //  3. bwd_coeff_kernel (hc_fused.hip, beside the forward finish whose floats it
 //     recomputes): gates and Sinkhorn backward -> dP, g2, sums over groups of
-//     16 tokens;
+//     16 tokens, and the forward's h_pre and h_res;
 //  4. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
 //     dP phi^T product on MFMA;
 //  5. bwd_dphi_kernel: vec(x)^T dP over groups of token tiles on MFMA (the
 //     tokens are the K dimension);
-//  6. the group partials of dphi and the per-token sums of db and dalpha are
+//  6. bwd_sums_kernel: the group partials of dphi and the sums of db and dalpha
 //     added in a fixed order.
 #include "hc.h"
 #include "hc_device.h"
@@ -60,97 +60,6 @@ __device__ __forceinline__ void split_bf8(const float v[8], uint4& hi, uint4& lo
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// ------------------------------------------------------------ phi rows
-
-// phi [R = 4C, 24] float32 -> per row 128 bytes: bf16 hi of columns 0..31 (24..31
-// zero), then bf16 lo = bf16(phi - hi). The B operand of dP phi^T: a lane takes
-// one row (channel) and 8 consecutive columns, 16 contiguous bytes.
-__global__ __launch_bounds__(256) void pack_phi_rows_kernel(const float* __restrict__ phi, int64_t R,
-                                                            uint4* __restrict__ out) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= R * 4) return;
-  const int64_t r = g >> 2;
-  const int q = (int)(g & 3);
-  float p[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int col = q * 8 + e;
-    p[e] = col < BCOL ? phi[r * BCOL + col] : 0.f;
-  }
-  uint4 hi, lo;
-  split_bf8(p, hi, lo);
-  out[r * 8 + q] = hi;
-  out[r * 8 + 4 + q] = lo;
-}
-
-// ------------------------------------------------------- per-token sums
-
-// One 256-thread workgroup per token t. Sums over the channels:
-//   dh[i]          = dH_pre[i]     = <dF_in, x_i>
-//   dh[4 + i]      = dH_post[i]    = <dX_next_i, F_out>
-//   dh[8 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>
-// and dF_out = sum_i H_post[i] dX_next_i (rounded once to bfloat16). Thread tid
-// takes the 8-channel chunks tid, tid + 256, ...; the threads' sums are added by
-// a butterfly in each wave and then the 4 waves in order.
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const uint16_t* __restrict__ X,
-                                                         const uint16_t* __restrict__ dXn,
-                                                         const uint16_t* __restrict__ Fo,
-                                                         const uint16_t* __restrict__ dFi, int64_t C,
-                                                         const float* __restrict__ h_post, float* __restrict__ dh,
-                                                         uint16_t* __restrict__ dFo) {
-  __shared__ float wsum[4][BCOL];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  float acc[BCOL];
-#pragma unroll
-  for (int k = 0; k < BCOL; ++k) acc[k] = 0.f;
-  const float4 hq = *reinterpret_cast<const float4*>(h_post + t * 4);
-  const float hpost[4] = {hq.x, hq.y, hq.z, hq.w};
-  const int64_t nch = C / 8;
-  const uint16_t* xr = X + t * BS * C;
-  const uint16_t* dr = dXn + t * BS * C;
-  for (int64_t j = tid; j < nch; j += 256) {
-    const int64_t c = j * 8;
-    uint4 xq[BS], dq[BS];
-#pragma unroll
-    for (int i = 0; i < BS; ++i) {
-      xq[i] = ld_nt16(xr + i * C + c);
-      dq[i] = ld_nt16(dr + i * C + c);
-    }
-    const uint4 fq = ld_nt16(Fo + t * C + c), gq = ld_nt16(dFi + t * C + c);
-    float x[BS][8], d[BS][8], f[8], gi[8], o[8];
-#pragma unroll
-    for (int i = 0; i < BS; ++i) {
-      unpack_bf8(xq[i], x[i]);
-      unpack_bf8(dq[i], d[i]);
-    }
-    unpack_bf8(fq, f);
-    unpack_bf8(gq, gi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] = hpost[0] * d[0][e] + hpost[1] * d[1][e] + hpost[2] * d[2][e] + hpost[3] * d[3][e];
-#pragma unroll
-      for (int i = 0; i < BS; ++i) {
-        acc[i] += gi[e] * x[i][e];
-        acc[4 + i] += d[i][e] * f[e];
-#pragma unroll
-        for (int k = 0; k < BS; ++k) acc[8 + 4 * i + k] += d[i][e] * x[k][e];
-      }
-    }
-    __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
-                                     pack_bf2_hw(o[6], o[7])},
-                                reinterpret_cast<u4_t*>(dFo + t * C + c));
-  }
-#pragma unroll
-  for (int k = 0; k < BCOL; ++k) acc[k] = wave_sum(acc[k]);
-  if ((tid & 63) == 0) {
-#pragma unroll
-    for (int k = 0; k < BCOL; ++k) wsum[tid >> 6][k] = acc[k];
-  }
-  __syncthreads();
-  if (tid < BCOL) dh[t * BCOL + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // ------------------------------------------------------------------- dX
@@ -415,35 +324,37 @@ __global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restric
       }
 }
 
-// dphi = the G group partials added in group order; one thread per entry.
-__global__ __launch_bounds__(256) void sum_groups_kernel(const float* __restrict__ part, int64_t n, int G,
-                                                         float* __restrict__ out) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= n) return;
-  float s = 0.f;
-  for (int k = 0; k < G; ++k) s += part[(int64_t)k * n + g];
-  out[g] = s;
-}
-
-// Column k of the sums over groups of 16 tokens [nrow][28] added over the
-// groups: dbias[k] for k < 24, dalpha[k - 24] for k = 24, 25, 26. One workgroup
-// per column; each thread adds the rows tid, tid + 256, ... in order, then a
-// tree in LDS.
-__global__ __launch_bounds__(256) void col_sum_kernel(const float* __restrict__ red, int64_t nrow,
-                                                      float* __restrict__ dbias, float* __restrict__ dalpha) {
-  __shared__ float s[256];
-  const int k = blockIdx.x, tid = threadIdx.x;
+// The final sums in one launch. Workgroups [0, nbp): dphi, the G group
+// partials added in group order, one thread per entry. Workgroup nbp + k:
+// column k of the sums over groups of 16 tokens [nrow][28] added over the
+// groups (dbias[k] for k < 24, dalpha[k - 24] for k = 24, 25, 26), each thread
+// the rows tid, tid + 256, ... in order, then a tree in LDS.
+__global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__ part, int64_t n, int G, int nbp,
+                                                       float* __restrict__ dphi, const float* __restrict__ red,
+                                                       int64_t nrow, float* __restrict__ dbias,
+                                                       float* __restrict__ dalpha) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < nbp) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
+    if (g >= n) return;
+    float s = 0.f;
+    for (int k = 0; k < G; ++k) s += part[(int64_t)k * n + g];
+    dphi[g] = s;
+    return;
+  }
+  __shared__ float sm[256];
+  const int k = (int)blockIdx.x - nbp;
   float v = 0.f;
   for (int64_t t = tid; t < nrow; t += 256) v += red[t * RED + k];
-  s[tid] = v;
+  sm[tid] = v;
   __syncthreads();
   for (int h = 128; h > 0; h >>= 1) {
-    if (tid < h) s[tid] += s[tid + h];
+    if (tid < h) sm[tid] += sm[tid + h];
     __syncthreads();
   }
   if (tid == 0) {
-    if (k < BCOL) dbias[k] = s[0];
-    else dalpha[k - BCOL] = s[0];
+    if (k < BCOL) dbias[k] = sm[0];
+    else dalpha[k - BCOL] = sm[0];
   }
 }
 
@@ -478,7 +389,7 @@ struct BwdWs {
   void* packed;
   float* partial;
   uint4* phi_rows;
-  float *h_pre, *h_post, *h_res, *dh, *dP, *g2, *red, *dphi_part;
+  float *h_pre, *h_res, *dh, *dP, *g2, *red, *dphi_part;
   int G;
 };
 
@@ -496,7 +407,6 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
   w.partial = (float*)take(fast_coeffs_partial_bytes(T, 4, C, 1));
   w.phi_rows = (uint4*)take(BS * C * 128);
   w.h_pre = (float*)take(T * 4 * 4);
-  w.h_post = (float*)take(T * 4 * 4);
   w.h_res = (float*)take(T * 16 * 4);
   w.dh = (float*)take(T * BCOL * 4);
   w.dP = (float*)take(T * DPS * 4);
@@ -527,18 +437,13 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
                                 float* dbias, float* dalpha, void* ws, hipStream_t st) {
   const BwdWs w = carve(ws, T, C, nullptr);
   const uint16_t* x = (const uint16_t*)X;
-  hipError_t e = launch_fast_coeffs_pre(X, T, C, phi, bias, a_pre, a_post, a_res, iters, w.h_pre, w.h_post,
-                                        w.h_res, nullptr, w.packed, w.partial, st);
+  hipError_t e = launch_fast_bwd_front(X, T, C, phi, w.packed, w.phi_rows, w.partial, st);
   if (e != hipSuccess) return e;
-  const int64_t R = BS * C;
-  hipLaunchKernelGGL(pack_phi_rows_kernel, dim3((unsigned)((R * 4 + 255) / 256)), dim3(256), 0, st, phi, R,
-                     w.phi_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dX_next,
-                     (const uint16_t*)F_out, (const uint16_t*)dF_in, C, w.h_post, w.dh, (uint16_t*)dF_out);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_fast_bwd_reduce(w.partial, X, dX_next, F_out, dF_in, T, C, bias, a_post, w.dh, dF_out, st)) !=
+      hipSuccess)
+    return e;
   if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, w.dh, w.dP, w.g2, w.red,
-                                  st)) != hipSuccess)
+                                  w.h_pre, w.h_res, st)) != hipSuccess)
     return e;
   hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)), dim3(512), 0,
                      st, x, (const uint16_t*)dX_next,
@@ -547,11 +452,9 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
   hipLaunchKernelGGL(bwd_dphi_kernel, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st, x,
                      w.dP, T, C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t nphi = R * BCOL;
-  hipLaunchKernelGGL(sum_groups_kernel, dim3((unsigned)((nphi + 255) / 256)), dim3(256), 0, st, w.dphi_part, nphi,
-                     w.G, dphi);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(col_sum_kernel, dim3(BCOL + 3), dim3(256), 0, st, w.red, (T + 15) / 16, dbias, dalpha);
+  const int64_t nphi = (int64_t)BS * C * BCOL, nbp = (nphi + 255) / 256;
+  hipLaunchKernelGGL(bwd_sums_kernel, dim3((unsigned)(nbp + BCOL + 3)), dim3(256), 0, st, w.dphi_part, nphi, w.G,
+                     (int)nbp, dphi, w.red, (T + 15) / 16, dbias, dalpha);
   return hipGetLastError();
 }
 

@@ -44,13 +44,23 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
                                 float a_pre, float a_post, float a_res, int iters, const void* F_out,
                                 const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi,
                                 float* dbias, float* dalpha, void* ws, hipStream_t st);
-// Gates' and Sinkhorn's backward from the projection partials of
-// launch_fast_coeffs_pre (hc_fused.hip): dh [T, 24] in, dP [T, 32], g2 [T] and the
-// sums red [ceil(T / 16), 28] over groups of 16 tokens out; dynamic LDS of
-// iters * 1 KB (iters <= 64).
+// Pieces of the backward in hc_fused.hip, beside the partial layout they read:
+//  front: phi packed for the projection (packed) and in the row form of the
+//    dP phi^T operand (phi_rows, 4C x 128 bytes), then the projection partials
+//    of X on 64-token items;
+//  reduce: per token dh [T, 24] = [dH_pre | dH_post | dH_res] (sums over C) and
+//    dF_out = H_post dX_next, h_post formed from the partials;
+//  coeffs: gates' and Sinkhorn's backward: dP [T, 32], g2 [T], the sums red
+//    [ceil(T / 16), 28] over groups of 16 tokens, and the forward's h_pre [T, 4]
+//    and h_res [T, 16]; dynamic LDS of iters * 1 KB (iters <= 64).
+hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const float* phi, void* packed,
+                                 uint4* phi_rows, float* partial, hipStream_t st);
+hipError_t launch_fast_bwd_reduce(const float* partial, const void* X, const void* dX_next, const void* F_out,
+                                  const void* dF_in, int64_t T, int64_t C, const float* bias, float a_post, float* dh,
+                                  void* dF_out, hipStream_t st);
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
-                                  float* red, hipStream_t st);
+                                  float* red, float* h_pre, float* h_res, hipStream_t st);
 
 // xHC fast paths (bfloat16 streams, C % 32 == 0). Workspace needs of each (all zero
 // when the shape has no fast path): the packed phi and the per-item partials.

@@ -39,9 +39,12 @@ constexpr int TOK = 16;             // tokens per tile (MFMA M)
 // and ncolp..2 ncolp-1 lo = bf16(phi - hi); columns past na + nb are zero. One
 // workgroup per 64 rows (K is a multiple of 64 on the fast paths): the rows are
 // read into LDS, then thread (row group g, column c) writes the two chunks.
+// With rows_out (the mHC backward, nc <= 32), thread (row t >> 2, column group
+// t & 3) also writes the row form: per row 128 bytes, bf16 hi of columns 0..31
+// then bf16 lo (the B operand of dP phi^T: one row, 8 consecutive columns).
 __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__ phi_a, int na,
                                                        const float* __restrict__ phi_b, int nb, int ncolp,
-                                                       uint16_t* __restrict__ packed) {
+                                                       uint16_t* __restrict__ packed, uint4* __restrict__ rows_out) {
   __shared__ float rows[64 * 32];
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int nc = na + nb;
@@ -50,6 +53,20 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__
     rows[r * 32 + c] = c < na ? phi_a[(r0 + r) * na + c] : phi_b[(r0 + r) * nb + (c - na)];
   }
   __syncthreads();
+  if (rows_out) {
+    const int r = threadIdx.x >> 2, q = threadIdx.x & 3;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float a = q * 8 + e < nc ? rows[r * 32 + q * 8 + e] : 0.f;
+      const float b = q * 8 + e + 1 < nc ? rows[r * 32 + q * 8 + e + 1] : 0.f;
+      const uint32_t h0 = f2bf(a), h1 = f2bf(b);
+      hi[e / 2] = h0 | (h1 << 16);
+      lo[e / 2] = f2bf(a - bf2f(h0)) | (f2bf(b - bf2f(h1)) << 16);
+    }
+    rows_out[(r0 + r) * 8 + q] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    rows_out[(r0 + r) * 8 + 4 + q] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
   if ((int)threadIdx.x >= 8 * ncolp) return;
   const int g = threadIdx.x / ncolp, c = threadIdx.x - g * ncolp;
   float p[8];
@@ -910,15 +927,17 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
 // (pre) and 2 dh s (1 - s) (post) with s = sigmoid(z). Then with rho = 1/r:
 // dP = alpha dz rho, d rho = sum alpha dz P, and the factor of vec x in its
 // gradient, 2 dss = -d rho rho^3 / (4C) (0 for the all-zero state).
-// Outputs per token: dP [32] (columns 24..31 zero: the A operand of the dx
-// product) and g2 (= 2 dss); per workgroup of 16 tokens, red [28] = the sums
+// Outputs per token: h_pre and h_res (the forward's maps, for the dX pass), dP
+// [32] (columns 24..31 zero: the A operand of the dx product) and g2 (= 2 dss);
+// per workgroup of 16 tokens, red [28] = the sums
 // over its tokens of dz [24] | dz P rho over each gate [3] | 0, which are then
 // added over the workgroups for db and dalpha.
 template <int TT>
 __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
                                                         const float* __restrict__ bias, Gate gate, int iters,
                                                         const float* __restrict__ dh, float* __restrict__ dP,
-                                                        float* __restrict__ g2, float* __restrict__ red) {
+                                                        float* __restrict__ g2, float* __restrict__ red,
+                                                        float* __restrict__ h_pre, float* __restrict__ h_res) {
   extern __shared__ float it_lds[];  // [iters][256]
   using PG = PartGeom<3, TT>;
   const int tid = threadIdx.x;
@@ -956,6 +975,10 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
     float rs = M + dpp<DPP_QXOR1>(M);
     rs += dpp<DPP_QXOR2>(rs);
     M = M / rs;
+  }
+  if (valid) {  // the forward's maps, for the dX pass
+    h_res[tt * 16 + e] = M;
+    if (e < 4) h_pre[tt * 4 + e] = sg;
   }
   // each lane reads back only the iterates it wrote: no barrier needed
   float G = dh[tc * 24 + 8 + e];
@@ -1018,6 +1041,91 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
     for (int k = 0; k < 16; ++k) sum += bsum[k][tid];
     red[(int64_t)blockIdx.x * 28 + tid] = sum;
   }
+}
+
+// One 256-thread workgroup per token t. h_post of the token from the partials
+// (the arithmetic of token_coeffs: slices in order, the same gate helpers), then
+// the sums over the channels:
+//   dh[i]          = dH_pre[i]     = <dF_in, x_i>
+//   dh[4 + i]      = dH_post[i]    = <dX_next_i, F_out>
+//   dh[8 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>
+// and dF_out = sum_i H_post[i] dX_next_i (rounded once to bfloat16). Thread tid
+// takes the 8-channel chunks tid, tid + 256, ...; the threads' sums are added by
+// a butterfly in each wave and then the 4 waves in order.
+template <int TT>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part,
+                                                         const uint16_t* __restrict__ X,
+                                                         const uint16_t* __restrict__ dXn,
+                                                         const uint16_t* __restrict__ Fo,
+                                                         const uint16_t* __restrict__ dFi, int64_t C, int S,
+                                                         const float* __restrict__ bias, float a_post,
+                                                         float* __restrict__ dh, uint16_t* __restrict__ dFo) {
+  __shared__ float wsum[4][24];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  float hpost[4];
+  {
+    using PG = PartGeom<3, TT>;
+    const int64_t tile = t / TT;
+    const int m = (int)(t - tile * TT);
+    const float* base = part + tile * S * PG::PART + m * PG::PROW;
+    float ss = 0.f, pe[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+      const float* b = base + (int64_t)s * PG::PART;
+      ss += b[PG::NCOLP];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe[i] += b[4 + i];
+    }
+    const float invr = inv_rms4(ss, C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hpost[i] = 2.0f * sigmoid(gate_logit(a_post, pe[i], invr, bias[4 + i]));
+  }
+  float acc[24];
+#pragma unroll
+  for (int k = 0; k < 24; ++k) acc[k] = 0.f;
+  const int64_t nch = C / 8;
+  const uint16_t* xr = X + t * NS4 * C;
+  const uint16_t* dr = dXn + t * NS4 * C;
+  for (int64_t j = tid; j < nch; j += 256) {
+    const int64_t c = j * 8;
+    uint4 xq[NS4], dq[NS4];
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      xq[i] = ld_stream(xr + i * C + c);
+      dq[i] = ld_stream(dr + i * C + c);
+    }
+    const uint4 fq = ld_stream(Fo + t * C + c), gq = ld_stream(dFi + t * C + c);
+    float x[NS4][8], d[NS4][8], f[8], gi[8], o[8];
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+      unpack8(xq[i], x[i]);
+      unpack8(dq[i], d[i]);
+    }
+    unpack8(fq, f);
+    unpack8(gq, gi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = hpost[0] * d[0][e] + hpost[1] * d[1][e] + hpost[2] * d[2][e] + hpost[3] * d[3][e];
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) {
+        acc[i] += gi[e] * x[i][e];
+        acc[4 + i] += d[i][e] * f[e];
+#pragma unroll
+        for (int k = 0; k < NS4; ++k) acc[8 + 4 * i + k] += d[i][e] * x[k][e];
+      }
+    }
+    __builtin_nontemporal_store(u32x4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                        pack_bf2_hw(o[6], o[7])},
+                                reinterpret_cast<u32x4_t*>(dFo + t * C + c));
+  }
+#pragma unroll
+  for (int k = 0; k < 24; ++k) acc[k] = wave_sum(acc[k]);
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 24; ++k) wsum[tid >> 6][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid < 24) dh[t * 24 + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // ------------------------------------------------------- xHC finish kernels
@@ -1424,9 +1532,9 @@ hipError_t launch_wide(const SplitArgs& A, hipStream_t st) {
 }
 
 hipError_t launch_pack(const float* phi_a, int na, const float* phi_b, int nb, int64_t K, int ncolp, void* packed,
-                       hipStream_t st) {
+                       hipStream_t st, uint4* rows_out = nullptr) {
   hipLaunchKernelGGL(pack_phi_kernel, dim3((unsigned)(K / 64)), dim3(256), 0, st, phi_a, na, phi_b, nb, ncolp,
-                     (uint16_t*)packed);
+                     (uint16_t*)packed, rows_out);
   return hipGetLastError();
 }
 
@@ -1543,13 +1651,29 @@ hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream
   return launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st);
 }
 
+hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const float* phi, void* packed,
+                                 uint4* phi_rows, float* partial, hipStream_t st) {
+  hipError_t e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st, phi_rows);
+  if (e != hipSuccess) return e;
+  return launch_wide<3, ROWS_CONTIG>(args(X, T, C, 4 * C, geom(T, C, 1, W_TOK), packed, partial), st);
+}
+
+hipError_t launch_fast_bwd_reduce(const float* partial, const void* X, const void* dX_next, const void* F_out,
+                                  const void* dF_in, int64_t T, int64_t C, const float* bias, float a_post, float* dh,
+                                  void* dF_out, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_reduce_kernel<W_TOK>, dim3((unsigned)T), dim3(256), 0, st, partial, (const uint16_t*)X,
+                     (const uint16_t*)dX_next, (const uint16_t*)F_out, (const uint16_t*)dF_in, C, (int)slices(C), bias,
+                     a_post, dh, (uint16_t*)dF_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
-                                  float* red, hipStream_t st) {
+                                  float* red, float* h_pre, float* h_res, hipStream_t st) {
   const int64_t threads = T * 16;
   hipLaunchKernelGGL(bwd_coeff_kernel<W_TOK>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
                      (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), bias,
-                     Gate{a_pre, a_post, a_res}, iters, dh, dP, g2, red);
+                     Gate{a_pre, a_post, a_res}, iters, dh, dP, g2, red, h_pre, h_res);
   return hipGetLastError();
 }
 
