@@ -145,6 +145,18 @@ def hc_baseline_bench(torch, hc, dev, reps: int = 20) -> dict:
                              "algorithmic_bytes": gain_bytes, "achieved_GBps": gain_bytes / t_gain / 1e9}}
 
 
+def backward_algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
+    """Bytes of one mHC backward call (n*n + 2n phi columns, float32 phi and dphi):
+    'one_pass': read x, dX_next, F_out, dF_in and write dX, dF_out once, phi read and
+    dphi written once; 'by_design': what the launch sequence moves (x read by the
+    projection, the channel sums, the dX pass and the dphi pass; dX_next and dF_in
+    by the sums and the dX pass; F_out by the sums)."""
+    s, f = n * C * esize, C * esize
+    phi_b = n * C * (n * n + 2 * n) * 4
+    return {"one_pass": T * (3 * s + 3 * f) + 2 * phi_b,
+            "by_design": T * (4 * s + 2 * s + 2 * f + f + s + f) + 2 * phi_b}
+
+
 def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
     """The mHC sublayer backward (hc_backward, n=4 C=4096 T=8192 bf16) on three
     rotating sets of state and upstream gradients; HIP events around the repeated
@@ -182,12 +194,8 @@ def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b) * 1e-3)
     t = sorted(times)[len(times) // 2]
-    s = n * C * 2
-    phi_b = n * C * (n * n + 2 * n) * 4
-    alg = T * (3 * s + 3 * C * 2) + 2 * phi_b
-    f = C * 2
-    # X 4 reads, dX_next 2, dF_in 2, F_out 1; dX and dF_out written once
-    pas = T * (4 * s + 2 * s + 2 * f + f + s + f) + 2 * phi_b
+    bb = backward_algorithmic_bytes(T, n, C)
+    alg, pas = bb["one_pass"], bb["by_design"]
     return {"workload": "mHC backward n=4 C=4096 T=8192 bf16 (20 Sinkhorn iterations recomputed)",
             "median_us": t * 1e6, "tokens_per_s": T / t, "algorithmic_bytes": alg,
             "achieved_GBps": alg / t / 1e9, "pct_hbm_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
