@@ -146,25 +146,27 @@ def hc_baseline_bench(torch, hc, dev, reps: int = 20) -> dict:
 
 
 def backward_algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
-    """Bytes of one mHC backward call (n*n + 2n phi columns, float32 phi and dphi):
-    'one_pass': read x, dX_next, F_out, dF_in and write dX, dF_out once, phi read and
-    dphi written once; 'by_design': what the launch sequence moves (x read by the
-    projection, the channel sums, the dX pass and the dphi pass; dX_next and dF_in
-    by the sums and the dX pass; F_out by the sums)."""
+    """Bytes of one mHC backward (both stages; n*n + 2n phi columns, float32 phi and
+    dphi, float32 map gradients dh [T, n*n + 2n]): 'one_pass': read x, dX_next,
+    F_out, dF_in and write dX, dF_out once, phi read and dphi written once;
+    'by_design': what the launches move (post stage: x, dX_next, F_out read, dF_out
+    written; main stage: x read by the projection, the dH_pre sums, the dX pass
+    and the dphi pass, dF_in by the sums and the dX pass, dX_next by the dX pass,
+    dX written)."""
     s, f = n * C * esize, C * esize
     phi_b = n * C * (n * n + 2 * n) * 4
+    dh_b = (n * n + 2 * n) * 4
+    post = s + s + f + f + dh_b
+    main = 4 * s + 2 * f + s + s + dh_b
     return {"one_pass": T * (3 * s + 3 * f) + 2 * phi_b,
-            "by_design": T * (4 * s + 2 * s + 2 * f + f + s + f) + 2 * phi_b}
+            "by_design": T * (post + main) + 2 * phi_b,
+            "post_stage": T * post, "main_stage": T * main + 2 * phi_b}
 
 
 def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
-    """The mHC sublayer backward (hc_backward, n=4 C=4096 T=8192 bf16) on three
-    rotating sets of state and upstream gradients; HIP events around the repeated
-    calls. algorithmic_bytes is the one-pass minimum per call (read X, F_out,
-    dX_next, dF_in; write dX, dF_out; phi read and dphi written once); pass_bytes
-    is what this kernel sequence moves by design (the state read by the
-    projection, the channel sums, the dX pass and the dphi pass; dX_next and dF_in
-    by the sums and the dX pass)."""
+    """The mHC sublayer backward (n=4 C=4096 T=8192 bf16): hc_backward_post then
+    hc_backward, on three rotating sets of state and upstream gradients; HIP
+    events around each stage of each repetition (median reported)."""
     T, n, C = 8192, 4, 4096
     g = torch.Generator(device=dev)
     g.manual_seed(5000)
@@ -176,30 +178,40 @@ def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
     phi = rn(n * C, n * n + 2 * n, std=0.02)
     bias = torch.zeros(n * n + 2 * n, device=dev)
     bias[2 * n:] = torch.eye(n, device=dev).flatten()
-    out = (torch.empty(T, n, C, dtype=torch.bfloat16, device=dev), torch.empty(T, C, dtype=torch.bfloat16, device=dev),
-           torch.empty(n * C, n * n + 2 * n, device=dev), torch.empty(n * n + 2 * n, device=dev),
-           torch.empty(3, device=dev))
+    h_post = torch.rand(T, n, device=dev, generator=g) * 2.0
+    dF_out = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
+    dh = torch.empty(T, n * n + 2 * n, device=dev)
+    out = (torch.empty(T, n, C, dtype=torch.bfloat16, device=dev), torch.empty(n * C, n * n + 2 * n, device=dev),
+           torch.empty(n * n + 2 * n, device=dev), torch.empty(3, device=dev))
     ws = torch.empty(hc.hc_backward_workspace_bytes(T, n, C, torch.bfloat16), dtype=torch.uint8, device=dev)
-    fn = lambda i: hc.hc_backward(Xs[i % 3], phi, bias, (0.01, 0.01, 0.01), Fs[i % 3], dXs[i % 3], dFs[i % 3],
-                                  SINKHORN_ITERS, out=out, workspace=ws)
+    post = lambda i: hc.hc_backward_post(Xs[i % 3], h_post, Fs[i % 3], dXs[i % 3], out=(dF_out, dh))
+    main = lambda i: hc.hc_backward(Xs[i % 3], phi, bias, (0.01, 0.01, 0.01), dXs[i % 3], dFs[i % 3], dh,
+                                    SINKHORN_ITERS, out=out, workspace=ws)
     for i in range(3):
-        fn(i)
+        post(i)
+        main(i)
     torch.cuda.synchronize()
-    times = []
+    tp, tm = [], []
     for r in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn(r)
-        b.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        post(r)
+        ev[1].record()
+        main(r)
+        ev[2].record()
         torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e-3)
-    t = sorted(times)[len(times) // 2]
+        tp.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        tm.append(ev[1].elapsed_time(ev[2]) * 1e-3)
+    med = lambda v: sorted(v)[len(v) // 2]
+    t_post, t_main = med(tp), med(tm)
+    t = t_post + t_main
     bb = backward_algorithmic_bytes(T, n, C)
-    alg, pas = bb["one_pass"], bb["by_design"]
     return {"workload": "mHC backward n=4 C=4096 T=8192 bf16 (20 Sinkhorn iterations recomputed)",
-            "median_us": t * 1e6, "tokens_per_s": T / t, "algorithmic_bytes": alg,
-            "achieved_GBps": alg / t / 1e9, "pct_hbm_peak": 100.0 * alg / t / 1e9 / HBM_PEAK_GBPS,
-            "pass_bytes": pas, "pass_GBps": pas / t / 1e9}
+            "us": t * 1e6, "post_stage_us": t_post * 1e6, "main_stage_us": t_main * 1e6, "tokens_per_s": T / t,
+            "algorithmic_bytes": bb["one_pass"], "achieved_GBps": bb["one_pass"] / t / 1e9,
+            "pct_hbm_peak": 100.0 * bb["one_pass"] / t / 1e9 / HBM_PEAK_GBPS,
+            "by_design_bytes": bb["by_design"], "by_design_GBps": bb["by_design"] / t / 1e9,
+            "post_stage_GBps": bb["post_stage"] / t_post / 1e9, "main_stage_GBps": bb["main_stage"] / t_main / 1e9}
 
 
 def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:

@@ -122,35 +122,48 @@ int hc_coeffs_pre(const void* X, int dtype, int64_t T, int n, int64_t C,
                   void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
- * hc_backward - gradients of one mHC sublayer ([mHC] 4.3.1 Kernel Fusion: the
- * backward of the Eq. 14-15 projection, two products over the same x, and a
- * Sinkhorn-Knopp backward that recomputes the iterates on chip; 4.3 recomputes
- * the forward's intermediates from x in the backward).
+ * hc_backward_post, hc_backward - gradients of one mHC sublayer ([mHC] 4.3.1
+ * Kernel Fusion: the backward of the Eq. 14-15 projection, two products over
+ * the same x, and a Sinkhorn-Knopp backward that recomputes the iterates on
+ * chip; 4.3 recomputes the forward's intermediates from x in the backward).
  *   Forward (hc_coeffs, hc_pre, hc_post with the same arguments):
  *     F_in = H_pre x,  X_next = H_res x + H_post^T F_out.
- *   Inputs: X [T, 4, C], F_out [T, C] (the forward's), dX_next [T, 4, C] and
- *     dF_in [T, C] (upstream gradients of X_next and F_in), all bfloat16;
- *     phi, bias, alpha_*, sinkhorn_iters as for hc_coeffs.
- *   Outputs: dX [T, 4, C] and dF_out [T, C] bfloat16 (rounded once from float32),
- *     dphi [4C, 24], dbias [24] (column order of phi), dalpha [3]
- *     (pre, post, res) float32; dphi, dbias and dalpha are sums over the T tokens.
+ *   Two stages, in the order a training step meets them:
+ *   hc_backward_post (before the sublayer function's backward, which needs
+ *     dF_out): from X [T, 4, C], F_out [T, C], dX_next [T, 4, C] (the upstream
+ *     gradient of X_next) and the forward's h_post [T, 4] float32:
+ *       dF_out [T, C]                = H_post dX_next (bfloat16, rounded once),
+ *       dh[:, 4:8]  = dH_post[i]     = <dX_next_i, F_out>,
+ *       dh[:, 8:24] = dH_res[i, j]   = <dX_next_i, x_j>  (index 8 + 4i + j).
+ *   hc_backward (once dF_in [T, C], the gradient of F_in, is known): fills
+ *     dh[:, 0:4] = dH_pre[i] = <dF_in, x_i>, reads dh[:, 4:24] as left by
+ *     hc_backward_post, and writes
+ *       dX [T, 4, C] (bfloat16, rounded once), dphi [4C, 24], dbias [24] (column
+ *       order of phi), dalpha [3] (pre, post, res) float32, the last three
+ *       summed over the T tokens.
+ *     phi, bias, alpha_*, sinkhorn_iters as for hc_coeffs; the maps are
+ *     recomputed from X. dh [T, 24] float32 is the gradient of the maps
+ *     [H_pre | H_post | H_res] per token.
  *   Covered: dtype HC_BF16 (HC_F32 -> HC_ERR_DTYPE), n = 4, C a multiple of 32,
  *   1 <= sinkhorn_iters <= HC_MAX_BWD_ITERS (else HC_ERR_SHAPE). The all-zero
  *   state takes 1/r = 0 (as the forward) and passes no gradient through r.
- *   Alignment: X, F_out, dX_next, dF_in, dX, dF_out 16 bytes; the float arrays 4
- *   bytes; workspace 256 bytes, at least hc_backward_workspace_bytes (the
- *   recomputed coefficients, projection partials, per-token gradients and the
- *   partial sums of dphi). No output may overlap an input, another output or the
- *   workspace (HC_ERR_ALIAS). Deterministic: every sum runs in a fixed order.
+ *   Alignment: the bfloat16 arrays and h_post 16 bytes, the other float arrays
+ *   4 bytes, workspace 256 bytes and at least hc_backward_workspace_bytes (the
+ *   packed phi, projection partials, recomputed maps, dP and the partial sums
+ *   of dphi). No output may overlap an input, another output or the workspace
+ *   (HC_ERR_ALIAS). Deterministic: every sum runs in a fixed order.
  *   hc_backward_workspace_bytes: 0 for T = 0, -1 for sizes or a dtype that
  *   hc_backward does not cover.
  */
 int64_t hc_backward_workspace_bytes(int64_t T, int n, int64_t C, int dtype);
+int hc_backward_post(const void* X, int dtype, int64_t T, int n, int64_t C,
+                     const float* h_post, const void* F_out, const void* dX_next,
+                     void* dF_out, float* dh, void* stream);
 int hc_backward(const void* X, int dtype, int64_t T, int n, int64_t C,
                 const float* phi, const float* bias,
                 float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters,
-                const void* F_out, const void* dX_next, const void* dF_in,
-                void* dX, void* dF_out, float* dphi, float* dbias, float* dalpha,
+                const void* dX_next, const void* dF_in, float* dh,
+                void* dX, float* dphi, float* dbias, float* dalpha,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /*

@@ -446,7 +446,9 @@ def mhc_sublayer_backward(X, phi, bias, alpha, F_out, dX_next, dF_in, sinkhorn_i
     Reading for the all-zero state: 1/r is taken as 0 there (as in the forward)
     and contributes no gradient.
     Returns dict(dX [T, n, C], dF_out [T, C], dphi [nC, n*n + 2n], dbias
-    [n*n + 2n], dalpha [3], dz [T, n*n + 2n]); dbias and dalpha sum over tokens.
+    [n*n + 2n], dalpha [3], dz [T, n*n + 2n], dh [T, n*n + 2n]); dh holds the
+    gradients of the maps [dH_pre | dH_post | dH_res (row-major)] per token;
+    dbias and dalpha sum over tokens.
     """
     X = _f64(X)
     T, n, C = X.shape
@@ -494,4 +496,5 @@ def mhc_sublayer_backward(X, phi, bias, alpha, F_out, dX_next, dF_in, sinkhorn_i
     dx = dP @ phi.T + 2.0 * dss[:, None] * x
     dphi = x.T @ dP
     dX = dX + dx.reshape(T, n, C)
-    return dict(dX=dX, dF_out=dF_out, dphi=dphi, dbias=dbias, dalpha=dalpha, dz=dz)
+    dh = np.concatenate([dh_pre, dh_post, dh_res.reshape(T, n * n)], axis=1)
+    return dict(dX=dX, dF_out=dF_out, dphi=dphi, dbias=dbias, dalpha=dalpha, dz=dz, dh=dh)

@@ -35,8 +35,9 @@ _SIGS = {
                                _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "hc_backward_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int]),
+    "hc_backward_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "hc_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float, _c_int,
-                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_post_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _c_float,
                                 _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "hc_phi_packed_bytes": (_c_i64, [_c_int, _c_i64, _c_int]),
@@ -198,28 +199,43 @@ def hc_backward_workspace_bytes(T: int, n: int, C: int, dtype) -> int:
     return int(lib().hc_backward_workspace_bytes(T, n, C, _DT[dtype]))
 
 
-def hc_backward(X, phi, bias, alpha, F_out, dX_next, dF_in, sinkhorn_iters=20, *, out=None, workspace=None,
-                stream=None):
-    """Gradients of one mHC sublayer (n = 4, bfloat16): (dX, dF_out, dphi, dbias, dalpha)."""
+def hc_backward_post(X, h_post, F_out, dX_next, *, out=None, stream=None):
+    """Backward, post stage (n = 4, bfloat16): (dF_out, dh) with dF_out = H_post dX_next
+    and dh [T, 24] float32 holding dH_post (columns 4..7) and dH_res (8..23)."""
     X = _dev_tensor(X, "X", (torch.bfloat16,))
     T, n, C = X.shape
     F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
     dX_next = _dev_tensor(dX_next, "dX_next", (X.dtype,))
+    if out is None:
+        out = (torch.empty(T, C, dtype=X.dtype, device=X.device), torch.empty(T, n * n + 2 * n, device=X.device))
+    dF_out, dh = out
+    _check("hc_backward_post", lib().hc_backward_post(_ptr(X), _DT[X.dtype], T, n, C, _ptr(_f32(h_post, "h_post")),
+                                                      _ptr(F_out), _ptr(dX_next), _ptr(dF_out),
+                                                      _ptr(_f32(dh, "dh")), _stream(X.device, stream)))
+    return dF_out, dh
+
+
+def hc_backward(X, phi, bias, alpha, dX_next, dF_in, dh, sinkhorn_iters=20, *, out=None, workspace=None,
+                stream=None):
+    """Backward, main stage (n = 4, bfloat16): fills dh[:, 0:4] (dH_pre), reads the rest of
+    dh from hc_backward_post, returns (dX, dphi, dbias, dalpha)."""
+    X = _dev_tensor(X, "X", (torch.bfloat16,))
+    T, n, C = X.shape
+    dX_next = _dev_tensor(dX_next, "dX_next", (X.dtype,))
     dF_in = _dev_tensor(dF_in, "dF_in", (X.dtype,))
-    phi, bias = _f32(phi, "phi"), _f32(bias, "bias")
+    phi, bias, dh = _f32(phi, "phi"), _f32(bias, "bias"), _f32(dh, "dh")
     if out is None:
         dev = X.device
-        out = (torch.empty_like(X), torch.empty(T, C, dtype=X.dtype, device=dev),
-               torch.empty(n * C, n * n + 2 * n, device=dev), torch.empty(n * n + 2 * n, device=dev),
-               torch.empty(3, device=dev))
-    dX, dF_out, dphi, dbias, dalpha = out
+        out = (torch.empty_like(X), torch.empty(n * C, n * n + 2 * n, device=dev),
+               torch.empty(n * n + 2 * n, device=dev), torch.empty(3, device=dev))
+    dX, dphi, dbias, dalpha = out
     ws = _workspace(hc_backward_workspace_bytes(T, n, C, X.dtype), X.device, workspace)
     a = [float(v) for v in alpha]
     _check("hc_backward", lib().hc_backward(_ptr(X), _DT[X.dtype], T, n, C, _ptr(phi), _ptr(bias), a[0], a[1], a[2],
-                                            int(sinkhorn_iters), _ptr(F_out), _ptr(dX_next), _ptr(dF_in),
-                                            _ptr(dX), _ptr(dF_out), _ptr(dphi), _ptr(dbias), _ptr(dalpha),
-                                            _ptr(ws), ws.numel(), _stream(X.device, stream)))
-    return dX, dF_out, dphi, dbias, dalpha
+                                            int(sinkhorn_iters), _ptr(dX_next), _ptr(dF_in), _ptr(dh), _ptr(dX),
+                                            _ptr(dphi), _ptr(dbias), _ptr(dalpha), _ptr(ws), ws.numel(),
+                                            _stream(X.device, stream)))
+    return dX, dphi, dbias, dalpha
 
 
 def hc_post_coeffs(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sinkhorn_iters=20, *, out=None,
@@ -451,7 +467,7 @@ def hc_copy_probe(src, dst, *, stream=None):
 
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
-    "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
+    "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward_post", "hc_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
     "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",

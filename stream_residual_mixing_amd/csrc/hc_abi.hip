@@ -233,42 +233,80 @@ int64_t hc_backward_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
   return hc::fast_backward_ws_bytes(T, C);
 }
 
+// the shapes and dtype both backward stages cover (T >= 0)
+static int check_backward_shape(int dtype, int64_t T, int n, int64_t C) {
+  if (!dtype_ok(dtype) || dtype != HC_BF16) return HC_ERR_DTYPE;
+  if (T < 0 || n != 4 || C < 32 || C % 32 != 0 || C > (1ll << 26)) return HC_ERR_SHAPE;
+  return HC_OK;
+}
+
+// pairwise overlap of outputs with every input and with each other
+static bool any_overlap(const void* const* outs, const int64_t* ob, int no, const void* const* ins,
+                        const int64_t* ib, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return true;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return true;
+  }
+  return false;
+}
+
+int hc_backward_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_post, const void* F_out,
+                     const void* dX_next, void* dF_out, float* dh, void* stream) {
+  int s = check_backward_shape(dtype, T, n, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!hc::fast_backward_supported(dtype, n, T, C, 1)) return HC_ERR_SHAPE;
+  if (!X || !h_post || !F_out || !dX_next || !dF_out || !dh) return HC_ERR_NULL;
+  for (const void* p : {X, (const void*)h_post, F_out, dX_next, (const void*)dF_out})
+    if (!aligned_to(p, 16)) return HC_ERR_ALIGN;
+  if (!aligned_to(dh, 4)) return HC_ERR_ALIGN;
+  const int64_t xb = T * 4 * C * 2, fb = T * C * 2;
+  const void* ins[4] = {X, h_post, F_out, dX_next};
+  const int64_t ib[4] = {xb, T * 16, fb, xb};
+  const void* outs[2] = {dF_out, dh};
+  const int64_t ob[2] = {fb, T * 24 * 4};
+  if (any_overlap(outs, ob, 2, ins, ib, 4)) return HC_ERR_ALIAS;
+  if ((s = device_status()) != HC_OK) return s;
+  return launch_status(
+      hc::launch_fast_backward_post(X, T, C, h_post, F_out, dX_next, dF_out, dh, (hipStream_t)stream));
+}
+
 int hc_backward(const void* X, int dtype, int64_t T, int n, int64_t C, const float* phi, const float* bias,
-                float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters, const void* F_out,
-                const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi, float* dbias,
-                float* dalpha, void* workspace, int64_t workspace_bytes, void* stream) {
-  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
-  if (dtype != HC_BF16) return HC_ERR_DTYPE;
-  if (T < 0 || n != 4 || C < 32 || C % 32 != 0 || C > (1ll << 26) || sinkhorn_iters < 1 ||
-      sinkhorn_iters > HC_MAX_BWD_ITERS)
-    return HC_ERR_SHAPE;
+                float alpha_pre, float alpha_post, float alpha_res, int sinkhorn_iters, const void* dX_next,
+                const void* dF_in, float* dh, void* dX, float* dphi, float* dbias, float* dalpha, void* workspace,
+                int64_t workspace_bytes, void* stream) {
+  int s = check_backward_shape(dtype, T, n, C);
+  if (s != HC_OK) return s;
+  if (sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_BWD_ITERS) return HC_ERR_SHAPE;
   if (T == 0) return HC_OK;
   if (!hc::fast_backward_supported(dtype, n, T, C, sinkhorn_iters)) return HC_ERR_SHAPE;
-  if (!X || !phi || !bias || !F_out || !dX_next || !dF_in || !dX || !dF_out || !dphi || !dbias || !dalpha)
-    return HC_ERR_NULL;
-  for (const void* p : {X, F_out, dX_next, dF_in, (const void*)dX, (const void*)dF_out})
+  if (!X || !phi || !bias || !dX_next || !dF_in || !dh || !dX || !dphi || !dbias || !dalpha) return HC_ERR_NULL;
+  for (const void* p : {X, dX_next, dF_in, (const void*)dX})
     if (!aligned_to(p, 16)) return HC_ERR_ALIGN;
-  for (const void* p : {(const void*)phi, (const void*)bias, (const void*)dphi, (const void*)dbias,
-                        (const void*)dalpha})
+  for (const void* p : {(const void*)phi, (const void*)bias, (const void*)dh, (const void*)dphi,
+                        (const void*)dbias, (const void*)dalpha})
     if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
   const int64_t wsb = hc::fast_backward_ws_bytes(T, C);
   if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
-  const int64_t xb = T * 4 * C * 2, fb = T * C * 2, pb = 4 * C * 24 * 4;
-  const void* ins[6] = {X, phi, bias, F_out, dX_next, dF_in};
-  const int64_t ib[6] = {xb, pb, 24 * 4, fb, xb, fb};
-  const void* outs[6] = {dX, dF_out, dphi, dbias, dalpha, workspace};
-  const int64_t ob[6] = {xb, fb, pb, 24 * 4, 3 * 4, wsb};
-  for (int i = 0; i < 6; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return HC_ERR_ALIAS;
-    for (int j = 0; j < i; ++j)
-      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  const int64_t xb = T * 4 * C * 2, fb = T * C * 2, pb = 4 * C * 24 * 4, hb = T * 24 * 4;
+  // dh is read and written: it may overlap nothing else
+  const void* ins[6] = {X, phi, bias, dX_next, dF_in, dh};
+  const int64_t ib[6] = {xb, pb, 24 * 4, xb, fb, hb};
+  const void* outs[5] = {dX, dphi, dbias, dalpha, workspace};
+  const int64_t ob[5] = {xb, pb, 24 * 4, 3 * 4, wsb};
+  if (any_overlap(outs, ob, 5, ins, ib, 6)) return HC_ERR_ALIAS;
+  {
+    const void* ins2[5] = {X, phi, bias, dX_next, dF_in};
+    const int64_t ib2[5] = {xb, pb, 24 * 4, xb, fb};
+    const void* outs2[1] = {dh};
+    const int64_t ob2[1] = {hb};
+    if (any_overlap(outs2, ob2, 1, ins2, ib2, 5)) return HC_ERR_ALIAS;
   }
-  int s = device_status();
-  if (s != HC_OK) return s;
+  if ((s = device_status()) != HC_OK) return s;
   return launch_status(hc::launch_fast_backward(X, T, C, phi, bias, alpha_pre, alpha_post, alpha_res,
-                                                sinkhorn_iters, F_out, dX_next, dF_in, dX, dF_out, dphi, dbias,
-                                                dalpha, workspace, (hipStream_t)stream));
+                                                sinkhorn_iters, dX_next, dF_in, dh, dX, dphi, dbias, dalpha,
+                                                workspace, (hipStream_t)stream));
 }
 
 int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,

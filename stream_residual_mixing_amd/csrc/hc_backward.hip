@@ -4,12 +4,15 @@
 // backward of the Eq. 14-15 kernel holds two products over the same x, and the
 // Sinkhorn-Knopp backward recomputes the iterates on chip and walks the
 // iterations; 4.3 also recomputes the mHC kernels' intermediates in the
-// backward instead of keeping them. Here, from X, F_out and the upstream
-// gradients dX_next and dF_in:
+// backward instead of keeping them. Two stages, in the order a training step
+// meets them:
+//  post stage (before the sublayer function's backward, which needs dF_out):
+//    bwd_post_kernel: dF_out = H_post dX_next (H_post the forward's) and per
+//    token dh[4:24] = [dH_post | dH_res] (sums over the channels);
+//  main stage (once dF_in is known):
 //  1. phi packed in two forms (projection and dP phi^T operands) and the
 //     projection partials of X by the forward's kernel (hc_fused.hip);
-//  2. bwd_reduce_kernel (hc_fused.hip): per token dh = [dH_pre | dH_post |
-//     dH_res] (sums over the channels) and dF_out = H_post dX_next;
+//  2. bwd_pre_sums_kernel: per token dh[0:4] = dH_pre (sums over the channels);
 //  3. bwd_coeff_kernel (hc_fused.hip, beside the forward finish whose floats it
 //     recomputes): gates and Sinkhorn backward -> dP, g2, sums over groups of
 //     16 tokens, and the forward's h_pre and h_res;
@@ -60,6 +63,106 @@ __device__ __forceinline__ void split_bf8(const float v[8], uint4& hi, uint4& lo
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// ------------------------------------------------------- per-token sums
+
+// One 256-thread workgroup per token t (post stage): dF_out = sum_i H_post[i]
+// dX_next_i (rounded once to bfloat16) and the sums over the channels
+//   dh[4 + i]      = dH_post[i]    = <dX_next_i, F_out>
+//   dh[8 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>.
+// Thread tid takes the 8-channel chunks tid, tid + 256, ...; the threads' sums
+// are added by a butterfly in each wave and then the 4 waves in order.
+__global__ __launch_bounds__(256) void bwd_post_kernel(const uint16_t* __restrict__ X,
+                                                       const uint16_t* __restrict__ dXn,
+                                                       const uint16_t* __restrict__ Fo, int64_t C,
+                                                       const float* __restrict__ h_post, float* __restrict__ dh,
+                                                       uint16_t* __restrict__ dFo) {
+  __shared__ float wsum[4][20];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float4 hq = *reinterpret_cast<const float4*>(h_post + t * 4);
+  const float hpost[4] = {hq.x, hq.y, hq.z, hq.w};
+  float acc[20];
+#pragma unroll
+  for (int k = 0; k < 20; ++k) acc[k] = 0.f;
+  const int64_t nch = C / 8;
+  const uint16_t* xr = X + t * BS * C;
+  const uint16_t* dr = dXn + t * BS * C;
+  for (int64_t j = tid; j < nch; j += 256) {
+    const int64_t c = j * 8;
+    uint4 xq[BS], dq[BS];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      xq[i] = ld_nt16(xr + i * C + c);
+      dq[i] = ld_nt16(dr + i * C + c);
+    }
+    const uint4 fq = ld_nt16(Fo + t * C + c);
+    float x[BS][8], d[BS][8], f[8], o[8];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      unpack_bf8(xq[i], x[i]);
+      unpack_bf8(dq[i], d[i]);
+    }
+    unpack_bf8(fq, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = hpost[0] * d[0][e] + hpost[1] * d[1][e] + hpost[2] * d[2][e] + hpost[3] * d[3][e];
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+        acc[i] += d[i][e] * f[e];
+#pragma unroll
+        for (int k = 0; k < BS; ++k) acc[4 + 4 * i + k] += d[i][e] * x[k][e];
+      }
+    }
+    __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                     pack_bf2_hw(o[6], o[7])},
+                                reinterpret_cast<u4_t*>(dFo + t * C + c));
+  }
+#pragma unroll
+  for (int k = 0; k < 20; ++k) acc[k] = wave_sum(acc[k]);
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 20; ++k) wsum[tid >> 6][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid < 20) dh[t * BCOL + 4 + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+}
+
+// One 256-thread workgroup per token t (main stage): dh[i] = dH_pre[i] =
+// <dF_in, x_i>, summed as in bwd_post_kernel.
+__global__ __launch_bounds__(256) void bwd_pre_sums_kernel(const uint16_t* __restrict__ X,
+                                                           const uint16_t* __restrict__ dFi, int64_t C,
+                                                           float* __restrict__ dh) {
+  __shared__ float wsum[4][4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int64_t nch = C / 8;
+  const uint16_t* xr = X + t * BS * C;
+  for (int64_t j = tid; j < nch; j += 256) {
+    const int64_t c = j * 8;
+    uint4 xq[BS];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) xq[i] = ld_nt16(xr + i * C + c);
+    const uint4 gq = ld_nt16(dFi + t * C + c);
+    float x[8], g[8];
+    unpack_bf8(gq, g);
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      unpack_bf8(xq[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i] += g[e] * x[e];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = wave_sum(acc[k]);
+  if ((tid & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wsum[tid >> 6][k] = acc[k];
+  }
+  __syncthreads();
+  if (tid < 4) dh[t * BCOL + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // ------------------------------------------------------------------- dX
@@ -389,7 +492,7 @@ struct BwdWs {
   void* packed;
   float* partial;
   uint4* phi_rows;
-  float *h_pre, *h_res, *dh, *dP, *g2, *red, *dphi_part;
+  float *h_pre, *h_res, *dP, *g2, *red, *dphi_part;
   int G;
 };
 
@@ -408,7 +511,6 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
   w.phi_rows = (uint4*)take(BS * C * 128);
   w.h_pre = (float*)take(T * 4 * 4);
   w.h_res = (float*)take(T * 16 * 4);
-  w.dh = (float*)take(T * BCOL * 4);
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
   w.red = (float*)take((T + 15) / 16 * RED * 4);
@@ -431,23 +533,29 @@ int64_t fast_backward_ws_bytes(int64_t T, int64_t C) {
   return total;
 }
 
+hipError_t launch_fast_backward_post(const void* X, int64_t T, int64_t C, const float* h_post, const void* F_out,
+                                     const void* dX_next, void* dF_out, float* dh, hipStream_t st) {
+  hipLaunchKernelGGL(bwd_post_kernel, dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)X,
+                     (const uint16_t*)dX_next, (const uint16_t*)F_out, C, h_post, dh, (uint16_t*)dF_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float* phi, const float* bias,
-                                float a_pre, float a_post, float a_res, int iters, const void* F_out,
-                                const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi,
-                                float* dbias, float* dalpha, void* ws, hipStream_t st) {
+                                float a_pre, float a_post, float a_res, int iters, const void* dX_next,
+                                const void* dF_in, float* dh, void* dX, float* dphi, float* dbias, float* dalpha,
+                                void* ws, hipStream_t st) {
   const BwdWs w = carve(ws, T, C, nullptr);
   const uint16_t* x = (const uint16_t*)X;
   hipError_t e = launch_fast_bwd_front(X, T, C, phi, w.packed, w.phi_rows, w.partial, st);
   if (e != hipSuccess) return e;
-  if ((e = launch_fast_bwd_reduce(w.partial, X, dX_next, F_out, dF_in, T, C, bias, a_post, w.dh, dF_out, st)) !=
-      hipSuccess)
-    return e;
-  if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, w.dh, w.dP, w.g2, w.red,
+  hipLaunchKernelGGL(bwd_pre_sums_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dF_in, C, dh);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                   w.h_pre, w.h_res, st)) != hipSuccess)
     return e;
   hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)), dim3(512), 0,
-                     st, x, (const uint16_t*)dX_next,
-                     (const uint16_t*)dF_in, T, C, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+                     st, x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, w.h_pre, w.h_res, w.dP, w.g2,
+                     w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dphi_kernel, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st, x,
                      w.dP, T, C, w.dphi_part);

@@ -35,29 +35,29 @@ hipError_t launch_fast_post_coeffs(const void* X, int64_t T, int64_t C, const fl
 
 bool fast_post_supported(int dtype, int n, int64_t C, const void* X, const void* F, const void* Y);
 
-// mHC sublayer backward for n = 4 bfloat16 streams (hc_backward.hip): shapes it
-// covers, its workspace, and the launch sequence (all device pointers; X, F_out,
-// dX_next, dF_in, dX, dF_out 16-byte aligned).
+// mHC sublayer backward for n = 4 bfloat16 streams (hc_backward.hip), in two
+// stages (all device pointers; the bfloat16 arrays 16-byte aligned):
+//  post: dF_out = H_post dX_next and dh[:, 4:24] = [dH_post | dH_res] from X,
+//    F_out, dX_next and the forward's h_post;
+//  main: dh[:, 0:4] = dH_pre from X and dF_in, then dX, dphi, dbias, dalpha.
 bool fast_backward_supported(int dtype, int n, int64_t T, int64_t C, int iters);
 int64_t fast_backward_ws_bytes(int64_t T, int64_t C);
+hipError_t launch_fast_backward_post(const void* X, int64_t T, int64_t C, const float* h_post, const void* F_out,
+                                     const void* dX_next, void* dF_out, float* dh, hipStream_t st);
 hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float* phi, const float* bias,
-                                float a_pre, float a_post, float a_res, int iters, const void* F_out,
-                                const void* dX_next, const void* dF_in, void* dX, void* dF_out, float* dphi,
-                                float* dbias, float* dalpha, void* ws, hipStream_t st);
+                                float a_pre, float a_post, float a_res, int iters, const void* dX_next,
+                                const void* dF_in, float* dh, void* dX, float* dphi, float* dbias, float* dalpha,
+                                void* ws, hipStream_t st);
 // Pieces of the backward in hc_fused.hip, beside the partial layout they read:
 //  front: phi packed for the projection (packed) and in the row form of the
 //    dP phi^T operand (phi_rows, 4C x 128 bytes), then the projection partials
 //    of X on 64-token items;
-//  reduce: per token dh [T, 24] = [dH_pre | dH_post | dH_res] (sums over C) and
-//    dF_out = H_post dX_next, h_post formed from the partials;
-//  coeffs: gates' and Sinkhorn's backward: dP [T, 32], g2 [T], the sums red
-//    [ceil(T / 16), 28] over groups of 16 tokens, and the forward's h_pre [T, 4]
-//    and h_res [T, 16]; dynamic LDS of iters * 1 KB (iters <= 64).
+//  coeffs: gates' and Sinkhorn's backward from dh [T, 24]: dP [T, 32], g2 [T],
+//    the sums red [ceil(T / 16), 28] over groups of 16 tokens, and the
+//    forward's h_pre [T, 4] and h_res [T, 16]; dynamic LDS of iters * 1 KB
+//    (iters <= 64).
 hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const float* phi, void* packed,
                                  uint4* phi_rows, float* partial, hipStream_t st);
-hipError_t launch_fast_bwd_reduce(const float* partial, const void* X, const void* dX_next, const void* F_out,
-                                  const void* dF_in, int64_t T, int64_t C, const float* bias, float a_post, float* dh,
-                                  void* dF_out, hipStream_t st);
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                   float* red, float* h_pre, float* h_res, hipStream_t st);

@@ -1043,91 +1043,6 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   }
 }
 
-// One 256-thread workgroup per token t. h_post of the token from the partials
-// (the arithmetic of token_coeffs: slices in order, the same gate helpers), then
-// the sums over the channels:
-//   dh[i]          = dH_pre[i]     = <dF_in, x_i>
-//   dh[4 + i]      = dH_post[i]    = <dX_next_i, F_out>
-//   dh[8 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>
-// and dF_out = sum_i H_post[i] dX_next_i (rounded once to bfloat16). Thread tid
-// takes the 8-channel chunks tid, tid + 256, ...; the threads' sums are added by
-// a butterfly in each wave and then the 4 waves in order.
-template <int TT>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part,
-                                                         const uint16_t* __restrict__ X,
-                                                         const uint16_t* __restrict__ dXn,
-                                                         const uint16_t* __restrict__ Fo,
-                                                         const uint16_t* __restrict__ dFi, int64_t C, int S,
-                                                         const float* __restrict__ bias, float a_post,
-                                                         float* __restrict__ dh, uint16_t* __restrict__ dFo) {
-  __shared__ float wsum[4][24];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  float hpost[4];
-  {
-    using PG = PartGeom<3, TT>;
-    const int64_t tile = t / TT;
-    const int m = (int)(t - tile * TT);
-    const float* base = part + tile * S * PG::PART + m * PG::PROW;
-    float ss = 0.f, pe[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) {
-      const float* b = base + (int64_t)s * PG::PART;
-      ss += b[PG::NCOLP];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pe[i] += b[4 + i];
-    }
-    const float invr = inv_rms4(ss, C);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hpost[i] = 2.0f * sigmoid(gate_logit(a_post, pe[i], invr, bias[4 + i]));
-  }
-  float acc[24];
-#pragma unroll
-  for (int k = 0; k < 24; ++k) acc[k] = 0.f;
-  const int64_t nch = C / 8;
-  const uint16_t* xr = X + t * NS4 * C;
-  const uint16_t* dr = dXn + t * NS4 * C;
-  for (int64_t j = tid; j < nch; j += 256) {
-    const int64_t c = j * 8;
-    uint4 xq[NS4], dq[NS4];
-#pragma unroll
-    for (int i = 0; i < NS4; ++i) {
-      xq[i] = ld_stream(xr + i * C + c);
-      dq[i] = ld_stream(dr + i * C + c);
-    }
-    const uint4 fq = ld_stream(Fo + t * C + c), gq = ld_stream(dFi + t * C + c);
-    float x[NS4][8], d[NS4][8], f[8], gi[8], o[8];
-#pragma unroll
-    for (int i = 0; i < NS4; ++i) {
-      unpack8(xq[i], x[i]);
-      unpack8(dq[i], d[i]);
-    }
-    unpack8(fq, f);
-    unpack8(gq, gi);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] = hpost[0] * d[0][e] + hpost[1] * d[1][e] + hpost[2] * d[2][e] + hpost[3] * d[3][e];
-#pragma unroll
-      for (int i = 0; i < NS4; ++i) {
-        acc[i] += gi[e] * x[i][e];
-        acc[4 + i] += d[i][e] * f[e];
-#pragma unroll
-        for (int k = 0; k < NS4; ++k) acc[8 + 4 * i + k] += d[i][e] * x[k][e];
-      }
-    }
-    __builtin_nontemporal_store(u32x4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
-                                        pack_bf2_hw(o[6], o[7])},
-                                reinterpret_cast<u32x4_t*>(dFo + t * C + c));
-  }
-#pragma unroll
-  for (int k = 0; k < 24; ++k) acc[k] = wave_sum(acc[k]);
-  if ((tid & 63) == 0) {
-#pragma unroll
-    for (int k = 0; k < 24; ++k) wsum[tid >> 6][k] = acc[k];
-  }
-  __syncthreads();
-  if (tid < 24) dh[t * 24 + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
-}
-
 // ------------------------------------------------------- xHC finish kernels
 
 // xHC full-state pass ([xHC] steps 1 and 2, parameterisation): 32 lanes per
@@ -1656,15 +1571,6 @@ hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const floa
   hipError_t e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st, phi_rows);
   if (e != hipSuccess) return e;
   return launch_wide<3, ROWS_CONTIG>(args(X, T, C, 4 * C, geom(T, C, 1, W_TOK), packed, partial), st);
-}
-
-hipError_t launch_fast_bwd_reduce(const float* partial, const void* X, const void* dX_next, const void* F_out,
-                                  const void* dF_in, int64_t T, int64_t C, const float* bias, float a_post, float* dh,
-                                  void* dF_out, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_reduce_kernel<W_TOK>, dim3((unsigned)T), dim3(256), 0, st, partial, (const uint16_t*)X,
-                     (const uint16_t*)dX_next, (const uint16_t*)F_out, (const uint16_t*)dF_in, C, (int)slices(C), bias,
-                     a_post, dh, (uint16_t*)dF_out);
-  return hipGetLastError();
 }
 
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,

@@ -241,13 +241,13 @@ def test_backward_validation(hc):
     assert L.hc_backward_workspace_bytes(T, 4, C, 0) == -1
     assert L.hc_backward_workspace_bytes(-1, 4, C, 1) == -1
     P = lambda k: ctypes.c_void_p(0x1000000 * (k + 1))  # distinct, far apart, 256-byte aligned
-    names = ["X", "phi", "bias", "Fo", "dXn", "dFi", "dX", "dFo", "dphi", "dbias", "dalpha", "ws"]
+
+    names = ["X", "phi", "bias", "dXn", "dFi", "dh", "dX", "dphi", "dbias", "dalpha", "ws"]
 
     def bwd(dt=1, T=T, n=4, C=C, iters=20, wsb=wsb, **kw):
         p = {nm: kw.get(nm, P(k)) for k, nm in enumerate(names)}
-        return L.hc_backward(p["X"], dt, T, n, C, p["phi"], p["bias"], 0.01, 0.01, 0.01, iters, p["Fo"],
-                             p["dXn"], p["dFi"], p["dX"], p["dFo"], p["dphi"], p["dbias"], p["dalpha"], p["ws"],
-                             wsb, None)
+        return L.hc_backward(p["X"], dt, T, n, C, p["phi"], p["bias"], 0.01, 0.01, 0.01, iters, p["dXn"], p["dFi"],
+                             p["dh"], p["dX"], p["dphi"], p["dbias"], p["dalpha"], p["ws"], wsb, None)
     assert bwd(dt=7) == -3 and bwd(dt=0) == -3
     assert bwd(n=3) == -2 and bwd(C=48) == -2 and bwd(C=0) == -2 and bwd(T=-1) == -2
     assert bwd(iters=0) == -2 and bwd(iters=65) == -2
@@ -256,9 +256,23 @@ def test_backward_validation(hc):
         assert bwd(**{nm: None}) == -1, nm
     assert bwd(X=ctypes.c_void_p(0x1000008)) == -4
     assert bwd(dX=ctypes.c_void_p(0x7000004)) == -4
-    assert bwd(dphi=ctypes.c_void_p(0x9000002)) == -4
-    assert bwd(ws=None) == -8 and bwd(wsb=wsb - 1) == -8 and bwd(ws=ctypes.c_void_p(0xc000010)) == -8
-    assert bwd(dX=ctypes.c_void_p(0x5000000)) == -5  # dX over dX_next
-    assert bwd(dFo=ctypes.c_void_p(0x4000000)) == -5  # dF_out over F_out
-    assert bwd(dbias=ctypes.c_void_p(0x9000010)) == -5  # dbias inside dphi
+    assert bwd(dphi=ctypes.c_void_p(0x8000002)) == -4
+    assert bwd(ws=None) == -8 and bwd(wsb=wsb - 1) == -8 and bwd(ws=ctypes.c_void_p(0xb000010)) == -8
+    assert bwd(dX=ctypes.c_void_p(0x4000000)) == -5  # dX over dX_next
+    assert bwd(dh=ctypes.c_void_p(0x1000000)) == -5  # dh over X
+    assert bwd(dbias=ctypes.c_void_p(0x8000010)) == -5  # dbias inside dphi
     assert bwd(ws=ctypes.c_void_p(0x7000000)) == -5  # workspace over dX
+
+    pn = ["X", "hp", "Fo", "dXn", "dFo", "dh"]
+
+    def post(dt=1, T=T, n=4, C=C, **kw):
+        p = {nm: kw.get(nm, P(k)) for k, nm in enumerate(pn)}
+        return L.hc_backward_post(p["X"], dt, T, n, C, p["hp"], p["Fo"], p["dXn"], p["dFo"], p["dh"], None)
+    assert post(dt=0) == -3 and post(n=2) == -2 and post(C=40) == -2 and post(T=-2) == -2
+    assert post(T=0, X=None) == 0
+    for nm in pn:
+        assert post(**{nm: None}) == -1, nm
+    assert post(hp=ctypes.c_void_p(0x2000004)) == -4  # h_post is read 16 bytes at a time
+    assert post(dh=ctypes.c_void_p(0x6000002)) == -4
+    assert post(dFo=ctypes.c_void_p(0x3000000)) == -5  # dF_out over F_out
+    assert post(dh=ctypes.c_void_p(0x5000010)) == -5  # dh inside dF_out

@@ -2,9 +2,14 @@
 against the fp64 oracle's mhc_sublayer_backward, through the C ABI, on the synth
 recipe's inputs and upstream gradients.
 
+The two stages run as a training step runs them: hc_backward_post (dF_out and
+the map gradients dH_post, dH_res, with the forward's h_post) and then
+hc_backward with dF_in.
+
 Tolerances. dX and dF_out are bfloat16 outputs rounded once from float32: the
 stream bound of the forward tests (relative L2 1e-2, per element max(2e-2, one
-bf16 ulp)). dphi, dbias and dalpha are float32 sums over the tokens of
+bf16 ulp)). The map gradients dh are float32 sums over the channels (relative
+L2 1e-4 as below). dphi, dbias and dalpha are float32 sums over the tokens of
 per-token gradients. Each of those carries float32 sums over the 4C channels,
 20 Sinkhorn steps in reverse and, for dphi, dP split into two bfloat16 parts on
 the matrix cores (16 significant bits, 2^-17 relative per element). That gives
@@ -37,10 +42,18 @@ def _inputs(seed, T, C, alpha=None, phi_scale=1.0):
 
 
 def _gpu(inp, g, iters=20):
-    out = hc.hc_backward(dev(inp["X"]), dev(inp["phi"]), dev(inp["bias"]), [float(a) for a in inp["alpha"]],
-                         dev(inp["F_out"]), dev(g["dX_next"]), dev(g["dF_in"]), iters)
+    """Forward coefficients, then the two backward stages as a training step runs
+    them: the post stage (dF_out, dH_post, dH_res), then the main stage with dF_in."""
+    X = dev(inp["X"])
+    phi, bias = dev(inp["phi"]), dev(inp["bias"])
+    alpha = [float(a) for a in inp["alpha"]]
+    _, h_post, _ = hc.hc_coeffs(X, phi, bias, alpha, iters)
+    dXn = dev(g["dX_next"])
+    dF_out, dh = hc.hc_backward_post(X, h_post, dev(inp["F_out"]), dXn)
+    dX, dphi, dbias, dalpha = hc.hc_backward(X, phi, bias, alpha, dXn, dev(g["dF_in"]), dh, iters)
     torch.cuda.synchronize()
-    return dict(zip(("dX", "dF_out", "dphi", "dbias", "dalpha"), (host64(t) for t in out)))
+    return dict(dX=host64(dX), dF_out=host64(dF_out), dphi=host64(dphi), dbias=host64(dbias), dalpha=host64(dalpha),
+                dh=host64(dh))
 
 
 def _oracle(inp, g, iters=20, rows=None, chunk=None):
@@ -49,7 +62,7 @@ def _oracle(inp, g, iters=20, rows=None, chunk=None):
     T = inp["X"].values.shape[0]
     chunk = chunk or T
     keep = np.arange(T) if rows is None else np.asarray(rows)
-    out = dict(dphi=0.0, dbias=0.0, dalpha=0.0, dX=[], dF_out=[])
+    out = dict(dphi=0.0, dbias=0.0, dalpha=0.0, dX=[], dF_out=[], dh=[])
     for s in range(0, T, chunk):
         sl = slice(s, min(T, s + chunk))
         r = O.mhc_sublayer_backward(inp["X"].values[sl], inp["phi"], inp["bias"], inp["alpha"],
@@ -58,10 +71,10 @@ def _oracle(inp, g, iters=20, rows=None, chunk=None):
         for k in ("dphi", "dbias", "dalpha"):
             out[k] = out[k] + r[k]
         sel = keep[(keep >= sl.start) & (keep < sl.stop)] - sl.start
-        out["dX"].append(r["dX"][sel])
-        out["dF_out"].append(r["dF_out"][sel])
-    out["dX"] = np.concatenate(out["dX"])
-    out["dF_out"] = np.concatenate(out["dF_out"])
+        for k in ("dX", "dF_out", "dh"):
+            out[k].append(r[k][sel])
+    for k in ("dX", "dF_out", "dh"):
+        out[k] = np.concatenate(out[k])
     return out
 
 
@@ -69,6 +82,7 @@ def _compare(got, ref, rows=None):
     sel = slice(None) if rows is None else np.asarray(rows)
     check_bf16("dX", got["dX"][sel], ref["dX"])
     check_bf16("dF_out", got["dF_out"][sel], ref["dF_out"])
+    check_fp32("dh", got["dh"][sel], ref["dh"], BWD_REL)
     errs = {k: check_fp32(k, got[k], ref[k], BWD_REL) for k in ("dphi", "dbias", "dalpha")}
     note(f"relative L2: {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
 
@@ -110,7 +124,7 @@ def test_backward_zero_state_tokens():
 
 
 def test_backward_deterministic():
-    """Every sum runs in a fixed order: two calls give the same bits."""
+    """Every sum runs in a fixed order: two runs give the same bits."""
     note("hc_backward determinism C=1024 T=300")
     inp, g = _inputs(440, 300, 1024)
     a, b = _gpu(inp, g), _gpu(inp, g)
