@@ -498,3 +498,101 @@ def mhc_sublayer_backward(X, phi, bias, alpha, F_out, dX_next, dF_in, sinkhorn_i
     dX = dX + dx.reshape(T, n, C)
     dh = np.concatenate([dh_pre, dh_post, dh_res.reshape(T, n * n)], axis=1)
     return dict(dX=dX, dF_out=dF_out, dphi=dphi, dbias=dbias, dalpha=dalpha, dz=dz, dh=dh)
+
+
+# ---------------------------------------------------------------------------
+# xHC backward (gradients of the routed step)
+# ---------------------------------------------------------------------------
+
+def _gates_backward(dz, P, rho, gate, x, phi, N):
+    """The shared tail of the gated-projection backward (Eq. 14-16 pattern):
+    z = gate * P * rho + b with P = x phi and rho = 1/r = (||x||^2 / N)^(-1/2).
+    Returns (d x [T, N], dphi, dbias, per-column dz P rho summed over tokens)."""
+    ss = np.sum(x * x, axis=-1)
+    dP = dz * gate[None, :] * rho[:, None]
+    drho = np.sum(dz * gate[None, :] * P, axis=-1)
+    dss = np.where(ss > 0.0, -0.5 * drho * rho ** 3 / N, 0.0)
+    dx = dP @ phi.T + 2.0 * dss[:, None] * x
+    return dx, x.T @ dP, dz.sum(axis=0), (dz * P * rho[:, None]).sum(axis=0)
+
+
+def _rho(x):
+    r = np.sqrt(np.mean(x * x, axis=-1))
+    return np.where(r > 0.0, 1.0 / np.where(r > 0.0, r, 1.0), 0.0)
+
+
+def xhc_route_backward(X, idx, phi_act, b_act, alpha_post, alpha_res, Wb, dX_next, sinkhorn_iters: int = 20):
+    """Gradients of xhc_route for the upstream gradient dX_next [T, N, C].
+
+    xHC summary step 3 with the parameterisation: on the active rows (slot order)
+    the route is the mHC post/res write X_A_new = H_res_A X_A + H_post_A Wb with
+    maps formed from the active state alone (r_A over k C), so its backward is
+    the chain rule of mhc_sublayer_backward without the pre map: dWb = H_post_A^T
+    dX_next_A, dH_post_A[a, j] = <dX_next_a, Wb_j>, dH_res_A[a, b] = <dX_next_a,
+    x_b>, dx_A = H_res_A^T dX_next_A, then 2 sigma' and the Sinkhorn backward, the
+    gates, the RMS factor and the projection. Rows not in idx pass through, so
+    their gradient is dX_next itself; the active rows are replaced, so theirs is
+    dx_A alone. idx is a constant (a discrete choice).
+    Returns dict(dX [T, N, C], dWb [T, K, C], dphi_act, db_act, dalpha_post,
+    dalpha_res, dh [T, k*K + k*k] = [dH_post (a*K + j) | dH_res (a*k + b)]).
+    """
+    X = _f64(X)
+    idx = np.asarray(idx)
+    Wb = _f64(Wb)
+    if Wb.ndim == 2:
+        Wb = Wb[:, None, :]
+    T, N, C = X.shape
+    k, K = idx.shape[1], Wb.shape[1]
+    X_A = xhc_gather(X, idx)
+    x = X_A.reshape(T, k * C)
+    phi = _f64(phi_act)
+    rho = _rho(x)
+    P = x @ phi
+    gate = np.concatenate([np.full(k * K, float(alpha_post)), np.full(k * k, float(alpha_res))])
+    z = gate[None, :] * P * rho[:, None] + _f64(b_act)[None, :]
+    s_post = sigmoid(z[:, :k * K]).reshape(T, k, K)
+    H_post = 2.0 * s_post
+    z_res = z[:, k * K:].reshape(T, k, k)
+    H_res = sinkhorn_knopp(z_res, sinkhorn_iters)
+    dXn_A = xhc_gather(dX_next, idx)
+    dWb = np.einsum("taj,tac->tjc", H_post, dXn_A)
+    dH_post = np.einsum("tac,tjc->taj", dXn_A, Wb)
+    dH_res = np.einsum("tac,tbc->tab", dXn_A, X_A)
+    dX_A = np.einsum("tab,tac->tbc", H_res, dXn_A)
+    dz = np.concatenate([(dH_post * 2.0 * s_post * (1.0 - s_post)).reshape(T, k * K),
+                         sinkhorn_knopp_backward(z_res, dH_res, sinkhorn_iters).reshape(T, k * k)], axis=1)
+    dx, dphi, dbias, u = _gates_backward(dz, P, rho, gate, x, phi, k * C)
+    dX_A = dX_A + dx.reshape(T, k, C)
+    dX = _f64(dX_next).copy()
+    dX[np.arange(T)[:, None], idx] = dX_A
+    dh = np.concatenate([dH_post.reshape(T, k * K), dH_res.reshape(T, k * k)], axis=1)
+    return dict(dX=dX, dWb=dWb, dphi_act=dphi, db_act=dbias, dalpha_post=u[:k * K].sum(),
+                dalpha_res=u[k * K:].sum(), dh=dh)
+
+
+def xhc_pre_backward(X, phi_pre, b_pre, alpha_pre, dF_in):
+    """Gradients of xhc_pre's dense read F_in = sum_i h_pre_i x_i for the upstream
+    gradient dF_in [T, C].
+
+    xHC summary step 2 with h_pre = sigma(alpha_pre (vec X) phi_pre / r + b_pre),
+    r over the whole N C state (as xhc_pre). dH_pre[i] = <dF_in, x_i>, dx_i +=
+    H_pre[i] dF_in, then sigma', the gate, the RMS factor and the projection.
+    Reading: the router's scores only choose the active set (they scale nothing),
+    and the choice is discrete, so the router weights receive no gradient.
+    Returns dict(dX [T, N, C], dphi_pre [NC, N], db_pre [N], dalpha_pre,
+    dh_pre [T, N]).
+    """
+    X = _f64(X)
+    T, N, C = X.shape
+    x = X.reshape(T, N * C)
+    phi = _f64(phi_pre)
+    rho = _rho(x)
+    P = x @ phi
+    gate = np.full(N, float(alpha_pre))
+    h = sigmoid(gate[None, :] * P * rho[:, None] + _f64(b_pre)[None, :])
+    dFi = _f64(dF_in)
+    dh_pre = np.einsum("tc,tic->ti", dFi, X)
+    dX = h[:, :, None] * dFi[:, None, :]
+    dz = dh_pre * h * (1.0 - h)
+    dx, dphi, dbias, u = _gates_backward(dz, P, rho, gate, x, phi, N * C)
+    return dict(dX=dX + dx.reshape(T, N, C), dphi_pre=dphi, db_pre=dbias, dalpha_pre=u.sum(), dh_pre=dh_pre)

@@ -735,3 +735,87 @@ def test_sublayer_backward_zero_state_and_bias_gradient():
     np.testing.assert_array_equal(g["dphi"], 0.0)
     np.testing.assert_allclose(g["dbias"], g["dz"].sum(axis=0), rtol=1e-15)
     np.testing.assert_array_equal(g["dalpha"], 0.0)
+
+
+@pytest.mark.parametrize("N,k,K,C", [(6, 3, 1, 3), (5, 2, 2, 4)])
+def test_route_backward_finite_differences(N, k, K, C):
+    """xhc_route_backward against central differences of L = <dX_next, X_next>
+    through xhc_route with the active set held fixed (a discrete choice): state,
+    phi_act, b_act, both gates and the write-back components."""
+    rng = np.random.default_rng(340 + N + K)
+    T = 2
+    X = rng.standard_normal((T, N, C))
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(T)])
+    phi = 0.3 * rng.standard_normal((k * C, k * K + k * k))
+    b = 0.5 * rng.standard_normal(k * K + k * k)
+    ap, ar = 0.8, 1.1
+    Wb = rng.standard_normal((T, K, C))
+    dXn = rng.standard_normal((T, N, C))
+    g = O.xhc_route_backward(X, idx, phi, b, ap, ar, Wb, dXn, 20)
+
+    def L(X, phi, b, ap, ar, Wb):
+        return np.sum(dXn * O.xhc_route(X, idx, phi, b, ap, ar, Wb, 20)[0])
+    cases = [("dX", X, lambda a: L(a, phi, b, ap, ar, Wb)), ("dphi_act", phi, lambda a: L(X, a, b, ap, ar, Wb)),
+             ("db_act", b, lambda a: L(X, phi, a, ap, ar, Wb)), ("dWb", Wb, lambda a: L(X, phi, b, ap, ar, a))]
+    for name, arr, f in cases:
+        want = _central_difference(f, arr)
+        np.testing.assert_allclose(g[name], want, rtol=0, atol=1e-7 * np.abs(want).max(), err_msg=name)
+    for name, v, f in (("dalpha_post", ap, lambda a: L(X, phi, b, a[0], ar, Wb)),
+                       ("dalpha_res", ar, lambda a: L(X, phi, b, ap, a[0], Wb))):
+        want = _central_difference(f, np.array([v]))[0]
+        assert math.isclose(g[name], want, rel_tol=1e-6), name
+    # the rows the route does not touch pass the upstream gradient through unchanged
+    inactive = np.ones((T, N), bool)
+    inactive[np.arange(T)[:, None], idx] = False
+    np.testing.assert_array_equal(g["dX"][inactive], dXn[inactive])
+
+
+def test_pre_backward_finite_differences_and_router():
+    """xhc_pre_backward against central differences of L = <dF_in, F_in> through
+    xhc_pre (state, phi_pre, b_pre, the gate); the router's weights change F_in
+    not at all while the active set stays the same, so they get no gradient."""
+    rng = np.random.default_rng(350)
+    T, N, C = 2, 6, 3
+    X = rng.standard_normal((T, N, C))
+    phi = 0.3 * rng.standard_normal((N * C, N))
+    b = 0.5 * rng.standard_normal(N)
+    a0 = 0.9
+    dFi = rng.standard_normal((T, C))
+    g = O.xhc_pre_backward(X, phi, b, a0, dFi)
+
+    def L(X, phi, b, a0):
+        return np.sum(dFi * O.xhc_pre(X, phi, b, a0)["F_in"])
+    for name, arr, f in (("dX", X, lambda a: L(a, phi, b, a0)), ("dphi_pre", phi, lambda a: L(X, a, b, a0)),
+                         ("db_pre", b, lambda a: L(X, phi, a, a0))):
+        want = _central_difference(f, arr)
+        np.testing.assert_allclose(g[name], want, rtol=0, atol=1e-7 * np.abs(want).max(), err_msg=name)
+    assert math.isclose(g["dalpha_pre"], _central_difference(lambda a: L(X, phi, b, a[0]), np.array([a0]))[0],
+                        rel_tol=1e-6)
+    W = rng.standard_normal((N * C, N - 2))
+    F0 = O.xhc_pre(X, phi, b, a0, W, 3, 2)["F_in"]
+    F1 = O.xhc_pre(X, phi, b, a0, W + 1e-3 * rng.standard_normal(W.shape), 3, 2)["F_in"]
+    np.testing.assert_array_equal(F0, F1)
+
+
+def test_route_backward_with_every_stream_active_is_the_mhc_backward():
+    """k = N with the identity active set: the route is the mHC post/res write, so
+    its gradients equal mhc_sublayer_backward's with a zero pre map, dF_in = 0 and
+    phi = [any pre columns | phi_act]."""
+    rng = np.random.default_rng(360)
+    T, n, C = 3, 4, 5
+    X = rng.standard_normal((T, n, C))
+    phi_act = 0.3 * rng.standard_normal((n * C, n + n * n))
+    b_act = 0.5 * rng.standard_normal(n + n * n)
+    F = rng.standard_normal((T, C))
+    dXn = rng.standard_normal((T, n, C))
+    idx = np.tile(np.arange(n), (T, 1))
+    g = O.xhc_route_backward(X, idx, phi_act, b_act, 0.7, 1.2, F, dXn, 20)
+    phi = np.concatenate([rng.standard_normal((n * C, n)), phi_act], axis=1)
+    bias = np.concatenate([np.zeros(n), b_act])
+    ref = O.mhc_sublayer_backward(X, phi, bias, (0.5, 0.7, 1.2), F, dXn, np.zeros((T, C)), 20)
+    np.testing.assert_allclose(g["dX"], ref["dX"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dWb"][:, 0], ref["dF_out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dphi_act"], ref["dphi"][:, n:], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["db_act"], ref["dbias"][n:], rtol=1e-12, atol=1e-12)
+    assert math.isclose(g["dalpha_post"], ref["dalpha"][1], rel_tol=1e-12)
+    assert math.isclose(g["dalpha_res"], ref["dalpha"][2], rel_tol=1e-12)
