@@ -288,6 +288,47 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
               int32_t* idx_out, float* score_out, float* h_post_out, float* h_res_out,
               void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * xhc_route_backward, xhc_pre_backward - gradients of the routed xHC step
+ * (xhc_pre, then xhc_route with K = 1), the backward of [xHC] steps 2 and 3 with
+ * the parameterisation: on the active rows the route is the mHC post/res write
+ * with maps formed from the active state alone, so its backward follows the
+ * mHC one ([mHC] 4.3.1: the Sinkhorn backward recomputes the iterates on chip;
+ * the maps are recomputed from X). The active set is a discrete choice: it and
+ * the router weights receive no gradient.
+ *   X [T, N, C]: the state both forward calls read, i.e. before xhc_route's
+ *   in-place update (keep it, or its active rows, for the backward).
+ *   xhc_route_backward (first; it does not need dF_in): dX [T, N, C] holds the
+ *     upstream gradient dX_next on entry and the route's gradient on exit: rows
+ *     outside the active set are left as they are (they pass through); the
+ *     active rows become H_res_A^T dX_next_A plus the maps' terms. Also
+ *     dWb [T, C] = H_post_A^T dX_next_A (the gradient of F_out), dphi_act
+ *     [4C, 20], db_act [20], dalpha [2] (post, res), dh [T, 20] = the map
+ *     gradients [dH_post (a) | dH_res (4a + b)]. idx [T, 4] as the forward used
+ *     (int32, 16-byte aligned); phi_act, b_act, alpha_*, sinkhorn_iters as for
+ *     xhc_route; Wb = F_out [T, C].
+ *   xhc_pre_backward (once dF_in, the gradient of F_in, is known): adds the
+ *     dense read's gradient to dX (in place), and writes dphi_pre [NC, N],
+ *     db_pre [N], dalpha [1], dh_pre [T, N] = <dF_in, x_i> (16-byte aligned).
+ *   Covered: dtype HC_BF16 (HC_F32 -> HC_ERR_DTYPE), N a multiple of 4 up to 16,
+ *   k = 4, K = 1, C a multiple of 32, 1 <= sinkhorn_iters <= HC_MAX_BWD_ITERS
+ *   (else HC_ERR_SHAPE). bfloat16 arrays 16 bytes aligned, float arrays 4;
+ *   workspace 256 bytes, at least xhc_backward_workspace_bytes (both calls).
+ *   dX overlaps nothing else; no output overlaps an input, another output or
+ *   the workspace (HC_ERR_ALIAS). Deterministic: every sum runs in a fixed order.
+ *   xhc_backward_workspace_bytes: 0 for T = 0, -1 for what the calls do not cover.
+ */
+int64_t xhc_backward_workspace_bytes(int64_t T, int N, int64_t C, int k, int K, int dtype);
+int xhc_route_backward(const void* X, int dtype, int64_t T, int N, int64_t C, int k, const int32_t* idx,
+                       const float* phi_act, const float* b_act, float alpha_post, float alpha_res,
+                       int sinkhorn_iters, const void* Wb, int K, void* dX, void* dWb, float* dphi_act,
+                       float* db_act, float* dalpha, float* dh, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+int xhc_pre_backward(const void* X, int dtype, int64_t T, int N, int64_t C, const float* phi_pre,
+                     const float* b_pre, float alpha_pre, const void* dF_in, void* dX, float* dphi_pre,
+                     float* db_pre, float* dalpha, float* dh_pre, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
 /* Workspace bytes needed by xhc_augment (0 when it needs none); -1 for invalid sizes. */
 int64_t xhc_augment_workspace_bytes(int64_t B, int64_t S, int64_t C, const int* kappa, int r, int dtype,
                                     int v_dtype);

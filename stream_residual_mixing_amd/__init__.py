@@ -54,6 +54,11 @@ _SIGS = {
                            _vp]),
     "xhc_augment_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int, _c_int]),
     "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
+    "xhc_backward_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
+    "xhc_route_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _c_float, _c_float,
+                                    _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "xhc_pre_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _c_i64, _vp]),
     "hc_copy_probe": (_c_int, [_vp, _vp, _c_i64, _vp]),
     "hc_tanh_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float,
                                 _vp, _vp, _vp, _vp]),
@@ -453,6 +458,54 @@ def hc_static_post(X, h_res, h_post, F_out, *, out=None, stream=None):
     return Y
 
 
+def xhc_backward_workspace_bytes(T: int, N: int, C: int, k: int, K: int, dtype) -> int:
+    return int(lib().xhc_backward_workspace_bytes(T, N, C, k, K, _DT[dtype]))
+
+
+def xhc_route_backward(X, idx, phi_act, b_act, alpha_post, alpha_res, F_out, dX, sinkhorn_iters=20, *, out=None,
+                       workspace=None, stream=None):
+    """Backward of xhc_route (k = 4, K = 1, bfloat16). X: the state before the route;
+    dX holds dX_next and is updated in place to the route's gradient. Returns
+    (dX, dF_out, dphi_act, db_act, dalpha [post, res], dh [T, 20])."""
+    X = _dev_tensor(X, "X", (torch.bfloat16,))
+    T, N, C = X.shape
+    idx = _dev_tensor(idx, "idx", (torch.int32,))
+    k = idx.shape[1]
+    F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
+    dX = _dev_tensor(dX, "dX", (X.dtype,))
+    if out is None:
+        dev = X.device
+        out = (torch.empty(T, C, dtype=X.dtype, device=dev), torch.empty(k * C, k + k * k, device=dev),
+               torch.empty(k + k * k, device=dev), torch.empty(2, device=dev), torch.empty(T, k + k * k, device=dev))
+    dF_out, dphi, db, dalpha, dh = out
+    ws = _workspace(xhc_backward_workspace_bytes(T, N, C, k, 1, X.dtype), X.device, workspace)
+    _check("xhc_route_backward", lib().xhc_route_backward(
+        _ptr(X), _DT[X.dtype], T, N, C, k, _ptr(idx), _ptr(_f32(phi_act, "phi_act")), _ptr(_f32(b_act, "b_act")),
+        float(alpha_post), float(alpha_res), int(sinkhorn_iters), _ptr(F_out), 1, _ptr(dX), _ptr(dF_out), _ptr(dphi),
+        _ptr(db), _ptr(dalpha), _ptr(dh), _ptr(ws), ws.numel(), _stream(X.device, stream)))
+    return dX, dF_out, dphi, db, dalpha, dh
+
+
+def xhc_pre_backward(X, phi_pre, b_pre, alpha_pre, dF_in, dX, *, out=None, workspace=None, stream=None):
+    """Backward of xhc_pre's dense read (bfloat16): dX += its gradient (in place).
+    Returns (dX, dphi_pre, db_pre, dalpha [1], dh_pre [T, N])."""
+    X = _dev_tensor(X, "X", (torch.bfloat16,))
+    T, N, C = X.shape
+    dF_in = _dev_tensor(dF_in, "dF_in", (X.dtype,))
+    dX = _dev_tensor(dX, "dX", (X.dtype,))
+    if out is None:
+        dev = X.device
+        out = (torch.empty(N * C, N, device=dev), torch.empty(N, device=dev), torch.empty(1, device=dev),
+               torch.empty(T, N, device=dev))
+    dphi, db, dalpha, dh = out
+    ws = _workspace(xhc_backward_workspace_bytes(T, N, C, 4, 1, X.dtype), X.device, workspace)
+    _check("xhc_pre_backward", lib().xhc_pre_backward(
+        _ptr(X), _DT[X.dtype], T, N, C, _ptr(_f32(phi_pre, "phi_pre")), _ptr(_f32(b_pre, "b_pre")), float(alpha_pre),
+        _ptr(dF_in), _ptr(dX), _ptr(dphi), _ptr(db), _ptr(dalpha), _ptr(dh), _ptr(ws), ws.numel(),
+        _stream(X.device, stream)))
+    return dX, dphi, db, dalpha, dh
+
+
 def hc_copy_probe(src, dst, *, stream=None):
     """Copy src into dst (same byte size, 16-byte aligned) with the library's streaming
     copy: a measurement probe of the device's streaming rate, not part of the method."""
@@ -467,7 +520,8 @@ def hc_copy_probe(src, dst, *, stream=None):
 
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
-    "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward_post", "hc_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
+    "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward_post", "hc_backward", "xhc_backward_workspace_bytes",
+    "xhc_route_backward", "xhc_pre_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
     "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",

@@ -309,6 +309,91 @@ int hc_backward(const void* X, int dtype, int64_t T, int n, int64_t C, const flo
                                                 workspace, (hipStream_t)stream));
 }
 
+int64_t xhc_backward_workspace_bytes(int64_t T, int N, int64_t C, int k, int K, int dtype) {
+  if (T < 0) return -1;
+  if (T == 0) return 0;
+  if (!hc::fast_xhc_backward_supported(dtype, N, k, K, T, C, 1)) return -1;
+  return hc::fast_xhc_backward_ws_bytes(T, N, C);
+}
+
+// the shapes both xHC backward calls cover (T >= 0)
+static int check_xhc_backward_shape(int dtype, int64_t T, int N, int64_t C) {
+  if (!dtype_ok(dtype) || dtype != HC_BF16) return HC_ERR_DTYPE;
+  if (T < 0 || N < 4 || N > 16 || N % 4 != 0 || C < 32 || C % 32 != 0 || C > (1ll << 26)) return HC_ERR_SHAPE;
+  return HC_OK;
+}
+
+int xhc_route_backward(const void* X, int dtype, int64_t T, int N, int64_t C, int k, const int32_t* idx,
+                       const float* phi_act, const float* b_act, float alpha_post, float alpha_res,
+                       int sinkhorn_iters, const void* Wb, int K, void* dX, void* dWb, float* dphi_act,
+                       float* db_act, float* dalpha, float* dh, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+  int s = check_xhc_backward_shape(dtype, T, N, C);
+  if (s != HC_OK) return s;
+  if (k != 4 || K != 1 || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_BWD_ITERS) return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!hc::fast_xhc_backward_supported(dtype, N, k, K, T, C, sinkhorn_iters)) return HC_ERR_SHAPE;
+  if (!X || !idx || !phi_act || !b_act || !Wb || !dX || !dWb || !dphi_act || !db_act || !dalpha || !dh)
+    return HC_ERR_NULL;
+  for (const void* p : {X, Wb, (const void*)dX, (const void*)dWb, (const void*)idx})
+    if (!aligned_to(p, 16)) return HC_ERR_ALIGN;
+  for (const void* p : {(const void*)phi_act, (const void*)b_act, (const void*)dphi_act, (const void*)db_act,
+                        (const void*)dalpha, (const void*)dh})
+    if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
+  const int64_t wsb = hc::fast_xhc_backward_ws_bytes(T, N, C);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t xb = T * N * C * 2, fb = T * C * 2, pb = 4 * C * 20 * 4;
+  // dX is read and written: it may overlap nothing else
+  const void* ins[6] = {X, idx, phi_act, b_act, Wb, dX};
+  const int64_t ib[6] = {xb, T * 4 * 4, pb, 20 * 4, fb, xb};
+  const void* outs[6] = {dWb, dphi_act, db_act, dalpha, dh, workspace};
+  const int64_t ob[6] = {fb, pb, 20 * 4, 2 * 4, T * 20 * 4, wsb};
+  if (any_overlap(outs, ob, 6, ins, ib, 6)) return HC_ERR_ALIAS;
+  {
+    const void* i2[5] = {X, idx, phi_act, b_act, Wb};
+    const int64_t b2[5] = {xb, T * 4 * 4, pb, 20 * 4, fb};
+    const void* o2[1] = {dX};
+    const int64_t ob2[1] = {xb};
+    if (any_overlap(o2, ob2, 1, i2, b2, 5)) return HC_ERR_ALIAS;
+  }
+  if ((s = device_status()) != HC_OK) return s;
+  return launch_status(hc::launch_fast_xroute_backward(X, T, N, C, idx, phi_act, b_act, alpha_post, alpha_res,
+                                                       sinkhorn_iters, Wb, dX, dWb, dphi_act, db_act, dalpha, dh,
+                                                       workspace, (hipStream_t)stream));
+}
+
+int xhc_pre_backward(const void* X, int dtype, int64_t T, int N, int64_t C, const float* phi_pre, const float* b_pre,
+                     float alpha_pre, const void* dF_in, void* dX, float* dphi_pre, float* db_pre, float* dalpha,
+                     float* dh_pre, void* workspace, int64_t workspace_bytes, void* stream) {
+  int s = check_xhc_backward_shape(dtype, T, N, C);
+  if (s != HC_OK || T == 0) return s;
+  if (!hc::fast_xhc_backward_supported(dtype, N, 4, 1, T, C, 1)) return HC_ERR_SHAPE;
+  if (!X || !phi_pre || !b_pre || !dF_in || !dX || !dphi_pre || !db_pre || !dalpha || !dh_pre) return HC_ERR_NULL;
+  for (const void* p : {X, dF_in, (const void*)dX, (const void*)dh_pre})
+    if (!aligned_to(p, 16)) return HC_ERR_ALIGN;
+  for (const void* p : {(const void*)phi_pre, (const void*)b_pre, (const void*)dphi_pre, (const void*)db_pre,
+                        (const void*)dalpha})
+    if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
+  const int64_t wsb = hc::fast_xhc_backward_ws_bytes(T, N, C);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t xb = T * N * C * 2, fb = T * C * 2, pb = (int64_t)N * C * N * 4;
+  const void* ins[5] = {X, phi_pre, b_pre, dF_in, dX};
+  const int64_t ib[5] = {xb, pb, N * 4, fb, xb};
+  const void* outs[5] = {dphi_pre, db_pre, dalpha, dh_pre, workspace};
+  const int64_t ob[5] = {pb, N * 4, 4, T * N * 4, wsb};
+  if (any_overlap(outs, ob, 5, ins, ib, 5)) return HC_ERR_ALIAS;
+  {
+    const void* i2[4] = {X, phi_pre, b_pre, dF_in};
+    const int64_t b2[4] = {xb, pb, N * 4, fb};
+    const void* o2[1] = {dX};
+    const int64_t ob2[1] = {xb};
+    if (any_overlap(o2, ob2, 1, i2, b2, 4)) return HC_ERR_ALIAS;
+  }
+  if ((s = device_status()) != HC_OK) return s;
+  return launch_status(hc::launch_fast_xpre_backward(X, T, N, C, phi_pre, b_pre, alpha_pre, dF_in, dX, dphi_pre,
+                                                     db_pre, dalpha, dh_pre, workspace, (hipStream_t)stream));
+}
+
 int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
             const float* h_post, const void* F_out, void* X_next, void* stream) {
   int s = check_mhc_common(X, dtype, T, n, C);

@@ -38,6 +38,31 @@ constexpr int BCOL = 24;  // n*n + 2n columns: [pre 4 | post 4 | res 16]
 constexpr int DPS = 32;   // floats per dP row (columns 24..31 zero)
 constexpr int RED = 28;   // floats per row of the per-token sums
 
+// Row modes of the passes: which stream row of a token slot i (of 4) is, and
+// which phi rows it multiplies.
+//  BM_MHC:   the n = 4 state: row t*4 + i, phi rows i*C + c;
+//  BM_ROUTE: the xHC active set: row t*N + idx[t*4 + i] (slot order), phi rows
+//            i*C + c (phi_act is in slot order); updated in place;
+//  BM_PRE:   stream group g = blockIdx.z of an N-stream state: row t*N + 4g + i,
+//            phi rows (4g + i)*C + c.
+constexpr int BM_MHC = 0, BM_ROUTE = 1, BM_PRE = 2;
+
+// stream index of slot i of token t (loaded from idx for BM_ROUTE and clamped
+// into [0, N), so no index reaches outside the token's row)
+template <int BM>
+__device__ __forceinline__ void slot_streams(const int32_t* idx, int64_t t, int N, int (&s)[4]) {
+  if constexpr (BM == BM_ROUTE) {
+    const int4 v = reinterpret_cast<const int4*>(idx)[t];
+    const int w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = w[i] < 0 ? 0 : (w[i] >= N ? N - 1 : w[i]);
+  } else {
+    const int g0 = BM == BM_PRE ? 4 * (int)blockIdx.z : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = g0 + i;
+  }
+}
+
 __device__ __forceinline__ bf8_t bf8(const uint4& q) { return __builtin_bit_cast(bf8_t, q); }
 
 __device__ __forceinline__ uint4 ld_nt16(const uint16_t* p) {
@@ -67,17 +92,22 @@ __device__ __forceinline__ void split_bf8(const float v[8], uint4& hi, uint4& lo
 
 // ------------------------------------------------------- per-token sums
 
-// One 256-thread workgroup per token t (post stage): dF_out = sum_i H_post[i]
-// dX_next_i (rounded once to bfloat16) and the sums over the channels
-//   dh[4 + i]      = dH_post[i]    = <dX_next_i, F_out>
-//   dh[8 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>.
-// Thread tid takes the 8-channel chunks tid, tid + 256, ...; the threads' sums
-// are added by a butterfly in each wave and then the 4 waves in order.
+// One 256-thread workgroup per token t (post stage), over the 4 slots of the
+// row mode (the n = 4 state, or the xHC active set with the write-back F_out):
+// dF_out = sum_i H_post[i] dX_next_i (rounded once to bfloat16) and the sums
+// over the channels
+//   dh[off + i]          = dH_post[i]    = <dX_next_i, F_out>
+//   dh[off + 4 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>
+// (dh rows of dhs floats). Thread tid takes the 8-channel chunks tid,
+// tid + 256, ...; the threads' sums are added by a butterfly in each wave and
+// then the 4 waves in order.
+template <int BM>
 __global__ __launch_bounds__(256) void bwd_post_kernel(const uint16_t* __restrict__ X,
                                                        const uint16_t* __restrict__ dXn,
-                                                       const uint16_t* __restrict__ Fo, int64_t C,
+                                                       const uint16_t* __restrict__ Fo, int64_t C, int N,
+                                                       const int32_t* __restrict__ idx,
                                                        const float* __restrict__ h_post, float* __restrict__ dh,
-                                                       uint16_t* __restrict__ dFo) {
+                                                       int dhs, int off, uint16_t* __restrict__ dFo) {
   __shared__ float wsum[4][20];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -87,15 +117,15 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const uint16_t* __restric
 #pragma unroll
   for (int k = 0; k < 20; ++k) acc[k] = 0.f;
   const int64_t nch = C / 8;
-  const uint16_t* xr = X + t * BS * C;
-  const uint16_t* dr = dXn + t * BS * C;
+  int sl[4];
+  slot_streams<BM>(idx, t, N, sl);
   for (int64_t j = tid; j < nch; j += 256) {
     const int64_t c = j * 8;
     uint4 xq[BS], dq[BS];
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
-      xq[i] = ld_nt16(xr + i * C + c);
-      dq[i] = ld_nt16(dr + i * C + c);
+      xq[i] = ld_nt16(X + (t * N + sl[i]) * C + c);
+      dq[i] = ld_nt16(dXn + (t * N + sl[i]) * C + c);
     }
     const uint4 fq = ld_nt16(Fo + t * C + c);
     float x[BS][8], d[BS][8], f[8], o[8];
@@ -126,43 +156,47 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const uint16_t* __restric
     for (int k = 0; k < 20; ++k) wsum[tid >> 6][k] = acc[k];
   }
   __syncthreads();
-  if (tid < 20) dh[t * BCOL + 4 + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+  if (tid < 20) dh[t * dhs + off + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // One 256-thread workgroup per token t (main stage): dh[i] = dH_pre[i] =
-// <dF_in, x_i>, summed as in bwd_post_kernel.
+// <dF_in, x_i> for the NS streams of the token's row (dh rows of dhs floats),
+// summed as in bwd_post_kernel.
+template <int NS>
 __global__ __launch_bounds__(256) void bwd_pre_sums_kernel(const uint16_t* __restrict__ X,
                                                            const uint16_t* __restrict__ dFi, int64_t C,
-                                                           float* __restrict__ dh) {
-  __shared__ float wsum[4][4];
+                                                           float* __restrict__ dh, int dhs) {
+  __shared__ float wsum[4][NS];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) acc[i] = 0.f;
   const int64_t nch = C / 8;
-  const uint16_t* xr = X + t * BS * C;
+  const uint16_t* xr = X + t * NS * C;
   for (int64_t j = tid; j < nch; j += 256) {
     const int64_t c = j * 8;
-    uint4 xq[BS];
+    uint4 xq[NS];
 #pragma unroll
-    for (int i = 0; i < BS; ++i) xq[i] = ld_nt16(xr + i * C + c);
+    for (int i = 0; i < NS; ++i) xq[i] = ld_nt16(xr + i * C + c);
     const uint4 gq = ld_nt16(dFi + t * C + c);
     float x[8], g[8];
     unpack_bf8(gq, g);
 #pragma unroll
-    for (int i = 0; i < BS; ++i) {
+    for (int i = 0; i < NS; ++i) {
       unpack_bf8(xq[i], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[i] += g[e] * x[e];
     }
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) acc[k] = wave_sum(acc[k]);
+  for (int k = 0; k < NS; ++k) acc[k] = wave_sum(acc[k]);
   if ((tid & 63) == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) wsum[tid >> 6][k] = acc[k];
+    for (int k = 0; k < NS; ++k) wsum[tid >> 6][k] = acc[k];
   }
   __syncthreads();
-  if (tid < 4) dh[t * BCOL + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+  if (tid < NS) dh[t * dhs + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // ------------------------------------------------------------------- dX
@@ -171,33 +205,41 @@ constexpr int XT = 32;        // tokens per item
 constexpr int XCH = 128;      // channels per item
 constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product tile in LDS
 
-// dX over items of 32 tokens x 128 channels x 4 streams, 512 threads. The grid
-// is (chunk, group): workgroup (c, j) keeps the channel chunk c and walks the
-// token tiles j, j + J, ... (J = gridDim.y), so its phi fragments load once.
-// Everything a tile needs from memory is loaded one tile ahead into a second
-// register set: thread (token tid >> 4, channels (tid & 15) * 8) takes its
-// 16-byte pieces of x and dX_next in the 4 streams and of dF_in; threads
-// tid < 192 one 16-byte piece of the tile's coefficients [h_res 16 | h_pre 4 |
-// g2 | 0 0 0] and threads tid < 256 one of its dP rows, both staged in LDS at
-// the start of the tile. Per tile:
-//  * MFMA phase: wave w forms dP phi^T for stream w >> 1, the four 16-channel
+// dX over items of 32 tokens x 128 channels x the 4 slots of the row mode, 512
+// threads. The grid is (chunk, group[, stream group for BM_PRE]): workgroup
+// (c, j) keeps the channel chunk c and walks the token tiles j, j + J, ...
+// (J = gridDim.y), so its phi fragments load once. Everything a tile needs
+// from memory is loaded one tile ahead into a second register set: thread
+// (token tid >> 4, channels (tid & 15) * 8) takes its 16-byte pieces of x and
+// dX_next in the 4 slots and of dF_in; threads tid < 192 one 16-byte piece of
+// the tile's coefficients [h_res 16 | h_pre 4 | g2 | 0 0 0] and threads
+// tid < 256 one of its dP rows, both staged in LDS at the start of the tile.
+// Per tile:
+//  * MFMA phase: wave w forms dP phi^T for slot w >> 1, the four 16-channel
 //    blocks (w & 1) * 4 .. + 3 and both 16-token blocks
 //    (v_mfma_f32_16x16x32_bf16; A = the tokens' dP rows split hi/lo, B = the
 //    channels' phi rows hi/lo; hi*hi + hi*lo + lo*hi into one float32
 //    accumulator) into the LDS product tile; then the next tile's loads are
 //    issued;
-//  * streaming phase: dX_j = sum_i H_res[i, j] dX_next_i + H_pre[j] dF_in +
-//    (dP phi^T)_j + g2 x_j, rounded once to bfloat16 and stored.
+//  * streaming phase, slot j:
+//      BM_MHC:   dX_j = sum_i H_res[i, j] dX_next_i + H_pre[j] dF_in + (dP phi^T)_j + g2 x_j
+//      BM_ROUTE: dX_j = sum_i H_res[i, j] dX_next_i + (dP phi^T)_j + g2 x_j, written over
+//                dX_next's row (the same memory)
+//      BM_PRE:   dX_j += H_pre[j] dF_in + (dP phi^T)_j + g2 x_j (dX_next is dX)
+//    rounded once to bfloat16 and stored.
 // Rows past T and channels past C are computed on clamped addresses and not
-// stored.
+// stored. In place is safe: a thread reads its (token, channels) of dX_next one
+// tile before it writes the same elements, and no other thread touches them.
 constexpr int CFR = 24;  // floats per token of the staged coefficients
 constexpr int DPR = 36;  // floats per token row of the staged dP tile (padded)
 
-__global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ dXn,
-                                                     const uint16_t* __restrict__ dFi, int64_t T, int64_t C,
-                                                     const float* __restrict__ h_pre, const float* __restrict__ h_res,
-                                                     const float* __restrict__ dP, const float* __restrict__ g2,
-                                                     const uint4* __restrict__ phi_rows, uint16_t* __restrict__ dX) {
+template <int BM>
+__global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict__ X, const uint16_t* dXn,
+                                                     const uint16_t* __restrict__ dFi, int64_t T, int64_t C, int N,
+                                                     const int32_t* __restrict__ idx, const float* __restrict__ h_pre,
+                                                     const float* __restrict__ h_res, const float* __restrict__ dP,
+                                                     const float* __restrict__ g2, const uint4* __restrict__ phi_rows,
+                                                     uint16_t* dX) {
   __shared__ __attribute__((aligned(16))) float prj[BS * XT * PRJ];
   __shared__ __attribute__((aligned(16))) float cf[XT * CFR];
   __shared__ __attribute__((aligned(16))) float dpt[XT * DPR];
@@ -210,6 +252,7 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   const int64_t cl = cok ? c : C - 8;
   const int si = wave >> 1, cb0 = (wave & 1) * 4;
   const int tau = lane & 15, q = lane >> 4;
+  const int g0 = BM == BM_PRE ? 4 * (int)blockIdx.z : 0;  // first phi row group (BM_PRE)
   // staging roles: coefficient piece (token tid / 6, piece tid % 6), dP piece
   // (token (tid & 255) >> 3, piece tid & 7)
   const int ctok = tid < 192 ? tid / 6 : 0, cpc = tid < 192 ? tid - 6 * ctok : 0;
@@ -220,7 +263,7 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   for (int cb = 0; cb < 4; ++cb) {
     int64_t ch = chunk * XCH + (cb0 + cb) * 16 + tau;
     ch = ch < C ? ch : C - 1;
-    const uint4* pr = phi_rows + ((int64_t)si * C + ch) * 8;
+    const uint4* pr = phi_rows + ((int64_t)(g0 + si) * C + ch) * 8;
     bh[cb] = pr[q];
     bl[cb] = pr[4 + q];
   }
@@ -228,21 +271,29 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   struct In {
     uint4 xq[BS], dq[BS], fq;
     float4 cv, dv;
+    int sl[4];  // the slots' streams
   };
   auto load = [&](int64_t tl, In& in) __attribute__((always_inline)) {
     const int64_t t = tl * XT + m;
     const int64_t tc = t < T ? t : T - 1;
+    slot_streams<BM>(idx, tc, N, in.sl);
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
-      in.xq[i] = ld_nt16(X + (tc * BS + i) * C + cl);
-      in.dq[i] = ld_nt16(dXn + (tc * BS + i) * C + cl);
+      in.xq[i] = ld_nt16(X + (tc * N + in.sl[i]) * C + cl);
+      in.dq[i] = ld_nt16(dXn + (tc * N + in.sl[i]) * C + cl);
     }
-    in.fq = ld_nt16(dFi + tc * C + cl);
+    if constexpr (BM != BM_ROUTE) in.fq = ld_nt16(dFi + tc * C + cl);
     int64_t t1 = tl * XT + ctok;
     t1 = t1 < T ? t1 : T - 1;
-    if (cpc < 4) in.cv = reinterpret_cast<const float4*>(h_res + t1 * 16)[cpc];
-    else if (cpc == 4) in.cv = *reinterpret_cast<const float4*>(h_pre + t1 * 4);
-    else in.cv = make_float4(g2[t1], 0.f, 0.f, 0.f);
+    if (cpc < 4) {
+      if constexpr (BM == BM_PRE) in.cv = make_float4(0.f, 0.f, 0.f, 0.f);
+      else in.cv = reinterpret_cast<const float4*>(h_res + t1 * 16)[cpc];
+    } else if (cpc == 4) {
+      if constexpr (BM == BM_ROUTE) in.cv = make_float4(0.f, 0.f, 0.f, 0.f);
+      else in.cv = *reinterpret_cast<const float4*>(h_pre + t1 * (BM == BM_PRE ? N : 4) + g0);
+    } else {
+      in.cv = make_float4(g2[t1], 0.f, 0.f, 0.f);
+    }
     int64_t t2 = tl * XT + dtok;
     t2 = t2 < T ? t2 : T - 1;
     in.dv = reinterpret_cast<const float4*>(dP + t2 * DPS)[dpc];
@@ -280,7 +331,7 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
     float d[BS][8], f[8];
 #pragma unroll
     for (int i = 0; i < BS; ++i) unpack_bf8(cur.dq[i], d[i]);
-    unpack_bf8(cur.fq, f);
+    if constexpr (BM != BM_ROUTE) unpack_bf8(cur.fq, f);
     const int64_t t = tl * XT + m;
     const bool ok = t < T && cok;
 #pragma unroll
@@ -291,13 +342,17 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
       float xj[8], o[8];
       unpack_bf8(cur.xq[j], xj);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        o[e] = H[0][j] * d[0][e] + H[1][j] * d[1][e] + H[2][j] * d[2][e] + H[3][j] * d[3][e] + hp[j] * f[e] +
-               p[e] + g4.x * xj[e];
+      for (int e = 0; e < 8; ++e) {
+        float v;
+        if constexpr (BM == BM_PRE) v = d[j][e] + hp[j] * f[e];
+        else v = H[0][j] * d[0][e] + H[1][j] * d[1][e] + H[2][j] * d[2][e] + H[3][j] * d[3][e];
+        if constexpr (BM == BM_MHC) v += hp[j] * f[e];
+        o[e] = v + p[e] + g4.x * xj[e];
+      }
       if (ok)
         __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]),
                                          pack_bf2_hw(o[4], o[5]), pack_bf2_hw(o[6], o[7])},
-                                    reinterpret_cast<u4_t*>(dX + (t * BS + j) * C + c));
+                                    reinterpret_cast<u4_t*>(dX + (t * N + cur.sl[j]) * C + c));
     }
     __syncthreads();  // the LDS tiles are rewritten by the next tile
     tl = nt;
@@ -325,17 +380,20 @@ __device__ __forceinline__ int xoff(int i, int m, int c) {
   return (i * FT + m) * FROW + (((c >> 3) ^ (((m >> 3) & 3) << 1)) << 4) + (c & 7) * 2;
 }
 
-// Partial dphi of a chunk of 128 channels x 4 streams over the token tiles g,
-// g + G, ... (g = blockIdx.y, G = gridDim.y <= the tile count):
-//   part[g][i*C + c][k] = sum_t x[t, i, c] dP[t, k]   (k < 24)
+// Partial dphi of a chunk of 128 channels x the 4 slots of the row mode over
+// the token tiles g, g + G, ... (g = blockIdx.y, G = gridDim.y <= the tile
+// count), with R = the phi row of the slot's channel c:
+//   part[g][R][k] = sum_t x[t, slot, c] dP[t, k]   (k < ncol)
 // on MFMA with the tokens as K: A = x^T (lane: one channel, 8 tokens, read from
 // the LDS state tile one element at a time), B = dP (lane: one column, 8 tokens,
 // from the transposed hi/lo tile in LDS), D += A B_hi + A B_lo. Wave w owns
 // stream w >> 1, channel blocks (w & 1) * 4 .. + 3 and both 16-column blocks;
 // its accumulators stay in registers over the workgroup's tiles. The next
 // tile's state and dP are loaded while the MFMAs of the current one run.
+template <int BM>
 __global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restrict__ X, const float* __restrict__ dP,
-                                                       int64_t T, int64_t C, float* __restrict__ part) {
+                                                       int64_t T, int64_t C, int N, const int32_t* __restrict__ idx,
+                                                       int ncol, int64_t nrows, float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) unsigned char xt[BS * FT * FROW];
   __shared__ __attribute__((aligned(16))) uint16_t dpt[2 * DPS * DPT];  // [hi | lo][column][token]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -350,6 +408,7 @@ __global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restric
   const int pm = (tid & 255) >> 3, pc = (tid & 7) * 4;
   const int si = wave >> 1, cb0 = (wave & 1) * 4;
   const int tau = lane & 15, q = lane >> 4;
+  const int g0 = BM == BM_PRE ? 4 * (int)blockIdx.z : 0;
 
   f4_t acc[4][2];
 #pragma unroll
@@ -363,9 +422,11 @@ __global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restric
     const int64_t t = tl * FT + m;
     const bool ok = t < T && cok;
     const int64_t tc = t < T ? t : T - 1;
+    int sl[4];
+    slot_streams<BM>(idx, tc, N, sl);
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
-      const uint4 v = ld_nt16(X + (tc * BS + i) * C + cl);
+      const uint4 v = ld_nt16(X + (tc * N + sl[i]) * C + cl);
       xq[i] = ok ? v : make_uint4(0, 0, 0, 0);
     }
     const int64_t t2 = tl * FT + pm;
@@ -414,7 +475,7 @@ __global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restric
     }
     __syncthreads();
   }
-  float* out = part + (int64_t)grp * BS * C * BCOL;
+  float* out = part + (int64_t)grp * nrows * ncol;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -423,18 +484,19 @@ __global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restric
       for (int e = 0; e < 4; ++e) {
         const int64_t ch = chunk * FCH + (cb0 + cb) * 16 + q * 4 + e;
         const int col = nb * 16 + tau;
-        if (ch < C && col < BCOL) out[((int64_t)si * C + ch) * BCOL + col] = acc[cb][nb][e];
+        if (ch < C && col < ncol) out[((int64_t)(g0 + si) * C + ch) * ncol + col] = acc[cb][nb][e];
       }
 }
 
 // The final sums in one launch. Workgroups [0, nbp): dphi, the G group
 // partials added in group order, one thread per entry. Workgroup nbp + k:
 // column k of the sums over groups of 16 tokens [nrow][28] added over the
-// groups (dbias[k] for k < 24, dalpha[k - 24] for k = 24, 25, 26), each thread
-// the rows tid, tid + 256, ... in order, then a tree in LDS.
+// groups: dbias[k] for k < nb, then dalpha[k - nb] = column a0 + (k - nb) for
+// the next workgroups; each thread the rows tid, tid + 256, ... in order, then
+// a tree in LDS.
 __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__ part, int64_t n, int G, int nbp,
                                                        float* __restrict__ dphi, const float* __restrict__ red,
-                                                       int64_t nrow, float* __restrict__ dbias,
+                                                       int64_t nrow, int nb, float* __restrict__ dbias, int a0,
                                                        float* __restrict__ dalpha) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < nbp) {
@@ -447,8 +509,9 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
   }
   __shared__ float sm[256];
   const int k = (int)blockIdx.x - nbp;
+  const int colk = k < nb ? k : a0 + (k - nb);
   float v = 0.f;
-  for (int64_t t = tid; t < nrow; t += 256) v += red[t * RED + k];
+  for (int64_t t = tid; t < nrow; t += 256) v += red[t * RED + colk];
   sm[tid] = v;
   __syncthreads();
   for (int h = 128; h > 0; h >>= 1) {
@@ -456,8 +519,8 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
     __syncthreads();
   }
   if (tid == 0) {
-    if (k < BCOL) dbias[k] = sm[0];
-    else dalpha[k - BCOL] = sm[0];
+    if (k < nb) dbias[k] = sm[0];
+    else dalpha[k - nb] = sm[0];
   }
 }
 
@@ -492,12 +555,15 @@ struct BwdWs {
   void* packed;
   float* partial;
   uint4* phi_rows;
-  float *h_pre, *h_res, *dP, *g2, *red, *dphi_part;
+  float *h_pre, *h_post, *h_res, *dP, *g2, *red, *dphi_part;
   int G;
 };
 
-// Workspace pieces in order; each 256-byte aligned.
-BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
+// Workspace pieces in order, each 256-byte aligned, for a backward whose phi
+// has nrows rows and ncol columns (packed B-operand form of pbytes, partials
+// of qbytes); h_post [T, 4] only for the xHC route, h_pre [T, hp] otherwise.
+BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pbytes, int64_t qbytes, int hp,
+            bool route, int64_t* total) {
   BwdWs w{};
   unsigned char* p = (unsigned char*)ws;
   int64_t off = 0;
@@ -506,18 +572,41 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t* total) {
     off += al256(bytes);
     return q;
   };
-  w.packed = take(fast_coeffs_packed_bytes(4, C, 1));
-  w.partial = (float*)take(fast_coeffs_partial_bytes(T, 4, C, 1));
-  w.phi_rows = (uint4*)take(BS * C * 128);
-  w.h_pre = (float*)take(T * 4 * 4);
+  w.packed = take(pbytes);
+  w.partial = (float*)take(qbytes);
+  w.phi_rows = (uint4*)take(nrows * 128);
+  w.h_pre = (float*)take(T * hp * 4);
+  w.h_post = route ? (float*)take(T * 4 * 4) : nullptr;
   w.h_res = (float*)take(T * 16 * 4);
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
   w.red = (float*)take((T + 15) / 16 * RED * 4);
   w.G = dphi_groups(T, C);
-  w.dphi_part = (float*)take((int64_t)w.G * BS * C * BCOL * 4);
+  w.dphi_part = (float*)take((int64_t)w.G * nrows * ncol * 4);
   if (total) *total = off;
   return w;
+}
+
+BwdWs carve_mhc(void* ws, int64_t T, int64_t C, int64_t* total) {
+  return carve(ws, T, C, BS * C, BCOL, fast_coeffs_packed_bytes(4, C, 1), fast_coeffs_partial_bytes(T, 4, C, 1), 4,
+               false, total);
+}
+// route: phi_act [4C, 20] packed as 3 x 16 columns (48 x 16 bytes per 8 rows)
+BwdWs carve_route(void* ws, int64_t T, int64_t C, int64_t* total) {
+  return carve(ws, T, C, BS * C, 20, BS * C / 8 * 48 * 16, fast_xroute_partial_bytes(T, C), 4, true, total);
+}
+// pre: phi_pre [NC, N] packed as 2 x 16 columns
+BwdWs carve_pre(void* ws, int64_t T, int N, int64_t C, int64_t* total) {
+  return carve(ws, T, C, (int64_t)N * C, N, (int64_t)N * C / 8 * 32 * 16, fast_xpre_partial_bytes(T, N, C), N, false,
+               total);
+}
+
+hipError_t launch_sums(const BwdWs& w, int64_t T, int64_t nrows, int ncol, float* dphi, float* dbias, int na0,
+                       int na, float* dalpha, hipStream_t st) {
+  const int64_t nphi = nrows * ncol, nbp = (nphi + 255) / 256;
+  hipLaunchKernelGGL(bwd_sums_kernel, dim3((unsigned)(nbp + ncol + na)), dim3(256), 0, st, w.dphi_part, nphi, w.G,
+                     (int)nbp, dphi, w.red, (T + 15) / 16, ncol, dbias, na0, dalpha);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -529,14 +618,15 @@ bool fast_backward_supported(int dtype, int n, int64_t T, int64_t C, int iters) 
 
 int64_t fast_backward_ws_bytes(int64_t T, int64_t C) {
   int64_t total = 0;
-  carve(nullptr, T, C, &total);
+  carve_mhc(nullptr, T, C, &total);
   return total;
 }
 
 hipError_t launch_fast_backward_post(const void* X, int64_t T, int64_t C, const float* h_post, const void* F_out,
                                      const void* dX_next, void* dF_out, float* dh, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_post_kernel, dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)X,
-                     (const uint16_t*)dX_next, (const uint16_t*)F_out, C, h_post, dh, (uint16_t*)dF_out);
+  hipLaunchKernelGGL(bwd_post_kernel<BM_MHC>, dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)X,
+                     (const uint16_t*)dX_next, (const uint16_t*)F_out, C, 4, (const int32_t*)nullptr, h_post, dh,
+                     BCOL, 4, (uint16_t*)dF_out);
   return hipGetLastError();
 }
 
@@ -544,26 +634,101 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
                                 float a_pre, float a_post, float a_res, int iters, const void* dX_next,
                                 const void* dF_in, float* dh, void* dX, float* dphi, float* dbias, float* dalpha,
                                 void* ws, hipStream_t st) {
-  const BwdWs w = carve(ws, T, C, nullptr);
+  const BwdWs w = carve_mhc(ws, T, C, nullptr);
   const uint16_t* x = (const uint16_t*)X;
   hipError_t e = launch_fast_bwd_front(X, T, C, phi, w.packed, w.phi_rows, w.partial, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_pre_sums_kernel, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dF_in, C, dh);
+  hipLaunchKernelGGL(bwd_pre_sums_kernel<4>, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dF_in, C, dh,
+                     BCOL);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                   w.h_pre, w.h_res, st)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(bwd_dx_kernel, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)), dim3(512), 0,
-                     st, x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, w.h_pre, w.h_res, w.dP, w.g2,
-                     w.phi_rows, (uint16_t*)dX);
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_MHC>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)),
+                     dim3(512), 0, st, x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, 4,
+                     (const int32_t*)nullptr, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dphi_kernel, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st, x,
-                     w.dP, T, C, w.dphi_part);
+  hipLaunchKernelGGL(bwd_dphi_kernel<BM_MHC>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st,
+                     x, w.dP, T, C, 4, (const int32_t*)nullptr, BCOL, (int64_t)BS * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t nphi = (int64_t)BS * C * BCOL, nbp = (nphi + 255) / 256;
-  hipLaunchKernelGGL(bwd_sums_kernel, dim3((unsigned)(nbp + BCOL + 3)), dim3(256), 0, st, w.dphi_part, nphi, w.G,
-                     (int)nbp, dphi, w.red, (T + 15) / 16, dbias, dalpha);
-  return hipGetLastError();
+  return launch_sums(w, T, (int64_t)BS * C, BCOL, dphi, dbias, BCOL, 3, dalpha, st);
+}
+
+// ------------------------------------------------------------------ xHC
+
+bool fast_xhc_backward_supported(int dtype, int N, int k, int K, int64_t T, int64_t C, int iters) {
+  return dtype == 1 && N % 4 == 0 && N >= 4 && N <= 16 && k == 4 && K == 1 && T >= 1 && iters >= 1 &&
+         iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 && fast_xroute_partial_bytes(T, C) > 0 &&
+         fast_xpre_partial_bytes(T, N, C) > 0 && (C + FCH - 1) / FCH <= 65535 && T * (int64_t)N * C < (1ll << 40);
+}
+
+int64_t fast_xhc_backward_ws_bytes(int64_t T, int N, int64_t C) {
+  int64_t a = 0, b = 0;
+  carve_route(nullptr, T, C, &a);
+  carve_pre(nullptr, T, N, C, &b);
+  return a > b ? a : b;
+}
+
+hipError_t launch_fast_xroute_backward(const void* X, int64_t T, int N, int64_t C, const int32_t* idx,
+                                       const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
+                                       const void* F_out, void* dX, void* dF_out, float* dphi_act, float* db_act,
+                                       float* dalpha, float* dh, void* ws, hipStream_t st) {
+  const BwdWs w = carve_route(ws, T, C, nullptr);
+  const uint16_t* x = (const uint16_t*)X;
+  // the active set's maps (the forward's kernels) and its projection partials
+  hipError_t e = launch_fast_xhc_active(X, T, N, C, idx, 1, phi_act, b_act, a_post, a_res, iters, w.h_post, w.h_res,
+                                        w.packed, w.partial, st, w.phi_rows);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_post_kernel<BM_ROUTE>, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dX,
+                     (const uint16_t*)F_out, C, N, idx, w.h_post, dh, 20, 0, (uint16_t*)dF_out);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_fast_xroute_bwd_coeffs(w.partial, T, C, b_act, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
+                                         w.h_res, st)) != hipSuccess)
+    return e;
+  // dphi reads x only: run it before the dX pass rewrites dX_next's active rows
+  hipLaunchKernelGGL(bwd_dphi_kernel<BM_ROUTE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0,
+                     st, x, w.dP, T, C, N, idx, 20, (int64_t)BS * C, w.dphi_part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_ROUTE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)),
+                     dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)nullptr, T, C, N, idx,
+                     (const float*)nullptr, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dalpha: the post and res gate sums (red columns 25, 26)
+  return launch_sums(w, T, (int64_t)BS * C, 20, dphi_act, db_act, 25, 2, dalpha, st);
+}
+
+hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C, const float* phi_pre,
+                                     const float* b_pre, float a_pre, const void* dF_in, void* dX, float* dphi_pre,
+                                     float* db_pre, float* dalpha, float* dh_pre, void* ws, hipStream_t st) {
+  const BwdWs w = carve_pre(ws, T, N, C, nullptr);
+  const uint16_t* x = (const uint16_t*)X;
+  hipError_t e = launch_fast_xpre_bwd_front(X, T, N, C, phi_pre, w.packed, w.phi_rows, w.partial, st);
+  if (e != hipSuccess) return e;
+  const dim3 tg((unsigned)T), tb(256);
+  switch (N) {
+    case 4: hipLaunchKernelGGL(bwd_pre_sums_kernel<4>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N); break;
+    case 8: hipLaunchKernelGGL(bwd_pre_sums_kernel<8>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N); break;
+    case 12:
+      hipLaunchKernelGGL(bwd_pre_sums_kernel<12>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N);
+      break;
+    default:
+      hipLaunchKernelGGL(bwd_pre_sums_kernel<16>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N);
+      break;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_fast_xpre_bwd_coeffs(w.partial, T, N, C, b_pre, a_pre, dh_pre, w.dP, w.g2, w.red, w.h_pre, st)) !=
+      hipSuccess)
+    return e;
+  const unsigned ng = (unsigned)(N / 4);
+  hipLaunchKernelGGL(bwd_dphi_kernel<BM_PRE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G, ng), dim3(512), 0,
+                     st, x, w.dP, T, C, N, (const int32_t*)nullptr, N, (int64_t)N * C, w.dphi_part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_PRE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C), ng),
+                     dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)dF_in, T, C, N,
+                     (const int32_t*)nullptr, w.h_pre, (const float*)nullptr, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // dalpha: the gate sum (red column 24)
+  return launch_sums(w, T, (int64_t)N * C, N, dphi_pre, db_pre, 24, 1, dalpha, st);
 }
 
 }  // namespace hc

@@ -932,12 +932,20 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
 // per workgroup of 16 tokens, red [28] = the sums
 // over its tokens of dz [24] | dz P rho over each gate [3] | 0, which are then
 // added over the workgroups for db and dalpha.
-template <int TT>
+//
+// ROUTE: the xHC active set (k = 4, K = 1) with columns [post 4 | res 16] and dh
+// [T, 20] in that order: lanes e < 4 carry post column e, no pre map (h_pre is
+// not written), and the red columns are dz [post 4 | res 16 | 0 0 0 0] | 0 |
+// dz P rho over post | over res | 0.
+template <int TT, bool ROUTE>
 __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
                                                         const float* __restrict__ bias, Gate gate, int iters,
                                                         const float* __restrict__ dh, float* __restrict__ dP,
                                                         float* __restrict__ g2, float* __restrict__ red,
                                                         float* __restrict__ h_pre, float* __restrict__ h_res) {
+  constexpr int RES0 = ROUTE ? 4 : 8;    // first res column
+  constexpr int NGC = ROUTE ? 4 : 8;     // gate (pre/post) columns before it
+  constexpr int DHS = ROUTE ? 20 : 24;   // dh row length
   extern __shared__ float it_lds[];  // [iters][256]
   using PG = PartGeom<3, TT>;
   const int tid = threadIdx.x;
@@ -954,13 +962,13 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   for (int s = 0; s < S; ++s) {
     const float* b = base + (int64_t)s * PG::PART;
     ss += b[PG::NCOLP];
-    pr += b[8 + e];
-    pe += b[e & 7];
+    pr += b[RES0 + e];
+    pe += b[e & (NGC - 1)];
   }
   const float invr = inv_rms4(ss, C);
-  const float a = e < 4 ? gate.a_pre : gate.a_post;
-  const float sg = sigmoid(gate_logit(a, pe, invr, bias[e & 7]));
-  const float z = gate_logit(gate.a_res, pr, invr, bias[8 + e]);
+  const float a = (ROUTE || e >= 4) ? gate.a_post : gate.a_pre;
+  const float sg = sigmoid(gate_logit(a, pe, invr, bias[e & (NGC - 1)]));
+  const float z = gate_logit(gate.a_res, pr, invr, bias[RES0 + e]);
   float zm = fmaxf(z, dpp<DPP_QXOR1>(z));
   zm = fmaxf(zm, dpp<DPP_QXOR2>(zm));
   zm = fmaxf(zm, dpp<DPP_ROR4>(zm));
@@ -978,10 +986,10 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   }
   if (valid) {  // the forward's maps, for the dX pass
     h_res[tt * 16 + e] = M;
-    if (e < 4) h_pre[tt * 4 + e] = sg;
+    if (!ROUTE && e < 4) h_pre[tt * 4 + e] = sg;
   }
   // each lane reads back only the iterates it wrote: no barrier needed
-  float G = dh[tc * 24 + 8 + e];
+  float G = dh[tc * DHS + RES0 + e];
   for (int it = iters - 1; it >= 0; --it) {
     // (the reverse walk divides by one reciprocal per sum, v_rcp_f32 to 1 ulp)
     const float Mk = it_lds[it * 256 + tid];
@@ -1004,9 +1012,9 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   }
   const float dz_res = G * M0;
   float dz_pp = 0.f;
-  if (e < 8) {
-    const float d = dh[tc * 24 + e];
-    dz_pp = (e < 4 ? d : 2.0f * d) * sg * (1.0f - sg);
+  if (e < NGC) {
+    const float d = dh[tc * DHS + e];
+    dz_pp = ((!ROUTE && e < 4) ? d : 2.0f * d) * sg * (1.0f - sg);
   }
   // sums over the 16 lanes: quads, then the four quads (every lane gets the total)
   auto row16 = [](float x) __attribute__((always_inline)) {
@@ -1016,24 +1024,89 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
     x += dpp<DPP_ROR4>(x);
     return x;
   };
-  const float drho = row16(gate.a_res * dz_res * pr + (e < 8 ? a * dz_pp * pe : 0.f));
-  const float u_pre = row16(e < 4 ? dz_pp * pe * invr : 0.f);
-  const float u_post = row16(e >= 4 && e < 8 ? dz_pp * pe * invr : 0.f);
+  const float drho = row16(gate.a_res * dz_res * pr + (e < NGC ? a * dz_pp * pe : 0.f));
+  const float u_pre = ROUTE ? 0.f : row16(e < 4 ? dz_pp * pe * invr : 0.f);
+  const float u_post = row16(e >= (ROUTE ? 0 : 4) && e < NGC ? dz_pp * pe * invr : 0.f);
   const float u_res = row16(dz_res * pr * invr);
   if (valid) {
-    dP[tt * 32 + 8 + e] = gate.a_res * dz_res * invr;
-    if (e < 8) {
-      dP[tt * 32 + e] = a * dz_pp * invr;
-      dP[tt * 32 + 24 + e] = 0.f;
-    }
+    dP[tt * 32 + RES0 + e] = gate.a_res * dz_res * invr;
+    if (e < NGC) dP[tt * 32 + e] = a * dz_pp * invr;
+    if (e < 32 - RES0 - 16) dP[tt * 32 + RES0 + 16 + e] = 0.f;
     if (e == 0) g2[tt] = -drho * invr * invr * invr / (float)(NS4 * C);
   }
   // the workgroup's 16 tokens added in token order (rows past T add zero)
   __shared__ float bsum[16][28];
   const int tk = tid >> 4;
-  bsum[tk][8 + e] = valid ? dz_res : 0.f;
-  if (e < 8) bsum[tk][e] = valid ? dz_pp : 0.f;
+  bsum[tk][RES0 + e] = valid ? dz_res : 0.f;
+  if (e < NGC) bsum[tk][e] = valid ? dz_pp : 0.f;
+  if (ROUTE && e < 4) bsum[tk][20 + e] = 0.f;
   if (e < 4) bsum[tk][24 + e] = !valid || e == 3 ? 0.f : (e == 0 ? u_pre : (e == 1 ? u_post : u_res));
+  __syncthreads();
+  if (tid < 28) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sum += bsum[k][tid];
+    red[(int64_t)blockIdx.x * 28 + tid] = sum;
+  }
+}
+
+// Backward of the xHC pre map h_pre = sigmoid(alpha_pre P / r + b_pre) for token
+// tt, from the full-state partials (xpre_finish_kernel's layout: per tile the
+// N/4 stream groups x S slices, columns [pre N | ...]). 16 lanes per token, lane
+// c < N for pre column c: P and the sum of squares added over the items in
+// order, r = sqrt(ss / (N C)) and h_pre as xpre_finish_kernel forms them, then
+// dz = dH_pre h (1 - h), dP = alpha dz / r and the gradient through r,
+// 2 dss = -d rho rho^3 / (N C). Outputs: dP [T, 32] (columns N..31 zero), g2,
+// h_pre [T, N], and per workgroup of 16 tokens red [28] = the sums of dz
+// [16, zero past N] | 0 x 8 | dz P rho over the gate | 0 0 0.
+template <int NB, int TT>
+__global__ __launch_bounds__(256) void bwd_xpre_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C,
+                                                             int N, int per_tile, const float* __restrict__ b_pre,
+                                                             float a_pre, const float* __restrict__ dh_pre,
+                                                             float* __restrict__ dP, float* __restrict__ g2,
+                                                             float* __restrict__ red, float* __restrict__ h_pre) {
+  using PG = PartGeom<NB, TT>;
+  const int tid = threadIdx.x;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
+  const int64_t tt = g >> 4;
+  const int c = (int)(g & 15);
+  const bool valid = tt < T;
+  const int64_t tc = valid ? tt : T - 1;
+  const int64_t tile = tc / TT;
+  const int mrow = (int)(tc - tile * TT);
+  const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
+  const int cc = c < N ? c : 0;
+  float ss = 0.f, pc = 0.f;
+#pragma unroll 4
+  for (int it = 0; it < per_tile; ++it) {
+    const float* b = base + (int64_t)it * PG::PART;
+    ss += b[PG::NCOLP];
+    pc += b[cc];
+  }
+  const float r = sqrtf(ss / (float)((double)N * (double)C));
+  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  const bool col = c < N;
+  const float h = sigmoid(a_pre * (pc * invr) + b_pre[cc]);
+  const float dz = col ? dh_pre[tc * N + c] * h * (1.0f - h) : 0.f;
+  auto row16 = [](float x) __attribute__((always_inline)) {
+    x += dpp<DPP_QXOR1>(x);
+    x += dpp<DPP_QXOR2>(x);
+    x += dpp<DPP_ROR8>(x);
+    x += dpp<DPP_ROR4>(x);
+    return x;
+  };
+  const float drho = row16(a_pre * dz * pc);
+  const float u = row16(dz * pc * invr);
+  if (valid) {
+    dP[tt * 32 + c] = col ? a_pre * dz * invr : 0.f;
+    dP[tt * 32 + 16 + c] = 0.f;
+    if (col) h_pre[tt * N + c] = h;
+    if (c == 0) g2[tt] = -drho * invr * invr * invr / (float)((double)N * (double)C);
+  }
+  __shared__ float bsum[16][28];
+  const int tk = tid >> 4;
+  bsum[tk][c] = valid ? dz : 0.f;
+  if (c < 12) bsum[tk][16 + c] = (c == 8 && valid) ? u : 0.f;
   __syncthreads();
   if (tid < 28) {
     float sum = 0.f;
@@ -1573,11 +1646,40 @@ hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const floa
   return launch_wide<3, ROWS_CONTIG>(args(X, T, C, 4 * C, geom(T, C, 1, W_TOK), packed, partial), st);
 }
 
+hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* b_act,
+                                         float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
+                                         float* red, float* h_res, hipStream_t st) {
+  const int64_t threads = T * 16;
+  hipLaunchKernelGGL((bwd_coeff_kernel<TILE, true>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), b_act,
+                     Gate{0.f, a_post, a_res}, iters, dh, dP, g2, red, nullptr, h_res);
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C, const float* phi_pre, void* packed,
+                                      uint4* phi_rows, float* partial, hipStream_t st) {
+  hipError_t e = launch_pack(phi_pre, N, nullptr, 0, (int64_t)N * C, 16, packed, st, phi_rows);
+  if (e != hipSuccess) return e;
+  return launch_wide<2, ROWS_GROUPS>(args(X, T, C, (int64_t)N * C, geom(T, C, N / 4, W_TOK), packed, partial), st);
+}
+
+hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, int64_t C, const float* b_pre,
+                                       float a_pre, const float* dh_pre, float* dP, float* g2, float* red,
+                                       float* h_pre, hipStream_t st) {
+  const int64_t threads = T * 16;
+  hipLaunchKernelGGL((bwd_xpre_coeff_kernel<2, W_TOK>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     partial, T, C, N, (int)((N / 4) * slices(C)), b_pre, a_pre, dh_pre, dP, g2, red, h_pre);
+  return hipGetLastError();
+}
+
+int64_t fast_xroute_partial_bytes(int64_t T, int64_t C) { return part_bytes(T, C, 1, 3); }
+int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C) { return part_bytes(T, C, N / 4, 2); }
+
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                   float* red, float* h_pre, float* h_res, hipStream_t st) {
   const int64_t threads = T * 16;
-  hipLaunchKernelGGL(bwd_coeff_kernel<W_TOK>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, false>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
                      (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), bias,
                      Gate{a_pre, a_post, a_res}, iters, dh, dP, g2, red, h_pre, h_res);
   return hipGetLastError();
@@ -1706,10 +1808,11 @@ hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* 
 
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
                                   const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
-                                  float* Hp, float* Hr, void* packed, float* partial, hipStream_t st) {
+                                  float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,
+                                  uint4* phi_rows) {
   const int ncols = 4 * K + 16;
   const int nb = nb_for(ncols);
-  hipError_t e = launch_pack(phi_act, ncols, nullptr, 0, 4 * C, nb * 8, packed, st);
+  hipError_t e = launch_pack(phi_act, ncols, nullptr, 0, 4 * C, nb * 8, packed, st, phi_rows);
   if (e != hipSuccess) return e;
   const Geom g = geom(T, C, 1, TILE);
   SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);

@@ -276,3 +276,50 @@ def test_backward_validation(hc):
     assert post(dh=ctypes.c_void_p(0x6000002)) == -4
     assert post(dFo=ctypes.c_void_p(0x3000000)) == -5  # dF_out over F_out
     assert post(dh=ctypes.c_void_p(0x5000010)) == -5  # dh inside dF_out
+
+
+def test_xhc_backward_validation(hc):
+    L = hc.lib()
+    T, N, C = 8, 16, 64
+    wsb = L.xhc_backward_workspace_bytes(T, N, C, 4, 1, 1)
+    assert wsb > 0
+    assert L.xhc_backward_workspace_bytes(0, N, C, 4, 1, 1) == 0
+    assert L.xhc_backward_workspace_bytes(T, 6, C, 4, 1, 1) == -1
+    assert L.xhc_backward_workspace_bytes(T, N, C, 3, 1, 1) == -1
+    assert L.xhc_backward_workspace_bytes(T, N, C, 4, 2, 1) == -1
+    assert L.xhc_backward_workspace_bytes(T, N, 40, 4, 1, 1) == -1
+    assert L.xhc_backward_workspace_bytes(T, N, C, 4, 1, 0) == -1
+    P = lambda k: ctypes.c_void_p(0x1000000 * (k + 1))  # distinct, far apart, 256-byte aligned
+    rn = ["X", "idx", "phi", "b", "Wb", "dX", "dWb", "dphi", "db", "da", "dh", "ws"]
+
+    def route(dt=1, T=T, N=N, C=C, k=4, K=1, iters=20, wsb=wsb, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(rn)}
+        return L.xhc_route_backward(p["X"], dt, T, N, C, k, p["idx"], p["phi"], p["b"], 0.01, 0.01, iters, p["Wb"],
+                                    K, p["dX"], p["dWb"], p["dphi"], p["db"], p["da"], p["dh"], p["ws"], wsb, None)
+    assert route(dt=0) == -3 and route(dt=5) == -3
+    assert route(N=6) == -2 and route(N=20) == -2 and route(k=3) == -2 and route(K=2) == -2 and route(C=48) == -2
+    assert route(iters=0) == -2 and route(iters=65) == -2 and route(T=-1) == -2
+    assert route(T=0, X=None) == 0
+    for nm in rn[:-1]:
+        assert route(**{nm: None}) == -1, nm
+    assert route(idx=ctypes.c_void_p(0x2000004)) == -4  # idx is read 16 bytes per token
+    assert route(dX=ctypes.c_void_p(0x6000008)) == -4
+    assert route(ws=None) == -8 and route(wsb=wsb - 1) == -8
+    assert route(dX=ctypes.c_void_p(0x1000000)) == -5  # dX over X
+    assert route(dh=ctypes.c_void_p(0x6000100)) == -5  # dh inside dX
+    assert route(dWb=ctypes.c_void_p(0x5000000)) == -5  # dF_out over F_out
+
+    pn = ["X", "phi", "b", "dFi", "dX", "dphi", "db", "da", "dh", "ws"]
+
+    def pre(dt=1, T=T, N=N, C=C, wsb=wsb, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(pn)}
+        return L.xhc_pre_backward(p["X"], dt, T, N, C, p["phi"], p["b"], 0.01, p["dFi"], p["dX"], p["dphi"], p["db"],
+                                  p["da"], p["dh"], p["ws"], wsb, None)
+    assert pre(dt=0) == -3 and pre(N=2) == -2 and pre(C=40) == -2 and pre(T=-3) == -2
+    assert pre(T=0, X=None) == 0
+    for nm in pn[:-1]:
+        assert pre(**{nm: None}) == -1, nm
+    assert pre(dh=ctypes.c_void_p(0x9000004)) == -4
+    assert pre(ws=None) == -8
+    assert pre(dX=ctypes.c_void_p(0x4000000)) == -5  # dX over dF_in
+    assert pre(dphi=ctypes.c_void_p(0x5000040)) == -5  # dphi inside dX

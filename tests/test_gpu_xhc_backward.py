@@ -1,0 +1,148 @@
+"""GPU parity of the xHC routed-step backward (xhc_route_backward, then
+xhc_pre_backward; k = 4, K = 1, bfloat16) against the fp64 oracle's
+xhc_route_backward and xhc_pre_backward, through the C ABI, on the synth
+recipe's xHC inputs and upstream gradients.
+
+Tolerances as for the mHC backward: the route's dX and dF_out are bfloat16
+outputs rounded once from float32 (the route's pass-through rows are compared
+bit for bit); the map gradients and dphi, db, dalpha are float32 sums (relative
+L2 1e-4, from the float32 channel sums, 20 reverse Sinkhorn steps and dP split
+into two bfloat16 parts on the matrix cores). The final dX is rounded twice: the
+route's gradient is stored in bfloat16, and the pre call adds its own term to
+it and rounds again. So per element it may be off by up to half a bfloat16 ulp
+of the route's value plus half an ulp of the sum; the bound is max(2e-2, one
+ulp of each), with relative L2 1e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from hc_testutil import BF16_MAX_ABS, BF16_REL_L2, bf16_ulp, check_bf16, check_fp32, dev, have_gpu, host64, note, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+if have_gpu():
+    import torch
+    import stream_residual_mixing_amd as hc
+
+BWD_REL = 1e-4
+
+
+def _inputs(seed, T, N, C, m=1, strong=False):
+    inp = synth.xhc_layer(seed, 0, T, N, C, 4, m, 1, synth.BF16)
+    g = synth.mhc_grads(seed, 0, T, N, C, synth.BF16)  # dX_next [T, N, C], dF_in [T, C]
+    if strong:  # gates and maps far from their values at z = b
+        inp["phi_act"] = (inp["phi_act"] * np.float32(10.0)).astype(np.float32)
+        inp["phi_pre"] = (inp["phi_pre"] * np.float32(10.0)).astype(np.float32)
+        inp["alpha_post"], inp["alpha_res"], inp["alpha_pre"] = 0.6, 0.9, 0.7
+    # the active set the forward chose
+    idx = O.xhc_pre(inp["X"].values, inp["phi_pre"], inp["b_pre"], inp["alpha_pre"], inp["w_router"], 4, m)["idx"]
+    return inp, g, idx.astype(np.int32)
+
+
+def _gpu(inp, g, idx, iters=20):
+    X = dev(inp["X"])
+    dX = dev(g["dX_next"]).clone()
+    r = hc.xhc_route_backward(X, dev(idx), dev(inp["phi_act"]), dev(inp["b_act"]), inp["alpha_post"],
+                              inp["alpha_res"], dev(inp["F_out"]), dX, iters)
+    torch.cuda.synchronize()
+    route = dict(zip(("dX", "dWb", "dphi_act", "db_act", "dalpha", "dh"), (host64(t) for t in r)))
+    p = hc.xhc_pre_backward(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], dev(g["dF_in"]), dX)
+    torch.cuda.synchronize()
+    pre = dict(zip(("dX", "dphi_pre", "db_pre", "dalpha", "dh_pre"), (host64(t) for t in p)))
+    return route, pre
+
+
+def _oracle(inp, g, idx, iters=20, chunk=None, rows=None):
+    T = inp["X"].values.shape[0]
+    chunk = chunk or T
+    keep = np.arange(T) if rows is None else np.asarray(rows)
+    acc = {}
+    per = {"dX_route": [], "dX": [], "dWb": [], "dh": [], "dh_pre": []}
+    for s in range(0, T, chunk):
+        sl = slice(s, min(T, s + chunk))
+        X = inp["X"].values[sl]
+        r = O.xhc_route_backward(X, idx[sl], inp["phi_act"], inp["b_act"], inp["alpha_post"], inp["alpha_res"],
+                                 inp["F_out"].values[sl], g["dX_next"].values[sl], iters)
+        p = O.xhc_pre_backward(X, inp["phi_pre"], inp["b_pre"], inp["alpha_pre"], g["dF_in"].values[sl])
+        for k, v in (("dphi_act", r["dphi_act"]), ("db_act", r["db_act"]),
+                     ("dalpha", np.array([r["dalpha_post"], r["dalpha_res"]])), ("dphi_pre", p["dphi_pre"]),
+                     ("db_pre", p["db_pre"]), ("dalpha_pre", np.array([p["dalpha_pre"]]))):
+            acc[k] = acc.get(k, 0.0) + v
+        sel = keep[(keep >= sl.start) & (keep < sl.stop)] - sl.start
+        per["dX_route"].append(r["dX"][sel])
+        per["dX"].append(r["dX"][sel] + p["dX"][sel])
+        per["dWb"].append(r["dWb"][sel, 0])
+        per["dh"].append(r["dh"][sel])
+        per["dh_pre"].append(p["dh_pre"][sel])
+    return {**acc, **{k: np.concatenate(v) for k, v in per.items()}}
+
+
+def _check_two_roundings(name, got, ref, ref_first):
+    """bfloat16 output rounded twice: after ref_first, then after adding to it."""
+    e = rel_l2(got, ref)
+    assert e <= BF16_REL_L2, f"{name}: relative L2 {e:.3e} > {BF16_REL_L2}"
+    err = np.abs(got - ref)
+    bound = np.maximum(BF16_MAX_ABS, bf16_ulp(ref_first) + bf16_ulp(ref))
+    bad = int(np.sum(err > bound))
+    assert bad == 0, f"{name}: {bad} elements exceed max(2e-2, ulp(first) + ulp(sum)); worst {err.max():.3e}"
+
+
+def _compare(route, pre, ref, g, idx, rows=None):
+    sel = slice(None) if rows is None else np.asarray(rows)
+    T = route["dX"].shape[0]
+    # rows outside the active set pass dX_next through unchanged (bit for bit)
+    inactive = np.ones(route["dX"].shape[:2], bool)
+    inactive[np.arange(T)[:, None], idx] = False
+    dXn = g["dX_next"].values.astype(np.float64)
+    np.testing.assert_array_equal(route["dX"][inactive], dXn[inactive])
+    check_bf16("route dX", route["dX"][sel], ref["dX_route"])
+    check_bf16("dF_out", route["dWb"][sel], ref["dWb"])
+    check_fp32("dh", route["dh"][sel], ref["dh"], BWD_REL)
+    _check_two_roundings("dX", pre["dX"][sel], ref["dX"], ref["dX_route"])
+    check_fp32("dh_pre", pre["dh_pre"][sel], ref["dh_pre"], BWD_REL)
+    errs = {k: check_fp32(k, route[k], ref[k], BWD_REL) for k in ("dphi_act", "db_act", "dalpha")}
+    errs.update({k: check_fp32(k, pre[k], ref[k], BWD_REL) for k in ("dphi_pre", "db_pre")})
+    errs["dalpha_pre"] = check_fp32("dalpha_pre", pre["dalpha"], ref["dalpha_pre"], BWD_REL)
+    note(f"relative L2: {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
+
+
+@pytest.mark.parametrize("N,C,T,m", [(16, 256, 70, 2), (8, 96, 33, 1), (4, 128, 40, 1), (12, 4096, 20, 2)])
+def test_xhc_backward_shapes(N, C, T, m):
+    """Several N (k = 4 active), ragged T, C not a multiple of the 128-channel
+    chunks, the workload's C; N = 4 is the dense case (every stream active)."""
+    note(f"xHC backward N={N} C={C} T={T} m={m} bf16")
+    inp, g, idx = _inputs(500 + N + T, T, N, C, m)
+    route, pre = _gpu(inp, g, idx)
+    _compare(route, pre, _oracle(inp, g, idx), g, idx)
+
+
+def test_xhc_backward_strong_gates():
+    note("xHC backward strong gates N=16 C=512 T=64")
+    inp, g, idx = _inputs(530, 64, 16, 512, 2, strong=True)
+    route, pre = _gpu(inp, g, idx)
+    _compare(route, pre, _oracle(inp, g, idx), g, idx)
+
+
+def test_xhc_backward_deterministic():
+    note("xHC backward determinism N=16 C=1024 T=100")
+    inp, g, idx = _inputs(540, 100, 16, 1024, 2)
+    a, b = _gpu(inp, g, idx), _gpu(inp, g, idx)
+    for x, y in zip(a, b):
+        for k in x:
+            np.testing.assert_array_equal(x[k], y[k], err_msg=k)
+
+
+def test_xhc_backward_full_size():
+    """The N = 16, k = 4, m = 2, C = 4096, T = 8192 workload: dphi, db, dalpha against
+    the oracle over every token (chunks of 256), dX, dF_out and the map gradients
+    on sampled tokens, the pass-through rows on every token."""
+    w = synth.WORKLOADS["xhc_N16_k4_m2_C4096_T8192_bf16_K1"]
+    T, N, C = w["T"], w["N"], w["C"]
+    note(f"xHC backward full size N={N} C={C} T={T} bf16")
+    inp, g, idx = _inputs(w["seed"], T, N, C, w["m"])
+    route, pre = _gpu(inp, g, idx)
+    rng = np.random.default_rng(550)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 126, replace=False)]))
+    _compare(route, pre, _oracle(inp, g, idx, chunk=256, rows=rows), g, idx, rows=rows)
