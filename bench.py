@@ -214,6 +214,65 @@ def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
             "post_stage_GBps": bb["post_stage"] / t_post / 1e9, "main_stage_GBps": bb["main_stage"] / t_main / 1e9}
 
 
+def xhc_backward_bench(torch, hc, dev, reps: int = 10) -> dict:
+    """The xHC routed-step backward (N=16, k=4, m=2, C=4096, T=8192, bf16, K=1):
+    xhc_route_backward then xhc_pre_backward on three rotating state sets (dX
+    updated in place, as a training step does); HIP events around each call of
+    each repetition (median reported). algorithmic_bytes is the one-pass
+    minimum: the route reads x and dX_next on the active rows and F_out and
+    writes dX on the active rows and dF_out; the pre call reads x, dF_in and dX
+    and writes dX over the whole state."""
+    N, k, m, C, T = 16, 4, 2, 4096, 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(6000)
+    rn = lambda *shape, std=1.0: torch.randn(*shape, device=dev, generator=g) * std
+    Xs = [rn(T, N, C).to(torch.bfloat16) for _ in range(3)]
+    dXs = [rn(T, N, C).to(torch.bfloat16) for _ in range(3)]
+    Fs = [rn(T, C).to(torch.bfloat16) for _ in range(3)]
+    dFs = [rn(T, C).to(torch.bfloat16) for _ in range(3)]
+    # an active set of m fixed and k - m routed streams per token, ascending
+    r = torch.rand(T, N - m, device=dev, generator=g).argsort(dim=1)[:, :k - m] + m
+    idx = torch.cat([torch.arange(m, device=dev).expand(T, m), r], 1).sort(dim=1).values.to(torch.int32).contiguous()
+    phi_act = rn(k * C, k + k * k, std=0.02)
+    b_act = torch.zeros(k + k * k, device=dev)
+    b_act[k:] = torch.eye(k, device=dev).flatten()
+    phi_pre, b_pre = rn(N * C, N, std=0.02), torch.zeros(N, device=dev)
+    ws = torch.empty(hc.xhc_backward_workspace_bytes(T, N, C, k, 1, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ro = (torch.empty(T, C, dtype=torch.bfloat16, device=dev), torch.empty(k * C, k + k * k, device=dev),
+          torch.empty(k + k * k, device=dev), torch.empty(2, device=dev), torch.empty(T, k + k * k, device=dev))
+    po = (torch.empty(N * C, N, device=dev), torch.empty(N, device=dev), torch.empty(1, device=dev),
+          torch.empty(T, N, device=dev))
+    route = lambda i: hc.xhc_route_backward(Xs[i % 3], idx, phi_act, b_act, 0.01, 0.01, Fs[i % 3], dXs[i % 3],
+                                            SINKHORN_ITERS, out=ro, workspace=ws)
+    pre = lambda i: hc.xhc_pre_backward(Xs[i % 3], phi_pre, b_pre, 0.01, dFs[i % 3], dXs[i % 3], out=po, workspace=ws)
+    for i in range(3):
+        route(i)
+        pre(i)
+    torch.cuda.synchronize()
+    tr, tp = [], []
+    for i in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        route(i)
+        ev[1].record()
+        pre(i)
+        ev[2].record()
+        torch.cuda.synchronize()
+        tr.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        tp.append(ev[1].elapsed_time(ev[2]) * 1e-3)
+    med = lambda v: sorted(v)[len(v) // 2]
+    t_r, t_p = med(tr), med(tp)
+    s_a, s_f, f = k * C * 2, N * C * 2, C * 2
+    alg_r = T * (2 * s_a + f + s_a + f) + 2 * k * C * (k + k * k) * 4
+    alg_p = T * (s_f + f + s_f + s_f) + 2 * N * C * N * 4
+    rate = lambda b, t: {"us": t * 1e6, "algorithmic_bytes": b, "achieved_GBps": b / t / 1e9,
+                         "pct_hbm_peak": 100.0 * b / t / 1e9 / HBM_PEAK_GBPS}
+    return {"workload": "xHC backward N=16 k=4 m=2 C=4096 T=8192 bf16 K=1 (routed step; 20 Sinkhorn iterations "
+                        "recomputed)",
+            "tokens_per_s": T / (t_r + t_p), "us": (t_r + t_p) * 1e6,
+            "xhc_route_backward": rate(alg_r, t_r), "xhc_pre_backward": rate(alg_p, t_p)}
+
+
 def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     """Throughput of the xHC sublayer (N=16, k=4, m=2, C=4096, T=8192, bf16) on
     seeded synthetic device data: the routed step xhc_pre + xhc_route (K=1, F_out
@@ -579,6 +638,7 @@ def main() -> int:
         result["xhc"] = xhc_bench(torch, hc, dev, max(3, min(args.steps, 20)), 3)
         result["hc_baseline"] = hc_baseline_bench(torch, hc, dev)
         result["backward"] = backward_bench(torch, hc, dev)
+        result["xhc_backward"] = xhc_backward_bench(torch, hc, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
