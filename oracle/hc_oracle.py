@@ -596,3 +596,80 @@ def xhc_pre_backward(X, phi_pre, b_pre, alpha_pre, dF_in):
     dz = dh_pre * h * (1.0 - h)
     dx, dphi, dbias, u = _gates_backward(dz, P, rho, gate, x, phi, N * C)
     return dict(dX=dX + dx.reshape(T, N, C), dphi_pre=dphi, db_pre=dbias, dalpha_pre=u.sum(), dh_pre=dh_pre)
+
+
+def causal_dwconv_backward(F_out, w, batch: int, seq: int, dg):
+    """Gradients of causal_dwconv (g = conv(F_out, w)) for the upstream dg [T, C]:
+    dF[t, c] = sum_s w[c, s] dg[t + kappa - 1 - s, c] (within the sequence: the
+    conv read F[t'] for the outputs t' .. t' + kappa - 1), dw[c, s] = sum over the
+    tokens t of dg[t, c] F[t - kappa + 1 + s, c] (zero before the sequence start).
+    Returns (dF [T, C], dw [C, kappa])."""
+    F = _f64(F_out).reshape(batch, seq, -1)
+    w = _f64(w)
+    G = _f64(dg).reshape(batch, seq, -1)
+    kappa = w.shape[1]
+    C = F.shape[2]
+    padF = np.concatenate([np.zeros((batch, kappa - 1, C)), F], axis=1)
+    padG = np.concatenate([G, np.zeros((batch, kappa - 1, C))], axis=1)
+    dF = np.zeros_like(F)
+    dw = np.zeros_like(w)
+    for s in range(kappa):
+        dF += w[None, None, :, s] * padG[:, kappa - 1 - s:kappa - 1 - s + seq, :]
+        dw[:, s] = np.sum(G * padF[:, s:s + seq, :], axis=(0, 1))
+    return dF.reshape(batch * seq, C), dw
+
+
+def modified_gram_schmidt_backward(comps, dV):
+    """Gradient of modified_gram_schmidt for the upstream dV [T, K_r, C].
+
+    The forward steps are recomputed and walked in reverse. Step (j, i) replaces
+    v by v - (n / d) V_i with n = <v, V_i>, d = <V_i, V_i>; for upstream gv:
+      d v_old = gv - (<V_i, gv> / d) V_i,
+      d V_i  += -(n / d) gv - <V_i, gv> (v_old / d - 2 n V_i / d^2).
+    The steps of component j run after those of every earlier component, so
+    walking j from the last down collects every term of dV_i before V_i's own
+    steps are walked. Returns d comps [T, K_r, C]."""
+    G = _f64(comps)
+    T, Kr, C = G.shape
+    V = np.empty_like(G)
+    V[:, 0] = G[:, 0]
+    steps = {}
+    for j in range(1, Kr):
+        v = G[:, j].copy()
+        for i in range(j):
+            steps[j, i] = v.copy()
+            n = np.sum(v * V[:, i], axis=1)
+            d = np.sum(V[:, i] * V[:, i], axis=1)
+            v = v - (n / d)[:, None] * V[:, i]
+        V[:, j] = v
+    gV = _f64(dV).copy()
+    dU = np.zeros_like(G)
+    for j in range(Kr - 1, 0, -1):
+        gv = gV[:, j].copy()
+        for i in range(j - 1, -1, -1):
+            v_old = steps[j, i]
+            Vi = V[:, i]
+            n = np.sum(v_old * Vi, axis=1)[:, None]
+            d = np.sum(Vi * Vi, axis=1)[:, None]
+            p = np.sum(Vi * gv, axis=1)[:, None]
+            gV[:, i] += -(n / d) * gv - p * (v_old / d - 2.0 * n * Vi / d ** 2)
+            gv = gv - (p / d) * Vi
+        dU[:, j] = gv
+    dU[:, 0] = gV[:, 0]
+    return dU
+
+
+def xhc_augment_backward(F_out, conv_ws, batch: int, seq: int, dV):
+    """Gradients of xhc_augment for the upstream dV [T, K_r, C]: Gram-Schmidt
+    backward, then component 0 (F_out itself) plus each causal conv's backward.
+    Returns dict(dF_out [T, C], dconv_ws [list of [C, kappa]])."""
+    F = _f64(F_out)
+    comps = [F] + [causal_dwconv(F, w, batch, seq) for w in conv_ws]
+    dU = modified_gram_schmidt_backward(np.stack(comps, axis=1), dV)
+    dF = dU[:, 0].copy()
+    dws = []
+    for j, w in enumerate(conv_ws):
+        df, dw = causal_dwconv_backward(F, w, batch, seq, dU[:, j + 1])
+        dF += df
+        dws.append(dw)
+    return dict(dF_out=dF, dconv_ws=dws)

@@ -819,3 +819,37 @@ def test_route_backward_with_every_stream_active_is_the_mhc_backward():
     np.testing.assert_allclose(g["db_act"], ref["dbias"][n:], rtol=1e-12, atol=1e-12)
     assert math.isclose(g["dalpha_post"], ref["dalpha"][1], rel_tol=1e-12)
     assert math.isclose(g["dalpha_res"], ref["dalpha"][2], rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("B,S,C,kappas", [(2, 5, 6, (2, 3, 4)), (1, 7, 5, (4, 8, 12))])
+def test_augment_backward_finite_differences(B, S, C, kappas):
+    """xhc_augment_backward against central differences of L = <dV, V> through
+    xhc_augment: F_out and every conv kernel (kernels longer than the sequence
+    included). C >= K_r keeps the components independent."""
+    rng = np.random.default_rng(370 + S)
+    F = rng.standard_normal((B * S, C))
+    ws = [0.5 * rng.standard_normal((C, k)) for k in kappas]
+    dV = rng.standard_normal((B * S, 4, C))
+    g = O.xhc_augment_backward(F, ws, B, S, dV)
+
+    def L(F, ws):
+        return np.sum(dV * O.xhc_augment(F, ws, B, S))
+    want = _central_difference(lambda a: L(a, ws), F)
+    np.testing.assert_allclose(g["dF_out"], want, rtol=0, atol=1e-7 * np.abs(want).max())
+    for j in range(len(ws)):
+        want = _central_difference(lambda a: L(F, [a if q == j else ws[q] for q in range(len(ws))]), ws[j])
+        np.testing.assert_allclose(g["dconv_ws"][j], want, rtol=0, atol=1e-7 * np.abs(want).max(), err_msg=str(j))
+
+
+def test_conv_backward_adjoint_identities():
+    """The conv is linear in F_out and in w, so <dg, conv(F, w)> equals <dF, F>
+    and <dw, w> exactly (up to rounding) for the backward's dF and dw."""
+    rng = np.random.default_rng(380)
+    B, S, C, k = 3, 9, 4, 5
+    F = rng.standard_normal((B * S, C))
+    w = rng.standard_normal((C, k))
+    dg = rng.standard_normal((B * S, C))
+    dF, dw = O.causal_dwconv_backward(F, w, B, S, dg)
+    val = np.sum(dg * O.causal_dwconv(F, w, B, S))
+    assert math.isclose(np.sum(dF * F), val, rel_tol=1e-12)
+    assert math.isclose(np.sum(dw * w), val, rel_tol=1e-12)
