@@ -290,32 +290,35 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
 
 /*
  * xhc_route_backward, xhc_pre_backward - gradients of the routed xHC step
- * (xhc_pre, then xhc_route with K = 1), the backward of [xHC] steps 2 and 3 with
- * the parameterisation: on the active rows the route is the mHC post/res write
- * with maps formed from the active state alone, so its backward follows the
- * mHC one ([mHC] 4.3.1: the Sinkhorn backward recomputes the iterates on chip;
- * the maps are recomputed from X). The active set is a discrete choice: it and
- * the router weights receive no gradient.
+ * (xhc_pre, then xhc_route with K = 1 or 4 write-back components), the
+ * backward of [xHC] steps 2 and 3 with the parameterisation: on the active rows
+ * the route is the mHC post/res write with maps formed from the active state
+ * alone, so its backward follows the mHC one ([mHC] 4.3.1: the Sinkhorn backward
+ * recomputes the iterates on chip; the maps are recomputed from X). The active
+ * set is a discrete choice: it and the router weights receive no gradient.
  *   X [T, N, C]: the state both forward calls read, i.e. before xhc_route's
  *   in-place update (keep it, or its active rows, for the backward).
  *   xhc_route_backward (first; it does not need dF_in): dX [T, N, C] holds the
  *     upstream gradient dX_next on entry and the route's gradient on exit: rows
  *     outside the active set are left as they are (they pass through); the
  *     active rows become H_res_A^T dX_next_A plus the maps' terms. Also
- *     dWb [T, C] = H_post_A^T dX_next_A (the gradient of F_out), dphi_act
- *     [4C, 20], db_act [20], dalpha [2] (post, res), dh [T, 20] = the map
- *     gradients [dH_post (a) | dH_res (4a + b)]. idx [T, 4] as the forward used
- *     (int32, 16-byte aligned); phi_act, b_act, alpha_*, sinkhorn_iters as for
- *     xhc_route; Wb = F_out [T, C].
+ *     dWb = H_post_A^T dX_next_A, the gradient of the write-back components Wb
+ *     [T, K, C] (bfloat16): K = 1 (Wb = F_out): dWb [T, C] bfloat16; K = 4 (Wb =
+ *     xhc_augment's V): dWb = dV [T, 4, C] float32, the input of
+ *     xhc_augment_backward. dphi_act [4C, 4K + 16], db_act [4K + 16], dalpha [2]
+ *     (post, res), dh [T, 4K + 16] = the map gradients [dH_post (a*K + j) |
+ *     dH_res (4a + b)]. idx [T, 4] as the forward used (int32, 16-byte aligned);
+ *     phi_act, b_act, alpha_*, sinkhorn_iters as for xhc_route.
  *   xhc_pre_backward (once dF_in, the gradient of F_in, is known): adds the
  *     dense read's gradient to dX (in place), and writes dphi_pre [NC, N],
  *     db_pre [N], dalpha [1], dh_pre [T, N] = <dF_in, x_i> (16-byte aligned).
  *   Covered: dtype HC_BF16 (HC_F32 -> HC_ERR_DTYPE), N a multiple of 4 up to 16,
- *   k = 4, K = 1, C a multiple of 32, 1 <= sinkhorn_iters <= HC_MAX_BWD_ITERS
- *   (else HC_ERR_SHAPE). bfloat16 arrays 16 bytes aligned, float arrays 4;
- *   workspace 256 bytes, at least xhc_backward_workspace_bytes (both calls).
- *   dX overlaps nothing else; no output overlaps an input, another output or
- *   the workspace (HC_ERR_ALIAS). Deterministic: every sum runs in a fixed order.
+ *   k = 4, K = 1 or 4, C a multiple of 32, 1 <= sinkhorn_iters <=
+ *   HC_MAX_BWD_ITERS (else HC_ERR_SHAPE). bfloat16 arrays and dWb 16 bytes
+ *   aligned, float arrays 4; workspace 256 bytes, at least
+ *   xhc_backward_workspace_bytes (both calls, either K). dX overlaps nothing
+ *   else; no output overlaps an input, another output or the workspace
+ *   (HC_ERR_ALIAS). Deterministic: every sum runs in a fixed order.
  *   xhc_backward_workspace_bytes: 0 for T = 0, -1 for what the calls do not cover.
  */
 int64_t xhc_backward_workspace_bytes(int64_t T, int N, int64_t C, int k, int K, int dtype);
@@ -353,6 +356,28 @@ int64_t xhc_augment_workspace_bytes(int64_t B, int64_t S, int64_t C, const int* 
 int xhc_augment(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
                 const float* conv_w, const int* kappa, int r,
                 void* V, int v_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * xhc_augment_backward - gradients of xhc_augment ([xHC] temporal feature
+ * augmentation) for the upstream gradient dV [T, 4, C] float32 of its output
+ * (xhc_route_backward's dWb for K = 4): the Gram-Schmidt steps walked in
+ * reverse (recomputed from each token's Gram matrix of [F_out, g_1, g_2, g_3]
+ * and of dV against them, in float64), then each causal conv's transpose:
+ *   dF_out[t, c] = dU_0[t, c] + sum_j sum_d w_j[c, kappa_j - 1 - d] dU_j[t + d, c]
+ *     (within the sequence), stored in `dtype`, rounded once;
+ *   dconv_w[j][c, s] = sum_t dU_j[t, c] F_out[t - kappa_j + 1 + s, c] (zeros before
+ *     the sequence start), float32 in conv_w's layout, summed over all tokens.
+ *   Covered: r = 3 convs of sizes kappa = {4, 8, 12} (else HC_ERR_SHAPE), F_out
+ *   bfloat16 or float32, any C. No epsilon (as the forward): a token whose
+ *   components are linearly dependent gives non-finite values.
+ *   Workspace: xhc_augment_backward_workspace_bytes (0 when B*S = 0, -1 for what
+ *   the call does not cover). Deterministic: every sum runs in a fixed order.
+ */
+int64_t xhc_augment_backward_workspace_bytes(int64_t B, int64_t S, int64_t C, const int* kappa, int r, int dtype);
+int xhc_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
+                         const float* conv_w, const int* kappa, int r, const float* dV,
+                         void* dF_out, float* dconv_w, void* workspace, int64_t workspace_bytes,
+                         void* stream);
 
 /* ----------------------------------------- HC baseline and gain diagnostic -- */
 

@@ -59,6 +59,9 @@ _SIGS = {
                                     _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "xhc_pre_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _c_i64, _vp]),
+    "xhc_augment_backward_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int]),
+    "xhc_augment_backward": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                      _c_i64, _vp]),
     "hc_copy_probe": (_c_int, [_vp, _vp, _c_i64, _vp]),
     "hc_tanh_coeffs": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _c_float, _c_float, _c_float,
                                 _vp, _vp, _vp, _vp]),
@@ -462,28 +465,34 @@ def xhc_backward_workspace_bytes(T: int, N: int, C: int, k: int, K: int, dtype) 
     return int(lib().xhc_backward_workspace_bytes(T, N, C, k, K, _DT[dtype]))
 
 
-def xhc_route_backward(X, idx, phi_act, b_act, alpha_post, alpha_res, F_out, dX, sinkhorn_iters=20, *, out=None,
+def xhc_route_backward(X, idx, phi_act, b_act, alpha_post, alpha_res, Wb, dX, sinkhorn_iters=20, *, out=None,
                        workspace=None, stream=None):
-    """Backward of xhc_route (k = 4, K = 1, bfloat16). X: the state before the route;
-    dX holds dX_next and is updated in place to the route's gradient. Returns
-    (dX, dF_out, dphi_act, db_act, dalpha [post, res], dh [T, 20])."""
+    """Backward of xhc_route (k = 4, bfloat16). X: the state before the route; Wb: F_out
+    [T, C] (K = 1) or the augmentation's V [T, 4, C] (K = 4); dX holds dX_next and is
+    updated in place to the route's gradient. Returns (dX, dWb, dphi_act, db_act,
+    dalpha [post, res], dh [T, 4K + 16]); dWb is bfloat16 [T, C] for K = 1 and
+    float32 [T, 4, C] for K = 4."""
     X = _dev_tensor(X, "X", (torch.bfloat16,))
     T, N, C = X.shape
     idx = _dev_tensor(idx, "idx", (torch.int32,))
     k = idx.shape[1]
-    F_out = _dev_tensor(F_out, "F_out", (X.dtype,))
+    Wb = _dev_tensor(Wb, "Wb", (X.dtype,))
+    K = 1 if Wb.dim() == 2 else Wb.shape[1]
     dX = _dev_tensor(dX, "dX", (X.dtype,))
+    nc = k * K + k * k
     if out is None:
         dev = X.device
-        out = (torch.empty(T, C, dtype=X.dtype, device=dev), torch.empty(k * C, k + k * k, device=dev),
-               torch.empty(k + k * k, device=dev), torch.empty(2, device=dev), torch.empty(T, k + k * k, device=dev))
-    dF_out, dphi, db, dalpha, dh = out
-    ws = _workspace(xhc_backward_workspace_bytes(T, N, C, k, 1, X.dtype), X.device, workspace)
+        dWb = (torch.empty(T, C, dtype=X.dtype, device=dev) if K == 1 else
+               torch.empty(T, K, C, dtype=torch.float32, device=dev))
+        out = (dWb, torch.empty(k * C, nc, device=dev), torch.empty(nc, device=dev), torch.empty(2, device=dev),
+               torch.empty(T, nc, device=dev))
+    dWb, dphi, db, dalpha, dh = out
+    ws = _workspace(xhc_backward_workspace_bytes(T, N, C, k, K, X.dtype), X.device, workspace)
     _check("xhc_route_backward", lib().xhc_route_backward(
         _ptr(X), _DT[X.dtype], T, N, C, k, _ptr(idx), _ptr(_f32(phi_act, "phi_act")), _ptr(_f32(b_act, "b_act")),
-        float(alpha_post), float(alpha_res), int(sinkhorn_iters), _ptr(F_out), 1, _ptr(dX), _ptr(dF_out), _ptr(dphi),
+        float(alpha_post), float(alpha_res), int(sinkhorn_iters), _ptr(Wb), K, _ptr(dX), _ptr(dWb), _ptr(dphi),
         _ptr(db), _ptr(dalpha), _ptr(dh), _ptr(ws), ws.numel(), _stream(X.device, stream)))
-    return dX, dF_out, dphi, db, dalpha, dh
+    return dX, dWb, dphi, db, dalpha, dh
 
 
 def xhc_pre_backward(X, phi_pre, b_pre, alpha_pre, dF_in, dX, *, out=None, workspace=None, stream=None):
@@ -506,6 +515,29 @@ def xhc_pre_backward(X, phi_pre, b_pre, alpha_pre, dF_in, dX, *, out=None, works
     return dX, dphi, db, dalpha, dh
 
 
+def xhc_augment_backward_workspace_bytes(B: int, S: int, C: int, kappas, dtype) -> int:
+    k = (ctypes.c_int * len(kappas))(*[int(x) for x in kappas])
+    return int(lib().xhc_augment_backward_workspace_bytes(B, S, C, k, len(kappas), _DT[dtype]))
+
+
+def xhc_augment_backward(F_out, conv_w, kappas, B, S, dV, *, out=None, workspace=None, stream=None):
+    """Backward of xhc_augment (kappas (4, 8, 12)): dV [T, 4, C] float32 in; returns
+    (dF_out [T, C] in F_out's dtype, dconv_w in conv_w's layout)."""
+    F_out = _dev_tensor(F_out, "F_out", _DT)
+    T, C = F_out.shape
+    dV = _f32(dV, "dV")
+    conv_w = _f32(conv_w, "conv_w")
+    if out is None:
+        out = (torch.empty_like(F_out), torch.empty_like(conv_w))
+    dF, dw = out
+    k = (ctypes.c_int * len(kappas))(*[int(x) for x in kappas])
+    ws = _workspace(xhc_augment_backward_workspace_bytes(B, S, C, kappas, F_out.dtype), F_out.device, workspace)
+    _check("xhc_augment_backward", lib().xhc_augment_backward(
+        _ptr(F_out), _DT[F_out.dtype], B, S, C, _ptr(conv_w), k, len(kappas), _ptr(dV), _ptr(dF), _ptr(dw),
+        _ptr(ws), ws.numel(), _stream(F_out.device, stream)))
+    return dF, dw
+
+
 def hc_copy_probe(src, dst, *, stream=None):
     """Copy src into dst (same byte size, 16-byte aligned) with the library's streaming
     copy: a measurement probe of the device's streaming rate, not part of the method."""
@@ -521,7 +553,7 @@ def hc_copy_probe(src, dst, *, stream=None):
 __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
     "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward_post", "hc_backward", "xhc_backward_workspace_bytes",
-    "xhc_route_backward", "xhc_pre_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
+    "xhc_route_backward", "xhc_pre_backward", "xhc_augment_backward_workspace_bytes", "xhc_augment_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
     "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",

@@ -330,7 +330,8 @@ int xhc_route_backward(const void* X, int dtype, int64_t T, int N, int64_t C, in
                        void* stream) {
   int s = check_xhc_backward_shape(dtype, T, N, C);
   if (s != HC_OK) return s;
-  if (k != 4 || K != 1 || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_BWD_ITERS) return HC_ERR_SHAPE;
+  if (k != 4 || (K != 1 && K != 4) || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_BWD_ITERS)
+    return HC_ERR_SHAPE;
   if (T == 0) return HC_OK;
   if (!hc::fast_xhc_backward_supported(dtype, N, k, K, T, C, sinkhorn_iters)) return HC_ERR_SHAPE;
   if (!X || !idx || !phi_act || !b_act || !Wb || !dX || !dWb || !dphi_act || !db_act || !dalpha || !dh)
@@ -342,24 +343,27 @@ int xhc_route_backward(const void* X, int dtype, int64_t T, int N, int64_t C, in
     if (!aligned_to(p, 4)) return HC_ERR_ALIGN;
   const int64_t wsb = hc::fast_xhc_backward_ws_bytes(T, N, C);
   if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
-  const int64_t xb = T * N * C * 2, fb = T * C * 2, pb = 4 * C * 20 * 4;
+  const int ncol = 4 * K + 16;
+  // Wb: K bfloat16 rows per token; dWb: bfloat16 for K = 1, float32 for K = 4
+  const int64_t xb = T * N * C * 2, wb = T * K * C * 2, dwb = K == 1 ? T * C * 2 : T * K * C * 4;
+  const int64_t pb = 4 * C * ncol * 4;
   // dX is read and written: it may overlap nothing else
   const void* ins[6] = {X, idx, phi_act, b_act, Wb, dX};
-  const int64_t ib[6] = {xb, T * 4 * 4, pb, 20 * 4, fb, xb};
+  const int64_t ib[6] = {xb, T * 4 * 4, pb, ncol * 4, wb, xb};
   const void* outs[6] = {dWb, dphi_act, db_act, dalpha, dh, workspace};
-  const int64_t ob[6] = {fb, pb, 20 * 4, 2 * 4, T * 20 * 4, wsb};
+  const int64_t ob[6] = {dwb, pb, ncol * 4, 2 * 4, T * ncol * 4, wsb};
   if (any_overlap(outs, ob, 6, ins, ib, 6)) return HC_ERR_ALIAS;
   {
     const void* i2[5] = {X, idx, phi_act, b_act, Wb};
-    const int64_t b2[5] = {xb, T * 4 * 4, pb, 20 * 4, fb};
+    const int64_t b2[5] = {xb, T * 4 * 4, pb, ncol * 4, wb};
     const void* o2[1] = {dX};
     const int64_t ob2[1] = {xb};
     if (any_overlap(o2, ob2, 1, i2, b2, 5)) return HC_ERR_ALIAS;
   }
   if ((s = device_status()) != HC_OK) return s;
   return launch_status(hc::launch_fast_xroute_backward(X, T, N, C, idx, phi_act, b_act, alpha_post, alpha_res,
-                                                       sinkhorn_iters, Wb, dX, dWb, dphi_act, db_act, dalpha, dh,
-                                                       workspace, (hipStream_t)stream));
+                                                       sinkhorn_iters, Wb, K, dX, dWb, dphi_act, db_act, dalpha,
+                                                       dh, workspace, (hipStream_t)stream));
 }
 
 int xhc_pre_backward(const void* X, int dtype, int64_t T, int N, int64_t C, const float* phi_pre, const float* b_pre,
@@ -392,6 +396,38 @@ int xhc_pre_backward(const void* X, int dtype, int64_t T, int N, int64_t C, cons
   if ((s = device_status()) != HC_OK) return s;
   return launch_status(hc::launch_fast_xpre_backward(X, T, N, C, phi_pre, b_pre, alpha_pre, dF_in, dX, dphi_pre,
                                                      db_pre, dalpha, dh_pre, workspace, (hipStream_t)stream));
+}
+
+int64_t xhc_augment_backward_workspace_bytes(int64_t B, int64_t S, int64_t C, const int* kappa, int r, int dtype) {
+  if (B < 0 || S < 0 || C < 1) return -1;
+  if (B == 0 || S == 0) return 0;
+  if (!hc::fast_augment_backward_supported(dtype, B, S, C, kappa, r)) return -1;
+  return hc::fast_augment_backward_ws_bytes(B, S, C);
+}
+
+int xhc_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C, const float* conv_w,
+                         const int* kappa, int r, const float* dV, void* dF_out, float* dconv_w, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (B < 0 || S < 0 || C < 1 || C > (1ll << 26) || r != 3 || !kappa) return HC_ERR_SHAPE;
+  if (B == 0 || S == 0) return HC_OK;
+  if (!hc::fast_augment_backward_supported(dtype, B, S, C, kappa, r)) return HC_ERR_SHAPE;
+  if (!F_out || !conv_w || !dV || !dF_out || !dconv_w) return HC_ERR_NULL;
+  if (!aligned_to(F_out, esize(dtype)) || !aligned_to(dF_out, esize(dtype)) || !aligned_to(conv_w, 4) ||
+      !aligned_to(dV, 4) || !aligned_to(dconv_w, 4))
+    return HC_ERR_ALIGN;
+  const int64_t wsb = hc::fast_augment_backward_ws_bytes(B, S, C);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t T = B * S, fb = T * C * esize(dtype), wb = C * 24 * 4;
+  const void* ins[3] = {F_out, conv_w, dV};
+  const int64_t ib[3] = {fb, wb, T * 4 * C * 4};
+  const void* outs[3] = {dF_out, dconv_w, workspace};
+  const int64_t ob[3] = {fb, wb, wsb};
+  if (any_overlap(outs, ob, 3, ins, ib, 3)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_fast_augment_backward(F_out, dtype, B, S, C, conv_w, dV, dF_out, dconv_w,
+                                                        workspace, (hipStream_t)stream));
 }
 
 int hc_post(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,

@@ -36,7 +36,7 @@ typedef unsigned u4_t __attribute__((ext_vector_type(4)));
 constexpr int BS = 4;     // streams
 constexpr int BCOL = 24;  // n*n + 2n columns: [pre 4 | post 4 | res 16]
 constexpr int DPS = 32;   // floats per dP row (columns 24..31 zero)
-constexpr int RED = 28;   // floats per row of the per-token sums
+constexpr int RED = 36;   // floats per row of the sums over 16 tokens: dz [32] | 3 gate sums | 0
 
 // Row modes of the passes: which stream row of a token slot i (of 4) is, and
 // which phi rows it multiplies.
@@ -93,70 +93,91 @@ __device__ __forceinline__ void split_bf8(const float v[8], uint4& hi, uint4& lo
 // ------------------------------------------------------- per-token sums
 
 // One 256-thread workgroup per token t (post stage), over the 4 slots of the
-// row mode (the n = 4 state, or the xHC active set with the write-back F_out):
-// dF_out = sum_i H_post[i] dX_next_i (rounded once to bfloat16) and the sums
-// over the channels
-//   dh[off + i]          = dH_post[i]    = <dX_next_i, F_out>
-//   dh[off + 4 + 4i + j] = dH_res[i][j]  = <dX_next_i, x_j>
-// (dh rows of dhs floats). Thread tid takes the 8-channel chunks tid,
-// tid + 256, ...; the threads' sums are added by a butterfly in each wave and
-// then the 4 waves in order.
-template <int BM>
+// row mode (the n = 4 state, or the xHC active set) with K write-back
+// components Wb_j (the n = 4 state and K = 1: F_out):
+//   dWb_j = sum_i H_post[i, j] dX_next_i     (K = 1: bfloat16, rounded once;
+//                                             K = 4: float32, for the
+//                                             augmentation backward)
+//   dh[off + i*K + j]          = dH_post[i, j] = <dX_next_i, Wb_j>
+//   dh[off + 4K + 4i + k]      = dH_res[i][k]  = <dX_next_i, x_k>
+// (dh rows of dhs floats; h_post [T, 4K] as the forward formed it). Thread tid
+// takes the 8-channel chunks tid, tid + 256, ...; the threads' sums are added
+// by a butterfly in each wave and then the 4 waves in order.
+template <int BM, int K>
 __global__ __launch_bounds__(256) void bwd_post_kernel(const uint16_t* __restrict__ X,
                                                        const uint16_t* __restrict__ dXn,
-                                                       const uint16_t* __restrict__ Fo, int64_t C, int N,
+                                                       const uint16_t* __restrict__ Wb, int64_t C, int N,
                                                        const int32_t* __restrict__ idx,
                                                        const float* __restrict__ h_post, float* __restrict__ dh,
-                                                       int dhs, int off, uint16_t* __restrict__ dFo) {
-  __shared__ float wsum[4][20];
+                                                       int dhs, int off, void* __restrict__ dWb) {
+  constexpr int NA = 4 * K + 16;  // sums per token
+  __shared__ float wsum[4][NA];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
-  const float4 hq = *reinterpret_cast<const float4*>(h_post + t * 4);
-  const float hpost[4] = {hq.x, hq.y, hq.z, hq.w};
-  float acc[20];
+  float hpost[4][K];  // hpost[i][j] = H_post[i, j]
 #pragma unroll
-  for (int k = 0; k < 20; ++k) acc[k] = 0.f;
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < K; ++j) hpost[i][j] = h_post[t * 4 * K + i * K + j];
+  float acc[NA];
+#pragma unroll
+  for (int k = 0; k < NA; ++k) acc[k] = 0.f;
   const int64_t nch = C / 8;
   int sl[4];
   slot_streams<BM>(idx, t, N, sl);
   for (int64_t j = tid; j < nch; j += 256) {
     const int64_t c = j * 8;
-    uint4 xq[BS], dq[BS];
+    uint4 xq[BS], dq[BS], wq[K];
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
       xq[i] = ld_nt16(X + (t * N + sl[i]) * C + c);
       dq[i] = ld_nt16(dXn + (t * N + sl[i]) * C + c);
     }
-    const uint4 fq = ld_nt16(Fo + t * C + c);
-    float x[BS][8], d[BS][8], f[8], o[8];
+#pragma unroll
+    for (int q = 0; q < K; ++q) wq[q] = ld_nt16(Wb + (t * K + q) * C + c);
+    float x[BS][8], d[BS][8], f[K][8];
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
       unpack_bf8(xq[i], x[i]);
       unpack_bf8(dq[i], d[i]);
     }
-    unpack_bf8(fq, f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[e] = hpost[0] * d[0][e] + hpost[1] * d[1][e] + hpost[2] * d[2][e] + hpost[3] * d[3][e];
+    for (int q = 0; q < K; ++q) unpack_bf8(wq[q], f[q]);
 #pragma unroll
-      for (int i = 0; i < BS; ++i) {
-        acc[i] += d[i][e] * f[e];
+    for (int q = 0; q < K; ++q) {
+      float o[8];
 #pragma unroll
-        for (int k = 0; k < BS; ++k) acc[4 + 4 * i + k] += d[i][e] * x[k][e];
+      for (int e = 0; e < 8; ++e)
+        o[e] = hpost[0][q] * d[0][e] + hpost[1][q] * d[1][e] + hpost[2][q] * d[2][e] + hpost[3][q] * d[3][e];
+      if constexpr (K == 1) {
+        __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
+                                         pack_bf2_hw(o[6], o[7])},
+                                    reinterpret_cast<u4_t*>(reinterpret_cast<uint16_t*>(dWb) + t * C + c));
+      } else {
+        float* dst = reinterpret_cast<float*>(dWb) + (t * K + q) * C + c;
+        __builtin_nontemporal_store(f4_t{o[0], o[1], o[2], o[3]}, reinterpret_cast<f4_t*>(dst));
+        __builtin_nontemporal_store(f4_t{o[4], o[5], o[6], o[7]}, reinterpret_cast<f4_t*>(dst) + 1);
       }
     }
-    __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]), pack_bf2_hw(o[4], o[5]),
-                                     pack_bf2_hw(o[6], o[7])},
-                                reinterpret_cast<u4_t*>(dFo + t * C + c));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+#pragma unroll
+        for (int q = 0; q < K; ++q) acc[i * K + q] += d[i][e] * f[q][e];
+#pragma unroll
+        for (int k = 0; k < BS; ++k) acc[4 * K + 4 * i + k] += d[i][e] * x[k][e];
+      }
+    }
   }
 #pragma unroll
-  for (int k = 0; k < 20; ++k) acc[k] = wave_sum(acc[k]);
+  for (int k = 0; k < NA; ++k) acc[k] = wave_sum(acc[k]);
   if ((tid & 63) == 0) {
 #pragma unroll
-    for (int k = 0; k < 20; ++k) wsum[tid >> 6][k] = acc[k];
+    for (int k = 0; k < NA; ++k) wsum[tid >> 6][k] = acc[k];
   }
   __syncthreads();
-  if (tid < 20) dh[t * dhs + off + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+  if (tid < NA) dh[t * dhs + off + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // One 256-thread workgroup per token t (main stage): dh[i] = dH_pre[i] =
@@ -524,6 +545,317 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
   }
 }
 
+// ------------------------------------------ temporal augmentation backward
+
+// Backward of xhc_augment for r = 3 causal depthwise convs of sizes 4, 8, 12
+// ([xHC] temporal feature augmentation): components u_0 = F_out, u_j = conv_j
+// (F_out), V = modified Gram-Schmidt of [u_0..u_3]; upstream dV [T, 4, C]
+// float32. Per token every vector involved lies in the span of u_0..u_3 and
+// dV_0..dV_3, so the Gram-Schmidt backward needs only the Gram matrix G = U U^T
+// and M = dV U^T (26 sums over the channels): dU_i = sum_q P[i][q] dV_q +
+// sum_k Q[i][k] u_k with 4 x 4 matrices P, Q from G and M. Four launches:
+//  1. aug_bwd_gram_kernel: one thread per channel walks a strip of tokens with
+//     the last 12 rows of F_out in registers (zeros before each sequence
+//     start), forms u_1..u_3 and the 26 products, adds them over each wave's
+//     64 channels, and stores the wave sums [T][waves][26];
+//  2. aug_bwd_coef_kernel: per token the wave sums added in order, then the
+//     Gram-Schmidt steps recomputed and walked in reverse in float64 on the
+//     4-coefficient representation: P, Q [T][32];
+//  3. aug_bwd_walk_kernel: one thread per channel walks a strip backwards (plus
+//     the 11 tokens after it, within the sequence): dU from P, Q, the window of
+//     the next 11 tokens' dU_j, dF_out[t] = dU_0[t] + sum_j sum_d w_j[kappa_j -
+//     1 - d] dU_j[t + d] (the conv's transpose), and the tap gradients dw_j[s] +=
+//     dU_j[t] F_out[t - kappa_j + 1 + s] summed over the strip's tokens;
+//  4. aug_bwd_wsum_kernel: the strips' tap sums added in strip order.
+constexpr int AB_STRIP = 128;  // tokens per strip
+constexpr int AB_NV = 26;      // sums per token: G (10, upper triangle) | M (16, M[j][i] = <dV_j, u_i>)
+constexpr int AB_K1 = 4, AB_K2 = 8, AB_K3 = 12, AB_TAPS = AB_K1 + AB_K2 + AB_K3;
+
+template <typename TF>
+__device__ __forceinline__ float ab_ld(const TF* p) {
+  if constexpr (sizeof(TF) == 2) return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+  else return *reinterpret_cast<const float*>(p);
+}
+
+// the three convs at the current token from the window win[0..11] = F_out[t-11..t]
+__device__ __forceinline__ void ab_convs(const float (&w)[AB_TAPS], const float (&win)[12], float (&u)[4]) {
+  u[0] = win[11];
+  float a = 0.f, b = 0.f, c = 0.f;
+#pragma unroll
+  for (int s = 0; s < AB_K1; ++s) a += w[s] * win[12 - AB_K1 + s];
+#pragma unroll
+  for (int s = 0; s < AB_K2; ++s) b += w[AB_K1 + s] * win[12 - AB_K2 + s];
+#pragma unroll
+  for (int s = 0; s < AB_K3; ++s) c += w[AB_K1 + AB_K2 + s] * win[12 - AB_K3 + s];
+  u[1] = a;
+  u[2] = b;
+  u[3] = c;
+}
+
+// taps of channel c (conv_w = [C, 4] | [C, 8] | [C, 12])
+__device__ __forceinline__ void ab_taps(const float* __restrict__ conv_w, int64_t C, int64_t c, float (&w)[AB_TAPS]) {
+#pragma unroll
+  for (int s = 0; s < AB_K1; ++s) w[s] = conv_w[c * AB_K1 + s];
+#pragma unroll
+  for (int s = 0; s < AB_K2; ++s) w[AB_K1 + s] = conv_w[AB_K1 * C + c * AB_K2 + s];
+#pragma unroll
+  for (int s = 0; s < AB_K3; ++s) w[AB_K1 + AB_K2 + s] = conv_w[(AB_K1 + AB_K2) * C + c * AB_K3 + s];
+}
+
+template <typename TF>
+__global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict__ F, int64_t T, int64_t S, int64_t C,
+                                                           const float* __restrict__ conv_w,
+                                                           const float* __restrict__ dV, float* __restrict__ part) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
+  const bool cok = c0 < C;
+  const int64_t c = cok ? c0 : C - 1;
+  const int64_t nw = (C + 63) / 64, wg = c0 >> 6;
+  const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
+  const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;
+  float w[AB_TAPS];
+  ab_taps(conv_w, C, c, w);
+  float win[12];  // before the first step: F_out[t0-12..t0-1], zero before the sequence start
+  const int64_t ss0 = t0 - t0 % S;  // first token of t0's sequence
+#pragma unroll
+  for (int s = 0; s < 12; ++s) {
+    const int64_t tt = t0 - 12 + s;
+    win[s] = tt >= ss0 ? ab_ld(F + tt * C + c) : 0.f;
+  }
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t % S == 0) {
+#pragma unroll
+      for (int s = 0; s < 12; ++s) win[s] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < 11; ++s) win[s] = win[s + 1];
+    win[11] = ab_ld(F + t * C + c);
+    float u[4], v[AB_NV];
+    ab_convs(w, win, u);
+    float dv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dv[j] = dV[(t * 4 + j) * C + c];
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = i; k < 4; ++k) v[n++] = u[i] * u[k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[10 + 4 * j + i] = dv[j] * u[i];
+#pragma unroll
+    for (int k = 0; k < AB_NV; ++k) v[k] = wave_sum(cok ? v[k] : 0.f);
+    if (lane == 0 && wg < nw) {
+#pragma unroll
+      for (int k = 0; k < AB_NV; ++k) part[(t * nw + wg) * AB_NV + k] = v[k];
+    }
+  }
+}
+
+// One wave per token: lane k < 26 adds sum k over the channel waves in order;
+// lane 0 then forms P and Q in float64.
+__global__ __launch_bounds__(64) void aug_bwd_coef_kernel(const float* __restrict__ part, int64_t T, int nw,
+                                                          float* __restrict__ coef) {
+  __shared__ double sv[AB_NV];
+  const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (lane < AB_NV) {
+    float s = 0.f;
+    for (int q = 0; q < nw; ++q) s += part[(t * nw + q) * AB_NV + lane];
+    sv[lane] = (double)s;
+  }
+  __syncthreads();
+  if (lane != 0) return;
+  double G[4][4], M[4][4];
+  {
+    int n = 0;
+    for (int i = 0; i < 4; ++i)
+      for (int k = i; k < 4; ++k) G[i][k] = G[k][i] = sv[n++];
+    for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < 4; ++i) M[j][i] = sv[10 + 4 * j + i];
+  }
+  auto gdot = [&](const double* a, const double* b) {  // <sum a_k u_k, sum b_l u_l>
+    double r = 0.0;
+    for (int k = 0; k < 4; ++k)
+      for (int l = 0; l < 4; ++l) r += a[k] * G[k][l] * b[l];
+    return r;
+  };
+  // forward: V_j = sum_k B[j][k] u_k, with the steps' v, n, d kept
+  double B[4][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}};
+  double vold[4][4][4], nn[4][4], dd[4][4];
+  for (int j = 1; j < 4; ++j) {
+    double v[4] = {0, 0, 0, 0};
+    v[j] = 1.0;
+    for (int i = 0; i < j; ++i) {
+      for (int k = 0; k < 4; ++k) vold[j][i][k] = v[k];
+      const double n = gdot(v, B[i]), d = gdot(B[i], B[i]);
+      nn[j][i] = n;
+      dd[j][i] = d;
+      for (int k = 0; k < 4; ++k) v[k] -= (n / d) * B[i][k];
+    }
+    for (int k = 0; k < 4; ++k) B[j][k] = v[k];
+  }
+  // reverse: a gradient vector is sum_q ga[q] dV_q + sum_k gb[k] u_k
+  double ga[4][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}}, gb[4][4] = {};
+  double P[4][4], Q[4][4];
+  for (int j = 3; j >= 1; --j) {
+    double a[4], b[4];
+    for (int k = 0; k < 4; ++k) {
+      a[k] = ga[j][k];
+      b[k] = gb[j][k];
+    }
+    for (int i = j - 1; i >= 0; --i) {
+      double p = 0.0;  // <V_i, g>
+      for (int k = 0; k < 4; ++k) {
+        double gk = 0.0;  // <u_k, g>
+        for (int q = 0; q < 4; ++q) gk += M[q][k] * a[q];
+        for (int l = 0; l < 4; ++l) gk += G[k][l] * b[l];
+        p += B[i][k] * gk;
+      }
+      const double n = nn[j][i], d = dd[j][i];
+      for (int k = 0; k < 4; ++k) {
+        ga[i][k] += -(n / d) * a[k];
+        gb[i][k] += -(n / d) * b[k] - p * (vold[j][i][k] / d - 2.0 * n * B[i][k] / (d * d));
+      }
+      for (int k = 0; k < 4; ++k) b[k] -= (p / d) * B[i][k];
+    }
+    for (int k = 0; k < 4; ++k) {
+      P[j][k] = a[k];
+      Q[j][k] = b[k];
+    }
+  }
+  for (int k = 0; k < 4; ++k) {
+    P[0][k] = ga[0][k];
+    Q[0][k] = gb[0][k];
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int k = 0; k < 4; ++k) {
+      coef[t * 32 + i * 4 + k] = (float)P[i][k];
+      coef[t * 32 + 16 + i * 4 + k] = (float)Q[i][k];
+    }
+}
+
+template <typename TF>
+__global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict__ F, int64_t T, int64_t S, int64_t C,
+                                                           const float* __restrict__ conv_w,
+                                                           const float* __restrict__ dV,
+                                                           const float* __restrict__ coef, TF* __restrict__ dF,
+                                                           float* __restrict__ wpart) {
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
+  const bool cok = c0 < C;
+  const int64_t c = cok ? c0 : C - 1;
+  const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
+  const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;  // strip [t0, t1)
+  // the walk starts up to 11 tokens after the strip, inside t1 - 1's sequence
+  const int64_t se = (t1 - 1) - (t1 - 1) % S + S;           // end of that sequence
+  const int64_t top = (t1 + 11 < se ? t1 + 11 : se) - 1;
+  float w[AB_TAPS];
+  ab_taps(conv_w, C, c, w);
+  float dw[AB_TAPS];
+#pragma unroll
+  for (int k = 0; k < AB_TAPS; ++k) dw[k] = 0.f;
+  float f1[AB_K1], f2[AB_K2], f3[AB_K3];  // fj[d] = dU_j[t + d], zero past the sequence
+#pragma unroll
+  for (int d = 0; d < AB_K1; ++d) f1[d] = 0.f;
+#pragma unroll
+  for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
+#pragma unroll
+  for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
+  float win[12];  // F_out[t-11..t], zero before the sequence start
+  auto load_win = [&](int64_t t) {
+    const int64_t ss = t - t % S;
+#pragma unroll
+    for (int s = 0; s < 12; ++s) {
+      const int64_t tt = t - 11 + s;
+      win[s] = tt >= ss ? ab_ld(F + tt * C + c) : 0.f;
+    }
+  };
+  load_win(top);
+  for (int64_t t = top; t >= t0; --t) {
+    float u[4];
+    ab_convs(w, win, u);
+    float dv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dv[j] = dV[(t * 4 + j) * C + c];
+    const float* cf = coef + t * 32;
+    float dU[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += cf[i * 4 + q] * dv[q];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s += cf[16 + i * 4 + k] * u[k];
+      dU[i] = s;
+    }
+#pragma unroll
+    for (int d = AB_K1 - 1; d > 0; --d) f1[d] = f1[d - 1];
+#pragma unroll
+    for (int d = AB_K2 - 1; d > 0; --d) f2[d] = f2[d - 1];
+#pragma unroll
+    for (int d = AB_K3 - 1; d > 0; --d) f3[d] = f3[d - 1];
+    f1[0] = dU[1];
+    f2[0] = dU[2];
+    f3[0] = dU[3];
+    if (t < t1) {
+      float g = dU[0];
+#pragma unroll
+      for (int d = 0; d < AB_K1; ++d) g += w[AB_K1 - 1 - d] * f1[d];
+#pragma unroll
+      for (int d = 0; d < AB_K2; ++d) g += w[AB_K1 + AB_K2 - 1 - d] * f2[d];
+#pragma unroll
+      for (int d = 0; d < AB_K3; ++d) g += w[AB_TAPS - 1 - d] * f3[d];
+      if (cok) {
+        if constexpr (sizeof(TF) == 2) reinterpret_cast<uint16_t*>(dF)[t * C + c] = (uint16_t)f2bf(g);
+        else reinterpret_cast<float*>(dF)[t * C + c] = g;
+      }
+#pragma unroll
+      for (int s = 0; s < AB_K1; ++s) dw[s] += dU[1] * win[12 - AB_K1 + s];
+#pragma unroll
+      for (int s = 0; s < AB_K2; ++s) dw[AB_K1 + s] += dU[2] * win[12 - AB_K2 + s];
+#pragma unroll
+      for (int s = 0; s < AB_K3; ++s) dw[AB_K1 + AB_K2 + s] += dU[3] * win[12 - AB_K3 + s];
+    }
+    if (t == t0) break;
+    if (t % S == 0) {  // t - 1 is in the previous sequence: nothing of this one reaches it
+#pragma unroll
+      for (int d = 0; d < AB_K1; ++d) f1[d] = 0.f;
+#pragma unroll
+      for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
+#pragma unroll
+      for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
+      load_win(t - 1);
+    } else {
+#pragma unroll
+      for (int s = 11; s > 0; --s) win[s] = win[s - 1];
+      const int64_t tt = t - 12;
+      win[0] = tt >= t - t % S ? ab_ld(F + tt * C + c) : 0.f;
+    }
+  }
+  if (cok) {
+#pragma unroll
+    for (int k = 0; k < AB_TAPS; ++k) wpart[((int64_t)blockIdx.y * C + c) * AB_TAPS + k] = dw[k];
+  }
+}
+
+// dconv_w in conv_w's layout from the strips' sums (strip order); one thread per tap.
+__global__ __launch_bounds__(256) void aug_bwd_wsum_kernel(const float* __restrict__ wpart, int nstrip, int64_t C,
+                                                           float* __restrict__ dconv) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= C * AB_TAPS) return;
+  const int64_t c = g / AB_TAPS;
+  const int k = (int)(g - c * AB_TAPS);
+  float s = 0.f;
+  for (int q = 0; q < nstrip; ++q) s += wpart[((int64_t)q * C + c) * AB_TAPS + k];
+  int64_t o;
+  if (k < AB_K1) o = c * AB_K1 + k;
+  else if (k < AB_K1 + AB_K2) o = AB_K1 * C + c * AB_K2 + (k - AB_K1);
+  else o = (AB_K1 + AB_K2) * C + c * AB_K3 + (k - AB_K1 - AB_K2);
+  dconv[o] = s;
+}
+
 int ncu_of_device() {
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -576,7 +908,7 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pby
   w.partial = (float*)take(qbytes);
   w.phi_rows = (uint4*)take(nrows * 128);
   w.h_pre = (float*)take(T * hp * 4);
-  w.h_post = route ? (float*)take(T * 4 * 4) : nullptr;
+  w.h_post = route ? (float*)take(T * 16 * 4) : nullptr;
   w.h_res = (float*)take(T * 16 * 4);
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
@@ -591,9 +923,12 @@ BwdWs carve_mhc(void* ws, int64_t T, int64_t C, int64_t* total) {
   return carve(ws, T, C, BS * C, BCOL, fast_coeffs_packed_bytes(4, C, 1), fast_coeffs_partial_bytes(T, 4, C, 1), 4,
                false, total);
 }
-// route: phi_act [4C, 20] packed as 3 x 16 columns (48 x 16 bytes per 8 rows)
-BwdWs carve_route(void* ws, int64_t T, int64_t C, int64_t* total) {
-  return carve(ws, T, C, BS * C, 20, BS * C / 8 * 48 * 16, fast_xroute_partial_bytes(T, C), 4, true, total);
+// route with K components: phi_act [4C, 4K + 16] packed as NB = 3 (K = 1) or 4
+// (K = 4) blocks of 16 columns, hi and lo (2 x 8 NB 16-byte chunks per 8 rows)
+BwdWs carve_route(void* ws, int64_t T, int64_t C, int K, int64_t* total) {
+  const int nb = K == 4 ? 4 : 3;
+  return carve(ws, T, C, BS * C, 4 * K + 16, BS * C / 8 * (16 * nb) * 16, fast_xroute_partial_bytes(T, C, K), 4,
+               true, total);
 }
 // pre: phi_pre [NC, N] packed as 2 x 16 columns
 BwdWs carve_pre(void* ws, int64_t T, int N, int64_t C, int64_t* total) {
@@ -624,9 +959,9 @@ int64_t fast_backward_ws_bytes(int64_t T, int64_t C) {
 
 hipError_t launch_fast_backward_post(const void* X, int64_t T, int64_t C, const float* h_post, const void* F_out,
                                      const void* dX_next, void* dF_out, float* dh, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_post_kernel<BM_MHC>, dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)X,
+  hipLaunchKernelGGL((bwd_post_kernel<BM_MHC, 1>), dim3((unsigned)T), dim3(256), 0, st, (const uint16_t*)X,
                      (const uint16_t*)dX_next, (const uint16_t*)F_out, C, 4, (const int32_t*)nullptr, h_post, dh,
-                     BCOL, 4, (uint16_t*)dF_out);
+                     BCOL, 4, dF_out);
   return hipGetLastError();
 }
 
@@ -651,50 +986,57 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
   hipLaunchKernelGGL(bwd_dphi_kernel<BM_MHC>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st,
                      x, w.dP, T, C, 4, (const int32_t*)nullptr, BCOL, (int64_t)BS * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_sums(w, T, (int64_t)BS * C, BCOL, dphi, dbias, BCOL, 3, dalpha, st);
+  return launch_sums(w, T, (int64_t)BS * C, BCOL, dphi, dbias, 32, 3, dalpha, st);
 }
 
 // ------------------------------------------------------------------ xHC
 
 bool fast_xhc_backward_supported(int dtype, int N, int k, int K, int64_t T, int64_t C, int iters) {
-  return dtype == 1 && N % 4 == 0 && N >= 4 && N <= 16 && k == 4 && K == 1 && T >= 1 && iters >= 1 &&
-         iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 && fast_xroute_partial_bytes(T, C) > 0 &&
+  return dtype == 1 && N % 4 == 0 && N >= 4 && N <= 16 && k == 4 && (K == 1 || K == 4) && T >= 1 && iters >= 1 &&
+         iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 && fast_xroute_partial_bytes(T, C, K) > 0 &&
          fast_xpre_partial_bytes(T, N, C) > 0 && (C + FCH - 1) / FCH <= 65535 && T * (int64_t)N * C < (1ll << 40);
 }
 
 int64_t fast_xhc_backward_ws_bytes(int64_t T, int N, int64_t C) {
-  int64_t a = 0, b = 0;
-  carve_route(nullptr, T, C, &a);
+  int64_t a = 0, b = 0, c = 0;
+  carve_route(nullptr, T, C, 1, &a);
+  carve_route(nullptr, T, C, 4, &c);
   carve_pre(nullptr, T, N, C, &b);
+  a = a > c ? a : c;
   return a > b ? a : b;
 }
 
 hipError_t launch_fast_xroute_backward(const void* X, int64_t T, int N, int64_t C, const int32_t* idx,
                                        const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
-                                       const void* F_out, void* dX, void* dF_out, float* dphi_act, float* db_act,
+                                       const void* Wb, int K, void* dX, void* dWb, float* dphi_act, float* db_act,
                                        float* dalpha, float* dh, void* ws, hipStream_t st) {
-  const BwdWs w = carve_route(ws, T, C, nullptr);
+  const BwdWs w = carve_route(ws, T, C, K, nullptr);
   const uint16_t* x = (const uint16_t*)X;
+  const int ncol = 4 * K + 16;
   // the active set's maps (the forward's kernels) and its projection partials
-  hipError_t e = launch_fast_xhc_active(X, T, N, C, idx, 1, phi_act, b_act, a_post, a_res, iters, w.h_post, w.h_res,
+  hipError_t e = launch_fast_xhc_active(X, T, N, C, idx, K, phi_act, b_act, a_post, a_res, iters, w.h_post, w.h_res,
                                         w.packed, w.partial, st, w.phi_rows);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_post_kernel<BM_ROUTE>, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dX,
-                     (const uint16_t*)F_out, C, N, idx, w.h_post, dh, 20, 0, (uint16_t*)dF_out);
+  if (K == 4)
+    hipLaunchKernelGGL((bwd_post_kernel<BM_ROUTE, 4>), dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dX,
+                       (const uint16_t*)Wb, C, N, idx, w.h_post, dh, ncol, 0, dWb);
+  else
+    hipLaunchKernelGGL((bwd_post_kernel<BM_ROUTE, 1>), dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dX,
+                       (const uint16_t*)Wb, C, N, idx, w.h_post, dh, ncol, 0, dWb);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_fast_xroute_bwd_coeffs(w.partial, T, C, b_act, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
+  if ((e = launch_fast_xroute_bwd_coeffs(w.partial, T, C, K, b_act, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                          w.h_res, st)) != hipSuccess)
     return e;
   // dphi reads x only: run it before the dX pass rewrites dX_next's active rows
   hipLaunchKernelGGL(bwd_dphi_kernel<BM_ROUTE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0,
-                     st, x, w.dP, T, C, N, idx, 20, (int64_t)BS * C, w.dphi_part);
+                     st, x, w.dP, T, C, N, idx, ncol, (int64_t)BS * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dx_kernel<BM_ROUTE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)),
                      dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)nullptr, T, C, N, idx,
                      (const float*)nullptr, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dalpha: the post and res gate sums (red columns 25, 26)
-  return launch_sums(w, T, (int64_t)BS * C, 20, dphi_act, db_act, 25, 2, dalpha, st);
+  // dalpha: the post and res gate sums (red columns 33, 34)
+  return launch_sums(w, T, (int64_t)BS * C, ncol, dphi_act, db_act, 33, 2, dalpha, st);
 }
 
 hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C, const float* phi_pre,
@@ -727,8 +1069,51 @@ hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C,
                      dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)dF_in, T, C, N,
                      (const int32_t*)nullptr, w.h_pre, (const float*)nullptr, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dalpha: the gate sum (red column 24)
-  return launch_sums(w, T, (int64_t)N * C, N, dphi_pre, db_pre, 24, 1, dalpha, st);
+  // dalpha: the gate sum (red column 32)
+  return launch_sums(w, T, (int64_t)N * C, N, dphi_pre, db_pre, 32, 1, dalpha, st);
+}
+
+
+// --------------------------------------------- augmentation backward (host)
+
+bool fast_augment_backward_supported(int dtype, int64_t B, int64_t S, int64_t C, const int* kappa, int r) {
+  return (dtype == 0 || dtype == 1) && B >= 1 && S >= 1 && C >= 1 && r == 3 && kappa && kappa[0] == AB_K1 &&
+         kappa[1] == AB_K2 && kappa[2] == AB_K3 && B * S * C < (1ll << 40);
+}
+
+int64_t fast_augment_backward_ws_bytes(int64_t B, int64_t S, int64_t C) {
+  const int64_t T = B * S, nw = (C + 63) / 64, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
+  return al256(T * nw * AB_NV * 4) + al256(T * 32 * 4) + al256(nstrip * C * AB_TAPS * 4);
+}
+
+hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
+                                        const float* conv_w, const float* dV, void* dF_out, float* dconv_w, void* ws,
+                                        hipStream_t st) {
+  const int64_t T = B * S, nw = (C + 63) / 64, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
+  unsigned char* p = (unsigned char*)ws;
+  float* part = (float*)p;
+  float* coef = (float*)(p + al256(T * nw * AB_NV * 4));
+  float* wpart = (float*)(p + al256(T * nw * AB_NV * 4) + al256(T * 32 * 4));
+  const dim3 grid((unsigned)((C + 255) / 256), (unsigned)nstrip), blk(256);
+  if (dtype == 1)
+    hipLaunchKernelGGL(aug_bwd_gram_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)F_out, T, S, C, conv_w, dV,
+                       part);
+  else
+    hipLaunchKernelGGL(aug_bwd_gram_kernel<float>, grid, blk, 0, st, (const float*)F_out, T, S, C, conv_w, dV, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(aug_bwd_coef_kernel, dim3((unsigned)T), dim3(64), 0, st, part, T, (int)nw, coef);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (dtype == 1)
+    hipLaunchKernelGGL(aug_bwd_walk_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)F_out, T, S, C, conv_w, dV,
+                       coef, (uint16_t*)dF_out, wpart);
+  else
+    hipLaunchKernelGGL(aug_bwd_walk_kernel<float>, grid, blk, 0, st, (const float*)F_out, T, S, C, conv_w, dV, coef,
+                       (float*)dF_out, wpart);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(aug_bwd_wsum_kernel, dim3((unsigned)((C * AB_TAPS + 255) / 256)), dim3(256), 0, st, wpart,
+                     (int)nstrip, C, dconv_w);
+  return hipGetLastError();
 }
 
 }  // namespace hc

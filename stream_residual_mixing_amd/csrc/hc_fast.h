@@ -48,38 +48,48 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
                                 float a_pre, float a_post, float a_res, int iters, const void* dX_next,
                                 const void* dF_in, float* dh, void* dX, float* dphi, float* dbias, float* dalpha,
                                 void* ws, hipStream_t st);
-// xHC routed-step backward (N % 4 == 0, N <= 16, k = 4, K = 1, bfloat16, C % 32 ==
-// 0; the bfloat16 arrays 16-byte aligned), both calls sharing one workspace size:
+// xHC routed-step backward (N % 4 == 0, N <= 16, k = 4, K = 1 or 4, bfloat16, C %
+// 32 == 0; the bfloat16 arrays 16-byte aligned), both calls sharing one workspace
+// size:
 //  route: dX holds dX_next on entry and the route's gradient on exit (only the
-//    active rows change); dF_out, dphi_act [4C, 20], db_act [20], dalpha [2]
-//    (post, res), dh [T, 20] = [dH_post | dH_res];
+//    active rows change); dWb (K = 1: dF_out [T, C] bfloat16; K = 4: dV [T, 4, C]
+//    float32), dphi_act [4C, 4K + 16], db_act, dalpha [2] (post, res), dh
+//    [T, 4K + 16] = [dH_post | dH_res];
 //  pre: dX += the dense read's gradient; dphi_pre [NC, N], db_pre [N],
 //    dalpha [1], dh_pre [T, N].
 bool fast_xhc_backward_supported(int dtype, int N, int k, int K, int64_t T, int64_t C, int iters);
 int64_t fast_xhc_backward_ws_bytes(int64_t T, int N, int64_t C);
 hipError_t launch_fast_xroute_backward(const void* X, int64_t T, int N, int64_t C, const int32_t* idx,
                                        const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
-                                       const void* F_out, void* dX, void* dF_out, float* dphi_act, float* db_act,
+                                       const void* Wb, int K, void* dX, void* dWb, float* dphi_act, float* db_act,
                                        float* dalpha, float* dh, void* ws, hipStream_t st);
 hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C, const float* phi_pre,
                                      const float* b_pre, float a_pre, const void* dF_in, void* dX, float* dphi_pre,
                                      float* db_pre, float* dalpha, float* dh_pre, void* ws, hipStream_t st);
+// Backward of the temporal augmentation for r = 3 convs of sizes (4, 8, 12): dV
+// [T, 4, C] float32 in; dF_out [T, C] (F_out's dtype, bfloat16 or float32) and
+// dconv_w (conv_w's layout) out; any C.
+bool fast_augment_backward_supported(int dtype, int64_t B, int64_t S, int64_t C, const int* kappa, int r);
+int64_t fast_augment_backward_ws_bytes(int64_t B, int64_t S, int64_t C);
+hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
+                                        const float* conv_w, const float* dV, void* dF_out, float* dconv_w, void* ws,
+                                        hipStream_t st);
 // Pieces of the backward in hc_fused.hip, beside the partial layout they read:
 //  front: phi packed for the projection (packed) and in the row form of the
 //    dP phi^T operand (phi_rows, 4C x 128 bytes), then the projection partials
 //    of X on 64-token items;
 //  coeffs: gates' and Sinkhorn's backward from dh [T, 24]: dP [T, 32], g2 [T],
-//    the sums red [ceil(T / 16), 28] over groups of 16 tokens, and the
+//    the sums red [ceil(T / 16), 36] over groups of 16 tokens, and the
 //    forward's h_pre [T, 4] and h_res [T, 16]; dynamic LDS of iters * 1 KB
 //    (iters <= 64).
 hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const float* phi, void* packed,
                                  uint4* phi_rows, float* partial, hipStream_t st);
 // xHC routed-step backward pieces: the gathered active set's coefficient
-// backward (partials of launch_fast_xhc_active, dh [T, 20] = [dH_post | dH_res],
-// h_res out), and the pre map's: the full-state projection of the pre columns
+// backward for K = 1 or 4 (partials of launch_fast_xhc_active, dh [T, 4K + 16] =
+// [dH_post | dH_res], h_res out), and the pre map's: the full-state projection of the pre columns
 // (pack + proj_wide on stream groups) and its backward (dh_pre [T, N] in; dP,
 // g2, red, h_pre [T, N] out). Partial buffer sizes of each.
-hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* b_act,
+hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, int K, const float* b_act,
                                          float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                          float* red, float* h_res, hipStream_t st);
 hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C, const float* phi_pre, void* packed,
@@ -87,7 +97,7 @@ hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C
 hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, int64_t C, const float* b_pre,
                                        float a_pre, const float* dh_pre, float* dP, float* g2, float* red,
                                        float* h_pre, hipStream_t st);
-int64_t fast_xroute_partial_bytes(int64_t T, int64_t C);
+int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K);
 int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C);
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,

@@ -929,25 +929,28 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
 // gradient, 2 dss = -d rho rho^3 / (4C) (0 for the all-zero state).
 // Outputs per token: h_pre and h_res (the forward's maps, for the dX pass), dP
 // [32] (columns 24..31 zero: the A operand of the dx product) and g2 (= 2 dss);
-// per workgroup of 16 tokens, red [28] = the sums
-// over its tokens of dz [24] | dz P rho over each gate [3] | 0, which are then
-// added over the workgroups for db and dalpha.
+// per workgroup of 16 tokens, red [36] = the sums
+// over its tokens of dz [32, zero past the map's columns] | dz P rho over the
+// pre, post and res gates [3] | 0, which are then added over the workgroups for
+// db and dalpha.
 //
-// ROUTE: the xHC active set (k = 4, K = 1) with columns [post 4 | res 16] and dh
-// [T, 20] in that order: lanes e < 4 carry post column e, no pre map (h_pre is
-// not written), and the red columns are dz [post 4 | res 16 | 0 0 0 0] | 0 |
-// dz P rho over post | over res | 0.
-template <int TT, bool ROUTE>
+// LAY = 0: mHC, columns [pre 4 | post 4 | res 16], dh [T, 24].
+// LAY = K (1 or 4): the xHC active set (k = 4) with K write-back components,
+// columns [post 4K (a*K + j) | res 16] and dh [T, 4K + 16] in that order: lanes
+// e < 4K carry post column e, no pre map (h_pre is not written).
+template <int TT, int LAY>
 __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
                                                         const float* __restrict__ bias, Gate gate, int iters,
                                                         const float* __restrict__ dh, float* __restrict__ dP,
                                                         float* __restrict__ g2, float* __restrict__ red,
                                                         float* __restrict__ h_pre, float* __restrict__ h_res) {
-  constexpr int RES0 = ROUTE ? 4 : 8;    // first res column
-  constexpr int NGC = ROUTE ? 4 : 8;     // gate (pre/post) columns before it
-  constexpr int DHS = ROUTE ? 20 : 24;   // dh row length
+  constexpr bool ROUTE = LAY != 0;
+  constexpr int RES0 = ROUTE ? 4 * LAY : 8;  // first res column
+  constexpr int NGC = RES0;                  // gate (pre/post) columns before it
+  constexpr int DHS = RES0 + 16;             // dh row length
+  static_assert(NGC == 4 || NGC == 8 || NGC == 16, "gate columns");
   extern __shared__ float it_lds[];  // [iters][256]
-  using PG = PartGeom<3, TT>;
+  using PG = PartGeom<(DHS > 24 ? 4 : 3), TT>;
   const int tid = threadIdx.x;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
   const int64_t tt = g >> 4;
@@ -1035,18 +1038,18 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
     if (e == 0) g2[tt] = -drho * invr * invr * invr / (float)(NS4 * C);
   }
   // the workgroup's 16 tokens added in token order (rows past T add zero)
-  __shared__ float bsum[16][28];
+  __shared__ float bsum[16][36];
   const int tk = tid >> 4;
   bsum[tk][RES0 + e] = valid ? dz_res : 0.f;
   if (e < NGC) bsum[tk][e] = valid ? dz_pp : 0.f;
-  if (ROUTE && e < 4) bsum[tk][20 + e] = 0.f;
-  if (e < 4) bsum[tk][24 + e] = !valid || e == 3 ? 0.f : (e == 0 ? u_pre : (e == 1 ? u_post : u_res));
+  if (e < 16 - RES0) bsum[tk][RES0 + 16 + e] = 0.f;
+  if (e < 4) bsum[tk][32 + e] = !valid || e == 3 ? 0.f : (e == 0 ? u_pre : (e == 1 ? u_post : u_res));
   __syncthreads();
-  if (tid < 28) {
+  if (tid < 36) {
     float sum = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) sum += bsum[k][tid];
-    red[(int64_t)blockIdx.x * 28 + tid] = sum;
+    red[(int64_t)blockIdx.x * 36 + tid] = sum;
   }
 }
 
@@ -1057,8 +1060,8 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
 // order, r = sqrt(ss / (N C)) and h_pre as xpre_finish_kernel forms them, then
 // dz = dH_pre h (1 - h), dP = alpha dz / r and the gradient through r,
 // 2 dss = -d rho rho^3 / (N C). Outputs: dP [T, 32] (columns N..31 zero), g2,
-// h_pre [T, N], and per workgroup of 16 tokens red [28] = the sums of dz
-// [16, zero past N] | 0 x 8 | dz P rho over the gate | 0 0 0.
+// h_pre [T, N], and per workgroup of 16 tokens red [36] = the sums of dz
+// [16, zero past N] | 0 x 16 | dz P rho over the gate | 0 0 0.
 template <int NB, int TT>
 __global__ __launch_bounds__(256) void bwd_xpre_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C,
                                                              int N, int per_tile, const float* __restrict__ b_pre,
@@ -1103,16 +1106,17 @@ __global__ __launch_bounds__(256) void bwd_xpre_coeff_kernel(const float* __rest
     if (col) h_pre[tt * N + c] = h;
     if (c == 0) g2[tt] = -drho * invr * invr * invr / (float)((double)N * (double)C);
   }
-  __shared__ float bsum[16][28];
+  __shared__ float bsum[16][36];
   const int tk = tid >> 4;
   bsum[tk][c] = valid ? dz : 0.f;
-  if (c < 12) bsum[tk][16 + c] = (c == 8 && valid) ? u : 0.f;
+  bsum[tk][16 + c] = 0.f;
+  if (c < 4) bsum[tk][32 + c] = (c == 0 && valid) ? u : 0.f;
   __syncthreads();
-  if (tid < 28) {
+  if (tid < 36) {
     float sum = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) sum += bsum[k][tid];
-    red[(int64_t)blockIdx.x * 28 + tid] = sum;
+    red[(int64_t)blockIdx.x * 36 + tid] = sum;
   }
 }
 
@@ -1646,13 +1650,18 @@ hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const floa
   return launch_wide<3, ROWS_CONTIG>(args(X, T, C, 4 * C, geom(T, C, 1, W_TOK), packed, partial), st);
 }
 
-hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* b_act,
+hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, int K, const float* b_act,
                                          float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                          float* red, float* h_res, hipStream_t st) {
-  const int64_t threads = T * 16;
-  hipLaunchKernelGGL((bwd_coeff_kernel<TILE, true>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                     (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), b_act,
-                     Gate{0.f, a_post, a_res}, iters, dh, dP, g2, red, nullptr, h_res);
+  const dim3 grid((unsigned)((T * 16 + 255) / 256)), blk(256);
+  const size_t lds = (size_t)iters * 256 * sizeof(float);
+  const Gate gt{0.f, a_post, a_res};
+  if (K == 4)
+    hipLaunchKernelGGL((bwd_coeff_kernel<TILE, 4>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
+                       iters, dh, dP, g2, red, nullptr, h_res);
+  else
+    hipLaunchKernelGGL((bwd_coeff_kernel<TILE, 1>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
+                       iters, dh, dP, g2, red, nullptr, h_res);
   return hipGetLastError();
 }
 
@@ -1672,14 +1681,14 @@ hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, i
   return hipGetLastError();
 }
 
-int64_t fast_xroute_partial_bytes(int64_t T, int64_t C) { return part_bytes(T, C, 1, 3); }
+int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K) { return part_bytes(T, C, 1, K == 4 ? 4 : 3); }
 int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C) { return part_bytes(T, C, N / 4, 2); }
 
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                   float* red, float* h_pre, float* h_res, hipStream_t st) {
   const int64_t threads = T * 16;
-  hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, false>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, 0>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
                      (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), bias,
                      Gate{a_pre, a_post, a_res}, iters, dh, dP, g2, red, h_pre, h_res);
   return hipGetLastError();

@@ -323,3 +323,30 @@ def test_xhc_backward_validation(hc):
     assert pre(ws=None) == -8
     assert pre(dX=ctypes.c_void_p(0x4000000)) == -5  # dX over dF_in
     assert pre(dphi=ctypes.c_void_p(0x5000040)) == -5  # dphi inside dX
+
+
+def test_augment_backward_validation(hc):
+    L = hc.lib()
+    B, S, C = 2, 16, 64
+    k = (ctypes.c_int * 3)(4, 8, 12)
+    kbad = (ctypes.c_int * 3)(4, 8, 10)
+    wsb = L.xhc_augment_backward_workspace_bytes(B, S, C, k, 3, 1)
+    assert wsb > 0
+    assert L.xhc_augment_backward_workspace_bytes(0, S, C, k, 3, 1) == 0
+    assert L.xhc_augment_backward_workspace_bytes(B, S, C, kbad, 3, 1) == -1
+    assert L.xhc_augment_backward_workspace_bytes(B, S, C, k, 2, 1) == -1
+    P = lambda j: ctypes.c_void_p(0x1000000 * (j + 1))
+
+    def aug(dt=1, B=B, S=S, C=C, kk=k, r=3, wsb=wsb, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["F", "w", "dV", "dF", "dw", "ws"])}
+        return L.xhc_augment_backward(p["F"], dt, B, S, C, p["w"], kk, r, p["dV"], p["dF"], p["dw"], p["ws"], wsb,
+                                      None)
+    assert aug(dt=4) == -3
+    assert aug(r=2) == -2 and aug(kk=kbad) == -2 and aug(C=0) == -2 and aug(B=-1) == -2
+    assert aug(B=0, F=None) == 0
+    for nm in ("F", "w", "dV", "dF", "dw"):
+        assert aug(**{nm: None}) == -1, nm
+    assert aug(dF=ctypes.c_void_p(0x4000001)) == -4
+    assert aug(ws=None) == -8 and aug(wsb=wsb - 1) == -8
+    assert aug(dF=ctypes.c_void_p(0x1000000)) == -5  # dF_out over F_out
+    assert aug(dw=ctypes.c_void_p(0x3000100)) == -5  # dconv inside dV

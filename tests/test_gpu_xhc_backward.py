@@ -146,3 +146,61 @@ def test_xhc_backward_full_size():
     rng = np.random.default_rng(550)
     rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 126, replace=False)]))
     _compare(route, pre, _oracle(inp, g, idx, chunk=256, rows=rows), g, idx, rows=rows)
+
+
+# ------------------------------------------------ augmented step (K = 4)
+
+def _aug_inputs(seed, B, S, N, C, m=2):
+    inp = synth.xhc_layer(seed, 0, B * S, N, C, 4, m, 4, synth.BF16)
+    g = synth.mhc_grads(seed, 0, B * S, N, C, synth.BF16)
+    idx = O.xhc_pre(inp["X"].values, inp["phi_pre"], inp["b_pre"], inp["alpha_pre"], inp["w_router"], 4, m)["idx"]
+    return inp, g, idx.astype(np.int32)
+
+
+@pytest.mark.parametrize("B,S,N,C", [(2, 200, 16, 96), (3, 7, 8, 512), (1, 300, 16, 4096)])
+def test_augmented_step_backward(B, S, N, C):
+    """K = 4: the GPU forward's V feeds xhc_route_backward (dV in float32), whose dV
+    feeds xhc_augment_backward (dF_out, the conv taps); each stage against the
+    oracle on the same inputs: several strips of 128 tokens with sequence starts
+    inside them, sequences shorter than the longest kernel, C past whole
+    channel blocks."""
+    note(f"xHC augmented backward B={B} S={S} N={N} C={C} bf16")
+    inp, g, idx = _aug_inputs(560 + S, B, S, N, C)
+    kap = inp["kappas"]
+    w = np.concatenate([x.reshape(-1) for x in inp["conv_w"]])
+    V = hc.xhc_augment(dev(inp["F_out"]), dev(w), kap, B, S)
+    torch.cuda.synchronize()
+    Vh = host64(V)
+    X = dev(inp["X"])
+    dX = dev(g["dX_next"]).clone()
+    dXo, dV, dphi, db, dal, dh = hc.xhc_route_backward(X, dev(idx), dev(inp["phi_act"]), dev(inp["b_act"]),
+                                                       inp["alpha_post"], inp["alpha_res"], V, dX)
+    dF, dw = hc.xhc_augment_backward(dev(inp["F_out"]), dev(w), kap, B, S, dV)
+    torch.cuda.synchronize()
+    r = O.xhc_route_backward(inp["X"].values, idx, inp["phi_act"], inp["b_act"], inp["alpha_post"],
+                             inp["alpha_res"], Vh, g["dX_next"].values, 20)
+    check_bf16("route dX", host64(dXo), r["dX"])
+    check_fp32("dV", host64(dV), r["dWb"], BWD_REL)
+    check_fp32("dh", host64(dh), r["dh"], BWD_REL)
+    errs = {"dphi_act": check_fp32("dphi_act", host64(dphi), r["dphi_act"], BWD_REL),
+            "db_act": check_fp32("db_act", host64(db), r["db_act"], BWD_REL),
+            "dalpha": check_fp32("dalpha", host64(dal), np.array([r["dalpha_post"], r["dalpha_res"]]), BWD_REL)}
+    # the augmentation backward on the GPU's own dV (its stage on its own input)
+    a = O.xhc_augment_backward(inp["F_out"].values, inp["conv_w"], B, S, host64(dV))
+    check_bf16("dF_out", host64(dF), a["dF_out"])
+    ref_w = np.concatenate([x.reshape(-1) for x in a["dconv_ws"]])
+    errs["dconv"] = check_fp32("dconv", host64(dw), ref_w, BWD_REL)
+    note(f"relative L2: {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
+
+
+def test_augment_backward_deterministic():
+    note("xhc_augment_backward determinism B=2 S=300 C=256")
+    B, S, C = 2, 300, 256
+    inp = synth.xhc_layer(590, 0, B * S, 4, C, 4, 1, 4, synth.BF16)
+    w = np.concatenate([x.reshape(-1) for x in inp["conv_w"]])
+    dV = torch.randn(B * S, 4, C, device="cuda", generator=torch.Generator(device="cuda").manual_seed(5))
+    a = hc.xhc_augment_backward(dev(inp["F_out"]), dev(w), inp["kappas"], B, S, dV)
+    b = hc.xhc_augment_backward(dev(inp["F_out"]), dev(w), inp["kappas"], B, S, dV)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
