@@ -267,10 +267,48 @@ def xhc_backward_bench(torch, hc, dev, reps: int = 10) -> dict:
     alg_p = T * (s_f + f + s_f + s_f) + 2 * N * C * N * 4
     rate = lambda b, t: {"us": t * 1e6, "algorithmic_bytes": b, "achieved_GBps": b / t / 1e9,
                          "pct_hbm_peak": 100.0 * b / t / 1e9 / HBM_PEAK_GBPS}
-    return {"workload": "xHC backward N=16 k=4 m=2 C=4096 T=8192 bf16 K=1 (routed step; 20 Sinkhorn iterations "
-                        "recomputed)",
+    # augmented step (K = 4, B = 2 sequences of S = 4096): route backward with the
+    # components V, then the augmentation backward of dV
+    B, S = 2, 4096
+    conv = torch.cat([rn(C, kk, std=(1.0 / kk) ** 0.5) for kk in (4, 8, 12)], 1).contiguous()
+    Vs = [hc.xhc_augment(Fs[i], conv, (4, 8, 12), B, S) for i in range(3)]
+    phi4 = rn(k * C, 4 * k + k * k, std=0.02)
+    b4 = torch.zeros(4 * k + k * k, device=dev)
+    b4[4 * k:] = torch.eye(k, device=dev).flatten()
+    ro4 = (torch.empty(T, 4, C, device=dev), torch.empty(k * C, 4 * k + k * k, device=dev),
+           torch.empty(4 * k + k * k, device=dev), torch.empty(2, device=dev), torch.empty(T, 4 * k + k * k, device=dev))
+    ao = (torch.empty(T, C, dtype=torch.bfloat16, device=dev), torch.empty_like(conv))
+    ws_a = torch.empty(hc.xhc_augment_backward_workspace_bytes(B, S, C, (4, 8, 12), torch.bfloat16), dtype=torch.uint8,
+                       device=dev)
+    route4 = lambda i: hc.xhc_route_backward(Xs[i % 3], idx, phi4, b4, 0.01, 0.01, Vs[i % 3], dXs[i % 3],
+                                             SINKHORN_ITERS, out=ro4, workspace=ws)
+    aug = lambda i: hc.xhc_augment_backward(Fs[i % 3], conv, (4, 8, 12), B, S, ro4[0], out=ao, workspace=ws_a)
+    for i in range(3):
+        route4(i)
+        aug(i)
+    torch.cuda.synchronize()
+    t4, ta = [], []
+    for i in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        route4(i)
+        ev[1].record()
+        aug(i)
+        ev[2].record()
+        torch.cuda.synchronize()
+        t4.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        ta.append(ev[1].elapsed_time(ev[2]) * 1e-3)
+    t_4, t_a = med(t4), med(ta)
+    # route K = 4: x and dX_next on the active rows and V read, dX and dV (float32) written
+    alg_4 = T * (2 * s_a + 4 * f + s_a + 4 * C * 4) + 2 * k * C * (4 * k + k * k) * 4
+    # augmentation: F_out and dV read, dF_out written (taps once)
+    alg_a = T * (f + 4 * C * 4 + f) + 2 * C * 24 * 4
+    return {"workload": "xHC backward N=16 k=4 m=2 C=4096 T=8192 bf16: routed step (K=1) and augmented step (K=4, "
+                        "B=2 S=4096, kappa 4,8,12); 20 Sinkhorn iterations recomputed",
             "tokens_per_s": T / (t_r + t_p), "us": (t_r + t_p) * 1e6,
-            "xhc_route_backward": rate(alg_r, t_r), "xhc_pre_backward": rate(alg_p, t_p)}
+            "xhc_route_backward": rate(alg_r, t_r), "xhc_pre_backward": rate(alg_p, t_p),
+            "augmented_us": (t_4 + t_a + t_p) * 1e6,
+            "xhc_route_backward_K4": rate(alg_4, t_4), "xhc_augment_backward": rate(alg_a, t_a)}
 
 
 def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
