@@ -554,22 +554,39 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
 // dV_0..dV_3, so the Gram-Schmidt backward needs only the Gram matrix G = U U^T
 // and M = dV U^T (26 sums over the channels): dU_i = sum_q P[i][q] dV_q +
 // sum_k Q[i][k] u_k with 4 x 4 matrices P, Q from G and M. Four launches:
-//  1. aug_bwd_gram_kernel: one thread per channel walks a strip of tokens with
-//     the last 12 rows of F_out in registers (zeros before each sequence
-//     start), forms u_1..u_3 and the 26 products, adds them over each wave's
-//     64 channels, and stores the wave sums [T][waves][26];
-//  2. aug_bwd_coef_kernel: per token the wave sums added in order, then the
-//     Gram-Schmidt steps recomputed and walked in reverse in float64 on the
-//     4-coefficient representation: P, Q [T][32];
+//  1. aug_bwd_gram_kernel: a workgroup takes 256 channels (one per thread) and
+//     a strip of tokens; each thread walks the strip with the last 12 rows of
+//     F_out in registers and the next 4 tokens' loads in flight, forms u_1..u_3
+//     and the 26 products, the wave sums them over its 64 channels in one
+//     reduce-scatter, and every 16 tokens the 4 waves' sums are added in LDS
+//     and stored as part [channel group][26][T];
+//  2. aug_bwd_coef_kernel: the channel groups' sums added in order per token,
+//     then one thread per token walks the Gram-Schmidt steps, recomputed, in
+//     reverse in float64 on the 4-coefficient representation: P, Q [T][32];
 //  3. aug_bwd_walk_kernel: one thread per channel walks a strip backwards (plus
-//     the 11 tokens after it, within the sequence): dU from P, Q, the window of
-//     the next 11 tokens' dU_j, dF_out[t] = dU_0[t] + sum_j sum_d w_j[kappa_j -
-//     1 - d] dU_j[t + d] (the conv's transpose), and the tap gradients dw_j[s] +=
-//     dU_j[t] F_out[t - kappa_j + 1 + s] summed over the strip's tokens;
+//     the 11 tokens after it, within the sequence), the strip's P, Q staged in
+//     LDS: dU from P, Q, the ring of the next 11 tokens' dU_j, dF_out[t] =
+//     dU_0[t] + sum_j sum_d w_j[kappa_j - 1 - d] dU_j[t + d] (the conv's
+//     transpose), and the tap gradients dw_j[s] += dU_j[t] F_out[t - kappa_j +
+//     1 + s] summed over the strip's tokens into wpart [strip][24][C];
 //  4. aug_bwd_wsum_kernel: the strips' tap sums added in strip order.
+// Both walks keep F_out's rows as loaded and mask, per token, the window
+// positions before the token's sequence start, so a sequence boundary inside a
+// strip needs no reload.
 constexpr int AB_STRIP = 128;  // tokens per strip
+constexpr int AB_GRP = 16;     // tokens per cross-wave sum of the Gram pass
+constexpr int AB_PF = 4;       // tokens per load group (the next group is in flight)
 constexpr int AB_NV = 26;      // sums per token: G (10, upper triangle) | M (16, M[j][i] = <dV_j, u_i>)
 constexpr int AB_K1 = 4, AB_K2 = 8, AB_K3 = 12, AB_TAPS = AB_K1 + AB_K2 + AB_K3;
+static_assert(AB_STRIP % AB_GRP == 0 && AB_GRP % AB_PF == 0, "strip, group and load group nest");
+
+// Workgroup barrier ordering LDS only: global loads in flight stay in flight
+// (a full __syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <typename TF>
 __device__ __forceinline__ float ab_ld(const TF* p) {
@@ -577,16 +594,23 @@ __device__ __forceinline__ float ab_ld(const TF* p) {
   else return *reinterpret_cast<const float*>(p);
 }
 
-// the three convs at the current token from the window win[0..11] = F_out[t-11..t]
-__device__ __forceinline__ void ab_convs(const float (&w)[AB_TAPS], const float (&win)[12], float (&u)[4]) {
-  u[0] = win[11];
+// win[s] = F_out[t - 11 + s] as loaded; ts = t's position in its sequence.
+// Positions before the sequence start read as zero.
+__device__ __forceinline__ void ab_mask(const float (&win)[12], int64_t ts, float (&wm)[12]) {
+#pragma unroll
+  for (int s = 0; s < 12; ++s) wm[s] = s + ts >= 11 ? win[s] : 0.f;
+}
+
+// the three convs at the current token from the masked window wm[0..11] = F_out[t-11..t]
+__device__ __forceinline__ void ab_convs(const float (&w)[AB_TAPS], const float (&wm)[12], float (&u)[4]) {
+  u[0] = wm[11];
   float a = 0.f, b = 0.f, c = 0.f;
 #pragma unroll
-  for (int s = 0; s < AB_K1; ++s) a += w[s] * win[12 - AB_K1 + s];
+  for (int s = 0; s < AB_K1; ++s) a += w[s] * wm[12 - AB_K1 + s];
 #pragma unroll
-  for (int s = 0; s < AB_K2; ++s) b += w[AB_K1 + s] * win[12 - AB_K2 + s];
+  for (int s = 0; s < AB_K2; ++s) b += w[AB_K1 + s] * wm[12 - AB_K2 + s];
 #pragma unroll
-  for (int s = 0; s < AB_K3; ++s) c += w[AB_K1 + AB_K2 + s] * win[12 - AB_K3 + s];
+  for (int s = 0; s < AB_K3; ++s) c += w[AB_K1 + AB_K2 + s] * wm[12 - AB_K3 + s];
   u[1] = a;
   u[2] = b;
   u[3] = c;
@@ -602,138 +626,252 @@ __device__ __forceinline__ void ab_taps(const float* __restrict__ conv_w, int64_
   for (int s = 0; s < AB_K3; ++s) w[AB_K1 + AB_K2 + s] = conv_w[(AB_K1 + AB_K2) * C + c * AB_K3 + s];
 }
 
+// partner exchange within rows of 16 lanes (DPP): lane i of a row reads lane i ^ 8
+// (rotate by 8), 7 - i within each half row (half mirror), i ^ 2 and i ^ 1 (quad
+// permutes)
+__device__ __forceinline__ float dpp_ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_hmirror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false));
+}
+
+// Reduce-scatter of 26 values over the wave: returns, in lanes 2k and 2k + 1,
+// the sum over the 64 lanes of v[k] (k < 26; lanes 52..63 return 0). Each level
+// halves the values a lane holds and pairs it with a lane that holds the other
+// half: lanes l and l + 32 (permlane32 swap), rows 2r and 2r + 1 (permlane16
+// swap), then within rows by DPP; after the level on lane bit b the lane keeps
+// the half selected by that bit, so value index k ends in lanes with l >> 1 = k.
+__device__ __forceinline__ float ab_reduce_scatter(const float (&v)[AB_NV], int lane) {
+  float a[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float y = k + 16 < AB_NV ? v[k + 16] : 0.f;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(y), false, false);
+    a[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // lanes < 32: value k; lanes >= 32: k + 16
+  }
+  float b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[k]), __float_as_uint(a[k + 8]), false, false);
+    b[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);  // even rows: a index k; odd rows: k + 8
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  float c[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = (b3 ? b[k + 4] : b[k]) + dpp_ror8(b3 ? b[k] : b[k + 4]);
+  float d[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) d[k] = (b2 ? c[k + 2] : c[k]) + dpp_hmirror(b2 ? c[k] : c[k + 2]);
+  const float e = (b1 ? d[1] : d[0]) + dpp_xor2(b1 ? d[0] : d[1]);
+  return e + dpp_xor1(e);
+}
+
 template <typename TF>
 __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict__ F, int64_t T, int64_t S, int64_t C,
                                                            const float* __restrict__ conv_w,
                                                            const float* __restrict__ dV, float* __restrict__ part) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ float red[2][AB_GRP][4][AB_NV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
   const bool cok = c0 < C;
   const int64_t c = cok ? c0 : C - 1;
-  const int64_t nw = (C + 63) / 64, wg = c0 >> 6;
   const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
   const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;
   float w[AB_TAPS];
   ab_taps(conv_w, C, c, w);
-  float win[12];  // before the first step: F_out[t0-12..t0-1], zero before the sequence start
-  const int64_t ss0 = t0 - t0 % S;  // first token of t0's sequence
+  float win[12];  // before the first token: F_out[t0-12..t0-1] as loaded (rows < 0 masked at use)
 #pragma unroll
   for (int s = 0; s < 12; ++s) {
     const int64_t tt = t0 - 12 + s;
-    win[s] = tt >= ss0 ? ab_ld(F + tt * C + c) : 0.f;
+    win[s] = ab_ld(F + (tt >= 0 ? tt : 0) * C + c);
   }
-  for (int64_t t = t0; t < t1; ++t) {
-    if (t % S == 0) {
+  struct Ld {
+    float f[AB_PF], dv[AB_PF][4];
+  };
+  auto load = [&](int64_t tb, Ld& L) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < 12; ++s) win[s] = 0.f;
+    for (int i = 0; i < AB_PF; ++i) {
+      const int64_t t = tb + i < T ? tb + i : T - 1;
+      L.f[i] = ab_ld(F + t * C + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) L.dv[i][j] = dV[(t * 4 + j) * C + c];
     }
+  };
+  int64_t tb = t0, ts = t0 % S;  // ts: position of token tb in its sequence
+  int rb = 0;                    // LDS buffer of the current group
+  auto step = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
+    const int64_t nb = tb + AB_PF;
+    load(nb, nxt);  // rows past T clamped: the last group's loads go unused
 #pragma unroll
-    for (int s = 0; s < 11; ++s) win[s] = win[s + 1];
-    win[11] = ab_ld(F + t * C + c);
-    float u[4], v[AB_NV];
-    ab_convs(w, win, u);
-    float dv[4];
+    for (int i = 0; i < AB_PF; ++i) {
+      const int64_t t = tb + i;
+      if (t < t1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dv[j] = dV[(t * 4 + j) * C + c];
-    int n = 0;
+        for (int s = 0; s < 11; ++s) win[s] = win[s + 1];
+        win[11] = cur.f[i];
+        float wm[12], u[4], v[AB_NV];
+        ab_mask(win, ts, wm);
+        ab_convs(w, wm, u);
+        int n = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int k = i; k < 4; ++k) v[n++] = u[i] * u[k];
+          for (int k = a; k < 4; ++k) v[n++] = cok ? u[a] * u[k] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[10 + 4 * j + i] = dv[j] * u[i];
+          for (int a = 0; a < 4; ++a) v[10 + 4 * j + a] = cok ? cur.dv[i][j] * u[a] : 0.f;
+        const float r = ab_reduce_scatter(v, lane);
+        const int gi = (int)((t - t0) % AB_GRP);
+        if (!(lane & 1) && (lane >> 1) < AB_NV) red[rb][gi][wave][lane >> 1] = r;
+        if (gi == AB_GRP - 1 || t == t1 - 1) {  // the group is complete: add the waves' sums, store
+          lds_barrier();
+          const int64_t g0 = t - gi;
 #pragma unroll
-    for (int k = 0; k < AB_NV; ++k) v[k] = wave_sum(cok ? v[k] : 0.f);
-    if (lane == 0 && wg < nw) {
-#pragma unroll
-      for (int k = 0; k < AB_NV; ++k) part[(t * nw + wg) * AB_NV + k] = v[k];
+          for (int e = tid; e < AB_NV * AB_GRP; e += 256) {
+            const int k = e >> 4, q = e & (AB_GRP - 1);
+            if (q <= gi) {
+              const float* rr = &red[rb][q][0][k];
+              part[((int64_t)blockIdx.x * AB_NV + k) * T + g0 + q] =
+                  ((rr[0] + rr[AB_NV]) + rr[2 * AB_NV]) + rr[3 * AB_NV];
+            }
+          }
+          rb ^= 1;
+        }
+        ts = ts + 1 == S ? 0 : ts + 1;
+      }
     }
+    tb = nb;
+    return nb < t1;
+  };
+  Ld a, b;
+  load(t0, a);
+  while (step(a, b) && step(b, a)) {
   }
 }
 
-// One wave per token: lane k < 26 adds sum k over the channel waves in order;
-// lane 0 then forms P and Q in float64.
-__global__ __launch_bounds__(64) void aug_bwd_coef_kernel(const float* __restrict__ part, int64_t T, int nw,
-                                                          float* __restrict__ coef) {
-  __shared__ double sv[AB_NV];
-  const int64_t t = blockIdx.x;
-  const int lane = threadIdx.x;
-  if (lane < AB_NV) {
-    float s = 0.f;
-    for (int q = 0; q < nw; ++q) s += part[(t * nw + q) * AB_NV + lane];
-    sv[lane] = (double)s;
+// A workgroup of 256 threads takes 64 tokens: the channel groups' sums are
+// added in order (float64) by all threads into LDS, then one thread per token
+// forms P and Q in float64.
+__global__ __launch_bounds__(256) void aug_bwd_coef_kernel(const float* __restrict__ part, int64_t T, int nq,
+                                                           float* __restrict__ coef) {
+  __shared__ double sd[AB_NV][64];
+  const int tid = threadIdx.x;
+  const int64_t tb = (int64_t)blockIdx.x * 64;
+  for (int e = tid; e < AB_NV * 64; e += 256) {
+    const int k = e >> 6, tl = e & 63;
+    const int64_t tt = tb + tl < T ? tb + tl : T - 1;
+    const float* pp = part + (int64_t)k * T + tt;
+    const int64_t qs = (int64_t)AB_NV * T;
+    double s = 0.0;
+    int q = 0;
+    for (; q + 8 <= nq; q += 8) {  // eight loads in flight, added in order
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = pp[(q + i) * qs];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += (double)v[i];
+    }
+    for (; q < nq; ++q) s += (double)pp[q * qs];
+    sd[k][tl] = s;
   }
   __syncthreads();
-  if (lane != 0) return;
+  const int64_t t = tb + tid;
+  if (tid >= 64 || t >= T) return;
+  double sv[AB_NV];
+#pragma unroll
+  for (int k = 0; k < AB_NV; ++k) sv[k] = sd[k][tid];
   double G[4][4], M[4][4];
   {
     int n = 0;
+#pragma unroll
     for (int i = 0; i < 4; ++i)
+#pragma unroll
       for (int k = i; k < 4; ++k) G[i][k] = G[k][i] = sv[n++];
+#pragma unroll
     for (int j = 0; j < 4; ++j)
+#pragma unroll
       for (int i = 0; i < 4; ++i) M[j][i] = sv[10 + 4 * j + i];
   }
   auto gdot = [&](const double* a, const double* b) {  // <sum a_k u_k, sum b_l u_l>
     double r = 0.0;
+#pragma unroll
     for (int k = 0; k < 4; ++k)
+#pragma unroll
       for (int l = 0; l < 4; ++l) r += a[k] * G[k][l] * b[l];
     return r;
   };
-  // forward: V_j = sum_k B[j][k] u_k, with the steps' v, n, d kept
+  // forward: V_j = sum_k B[j][k] u_k, with each step's n = <v, V_i>, d = <V_i, V_i>
   double B[4][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}};
-  double vold[4][4][4], nn[4][4], dd[4][4];
+  double nn[4][4], dd[4][4];
+#pragma unroll
   for (int j = 1; j < 4; ++j) {
     double v[4] = {0, 0, 0, 0};
     v[j] = 1.0;
+#pragma unroll
     for (int i = 0; i < j; ++i) {
-      for (int k = 0; k < 4; ++k) vold[j][i][k] = v[k];
       const double n = gdot(v, B[i]), d = gdot(B[i], B[i]);
       nn[j][i] = n;
       dd[j][i] = d;
+#pragma unroll
       for (int k = 0; k < 4; ++k) v[k] -= (n / d) * B[i][k];
     }
+#pragma unroll
     for (int k = 0; k < 4; ++k) B[j][k] = v[k];
   }
-  // reverse: a gradient vector is sum_q ga[q] dV_q + sum_k gb[k] u_k
+  // reverse: a gradient vector is sum_q ga[q] dV_q + sum_k gb[k] u_k; the vector
+  // before step (j, i) is recovered from the one after it: v_old = v + (n / d) V_i
   double ga[4][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}}, gb[4][4] = {};
-  double P[4][4], Q[4][4];
+#pragma unroll
   for (int j = 3; j >= 1; --j) {
-    double a[4], b[4];
+    double a[4], b[4], vo[4];
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
       a[k] = ga[j][k];
       b[k] = gb[j][k];
+      vo[k] = B[j][k];
     }
+#pragma unroll
     for (int i = j - 1; i >= 0; --i) {
+      const double n = nn[j][i], d = dd[j][i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vo[k] += (n / d) * B[i][k];
       double p = 0.0;  // <V_i, g>
+#pragma unroll
       for (int k = 0; k < 4; ++k) {
         double gk = 0.0;  // <u_k, g>
+#pragma unroll
         for (int q = 0; q < 4; ++q) gk += M[q][k] * a[q];
+#pragma unroll
         for (int l = 0; l < 4; ++l) gk += G[k][l] * b[l];
         p += B[i][k] * gk;
       }
-      const double n = nn[j][i], d = dd[j][i];
+#pragma unroll
       for (int k = 0; k < 4; ++k) {
         ga[i][k] += -(n / d) * a[k];
-        gb[i][k] += -(n / d) * b[k] - p * (vold[j][i][k] / d - 2.0 * n * B[i][k] / (d * d));
+        gb[i][k] += -(n / d) * b[k] - p * (vo[k] / d - 2.0 * n * B[i][k] / (d * d));
       }
+#pragma unroll
       for (int k = 0; k < 4; ++k) b[k] -= (p / d) * B[i][k];
     }
+#pragma unroll
     for (int k = 0; k < 4; ++k) {
-      P[j][k] = a[k];
-      Q[j][k] = b[k];
+      coef[t * 32 + j * 4 + k] = (float)a[k];
+      coef[t * 32 + 16 + j * 4 + k] = (float)b[k];
     }
   }
+#pragma unroll
   for (int k = 0; k < 4; ++k) {
-    P[0][k] = ga[0][k];
-    Q[0][k] = gb[0][k];
+    coef[t * 32 + k] = (float)ga[0][k];
+    coef[t * 32 + 16 + k] = (float)gb[0][k];
   }
-  for (int i = 0; i < 4; ++i)
-    for (int k = 0; k < 4; ++k) {
-      coef[t * 32 + i * 4 + k] = (float)P[i][k];
-      coef[t * 32 + 16 + i * 4 + k] = (float)Q[i][k];
-    }
 }
 
 template <typename TF>
@@ -742,6 +880,7 @@ __global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict_
                                                            const float* __restrict__ dV,
                                                            const float* __restrict__ coef, TF* __restrict__ dF,
                                                            float* __restrict__ wpart) {
+  __shared__ __attribute__((aligned(16))) float cfs[(AB_STRIP + 11) * 32];
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
   const bool cok = c0 < C;
@@ -749,8 +888,13 @@ __global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict_
   const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
   const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;  // strip [t0, t1)
   // the walk starts up to 11 tokens after the strip, inside t1 - 1's sequence
-  const int64_t se = (t1 - 1) - (t1 - 1) % S + S;           // end of that sequence
+  const int64_t se = (t1 - 1) - (t1 - 1) % S + S;  // end of that sequence
   const int64_t top = (t1 + 11 < se ? t1 + 11 : se) - 1;
+  {  // P, Q of tokens t0..top into LDS
+    const float4* src = reinterpret_cast<const float4*>(coef + t0 * 32);
+    float4* dst = reinterpret_cast<float4*>(cfs);
+    for (int64_t e = tid; e < (top - t0 + 1) * 8; e += 256) dst[e] = src[e];
+  }
   float w[AB_TAPS];
   ab_taps(conv_w, C, c, w);
   float dw[AB_TAPS];
@@ -763,92 +907,111 @@ __global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict_
   for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
 #pragma unroll
   for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
-  float win[12];  // F_out[t-11..t], zero before the sequence start
-  auto load_win = [&](int64_t t) {
-    const int64_t ss = t - t % S;
+  float win[12];  // F_out[t-11..t] as loaded (rows < 0 masked at use)
 #pragma unroll
-    for (int s = 0; s < 12; ++s) {
-      const int64_t tt = t - 11 + s;
-      win[s] = tt >= ss ? ab_ld(F + tt * C + c) : 0.f;
+  for (int s = 0; s < 12; ++s) {
+    const int64_t tt = top - 11 + s;
+    win[s] = ab_ld(F + (tt >= 0 ? tt : 0) * C + c);
+  }
+  // load group of tokens tb, tb - 1, ..: F_out[t - 12] (the row entering the
+  // window after t) and dV[t]
+  struct Ld {
+    float f[AB_PF], dv[AB_PF][4];
+  };
+  auto load = [&](int64_t tb, Ld& L) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AB_PF; ++i) {
+      const int64_t t = tb - i >= t0 ? tb - i : t0;
+      L.f[i] = ab_ld(F + (t >= 12 ? t - 12 : 0) * C + c);  // rows < 0: masked at use
+#pragma unroll
+      for (int j = 0; j < 4; ++j) L.dv[i][j] = dV[(t * 4 + j) * C + c];
     }
   };
-  load_win(top);
-  for (int64_t t = top; t >= t0; --t) {
-    float u[4];
-    ab_convs(w, win, u);
-    float dv[4];
+  __syncthreads();
+  int64_t tb = top, ts = top % S;  // ts: position of token tb in its sequence
+  auto step = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
+    const int64_t nb = tb - AB_PF;
+    load(nb, nxt);  // tokens below t0 clamped: the last group's loads go unused
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dv[j] = dV[(t * 4 + j) * C + c];
-    const float* cf = coef + t * 32;
-    float dU[4];
+    for (int i = 0; i < AB_PF; ++i) {
+      const int64_t t = tb - i;
+      if (t >= t0) {
+        float wm[12], u[4];
+        ab_mask(win, ts, wm);
+        ab_convs(w, wm, u);
+        const float4* cp = reinterpret_cast<const float4*>(cfs + (t - t0) * 32);
+        float dU[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const float4 pr = cp[r], qr = cp[4 + r];
+          dU[r] = pr.x * cur.dv[i][0] + pr.y * cur.dv[i][1] + pr.z * cur.dv[i][2] + pr.w * cur.dv[i][3] +
+                  qr.x * u[0] + qr.y * u[1] + qr.z * u[2] + qr.w * u[3];
+        }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s += cf[i * 4 + q] * dv[q];
+        for (int d = AB_K1 - 1; d > 0; --d) f1[d] = f1[d - 1];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s += cf[16 + i * 4 + k] * u[k];
-      dU[i] = s;
-    }
+        for (int d = AB_K2 - 1; d > 0; --d) f2[d] = f2[d - 1];
 #pragma unroll
-    for (int d = AB_K1 - 1; d > 0; --d) f1[d] = f1[d - 1];
+        for (int d = AB_K3 - 1; d > 0; --d) f3[d] = f3[d - 1];
+        f1[0] = dU[1];
+        f2[0] = dU[2];
+        f3[0] = dU[3];
+        if (t < t1) {
+          float g = dU[0];
 #pragma unroll
-    for (int d = AB_K2 - 1; d > 0; --d) f2[d] = f2[d - 1];
+          for (int d = 0; d < AB_K1; ++d) g += w[AB_K1 - 1 - d] * f1[d];
 #pragma unroll
-    for (int d = AB_K3 - 1; d > 0; --d) f3[d] = f3[d - 1];
-    f1[0] = dU[1];
-    f2[0] = dU[2];
-    f3[0] = dU[3];
-    if (t < t1) {
-      float g = dU[0];
+          for (int d = 0; d < AB_K2; ++d) g += w[AB_K1 + AB_K2 - 1 - d] * f2[d];
 #pragma unroll
-      for (int d = 0; d < AB_K1; ++d) g += w[AB_K1 - 1 - d] * f1[d];
+          for (int d = 0; d < AB_K3; ++d) g += w[AB_TAPS - 1 - d] * f3[d];
+          if (cok) {
+            if constexpr (sizeof(TF) == 2) reinterpret_cast<uint16_t*>(dF)[t * C + c] = (uint16_t)f2bf(g);
+            else reinterpret_cast<float*>(dF)[t * C + c] = g;
+          }
 #pragma unroll
-      for (int d = 0; d < AB_K2; ++d) g += w[AB_K1 + AB_K2 - 1 - d] * f2[d];
+          for (int s = 0; s < AB_K1; ++s) dw[s] += dU[1] * wm[12 - AB_K1 + s];
 #pragma unroll
-      for (int d = 0; d < AB_K3; ++d) g += w[AB_TAPS - 1 - d] * f3[d];
-      if (cok) {
-        if constexpr (sizeof(TF) == 2) reinterpret_cast<uint16_t*>(dF)[t * C + c] = (uint16_t)f2bf(g);
-        else reinterpret_cast<float*>(dF)[t * C + c] = g;
+          for (int s = 0; s < AB_K2; ++s) dw[AB_K1 + s] += dU[2] * wm[12 - AB_K2 + s];
+#pragma unroll
+          for (int s = 0; s < AB_K3; ++s) dw[AB_K1 + AB_K2 + s] += dU[3] * wm[12 - AB_K3 + s];
+        }
+        if (ts == 0) {  // t - 1 is in the previous sequence: nothing of this one reaches it
+#pragma unroll
+          for (int d = 0; d < AB_K1; ++d) f1[d] = 0.f;
+#pragma unroll
+          for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
+#pragma unroll
+          for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
+        }
+#pragma unroll
+        for (int s = 11; s > 0; --s) win[s] = win[s - 1];
+        win[0] = cur.f[i];
+        ts = ts == 0 ? S - 1 : ts - 1;
       }
-#pragma unroll
-      for (int s = 0; s < AB_K1; ++s) dw[s] += dU[1] * win[12 - AB_K1 + s];
-#pragma unroll
-      for (int s = 0; s < AB_K2; ++s) dw[AB_K1 + s] += dU[2] * win[12 - AB_K2 + s];
-#pragma unroll
-      for (int s = 0; s < AB_K3; ++s) dw[AB_K1 + AB_K2 + s] += dU[3] * win[12 - AB_K3 + s];
     }
-    if (t == t0) break;
-    if (t % S == 0) {  // t - 1 is in the previous sequence: nothing of this one reaches it
-#pragma unroll
-      for (int d = 0; d < AB_K1; ++d) f1[d] = 0.f;
-#pragma unroll
-      for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
-#pragma unroll
-      for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
-      load_win(t - 1);
-    } else {
-#pragma unroll
-      for (int s = 11; s > 0; --s) win[s] = win[s - 1];
-      const int64_t tt = t - 12;
-      win[0] = tt >= t - t % S ? ab_ld(F + tt * C + c) : 0.f;
-    }
+    tb = nb;
+    return nb >= t0;
+  };
+  Ld a, b;
+  load(top, a);
+  while (step(a, b) && step(b, a)) {
   }
   if (cok) {
 #pragma unroll
-    for (int k = 0; k < AB_TAPS; ++k) wpart[((int64_t)blockIdx.y * C + c) * AB_TAPS + k] = dw[k];
+    for (int k = 0; k < AB_TAPS; ++k) wpart[((int64_t)blockIdx.y * AB_TAPS + k) * C + c] = dw[k];
   }
 }
 
-// dconv_w in conv_w's layout from the strips' sums (strip order); one thread per tap.
+// dconv_w in conv_w's layout from the strips' sums (strip order); one thread per
+// (tap, channel).
 __global__ __launch_bounds__(256) void aug_bwd_wsum_kernel(const float* __restrict__ wpart, int nstrip, int64_t C,
                                                            float* __restrict__ dconv) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= C * AB_TAPS) return;
-  const int64_t c = g / AB_TAPS;
-  const int k = (int)(g - c * AB_TAPS);
+  const int k = (int)(g / C);
+  const int64_t c = g - k * C;
   float s = 0.f;
-  for (int q = 0; q < nstrip; ++q) s += wpart[((int64_t)q * C + c) * AB_TAPS + k];
+  for (int q = 0; q < nstrip; ++q) s += wpart[((int64_t)q * AB_TAPS + k) * C + c];
   int64_t o;
   if (k < AB_K1) o = c * AB_K1 + k;
   else if (k < AB_K1 + AB_K2) o = AB_K1 * C + c * AB_K2 + (k - AB_K1);
@@ -1082,19 +1245,19 @@ bool fast_augment_backward_supported(int dtype, int64_t B, int64_t S, int64_t C,
 }
 
 int64_t fast_augment_backward_ws_bytes(int64_t B, int64_t S, int64_t C) {
-  const int64_t T = B * S, nw = (C + 63) / 64, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
-  return al256(T * nw * AB_NV * 4) + al256(T * 32 * 4) + al256(nstrip * C * AB_TAPS * 4);
+  const int64_t T = B * S, nq = (C + 255) / 256, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
+  return al256(nq * AB_NV * T * 4) + al256(T * 32 * 4) + al256(nstrip * AB_TAPS * C * 4);
 }
 
 hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
                                         const float* conv_w, const float* dV, void* dF_out, float* dconv_w, void* ws,
                                         hipStream_t st) {
-  const int64_t T = B * S, nw = (C + 63) / 64, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
+  const int64_t T = B * S, nq = (C + 255) / 256, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
   unsigned char* p = (unsigned char*)ws;
   float* part = (float*)p;
-  float* coef = (float*)(p + al256(T * nw * AB_NV * 4));
-  float* wpart = (float*)(p + al256(T * nw * AB_NV * 4) + al256(T * 32 * 4));
-  const dim3 grid((unsigned)((C + 255) / 256), (unsigned)nstrip), blk(256);
+  float* coef = (float*)(p + al256(nq * AB_NV * T * 4));
+  float* wpart = (float*)(p + al256(nq * AB_NV * T * 4) + al256(T * 32 * 4));
+  const dim3 grid((unsigned)nq, (unsigned)nstrip), blk(256);
   if (dtype == 1)
     hipLaunchKernelGGL(aug_bwd_gram_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)F_out, T, S, C, conv_w, dV,
                        part);
@@ -1102,7 +1265,7 @@ hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B,
     hipLaunchKernelGGL(aug_bwd_gram_kernel<float>, grid, blk, 0, st, (const float*)F_out, T, S, C, conv_w, dV, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(aug_bwd_coef_kernel, dim3((unsigned)T), dim3(64), 0, st, part, T, (int)nw, coef);
+  hipLaunchKernelGGL(aug_bwd_coef_kernel, dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st, part, T, (int)nq, coef);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (dtype == 1)
     hipLaunchKernelGGL(aug_bwd_walk_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)F_out, T, S, C, conv_w, dV,
