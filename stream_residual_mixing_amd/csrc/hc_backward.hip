@@ -588,6 +588,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// element at byte offset `off` (per lane, 32 bits) of the row starting at `row`
+// (uniform): the address splits into a scalar base and a 32-bit lane offset
+template <typename TF>
+__device__ __forceinline__ float ab_ldo(const TF* row, uint32_t off) {
+  const TF* p = reinterpret_cast<const TF*>(reinterpret_cast<const char*>(row) + off);
+  if constexpr (sizeof(TF) == 2) return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+  else return *reinterpret_cast<const float*>(p);
+}
+
 template <typename TF>
 __device__ __forceinline__ float ab_ld(const TF* p) {
   if constexpr (sizeof(TF) == 2) return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
@@ -680,7 +689,7 @@ __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict_
   __shared__ float red[2][AB_GRP][4][AB_NV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
-  const bool cok = c0 < C;
+  const bool cok = c0 < C;  // lanes past C load zeros, so their products vanish
   const int64_t c = cok ? c0 : C - 1;
   const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
   const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;
@@ -690,70 +699,106 @@ __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict_
 #pragma unroll
   for (int s = 0; s < 12; ++s) {
     const int64_t tt = t0 - 12 + s;
-    win[s] = ab_ld(F + (tt >= 0 ? tt : 0) * C + c);
+    const float x = ab_ld(F + (tt >= 0 ? tt : 0) * C + c);  // loaded unconditionally, then selected
+    win[s] = cok ? x : 0.f;
   }
   struct Ld {
     float f[AB_PF], dv[AB_PF][4];
   };
-  auto load = [&](int64_t tb, Ld& L) __attribute__((always_inline)) {
+  const uint32_t ofF = (uint32_t)c * (uint32_t)sizeof(TF), ofV = (uint32_t)c * 4u;
+  // CLAMP: rows past T read row T - 1 (the strip's last group)
+  auto load = [&](int64_t tb, Ld& L, bool clamp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AB_PF; ++i) {
-      const int64_t t = tb + i < T ? tb + i : T - 1;
-      L.f[i] = ab_ld(F + t * C + c);
+      const int64_t t = clamp && tb + i >= T ? T - 1 : tb + i;
+      const float x = ab_ldo(F + t * C, ofF);  // loaded unconditionally, then selected
+      L.f[i] = cok ? x : 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L.dv[i][j] = dV[(t * 4 + j) * C + c];
-    }
-  };
-  int64_t tb = t0, ts = t0 % S;  // ts: position of token tb in its sequence
-  int rb = 0;                    // LDS buffer of the current group
-  auto step = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
-    const int64_t nb = tb + AB_PF;
-    load(nb, nxt);  // rows past T clamped: the last group's loads go unused
-#pragma unroll
-    for (int i = 0; i < AB_PF; ++i) {
-      const int64_t t = tb + i;
-      if (t < t1) {
-#pragma unroll
-        for (int s = 0; s < 11; ++s) win[s] = win[s + 1];
-        win[11] = cur.f[i];
-        float wm[12], u[4], v[AB_NV];
-        ab_mask(win, ts, wm);
-        ab_convs(w, wm, u);
-        int n = 0;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int k = a; k < 4; ++k) v[n++] = cok ? u[a] * u[k] : 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int a = 0; a < 4; ++a) v[10 + 4 * j + a] = cok ? cur.dv[i][j] * u[a] : 0.f;
-        const float r = ab_reduce_scatter(v, lane);
-        const int gi = (int)((t - t0) % AB_GRP);
-        if (!(lane & 1) && (lane >> 1) < AB_NV) red[rb][gi][wave][lane >> 1] = r;
-        if (gi == AB_GRP - 1 || t == t1 - 1) {  // the group is complete: add the waves' sums, store
-          lds_barrier();
-          const int64_t g0 = t - gi;
-#pragma unroll
-          for (int e = tid; e < AB_NV * AB_GRP; e += 256) {
-            const int k = e >> 4, q = e & (AB_GRP - 1);
-            if (q <= gi) {
-              const float* rr = &red[rb][q][0][k];
-              part[((int64_t)blockIdx.x * AB_NV + k) * T + g0 + q] =
-                  ((rr[0] + rr[AB_NV]) + rr[2 * AB_NV]) + rr[3 * AB_NV];
-            }
-          }
-          rb ^= 1;
-        }
-        ts = ts + 1 == S ? 0 : ts + 1;
+      for (int j = 0; j < 4; ++j) {
+        const float y = ab_ldo(dV + (t * 4 + j) * C, ofV);
+        L.dv[i][j] = cok ? y : 0.f;
       }
     }
+  };
+  // one token: window advanced by the row `f`, products of the token's components
+  // with dv, their wave sums into red[rb][gi]
+  auto token = [&](float f, const float (&dv)[4], int64_t ts, bool masked, int rb, int gi)
+                   __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 11; ++s) win[s] = win[s + 1];
+    win[11] = f;
+    float wm[12], u[4], v[AB_NV];
+    if (masked) ab_mask(win, ts, wm);
+    else
+#pragma unroll
+      for (int s = 0; s < 12; ++s) wm[s] = win[s];
+    ab_convs(w, wm, u);
+    int n = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int k = a; k < 4; ++k) v[n++] = u[a] * u[k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) v[10 + 4 * j + a] = dv[j] * u[a];
+    const float r = ab_reduce_scatter(v, lane);
+    if (!(lane & 1) && (lane >> 1) < AB_NV) red[rb][gi][wave][lane >> 1] = r;
+  };
+  int64_t tb = t0, ts = t0 % S;  // ts: position of token tb in its sequence
+  int rb = 0;                    // LDS buffer of the current 16-token group
+  // after every 16 tokens and at the strip's end the waves' sums are added and stored
+  auto flush = [&](int gi0, int64_t nb) __attribute__((always_inline)) {
+    if (gi0 + AB_PF == AB_GRP || nb >= t1) {
+      lds_barrier();
+      const int64_t g0 = tb - gi0;
+      const int ng = (int)(t1 - g0 < AB_GRP ? t1 - g0 : AB_GRP);  // tokens of the group inside the strip
+#pragma unroll
+      for (int e = tid; e < AB_NV * AB_GRP; e += 256) {
+        const int k = e >> 4, q = e & (AB_GRP - 1);
+        if (q < ng) {
+          const float* rr = &red[rb][q][0][k];
+          part[((int64_t)blockIdx.x * AB_NV + k) * T + g0 + q] = ((rr[0] + rr[AB_NV]) + rr[2 * AB_NV]) + rr[3 * AB_NV];
+        }
+      }
+      rb ^= 1;
+    }
+  };
+  // one load group of AB_PF tokens tb.. while the next group loads. Fast: every
+  // token inside the strip, at least 11 past its sequence start, and the next
+  // group's rows inside T. General: tokens past t1 are computed on clamped rows
+  // and never stored, and the window is masked per token.
+  auto step_fast = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
+    const int64_t nb = tb + AB_PF;
+    load(nb, nxt, false);
+    const int gi0 = (int)((tb - t0) & (AB_GRP - 1));
+#pragma unroll
+    for (int i = 0; i < AB_PF; ++i) token(cur.f[i], cur.dv[i], 0, false, rb, gi0 + i);
+    ts = ts + AB_PF == S ? 0 : ts + AB_PF;  // the pair's condition keeps ts + AB_PF <= S
+    flush(gi0, nb);
+    tb = nb;
+  };
+  auto step_general = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
+    const int64_t nb = tb + AB_PF;
+    load(nb, nxt, true);
+    const int gi0 = (int)((tb - t0) & (AB_GRP - 1));
+#pragma unroll
+    for (int i = 0; i < AB_PF; ++i) {
+      token(cur.f[i], cur.dv[i], ts, true, rb, gi0 + i);
+      ts = ts + 1 == S ? 0 : ts + 1;
+    }
+    flush(gi0, nb);
     tb = nb;
     return nb < t1;
   };
   Ld a, b;
-  load(t0, a);
-  while (step(a, b) && step(b, a)) {
+  load(t0, a, true);
+  for (;;) {  // pairs of groups keep the roles of a and b fixed
+    while (tb + 3 * AB_PF <= T && tb + 2 * AB_PF <= t1 && ts >= 11 && ts + 2 * AB_PF <= S) {
+      step_fast(a, b);
+      step_fast(b, a);
+    }
+    if (tb >= t1 || !step_general(a, b) || !step_general(b, a)) break;
   }
 }
 
@@ -900,13 +945,11 @@ __global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict_
   float dw[AB_TAPS];
 #pragma unroll
   for (int k = 0; k < AB_TAPS; ++k) dw[k] = 0.f;
-  float f1[AB_K1], f2[AB_K2], f3[AB_K3];  // fj[d] = dU_j[t + d], zero past the sequence
+  // acc[d]: what the tokens after t, within t's sequence, add to dF_out[t - d]
+  // through the convs' transpose
+  float acc[11];
 #pragma unroll
-  for (int d = 0; d < AB_K1; ++d) f1[d] = 0.f;
-#pragma unroll
-  for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
-#pragma unroll
-  for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
+  for (int d = 0; d < 11; ++d) acc[d] = 0.f;
   float win[12];  // F_out[t-11..t] as loaded (rows < 0 masked at use)
 #pragma unroll
   for (int s = 0; s < 12; ++s) {
@@ -918,83 +961,98 @@ __global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict_
   struct Ld {
     float f[AB_PF], dv[AB_PF][4];
   };
-  auto load = [&](int64_t tb, Ld& L) __attribute__((always_inline)) {
+  const uint32_t ofF = (uint32_t)c * (uint32_t)sizeof(TF), ofV = (uint32_t)c * 4u;
+  // CLAMP: tokens below t0 read t0's rows, rows < 0 row 0 (masked at use)
+  auto load = [&](int64_t tb, Ld& L, bool clamp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AB_PF; ++i) {
-      const int64_t t = tb - i >= t0 ? tb - i : t0;
-      L.f[i] = ab_ld(F + (t >= 12 ? t - 12 : 0) * C + c);  // rows < 0: masked at use
+      const int64_t t = clamp && tb - i < t0 ? t0 : tb - i;
+      L.f[i] = ab_ldo(F + (clamp && t < 12 ? 0 : t - 12) * C, ofF);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L.dv[i][j] = dV[(t * 4 + j) * C + c];
+      for (int j = 0; j < 4; ++j) L.dv[i][j] = ab_ldo(dV + (t * 4 + j) * C, ofV);
     }
+  };
+  // one token t (ts: its position in the sequence). GENERAL: the window masked
+  // at the sequence start, the transpose's sums cleared when t starts its
+  // sequence, and dF_out and the tap sums taken only for t in [t0, t1) (the
+  // group may hold halo tokens and, at the end, tokens below t0).
+  auto token = [&](float fnext, const float (&dv)[4], int64_t t, int64_t ts, bool general)
+                   __attribute__((always_inline)) {
+    float wm[12], u[4];
+    if (general) ab_mask(win, ts, wm);
+    else
+#pragma unroll
+      for (int s = 0; s < 12; ++s) wm[s] = win[s];
+    ab_convs(w, wm, u);
+    const float4* cp = reinterpret_cast<const float4*>(cfs + (t - t0) * 32);
+    float dU[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 pr = cp[r], qr = cp[4 + r];
+      dU[r] = pr.x * dv[0] + pr.y * dv[1] + pr.z * dv[2] + pr.w * dv[3] + qr.x * u[0] + qr.y * u[1] + qr.z * u[2] +
+              qr.w * u[3];
+    }
+    const float g = acc[0] + dU[0] + w[AB_K1 - 1] * dU[1] + w[AB_K1 + AB_K2 - 1] * dU[2] + w[AB_TAPS - 1] * dU[3];
+    const bool in = !general || (t >= t0 && t < t1);
+    if (in && cok) {
+      char* row = reinterpret_cast<char*>(dF + t * C) + ofF;
+      if constexpr (sizeof(TF) == 2) *reinterpret_cast<uint16_t*>(row) = (uint16_t)f2bf(g);
+      else *reinterpret_cast<float*>(row) = g;
+    }
+    // dU_j[t] reaches dF_out[t - d] with tap w_j[kappa_j - 1 - d], d < kappa_j
+#pragma unroll
+    for (int d = 1; d < 12; ++d) {
+      float a = d < 11 ? acc[d] : 0.f;
+      if (d < AB_K1) a += w[AB_K1 - 1 - d] * dU[1];
+      if (d < AB_K2) a += w[AB_K1 + AB_K2 - 1 - d] * dU[2];
+      a += w[AB_TAPS - 1 - d] * dU[3];
+      acc[d - 1] = general && ts == 0 ? 0.f : a;  // t - 1 lies in the previous sequence
+    }
+    float e1 = dU[1], e2 = dU[2], e3 = dU[3];
+    if (general && !in) e1 = e2 = e3 = 0.f;
+#pragma unroll
+    for (int s = 0; s < AB_K1; ++s) dw[s] += e1 * wm[12 - AB_K1 + s];
+#pragma unroll
+    for (int s = 0; s < AB_K2; ++s) dw[AB_K1 + s] += e2 * wm[12 - AB_K2 + s];
+#pragma unroll
+    for (int s = 0; s < AB_K3; ++s) dw[AB_K1 + AB_K2 + s] += e3 * wm[12 - AB_K3 + s];
+#pragma unroll
+    for (int s = 11; s > 0; --s) win[s] = win[s - 1];
+    win[0] = fnext;
   };
   __syncthreads();
   int64_t tb = top, ts = top % S;  // ts: position of token tb in its sequence
-  auto step = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
+  // one load group of AB_PF tokens tb, tb - 1, .. while the next group loads.
+  // Fast: every token inside the strip and at least 11 past its sequence start,
+  // the next group's tokens not below t0. General: everything else.
+  auto step_fast = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
     const int64_t nb = tb - AB_PF;
-    load(nb, nxt);  // tokens below t0 clamped: the last group's loads go unused
+    load(nb, nxt, false);
+#pragma unroll
+    for (int i = 0; i < AB_PF; ++i) token(cur.f[i], cur.dv[i], tb - i, 0, false);
+    ts -= AB_PF;  // the pair's condition keeps ts >= AB_PF
+    tb = nb;
+  };
+  auto step_general = [&](Ld& cur, Ld& nxt) __attribute__((always_inline)) {
+    const int64_t nb = tb - AB_PF;
+    load(nb, nxt, true);  // tokens below t0 clamped: the last group's loads go unused
 #pragma unroll
     for (int i = 0; i < AB_PF; ++i) {
-      const int64_t t = tb - i;
-      if (t >= t0) {
-        float wm[12], u[4];
-        ab_mask(win, ts, wm);
-        ab_convs(w, wm, u);
-        const float4* cp = reinterpret_cast<const float4*>(cfs + (t - t0) * 32);
-        float dU[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float4 pr = cp[r], qr = cp[4 + r];
-          dU[r] = pr.x * cur.dv[i][0] + pr.y * cur.dv[i][1] + pr.z * cur.dv[i][2] + pr.w * cur.dv[i][3] +
-                  qr.x * u[0] + qr.y * u[1] + qr.z * u[2] + qr.w * u[3];
-        }
-#pragma unroll
-        for (int d = AB_K1 - 1; d > 0; --d) f1[d] = f1[d - 1];
-#pragma unroll
-        for (int d = AB_K2 - 1; d > 0; --d) f2[d] = f2[d - 1];
-#pragma unroll
-        for (int d = AB_K3 - 1; d > 0; --d) f3[d] = f3[d - 1];
-        f1[0] = dU[1];
-        f2[0] = dU[2];
-        f3[0] = dU[3];
-        if (t < t1) {
-          float g = dU[0];
-#pragma unroll
-          for (int d = 0; d < AB_K1; ++d) g += w[AB_K1 - 1 - d] * f1[d];
-#pragma unroll
-          for (int d = 0; d < AB_K2; ++d) g += w[AB_K1 + AB_K2 - 1 - d] * f2[d];
-#pragma unroll
-          for (int d = 0; d < AB_K3; ++d) g += w[AB_TAPS - 1 - d] * f3[d];
-          if (cok) {
-            if constexpr (sizeof(TF) == 2) reinterpret_cast<uint16_t*>(dF)[t * C + c] = (uint16_t)f2bf(g);
-            else reinterpret_cast<float*>(dF)[t * C + c] = g;
-          }
-#pragma unroll
-          for (int s = 0; s < AB_K1; ++s) dw[s] += dU[1] * wm[12 - AB_K1 + s];
-#pragma unroll
-          for (int s = 0; s < AB_K2; ++s) dw[AB_K1 + s] += dU[2] * wm[12 - AB_K2 + s];
-#pragma unroll
-          for (int s = 0; s < AB_K3; ++s) dw[AB_K1 + AB_K2 + s] += dU[3] * wm[12 - AB_K3 + s];
-        }
-        if (ts == 0) {  // t - 1 is in the previous sequence: nothing of this one reaches it
-#pragma unroll
-          for (int d = 0; d < AB_K1; ++d) f1[d] = 0.f;
-#pragma unroll
-          for (int d = 0; d < AB_K2; ++d) f2[d] = 0.f;
-#pragma unroll
-          for (int d = 0; d < AB_K3; ++d) f3[d] = 0.f;
-        }
-#pragma unroll
-        for (int s = 11; s > 0; --s) win[s] = win[s - 1];
-        win[0] = cur.f[i];
-        ts = ts == 0 ? S - 1 : ts - 1;
-      }
+      token(cur.f[i], cur.dv[i], tb - i, ts, true);
+      ts = ts == 0 ? S - 1 : ts - 1;
     }
     tb = nb;
     return nb >= t0;
   };
   Ld a, b;
-  load(top, a);
-  while (step(a, b) && step(b, a)) {
+  load(top, a, true);
+  for (;;) {  // pairs of groups keep the roles of a and b fixed
+    // (the pair's loads reach token tb - 3 AB_PF + 1 and its row tb - 3 AB_PF - 11)
+    while (tb < t1 && tb - 3 * AB_PF + 1 >= t0 && tb >= 3 * AB_PF + 11 && ts >= 11 + 2 * AB_PF - 1) {
+      step_fast(a, b);
+      step_fast(b, a);
+    }
+    if (tb < t0 || !step_general(a, b) || !step_general(b, a)) break;
   }
   if (cok) {
 #pragma unroll

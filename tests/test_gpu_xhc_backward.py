@@ -204,3 +204,52 @@ def test_augment_backward_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def _aug_only(seed, B, S, C, dtype):
+    """F_out, conv taps (as the xHC recipe draws them) and a seeded upstream dV."""
+    rng = synth.make_rng(seed, 0)
+    F = synth.Tensor(synth.normal(rng, (B * S, C)), dtype)
+    ws = [synth.normal(rng, (C, k), float(np.sqrt(1.0 / k))) for k in (4, 8, 12)]
+    dV = synth.normal(synth.make_rng(seed, 0, stream=2), (B * S, 4, C))
+    return F, ws, dV
+
+
+def _aug_only_check(F, ws, dV, B, S):
+    w = np.concatenate([x.reshape(-1) for x in ws])
+    dF, dw = hc.xhc_augment_backward(dev(F), dev(w), (4, 8, 12), B, S, torch.from_numpy(dV).cuda())
+    torch.cuda.synchronize()
+    a = O.xhc_augment_backward(F.values, ws, B, S, dV.astype(np.float64))
+    if F.dtype == synth.BF16:
+        check_bf16("dF_out", host64(dF), a["dF_out"])
+        e = rel_l2(host64(dF), a["dF_out"])
+    else:
+        e = check_fp32("dF_out", host64(dF), a["dF_out"], BWD_REL)
+    ed = check_fp32("dconv", host64(dw), np.concatenate([x.reshape(-1) for x in a["dconv_ws"]]), BWD_REL)
+    note(f"relative L2: dF_out {e:.2e}, dconv {ed:.2e}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 11, 12, 13])
+def test_augment_backward_short_sequences(S):
+    """Sequences no longer than the convs' reach: every token near a sequence
+    start (masked windows, the transpose's sums cleared at each start, the
+    position wrapping inside one load group); C = 200 leaves part of the last
+    channel block idle."""
+    B = 37
+    note(f"xhc_augment_backward short sequences B={B} S={S} C=200 bf16")
+    _aug_only_check(*_aug_only(600 + S, B, S, 200, synth.BF16), B, S)
+
+
+@pytest.mark.parametrize("B,S,C", [(3, 100, 300), (1, 517, 64)])
+def test_augment_backward_float32(B, S, C):
+    """F_out and dF_out in float32: the same kernels on float32 rows."""
+    note(f"xhc_augment_backward float32 B={B} S={S} C={C}")
+    _aug_only_check(*_aug_only(620 + S, B, S, C, synth.F32), B, S)
+
+
+def test_augment_backward_full_size():
+    """The augmented workload's shape, B = 2 sequences of S = 4096, C = 4096, in one
+    call: dF_out over every element and the conv taps summed over all tokens."""
+    B, S, C = 2, 4096, 4096
+    note(f"xhc_augment_backward full size B={B} S={S} C={C} bf16")
+    _aug_only_check(*_aug_only(640, B, S, C, synth.BF16), B, S)
