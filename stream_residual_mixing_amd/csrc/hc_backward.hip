@@ -1214,8 +1214,10 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
 
 bool fast_xhc_backward_supported(int dtype, int N, int k, int K, int64_t T, int64_t C, int iters) {
   return dtype == 1 && N % 4 == 0 && N >= 4 && N <= 16 && k == 4 && (K == 1 || K == 4) && T >= 1 && iters >= 1 &&
-         iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 && fast_xroute_partial_bytes(T, C, K) > 0 &&
-         fast_xpre_partial_bytes(T, N, C) > 0 && (C + FCH - 1) / FCH <= 65535 && T * (int64_t)N * C < (1ll << 40);
+         iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 && C < (1ll << 24) &&
+         // the projection partials are addressed with 32-bit buffer offsets
+         fast_xroute_partial_bytes(T, C, K) < (1ll << 31) && fast_xpre_partial_bytes(T, N, C) < (1ll << 31) &&
+         (C + FCH - 1) / FCH <= 65535 && T * (int64_t)N * C < (1ll << 40);
 }
 
 int64_t fast_xhc_backward_ws_bytes(int64_t T, int N, int64_t C) {
@@ -1265,20 +1267,9 @@ hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C,
                                      float* db_pre, float* dalpha, float* dh_pre, void* ws, hipStream_t st) {
   const BwdWs w = carve_pre(ws, T, N, C, nullptr);
   const uint16_t* x = (const uint16_t*)X;
-  hipError_t e = launch_fast_xpre_bwd_front(X, T, N, C, phi_pre, w.packed, w.phi_rows, w.partial, st);
+  // the projection recompute also forms dH_pre = <dF_in, x_i> (same read of the state)
+  hipError_t e = launch_fast_xpre_bwd_front(X, T, N, C, phi_pre, dF_in, w.packed, w.phi_rows, w.partial, st);
   if (e != hipSuccess) return e;
-  const dim3 tg((unsigned)T), tb(256);
-  switch (N) {
-    case 4: hipLaunchKernelGGL(bwd_pre_sums_kernel<4>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N); break;
-    case 8: hipLaunchKernelGGL(bwd_pre_sums_kernel<8>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N); break;
-    case 12:
-      hipLaunchKernelGGL(bwd_pre_sums_kernel<12>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N);
-      break;
-    default:
-      hipLaunchKernelGGL(bwd_pre_sums_kernel<16>, tg, tb, 0, st, x, (const uint16_t*)dF_in, C, dh_pre, N);
-      break;
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_fast_xpre_bwd_coeffs(w.partial, T, N, C, b_pre, a_pre, dh_pre, w.dP, w.g2, w.red, w.h_pre, st)) !=
       hipSuccess)
     return e;

@@ -86,17 +86,19 @@ hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const floa
                                  uint4* phi_rows, float* partial, hipStream_t st);
 // xHC routed-step backward pieces: the gathered active set's coefficient
 // backward for K = 1 or 4 (partials of launch_fast_xhc_active, dh [T, 4K + 16] =
-// [dH_post | dH_res], h_res out), and the pre map's: the full-state projection of the pre columns
-// (pack + proj_wide on stream groups) and its backward (dh_pre [T, N] in; dP,
-// g2, red, h_pre [T, N] out). Partial buffer sizes of each.
+// [dH_post | dH_res], h_res out), and the pre map's: the full-state projection of
+// the pre columns with the sums <dF_in, x_i> from the same read of the state
+// (pack + proj_wide on stream groups), and its backward (dh_pre [T, N], dP, g2,
+// red, h_pre [T, N] out). Partial buffer sizes of each.
 hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, int K, const float* b_act,
                                          float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
                                          float* red, float* h_res, hipStream_t st);
-hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C, const float* phi_pre, void* packed,
-                                      uint4* phi_rows, float* partial, hipStream_t st);
+hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C, const float* phi_pre,
+                                      const void* dF_in, void* packed, uint4* phi_rows, float* partial,
+                                      hipStream_t st);
 hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, int64_t C, const float* b_pre,
-                                       float a_pre, const float* dh_pre, float* dP, float* g2, float* red,
-                                       float* h_pre, hipStream_t st);
+                                       float a_pre, float* dh_pre, float* dP, float* g2, float* red, float* h_pre,
+                                       hipStream_t st);
 int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K);
 int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C);
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,

@@ -131,6 +131,28 @@ __device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Lane exchange within rows of 16 lanes (DPP): quad permutations and row rotations.
+constexpr int DPP_QXOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QXOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROR4 = 0x124;  // row_ror:4
+constexpr int DPP_ROR8 = 0x128;  // row_ror:8
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// the sum over a row of 16 lanes, in every lane of the row
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<DPP_QXOR1>(x);
+  x += dpp<DPP_QXOR2>(x);
+  x += dpp<DPP_ROR8>(x);
+  x += dpp<DPP_ROR4>(x);
+  return x;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
 // v if keep, else zeros: per-component selects (a select between two uint4
 // objects can become a select of their addresses, which puts them in scratch).
 __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
@@ -157,11 +179,11 @@ constexpr int SPI = 4;                   // super-chunks per item
 constexpr int NCOEF = TILE * 20;         // h_res (16) | h_post (4) per token of a tile
 enum : int { ROWS_CONTIG = 0, ROWS_GROUPS = 1, ROWS_GATHER = 2 };
 
-template <int NB, int TT = TILE>  // TT: tokens per item
+template <int NB, int TT = TILE, int EX = 0>  // TT: tokens per item; EX: extra columns after ss
 struct PartGeom {
-  static constexpr int NCP = NB * 16;    // packed hi | lo columns
-  static constexpr int NCOLP = NB * 8;   // logical columns (padded)
-  static constexpr int PROW = NCOLP + 1; // floats per token of a partial
+  static constexpr int NCP = NB * 16;         // packed hi | lo columns
+  static constexpr int NCOLP = NB * 8;        // logical columns (padded)
+  static constexpr int PROW = NCOLP + 1 + EX; // floats per token of a partial: columns | ss | EX extra
   static constexpr int PART = TT * PROW;
   static constexpr int NPEND = (PART + STHR - 1) / STHR;
 };
@@ -194,6 +216,7 @@ struct SplitArgs {
   uint16_t* Y;             // POST: [T, 4, C]
   const uint16_t* phi_p;   // packed phi, NB * 16 columns
   float* part;             // [nitem][tokens per item][PROW]
+  const uint16_t* dF;      // proj_wide_kernel with DH: dF_in [T, C]
 };
 
 template <bool POST, int NB, int MODE>
@@ -619,15 +642,20 @@ constexpr int W_SPI = 8;
 constexpr int W_LROW = W_SC * 2 + 16;         // bytes per (stream, token) row in LDS, padded
 constexpr int W_LBUF = NS4 * W_TOK * W_LROW;  // bytes per LDS buffer
 
-template <int NB, int MODE>
+// With DH, each streaming thread also takes its 16-byte piece of dF_in at the
+// same (token, channels) and adds <dF_in, x_i> over its 8 channels for the
+// group's 4 streams; at the item end the 16 lanes of a token are summed (DPP)
+// and the 4 sums go to the partial's extra columns (the gradient of the pre
+// map's input in the xHC backward, from the same read of the state).
+template <int NB, int MODE, bool DH = false>
 __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   static_assert(MODE != ROWS_GATHER, "gathered rows use mhc_split_kernel");
   // NB = 4 (4 token blocks x 4 accumulator sets) would exceed the registers
   static_assert(NB <= 3, "more columns use the 32-token items of mhc_split_kernel");
-  using PG = PartGeom<NB, W_TOK>;
+  using PG = PartGeom<NB, W_TOK, DH ? NS4 : 0>;
   constexpr int NCP = PG::NCP;
   constexpr int NPH = (32 * PG::PROW + STHR - 1) / STHR;  // partial floats per thread per 32-token half
-  static_assert(SWAVE * 32 * (NCP + 1) * 4 + SWAVE * 32 * 4 <= W_LBUF, "reduction buffer");
+  static_assert(SWAVE * 32 * (NCP + 1) * 4 + SWAVE * 32 * 4 + 32 * NS4 * 4 <= W_LBUF, "reduction buffer");
   const uint16_t* X = A.X;
   const int64_t T = A.T, C = A.C;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * W_LBUF];
@@ -666,7 +694,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   // Loads are unconditional (clamped rows and channels), as in mhc_split_kernel.
-  auto load_half = [&](const Item& it, int64_t s, auto P, uint4 (&xv)[NS4]) __attribute__((always_inline)) {
+  auto load_half = [&](const Item& it, int64_t s, auto P, uint4 (&xv)[NS4], uint4& dv) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     int64_t t = (int64_t)it.tile * W_TOK + st_tok + 32 * p;
     t = t < T ? t : T - 1;
@@ -675,18 +703,36 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     const uint16_t* xg = X + t * A.rowstride + cc + (int64_t)(MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
 #pragma unroll
     for (int i = 0; i < NS4; ++i) xv[i] = ld_stream(xg + i * C);
+    if constexpr (DH) dv = ld_stream(A.dF + t * C + cc);
   };
+  float dh[2][NS4];  // DH: this thread's <dF_in, x_i> of the item, per token half
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) dh[r][i] = 0.f;
   // the tile in LDS holds zeros for rows past T and channels past C
-  auto stream_half = [&](const Item& it, int64_t s, auto P, const uint4 (&xc)[NS4], unsigned char* buf)
-                         __attribute__((always_inline)) {
+  auto stream_half = [&](const Item& it, int64_t s, auto P, const uint4 (&xc)[NS4], const uint4& dc,
+                         unsigned char* buf) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     const int m = st_tok + 32 * p;
     const bool ok = ((int64_t)it.tile * W_TOK + m < T) && (s * W_SC + st_c8 < C);
+    const uint4 dz = keep_or_zero(ok, dc);
 #pragma unroll
-    for (int i = 0; i < NS4; ++i)
-      *reinterpret_cast<uint4*>(buf + (i * W_TOK + m) * W_LROW + st_c8 * 2) = keep_or_zero(ok, xc[i]);
+    for (int i = 0; i < NS4; ++i) {
+      const uint4 xz = keep_or_zero(ok, xc[i]);
+      *reinterpret_cast<uint4*>(buf + (i * W_TOK + m) * W_LROW + st_c8 * 2) = xz;
+      if constexpr (DH) {  // bf16 pairs multiplied into the float32 sum (v_dot2_f32_bf16)
+        float a = dh[p][i];
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xz.x), as_bf16x2(dz.x), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xz.y), as_bf16x2(dz.y), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xz.z), as_bf16x2(dz.z), a, false);
+        a = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xz.w), as_bf16x2(dz.w), a, false);
+        dh[p][i] = a;
+      }
+    }
   };
   uint4 xq[4][NS4];
+  uint4 dq[4];  // DH: the dF_in pieces beside xq
   uint4 pfq[2][NB];
   auto load_pf = [&](const Item& it2, int64_t s2, int si, uint4 (&dst)[NB]) __attribute__((always_inline)) {
     const int64_t cg = s2 * W_SC + cgw * 32;
@@ -720,12 +766,12 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     constexpr int h0 = 2 * j, h1 = 2 * j + 1;
     constexpr int q0 = h0 % 4, q1 = h1 % 4;
     const int64_t s = it.s0 + j;
-    stream_half(it, s, H0{}, xq[q0], buf);
-    if constexpr (h0 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h0 + 4) / 2, H0{}, xq[q0]);
-    else load_half(nx, nx.s0 + (h0 + 4 - 2 * W_SPI) / 2, H0{}, xq[q0]);
-    stream_half(it, s, H1{}, xq[q1], buf);
-    if constexpr (h1 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h1 + 4) / 2, H1{}, xq[q1]);
-    else load_half(nx, nx.s0 + (h1 + 4 - 2 * W_SPI) / 2, H1{}, xq[q1]);
+    stream_half(it, s, H0{}, xq[q0], dq[q0], buf);
+    if constexpr (h0 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h0 + 4) / 2, H0{}, xq[q0], dq[q0]);
+    else load_half(nx, nx.s0 + (h0 + 4 - 2 * W_SPI) / 2, H0{}, xq[q0], dq[q0]);
+    stream_half(it, s, H1{}, xq[q1], dq[q1], buf);
+    if constexpr (h1 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h1 + 4) / 2, H1{}, xq[q1], dq[q1]);
+    else load_half(nx, nx.s0 + (h1 + 4 - 2 * W_SPI) / 2, H1{}, xq[q1], dq[q1]);
     __syncthreads();
     if constexpr (j + 1 < W_SPI) mfma_phase(buf, it, it.s0 + j + 1);
     else mfma_phase(buf, nx, nx.s0);
@@ -733,10 +779,10 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 
   int item = (int)blockIdx.x;
   Item it = item_of(item);
-  load_half(it, it.s0, H0{}, xq[0]);
-  load_half(it, it.s0, H1{}, xq[1]);
-  load_half(it, it.s0 + 1, H0{}, xq[2]);
-  load_half(it, it.s0 + 1, H1{}, xq[3]);
+  load_half(it, it.s0, H0{}, xq[0], dq[0]);
+  load_half(it, it.s0, H1{}, xq[1], dq[1]);
+  load_half(it, it.s0 + 1, H0{}, xq[2], dq[2]);
+  load_half(it, it.s0 + 1, H1{}, xq[3], dq[3]);
   load_pf(it, it.s0, 0, pfq[0]);
   load_pf(it, it.s0, 1, pfq[1]);
   // the partial sums this thread reduced for the previous item (pitem; -1: none):
@@ -771,9 +817,22 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     // through the buffer the last MFMA phase read
     float* red = reinterpret_cast<float*>(lds + ((step - 1) & 1) * W_LBUF);  // [SWAVE][32][NCP + 1]
     float* ssr = red + SWAVE * 32 * (NCP + 1);                                // [SWAVE][32]
+    float* dhr = ssr + SWAVE * 32;                                            // DH: [32][NS4]
+    if constexpr (DH) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < NS4; ++i) dh[r][i] = row16_sum(dh[r][i]);
+    }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       __syncthreads();
+      if constexpr (DH) {
+        if ((tid & 15) == 0) {
+#pragma unroll
+          for (int i = 0; i < NS4; ++i) dhr[st_tok * NS4 + i] = dh[r][i];
+        }
+      }
 #pragma unroll
       for (int tbb = 0; tbb < 2; ++tbb) {
         const int tb = 2 * r + tbb;
@@ -797,13 +856,19 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 #pragma unroll
           for (int w = 0; w < SWAVE; ++w)
             sum += red[(w * 32 + m) * (NCP + 1) + col] + red[(w * 32 + m) * (NCP + 1) + PG::NCOLP + col];
-        } else {
+        } else if (col == PG::NCOLP) {
 #pragma unroll
           for (int w = 0; w < SWAVE; ++w) sum += ssr[w * 32 + m];
+        } else {
+          sum = dhr[m * NS4 + (col - PG::NCOLP - 1)];
         }
         pend[r][u] = sum;
       }
     }
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) dh[r][i] = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -819,16 +884,6 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 
 // Partial sums of an item: W_TOK-token items (proj_wide_kernel) or TILE-token
 // items (mhc_split_kernel); the finish kernels take the item size TT.
-
-// Lane exchange within rows of 16 lanes (DPP): quad permutations and row rotations.
-constexpr int DPP_QXOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-constexpr int DPP_QXOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
-constexpr int DPP_ROR4 = 0x124;  // row_ror:4
-constexpr int DPP_ROR8 = 0x128;  // row_ror:8
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
 
 // 1 / r with r = sqrt(ss / 4C), the token's RMS over the flattened state
 // (0 for an all-zero state), and the gate logit alpha * P / r + b: shared by
@@ -1054,21 +1109,24 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
 }
 
 // Backward of the xHC pre map h_pre = sigmoid(alpha_pre P / r + b_pre) for token
-// tt, from the full-state partials (xpre_finish_kernel's layout: per tile the
-// N/4 stream groups x S slices, columns [pre N | ...]). 16 lanes per token, lane
-// c < N for pre column c: P and the sum of squares added over the items in
-// order, r = sqrt(ss / (N C)) and h_pre as xpre_finish_kernel forms them, then
-// dz = dH_pre h (1 - h), dP = alpha dz / r and the gradient through r,
-// 2 dss = -d rho rho^3 / (N C). Outputs: dP [T, 32] (columns N..31 zero), g2,
-// h_pre [T, N], and per workgroup of 16 tokens red [36] = the sums of dz
-// [16, zero past N] | 0 x 16 | dz P rho over the gate | 0 0 0.
+// tt, from the full-state partials of proj_wide_kernel with DH (per tile the N/4
+// stream groups x S slices, columns [pre N | ... | ss | <dF_in, x_i> of the
+// group's 4 streams]). 16 lanes per token, lane c < N for pre column c: P and
+// the sum of squares added over the items in order, dH_pre[c] = <dF_in, x_c>
+// added over the S items of c's group in order, r = sqrt(ss / (N C)) and h_pre
+// as xpre_finish_kernel forms them, then dz = dH_pre h (1 - h), dP = alpha dz /
+// r and the gradient through r, 2 dss = -d rho rho^3 / (N C). Outputs: dh_pre
+// [T, N], dP [T, 32] (columns N..31 zero), g2, h_pre [T, N], and per workgroup
+// of 16 tokens red [36] = the sums of dz [16, zero past N] | 0 x 16 | dz P rho
+// over the gate | 0 0 0.
 template <int NB, int TT>
 __global__ __launch_bounds__(256) void bwd_xpre_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C,
-                                                             int N, int per_tile, const float* __restrict__ b_pre,
-                                                             float a_pre, const float* __restrict__ dh_pre,
+                                                             int N, int S, const float* __restrict__ b_pre,
+                                                             float a_pre, float* __restrict__ dh_pre,
                                                              float* __restrict__ dP, float* __restrict__ g2,
                                                              float* __restrict__ red, float* __restrict__ h_pre) {
-  using PG = PartGeom<NB, TT>;
+  using PG = PartGeom<NB, TT, NS4>;
+  const int per_tile = (N / 4) * S;
   const int tid = threadIdx.x;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
   const int64_t tt = g >> 4;
@@ -1079,28 +1137,27 @@ __global__ __launch_bounds__(256) void bwd_xpre_coeff_kernel(const float* __rest
   const int mrow = (int)(tc - tile * TT);
   const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
   const int cc = c < N ? c : 0;
-  float ss = 0.f, pc = 0.f;
+  float ss = 0.f, pc = 0.f, dhc = 0.f;
 #pragma unroll 4
   for (int it = 0; it < per_tile; ++it) {
     const float* b = base + (int64_t)it * PG::PART;
     ss += b[PG::NCOLP];
     pc += b[cc];
   }
+  {
+    const float* b = base + (int64_t)(cc >> 2) * S * PG::PART + PG::NCOLP + 1 + (cc & 3);
+#pragma unroll 4
+    for (int it = 0; it < S; ++it) dhc += b[(int64_t)it * PG::PART];
+  }
   const float r = sqrtf(ss / (float)((double)N * (double)C));
   const float invr = (r > 0.f) ? 1.0f / r : 0.f;
   const bool col = c < N;
   const float h = sigmoid(a_pre * (pc * invr) + b_pre[cc]);
-  const float dz = col ? dh_pre[tc * N + c] * h * (1.0f - h) : 0.f;
-  auto row16 = [](float x) __attribute__((always_inline)) {
-    x += dpp<DPP_QXOR1>(x);
-    x += dpp<DPP_QXOR2>(x);
-    x += dpp<DPP_ROR8>(x);
-    x += dpp<DPP_ROR4>(x);
-    return x;
-  };
-  const float drho = row16(a_pre * dz * pc);
-  const float u = row16(dz * pc * invr);
+  const float dz = col ? dhc * h * (1.0f - h) : 0.f;
+  const float drho = row16_sum(a_pre * dz * pc);
+  const float u = row16_sum(dz * pc * invr);
   if (valid) {
+    if (col) dh_pre[tt * N + c] = dhc;
     dP[tt * 32 + c] = col ? a_pre * dz * invr : 0.f;
     dP[tt * 32 + 16 + c] = 0.f;
     if (col) h_pre[tt * N + c] = h;
@@ -1474,8 +1531,8 @@ bool shape_ok(int64_t T, int64_t C, int NG, int NB) {
   if (C % 32 != 0 || C < 32 || C >= (1ll << 24)) return false;
   return part_tokens(T) * NG * slices(C) * (NB * 8 + 1) * 4 < (1ll << 31);
 }
-int64_t part_bytes(int64_t T, int64_t C, int NG, int NB) {
-  return part_tokens(T) * NG * slices(C) * (NB * 8 + 1) * 4;
+int64_t part_bytes(int64_t T, int64_t C, int NG, int NB, int EX = 0) {
+  return part_tokens(T) * NG * slices(C) * (NB * 8 + 1 + EX) * 4;
 }
 int nb_for(int ncols) { return ncols <= 16 ? 2 : (ncols <= 24 ? 3 : 4); }
 int grid_for(int nitem) {
@@ -1516,10 +1573,11 @@ hipError_t launch_split_nb(int nb, const SplitArgs& A, hipStream_t st) {
   }
 }
 
-// projection only, W_TOK-token items (A from geom(..., W_TOK))
-template <int NB, int MODE>
+// projection only, W_TOK-token items (A from geom(..., W_TOK)); DH: with the
+// dF_in sums (A.dF)
+template <int NB, int MODE, bool DH = false>
 hipError_t launch_wide(const SplitArgs& A, hipStream_t st) {
-  hipLaunchKernelGGL((proj_wide_kernel<NB, MODE>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
+  hipLaunchKernelGGL((proj_wide_kernel<NB, MODE, DH>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
   return hipGetLastError();
 }
 
@@ -1665,24 +1723,27 @@ hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C, const float* phi_pre, void* packed,
-                                      uint4* phi_rows, float* partial, hipStream_t st) {
+hipError_t launch_fast_xpre_bwd_front(const void* X, int64_t T, int N, int64_t C, const float* phi_pre,
+                                      const void* dF_in, void* packed, uint4* phi_rows, float* partial,
+                                      hipStream_t st) {
   hipError_t e = launch_pack(phi_pre, N, nullptr, 0, (int64_t)N * C, 16, packed, st, phi_rows);
   if (e != hipSuccess) return e;
-  return launch_wide<2, ROWS_GROUPS>(args(X, T, C, (int64_t)N * C, geom(T, C, N / 4, W_TOK), packed, partial), st);
+  SplitArgs A = args(X, T, C, (int64_t)N * C, geom(T, C, N / 4, W_TOK), packed, partial);
+  A.dF = (const uint16_t*)dF_in;
+  return launch_wide<2, ROWS_GROUPS, true>(A, st);
 }
 
 hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, int64_t C, const float* b_pre,
-                                       float a_pre, const float* dh_pre, float* dP, float* g2, float* red,
-                                       float* h_pre, hipStream_t st) {
+                                       float a_pre, float* dh_pre, float* dP, float* g2, float* red, float* h_pre,
+                                       hipStream_t st) {
   const int64_t threads = T * 16;
   hipLaunchKernelGGL((bwd_xpre_coeff_kernel<2, W_TOK>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     partial, T, C, N, (int)((N / 4) * slices(C)), b_pre, a_pre, dh_pre, dP, g2, red, h_pre);
+                     partial, T, C, N, (int)slices(C), b_pre, a_pre, dh_pre, dP, g2, red, h_pre);
   return hipGetLastError();
 }
 
 int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K) { return part_bytes(T, C, 1, K == 4 ? 4 : 3); }
-int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C) { return part_bytes(T, C, N / 4, 2); }
+int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C) { return part_bytes(T, C, N / 4, 2, NS4); }
 
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
                                   float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
