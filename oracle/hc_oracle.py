@@ -673,3 +673,76 @@ def xhc_augment_backward(F_out, conv_ws, batch: int, seq: int, dV):
         dF += df
         dws.append(dw)
     return dict(dF_out=dF, dconv_ws=dws)
+
+
+# ------------------------------------------------------------------ xHC-Flash
+#
+# "xHC: Expanded Hyper-Connections" (paper summary, memory efficiency; project
+# page, xHC-Flash): a block of L consecutive sublayers shares one routing
+# decision, forms every sublayer's pre map from the block-entry state, and
+# defers the residual mixing to the block's last sublayer (attention + MLP: L =
+# 2; the four-sublayer variant: L = 4); a light correction rebuilds the later
+# sublayers' inputs without reading the state again. The pages give no
+# formulas; the readings taken here:
+#  * sublayer l has its own phi_pre^(l), b_pre^(l) (alpha_pre shared) applied to
+#    the RMS-normalised flattening of the entry state X_0, as xhc_pre forms h_pre;
+#  * the router runs once on X_0; its active set idx serves all L sublayers;
+#  * the active maps come from X_0's active rows: a post map per sublayer (one
+#    write-back component each) and one H_res for the block, i.e.
+#    xhc_active_coeffs with K = L (post columns a*L + l);
+#  * sublayers l < L-1 add H_post[:, l] F_out^(l) to the active rows with no
+#    mixing; the last one mixes with H_res and adds its own write, as xhc_route.
+# Under these readings the later dense reads are exact functions of the entry
+# state's dense reads and the earlier outputs (xhc_flash_input).
+
+
+def xhc_flash_pre(X, phi_pres, b_pres, alpha_pre, w_router, k: int, m: int):
+    """Block entry: the shared active set and the L pre maps and dense reads of X_0.
+    Returns dict(idx [T, k], score, h_pre [L, T, N], F_pre [L, T, C])."""
+    first = xhc_pre(X, phi_pres[0], b_pres[0], alpha_pre, w_router, k, m)
+    hs, fs = [first["h_pre"]], [first["F_in"]]
+    for l in range(1, len(phi_pres)):
+        r = xhc_pre(X, phi_pres[l], b_pres[l], alpha_pre)
+        hs.append(r["h_pre"])
+        fs.append(r["F_in"])
+    return dict(idx=first["idx"], score=first["score"], h_pre=np.stack(hs), F_pre=np.stack(fs))
+
+
+def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L: int, sinkhorn_iters: int = 20):
+    """The block's maps from X_0's active rows: H_post [T, k, L] (column l: sublayer
+    l's post map) and the block's H_res [T, k, k]."""
+    return xhc_active_coeffs(xhc_gather(X, idx), phi_act, b_act, alpha_post, alpha_res, L, sinkhorn_iters)
+
+
+def xhc_flash_input(l: int, F_pre_l, h_pre_l, idx, H_post, F_outs):
+    """Sublayer l's input without a second read of the state. Before l the block
+    only added H_post[:, j] F_out^(j) to the active rows, so its dense read is
+      F_in^(l) = F_pre^(l) + sum_{j<l} c_j F_out^(j),
+      c_j[t] = sum_a h_pre^(l)[t, idx[t, a]] H_post[t, a, j].
+    F_outs: [T, L, C] or a list (only j < l used)."""
+    F = _f64(F_pre_l).copy()
+    T = F.shape[0]
+    idx = np.asarray(idx)
+    h_act = _f64(h_pre_l)[np.arange(T)[:, None], idx]  # [T, k]
+    H_post = _f64(H_post)
+    for j in range(l):
+        c = np.sum(h_act * H_post[:, :, j], axis=1)
+        F += c[:, None] * _f64(F_outs[:, j] if not isinstance(F_outs, list) else F_outs[j])
+    return F
+
+
+def xhc_flash_post(X, idx, H_post, H_res, F_outs):
+    """Block end: the active rows after all L sublayers,
+      X_L,A = H_res (X_0,A + sum_{j<L-1} H_post[:, j] F_out^(j)) + H_post[:, L-1] F_out^(L-1);
+    the other rows pass through. F_outs [T, L, C]. Returns X_L [T, N, C] fp64."""
+    X = _f64(X).copy()
+    idx = np.asarray(idx)
+    F = _f64(F_outs)
+    T, L = F.shape[0], F.shape[1]
+    H_post = _f64(H_post)
+    X_A = xhc_gather(X, idx)
+    if L > 1:
+        X_A = X_A + np.einsum("taj,tjc->tac", H_post[:, :, :L - 1], F[:, :L - 1])
+    X_A = np.einsum("tab,tbc->tac", _f64(H_res), X_A) + H_post[:, :, L - 1, None] * F[:, None, L - 1]
+    X[np.arange(T)[:, None], idx] = X_A
+    return X

@@ -853,3 +853,87 @@ def test_conv_backward_adjoint_identities():
     val = np.sum(dg * O.causal_dwconv(F, w, B, S))
     assert math.isclose(np.sum(dF * F), val, rel_tol=1e-12)
     assert math.isclose(np.sum(dw * w), val, rel_tol=1e-12)
+
+
+# ------------------------------------------------------------------ xHC-Flash
+
+def _flash_case(seed, T=6, N=8, C=5, k=4, m=2, L=2):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, N, C))
+    phis = [rng.standard_normal((N * C, N)) * 0.3 for _ in range(L)]
+    bs = [rng.standard_normal(N) * 0.2 for _ in range(L)]
+    w_r = rng.standard_normal((N * C, N - m)) * 0.3
+    phi_act = rng.standard_normal((k * C, k * L + k * k)) * 0.3
+    b_act = rng.standard_normal(k * L + k * k) * 0.2
+    F_outs = rng.standard_normal((T, L, C))
+    return X, phis, bs, w_r, phi_act, b_act, F_outs
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_flash_matches_materialised_block(L):
+    """The block run sublayer by sublayer with the state written out after each
+    one (sublayers before the last add their post write to the active rows, the
+    last mixes with H_res and adds its own, every sublayer's input is the dense
+    read of the state as it then is) gives the inputs xhc_flash_input rebuilds
+    from the entry-state reads and the state xhc_flash_post writes."""
+    X0, phis, bs, w_r, phi_act, b_act, F_outs = _flash_case(700 + L, L=L)
+    k, m = 4, 2
+    pre = O.xhc_flash_pre(X0, phis, bs, 0.7, w_r, k, m)
+    idx = pre["idx"]
+    H_post, H_res = O.xhc_flash_maps(X0, idx, phi_act, b_act, 0.6, 0.9, L, 20)
+    T = X0.shape[0]
+    rows = np.arange(T)[:, None]
+    Xs = X0.copy()
+    for l in range(L):
+        want = np.einsum("ti,tic->tc", pre["h_pre"][l], Xs)  # dense read of the current state
+        got = O.xhc_flash_input(l, pre["F_pre"][l], pre["h_pre"][l], idx, H_post, F_outs)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+        XA = Xs[rows, idx]
+        for a in range(k):
+            upd = H_post[:, a, l, None] * F_outs[:, l]
+            if l < L - 1:
+                XA[:, a] = XA[:, a] + upd
+        if l == L - 1:
+            mixed = np.zeros_like(XA)
+            for a in range(k):
+                for b in range(k):
+                    mixed[:, a] += H_res[:, a, b, None] * XA[:, b]
+                mixed[:, a] += H_post[:, a, l, None] * F_outs[:, l]
+            XA = mixed
+        Xs[rows, idx] = XA
+    np.testing.assert_allclose(O.xhc_flash_post(X0, idx, H_post, H_res, F_outs), Xs, rtol=1e-12, atol=1e-12)
+    # rows outside the active set are the entry state's
+    act = np.zeros((T, X0.shape[1]), bool)
+    act[rows, idx] = True
+    np.testing.assert_array_equal(O.xhc_flash_post(X0, idx, H_post, H_res, F_outs)[~act], X0[~act])
+
+
+def test_flash_single_sublayer_is_xhc():
+    """L = 1 is one plain xHC sublayer: the same h_pre, dense read and active set
+    as xhc_pre, and the block end equals xhc_route with Wb = F_out."""
+    X0, phis, bs, w_r, phi_act, b_act, F_outs = _flash_case(720, L=1)
+    pre = O.xhc_flash_pre(X0, phis, bs, 0.7, w_r, 4, 2)
+    ref = O.xhc_pre(X0, phis[0], bs[0], 0.7, w_r, 4, 2)
+    np.testing.assert_array_equal(pre["idx"], ref["idx"])
+    np.testing.assert_allclose(pre["h_pre"][0], ref["h_pre"], rtol=1e-14)
+    np.testing.assert_allclose(pre["F_pre"][0], ref["F_in"], rtol=1e-14)
+    H_post, H_res = O.xhc_flash_maps(X0, pre["idx"], phi_act, b_act, 0.6, 0.9, 1, 20)
+    X1, hp, hr = O.xhc_route(X0, pre["idx"], phi_act, b_act, 0.6, 0.9, F_outs[:, 0], 20)
+    np.testing.assert_allclose(O.xhc_flash_post(X0, pre["idx"], H_post, H_res, F_outs), X1, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(H_post, hp, rtol=1e-14)
+
+
+def test_flash_correction_coefficient_by_hand():
+    """One token, N = 6, k = 4 active streams idx = (0, 1, 3, 5), L = 2: the
+    correction of sublayer 1 is c = sum_a h_pre^(1)[idx_a] H_post[a, 0] (here
+    0.5*1 + 0.25*2 + 1*0 + 2*0.5 = 2), so F_in^(1) = F_pre^(1) + 2 F_out^(0)."""
+    h1 = np.array([[0.5, 0.25, 9.0, 1.0, 9.0, 2.0]])
+    idx = np.array([[0, 1, 3, 5]])
+    H_post = np.zeros((1, 4, 2))
+    H_post[0, :, 0] = [1.0, 2.0, 0.0, 0.5]
+    H_post[0, :, 1] = [7.0, 7.0, 7.0, 7.0]  # sublayer 1's own map plays no part in its input
+    F_pre1 = np.array([[1.0, -1.0, 3.0]])
+    F_outs = np.array([[[2.0, 0.0, -1.0], [100.0, 100.0, 100.0]]])
+    got = O.xhc_flash_input(1, F_pre1, h1, idx, H_post, F_outs)
+    np.testing.assert_allclose(got, [[5.0, -1.0, 1.0]], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.xhc_flash_input(0, F_pre1, h1, idx, H_post, F_outs), F_pre1, rtol=0, atol=0)
