@@ -311,6 +311,78 @@ def xhc_backward_bench(torch, hc, dev, reps: int = 10) -> dict:
             "xhc_route_backward_K4": rate(alg_4, t_4), "xhc_augment_backward": rate(alg_a, t_a)}
 
 
+def flash_bench(torch, hc, dev, reps: int = 10) -> dict:
+    """xHC-Flash blocks of L = 2 (attention + MLP) and L = 4 sublayers at N=16, k=4,
+    m=2, C=4096, T=8192 bf16, on three rotating entry states: xhc_flash_pre (routing,
+    L pre maps, the L dense reads), xhc_flash_maps, xhc_flash_input for l = 1..L-1
+    (sublayer 0 reads F_pre[0] as is), xhc_flash_post; HIP events around the block
+    (median). algorithmic_bytes: the entry state read once, F_pre written, the
+    active rows read for the maps, each corrected input's reads and write, and the
+    block end's active rows read and written with the L outputs read."""
+    N, k, m, C, T = 16, 4, 2, 4096, 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(7000)
+    rn = lambda *shape, std=1.0: torch.randn(*shape, device=dev, generator=g) * std
+    Xs = [rn(T, N, C).to(torch.bfloat16) for _ in range(3)]
+    w_r = rn(N * C, N - m, std=(1.0 / (N * C)) ** 0.5)
+    out = {}
+    for L in (2, 4):
+        phi_pre, b_pre = rn(L, N * C, N, std=0.02), torch.zeros(L, N, device=dev)
+        phi_act = rn(k * C, k * L + k * k, std=0.02)
+        b_act = torch.zeros(k * L + k * k, device=dev)
+        b_act[k * L:] = torch.eye(k, device=dev).flatten()
+        F_outs = rn(T, L, C).to(torch.bfloat16)
+        po = (torch.empty(T, k, dtype=torch.int32, device=dev), torch.empty(T, N - m, device=dev),
+              torch.empty(L, T, N, device=dev), torch.empty(L, T, C, dtype=torch.bfloat16, device=dev))
+        mo = (torch.empty(T, k, L, device=dev), torch.empty(T, k, k, device=dev))
+        F_in = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(hc.xhc_flash_pre_workspace_bytes(T, N, C, m, L, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+        wsm = torch.empty(hc.xhc_flash_maps_workspace_bytes(T, N, C, k, L, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+        wsq = torch.empty(hc.xhc_flash_post_workspace_bytes(T, k, L), dtype=torch.uint8, device=dev)
+
+        def block(i, ev=None):
+            X = Xs[i % 3]
+            idx, _, h_pre, F_pre = hc.xhc_flash_pre(X, phi_pre, b_pre, 0.01, w_r, k=k, m=m, out=po, workspace=wsp)
+            if ev:
+                ev[1].record()
+            Hp, Hr = hc.xhc_flash_maps(X, idx, phi_act, b_act, 0.01, 0.01, L, out=mo, workspace=wsm)
+            if ev:
+                ev[2].record()
+            for l in range(1, L):
+                hc.xhc_flash_input(l, F_pre[l], h_pre[l], idx, Hp, F_outs, out=F_in)
+            if ev:
+                ev[3].record()
+            hc.xhc_flash_post(X, idx, Hp, Hr, F_outs, workspace=wsq)
+
+        for i in range(3):
+            block(i)
+        torch.cuda.synchronize()
+        tt = [[], [], [], [], []]
+        for i in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record()
+            block(i, ev)
+            ev[4].record()
+            torch.cuda.synchronize()
+            for j in range(4):
+                tt[j].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
+            tt[4].append(ev[0].elapsed_time(ev[4]) * 1e-3)
+        md = [sorted(v)[len(v) // 2] for v in tt]
+        e = 2
+        alg = (T * N * C * e + L * T * C * e + T * k * C * e
+               + sum((2 + l) * T * C * e for l in range(1, L))
+               + 2 * T * k * C * e + L * T * C * e)
+        out[f"L{L}"] = {"block_us": md[4] * 1e6, "per_sublayer_us": md[4] * 1e6 / L,
+                        "xhc_flash_pre_us": md[0] * 1e6, "xhc_flash_maps_us": md[1] * 1e6,
+                        "xhc_flash_input_us": md[2] * 1e6, "xhc_flash_post_us": md[3] * 1e6,
+                        "algorithmic_bytes": alg, "achieved_GBps": alg / md[4] / 1e9,
+                        "tokens_per_s_per_sublayer": T * L / md[4]}
+    return {"workload": "xHC-Flash N=16 k=4 m=2 C=4096 T=8192 bf16, blocks of L = 2 and 4 sublayers (K = 1 each)",
+            **out}
+
+
 def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     """Throughput of the xHC sublayer (N=16, k=4, m=2, C=4096, T=8192, bf16) on
     seeded synthetic device data: the routed step xhc_pre + xhc_route (K=1, F_out
@@ -677,6 +749,7 @@ def main() -> int:
         result["hc_baseline"] = hc_baseline_bench(torch, hc, dev)
         result["backward"] = backward_bench(torch, hc, dev)
         result["xhc_backward"] = xhc_backward_bench(torch, hc, dev)
+        result["flash"] = flash_bench(torch, hc, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)

@@ -69,6 +69,7 @@ extern "C" {
 #define HC_MAX_KAPPA 32       /* causal conv kernel size */
 #define HC_MAX_ITERS 10000    /* Sinkhorn iterations */
 #define HC_MAX_BWD_ITERS 64   /* Sinkhorn iterations of hc_backward (iterates kept on chip) */
+#define HC_MAX_FLASH_SUBLAYERS 4 /* L, sublayers of an xHC-Flash block */
 
 /* Human-readable text of a status code (static string, never NULL). */
 const char* hc_status_string(int status);
@@ -378,6 +379,67 @@ int xhc_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int
                          const float* conv_w, const int* kappa, int r, const float* dV,
                          void* dF_out, float* dconv_w, void* workspace, int64_t workspace_bytes,
                          void* stream);
+
+/*
+ * xHC-Flash ([xHC] memory efficiency; [xHC-R] method and memory-efficiency table): a block of L
+ * consecutive sublayers (L = 2: attention + MLP; L = 4: the four-sublayer
+ * variant) shares one routing decision and the block-entry state's full-state
+ * reads; the residual mixing of the active streams is deferred to the block's
+ * last sublayer, and the later sublayers' inputs are rebuilt from the entry
+ * state's dense reads without reading the state again. Readings (the pages give
+ * no formulas): sublayer l has its own phi_pre^(l), b_pre^(l) (alpha_pre shared)
+ * on the RMS-normalised entry state, as xhc_pre forms h_pre; the router runs
+ * once at block entry; the active maps come from the entry state's active rows
+ * with one post column per sublayer and one H_res; sublayers l < L-1 add
+ * H_post[:, l] F_out^(l) to the active rows with no mixing and the last mixes
+ * with H_res and adds its own write. A block runs:
+ *   xhc_flash_pre(X_0) -> idx, h_pre, F_pre;  xhc_flash_maps(X_0, idx) -> H_post, H_res;
+ *   for l: F_in^(l) = xhc_flash_input(l, ...); F_out^(l) = sublayer_l(F_in^(l));
+ *   xhc_flash_post(X_0 -> X_L, F_outs).
+ * X_0 is read by the first two calls and updated in place by the last.
+ *
+ * xhc_flash_pre: idx [T, k] (int32) from the router w_router [N*C, N-m] as
+ *   xhc_pre selects it (m fixed streams + the top k-m candidates, ascending);
+ *   score [T, N-m] (may be NULL); h_pre [L, T, N] float32 with phi_pre [L, N*C, N],
+ *   b_pre [L, N]; F_pre [L, T, C] in X's dtype: F_pre[l] = sum_i h_pre[l, :, i] X_0[:, i]
+ *   (the L dense reads come from one pass over X_0 for bfloat16 with N a
+ *   multiple of 4 up to 16, C % 8 == 0 and 16-byte aligned X and F_pre).
+ *   Requires 1 <= m < N, m <= k <= min(N, HC_MAX_ACTIVE), 1 <= L <=
+ *   HC_MAX_FLASH_SUBLAYERS. Workspace: xhc_flash_pre_workspace_bytes.
+ * xhc_flash_maps: H_post [T, k, L] (column l: sublayer l's 2 sigma post map) and
+ *   H_res [T, k, k] (Sinkhorn, sinkhorn_iters) from the active rows of X_0 (idx),
+ *   phi_act [k*C, k*L + k*k] with columns [post (a*L + l) | res (a*k + b)], b_act
+ *   in the same order: xhc_route's maps with K = L write-back columns.
+ *   Workspace: xhc_flash_maps_workspace_bytes.
+ * xhc_flash_input: sublayer l's input F_in [T, C] = F_pre_l + sum_{j<l} c_j
+ *   F_outs[:, j] with c_j[t] = sum_a h_pre_l[t, idx[t, a]] H_post[t, a, j];
+ *   F_pre_l = F_pre[l], h_pre_l = h_pre[l] [T, N], F_outs [T, L, C] in the stream
+ *   dtype (rows j < l read; may be NULL for l = 0). F_in may be F_pre_l itself.
+ *   Computed in float32, rounded once. No workspace.
+ * xhc_flash_post: X_0 -> X_L in place on the active rows:
+ *   X_L,A = H_res (X_0,A + sum_{j<L-1} H_post[:, j] F_out^(j)) + H_post[:, L-1] F_out^(L-1),
+ *   computed as one mix with the write maps E[:, j] = H_res H_post[:, j] (j < L-1)
+ *   and E[:, L-1] = H_post[:, L-1] (kept in the workspace, T*k*L floats,
+ *   xhc_flash_post_workspace_bytes); rows outside the active set untouched.
+ * All: dtype HC_F32 or HC_BF16; float arrays 4-byte aligned, stream arrays aligned
+ * to their element size, workspaces 256 bytes; outputs overlap no input, other
+ * output or workspace (HC_ERR_ALIAS). Workspace queries: -1 for invalid sizes.
+ */
+int64_t xhc_flash_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int L, int dtype);
+int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, int L, const float* phi_pre,
+                  const float* b_pre, float alpha_pre, const float* w_router, int32_t* idx, float* score,
+                  float* h_pre, void* F_pre, void* workspace, int64_t workspace_bytes, void* stream);
+int64_t xhc_flash_maps_workspace_bytes(int64_t T, int N, int64_t C, int k, int L, int dtype);
+int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
+                   const float* phi_act, const float* b_act, float alpha_post, float alpha_res, int sinkhorn_iters,
+                   float* H_post, float* H_res, void* workspace, int64_t workspace_bytes, void* stream);
+int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int l, const void* F_pre_l,
+                    const float* h_pre_l, const int32_t* idx, const float* H_post, const void* F_outs, void* F_in,
+                    void* stream);
+int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L);
+int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
+                   const float* H_post, const float* H_res, const void* F_outs, void* workspace,
+                   int64_t workspace_bytes, void* stream);
 
 /* ----------------------------------------- HC baseline and gain diagnostic -- */
 

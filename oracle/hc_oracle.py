@@ -677,8 +677,8 @@ def xhc_augment_backward(F_out, conv_ws, batch: int, seq: int, dV):
 
 # ------------------------------------------------------------------ xHC-Flash
 #
-# "xHC: Expanded Hyper-Connections" (paper summary, memory efficiency; project
-# page, xHC-Flash): a block of L consecutive sublayers shares one routing
+# "xHC: Expanded Hyper-Connections" (paper summary, memory efficiency and the
+# xHC-Flash variant; repository README, method and memory-efficiency table): a block of L consecutive sublayers shares one routing
 # decision, forms every sublayer's pre map from the block-entry state, and
 # defers the residual mixing to the block's last sublayer (attention + MLP: L =
 # 2; the four-sublayer variant: L = 4); a light correction rebuilds the later

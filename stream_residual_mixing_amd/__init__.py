@@ -53,6 +53,17 @@ _SIGS = {
                            _c_float, _c_float, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64,
                            _vp]),
     "xhc_augment_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int, _c_int]),
+    "xhc_flash_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
+    "xhc_flash_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _c_float,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "xhc_flash_maps_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
+    "xhc_flash_maps": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _c_float,
+                                _c_float, _c_int, _vp, _vp, _vp, _c_i64, _vp]),
+    "xhc_flash_input": (_c_int, [_c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp]),
+    "xhc_flash_post_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_int]),
+    "xhc_flash_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                _c_i64, _vp]),
     "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
     "xhc_backward_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_route_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _c_float, _c_float,
@@ -377,6 +388,91 @@ def xhc_route(X, Wb, phi_act, b_act, alpha_post, alpha_res, *, k=4, m=2, idx=Non
     return out
 
 
+def xhc_flash_pre_workspace_bytes(T: int, N: int, C: int, m: int, L: int, dtype) -> int:
+    return int(lib().xhc_flash_pre_workspace_bytes(T, N, C, m, L, _DT[dtype]))
+
+
+def xhc_flash_pre(X, phi_pre, b_pre, alpha_pre, w_router, *, k=4, m=2, out=None, workspace=None, stream=None):
+    """xHC-Flash block entry: phi_pre [L, N*C, N], b_pre [L, N]. Returns (idx [T, k],
+    score [T, N-m], h_pre [L, T, N], F_pre [L, T, C])."""
+    X = _dev_tensor(X, "X", _DT)
+    T, N, C = X.shape
+    dev = X.device
+    phi_pre = _f32(phi_pre, "phi_pre")
+    L = phi_pre.shape[0]
+    if out is None:
+        out = (torch.empty(T, k, dtype=torch.int32, device=dev), torch.empty(T, N - m, device=dev),
+               torch.empty(L, T, N, device=dev), torch.empty(L, T, C, dtype=X.dtype, device=dev))
+    idx, score, h_pre, F_pre = out
+    ws = _workspace(xhc_flash_pre_workspace_bytes(T, N, C, m, L, X.dtype), dev, workspace)
+    _check("xhc_flash_pre", lib().xhc_flash_pre(_ptr(X), _DT[X.dtype], T, N, C, k, m, L, _ptr(phi_pre),
+                                                _ptr(_f32(b_pre, "b_pre")), float(alpha_pre),
+                                                _ptr(_f32(w_router, "w_router")), _ptr(idx), _ptr(score),
+                                                _ptr(h_pre), _ptr(F_pre), _ptr(ws), ws.numel(), _stream(dev, stream)))
+    return idx, score, h_pre, F_pre
+
+
+def xhc_flash_maps_workspace_bytes(T: int, N: int, C: int, k: int, L: int, dtype) -> int:
+    return int(lib().xhc_flash_maps_workspace_bytes(T, N, C, k, L, _DT[dtype]))
+
+
+def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L, *, sinkhorn_iters=20, out=None,
+                   workspace=None, stream=None):
+    """The block's maps from X's active rows: returns (H_post [T, k, L], H_res [T, k, k])."""
+    X = _dev_tensor(X, "X", _DT)
+    T, N, C = X.shape
+    idx = _dev_tensor(idx, "idx", (torch.int32,))
+    k = idx.shape[1]
+    dev = X.device
+    if out is None:
+        out = (torch.empty(T, k, L, device=dev), torch.empty(T, k, k, device=dev))
+    Hp, Hr = out
+    ws = _workspace(xhc_flash_maps_workspace_bytes(T, N, C, k, L, X.dtype), dev, workspace)
+    _check("xhc_flash_maps", lib().xhc_flash_maps(_ptr(X), _DT[X.dtype], T, N, C, k, L, _ptr(idx),
+                                                  _ptr(_f32(phi_act, "phi_act")), _ptr(_f32(b_act, "b_act")),
+                                                  float(alpha_post), float(alpha_res), int(sinkhorn_iters), _ptr(Hp),
+                                                  _ptr(Hr), _ptr(ws), ws.numel(), _stream(dev, stream)))
+    return Hp, Hr
+
+
+def xhc_flash_input(l, F_pre_l, h_pre_l, idx, H_post, F_outs, *, N=None, out=None, stream=None):
+    """Sublayer l's input from the entry-state read F_pre_l [T, C] and the earlier
+    outputs F_outs [T, L, C] (rows j < l read). Returns F_in [T, C]."""
+    F_pre_l = _dev_tensor(F_pre_l, "F_pre_l", _DT)
+    T, C = F_pre_l.shape
+    h_pre_l = _f32(h_pre_l, "h_pre_l")
+    N = h_pre_l.shape[1] if N is None else N
+    idx = _dev_tensor(idx, "idx", (torch.int32,))
+    H_post = _f32(H_post, "H_post")
+    k, L = H_post.shape[1], H_post.shape[2]
+    F_outs = None if F_outs is None else _dev_tensor(F_outs, "F_outs", (F_pre_l.dtype,))
+    F_in = torch.empty_like(F_pre_l) if out is None else out
+    _check("xhc_flash_input", lib().xhc_flash_input(_DT[F_pre_l.dtype], T, N, C, k, L, int(l), _ptr(F_pre_l),
+                                                    _ptr(h_pre_l), _ptr(idx), _ptr(H_post), _ptr(F_outs), _ptr(F_in),
+                                                    _stream(F_pre_l.device, stream)))
+    return F_in
+
+
+def xhc_flash_post_workspace_bytes(T: int, k: int, L: int) -> int:
+    return int(lib().xhc_flash_post_workspace_bytes(T, k, L))
+
+
+def xhc_flash_post(X, idx, H_post, H_res, F_outs, *, workspace=None, stream=None):
+    """Block end in place on X [T, N, C] from the entry state's active rows and
+    F_outs [T, L, C]. Returns X."""
+    X = _dev_tensor(X, "X", _DT)
+    T, N, C = X.shape
+    idx = _dev_tensor(idx, "idx", (torch.int32,))
+    H_post = _f32(H_post, "H_post")
+    k, L = H_post.shape[1], H_post.shape[2]
+    F_outs = _dev_tensor(F_outs, "F_outs", (X.dtype,))
+    ws = _workspace(xhc_flash_post_workspace_bytes(T, k, L), X.device, workspace)
+    _check("xhc_flash_post", lib().xhc_flash_post(_ptr(X), _DT[X.dtype], T, N, C, k, L, _ptr(idx), _ptr(H_post),
+                                                  _ptr(_f32(H_res, "H_res")), _ptr(F_outs), _ptr(ws), ws.numel(),
+                                                  _stream(X.device, stream)))
+    return X
+
+
 def xhc_augment_workspace_bytes(batch, seq, C, kappas, dtype, v_dtype=None) -> int:
     karr = (ctypes.c_int * max(len(kappas), 1))(*[int(x) for x in kappas])
     vdt = dtype if v_dtype is None else v_dtype
@@ -555,6 +651,8 @@ __all__ = [
     "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward_post", "hc_backward", "xhc_backward_workspace_bytes",
     "xhc_route_backward", "xhc_pre_backward", "xhc_augment_backward_workspace_bytes", "xhc_augment_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
-    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "hc_tanh_coeffs", "hc_amax_gain",
+    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "xhc_flash_pre_workspace_bytes", "xhc_flash_pre",
+    "xhc_flash_maps_workspace_bytes", "xhc_flash_maps", "xhc_flash_input", "xhc_flash_post_workspace_bytes",
+    "xhc_flash_post", "hc_tanh_coeffs", "hc_amax_gain",
     "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",
 ]

@@ -785,6 +785,204 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
                                               Wb, K, st));
 }
 
+// ---------------------------------------------------------------- xHC-Flash
+
+static int64_t flash_pre_ws(int64_t T, int N, int64_t C, int m, int dtype) {
+  return xhc_pre_ws(T, N, C, m, 1, dtype) + align256(T * (N - m) * 4);
+}
+
+int64_t xhc_flash_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int L, int dtype) {
+  if (T < 0 || N < 2 || N > HC_MAX_STREAMS || m < 1 || m >= N || C < 1 || L < 1 || L > HC_MAX_FLASH_SUBLAYERS ||
+      !dtype_ok(dtype))
+    return -1;
+  return flash_pre_ws(T, N, C, m, dtype);
+}
+
+int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, int L, const float* phi_pre,
+                  const float* b_pre, float alpha_pre, const float* w_router, int32_t* idx, float* score,
+                  float* h_pre, void* F_pre, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || N < 2 || N > HC_MAX_STREAMS || m < 1 || k < m || k > N ||
+      m >= N || k > HC_MAX_ACTIVE || L < 1 || L > HC_MAX_FLASH_SUBLAYERS)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!X || !phi_pre || !b_pre || !w_router || !idx || !h_pre || !F_pre) return HC_ERR_NULL;
+  const size_t es = esize(dtype);
+  if (!aligned_to(X, es) || !aligned_to(F_pre, es) || !aligned_to(phi_pre, 4) || !aligned_to(b_pre, 4) ||
+      !aligned_to(w_router, 4) || !aligned_to(h_pre, 4) || !aligned_to(idx, 4) || (score && !aligned_to(score, 4)))
+    return HC_ERR_ALIGN;
+  const int64_t wsb = flash_pre_ws(T, N, C, m, dtype);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t NC = (int64_t)N * C;
+  const void* outs[4] = {F_pre, h_pre, idx, score};
+  const int64_t ob[4] = {L * T * C * (int64_t)es, L * T * N * 4, T * k * 4, T * (N - m) * 4};
+  const void* ins[5] = {X, phi_pre, b_pre, w_router, workspace};
+  const int64_t ib[5] = {T * NC * (int64_t)es, L * NC * N * 4, (int64_t)L * N * 4, NC * (N - m) * 4, wsb};
+  if (any_overlap(outs, ob, 4, ins, ib, 5)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* p = (char*)workspace;
+  const int pcols = N + (N - m);
+  float* P = (float*)p;
+  p += align256(T * pcols * 4);
+  float* ss = (float*)p;
+  p += align256(T * 4);
+  p += align256(T * N * 4);  // (xhc_pre's h_pre scratch; h_pre is an output here)
+  const hc::XhcFastWs f = hc::xhc_pre_fast_ws(T, N, C, m, 1, dtype);
+  void* packed = p;
+  float* partial = (float*)(p + align256(f.packed));
+  p += align256(f.packed) + align256(f.partial);
+  float* sc = score ? score : (float*)p;
+  const bool fast = f.packed > 0 && aligned_to(X, 16);
+  hipError_t e = hipSuccess;
+  // sublayer l's pre map from its own phi_pre^(l), b_pre^(l); the router with the first
+  for (int l = 0; l < L && e == hipSuccess; ++l) {
+    const float* phl = phi_pre + (int64_t)l * NC * N;
+    const float* bl = b_pre + (int64_t)l * N;
+    float* hl = h_pre + (int64_t)l * T * N;
+    const float* wr = l == 0 ? w_router : nullptr;
+    if (fast) {
+      e = hc::launch_fast_xhc_full(X, T, N, C, k, m, phl, bl, alpha_pre, wr, hl, l == 0 ? sc : nullptr,
+                                   l == 0 ? idx : nullptr, nullptr, packed, partial, st);
+    } else {
+      e = hc::launch_proj_generic(dtype, X, NC, T, C, N, nullptr, N, phl, N, wr, wr ? N - m : 0, P, ss, st);
+      if (e == hipSuccess)
+        e = hc::launch_xhc_select(P, wr ? pcols : N, 0, N, ss, (float)((double)N * (double)C), T, N, k, m,
+                                  alpha_pre, bl, hl, wr ? sc : nullptr, wr ? idx : nullptr, st);
+    }
+  }
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  // the L dense reads of the entry state
+  if (hc::fast_pre_multi_supported(dtype, N, C, L, X, F_pre))
+    return launch_status(hc::launch_fast_pre_multi(X, T, N, C, L, h_pre, F_pre, st));
+  for (int l = 0; l < L; ++l) {
+    void* Fl = (char*)F_pre + (int64_t)l * T * C * (int64_t)es;
+    e = hc::launch_pre_generic(dtype, vec_ok(C, {X, Fl}), X, T, N, C, h_pre + (int64_t)l * T * N, Fl, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+  }
+  return HC_OK;
+}
+
+static int64_t flash_maps_ws(int64_t T, int64_t C, int k, int L, int dtype) {
+  const hc::XhcFastWs f = hc::xhc_route_fast_ws(T, C, k, L, dtype);
+  return align256(T * (k * L + k * k) * 4) + align256(T * 4) + align256(f.packed) + align256(f.partial);
+}
+
+int64_t xhc_flash_maps_workspace_bytes(int64_t T, int N, int64_t C, int k, int L, int dtype) {
+  if (T < 0 || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE || C < 1 || L < 1 ||
+      L > HC_MAX_FLASH_SUBLAYERS || !dtype_ok(dtype))
+    return -1;
+  return flash_maps_ws(T, C, k, L, dtype);
+}
+
+int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
+                   const float* phi_act, const float* b_act, float alpha_post, float alpha_res, int sinkhorn_iters,
+                   float* H_post, float* H_res, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
+      L < 1 || L > HC_MAX_FLASH_SUBLAYERS || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!X || !idx || !phi_act || !b_act || !H_post || !H_res) return HC_ERR_NULL;
+  if (!aligned_to(X, esize(dtype)) || !aligned_to(idx, 4) || !aligned_to(phi_act, 4) || !aligned_to(b_act, 4) ||
+      !aligned_to(H_post, 4) || !aligned_to(H_res, 4))
+    return HC_ERR_ALIGN;
+  const int64_t wsb = flash_maps_ws(T, C, k, L, dtype);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int acols = k * L + k * k;
+  const void* outs[2] = {H_post, H_res};
+  const int64_t ob[2] = {T * k * L * 4, T * k * k * 4};
+  const void* ins[5] = {X, idx, phi_act, b_act, workspace};
+  const int64_t ib[5] = {T * N * C * (int64_t)esize(dtype), T * k * 4, (int64_t)k * C * acols * 4, acols * 4, wsb};
+  if (any_overlap(outs, ob, 2, ins, ib, 5)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* p = (char*)workspace;
+  float* P = (float*)p;
+  p += align256(T * acols * 4);
+  float* ss = (float*)p;
+  p += align256(T * 4);
+  const hc::XhcFastWs f = hc::xhc_route_fast_ws(T, C, k, L, dtype);
+  void* packed = p;
+  float* partial = (float*)(p + align256(f.packed));
+  hipError_t e;
+  if (aligned_to(X, 16) && f.packed > 0) {
+    e = hc::launch_fast_xhc_active(X, T, N, C, idx, L, phi_act, b_act, alpha_post, alpha_res, sinkhorn_iters,
+                                   H_post, H_res, packed, partial, st);
+  } else {
+    e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, k, idx, N, phi_act, acols, nullptr, 0, P, ss, st);
+    if (e != hipSuccess) return HC_ERR_LAUNCH;
+    e = hc::launch_coeff_epilogue(P, ss, (float)((double)k * (double)C), T, 0, k * L, k, 0.f, alpha_post,
+                                  alpha_res, b_act, sinkhorn_iters, nullptr, H_post, H_res, st);
+  }
+  return launch_status(e);
+}
+
+int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int l, const void* F_pre_l,
+                    const float* h_pre_l, const int32_t* idx, const float* H_post, const void* F_outs, void* F_in,
+                    void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
+      L < 1 || L > HC_MAX_FLASH_SUBLAYERS || l < 0 || l >= L)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!F_pre_l || !h_pre_l || !idx || !H_post || !F_in || (l > 0 && !F_outs)) return HC_ERR_NULL;
+  const size_t es = esize(dtype);
+  if (!aligned_to(F_pre_l, es) || !aligned_to(F_in, es) || (F_outs && !aligned_to(F_outs, es)) ||
+      !aligned_to(h_pre_l, 4) || !aligned_to(idx, 4) || !aligned_to(H_post, 4))
+    return HC_ERR_ALIGN;
+  const int64_t fb = T * C * (int64_t)es;
+  // F_in may be F_pre_l itself (each element is read before it is written); no other overlap
+  const void* outs[1] = {F_in};
+  const int64_t ob[1] = {fb};
+  const void* ins[5] = {F_in == F_pre_l ? nullptr : F_pre_l, h_pre_l, idx, H_post, l > 0 ? F_outs : nullptr};
+  const int64_t ib[5] = {fb, T * N * 4, T * k * 4, T * k * L * 4, T * L * C * (int64_t)es};
+  if (any_overlap(outs, ob, 1, ins, ib, 5)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  return launch_status(hc::launch_flash_input(dtype, vec_ok(C, {F_pre_l, F_outs, F_in}), T, N, C, k, L, l, F_pre_l,
+                                              h_pre_l, idx, H_post, F_outs, F_in, (hipStream_t)stream));
+}
+
+int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L) {
+  if (T < 0 || k < 1 || k > HC_MAX_ACTIVE || L < 1 || L > HC_MAX_FLASH_SUBLAYERS) return -1;
+  return align256(T * k * L * 4);
+}
+
+int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
+                   const float* H_post, const float* H_res, const void* F_outs, void* workspace,
+                   int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
+      L < 1 || L > HC_MAX_FLASH_SUBLAYERS)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!X || !idx || !H_post || !H_res || !F_outs) return HC_ERR_NULL;
+  const size_t es = esize(dtype);
+  if (!aligned_to(X, es) || !aligned_to(F_outs, es) || !aligned_to(idx, 4) || !aligned_to(H_post, 4) ||
+      !aligned_to(H_res, 4))
+    return HC_ERR_ALIGN;
+  const int64_t wsb = align256(T * k * L * 4);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const void* outs[2] = {X, workspace};
+  const int64_t ob[2] = {T * N * C * (int64_t)es, wsb};
+  const void* ins[4] = {idx, H_post, H_res, F_outs};
+  const int64_t ib[4] = {T * k * 4, T * k * L * 4, T * k * k * 4, T * L * C * (int64_t)es};
+  if (any_overlap(outs, ob, 2, ins, ib, 4)) return HC_ERR_ALIAS;
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  float* E = (float*)workspace;
+  hipError_t e = hc::launch_flash_post_maps(T, k, L, H_post, H_res, E, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  if (hc::fast_mix_supported(dtype, k, L, C, X, F_outs))
+    return launch_status(hc::launch_fast_mix(X, T, N, C, idx, H_res, E, F_outs, L, st));
+  return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, F_outs}), X, T, N, C, k, idx, H_res, E, F_outs, L,
+                                              st));
+}
+
 static int augment_spec(int64_t B, int64_t S, int64_t C, const int* kappa, int r, hc::ConvSpec& spec,
                         int64_t& wtot) {
   if (B < 0 || S < 0 || C < 1 || C > (1ll << 26) || r < 0 || r > HC_MAX_COMPONENTS - 1) return HC_ERR_SHAPE;

@@ -57,4 +57,19 @@ hipError_t launch_static_maps(const float* logits, int n, int iters, float* h_pr
 hipError_t launch_static_apply(int dtype, bool post, bool vec, const void* X, int64_t T, int n, int64_t C,
                                const float* h1, const float* h2, const void* F, void* Y, hipStream_t st);
 
+// ---- xHC-Flash (hc_flash.hip)
+// The L dense reads of the block-entry state from one pass: h_pre [L, T, N], F [L, T, C]
+// (bfloat16, N % 4 == 0, N <= 16, L <= 4, C % 8 == 0, 16-byte aligned X and F).
+bool fast_pre_multi_supported(int dtype, int N, int64_t C, int L, const void* X, const void* F);
+hipError_t launch_fast_pre_multi(const void* X, int64_t T, int N, int64_t C, int L, const float* h_pre, void* F,
+                                 hipStream_t st);
+// F_in = F_pre_l + sum_{j<l} c_j F_outs[:, j] (h_pre_l [T, N], H_post [T, k, L], F_outs [T, L, C]);
+// vec: C % 8 == 0 with the three stream arrays 16-byte aligned.
+hipError_t launch_flash_input(int dtype, bool vec, int64_t T, int N, int64_t C, int k, int L, int l,
+                              const void* F_pre, const float* h_pre, const int32_t* idx, const float* H_post,
+                              const void* F_outs, void* F_in, hipStream_t st);
+// E [T, k, L]: the block end's write maps (H_res H_post[:, j] for j < L - 1, H_post[:, L - 1]).
+hipError_t launch_flash_post_maps(int64_t T, int k, int L, const float* H_post, const float* H_res, float* E,
+                                  hipStream_t st);
+
 }  // namespace hc

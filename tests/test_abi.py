@@ -350,3 +350,62 @@ def test_augment_backward_validation(hc):
     assert aug(ws=None) == -8 and aug(wsb=wsb - 1) == -8
     assert aug(dF=ctypes.c_void_p(0x1000000)) == -5  # dF_out over F_out
     assert aug(dw=ctypes.c_void_p(0x3000100)) == -5  # dconv inside dV
+
+
+def test_flash_validation(hc):
+    L = hc.lib()
+    T, N, C, k, m, Ls = 8, 16, 64, 4, 2, 2
+    assert L.xhc_flash_pre_workspace_bytes(T, N, C, m, Ls, 1) > 0
+    assert L.xhc_flash_pre_workspace_bytes(T, N, C, m, 5, 1) == -1
+    assert L.xhc_flash_pre_workspace_bytes(T, N, C, N, Ls, 1) == -1  # m = N leaves nothing to route
+    assert L.xhc_flash_maps_workspace_bytes(T, N, C, k, 0, 1) == -1
+    assert L.xhc_flash_post_workspace_bytes(T, k, Ls) >= T * k * Ls * 4
+    assert L.xhc_flash_post_workspace_bytes(T, k, 5) == -1
+    P = lambda j: ctypes.c_void_p(0x1000000 * (j + 1))
+    wsp = L.xhc_flash_pre_workspace_bytes(T, N, C, m, Ls, 1)
+
+    def pre(dt=1, T=T, k=k, m=m, Lb=Ls, wsb=wsp, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["X", "phi", "b", "w", "idx", "sc", "h", "F", "ws"])}
+        return L.xhc_flash_pre(p["X"], dt, T, N, C, k, m, Lb, p["phi"], p["b"], ctypes.c_float(0.01), p["w"],
+                               p["idx"], p["sc"], p["h"], p["F"], p["ws"], wsb, None)
+    assert pre(dt=5) == -3
+    assert pre(Lb=0) == -2 and pre(Lb=5) == -2 and pre(k=1) == -2 and pre(m=N) == -2
+    assert pre(T=0, X=None) == 0
+    for nm in ("X", "phi", "b", "w", "idx", "h", "F"):
+        assert pre(**{nm: None}) == -1, nm
+    assert pre(F=ctypes.c_void_p(0x8000001)) == -4
+    assert pre(ws=None) == -8 and pre(wsb=wsp - 1) == -8
+    assert pre(F=ctypes.c_void_p(0x1000000)) == -5  # F_pre over X
+    assert pre(idx=ctypes.c_void_p(0x7000000)) == -5  # idx over h_pre
+
+    wsm = L.xhc_flash_maps_workspace_bytes(T, N, C, k, Ls, 1)
+
+    def maps(Lb=Ls, iters=20, wsb=wsm, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["X", "idx", "phi", "b", "Hp", "Hr", "ws"])}
+        return L.xhc_flash_maps(p["X"], 1, T, N, C, k, Lb, p["idx"], p["phi"], p["b"], ctypes.c_float(0.01),
+                                ctypes.c_float(0.01), iters, p["Hp"], p["Hr"], p["ws"], wsb, None)
+    assert maps(Lb=5) == -2 and maps(iters=0) == -2
+    for nm in ("X", "idx", "phi", "b", "Hp", "Hr"):
+        assert maps(**{nm: None}) == -1, nm
+    assert maps(wsb=wsm - 1) == -8
+    assert maps(Hr=ctypes.c_void_p(0x5000000)) == -5  # H_res over H_post
+
+    def inp(l=1, Lb=Ls, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["Fp", "h", "idx", "Hp", "Fo", "Fi"])}
+        return L.xhc_flash_input(1, T, N, C, k, Lb, l, p["Fp"], p["h"], p["idx"], p["Hp"], p["Fo"], p["Fi"], None)
+    assert inp(l=2) == -2 and inp(l=-1) == -2 and inp(Lb=0) == -2
+    for nm in ("Fp", "h", "idx", "Hp", "Fo", "Fi"):
+        assert inp(**{nm: None}) == -1, nm
+    assert inp(Fi=ctypes.c_void_p(0x6000001)) == -4
+    assert inp(Fi=ctypes.c_void_p(0x5000000)) == -5  # F_in over F_outs
+
+    wsq = L.xhc_flash_post_workspace_bytes(T, k, Ls)
+
+    def post(Lb=Ls, wsb=wsq, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["X", "idx", "Hp", "Hr", "Fo", "ws"])}
+        return L.xhc_flash_post(p["X"], 1, T, N, C, k, Lb, p["idx"], p["Hp"], p["Hr"], p["Fo"], p["ws"], wsb, None)
+    assert post(Lb=5) == -2
+    for nm in ("X", "idx", "Hp", "Hr", "Fo"):
+        assert post(**{nm: None}) == -1, nm
+    assert post(ws=None) == -8 and post(wsb=wsq - 1) == -8
+    assert post(ws=ctypes.c_void_p(0x1000000)) == -5  # workspace inside X

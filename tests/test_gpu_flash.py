@@ -1,0 +1,143 @@
+"""GPU parity of the xHC-Flash calls (xhc_flash_pre, xhc_flash_maps,
+xhc_flash_input, xhc_flash_post) against the fp64 oracle, through the C ABI.
+
+Each stage is checked against the oracle on the GPU's own inputs to that stage
+(the GPU's idx, h_pre, F_pre, H_post, H_res), so every bfloat16 output is
+rounded once and the stream bound holds: relative L2 1e-2 and per element
+max(2e-2, one bf16 ulp). Float32 outputs (h_pre, H_post, H_res, scores) carry
+float32 sums over N*C or k*C products and 20 Sinkhorn steps: relative L2 1e-5
+(the default float32 bound of these tests). The active set is compared bit-exactly on
+inputs whose top router scores are at least 1e-3 apart.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from hc_testutil import check_bf16, check_fp32, check_stream, dev, have_gpu, host64, note
+
+pytestmark = pytest.mark.gpu
+
+if have_gpu():
+    import torch
+    import stream_residual_mixing_amd as hc
+
+GAP = 1e-3
+
+
+def _gaps(X, w_r, k, m, seed):
+    """Redraw (seeded) the tokens whose top-(k-m+1) candidate scores are within GAP."""
+    rng = synth.make_rng(seed, 0, stream=7)
+    todo = np.arange(X.shape[0])
+    for _ in range(50):
+        s = np.concatenate([O.xhc_router_scores(X.values[todo[i:i + 256]], w_r) for i in range(0, todo.size, 256)])
+        top = -np.sort(-s, axis=1)[:, : k - m + 1]
+        bad = todo[np.any(top[:, :-1] - top[:, 1:] <= GAP, axis=1)]
+        if bad.size == 0:
+            return
+        synth.redraw_rows(rng, X, bad)
+        todo = bad
+    raise AssertionError("could not enforce score gaps")
+
+
+def _inputs(seed, T, N, C, k, m, L, dtype, alpha=0.01, phi_std=synth.PHI_STD):
+    """Block-entry state, L pre maps, the router, the active maps' weights (identity
+    res logits, as the xHC recipe) and L sublayer outputs, all seeded."""
+    rng = synth.make_rng(seed, 0)
+    X = synth.Tensor(synth.normal(rng, (T, N, C)), dtype)
+    inp = dict(X=X, phi_pre=synth.normal(rng, (L, N * C, N), phi_std),
+               b_pre=synth.normal(rng, (L, N), 0.1),
+               w_router=synth.normal(rng, (N * C, N - m), float(np.sqrt(1.0 / (N * C)))),
+               phi_act=synth.normal(rng, (k * C, k * L + k * k), phi_std))
+    b_act = np.zeros(k * L + k * k, np.float32)
+    b_act[k * L:] = np.eye(k, dtype=np.float32).reshape(-1)
+    inp["b_act"] = b_act
+    inp["F_outs"] = synth.Tensor(synth.normal(rng, (T, L, C)), dtype)
+    inp["alpha"] = alpha
+    _gaps(X, inp["w_router"], k, m, seed)
+    return inp
+
+
+def _run_and_check(inp, k, m, L, sample=None):
+    X = dev(inp["X"])
+    T, N, C = X.shape
+    sl = (lambda a: a) if sample is None else (lambda a: a[sample])
+    a = inp["alpha"]
+    idx, score, h_pre, F_pre = hc.xhc_flash_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), a, dev(inp["w_router"]),
+                                                k=k, m=m)
+    Hp, Hr = hc.xhc_flash_maps(X, idx, dev(inp["phi_act"]), dev(inp["b_act"]), a, a, L)
+    F_outs = dev(inp["F_outs"])
+    F_in = [hc.xhc_flash_input(l, F_pre[l], h_pre[l], idx, Hp, F_outs) for l in range(L)]
+    Xp = X.clone()
+    hc.xhc_flash_post(Xp, idx, Hp, Hr, F_outs)
+    torch.cuda.synchronize()
+    dt = inp["X"].dtype
+    Xv = sl(inp["X"].values)
+    pre = O.xhc_flash_pre(Xv, list(inp["phi_pre"]), list(inp["b_pre"]), a, inp["w_router"], k, m)
+    gidx = sl(idx.cpu().numpy()).astype(np.int64)
+    np.testing.assert_array_equal(gidx, pre["idx"])
+    check_fp32("score", sl(host64(score)), pre["score"])
+    check_fp32("h_pre", host64(h_pre)[:, sample] if sample is not None else host64(h_pre), pre["h_pre"])
+    gF = host64(F_pre)
+    for l in range(L):
+        check_stream(f"F_pre[{l}]", dt, sl(gF[l]), pre["F_pre"][l])
+    ref_hp, ref_hr = O.xhc_flash_maps(Xv, gidx, inp["phi_act"], inp["b_act"], a, a, L)
+    check_fp32("H_post", sl(host64(Hp)), ref_hp)
+    check_fp32("H_res", sl(host64(Hr)), ref_hr)
+    gh, gHp, gHr = host64(h_pre), sl(host64(Hp)), sl(host64(Hr))
+    Fo = sl(inp["F_outs"].values.astype(np.float64))
+    for l in range(L):  # the correction on the GPU's own F_pre, h_pre and H_post
+        ref = O.xhc_flash_input(l, sl(gF[l]), sl(gh[l]), gidx, gHp, Fo)
+        check_stream(f"F_in[{l}]", dt, sl(host64(F_in[l])), ref)
+    ref_X = O.xhc_flash_post(Xv, gidx, gHp, gHr, Fo)
+    gX = sl(host64(Xp))
+    act = np.zeros(gX.shape[:2], bool)
+    act[np.arange(gX.shape[0])[:, None], gidx] = True
+    assert np.array_equal(gX[~act], Xv[~act]), "rows outside the active set changed"
+    check_stream("X_L active rows", dt, gX[act], ref_X[act])
+    return dict(idx=idx, h_pre=h_pre, F_pre=F_pre, Hp=Hp, Hr=Hr, F_outs=F_outs)
+
+
+@pytest.mark.parametrize("L,N,C,T,k,m,dtype", [
+    (2, 16, 256, 70, 4, 2, synth.BF16),   # attention + MLP, the fast paths, ragged T
+    (4, 16, 128, 33, 4, 2, synth.BF16),   # the four-sublayer block
+    (3, 8, 96, 40, 4, 1, synth.BF16),     # C not a multiple of 128, N = 8
+    (1, 16, 256, 5, 4, 2, synth.BF16),    # one sublayer: plain xHC
+    (2, 6, 40, 29, 3, 1, synth.F32),      # float32 and shapes only the generic kernels take
+    (4, 12, 64, 1, 4, 2, synth.BF16),     # one token
+])
+def test_flash_block(L, N, C, T, k, m, dtype):
+    note(f"xhc_flash L={L} N={N} C={C} T={T} k={k} m={m} {dtype}")
+    _run_and_check(_inputs(800 + 7 * L + N + T, T, N, C, k, m, L, dtype), k, m, L)
+
+
+def test_flash_strong_maps():
+    """Gates and weights large enough that h_pre, H_post and H_res are far from
+    their values at the bias, so the correction scalars vary per token."""
+    note("xhc_flash strong maps L=2 N=16 C=256 T=64")
+    _run_and_check(_inputs(830, 64, 16, 256, 4, 2, 2, synth.BF16, alpha=0.8, phi_std=0.3), 4, 2, 2)
+
+
+def test_flash_input_in_place():
+    """F_in may be written over F_pre_l itself: same values as into a fresh buffer."""
+    note("xhc_flash_input in place L=3 N=16 C=256 T=40")
+    inp = _inputs(840, 40, 16, 256, 4, 2, 3, synth.BF16)
+    r = _run_and_check(inp, 4, 2, 3)
+    fresh = hc.xhc_flash_input(2, r["F_pre"][2], r["h_pre"][2], r["idx"], r["Hp"], r["F_outs"])
+    buf = r["F_pre"][2].clone()
+    hc.xhc_flash_input(2, buf, r["h_pre"][2], r["idx"], r["Hp"], r["F_outs"], out=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(fresh, buf)
+
+
+@pytest.mark.parametrize("L", [2, 4])
+def test_flash_full_size(L):
+    """N = 16, k = 4, m = 2, C = 4096, T = 8192 (the xHC workload's shape) in one
+    block; every call on all tokens, the oracle on 256 sampled tokens (each token's
+    block is independent of the others)."""
+    note(f"xhc_flash full size L={L} N=16 C=4096 T=8192 bf16")
+    T, N, C = 8192, 16, 4096
+    inp = _inputs(850 + L, T, N, C, 4, 2, L, synth.BF16)
+    rng = np.random.default_rng(860 + L)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 254, replace=False)]))
+    _run_and_check(inp, 4, 2, L, sample=sample)
