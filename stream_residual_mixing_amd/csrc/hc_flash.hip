@@ -16,6 +16,7 @@
 //  * flash_post_maps_kernel: the block end as one mix of the entry state's
 //    active rows, X_L,A = H_res X_0,A + sum_j E[:, j] F_out^(j), with E[:, j] =
 //    H_res H_post[:, j] for j < L-1 and H_post[:, L-1] for the last sublayer.
+#include "hc.h"
 #include "hc_device.h"
 #include "hc_launch.h"
 
@@ -73,47 +74,61 @@ __global__ __launch_bounds__(256) void pre_multi_kernel(const uint16_t* __restri
 }
 
 // F_in[t, c] = F_pre_l[t, c] + sum_{j<l} c_j[t] F_outs[t, j, c], c_j[t] = sum_a
-// h_pre_l[t, idx[t, a]] H_post[t, a, j] (H_post [T, k, L]); V consecutive
-// channels per thread (V = 8 needs C % 8 == 0 and 16-byte aligned rows). Each
-// thread forms its token's c_j itself (k * l products). Indices are clamped
-// into [0, N).
+// h_pre_l[t, idx[t, a]] H_post[t, a, j] (H_post [T, k, L]). Workgroup (x, t)
+// takes token t's channels [x * 256 V, (x + 1) * 256 V), V per thread (V = 8
+// needs C % 8 == 0 and 16-byte aligned rows): the first l lanes form the
+// token's c_j into LDS while every thread's row loads are in flight. Indices
+// are clamped into [0, N). Workgroup (t, x): blockIdx.x = t, blockIdx.y = x.
+constexpr int FI_THR = 256;
+constexpr int FI_MAXL = 3;  // l < L <= HC_MAX_FLASH_SUBLAYERS
+static_assert(HC_MAX_FLASH_SUBLAYERS - 1 <= FI_MAXL, "earlier outputs a corrected input can take");
 template <typename TE, int V>
-__global__ __launch_bounds__(256) void flash_input_kernel(int64_t T, int N, int64_t C, int k, int L, int l,
-                                                          const TE* F_pre, const float* __restrict__ h_pre,
-                                                          const int32_t* __restrict__ idx,
-                                                          const float* __restrict__ H_post,
-                                                          const TE* __restrict__ F_outs, TE* F_in) {  // F_in may be F_pre
-  const int64_t nv = C / V;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= T * nv) return;
-  const int64_t t = g / nv;
-  const int64_t c0 = (g - t * nv) * V;
-  float acc[V];
+__global__ __launch_bounds__(FI_THR) void flash_input_kernel(int64_t T, int N, int64_t C, int k, int L, int l,
+                                                             const TE* F_pre, const float* __restrict__ h_pre,
+                                                             const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ H_post,
+                                                             const TE* __restrict__ F_outs, TE* F_in) {  // F_in may be F_pre
+  __shared__ float cs[FI_MAXL];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const int64_t c0 = ((int64_t)blockIdx.y * FI_THR + tid) * V;
+  const bool ok = c0 < C;
+  const int64_t cc = ok ? c0 : 0;
+  float acc[V], f[FI_MAXL][V];
   if constexpr (V == 8) {
-    load8(F_pre + t * C + c0, acc);
+    load8(F_pre + t * C + cc, acc);
+#pragma unroll
+    for (int j = 0; j < FI_MAXL; ++j)
+      if (j < l) load8(F_outs + (t * L + j) * C + cc, f[j]);
   } else {
-    acc[0] = Elem<TE>::ld(F_pre + t * C + c0);
+    acc[0] = Elem<TE>::ld(F_pre + t * C + cc);
+#pragma unroll
+    for (int j = 0; j < FI_MAXL; ++j)
+      if (j < l) f[j][0] = Elem<TE>::ld(F_outs + (t * L + j) * C + cc);
   }
-  for (int j = 0; j < l; ++j) {
+  if (tid < l) {
     float cj = 0.f;
     for (int a = 0; a < k; ++a) {
       int s = idx[t * k + a];
       s = s < 0 ? 0 : (s >= N ? N - 1 : s);
-      cj += h_pre[t * N + s] * H_post[(t * k + a) * L + j];
+      cj += h_pre[t * N + s] * H_post[(t * k + a) * L + tid];
     }
-    const TE* fo = F_outs + (t * L + j) * C + c0;
-    if constexpr (V == 8) {
-      float f[8];
-      load8(fo, f);
+    cs[tid] = cj;
+  }
+  __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += cj * f[e];
-    } else {
-      acc[0] += cj * Elem<TE>::ld(fo);
+  for (int j = 0; j < FI_MAXL; ++j) {
+    if (j < l) {
+      const float cj = cs[j];
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += cj * f[j][e];
     }
   }
-  TE* out = F_in + t * C + c0;
+  if (ok) {
+    TE* out = F_in + t * C + c0;
 #pragma unroll
-  for (int e = 0; e < V; ++e) Elem<TE>::st(out + e, acc[e]);
+    for (int e = 0; e < V; ++e) Elem<TE>::st(out + e, acc[e]);
+  }
 }
 
 // E[t, a, j] = sum_b H_res[t, a, b] H_post[t, b, j] for j < L - 1 and
@@ -170,8 +185,7 @@ hipError_t launch_flash_input(int dtype, bool vec, int64_t T, int N, int64_t C, 
                               const void* F_pre, const float* h_pre, const int32_t* idx, const float* H_post,
                               const void* F_outs, void* F_in, hipStream_t st) {
   const int V = vec ? 8 : 1;
-  const int64_t work = T * (C / V);
-  const dim3 grid((unsigned)((work + 255) / 256)), blk(256);
+  const dim3 grid((unsigned)T, (unsigned)((C / V + FI_THR - 1) / FI_THR)), blk(FI_THR);
 #define HC_FI(TE, VV)                                                                                        \
   hipLaunchKernelGGL((flash_input_kernel<TE, VV>), grid, blk, 0, st, T, N, C, k, L, l, (const TE*)F_pre, h_pre, \
                      idx, H_post, (const TE*)F_outs, (TE*)F_in)
