@@ -1087,18 +1087,19 @@ int ncu_of_device() {
 
 int64_t al256(int64_t b) { return (b + 255) / 256 * 256; }
 
-// token groups of the dphi pass: about two workgroups per CU, at most the tile count
-int dphi_groups(int64_t T, int64_t C) {
-  const int64_t nchunk = (C + FCH - 1) / FCH, ntile = (T + FT - 1) / FT;
+// token groups of the dphi pass: about two workgroups per CU over the chunks and
+// the nz stream groups (grid z), at most the tile count
+int dphi_groups(int64_t T, int64_t C, int nz) {
+  const int64_t nchunk = (C + FCH - 1) / FCH * nz, ntile = (T + FT - 1) / FT;
   int64_t g = (2 * (int64_t)ncu_of_device() + nchunk - 1) / nchunk;
   g = g < 1 ? 1 : g;
   return (int)(g < ntile ? g : ntile);
 }
 
-// token-tile groups of the dX pass: about one workgroup per CU over the chunks,
-// at most the tile count
-int dx_groups(int64_t T, int64_t C) {
-  const int64_t nchunk = (C + XCH - 1) / XCH, ntile = (T + XT - 1) / XT;
+// token-tile groups of the dX pass: about one workgroup per CU over the chunks and
+// the nz stream groups (grid z), at most the tile count
+int dx_groups(int64_t T, int64_t C, int nz) {
+  const int64_t nchunk = (C + XCH - 1) / XCH * nz, ntile = (T + XT - 1) / XT;
   int64_t g = (int64_t)ncu_of_device() / nchunk;
   g = g < 1 ? 1 : g;
   return (int)(g < ntile ? g : ntile);
@@ -1134,7 +1135,7 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pby
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
   w.red = (float*)take((T + 15) / 16 * RED * 4);
-  w.G = dphi_groups(T, C);
+  w.G = dphi_groups(T, C, hp > 4 ? hp / 4 : 1);  // the pre mode's N / 4 stream groups
   w.dphi_part = (float*)take((int64_t)w.G * nrows * ncol * 4);
   if (total) *total = off;
   return w;
@@ -1200,7 +1201,7 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
   if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                   w.h_pre, w.h_res, st)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(bwd_dx_kernel<BM_MHC>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)),
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_MHC>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, 1)),
                      dim3(512), 0, st, x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, 4,
                      (const int32_t*)nullptr, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1254,7 +1255,7 @@ hipError_t launch_fast_xroute_backward(const void* X, int64_t T, int N, int64_t 
   hipLaunchKernelGGL(bwd_dphi_kernel<BM_ROUTE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0,
                      st, x, w.dP, T, C, N, idx, ncol, (int64_t)BS * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dx_kernel<BM_ROUTE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C)),
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_ROUTE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, 1)),
                      dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)nullptr, T, C, N, idx,
                      (const float*)nullptr, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1277,7 +1278,7 @@ hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C,
   hipLaunchKernelGGL(bwd_dphi_kernel<BM_PRE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G, ng), dim3(512), 0,
                      st, x, w.dP, T, C, N, (const int32_t*)nullptr, N, (int64_t)N * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dx_kernel<BM_PRE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C), ng),
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_PRE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, (int)ng), ng),
                      dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)dF_in, T, C, N,
                      (const int32_t*)nullptr, w.h_pre, (const float*)nullptr, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
   if ((e = hipGetLastError()) != hipSuccess) return e;

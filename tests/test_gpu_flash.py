@@ -105,6 +105,7 @@ def _run_and_check(inp, k, m, L, sample=None):
     (1, 16, 256, 5, 4, 2, synth.BF16),    # one sublayer: plain xHC
     (2, 6, 40, 29, 3, 1, synth.F32),      # float32 and shapes only the generic kernels take
     (4, 12, 64, 1, 4, 2, synth.BF16),     # one token
+    (2, 16, 40, 20, 4, 2, synth.BF16),    # C % 32 != 0: generic projections beside the 16-byte kernels
 ])
 def test_flash_block(L, N, C, T, k, m, dtype):
     note(f"xhc_flash L={L} N={N} C={C} T={T} k={k} m={m} {dtype}")
