@@ -97,6 +97,29 @@ def _logits_no_bias(X, phi, bias, alpha):
     return _keep("mhc_logits")(X, phi, np.zeros_like(np.asarray(bias, np.float64)), alpha)
 
 
+def _gates_backward_no_rms(dz, P, rho, gate, x, phi, N):
+    dP = dz * gate[None, :] * rho[:, None]
+    dx = dP @ phi.T  # the gradient through the RMS factor forgotten
+    return dx, x.T @ dP, dz.sum(axis=0), (dz * P * rho[:, None]).sum(axis=0)
+
+
+def _conv_backward_causal(F_out, w, batch, seq, dg):
+    dF, dw = _keep("causal_dwconv_backward")(F_out, w, batch, seq, dg)
+    return _keep("causal_dwconv")(dg, w, batch, seq), dw  # the forward direction instead of the transpose
+
+
+def _mgs_backward_sign(comps, dV):
+    return -_keep("modified_gram_schmidt_backward")(comps, dV)
+
+
+def _route_backward_drops_passthrough(X, idx, phi_act, b_act, alpha_post, alpha_res, Wb, dX_next, sinkhorn_iters=20):
+    r = dict(_keep("xhc_route_backward")(X, idx, phi_act, b_act, alpha_post, alpha_res, Wb, dX_next, sinkhorn_iters))
+    keep = np.zeros(r["dX"].shape[:2], bool)
+    keep[np.arange(keep.shape[0])[:, None], np.asarray(idx)] = True
+    r["dX"] = np.where(keep[:, :, None], r["dX"], 0.0)  # inactive rows get no gradient
+    return r
+
+
 MUTANTS = {
     "sinkhorn_rows_first": ("sinkhorn_knopp", _sinkhorn_rows_first),
     "post_gate_sigma": ("hc_coeffs", _coeffs_post_sigma),
@@ -110,6 +133,10 @@ MUTANTS = {
     "sinkhorn_backward_sign": ("sinkhorn_knopp_backward", _sinkhorn_bwd_sign),
     "route_drops_inactive": ("xhc_route", _route_zero_inactive),
     "logits_without_bias": ("mhc_logits", _logits_no_bias),
+    "gates_backward_without_rms_term": ("_gates_backward", _gates_backward_no_rms),
+    "conv_backward_forward_direction": ("causal_dwconv_backward", _conv_backward_causal),
+    "gram_schmidt_backward_sign": ("modified_gram_schmidt_backward", _mgs_backward_sign),
+    "route_backward_drops_passthrough": ("xhc_route_backward", _route_backward_drops_passthrough),
 }
 
 
@@ -117,4 +144,5 @@ def apply(name):
     fn, repl = MUTANTS[name]
     _keep(fn)
     setattr(H, fn, repl)
-    setattr(oracle, fn, repl)
+    if hasattr(oracle, fn):  # names with a leading underscore stay in the module
+        setattr(oracle, fn, repl)
