@@ -29,7 +29,6 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int NS4 = 4;              // streams
 constexpr int NCOL = 24;            // n*n + 2n
-constexpr int NCP = 48;             // packed hi|lo columns
 constexpr int TOK = 16;             // tokens per tile (MFMA M)
 
 // ------------------------------------------------------------- phi packing
