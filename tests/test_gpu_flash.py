@@ -142,3 +142,30 @@ def test_flash_full_size(L):
     rng = np.random.default_rng(860 + L)
     sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 254, replace=False)]))
     _run_and_check(inp, 4, 2, L, sample=sample)
+
+
+def test_flash_single_sublayer_matches_xhc_calls():
+    """A block of one sublayer is one plain xHC sublayer: xhc_flash_pre +
+    xhc_flash_maps + xhc_flash_post give the same active set, h_pre, dense read,
+    maps and state, bit for bit, as xhc_pre + xhc_route on the same inputs."""
+    note("xhc_flash L=1 against xhc_pre + xhc_route N=16 C=256 T=50")
+    k, m = 4, 2
+    inp = _inputs(870, 50, 16, 256, k, m, 1, synth.BF16, alpha=0.5, phi_std=0.2)
+    X = dev(inp["X"])
+    a = inp["alpha"]
+    idx, score, h_pre, F_pre = hc.xhc_flash_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), a, dev(inp["w_router"]),
+                                                k=k, m=m)
+    Hp, Hr = hc.xhc_flash_maps(X, idx, dev(inp["phi_act"]), dev(inp["b_act"]), a, a, 1)
+    F_outs = dev(inp["F_outs"])
+    Xf = X.clone()
+    hc.xhc_flash_post(Xf, idx, Hp, Hr, F_outs)
+    pre = hc.xhc_pre(X, dev(inp["phi_pre"][0]), dev(inp["b_pre"][0]), a, w_router=dev(inp["w_router"]), k=k, m=m)
+    Xr = X.clone()
+    out = hc.xhc_route(Xr, F_outs[:, 0].contiguous(), dev(inp["phi_act"]), dev(inp["b_act"]), a, a, k=k, m=m,
+                       idx=pre["idx"], want_coeffs=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, pre["idx"])
+    assert torch.equal(h_pre[0], pre["h_pre"])
+    assert torch.equal(F_pre[0], pre["F_in"])
+    assert torch.equal(Hp, out["h_post"]) and torch.equal(Hr, out["h_res"])
+    assert torch.equal(Xf, Xr)
