@@ -573,12 +573,14 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
 // Both walks keep F_out's rows as loaded and mask, per token, the window
 // positions before the token's sequence start, so a sequence boundary inside a
 // strip needs no reload.
-constexpr int AB_STRIP = 128;  // tokens per strip
+constexpr int AB_STRIP = 128;  // tokens per strip (AB_STRIP2 when that still gives enough workgroups)
+constexpr int AB_STRIP2 = 256;
 constexpr int AB_GRP = 16;     // tokens per cross-wave sum of the Gram pass
 constexpr int AB_PF = 4;       // tokens per load group (the next group is in flight)
 constexpr int AB_NV = 26;      // sums per token: G (10, upper triangle) | M (16, M[j][i] = <dV_j, u_i>)
 constexpr int AB_K1 = 4, AB_K2 = 8, AB_K3 = 12, AB_TAPS = AB_K1 + AB_K2 + AB_K3;
-static_assert(AB_STRIP % AB_GRP == 0 && AB_GRP % AB_PF == 0, "strip, group and load group nest");
+static_assert(AB_STRIP % AB_GRP == 0 && AB_STRIP2 % AB_GRP == 0 && AB_GRP % AB_PF == 0,
+              "strip, group and load group nest");
 
 // Workgroup barrier ordering LDS only: global loads in flight stay in flight
 // (a full __syncthreads also waits for them).
@@ -682,7 +684,7 @@ __device__ __forceinline__ float ab_reduce_scatter(const float (&v)[AB_NV], int 
   return e + dpp_xor1(e);
 }
 
-template <typename TF>
+template <typename TF, int ST>  // ST: tokens per strip
 __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict__ F, int64_t T, int64_t S, int64_t C,
                                                            const float* __restrict__ conv_w,
                                                            const float* __restrict__ dV, float* __restrict__ part) {
@@ -691,8 +693,8 @@ __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict_
   const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
   const bool cok = c0 < C;  // lanes past C load zeros, so their products vanish
   const int64_t c = cok ? c0 : C - 1;
-  const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
-  const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;
+  const int64_t t0 = (int64_t)blockIdx.y * ST;
+  const int64_t t1 = t0 + ST < T ? t0 + ST : T;
   float w[AB_TAPS];
   ab_taps(conv_w, C, c, w);
   float win[12];  // before the first token: F_out[t0-12..t0-1] as loaded (rows < 0 masked at use)
@@ -919,19 +921,19 @@ __global__ __launch_bounds__(256) void aug_bwd_coef_kernel(const float* __restri
   }
 }
 
-template <typename TF>
+template <typename TF, int ST>  // ST: tokens per strip
 __global__ __launch_bounds__(256) void aug_bwd_walk_kernel(const TF* __restrict__ F, int64_t T, int64_t S, int64_t C,
                                                            const float* __restrict__ conv_w,
                                                            const float* __restrict__ dV,
                                                            const float* __restrict__ coef, TF* __restrict__ dF,
                                                            float* __restrict__ wpart) {
-  __shared__ __attribute__((aligned(16))) float cfs[(AB_STRIP + 11) * 32];
+  __shared__ __attribute__((aligned(16))) float cfs[(ST + 11) * 32];
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
   const bool cok = c0 < C;
   const int64_t c = cok ? c0 : C - 1;
-  const int64_t t0 = (int64_t)blockIdx.y * AB_STRIP;
-  const int64_t t1 = t0 + AB_STRIP < T ? t0 + AB_STRIP : T;  // strip [t0, t1)
+  const int64_t t0 = (int64_t)blockIdx.y * ST;
+  const int64_t t1 = t0 + ST < T ? t0 + ST : T;  // strip [t0, t1)
   // the walk starts up to 11 tokens after the strip, inside t1 - 1's sequence
   const int64_t se = (t1 - 1) - (t1 - 1) % S + S;  // end of that sequence
   const int64_t top = (t1 + 11 < se ? t1 + 11 : se) - 1;
@@ -1294,7 +1296,16 @@ bool fast_augment_backward_supported(int dtype, int64_t B, int64_t S, int64_t C,
          kappa[1] == AB_K2 && kappa[2] == AB_K3 && B * S * C < (1ll << 40);
 }
 
+// tokens per strip of the reverse walk: the longer strip (fewer halo tokens
+// walked twice) while it leaves at least two workgroups per CU (walk at B = 2,
+// S = 4096, C = 4096: 143 against 161 us)
+int64_t aug_strip(int64_t T, int64_t C) {
+  const int64_t nq = (C + 255) / 256;
+  return nq * ((T + AB_STRIP2 - 1) / AB_STRIP2) >= 2 * (int64_t)ncu_of_device() ? AB_STRIP2 : AB_STRIP;
+}
+
 int64_t fast_augment_backward_ws_bytes(int64_t B, int64_t S, int64_t C) {
+  // the tap partials are sized for the shorter strip (the most strips)
   const int64_t T = B * S, nq = (C + 255) / 256, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
   return al256(nq * AB_NV * T * 4) + al256(T * 32 * 4) + al256(nstrip * AB_TAPS * C * 4);
 }
@@ -1302,27 +1313,35 @@ int64_t fast_augment_backward_ws_bytes(int64_t B, int64_t S, int64_t C) {
 hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int64_t C,
                                         const float* conv_w, const float* dV, void* dF_out, float* dconv_w, void* ws,
                                         hipStream_t st) {
-  const int64_t T = B * S, nq = (C + 255) / 256, nstrip = (T + AB_STRIP - 1) / AB_STRIP;
+  const int64_t T = B * S, nq = (C + 255) / 256, strip = aug_strip(T, C), nstrip = (T + strip - 1) / strip;
   unsigned char* p = (unsigned char*)ws;
   float* part = (float*)p;
   float* coef = (float*)(p + al256(nq * AB_NV * T * 4));
   float* wpart = (float*)(p + al256(nq * AB_NV * T * 4) + al256(T * 32 * 4));
   const dim3 grid((unsigned)nq, (unsigned)nstrip), blk(256);
+  // the Gram pass walks no halo: it keeps the shorter strips (more workgroups)
+  const dim3 ggrid((unsigned)nq, (unsigned)((T + AB_STRIP - 1) / AB_STRIP));
   if (dtype == 1)
-    hipLaunchKernelGGL(aug_bwd_gram_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)F_out, T, S, C, conv_w, dV,
-                       part);
+    hipLaunchKernelGGL((aug_bwd_gram_kernel<uint16_t, AB_STRIP>), ggrid, blk, 0, st, (const uint16_t*)F_out, T, S, C,
+                       conv_w, dV, part);
   else
-    hipLaunchKernelGGL(aug_bwd_gram_kernel<float>, grid, blk, 0, st, (const float*)F_out, T, S, C, conv_w, dV, part);
+    hipLaunchKernelGGL((aug_bwd_gram_kernel<float, AB_STRIP>), ggrid, blk, 0, st, (const float*)F_out, T, S, C,
+                       conv_w, dV, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(aug_bwd_coef_kernel, dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st, part, T, (int)nq, coef);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (dtype == 1)
-    hipLaunchKernelGGL(aug_bwd_walk_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)F_out, T, S, C, conv_w, dV,
-                       coef, (uint16_t*)dF_out, wpart);
-  else
-    hipLaunchKernelGGL(aug_bwd_walk_kernel<float>, grid, blk, 0, st, (const float*)F_out, T, S, C, conv_w, dV, coef,
-                       (float*)dF_out, wpart);
+#define HC_AUG_WALK(TF, ST)                                                                                 \
+  hipLaunchKernelGGL((aug_bwd_walk_kernel<TF, ST>), grid, blk, 0, st, (const TF*)F_out, T, S, C, conv_w, dV, coef, \
+                     (TF*)dF_out, wpart)
+  if (dtype == 1) {
+    if (strip == AB_STRIP2) HC_AUG_WALK(uint16_t, AB_STRIP2);
+    else HC_AUG_WALK(uint16_t, AB_STRIP);
+  } else {
+    if (strip == AB_STRIP2) HC_AUG_WALK(float, AB_STRIP2);
+    else HC_AUG_WALK(float, AB_STRIP);
+  }
+#undef HC_AUG_WALK
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(aug_bwd_wsum_kernel, dim3((unsigned)((C * AB_TAPS + 255) / 256)), dim3(256), 0, st, wpart,
                      (int)nstrip, C, dconv_w);

@@ -253,3 +253,12 @@ def test_augment_backward_full_size():
     B, S, C = 2, 4096, 4096
     note(f"xhc_augment_backward full size B={B} S={S} C={C} bf16")
     _aug_only_check(*_aug_only(640, B, S, C, synth.BF16), B, S)
+
+
+def test_augment_backward_long_strips():
+    """A shape that takes the 256-token strips (at least two workgroups per CU)
+    with sequence starts inside strips (every 3000 tokens) and a ragged last strip
+    (9000 = 35 * 256 + 40)."""
+    B, S, C = 3, 3000, 4096
+    note(f"xhc_augment_backward long strips B={B} S={S} C={C} bf16")
+    _aug_only_check(*_aug_only(650, B, S, C, synth.BF16), B, S)
