@@ -684,66 +684,98 @@ __device__ __forceinline__ float ab_reduce_scatter(const float (&v)[AB_NV], int 
   return e + dpp_xor1(e);
 }
 
-template <typename TF, int ST>  // ST: tokens per strip
+// CPT channels per thread (2: adjacent channel pairs, C even, rows aligned to a
+// pair): the products of a thread's channels are added before the one
+// reduce-scatter per token, so each cross-lane exchange serves 2x the channels.
+template <typename TF, int CPT>
+__device__ __forceinline__ void ab_ld_pair(const TF* row, uint32_t off, float (&v)[CPT]) {
+  if constexpr (CPT == 1) {
+    v[0] = ab_ldo(row, off);
+  } else if constexpr (sizeof(TF) == 2) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(row) + off);
+    v[0] = __uint_as_float(u << 16);
+    v[1] = __uint_as_float(u & 0xffff0000u);
+  } else {
+    const float2 u = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(row) + off);
+    v[0] = u.x;
+    v[1] = u.y;
+  }
+}
+
+template <typename TF, int ST, int CPT>  // ST: tokens per strip; CPT: channels per thread
 __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict__ F, int64_t T, int64_t S, int64_t C,
                                                            const float* __restrict__ conv_w,
                                                            const float* __restrict__ dV, float* __restrict__ part) {
   __shared__ float red[2][AB_GRP][4][AB_NV];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * 256 + tid;
-  const bool cok = c0 < C;  // lanes past C load zeros, so their products vanish
-  const int64_t c = cok ? c0 : C - 1;
+  const int64_t c0 = ((int64_t)blockIdx.x * 256 + tid) * CPT;
+  const bool cok = c0 < C;  // lanes past C load zeros, so their products vanish (C % CPT == 0)
+  const int64_t c = cok ? c0 : C - CPT;
   const int64_t t0 = (int64_t)blockIdx.y * ST;
   const int64_t t1 = t0 + ST < T ? t0 + ST : T;
-  float w[AB_TAPS];
-  ab_taps(conv_w, C, c, w);
-  float win[12];  // before the first token: F_out[t0-12..t0-1] as loaded (rows < 0 masked at use)
+  float w[CPT][AB_TAPS];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) ab_taps(conv_w, C, c + e, w[e]);
+  const uint32_t ofF = (uint32_t)c * (uint32_t)sizeof(TF), ofV = (uint32_t)c * 4u;
+  float win[CPT][12];  // before the first token: F_out[t0-12..t0-1] as loaded (rows < 0 masked at use)
 #pragma unroll
   for (int s = 0; s < 12; ++s) {
     const int64_t tt = t0 - 12 + s;
-    const float x = ab_ld(F + (tt >= 0 ? tt : 0) * C + c);  // loaded unconditionally, then selected
-    win[s] = cok ? x : 0.f;
+    float x[CPT];
+    ab_ld_pair<TF, CPT>(F + (tt >= 0 ? tt : 0) * C, ofF, x);  // loaded unconditionally, then selected
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) win[e][s] = cok ? x[e] : 0.f;
   }
   struct Ld {
-    float f[AB_PF], dv[AB_PF][4];
+    float f[AB_PF][CPT], dv[AB_PF][4][CPT];
   };
-  const uint32_t ofF = (uint32_t)c * (uint32_t)sizeof(TF), ofV = (uint32_t)c * 4u;
   // CLAMP: rows past T read row T - 1 (the strip's last group)
   auto load = [&](int64_t tb, Ld& L, bool clamp) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AB_PF; ++i) {
       const int64_t t = clamp && tb + i >= T ? T - 1 : tb + i;
-      const float x = ab_ldo(F + t * C, ofF);  // loaded unconditionally, then selected
-      L.f[i] = cok ? x : 0.f;
+      float x[CPT];
+      ab_ld_pair<TF, CPT>(F + t * C, ofF, x);  // loaded unconditionally, then selected
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) L.f[i][e] = cok ? x[e] : 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float y = ab_ldo(dV + (t * 4 + j) * C, ofV);
-        L.dv[i][j] = cok ? y : 0.f;
+        float y[CPT];
+        ab_ld_pair<float, CPT>(dV + (t * 4 + j) * C, ofV, y);
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) L.dv[i][j][e] = cok ? y[e] : 0.f;
       }
     }
   };
-  // one token: window advanced by the row `f`, products of the token's components
-  // with dv, their wave sums into red[rb][gi]
-  auto token = [&](float f, const float (&dv)[4], int64_t ts, bool masked, int rb, int gi)
+  // one token: windows advanced by the rows `f`, products of the token's
+  // components with dv summed over the thread's channels, their wave sums into
+  // red[rb][gi]
+  auto token = [&](const float (&f)[CPT], const float (&dv)[4][CPT], int64_t ts, bool masked, int rb, int gi)
                    __attribute__((always_inline)) {
+    float v[AB_NV];
 #pragma unroll
-    for (int s = 0; s < 11; ++s) win[s] = win[s + 1];
-    win[11] = f;
-    float wm[12], u[4], v[AB_NV];
-    if (masked) ab_mask(win, ts, wm);
-    else
+    for (int n = 0; n < AB_NV; ++n) v[n] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 12; ++s) wm[s] = win[s];
-    ab_convs(w, wm, u);
-    int n = 0;
+    for (int e = 0; e < CPT; ++e) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int s = 0; s < 11; ++s) win[e][s] = win[e][s + 1];
+      win[e][11] = f[e];
+      float wm[12], u[4];
+      if (masked) ab_mask(win[e], ts, wm);
+      else
 #pragma unroll
-      for (int k = a; k < 4; ++k) v[n++] = u[a] * u[k];
+        for (int s = 0; s < 12; ++s) wm[s] = win[e][s];
+      ab_convs(w[e], wm, u);
+      int n = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) v[10 + 4 * j + a] = dv[j] * u[a];
+        for (int k = a; k < 4; ++k) v[n++] += u[a] * u[k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) v[10 + 4 * j + a] += dv[j][e] * u[a];
+    }
     const float r = ab_reduce_scatter(v, lane);
     if (!(lane & 1) && (lane >> 1) < AB_NV) red[rb][gi][wave][lane >> 1] = r;
   };
@@ -1319,17 +1351,27 @@ hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B,
   float* coef = (float*)(p + al256(nq * AB_NV * T * 4));
   float* wpart = (float*)(p + al256(nq * AB_NV * T * 4) + al256(T * 32 * 4));
   const dim3 grid((unsigned)nq, (unsigned)nstrip), blk(256);
-  // the Gram pass walks no halo: it keeps the shorter strips (more workgroups)
-  const dim3 ggrid((unsigned)nq, (unsigned)((T + AB_STRIP - 1) / AB_STRIP));
-  if (dtype == 1)
-    hipLaunchKernelGGL((aug_bwd_gram_kernel<uint16_t, AB_STRIP>), ggrid, blk, 0, st, (const uint16_t*)F_out, T, S, C,
-                       conv_w, dV, part);
-  else
-    hipLaunchKernelGGL((aug_bwd_gram_kernel<float, AB_STRIP>), ggrid, blk, 0, st, (const float*)F_out, T, S, C,
-                       conv_w, dV, part);
+  // the Gram pass walks no halo: it keeps the shorter strips (more workgroups);
+  // channel pairs per thread when C is even and the rows are pair-aligned
+  const size_t fes = dtype == 1 ? 2 : 4;
+  const bool pairs = C % 2 == 0 && reinterpret_cast<uintptr_t>(F_out) % (2 * fes) == 0 &&
+                     reinterpret_cast<uintptr_t>(dV) % 8 == 0;
+  const int64_t nqg = pairs ? (C + 511) / 512 : nq;  // channel groups of the Gram pass
+  const dim3 ggrid((unsigned)nqg, (unsigned)((T + AB_STRIP - 1) / AB_STRIP));
+#define HC_AUG_GRAM(TF, CPT)                                                                                       \
+  hipLaunchKernelGGL((aug_bwd_gram_kernel<TF, AB_STRIP, CPT>), ggrid, blk, 0, st, (const TF*)F_out, T, S, C, conv_w, \
+                     dV, part)
+  if (dtype == 1) {
+    if (pairs) HC_AUG_GRAM(uint16_t, 2);
+    else HC_AUG_GRAM(uint16_t, 1);
+  } else {
+    if (pairs) HC_AUG_GRAM(float, 2);
+    else HC_AUG_GRAM(float, 1);
+  }
+#undef HC_AUG_GRAM
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(aug_bwd_coef_kernel, dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st, part, T, (int)nq, coef);
+  hipLaunchKernelGGL(aug_bwd_coef_kernel, dim3((unsigned)((T + 63) / 64)), dim3(256), 0, st, part, T, (int)nqg, coef);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 #define HC_AUG_WALK(TF, ST)                                                                                 \
   hipLaunchKernelGGL((aug_bwd_walk_kernel<TF, ST>), grid, blk, 0, st, (const TF*)F_out, T, S, C, conv_w, dV, coef, \

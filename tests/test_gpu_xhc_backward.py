@@ -262,3 +262,10 @@ def test_augment_backward_long_strips():
     B, S, C = 3, 3000, 4096
     note(f"xhc_augment_backward long strips B={B} S={S} C={C} bf16")
     _aug_only_check(*_aug_only(650, B, S, C, synth.BF16), B, S)
+
+
+def test_augment_backward_odd_channels():
+    """C odd: the Gram pass takes one channel per thread (the pair path needs even C)."""
+    B, S, C = 5, 37, 201
+    note(f"xhc_augment_backward odd C B={B} S={S} C={C} bf16")
+    _aug_only_check(*_aug_only(660, B, S, C, synth.BF16), B, S)
