@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
 //     a strip of tokens; each thread walks the strip with the last 12 rows of
 //     F_out in registers and the next 4 tokens' loads in flight, forms u_1..u_3
 //     and the 26 products, the wave sums them over its 64 channels in one
-//     reduce-scatter, and every 16 tokens the 4 waves' sums are added in LDS
+//     reduce-scatter, and every 32 tokens the 4 waves' sums are added in LDS
 //     and stored as part [channel group][26][T];
 //  2. aug_bwd_coef_kernel: the channel groups' sums added in order per token,
 //     then one thread per token walks the Gram-Schmidt steps, recomputed, in
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(256) void bwd_sums_kernel(const float* __restrict__
 // strip needs no reload.
 constexpr int AB_STRIP = 128;  // tokens per strip (AB_STRIP2 when that still gives enough workgroups)
 constexpr int AB_STRIP2 = 256;
-constexpr int AB_GRP = 16;     // tokens per cross-wave sum of the Gram pass
+constexpr int AB_GRP = 32;     // tokens per cross-wave sum of the Gram pass
 constexpr int AB_PF = 4;       // tokens per load group (the next group is in flight)
 constexpr int AB_NV = 26;      // sums per token: G (10, upper triangle) | M (16, M[j][i] = <dV_j, u_i>)
 constexpr int AB_K1 = 4, AB_K2 = 8, AB_K3 = 12, AB_TAPS = AB_K1 + AB_K2 + AB_K3;
@@ -781,7 +781,7 @@ __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict_
   };
   int64_t tb = t0, ts = t0 % S;  // ts: position of token tb in its sequence
   int rb = 0;                    // LDS buffer of the current 16-token group
-  // after every 16 tokens and at the strip's end the waves' sums are added and stored
+  // after every 32 tokens and at the strip's end the waves' sums are added and stored
   auto flush = [&](int gi0, int64_t nb) __attribute__((always_inline)) {
     if (gi0 + AB_PF == AB_GRP || nb >= t1) {
       lds_barrier();
@@ -789,7 +789,7 @@ __global__ __launch_bounds__(256) void aug_bwd_gram_kernel(const TF* __restrict_
       const int ng = (int)(t1 - g0 < AB_GRP ? t1 - g0 : AB_GRP);  // tokens of the group inside the strip
 #pragma unroll
       for (int e = tid; e < AB_NV * AB_GRP; e += 256) {
-        const int k = e >> 4, q = e & (AB_GRP - 1);
+        const int k = e / AB_GRP, q = e & (AB_GRP - 1);
         if (q < ng) {
           const float* rr = &red[rb][q][0][k];
           part[((int64_t)blockIdx.x * AB_NV + k) * T + g0 + q] = ((rr[0] + rr[AB_NV]) + rr[2 * AB_NV]) + rr[3 * AB_NV];
