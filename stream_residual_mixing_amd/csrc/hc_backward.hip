@@ -17,9 +17,10 @@
 //     recomputes): gates and Sinkhorn backward -> dP, g2, sums over groups of
 //     16 tokens, and the forward's h_pre and h_res;
 //  4. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
-//     dP phi^T product on MFMA;
-//  5. bwd_dphi_kernel: vec(x)^T dP over groups of token tiles on MFMA (the
-//     tokens are the K dimension);
+//     dP phi^T product on MFMA, and (xHC route and pre modes) from the same
+//     tiles of x the dphi partials vec(x)^T dP over groups of token tiles on
+//     MFMA (the tokens are the K dimension);
+//  5. bwd_dphi_kernel (n = 4 mHC): the same dphi partials in a pass of their own;
 //  6. bwd_sums_kernel: the group partials of dphi and the sums of db and dalpha
 //     added in a fixed order.
 #include "hc.h"
@@ -222,9 +223,24 @@ __global__ __launch_bounds__(256) void bwd_pre_sums_kernel(const uint16_t* __res
 
 // ------------------------------------------------------------------- dX
 
+constexpr int FT = 32;          // tokens per tile
+constexpr int FCH = 128;        // channels per chunk
+constexpr int FROW = FCH * 2;   // bytes per (stream, token) row of the state tile
+constexpr int DPT = FT + 8;     // bfloat16 per column of the transposed dP tile (80 bytes)
+
+// Byte offset of (stream i, token m, channel c) in the state tile. The 16-byte
+// block c >> 3 of a row sits at block (c >> 3) ^ (((m >> 3) & 3) << 1): the
+// A-fragment reads (16 consecutive channels of tokens m, m + 8, m + 16, m + 24)
+// then fall in distinct banks.
+__device__ __forceinline__ int xoff(int i, int m, int c) {
+  return (i * FT + m) * FROW + (((c >> 3) ^ (((m >> 3) & 3) << 1)) << 4) + (c & 7) * 2;
+}
+
+
 constexpr int XT = 32;        // tokens per item
 constexpr int XCH = 128;      // channels per item
 constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product tile in LDS
+static_assert(XT == FT && XCH == FCH, "the dphi MFMAs take the dX tile's state rows");
 
 // dX over items of 32 tokens x 128 channels x the 4 slots of the row mode, 512
 // threads. The grid is (chunk, group[, stream group for BM_PRE]): workgroup
@@ -241,7 +257,11 @@ constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product t
 //    (v_mfma_f32_16x16x32_bf16; A = the tokens' dP rows split hi/lo, B = the
 //    channels' phi rows hi/lo; hi*hi + hi*lo + lo*hi into one float32
 //    accumulator) into the LDS product tile; then the next tile's loads are
-//    issued;
+//    issued, and (route and pre modes) the same wave adds the tile's x^T dP to its dphi
+//    accumulators for the same slot and channel blocks and both 16-column
+//    blocks of dP, with the tokens as K (A = x^T, one channel and 8 tokens a
+//    lane, read from the state tile the threads also stage in LDS; B = dP
+//    transposed and split hi/lo, zero past T; D += A B_hi + A B_lo);
 //  * streaming phase, slot j:
 //      BM_MHC:   dX_j = sum_i H_res[i, j] dX_next_i + H_pre[j] dF_in + (dP phi^T)_j + g2 x_j
 //      BM_ROUTE: dX_j = sum_i H_res[i, j] dX_next_i + (dP phi^T)_j + g2 x_j, written over
@@ -249,7 +269,10 @@ constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product t
 //      BM_PRE:   dX_j += H_pre[j] dF_in + (dP phi^T)_j + g2 x_j (dX_next is dX)
 //    rounded once to bfloat16 and stored.
 // Rows past T and channels past C are computed on clamped addresses and not
-// stored. In place is safe: a thread reads its (token, channels) of dX_next one
+// stored. After the last tile (route and pre modes) each workgroup writes its dphi partials,
+//   part[blockIdx.y][R][k] = sum over its tiles of x[t, slot, c] dP[t, k]   (k < ncol)
+// with R the phi row of the slot's channel c, added over the groups later in a
+// fixed order. In place is safe: a thread reads its (token, channels) of dX_next one
 // tile before it writes the same elements, and no other thread touches them.
 constexpr int CFR = 24;  // floats per token of the staged coefficients
 constexpr int DPR = 36;  // floats per token row of the staged dP tile (padded)
@@ -260,10 +283,16 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ idx, const float* __restrict__ h_pre,
                                                      const float* __restrict__ h_res, const float* __restrict__ dP,
                                                      const float* __restrict__ g2, const uint4* __restrict__ phi_rows,
-                                                     uint16_t* dX) {
+                                                     uint16_t* dX, int ncol, int64_t nrows,
+                                                     float* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) float prj[BS * XT * PRJ];
   __shared__ __attribute__((aligned(16))) float cf[XT * CFR];
   __shared__ __attribute__((aligned(16))) float dpt[XT * DPR];
+  // the dphi MFMAs ride along in the route and pre modes; the mHC mode's
+  // H_res product holds too many registers for them, so it keeps its own pass
+  constexpr bool FUSE = BM != BM_MHC;
+  __shared__ __attribute__((aligned(16))) unsigned char xt[FUSE ? BS * FT * FROW : 16];
+  __shared__ __attribute__((aligned(16))) uint16_t dph[FUSE ? 2 * DPS * DPT : 8];  // [hi | lo][column][token]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t chunk = blockIdx.x;
   const int64_t J = gridDim.y, ntile = (T + XT - 1) / XT;
@@ -279,6 +308,12 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   const int ctok = tid < 192 ? tid / 6 : 0, cpc = tid < 192 ? tid - 6 * ctok : 0;
   const int dtok = (tid & 255) >> 3, dpc = tid & 7;
 
+  constexpr int PNB = BM == BM_PRE ? 1 : 2;  // dP column blocks of 16 (the pre mode has N <= 16 columns)
+  f4_t pacc[4][PNB];                        // dphi: [channel block][dP column block]
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < PNB; ++nb) pacc[cb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
   uint4 bh[4], bl[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
@@ -322,7 +357,23 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   // one tile: returns false after the last
   auto step = [&](int64_t& tl, In& cur, In& nxt) __attribute__((always_inline)) {
     if (tid < 192) *reinterpret_cast<float4*>(cf + ctok * CFR + cpc * 4) = cur.cv;
+    if constexpr (FUSE) {
+#pragma unroll
+      for (int i = 0; i < BS; ++i) *reinterpret_cast<uint4*>(xt + xoff(i, m, c8)) = cur.xq[i];
+    }
     if (tid < 256) *reinterpret_cast<float4*>(dpt + dtok * DPR + dpc * 4) = cur.dv;
+    if (FUSE && tid < 256) {
+      const bool pok = tl * XT + dtok < T;
+      const float v[4] = {cur.dv.x, cur.dv.y, cur.dv.z, cur.dv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float vk = pok ? v[k] : 0.f;
+        const uint32_t h = f2bf(vk);
+        const uint32_t l = f2bf(vk - bf2f(h));
+        dph[(dpc * 4 + k) * DPT + dtok] = (uint16_t)h;
+        dph[(DPS + dpc * 4 + k) * DPT + dtok] = (uint16_t)l;
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -343,6 +394,31 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
     }
     const int64_t nt = tl + J;
     if (nt < ntile) load(nt, nxt);
+    if constexpr (FUSE) {
+      uint4 ph[PNB], pl[PNB];
+#pragma unroll
+      for (int nb = 0; nb < PNB; ++nb) {
+        ph[nb] = *reinterpret_cast<const uint4*>(dph + (nb * 16 + tau) * DPT + q * 8);
+        pl[nb] = *reinterpret_cast<const uint4*>(dph + (DPS + nb * 16 + tau) * DPT + q * 8);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int chl = (cb0 + cb) * 16 + tau;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(xt + xoff(si, q * 8 + 2 * k, chl));
+          const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(xt + xoff(si, q * 8 + 2 * k + 1, chl));
+          w[k] = lo16 | (hi16 << 16);
+        }
+        const uint4 xa = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+        for (int nb = 0; nb < PNB; ++nb) {
+          pacc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(xa), bf8(ph[nb]), pacc[cb][nb], 0, 0, 0);
+          pacc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(xa), bf8(pl[nb]), pacc[cb][nb], 0, 0, 0);
+        }
+      }
+    }
     __syncthreads();
     const float4* c4 = reinterpret_cast<const float4*>(cf + m * CFR);
     const float4 r0 = c4[0], r1 = c4[1], r2 = c4[2], r3 = c4[3], hp4 = c4[4], g4 = c4[5];
@@ -361,7 +437,8 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
       const float4 p0 = pj[0], p1 = pj[1];
       const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
       float xj[8], o[8];
-      unpack_bf8(cur.xq[j], xj);
+      if constexpr (FUSE) unpack_bf8(*reinterpret_cast<const uint4*>(xt + xoff(j, m, c8)), xj);
+      else unpack_bf8(cur.xq[j], xj);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v;
@@ -384,24 +461,21 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   load(tl, a);
   while (step(tl, a, b) && step(tl, b, a)) {
   }
+  if constexpr (!FUSE) return;
+  float* out = part + (int64_t)blockIdx.y * nrows * ncol;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < PNB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ch = chunk * XCH + (cb0 + cb) * 16 + q * 4 + e;
+        const int col = nb * 16 + tau;
+        if (ch < C && col < ncol) out[((int64_t)(g0 + si) * C + ch) * ncol + col] = pacc[cb][nb][e];
+      }
 }
 
-// ----------------------------------------------------------------- dphi
-
-constexpr int FT = 32;          // tokens per tile
-constexpr int FCH = 128;        // channels per chunk
-constexpr int FROW = FCH * 2;   // bytes per (stream, token) row of the state tile
-constexpr int DPT = FT + 8;     // bfloat16 per column of the transposed dP tile (80 bytes)
-
-// Byte offset of (stream i, token m, channel c) in the state tile. The 16-byte
-// block c >> 3 of a row sits at block (c >> 3) ^ (((m >> 3) & 3) << 1): the
-// A-fragment reads (16 consecutive channels of tokens m, m + 8, m + 16, m + 24)
-// then fall in distinct banks.
-__device__ __forceinline__ int xoff(int i, int m, int c) {
-  return (i * FT + m) * FROW + (((c >> 3) ^ (((m >> 3) & 3) << 1)) << 4) + (c & 7) * 2;
-}
-
-// Partial dphi of a chunk of 128 channels x the 4 slots of the row mode over
+// Partial dphi of a chunk of 128 channels x the 4 slots of the n = 4 mHC mode over
 // the token tiles g, g + G, ... (g = blockIdx.y, G = gridDim.y <= the tile
 // count), with R = the phi row of the slot's channel c:
 //   part[g][R][k] = sum_t x[t, slot, c] dP[t, k]   (k < ncol)
@@ -1130,8 +1204,9 @@ int dphi_groups(int64_t T, int64_t C, int nz) {
   return (int)(g < ntile ? g : ntile);
 }
 
-// token-tile groups of the dX pass: about one workgroup per CU over the chunks and
-// the nz stream groups (grid z), at most the tile count
+// token-tile groups of the dX pass (and of its dphi partials): about one
+// workgroup per CU over the chunks and the nz stream groups (grid z), at most
+// the tile count
 int dx_groups(int64_t T, int64_t C, int nz) {
   const int64_t nchunk = (C + XCH - 1) / XCH * nz, ntile = (T + XT - 1) / XT;
   int64_t g = (int64_t)ncu_of_device() / nchunk;
@@ -1169,7 +1244,9 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pby
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
   w.red = (float*)take((T + 15) / 16 * RED * 4);
-  w.G = dphi_groups(T, C, hp > 4 ? hp / 4 : 1);  // the pre mode's N / 4 stream groups
+  // dphi partials: the dX pass's groups where it forms them (route, pre: N / 4
+  // stream groups), else the separate pass's (n = 4 mHC)
+  w.G = route || hp > 4 ? dx_groups(T, C, hp > 4 ? hp / 4 : 1) : dphi_groups(T, C, 1);
   w.dphi_part = (float*)take((int64_t)w.G * nrows * ncol * 4);
   if (total) *total = off;
   return w;
@@ -1237,7 +1314,8 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
     return e;
   hipLaunchKernelGGL(bwd_dx_kernel<BM_MHC>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, 1)),
                      dim3(512), 0, st, x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, 4,
-                     (const int32_t*)nullptr, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+                     (const int32_t*)nullptr, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX, 0, (int64_t)0,
+                     (float*)nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dphi_kernel<BM_MHC>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st,
                      x, w.dP, T, C, 4, (const int32_t*)nullptr, BCOL, (int64_t)BS * C, w.dphi_part);
@@ -1285,13 +1363,9 @@ hipError_t launch_fast_xroute_backward(const void* X, int64_t T, int N, int64_t 
   if ((e = launch_fast_xroute_bwd_coeffs(w.partial, T, C, K, b_act, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                          w.h_res, st)) != hipSuccess)
     return e;
-  // dphi reads x only: run it before the dX pass rewrites dX_next's active rows
-  hipLaunchKernelGGL(bwd_dphi_kernel<BM_ROUTE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0,
-                     st, x, w.dP, T, C, N, idx, ncol, (int64_t)BS * C, w.dphi_part);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dx_kernel<BM_ROUTE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, 1)),
-                     dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)nullptr, T, C, N, idx,
-                     (const float*)nullptr, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_ROUTE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)w.G), dim3(512), 0, st,
+                     x, (const uint16_t*)dX, (const uint16_t*)nullptr, T, C, N, idx, (const float*)nullptr, w.h_res,
+                     w.dP, w.g2, w.phi_rows, (uint16_t*)dX, ncol, (int64_t)BS * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // dalpha: the post and res gate sums (red columns 33, 34)
   return launch_sums(w, T, (int64_t)BS * C, ncol, dphi_act, db_act, 33, 2, dalpha, st);
@@ -1309,12 +1383,9 @@ hipError_t launch_fast_xpre_backward(const void* X, int64_t T, int N, int64_t C,
       hipSuccess)
     return e;
   const unsigned ng = (unsigned)(N / 4);
-  hipLaunchKernelGGL(bwd_dphi_kernel<BM_PRE>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G, ng), dim3(512), 0,
-                     st, x, w.dP, T, C, N, (const int32_t*)nullptr, N, (int64_t)N * C, w.dphi_part);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dx_kernel<BM_PRE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, (int)ng), ng),
-                     dim3(512), 0, st, x, (const uint16_t*)dX, (const uint16_t*)dF_in, T, C, N,
-                     (const int32_t*)nullptr, w.h_pre, (const float*)nullptr, w.dP, w.g2, w.phi_rows, (uint16_t*)dX);
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_PRE>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)w.G, ng), dim3(512), 0,
+                     st, x, (const uint16_t*)dX, (const uint16_t*)dF_in, T, C, N, (const int32_t*)nullptr, w.h_pre,
+                     (const float*)nullptr, w.dP, w.g2, w.phi_rows, (uint16_t*)dX, N, (int64_t)N * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // dalpha: the gate sum (red column 32)
   return launch_sums(w, T, (int64_t)N * C, N, dphi_pre, db_pre, 32, 1, dalpha, st);
