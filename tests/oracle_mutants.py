@@ -120,7 +120,19 @@ def _route_backward_drops_passthrough(X, idx, phi_act, b_act, alpha_post, alpha_
     return r
 
 
+def _router_without_rms(X, w_router):
+    X = np.asarray(X, np.float64)
+    return H.sigmoid(X.reshape(X.shape[0], -1) @ np.asarray(w_router, np.float64))  # state not normalised
+
+
+def _router_without_sigmoid(X, w_router):
+    u, _ = H.rms_normalise(H.flatten_state(X))
+    return u @ np.asarray(w_router, np.float64)  # raw logits instead of sigma(logits)
+
+
 MUTANTS = {
+    "router_without_rms": ("xhc_router_scores", _router_without_rms),
+    "router_without_sigmoid": ("xhc_router_scores", _router_without_sigmoid),
     "sinkhorn_rows_first": ("sinkhorn_knopp", _sinkhorn_rows_first),
     "post_gate_sigma": ("hc_coeffs", _coeffs_post_sigma),
     "rms_is_two_norm": ("rms_normalise", _rms_sum),

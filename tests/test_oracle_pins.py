@@ -356,6 +356,46 @@ def test_router_duplicate_columns_tie_to_lower_index():
     assert hits > 0
 
 
+def test_router_scores_single_nonzero_entry_closed_form():
+    # One nonzero entry a at (stream i, channel c): r = |a| / sqrt(N C), so the
+    # normalised state is sign(a) sqrt(N C) at row i*C + c and zero elsewhere, and
+    # each candidate's score is 1 / (1 + exp(-sign(a) sqrt(N C) W_r[i*C + c, j]))
+    # (xHC summary, sparse residual streams, step 1; reading: sigma of a linear
+    # router on the RMS-normalised flattened state). Scalar math.exp, no matmul.
+    rng = np.random.default_rng(23)
+    N, C, m = 5, 3, 2
+    W = 0.4 * rng.standard_normal((N * C, N - m))
+    cases = [(0, 0, 2.5), (3, 1, -0.75), (4, 2, 1e-3), (2, 0, -40.0)]
+    X = np.zeros((len(cases), N, C))
+    for t, (i, c, a) in enumerate(cases):
+        X[t, i, c] = a
+    s = O.xhc_router_scores(X, W)
+    assert s.shape == (len(cases), N - m)
+    for t, (i, c, a) in enumerate(cases):
+        for j in range(N - m):
+            logit = math.copysign(math.sqrt(N * C), a) * W[i * C + c, j]
+            assert abs(s[t, j] - 1.0 / (1.0 + math.exp(-logit))) < 1e-15, (t, j)
+    # The score does not depend on |a| (the RMS factor cancels it), only on its sign.
+    np.testing.assert_array_equal(O.xhc_router_scores(7.0 * X, W), s)
+
+
+def test_router_scores_brute_force_loops():
+    # Every score from scalar loops: the token's sum of squares, r, each logit as
+    # an exactly rounded sum over the N*C flattened entries in stream-major order,
+    # then the logistic function.
+    rng = np.random.default_rng(24)
+    T, N, C, m = 4, 4, 3, 1
+    X = rng.standard_normal((T, N, C))
+    W = rng.standard_normal((N * C, N - m))
+    s = O.xhc_router_scores(X, W)
+    for t in range(T):
+        vals = [X[t, i, c] for i in range(N) for c in range(C)]
+        r = math.sqrt(math.fsum(v * v for v in vals) / (N * C))
+        for j in range(N - m):
+            logit = math.fsum(vals[q] / r * W[q, j] for q in range(N * C))
+            assert abs(s[t, j] - 1.0 / (1.0 + math.exp(-logit))) < 1e-13, (t, j)
+
+
 def test_router_selection_independent_of_normalisation():
     # No bias and r > 0: ordering of u @ W equals ordering of x @ W.
     rng = np.random.default_rng(21)
