@@ -404,3 +404,133 @@ def test_chain_with_post_pre_C7168():
         for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (h_pre, h_post_n, h_res_n), r2):
             check_fp32(name, host64(g), r)
         X, h_post, h_res = Xn, h_post_n, h_res_n
+
+
+# ------------------------------- the benchmarked launch: several items per workgroup
+
+def _round_sample(T, rounds=4, per_round=64, seed=303):
+    """Tokens from every round of items a persistent workgroup takes (at T = 8192,
+    C = 4096 the 1,024 items are tile-major over 256 workgroups, so round r covers
+    tokens 2048 r .. 2048 r + 2047), plus the round boundaries and both ends."""
+    rng = np.random.default_rng(seed)
+    q = T // rounds
+    parts = [np.array([0, T - 1])]
+    for r in range(rounds):
+        parts.append(rng.choice(np.arange(r * q, (r + 1) * q), per_round, replace=False))
+        parts.append(np.array([r * q, min(T - 1, (r + 1) * q - 1)]))
+    return np.unique(np.concatenate(parts))
+
+
+def _bf16_ulp_dev(v):
+    """One bfloat16 ulp at |v| on the device (0 where v == 0), float64."""
+    m, e = torch.frexp(v.double())
+    return torch.where(v == 0, torch.zeros_like(m), torch.ldexp(torch.ones_like(m), e - 8))
+
+
+def _check_conservation_all_tokens(X0, Xn, h_res, h_post, F):
+    """sum_i X_next = sum_i X + (sum_i h_post) F on every token and channel (Eq. 6:
+    H_res has unit column sums), within the column-sum error, fp32 accumulation and
+    the bf16 rounding of the four stored streams; in float64 on the device."""
+    cs = (h_res.double().sum(-2) - 1).abs().max().item()
+    assert cs < 1e-6, f"column sums off by {cs:.2e}"
+    for s in range(0, X0.shape[0], 2048):
+        x = X0[s:s + 2048].double()
+        xn = Xn[s:s + 2048].double()
+        f = F[s:s + 2048].double()
+        hp = h_post[s:s + 2048].double()
+        lhs = xn.sum(1)
+        rhs = x.sum(1) + hp.sum(1, keepdim=True) * f
+        bound = 0.5 * _bf16_ulp_dev(xn).sum(1) + 1e-5 * (x.abs().sum(1) + hp.abs().sum(1, keepdim=True) * f.abs())
+        bad = int(((lhs - rhs).abs() > bound).sum().item())
+        assert bad == 0, f"stream-sum conservation fails on {bad} elements (tokens {s}..)"
+
+
+def _full_size_post_case(fused_pre, in_place):
+    w = synth.WORKLOADS["mhc_n4_C4096_T8192_bf16"]
+    T, n, C = w["T"], w["n"], w["C"]
+    note(f"mHC {'hc_post_pre' if fused_pre else 'hc_post_coeffs'} full size n=4 C=4096 T=8192 bf16 "
+         f"in_place={in_place}")
+    inp = synth.mhc_layer(1, 0, T, n, C, synth.BF16)
+    nxt = synth.mhc_layer(1, 1, T, n, C, synth.BF16, draw_x=False)
+    X = dev(inp["X"])
+    X0 = X.clone()
+    F = dev(inp["F_out"])
+    h_pre, h_post, h_res = hc.hc_coeffs(X, dev(inp["phi"]), dev(inp["bias"]), [0.01] * 3)
+    args = (X, h_res, h_post, F, dev(nxt["phi"]), dev(nxt["bias"]), [0.01] * 3)
+    out = X if in_place else None
+    if fused_pre:
+        Xn, (hp2, hq2, hr2), F_in = hc.hc_post_pre(*args, out=out)
+    else:
+        Xn, (hp2, hq2, hr2) = hc.hc_post_coeffs(*args, out=out)
+    torch.cuda.synchronize()
+    sample = _round_sample(T)
+    st = torch.from_numpy(sample).cuda()
+    sub = dict(inp)
+    sub["X"] = synth.Tensor(inp["X"].values[sample], synth.BF16)
+    sub["F_out"] = synth.Tensor(inp["F_out"].values[sample], synth.BF16)
+    ref = _oracle(sub)
+    check_bf16("X_next (sampled)", host64(Xn[st]), ref["X_next"], literal_max_abs=True)
+    Xs = host64(Xn[st])
+    r2 = O.hc_coeffs(Xs, nxt["phi"], nxt["bias"], nxt["alpha"])
+    for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (hp2, hq2, hr2), r2):
+        check_fp32(name + " (sampled)", host64(g[st]), r)
+    if fused_pre:
+        check_bf16("F_in' (sampled)", host64(F_in[st]), O.hc_pre(Xs, r2[0]), literal_below=8.0)
+        # every token: the pre-read equals hc_pre(X_next, h_pre') bit for bit
+        F_ref = hc.hc_pre(Xn, hp2)
+        torch.cuda.synchronize()
+        assert torch.equal(F_in.view(torch.int16), F_ref.view(torch.int16))
+    # every token: Sinkhorn sums, gate ranges, stream-sum conservation of the write
+    hr = hr2.double()
+    assert (hr >= 0).all().item()
+    assert (hr.sum(-1) - 1).abs().max().item() < 1e-6 and (hr.sum(-2) - 1).abs().max().item() < 1e-6
+    assert ((hp2 > 0) & (hp2 < 1)).all().item() and ((hq2 > 0) & (hq2 < 2)).all().item()
+    _check_conservation_all_tokens(X0, Xn, h_res, h_post, F)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_post_pre_n4_C4096_T8192_full_size(in_place):
+    _full_size_post_case(True, in_place)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_post_coeffs_n4_C4096_T8192_full_size(in_place):
+    _full_size_post_case(False, in_place)
+
+
+@pytest.mark.slow
+def test_post_pre_chain_n4_C7168_T16384_full_size():
+    """The 8-layer C = 7168, T = 16384 chain through hc_post_pre (14 items per
+    workgroup): per layer the oracle on sampled tokens of the GPU's own input
+    state, the pre-read bit-exact against hc_pre on every token, and stream-sum
+    conservation on every token."""
+    w = synth.WORKLOADS["mhc_n4_C7168_T16384_bf16_8layers"]
+    T, n, C, layers = w["T"], w["n"], w["C"], w["layers"]
+    sample = _round_sample(T, rounds=8, per_round=16, seed=404)
+    st = torch.from_numpy(sample).cuda()
+    first = synth.mhc_layer(2, 0, T, n, C, w["dtype"])
+    X = dev(first["X"])
+    del first["X"]
+    h_pre, h_post, h_res, F_in = hc.hc_coeffs_pre(X, dev(first["phi"]), dev(first["bias"]), [0.01] * 3)
+    cur = first
+    ping = torch.empty_like(X)
+    for layer in range(layers):
+        note(f"mHC hc_post_pre chain layer {layer} (n=4 C=7168 T=16384 bf16)")
+        nxt = synth.mhc_layer(2, layer + 1, T, n, C, w["dtype"], draw_x=False)
+        F = dev(cur["F_out"])
+        Xs = host64(X[st])
+        ref = O.mhc_sublayer(Xs, cur["phi"], cur["bias"], cur["alpha"], cur["F_out"].values[sample])
+        check_bf16(f"F_in layer {layer}", host64(F_in[st]), ref["F_in"])
+        Xn, (h_pre, h_post_n, h_res_n), F_in = hc.hc_post_pre(X, h_res, h_post, F, dev(nxt["phi"]),
+                                                              dev(nxt["bias"]), [0.01] * 3, out=ping)
+        F_ref = hc.hc_pre(Xn, h_pre)
+        torch.cuda.synchronize()
+        check_bf16(f"X_next layer {layer}", host64(Xn[st]), ref["X_next"])
+        r2 = O.hc_coeffs(host64(Xn[st]), nxt["phi"], nxt["bias"], nxt["alpha"])
+        for name, g, r in zip(("h_pre'", "h_post'", "h_res'"), (h_pre, h_post_n, h_res_n), r2):
+            check_fp32(f"{name} layer {layer}", host64(g[st]), r)
+        assert torch.equal(F_in.view(torch.int16), F_ref.view(torch.int16))
+        _check_conservation_all_tokens(X, Xn, h_res, h_post, F)
+        ping, X = X, Xn
+        h_post, h_res, cur = h_post_n, h_res_n, nxt
+        del F, F_ref
