@@ -14,7 +14,10 @@
 // the second pass rebuilds B (in float64) and writes V = B A. The full-C
 // reductions then need no workgroup to hold a token's whole row. (In float32
 // this matches float64 modified Gram-Schmidt to about 3e-8 relative L2 on
-// data of this shape, as the float32 modified form does.)
+// data of this shape, as the float32 modified form does.) Tokens whose Gram
+// matrix shows a component close to the span of the earlier ones, where this
+// form loses accuracy faster than the modified one, are then redone by a third
+// pass that runs the modified form literally.
 //
 // The Gram pass works one position per lane (below); the apply pass, whose
 // stores must run along the channels, works one channel pair per thread: a
@@ -339,9 +342,71 @@ __global__ __launch_bounds__(GW) void aug_gram_kernel(const TF* __restrict__ F, 
   }
 }
 
+// The coefficients of token t's components from its Gram partials: v_j =
+// sum_k B[j][k] a_k, with <a_j, v_i> = B_i . G[:, j] and <v_i, v_i> = B_i^T G B_i
+// (the slices added in order, all in float64). vv[j] = <v_j, v_j>, gd[j] = G[j][j].
+__device__ __forceinline__ void gram_to_b(const float* __restrict__ gram, int64_t t, int nslice, double Bm[4][4],
+                                          double vv[4], double gd[4]) {
+  double G[4][4];
+  double gs[NG10];
+#pragma unroll
+  for (int k = 0; k < NG10; ++k) gs[k] = 0.0;
+  for (int sl = 0; sl < nslice; ++sl) {
+    const float* gp = gram + (t * nslice + sl) * NG10;
+#pragma unroll
+    for (int k = 0; k < NG10; ++k) gs[k] += (double)gp[k];
+  }
+  int q = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = i; j < 4; ++j) {
+      G[i][j] = gs[q];
+      G[j][i] = gs[q];
+      ++q;
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Bm[i][j] = i == j ? 1.0 : 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < j; ++i) {
+      double num = 0.0;
+#pragma unroll
+      for (int k = 0; k <= i; ++k) num += Bm[i][k] * G[k][j];
+      const double cji = num / vv[i];
+#pragma unroll
+      for (int k = 0; k <= i; ++k) Bm[j][k] -= cji * Bm[i][k];
+    }
+    double qf = 0.0;
+#pragma unroll
+    for (int k = 0; k <= j; ++k)
+#pragma unroll
+      for (int l = 0; l <= j; ++l) qf += Bm[j][k] * G[k][l] * Bm[j][l];
+    vv[j] = qf;
+    gd[j] = G[j][j];
+  }
+}
+
+// The Gram form loses accuracy as a component approaches the span of the earlier
+// ones: its error grows with the square of the condition number, the modified
+// form's with the condition number. vv_j / G_jj is the squared sine of the angle
+// between a_j and that span; a token with any of these below GS_MIN_SIN2 (an angle
+// under 30 degrees), or not finite, is redone by the literal modified form
+// (aug_mgs_fix_kernel). On the workload's data the smallest value is near 1.
+constexpr double GS_MIN_SIN2 = 0.25;
+
+__device__ __forceinline__ bool gram_ill_conditioned(const double vv[4], const double gd[4]) {
+  bool bad = false;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) bad |= !(vv[j] >= GS_MIN_SIN2 * gd[j]);  // NaN counts as bad
+  return bad;
+}
+
 // Pass 2: thread i < strip length builds B of token p0 + i from its Gram matrix
-// (slices added in order, float64) into LDS; then V[t, j] = a_j + sum_{k<j}
-// B[j][k] a_k.
+// into LDS; then V[t, j] = a_j + sum_{k<j} B[j][k] a_k.
 template <bool FC, typename TF, typename TV>
 __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F, int64_t S, int64_t C,
                                                         const float* __restrict__ w, int nstrip, int nslice_a,
@@ -351,45 +416,8 @@ __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F
   const Place pl = place<CH_A>(S, C, nstrip, nslice_a);
   if ((int64_t)threadIdx.x < pl.p1 - pl.p0) {
     const int64_t t = pl.b * S + pl.p0 + threadIdx.x;
-    double G[4][4];
-    double gs[NG10];
-#pragma unroll
-    for (int k = 0; k < NG10; ++k) gs[k] = 0.0;
-    for (int sl = 0; sl < nslice; ++sl) {
-      const float* gp = gram + (t * nslice + sl) * NG10;
-#pragma unroll
-      for (int k = 0; k < NG10; ++k) gs[k] += (double)gp[k];
-    }
-    int q = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = i; j < 4; ++j) {
-        G[i][j] = gs[q];
-        G[j][i] = gs[q];
-        ++q;
-      }
-    // rows B_j of v_j = sum_k B[j][k] a_k; <a_j, v_i> = B_i . G[:, j], <v_i, v_i> = B_i^T G B_i
-    double Bm[4][4] = {{1, 0, 0, 0}, {0, 1, 0, 0}, {0, 0, 1, 0}, {0, 0, 0, 1}};
-    double vv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int i = 0; i < j; ++i) {
-        double num = 0.0;
-#pragma unroll
-        for (int k = 0; k <= i; ++k) num += Bm[i][k] * G[k][j];
-        const double cji = num / vv[i];
-#pragma unroll
-        for (int k = 0; k <= i; ++k) Bm[j][k] -= cji * Bm[i][k];
-      }
-      double qf = 0.0;
-#pragma unroll
-      for (int k = 0; k <= j; ++k)
-#pragma unroll
-        for (int l = 0; l <= j; ++l) qf += Bm[j][k] * G[k][l] * Bm[j][l];
-      vv[j] = qf;
-    }
+    double Bm[4][4], vv[4], gd[4];
+    gram_to_b(gram, t, nslice, Bm, vv, gd);
     float* out = Bs[threadIdx.x];
     out[0] = (float)Bm[1][0];
     out[1] = (float)Bm[2][0];
@@ -426,6 +454,128 @@ __global__ __launch_bounds__(256) void aug_apply_kernel(const TF* __restrict__ F
   });
 }
 
+
+// Pass 3, for the tokens gram_ill_conditioned() flags: the modified Gram-Schmidt
+// of the xHC summary (temporal feature augmentation) taken literally in float32,
+// overwriting what pass 2 wrote for them. A workgroup of 256 threads checks 64
+// consecutive tokens (wave 0, one token per lane) and then works through the
+// flagged ones in token order, all 256 threads over the channels. A channel's
+// components are recomputed in every round instead of being stored, so any C
+// fits; each round forms the same float32 values by the same fused steps:
+//   round 1: n0 = <v0, v0>, d_j0 = <a_j, v0> (v0 = a0)
+//   round 2: v1 = a1 - c10 v0; n1 = <v1, v1>, d_j1 = <a_j - c_j0 v0, v1> (j = 2, 3)
+//   round 3: v2 = (a2 - c20 v0) - c21 v1; n2 = <v2, v2>, d32 = <(a3 - c30 v0) - c31 v1, v2>
+//   round 4: v3 = ((a3 - c30 v0) - c31 v1) - c32 v2; store v0..v3
+// with c_ji = d_ji / n_i. Sums are float32, per thread over its channels, then
+// over the lanes and the 4 waves in a fixed order.
+constexpr int FIX_TOK = 64;
+
+template <typename TF>
+__device__ __forceinline__ void conv_at(const TF* __restrict__ Fseq, int64_t pos, int64_t C, int64_t c,
+                                        const float* __restrict__ w, float a[4]) {
+  a[0] = Elem<TF>::ld(Fseq + pos * C + c);
+  const int kap[3] = {K1, K2, K3};
+  const float* wj = w;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    float g = 0.f;
+    for (int s = 0; s < kap[j]; ++s) {
+      const int64_t src = pos - kap[j] + 1 + s;
+      if (src >= 0) g = __fmaf_rn(wj[c * kap[j] + s], Elem<TF>::ld(Fseq + src * C + c), g);
+    }
+    a[j + 1] = g;
+    wj += kap[j] * C;
+  }
+}
+
+template <int NS>
+__device__ __forceinline__ void block_sums(float (&v)[NS], float (*red)[4]) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) v[k] = wave_sum(v[k]);
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int k = 0; k < NS; ++k) red[wid][k] = v[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NS; ++k) v[k] = ((red[0][k] + red[1][k]) + red[2][k]) + red[3][k];
+}
+
+template <typename TF, typename TV>
+__global__ __launch_bounds__(256) void aug_mgs_fix_kernel(const TF* __restrict__ F, int64_t S, int64_t T, int64_t C,
+                                                          const float* __restrict__ w, int nslice,
+                                                          const float* __restrict__ gram, TV* __restrict__ V) {
+  __shared__ unsigned long long flags;
+  __shared__ float red[4][4];
+  const int64_t t0 = (int64_t)blockIdx.x * FIX_TOK;
+  if (threadIdx.x < 64) {
+    const int64_t t = t0 + threadIdx.x;
+    bool bad = false;
+    if (t < T) {
+      double Bm[4][4], vv[4], gd[4];
+      gram_to_b(gram, t, nslice, Bm, vv, gd);
+      bad = gram_ill_conditioned(vv, gd);
+    }
+    const unsigned long long m = __ballot(bad);
+    if (threadIdx.x == 0) flags = m;
+  }
+  __syncthreads();
+  unsigned long long m = flags;
+  while (m) {
+    const int i = __builtin_ctzll(m);
+    m &= m - 1;
+    const int64_t t = t0 + i;
+    const int64_t pos = t % S;
+    const TF* Fseq = F + (t - pos) * C;
+    float a[4];
+    float r1[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t c = threadIdx.x; c < C; c += 256) {
+      conv_at(Fseq, pos, C, c, w, a);
+      r1[0] = __fmaf_rn(a[0], a[0], r1[0]);
+      r1[1] = __fmaf_rn(a[1], a[0], r1[1]);
+      r1[2] = __fmaf_rn(a[2], a[0], r1[2]);
+      r1[3] = __fmaf_rn(a[3], a[0], r1[3]);
+    }
+    block_sums<4>(r1, red);
+    const float c10 = r1[1] / r1[0], c20 = r1[2] / r1[0], c30 = r1[3] / r1[0];
+    float r2[3] = {0.f, 0.f, 0.f};
+    for (int64_t c = threadIdx.x; c < C; c += 256) {
+      conv_at(Fseq, pos, C, c, w, a);
+      const float v1 = __fmaf_rn(-c10, a[0], a[1]);
+      const float u2 = __fmaf_rn(-c20, a[0], a[2]);
+      const float u3 = __fmaf_rn(-c30, a[0], a[3]);
+      r2[0] = __fmaf_rn(v1, v1, r2[0]);
+      r2[1] = __fmaf_rn(u2, v1, r2[1]);
+      r2[2] = __fmaf_rn(u3, v1, r2[2]);
+    }
+    block_sums<3>(r2, red);
+    const float c21 = r2[1] / r2[0], c31 = r2[2] / r2[0];
+    float r3[2] = {0.f, 0.f};
+    for (int64_t c = threadIdx.x; c < C; c += 256) {
+      conv_at(Fseq, pos, C, c, w, a);
+      const float v1 = __fmaf_rn(-c10, a[0], a[1]);
+      const float v2 = __fmaf_rn(-c21, v1, __fmaf_rn(-c20, a[0], a[2]));
+      const float u3 = __fmaf_rn(-c31, v1, __fmaf_rn(-c30, a[0], a[3]));
+      r3[0] = __fmaf_rn(v2, v2, r3[0]);
+      r3[1] = __fmaf_rn(u3, v2, r3[1]);
+    }
+    block_sums<2>(r3, red);
+    const float c32 = r3[1] / r3[0];
+    TV* out = V + t * 4 * C;
+    for (int64_t c = threadIdx.x; c < C; c += 256) {
+      conv_at(Fseq, pos, C, c, w, a);
+      const float v1 = __fmaf_rn(-c10, a[0], a[1]);
+      const float v2 = __fmaf_rn(-c21, v1, __fmaf_rn(-c20, a[0], a[2]));
+      const float v3 = __fmaf_rn(-c32, v2, __fmaf_rn(-c31, v1, __fmaf_rn(-c30, a[0], a[3])));
+      Elem<TV>::st(out + c, a[0]);
+      Elem<TV>::st(out + C + c, v1);
+      Elem<TV>::st(out + 2 * C + c, v2);
+      Elem<TV>::st(out + 3 * C + c, v3);
+    }
+  }
+}
+
 template <typename TF, typename TV>
 hipError_t launch_aug(const void* F, int64_t B, int64_t S, int64_t C, const float* w, void* V, float* gram,
                       hipStream_t st) {
@@ -443,6 +593,11 @@ hipError_t launch_aug(const void* F, int64_t B, int64_t S, int64_t C, const floa
   else
     hipLaunchKernelGGL((aug_apply_kernel<false, TF, TV>), grid_a, blk, 0, st, (const TF*)F, S, C, w, nstrip,
                        nslice_a, nslice, (const float*)gram, (TV*)V);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t T = B * S;
+  hipLaunchKernelGGL((aug_mgs_fix_kernel<TF, TV>), dim3((unsigned)((T + FIX_TOK - 1) / FIX_TOK)), blk, 0, st,
+                     (const TF*)F, S, T, C, w, nslice, (const float*)gram, (TV*)V);
   return hipGetLastError();
 }
 

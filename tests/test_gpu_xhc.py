@@ -77,6 +77,19 @@ def _check_route(X_before, inp, idx, Wb_host, got_X, got_coeffs, sample=None):
     check_bf16("X_active", gX[act], ref_X[act])
 
 
+def _check_inactive_bit_identical_all_tokens(X_before, X_after, idx):
+    """On the device, every token: the rows outside the active set are bit for bit
+    the input rows (in-place scatter, inactive streams never written)."""
+    T, N = X_before.shape[:2]
+    act = torch.zeros(T, N, dtype=torch.bool, device=X_before.device)
+    act.scatter_(1, idx.long(), True)
+    assert int(act.sum().item()) == T * idx.shape[1], "active indices repeat within a token"
+    ib = X_before.view(torch.int16) if X_before.dtype == torch.bfloat16 else X_before.view(torch.int32)
+    ia = X_after.view(torch.int16) if X_after.dtype == torch.bfloat16 else X_after.view(torch.int32)
+    same = (ib == ia).all(dim=2)
+    assert bool(same[~act].all().item()), f"{int((~same[~act]).sum().item())} inactive rows changed"
+
+
 @pytest.mark.parametrize("T", [1, 77])
 def test_xhc_N16_C4096_pre_and_route(T):
     N, k, m, C = 16, 4, 2, 4096
@@ -120,9 +133,12 @@ def test_xhc_N16_C4096_T8192_full_size():
     sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 126, replace=False)]))
     _check_pre(inp, k, m, pre, sample)
     idx = pre["idx"].cpu().numpy().astype(np.int64)
+    X0 = X.clone()
     out = hc.xhc_route(X, dev(inp["F_out"]), dev(inp["phi_act"]), dev(inp["b_act"]), inp["alpha_post"],
                        inp["alpha_res"], k=k, m=m, idx=pre["idx"], want_coeffs=True)
     torch.cuda.synchronize()
+    _check_inactive_bit_identical_all_tokens(X0, X, pre["idx"])
+    del X0
     _check_route(inp["X"].values, inp, idx, inp["F_out"].values, X, out, sample)
 
 
@@ -165,10 +181,15 @@ def test_xhc_N16_C4096_T8192_K4_full_size():
     w = dev(np.concatenate([wj.reshape(-1) for wj in inp["conv_w"]]))
     V = hc.xhc_augment(F, w, inp["kappas"], B, S)
     X = dev(inp["X"])
+    X0 = X.clone()
     pre = hc.xhc_pre(X, dev(inp["phi_pre"]), dev(inp["b_pre"]), inp["alpha_pre"], dev(inp["w_router"]), k, m)
     out = hc.xhc_route(X, V, dev(inp["phi_act"]), dev(inp["b_act"]), inp["alpha_post"], inp["alpha_res"],
                        k=k, m=m, idx=pre["idx"], want_coeffs=True)
     torch.cuda.synchronize()
+    _check_inactive_bit_identical_all_tokens(X0, X, pre["idx"])
+    del X0
+    s_all = _router_scores_chunked(inp["X"].values, inp["w_router"])
+    np.testing.assert_array_equal(pre["idx"].cpu().numpy(), O.xhc_select(s_all, k, m))
     rng = np.random.default_rng(404)
     # sample includes sequence starts (zero padding) and the boundary between sequences
     sample = np.unique(np.concatenate([[0, 1, S - 1, S, S + 1, T - 1], rng.choice(T, 90, replace=False)]))
@@ -413,3 +434,70 @@ def test_fast_route_shapes(K, C, T):
     check_fp32("route score", host64(out2["score"]), s_ref)
     _check_route(inp["X"].values.astype(np.float64), inp, out2["idx"].cpu().numpy().astype(np.int64),
                  Wb.values.astype(np.float64), X2, out2)
+
+
+# ------------------------------- Gram-Schmidt on nearly dependent components
+
+def _near_dependent_case(kind, B, S, C, rng):
+    """F_out and conv taps whose components are close to linearly dependent:
+    'current': each conv puts weight 1 on the current token and eps * N(0, 1/kappa)
+    on the others, so every g_j is F_out plus an eps-sized part; 'smooth': F_out
+    varies slowly along the sequence (a sine per channel of period P plus 1% noise)
+    and the taps are shared by all channels, so the convs are close to multiples
+    of F_out and its first differences."""
+    name, par = kind.split(":")
+    if name == "current":
+        eps = float(par)
+        F = rng.standard_normal((B * S, C)).astype(np.float32)
+        ws = []
+        for kk in (4, 8, 12):
+            w = (eps * rng.standard_normal((C, kk)) / np.sqrt(kk)).astype(np.float32)
+            w[:, kk - 1] = 1.0
+            ws.append(w)
+    else:
+        P = float(par)
+        t = np.tile(np.arange(S), B)[:, None]
+        th = rng.uniform(0, 2 * np.pi, (1, C))
+        amp = rng.uniform(0.5, 2.0, (1, C))
+        F = (amp * np.sin(2 * np.pi * t / P + th) + 0.01 * rng.standard_normal((B * S, C))).astype(np.float32)
+        ws = [np.tile((rng.standard_normal(kk) / np.sqrt(kk)).astype(np.float32), (C, 1)) for kk in (4, 8, 12)]
+    return F, ws
+
+
+@pytest.mark.parametrize("kind", ["current:1e-1", "current:1e-2", "current:1e-3", "smooth:64", "smooth:4096"])
+@pytest.mark.parametrize("fdt,vdt", [(synth.F32, "f32"), (synth.BF16, "f32"), (synth.BF16, "bf16")])
+def test_augment_nearly_dependent_components(kind, fdt, vdt):
+    """The fast augmentation (kappa = 4, 8, 12, C = 4096) on nearly dependent
+    components, against the float64 modified Gram-Schmidt. The float32 modified
+    form errs on v_j by about u ||a_j|| / ||v_j|| (u = 2^-24: the rounding of the
+    conv output, amplified by the cancellation), a Gram-matrix form by its square;
+    per token and component the error must stay within 64 u ||a_j|| / ||v_j||
+    (float32 V; bfloat16 V: the stream bound). Positions with a full 11-token
+    window only: nearer a sequence start the components are exactly dependent for
+    the 'current' taps (the modified form divides 0 by 0 there)."""
+    B, S, C = 2, 96, 4096
+    seeds = {"current:1e-1": 71, "current:1e-2": 72, "current:1e-3": 73, "smooth:64": 74, "smooth:4096": 75}
+    rng = np.random.default_rng(seeds[kind])
+    F, ws = _near_dependent_case(kind, B, S, C, rng)
+    Ft = synth.Tensor(F, fdt)
+    note(f"xHC augment nearly dependent components {kind} F={fdt} V={vdt} B={B} S={S} C={C}")
+    V = hc.xhc_augment(dev(Ft), dev(np.concatenate([w.reshape(-1) for w in ws])), (4, 8, 12), B, S,
+                       v_dtype=torch.bfloat16 if vdt == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    got = host64(V)
+    ref = O.xhc_augment(Ft.values, ws, B, S)
+    keep = np.tile(np.arange(S), B) >= 11
+    assert np.all(np.isfinite(ref[keep])) and np.all(np.isfinite(got[keep]))
+    np.testing.assert_array_equal(got[:, 0], Ft.values)  # v_1 = F_out exactly
+    if vdt == "bf16":
+        check_bf16("V nearly dependent", got[keep], ref[keep])
+        return
+    u = 2.0 ** -24
+    for j, w in enumerate(ws, start=1):
+        a = O.causal_dwconv(Ft.values, w, B, S)[keep]
+        r, g = ref[keep, j], got[keep, j]
+        err = np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)
+        amp = np.linalg.norm(a, axis=1) / np.linalg.norm(r, axis=1)
+        worst = float(np.max(err / (u * amp)))
+        note(f"  v_{j + 1}: worst error {worst:.1f} u ||a||/||v||, largest ||a||/||v|| {amp.max():.1f}")
+        assert worst <= 64.0, f"v_{j + 1}: error {worst:.1f} u ||a_j||/||v_j|| > 64"
