@@ -79,14 +79,21 @@ def _oracle(inp, g, idx, iters=20, chunk=None, rows=None):
     return {**acc, **{k: np.concatenate(v) for k, v in per.items()}}
 
 
-def _check_two_roundings(name, got, ref, ref_first):
-    """bfloat16 output rounded twice: after ref_first, then after adding to it."""
+def _check_two_roundings(name, got, ref, got_first, ref_first):
+    """bfloat16 output rounded twice: the route stores got_first = rnd(a) (a the float32
+    route gradient), the pre call then stores got = rnd(got_first + b) (b its float32
+    gradient). Round to nearest even moves a value by at most half an ulp of the
+    rounded result, so |got - ref| <= ulp(got_first)/2 + ulp(got)/2 + |a - ref_first| +
+    |b - (ref - ref_first)|; the float32 errors of a and b are bounded here by 2e-5 of
+    the magnitudes plus 1e-6. Per element: within max(2e-2, that bound)."""
     e = rel_l2(got, ref)
     assert e <= BF16_REL_L2, f"{name}: relative L2 {e:.3e} > {BF16_REL_L2}"
     err = np.abs(got - ref)
-    bound = np.maximum(BF16_MAX_ABS, bf16_ulp(ref_first) + bf16_ulp(ref))
+    fp32 = 2e-5 * (np.abs(ref_first) + np.abs(ref - ref_first)) + 1e-6
+    bound = np.maximum(BF16_MAX_ABS, 0.5 * bf16_ulp(got_first) + 0.5 * bf16_ulp(got) + fp32)
     bad = int(np.sum(err > bound))
-    assert bad == 0, f"{name}: {bad} elements exceed max(2e-2, ulp(first) + ulp(sum)); worst {err.max():.3e}"
+    assert bad == 0, (f"{name}: {bad} elements exceed max(2e-2, ulp(first)/2 + ulp(sum)/2 + float32 error); "
+                      f"worst {err.max():.3e}")
 
 
 def _compare(route, pre, ref, g, idx, rows=None):
@@ -100,7 +107,7 @@ def _compare(route, pre, ref, g, idx, rows=None):
     check_bf16("route dX", route["dX"][sel], ref["dX_route"])
     check_bf16("dF_out", route["dWb"][sel], ref["dWb"])
     check_fp32("dh", route["dh"][sel], ref["dh"], BWD_REL)
-    _check_two_roundings("dX", pre["dX"][sel], ref["dX"], ref["dX_route"])
+    _check_two_roundings("dX", pre["dX"][sel], ref["dX"], route["dX"][sel], ref["dX_route"])
     check_fp32("dh_pre", pre["dh_pre"][sel], ref["dh_pre"], BWD_REL)
     errs = {k: check_fp32(k, route[k], ref[k], BWD_REL) for k in ("dphi_act", "db_act", "dalpha")}
     errs.update({k: check_fp32(k, pre[k], ref[k], BWD_REL) for k in ("dphi_pre", "db_pre")})
