@@ -60,6 +60,7 @@ extern "C" {
 #define HC_ERR_DEVICE (-6)    /* no usable HIP device */
 #define HC_ERR_LAUNCH (-7)    /* a kernel launch failed */
 #define HC_ERR_WORKSPACE (-8) /* workspace missing, misaligned or too small */
+#define HC_ERR_SCRATCH (-9)   /* the sizes need more than the library's fixed scratch */
 
 /* Limits checked by every call. */
 #define HC_MAX_STREAMS 64     /* n (mHC) and N (xHC) */
@@ -234,6 +235,30 @@ int hc_post_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const flo
                 float alpha_res, int sinkhorn_iters, float* h_pre_next, float* h_post_next,
                 float* h_res_next, void* F_in_next, void* workspace, int64_t workspace_bytes,
                 void* stream);
+
+/*
+ * hc_post_pre_noalloc - hc_post_pre for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments and results as hc_post_pre (the same
+ * kernels run), without workspace / workspace_bytes: the workspace is a fixed
+ * device array inside the library, HC_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the first call on that GPU until the process ends. The call allocates and
+ * frees nothing. Limit: hc_coeffs_workspace_bytes(T, n, C, dtype) must not
+ * exceed HC_NOALLOC_SCRATCH_BYTES, else HC_ERR_SCRATCH is returned before any
+ * work (32 MiB covers bfloat16 n = 4 states of C = 4096 up to about 62,000 tokens
+ * and of C = 7168 up to about 37,000). The first call on a device looks up that device's copy of the
+ * array (a HIP symbol query, with the device current); HC_ERR_DEVICE if that
+ * fails. Every call on one GPU shares that GPU's array, whose contents persist
+ * from call to call (nothing in it needs to start at zero): calls that overlap
+ * in time on one GPU (different streams, unordered) race on it and must be
+ * ordered by the caller.
+ */
+#define HC_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int hc_post_pre_noalloc(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                        const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                        const void* phi_next_packed, const float* bias_next, float alpha_pre, float alpha_post,
+                        float alpha_res, int sinkhorn_iters, float* h_pre_next, float* h_post_next,
+                        float* h_res_next, void* F_in_next, void* stream);
 
 /* ------------------------------------------------------------------ xHC -- */
 

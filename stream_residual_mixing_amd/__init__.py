@@ -44,6 +44,8 @@ _SIGS = {
     "hc_phi_pack": (_c_int, [_vp, _c_int, _c_i64, _c_int, _vp, _c_i64, _vp]),
     "hc_post_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_float,
                              _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "hc_post_pre_noalloc": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _c_float, _c_float, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "xhc_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _c_float, _vp,
                          _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
@@ -389,6 +391,35 @@ def hc_post_pre(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sinkho
         _ptr(X), _DT[X.dtype], T, n, C, _ptr(h_res), _ptr(h_post), _ptr(F_out), _ptr(X_next), _ptr(phi_next),
         _ptr(pk), _ptr(bias_next), a[0], a[1], a[2], int(sinkhorn_iters), _ptr(hp), _ptr(hq), _ptr(hr),
         _ptr(F_in), _ptr(ws), _nbytes(ws), _stream(dev, stream)))
+    return X_next, (hp, hq, hr), F_in
+
+
+# The fixed per-GPU scratch of hc_post_pre_noalloc (HC_NOALLOC_SCRATCH_BYTES in hc.h).
+HC_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def hc_post_pre_noalloc(X, h_res, h_post, F_out, phi_next, bias_next, alpha_next, sinkhorn_iters=20, *,
+                        phi_next_packed=None, out=None, coeffs_out=None, F_in_out=None, want_h_pre=True,
+                        stream=None):
+    """hc_post_pre with the library's fixed scratch as its workspace (no device memory is
+    allocated by the C call; pass every output to allocate nothing here either).
+    Returns (X_next, (h_pre' or None, h_post', h_res'), F_in')."""
+    X = _state(X)
+    T, n, C = X.shape
+    dev = X.device
+    F_out = _dev_tensor(F_out, "F_out", (X.dtype,), (T, C), dev)
+    h_res = _f32(h_res, "h_res", (T, n, n), dev)
+    h_post = _f32(h_post, "h_post", (T, n), dev)
+    phi_next, bias_next = _phi_bias(phi_next, bias_next, n, C, dev, "phi_next", "bias_next")
+    pk = None if phi_next_packed is None else _packed(phi_next_packed, "phi_next_packed", n, C, X.dtype, dev)
+    X_next = _stream_out(out, "X_next out", (T, n, C), X.dtype, dev)
+    hp, hq, hr = _coeff_outs(coeffs_out, T, n, dev, want_h_pre)
+    F_in = _stream_out(F_in_out, "F_in out", (T, C), X.dtype, dev)
+    a = [float(v) for v in alpha_next]
+    _check("hc_post_pre_noalloc", lib().hc_post_pre_noalloc(
+        _ptr(X), _DT[X.dtype], T, n, C, _ptr(h_res), _ptr(h_post), _ptr(F_out), _ptr(X_next), _ptr(phi_next),
+        _ptr(pk), _ptr(bias_next), a[0], a[1], a[2], int(sinkhorn_iters), _ptr(hp), _ptr(hq), _ptr(hr),
+        _ptr(F_in), _stream(dev, stream)))
     return X_next, (hp, hq, hr), F_in
 
 
@@ -816,6 +847,7 @@ __all__ = [
     "LIB_PATH", "HCError", "lib", "status_string", "hc_coeffs_workspace_bytes", "hc_coeffs", "hc_pre",
     "hc_coeffs_pre", "hc_post", "hc_backward_workspace_bytes", "hc_backward_post", "hc_backward", "xhc_backward_workspace_bytes",
     "xhc_route_backward", "xhc_pre_backward", "xhc_augment_backward_workspace_bytes", "xhc_augment_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
+    "hc_post_pre_noalloc", "HC_NOALLOC_SCRATCH_BYTES",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
     "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "xhc_flash_pre_workspace_bytes", "xhc_flash_pre",
     "xhc_flash_maps_workspace_bytes", "xhc_flash_maps", "xhc_flash_input", "xhc_flash_post_workspace_bytes",

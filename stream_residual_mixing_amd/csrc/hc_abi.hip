@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "hc.h"
 #include "hc_launch.h"
 #include "hc_fast.h"
@@ -145,6 +147,7 @@ const char* hc_status_string(int status) {
     case HC_ERR_DEVICE: return "no usable HIP device";
     case HC_ERR_LAUNCH: return "a kernel launch failed";
     case HC_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case HC_ERR_SCRATCH: return "the sizes need more than the library's fixed scratch (HC_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -580,6 +583,56 @@ int hc_post_pre(const void* X, int dtype, int64_t T, int n, int64_t C, const flo
   if (s != HC_OK) return s;
   return launch_status(hc::launch_pre_generic(dtype, vec_ok(C, {X_next, F_in_next}), X_next, T, n, C, hp,
                                               F_in_next, st));
+}
+
+// ------------------------------------------------------------- no-alloc --
+
+}  // extern "C"
+
+// The workspace of hc_post_pre_noalloc: a file-scope device array, one copy per
+// GPU. In host code `scratch` names a host-side stand-in, not device memory, so
+// its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[HC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HC_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HC_ERR_DEVICE;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hc_post_pre_noalloc(const void* X, int dtype, int64_t T, int n, int64_t C, const float* h_res,
+                        const float* h_post, const void* F_out, void* X_next, const float* phi_next,
+                        const void* phi_next_packed, const float* bias_next, float alpha_pre, float alpha_post,
+                        float alpha_res, int sinkhorn_iters, float* h_pre_next, float* h_post_next,
+                        float* h_res_next, void* F_in_next, void* stream) {
+  int s = check_mhc_common(X, dtype, T, n, C);
+  if (s != HC_OK) return s;
+  if (sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS) return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (mhc_ws_bytes(T, n, C, dtype) > HC_NOALLOC_SCRATCH_BYTES) return HC_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != HC_OK) return s;
+  return hc_post_pre(X, dtype, T, n, C, h_res, h_post, F_out, X_next, phi_next, phi_next_packed, bias_next,
+                     alpha_pre, alpha_post, alpha_res, sinkhorn_iters, h_pre_next, h_post_next, h_res_next,
+                     F_in_next, ws, HC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ------------------------------------------------------------------ xHC --

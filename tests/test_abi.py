@@ -50,7 +50,7 @@ def test_binding_names_match_c_entry_points(hc):
 
 def test_status_strings(hc):
     L = hc.lib()
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert L.hc_status_string(code)
     assert L.hc_version() >= 100
 
