@@ -431,20 +431,26 @@ int xhc_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int
  *   multiple of 4 up to 16, C % 8 == 0 and 16-byte aligned X and F_pre).
  *   Requires 1 <= m < N, m <= k <= min(N, HC_MAX_ACTIVE), 1 <= L <=
  *   HC_MAX_FLASH_SUBLAYERS. Workspace: xhc_flash_pre_workspace_bytes.
- * xhc_flash_maps: H_post [T, k, L] (column l: sublayer l's 2 sigma post map) and
- *   H_res [T, k, k] (Sinkhorn, sinkhorn_iters) from the active rows of X_0 (idx),
- *   phi_act [k*C, k*L + k*k] with columns [post (a*L + l) | res (a*k + b)], b_act
- *   in the same order: xhc_route's maps with K = L write-back columns.
+ * The block's write-back components: the last sublayer (the MLP, which [xHC-R]'s
+ * default configuration augments) may write back K_last components (its
+ * xhc_augment output V, K_last = K_r = 4) instead of its F_out (K_last = 1); the
+ * earlier sublayers write back their F_out. Kb = L - 1 + K_last components in
+ * all, W [T, Kb, C] in the stream dtype: F_out^(0..L-2), then the last
+ * sublayer's K_last components. 1 <= K_last, Kb <= HC_MAX_COMPONENTS.
+ * xhc_flash_maps: H_post [T, k, Kb] (column j: the 2 sigma post map of component
+ *   j) and H_res [T, k, k] (Sinkhorn, sinkhorn_iters) from the active rows of X_0
+ *   (idx), phi_act [k*C, k*Kb + k*k] with columns [post (a*Kb + j) | res (a*k + b)],
+ *   b_act in the same order: xhc_route's maps with K = Kb write-back columns.
  *   Workspace: xhc_flash_maps_workspace_bytes.
  * xhc_flash_input: sublayer l's input F_in [T, C] = F_pre_l + sum_{j<l} c_j
- *   F_outs[:, j] with c_j[t] = sum_a h_pre_l[t, idx[t, a]] H_post[t, a, j];
- *   F_pre_l = F_pre[l], h_pre_l = h_pre[l] [T, N], F_outs [T, L, C] in the stream
- *   dtype (rows j < l read; may be NULL for l = 0). F_in may be F_pre_l itself.
- *   Computed in float32, rounded once. No workspace.
+ *   W[:, j] with c_j[t] = sum_a h_pre_l[t, idx[t, a]] H_post[t, a, j];
+ *   F_pre_l = F_pre[l], h_pre_l = h_pre[l] [T, N], W (F_outs) [T, Kb, C] (rows
+ *   j < l read; may be NULL for l = 0). F_in may be F_pre_l itself. Computed in
+ *   float32, rounded once. No workspace.
  * xhc_flash_post: X_0 -> X_L in place on the active rows:
- *   X_L,A = H_res (X_0,A + sum_{j<L-1} H_post[:, j] F_out^(j)) + H_post[:, L-1] F_out^(L-1),
+ *   X_L,A = H_res (X_0,A + sum_{j<L-1} H_post[:, j] W_j) + sum_{j>=L-1} H_post[:, j] W_j,
  *   computed as one mix with the write maps E[:, j] = H_res H_post[:, j] (j < L-1)
- *   and E[:, L-1] = H_post[:, L-1] (kept in the workspace, T*k*L floats,
+ *   and E[:, j] = H_post[:, j] (j >= L-1) (kept in the workspace, T*k*Kb floats,
  *   xhc_flash_post_workspace_bytes); rows outside the active set untouched.
  * All: dtype HC_F32 or HC_BF16; float arrays 4-byte aligned, stream arrays aligned
  * to their element size, workspaces 256 bytes; outputs overlap no input, other
@@ -454,15 +460,16 @@ int64_t xhc_flash_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int L,
 int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, int L, const float* phi_pre,
                   const float* b_pre, float alpha_pre, const float* w_router, int32_t* idx, float* score,
                   float* h_pre, void* F_pre, void* workspace, int64_t workspace_bytes, void* stream);
-int64_t xhc_flash_maps_workspace_bytes(int64_t T, int N, int64_t C, int k, int L, int dtype);
-int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
-                   const float* phi_act, const float* b_act, float alpha_post, float alpha_res, int sinkhorn_iters,
-                   float* H_post, float* H_res, void* workspace, int64_t workspace_bytes, void* stream);
-int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int l, const void* F_pre_l,
+int64_t xhc_flash_maps_workspace_bytes(int64_t T, int N, int64_t C, int k, int L, int K_last, int dtype);
+int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last,
+                   const int32_t* idx, const float* phi_act, const float* b_act, float alpha_post, float alpha_res,
+                   int sinkhorn_iters, float* H_post, float* H_res, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last, int l, const void* F_pre_l,
                     const float* h_pre_l, const int32_t* idx, const float* H_post, const void* F_outs, void* F_in,
                     void* stream);
-int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L);
-int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
+int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L, int K_last);
+int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last, const int32_t* idx,
                    const float* H_post, const float* H_res, const void* F_outs, void* workspace,
                    int64_t workspace_bytes, void* stream);
 

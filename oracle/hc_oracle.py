@@ -708,10 +708,15 @@ def xhc_flash_pre(X, phi_pres, b_pres, alpha_pre, w_router, k: int, m: int):
     return dict(idx=first["idx"], score=first["score"], h_pre=np.stack(hs), F_pre=np.stack(fs))
 
 
-def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L: int, sinkhorn_iters: int = 20):
-    """The block's maps from X_0's active rows: H_post [T, k, L] (column l: sublayer
-    l's post map) and the block's H_res [T, k, k]."""
-    return xhc_active_coeffs(xhc_gather(X, idx), phi_act, b_act, alpha_post, alpha_res, L, sinkhorn_iters)
+def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L: int, sinkhorn_iters: int = 20,
+                   K_last: int = 1):
+    """The block's maps from X_0's active rows: H_post [T, k, L - 1 + K_last] (column
+    l < L - 1: sublayer l's post map; columns L - 1 ..: one per write-back component
+    of the last sublayer, which the README's configuration augments on the MLP
+    side, K_last = K_r = 4) and the block's H_res [T, k, k]; phi_act has
+    k (L - 1 + K_last) + k*k columns in xhc_active_coeffs' order."""
+    return xhc_active_coeffs(xhc_gather(X, idx), phi_act, b_act, alpha_post, alpha_res, L - 1 + K_last,
+                             sinkhorn_iters)
 
 
 def xhc_flash_input(l: int, F_pre_l, h_pre_l, idx, H_post, F_outs):
@@ -731,18 +736,22 @@ def xhc_flash_input(l: int, F_pre_l, h_pre_l, idx, H_post, F_outs):
     return F
 
 
-def xhc_flash_post(X, idx, H_post, H_res, F_outs):
+def xhc_flash_post(X, idx, H_post, H_res, F_outs, K_last: int = 1):
     """Block end: the active rows after all L sublayers,
-      X_L,A = H_res (X_0,A + sum_{j<L-1} H_post[:, j] F_out^(j)) + H_post[:, L-1] F_out^(L-1);
-    the other rows pass through. F_outs [T, L, C]. Returns X_L [T, N, C] fp64."""
+      X_L,A = H_res (X_0,A + sum_{j<L-1} H_post[:, j] W_j) + sum_{j>=L-1} H_post[:, j] W_j;
+    the other rows pass through. F_outs = W [T, L - 1 + K_last, C]: the outputs
+    F_out^(0..L-2) of the sublayers before the last, then the last sublayer's K_last
+    write-back components (F_out^(L-1) itself when K_last = 1, the augmentation's
+    V with K_last = K_r). Returns X_L [T, N, C] fp64."""
     X = _f64(X).copy()
     idx = np.asarray(idx)
     F = _f64(F_outs)
-    T, L = F.shape[0], F.shape[1]
+    T, Kb = F.shape[0], F.shape[1]
+    L = Kb - K_last + 1
     H_post = _f64(H_post)
     X_A = xhc_gather(X, idx)
     if L > 1:
         X_A = X_A + np.einsum("taj,tjc->tac", H_post[:, :, :L - 1], F[:, :L - 1])
-    X_A = np.einsum("tab,tbc->tac", _f64(H_res), X_A) + H_post[:, :, L - 1, None] * F[:, None, L - 1]
+    X_A = np.einsum("tab,tbc->tac", _f64(H_res), X_A) + np.einsum("taj,tjc->tac", H_post[:, :, L - 1:], F[:, L - 1:])
     X[np.arange(T)[:, None], idx] = X_A
     return X

@@ -58,14 +58,14 @@ _SIGS = {
     "xhc_flash_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_flash_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _c_float,
                                _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
-    "xhc_flash_maps_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
-    "xhc_flash_maps": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _c_float,
-                                _c_float, _c_int, _vp, _vp, _vp, _c_i64, _vp]),
-    "xhc_flash_input": (_c_int, [_c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
-                                 _vp, _vp]),
-    "xhc_flash_post_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_int]),
-    "xhc_flash_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
-                                _c_i64, _vp]),
+    "xhc_flash_maps_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int]),
+    "xhc_flash_maps": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                _c_float, _c_float, _c_int, _vp, _vp, _vp, _c_i64, _vp]),
+    "xhc_flash_input": (_c_int, [_c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp]),
+    "xhc_flash_post_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_int, _c_int]),
+    "xhc_flash_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                _vp, _c_i64, _vp]),
     "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
     "xhc_backward_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_route_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _c_float, _c_float,
@@ -546,13 +546,14 @@ def xhc_flash_pre(X, phi_pre, b_pre, alpha_pre, w_router, *, k=4, m=2, out=None,
     return idx, score, h_pre, F_pre
 
 
-def xhc_flash_maps_workspace_bytes(T: int, N: int, C: int, k: int, L: int, dtype) -> int:
-    return int(lib().xhc_flash_maps_workspace_bytes(T, N, C, k, L, _DT[dtype]))
+def xhc_flash_maps_workspace_bytes(T: int, N: int, C: int, k: int, L: int, dtype, K_last: int = 1) -> int:
+    return int(lib().xhc_flash_maps_workspace_bytes(T, N, C, k, L, K_last, _DT[dtype]))
 
 
-def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L, *, sinkhorn_iters=20, out=None,
+def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L, *, K_last=1, sinkhorn_iters=20, out=None,
                    workspace=None, stream=None):
-    """The block's maps from X's active rows: returns (H_post [T, k, L], H_res [T, k, k])."""
+    """The block's maps from X's active rows: returns (H_post [T, k, Kb], H_res [T, k, k]),
+    Kb = L - 1 + K_last write-back components (K_last: the last sublayer's)."""
     X = _state(X)
     T, N, C = X.shape
     dev = X.device
@@ -560,24 +561,26 @@ def xhc_flash_maps(X, idx, phi_act, b_act, alpha_post, alpha_res, L, *, sinkhorn
     if idx.dim() != 2 or idx.shape[0] != T:
         raise ValueError(f"idx has shape {tuple(idx.shape)}, expected ({T}, k)")
     k = idx.shape[1]
-    nc = k * L + k * k
+    Kb = L - 1 + K_last
+    nc = k * Kb + k * k
     phi_act = _f32(phi_act, "phi_act", (k * C, nc), dev)
     b_act = _f32(b_act, "b_act", (nc,), dev)
     if out is None:
-        out = (torch.empty(T, k, L, device=dev), torch.empty(T, k, k, device=dev))
-    Hp = _f32(out[0], "H_post out", (T, k, L), dev)
+        out = (torch.empty(T, k, Kb, device=dev), torch.empty(T, k, k, device=dev))
+    Hp = _f32(out[0], "H_post out", (T, k, Kb), dev)
     Hr = _f32(out[1], "H_res out", (T, k, k), dev)
-    ws = _workspace(xhc_flash_maps_workspace_bytes(T, N, C, k, L, X.dtype), dev, workspace)
-    _check("xhc_flash_maps", lib().xhc_flash_maps(_ptr(X), _DT[X.dtype], T, N, C, k, L, _ptr(idx), _ptr(phi_act),
-                                                  _ptr(b_act), float(alpha_post), float(alpha_res),
+    ws = _workspace(xhc_flash_maps_workspace_bytes(T, N, C, k, L, X.dtype, K_last), dev, workspace)
+    _check("xhc_flash_maps", lib().xhc_flash_maps(_ptr(X), _DT[X.dtype], T, N, C, k, L, K_last, _ptr(idx),
+                                                  _ptr(phi_act), _ptr(b_act), float(alpha_post), float(alpha_res),
                                                   int(sinkhorn_iters), _ptr(Hp), _ptr(Hr), _ptr(ws), _nbytes(ws),
                                                   _stream(dev, stream)))
     return Hp, Hr
 
 
-def xhc_flash_input(l, F_pre_l, h_pre_l, idx, H_post, F_outs, *, N=None, out=None, stream=None):
-    """Sublayer l's input from the entry-state read F_pre_l [T, C] and the earlier
-    outputs F_outs [T, L, C] (rows j < l read). Returns F_in [T, C]."""
+def xhc_flash_input(l, F_pre_l, h_pre_l, idx, H_post, F_outs, *, K_last=1, N=None, out=None, stream=None):
+    """Sublayer l's input from the entry-state read F_pre_l [T, C] and the block's
+    write-back components F_outs [T, Kb, C] (rows j < l read; Kb = L - 1 + K_last, the
+    width of H_post [T, k, Kb]). Returns F_in [T, C]."""
     F_pre_l = _dev_tensor(F_pre_l, "F_pre_l", _DT)
     if F_pre_l.dim() != 2:
         raise ValueError(f"F_pre_l must be [T, C], got shape {tuple(F_pre_l.shape)}")
@@ -591,37 +594,40 @@ def xhc_flash_input(l, F_pre_l, h_pre_l, idx, H_post, F_outs, *, N=None, out=Non
     N = h_pre_l.shape[1]
     H_post = _f32(H_post, "H_post", device=dev)
     if H_post.dim() != 3 or H_post.shape[0] != T:
-        raise ValueError(f"H_post has shape {tuple(H_post.shape)}, expected ({T}, k, L)")
-    k, L = H_post.shape[1], H_post.shape[2]
+        raise ValueError(f"H_post has shape {tuple(H_post.shape)}, expected ({T}, k, Kb)")
+    k, Kb = H_post.shape[1], H_post.shape[2]
+    L = Kb - K_last + 1
     idx = _i32(idx, "idx", (T, k), dev)
-    F_outs = None if F_outs is None else _dev_tensor(F_outs, "F_outs", (F_pre_l.dtype,), (T, L, C), dev)
+    F_outs = None if F_outs is None else _dev_tensor(F_outs, "F_outs", (F_pre_l.dtype,), (T, Kb, C), dev)
     F_in = _stream_out(out, "F_in out", (T, C), F_pre_l.dtype, dev)
-    _check("xhc_flash_input", lib().xhc_flash_input(_DT[F_pre_l.dtype], T, N, C, k, L, int(l), _ptr(F_pre_l),
+    _check("xhc_flash_input", lib().xhc_flash_input(_DT[F_pre_l.dtype], T, N, C, k, L, K_last, int(l), _ptr(F_pre_l),
                                                     _ptr(h_pre_l), _ptr(idx), _ptr(H_post), _ptr(F_outs), _ptr(F_in),
                                                     _stream(dev, stream)))
     return F_in
 
 
-def xhc_flash_post_workspace_bytes(T: int, k: int, L: int) -> int:
-    return int(lib().xhc_flash_post_workspace_bytes(T, k, L))
+def xhc_flash_post_workspace_bytes(T: int, k: int, L: int, K_last: int = 1) -> int:
+    return int(lib().xhc_flash_post_workspace_bytes(T, k, L, K_last))
 
 
-def xhc_flash_post(X, idx, H_post, H_res, F_outs, *, workspace=None, stream=None):
-    """Block end in place on X [T, N, C] from the entry state's active rows and
-    F_outs [T, L, C]. Returns X."""
+def xhc_flash_post(X, idx, H_post, H_res, F_outs, *, K_last=1, workspace=None, stream=None):
+    """Block end in place on X [T, N, C] from the entry state's active rows and the
+    write-back components F_outs [T, Kb, C] (the earlier sublayers' outputs, then the
+    last sublayer's K_last components; Kb = H_post.shape[2]). Returns X."""
     X = _state(X)
     T, N, C = X.shape
     dev = X.device
     H_post = _f32(H_post, "H_post", device=dev)
     if H_post.dim() != 3 or H_post.shape[0] != T:
-        raise ValueError(f"H_post has shape {tuple(H_post.shape)}, expected ({T}, k, L)")
-    k, L = H_post.shape[1], H_post.shape[2]
+        raise ValueError(f"H_post has shape {tuple(H_post.shape)}, expected ({T}, k, Kb)")
+    k, Kb = H_post.shape[1], H_post.shape[2]
+    L = Kb - K_last + 1
     idx = _i32(idx, "idx", (T, k), dev)
     H_res = _f32(H_res, "H_res", (T, k, k), dev)
-    F_outs = _dev_tensor(F_outs, "F_outs", (X.dtype,), (T, L, C), dev)
-    ws = _workspace(xhc_flash_post_workspace_bytes(T, k, L), dev, workspace)
-    _check("xhc_flash_post", lib().xhc_flash_post(_ptr(X), _DT[X.dtype], T, N, C, k, L, _ptr(idx), _ptr(H_post),
-                                                  _ptr(H_res), _ptr(F_outs), _ptr(ws), _nbytes(ws),
+    F_outs = _dev_tensor(F_outs, "F_outs", (X.dtype,), (T, Kb, C), dev)
+    ws = _workspace(xhc_flash_post_workspace_bytes(T, k, L, K_last), dev, workspace)
+    _check("xhc_flash_post", lib().xhc_flash_post(_ptr(X), _DT[X.dtype], T, N, C, k, L, K_last, _ptr(idx),
+                                                  _ptr(H_post), _ptr(H_res), _ptr(F_outs), _ptr(ws), _nbytes(ws),
                                                   _stream(dev, stream)))
     return X
 

@@ -152,7 +152,7 @@ const char* hc_status_string(int status) {
   }
 }
 
-int hc_version(void) { return 100; }
+int hc_version(void) { return 101; }
 
 int64_t hc_coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
   if (T < 0 || n < 1 || n > HC_MAX_MHC_STREAMS || C < 1 || !dtype_ok(dtype)) return -1;
@@ -840,15 +840,18 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
 
 // ---------------------------------------------------------------- xHC-Flash
 
-static int64_t flash_pre_ws(int64_t T, int N, int64_t C, int m, int dtype) {
-  return xhc_pre_ws(T, N, C, m, 1, dtype) + align256(T * (N - m) * 4);
+// xhc_flash_pre workspace: xhc_pre's (one pass per pre map), a score scratch, and
+// the one-pass block entry's packed phi and partials (L >= 2 on the fast path).
+static int64_t flash_pre_ws(int64_t T, int N, int64_t C, int m, int L, int dtype) {
+  const hc::XhcFastWs f = hc::flash_entry_fast_ws(T, N, C, m, L, dtype);
+  return xhc_pre_ws(T, N, C, m, 1, dtype) + align256(T * (N - m) * 4) + align256(f.packed) + align256(f.partial);
 }
 
 int64_t xhc_flash_pre_workspace_bytes(int64_t T, int N, int64_t C, int m, int L, int dtype) {
   if (T < 0 || N < 2 || N > HC_MAX_STREAMS || m < 1 || m >= N || C < 1 || L < 1 || L > HC_MAX_FLASH_SUBLAYERS ||
       !dtype_ok(dtype))
     return -1;
-  return flash_pre_ws(T, N, C, m, dtype);
+  return flash_pre_ws(T, N, C, m, L, dtype);
 }
 
 int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, int L, const float* phi_pre,
@@ -864,7 +867,7 @@ int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, 
   if (!aligned_to(X, es) || !aligned_to(F_pre, es) || !aligned_to(phi_pre, 4) || !aligned_to(b_pre, 4) ||
       !aligned_to(w_router, 4) || !aligned_to(h_pre, 4) || !aligned_to(idx, 4) || (score && !aligned_to(score, 4)))
     return HC_ERR_ALIGN;
-  const int64_t wsb = flash_pre_ws(T, N, C, m, dtype);
+  const int64_t wsb = flash_pre_ws(T, N, C, m, L, dtype);
   if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
   const int64_t NC = (int64_t)N * C;
   const void* outs[4] = {F_pre, h_pre, idx, score};
@@ -887,10 +890,17 @@ int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, 
   float* partial = (float*)(p + align256(f.packed));
   p += align256(f.packed) + align256(f.partial);
   float* sc = score ? score : (float*)p;
+  p += align256(T * (N - m) * 4);
   const bool fast = f.packed > 0 && aligned_to(X, 16);
+  const hc::XhcFastWs fe = hc::flash_entry_fast_ws(T, N, C, m, L, dtype);
   hipError_t e = hipSuccess;
-  // sublayer l's pre map from its own phi_pre^(l), b_pre^(l); the router with the first
-  for (int l = 0; l < L && e == hipSuccess; ++l) {
+  // the router and all L pre maps from one projection pass over the entry state,
+  // else sublayer l's pre map from its own phi_pre^(l), b_pre^(l) (the router with the first)
+  const bool one_pass = fe.packed > 0 && aligned_to(X, 16);
+  if (one_pass)
+    e = hc::launch_fast_flash_entry(X, T, N, C, k, m, L, phi_pre, b_pre, alpha_pre, w_router, h_pre, sc, idx, p,
+                                    (float*)(p + align256(fe.packed)), st);
+  for (int l = 0; l < (one_pass ? 0 : L) && e == hipSuccess; ++l) {
     const float* phl = phi_pre + (int64_t)l * NC * N;
     const float* bl = b_pre + (int64_t)l * N;
     float* hl = h_pre + (int64_t)l * T * N;
@@ -917,25 +927,32 @@ int xhc_flash_pre(const void* X, int dtype, int64_t T, int N, int64_t C, int k, 
   return HC_OK;
 }
 
-static int64_t flash_maps_ws(int64_t T, int64_t C, int k, int L, int dtype) {
-  const hc::XhcFastWs f = hc::xhc_route_fast_ws(T, C, k, L, dtype);
-  return align256(T * (k * L + k * k) * 4) + align256(T * 4) + align256(f.packed) + align256(f.partial);
+// write-back components of a block: L - 1 earlier outputs and the last sublayer's K_last
+static bool flash_components_ok(int L, int K_last) {
+  return L >= 1 && L <= HC_MAX_FLASH_SUBLAYERS && K_last >= 1 && L - 1 + K_last <= HC_MAX_COMPONENTS;
 }
 
-int64_t xhc_flash_maps_workspace_bytes(int64_t T, int N, int64_t C, int k, int L, int dtype) {
-  if (T < 0 || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE || C < 1 || L < 1 ||
-      L > HC_MAX_FLASH_SUBLAYERS || !dtype_ok(dtype))
+static int64_t flash_maps_ws(int64_t T, int64_t C, int k, int Kb, int dtype) {
+  const hc::XhcFastWs f = hc::xhc_route_fast_ws(T, C, k, Kb, dtype);
+  return align256(T * (k * Kb + k * k) * 4) + align256(T * 4) + align256(f.packed) + align256(f.partial);
+}
+
+int64_t xhc_flash_maps_workspace_bytes(int64_t T, int N, int64_t C, int k, int L, int K_last, int dtype) {
+  if (T < 0 || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE || C < 1 ||
+      !flash_components_ok(L, K_last) || !dtype_ok(dtype))
     return -1;
-  return flash_maps_ws(T, C, k, L, dtype);
+  return flash_maps_ws(T, C, k, L - 1 + K_last, dtype);
 }
 
-int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
-                   const float* phi_act, const float* b_act, float alpha_post, float alpha_res, int sinkhorn_iters,
-                   float* H_post, float* H_res, void* workspace, int64_t workspace_bytes, void* stream) {
+int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last,
+                   const int32_t* idx, const float* phi_act, const float* b_act, float alpha_post, float alpha_res,
+                   int sinkhorn_iters, float* H_post, float* H_res, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
   if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
   if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
-      L < 1 || L > HC_MAX_FLASH_SUBLAYERS || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS)
+      !flash_components_ok(L, K_last) || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS)
     return HC_ERR_SHAPE;
+  L = L - 1 + K_last;  // from here on: the write-back columns Kb
   if (T == 0) return HC_OK;
   if (!X || !idx || !phi_act || !b_act || !H_post || !H_res) return HC_ERR_NULL;
   if (!aligned_to(X, esize(dtype)) || !aligned_to(idx, 4) || !aligned_to(phi_act, 4) || !aligned_to(b_act, 4) ||
@@ -973,13 +990,14 @@ int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k,
   return launch_status(e);
 }
 
-int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int l, const void* F_pre_l,
+int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last, int l, const void* F_pre_l,
                     const float* h_pre_l, const int32_t* idx, const float* H_post, const void* F_outs, void* F_in,
                     void* stream) {
   if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
   if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
-      L < 1 || L > HC_MAX_FLASH_SUBLAYERS || l < 0 || l >= L)
+      !flash_components_ok(L, K_last) || l < 0 || l >= L)
     return HC_ERR_SHAPE;
+  L = L - 1 + K_last;  // H_post's and F_outs' row length Kb (only components j < l are read)
   if (T == 0) return HC_OK;
   if (!F_pre_l || !h_pre_l || !idx || !H_post || !F_in || (l > 0 && !F_outs)) return HC_ERR_NULL;
   const size_t es = esize(dtype);
@@ -999,18 +1017,20 @@ int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int l,
                                               h_pre_l, idx, H_post, F_outs, F_in, (hipStream_t)stream));
 }
 
-int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L) {
-  if (T < 0 || k < 1 || k > HC_MAX_ACTIVE || L < 1 || L > HC_MAX_FLASH_SUBLAYERS) return -1;
-  return align256(T * k * L * 4);
+int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L, int K_last) {
+  if (T < 0 || k < 1 || k > HC_MAX_ACTIVE || !flash_components_ok(L, K_last)) return -1;
+  return align256(T * k * (L - 1 + K_last) * 4);
 }
 
-int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, const int32_t* idx,
+int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last, const int32_t* idx,
                    const float* H_post, const float* H_res, const void* F_outs, void* workspace,
                    int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
   if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
-      L < 1 || L > HC_MAX_FLASH_SUBLAYERS)
+      !flash_components_ok(L, K_last))
     return HC_ERR_SHAPE;
+  const int Lsub = L;
+  L = L - 1 + K_last;  // from here on: the write-back components Kb
   if (T == 0) return HC_OK;
   if (!X || !idx || !H_post || !H_res || !F_outs) return HC_ERR_NULL;
   const size_t es = esize(dtype);
@@ -1028,7 +1048,7 @@ int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L
   if (s != HC_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   float* E = (float*)workspace;
-  hipError_t e = hc::launch_flash_post_maps(T, k, L, H_post, H_res, E, st);
+  hipError_t e = hc::launch_flash_post_maps(T, k, Lsub, L, H_post, H_res, E, st);
   if (e != hipSuccess) return HC_ERR_LAUNCH;
   if (hc::fast_mix_supported(dtype, k, L, C, X, F_outs))
     return launch_status(hc::launch_fast_mix(X, T, N, C, idx, H_res, E, F_outs, L, st));

@@ -113,6 +113,13 @@ struct XhcFastWs {
 // full-state projection (pre columns N and/or router columns N - m): N % 4 == 0, N <= 16
 XhcFastWs xhc_pre_fast_ws(int64_t T, int N, int64_t C, int m, bool with_router, int dtype);
 XhcFastWs xhc_router_fast_ws(int64_t T, int N, int64_t C, int m, int dtype);
+// xHC-Flash block entry (L >= 2) as one projection pass of the router and the L pre
+// maps: workspace need ({0, 0} when not covered).
+XhcFastWs flash_entry_fast_ws(int64_t T, int N, int64_t C, int m, int L, int dtype);
+hipError_t launch_fast_flash_entry(const void* X, int64_t T, int N, int64_t C, int k, int m, int L,
+                                   const float* phi_pre, const float* b_pre, float a_pre, const float* w_router,
+                                   float* h_pre, float* score, int32_t* idx, void* packed, float* partial,
+                                   hipStream_t st);
 // active-set projection: k == 4, k*K + k*k <= 32
 XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype);
 // Full-state pass: h_pre (phi_pre != nullptr) and/or router scores + selection

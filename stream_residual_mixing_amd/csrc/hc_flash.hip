@@ -131,21 +131,23 @@ __global__ __launch_bounds__(FI_THR) void flash_input_kernel(int64_t T, int N, i
   }
 }
 
-// E[t, a, j] = sum_b H_res[t, a, b] H_post[t, b, j] for j < L - 1 and
-// H_post[t, a, L - 1] for j = L - 1: one thread per (t, a, j).
-__global__ __launch_bounds__(256) void flash_post_maps_kernel(int64_t T, int k, int L, const float* __restrict__ H_post,
+// E[t, a, j] = sum_b H_res[t, a, b] H_post[t, b, j] for the components of the
+// sublayers before the last (j < L - 1) and H_post[t, a, j] for the last
+// sublayer's components (L - 1 <= j < Kb): one thread per (t, a, j).
+__global__ __launch_bounds__(256) void flash_post_maps_kernel(int64_t T, int k, int L, int Kb,
+                                                              const float* __restrict__ H_post,
                                                               const float* __restrict__ H_res, float* __restrict__ E) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= T * k * L) return;
-  const int64_t t = g / (k * L);
-  const int r = (int)(g - t * k * L);
-  const int a = r / L, j = r - a * L;
+  if (g >= T * k * Kb) return;
+  const int64_t t = g / (k * Kb);
+  const int r = (int)(g - t * k * Kb);
+  const int a = r / Kb, j = r - a * Kb;
   float v;
-  if (j == L - 1) {
-    v = H_post[(t * k + a) * L + j];
+  if (j >= L - 1) {
+    v = H_post[(t * k + a) * Kb + j];
   } else {
     v = 0.f;
-    for (int b = 0; b < k; ++b) v += H_res[(t * k + a) * k + b] * H_post[(t * k + b) * L + j];
+    for (int b = 0; b < k; ++b) v += H_res[(t * k + a) * k + b] * H_post[(t * k + b) * Kb + j];
   }
   E[g] = v;
 }
@@ -200,10 +202,10 @@ hipError_t launch_flash_input(int dtype, bool vec, int64_t T, int N, int64_t C, 
   return hipGetLastError();
 }
 
-hipError_t launch_flash_post_maps(int64_t T, int k, int L, const float* H_post, const float* H_res, float* E,
+hipError_t launch_flash_post_maps(int64_t T, int k, int L, int Kb, const float* H_post, const float* H_res, float* E,
                                   hipStream_t st) {
-  const int64_t n = T * k * L;
-  hipLaunchKernelGGL(flash_post_maps_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T, k, L, H_post,
+  const int64_t n = T * k * Kb;
+  hipLaunchKernelGGL(flash_post_maps_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T, k, L, Kb, H_post,
                      H_res, E);
   return hipGetLastError();
 }

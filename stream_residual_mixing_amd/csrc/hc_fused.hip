@@ -41,6 +41,20 @@ constexpr int TOK = 16;             // tokens per tile (MFMA M)
 // With rows_out (the mHC backward, nc <= 32), thread (row t >> 2, column group
 // t & 3) also writes the row form: per row 128 bytes, bf16 hi of columns 0..31
 // then bf16 lo (the B operand of dP phi^T: one row, 8 consecutive columns).
+// 8 consecutive rows of one column -> hi = bf16(p) and lo = bf16(p - hi) (p - hi is
+// exact in float32), 8 bf16 each.
+__device__ __forceinline__ void pack8_hilo(const float p[8], uint4& hi_out, uint4& lo_out) {
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const uint32_t h0 = f2bf(p[e]), h1 = f2bf(p[e + 1]);
+    hi[e / 2] = h0 | (h1 << 16);
+    lo[e / 2] = f2bf(p[e] - bf2f(h0)) | (f2bf(p[e + 1] - bf2f(h1)) << 16);
+  }
+  hi_out = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  lo_out = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
 __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__ phi_a, int na,
                                                        const float* __restrict__ phi_b, int nb, int ncolp,
                                                        uint16_t* __restrict__ packed, uint4* __restrict__ rows_out) {
@@ -71,17 +85,40 @@ __global__ __launch_bounds__(256) void pack_phi_kernel(const float* __restrict__
   float p[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) p[e] = c < nc ? rows[(g * 8 + e) * 32 + c] : 0.f;
-  uint32_t hi[4], lo[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const uint32_t h0 = f2bf(p[e]), h1 = f2bf(p[e + 1]);
-    hi[e / 2] = h0 | (h1 << 16);
-    // p - hi is exact in float32
-    lo[e / 2] = f2bf(p[e] - bf2f(h0)) | (f2bf(p[e + 1] - bf2f(h1)) << 16);
-  }
   uint4* out = reinterpret_cast<uint4*>(packed) + (r0 / 8 + g) * (2 * ncolp);
-  out[c] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  out[ncolp + c] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  pack8_hilo(p, out[c], out[ncolp + c]);
+}
+
+// The same packed form for the columns of up to 5 row-major sources [K, nc_j]
+// placed side by side (at most 80 columns): the xHC-Flash block entry packs the
+// router and the L pre maps into one operand.
+struct PackSrcs {
+  const float* p[5];
+  int nc[5];
+  int ns;
+};
+constexpr int PACK_MAXC = 80;
+__global__ __launch_bounds__(256) void pack_phi_multi_kernel(PackSrcs S, int ncolp, uint16_t* __restrict__ packed) {
+  __shared__ float rows[64 * PACK_MAXC];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  // 4 threads per row: source j's columns of row r are read at c = (tid & 3) + 4 i,
+  // so the threads of a workgroup read each source's 64 rows as one contiguous block
+  const int r = threadIdx.x >> 2, c4 = threadIdx.x & 3;
+  int nc = 0;
+  for (int j = 0; j < S.ns; ++j) {
+    const float* src = S.p[j] + (r0 + r) * S.nc[j];
+    for (int c = c4; c < S.nc[j]; c += 4) rows[r * PACK_MAXC + nc + c] = src[c];
+    nc += S.nc[j];
+  }
+  __syncthreads();
+  for (int w = threadIdx.x; w < 8 * ncolp; w += 256) {
+    const int g = w / ncolp, c = w - g * ncolp;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = c < nc ? rows[(g * 8 + e) * PACK_MAXC + c] : 0.f;
+    uint4* out = reinterpret_cast<uint4*>(packed) + (r0 / 8 + g) * (2 * ncolp);
+    pack8_hilo(p, out[c], out[ncolp + c]);
+  }
 }
 
 // ---------------------------------------------------------- stream kernel
@@ -646,15 +683,31 @@ constexpr int W_LBUF = NS4 * W_TOK * W_LROW;  // bytes per LDS buffer
 // group's 4 streams; at the item end the 16 lanes of a token are summed (DPP)
 // and the 4 sums go to the partial's extra columns (the gradient of the pre
 // map's input in the xHC backward, from the same read of the state).
-template <int NB, int MODE, bool DH = false>
+//
+// When NB is even the hi and lo halves of the packed columns fall in separate
+// 16-column blocks (hi blocks 0 .. NB/2 - 1, lo blocks NB/2 .. NB - 1), and each
+// hi block and its lo block accumulate into one set of registers (the two
+// products are added in float32 anyway): NB/2 accumulator sets per token block
+// instead of NB, which is what lets 32 columns (NB = 4) run on 64-token items.
+//
+// QD token halves are in flight (4: two super-chunks ahead; 2: one, for the
+// widest column counts, whose accumulators and phi fragments need the registers).
+template <int NB, int MODE, bool DH = false, bool SH = false, int QD = 4>  // SH: hi and lo share accumulators
 __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   static_assert(MODE != ROWS_GATHER, "gathered rows use mhc_split_kernel");
-  // NB = 4 (4 token blocks x 4 accumulator sets) would exceed the registers
-  static_assert(NB <= 3, "more columns use the 32-token items of mhc_split_kernel");
+  static_assert(!SH || NB % 2 == 0, "shared accumulators pair hi block b with lo block b + NB / 2");
+  static_assert(QD == 2 || QD == 4, "token halves in flight");
+  constexpr int NA = SH ? NB / 2 : NB;   // accumulator sets per token block
+  static_assert(NA <= 5, "4 token blocks x more accumulator sets exceed the registers");
   using PG = PartGeom<NB, W_TOK, DH ? NS4 : 0>;
   constexpr int NCP = PG::NCP;
-  constexpr int NPH = (32 * PG::PROW + STHR - 1) / STHR;  // partial floats per thread per 32-token half
-  static_assert(SWAVE * 32 * (NCP + 1) * 4 + SWAVE * 32 * 4 + 32 * NS4 * 4 <= W_LBUF, "reduction buffer");
+  constexpr int RS = NA * 16 + 1;  // floats per (wave, token) row of the reduction buffer
+  // the item-end reduction takes TPR tokens per round through one LDS buffer
+  constexpr int TPR = SWAVE * 32 * RS * 4 + SWAVE * 32 * 4 + 32 * NS4 * 4 <= W_LBUF ? 32 : 16;
+  constexpr int NR = W_TOK / TPR;                            // rounds
+  constexpr int NPH = (TPR * PG::PROW + STHR - 1) / STHR;   // partial floats per thread per round
+  static_assert(SWAVE * TPR * RS * 4 + SWAVE * TPR * 4 + TPR * NS4 * 4 <= W_LBUF, "reduction buffer");
+  static_assert(!DH || TPR == 32, "the dF_in sums are kept per 32-token half");
   const uint16_t* X = A.X;
   const int64_t T = A.T, C = A.C;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * W_LBUF];
@@ -670,12 +723,12 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   const int nk = (A.nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
   const int per_tile = A.NG * A.S;
 
-  floatx4_t acc[4][NB], gram[4];
+  floatx4_t acc[4][NA], gram[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NA; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
   const __amdgpu_buffer_rsrc_t pres =
       __builtin_amdgcn_make_buffer_rsrc(A.part, 0, (uint32_t)((int64_t)A.nitem * PG::PART * 4), BUF_DW3);
@@ -730,8 +783,8 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
       }
     }
   };
-  uint4 xq[4][NS4];
-  uint4 dq[4];  // DH: the dF_in pieces beside xq
+  uint4 xq[QD][NS4];
+  uint4 dq[QD];  // DH: the dF_in pieces beside xq
   uint4 pfq[2][NB];
   auto load_pf = [&](const Item& it2, int64_t s2, int si, uint4 (&dst)[NB]) __attribute__((always_inline)) {
     const int64_t cg = s2 * W_SC + cgw * 32;
@@ -751,26 +804,27 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
                                                          (cgw * 32 + q * 8) * 2);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          acc[tb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pfq[si][b]), acc[tb][b], 0, 0, 0);
+          acc[tb][b % NA] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pfq[si][b]), acc[tb][b % NA], 0, 0, 0);
         gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
       }
       load_pf(nit, ns, si, pfq[si]);
     }
   };
-  // Super-chunk j of item `it`: half h (= 2j + p) uses queue slot h mod 4 and is
-  // refilled with half h + 4 (for the last 4 halves: the next item's first 4).
-  static_assert(2 * W_SPI % 4 == 0, "queue slots");
+  // Super-chunk j of item `it`: half h (= 2j + p) uses queue slot h mod QD and is
+  // refilled with half h + QD (for the last QD halves: the next item's first QD).
+  static_assert(2 * W_SPI % QD == 0, "queue slots");
   auto body = [&](const Item& it, auto J, const Item& nx, unsigned char* buf) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     constexpr int h0 = 2 * j, h1 = 2 * j + 1;
-    constexpr int q0 = h0 % 4, q1 = h1 % 4;
+    constexpr int q0 = h0 % QD, q1 = h1 % QD;
     const int64_t s = it.s0 + j;
     stream_half(it, s, H0{}, xq[q0], dq[q0], buf);
-    if constexpr (h0 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h0 + 4) / 2, H0{}, xq[q0], dq[q0]);
-    else load_half(nx, nx.s0 + (h0 + 4 - 2 * W_SPI) / 2, H0{}, xq[q0], dq[q0]);
+    if constexpr (h0 + QD < 2 * W_SPI) load_half(it, it.s0 + (h0 + QD) / 2, H0{}, xq[q0], dq[q0]);
+    else load_half(nx, nx.s0 + (h0 + QD - 2 * W_SPI) / 2, H0{}, xq[q0], dq[q0]);
     stream_half(it, s, H1{}, xq[q1], dq[q1], buf);
-    if constexpr (h1 + 4 < 2 * W_SPI) load_half(it, it.s0 + (h1 + 4) / 2, H1{}, xq[q1], dq[q1]);
-    else load_half(nx, nx.s0 + (h1 + 4 - 2 * W_SPI) / 2, H1{}, xq[q1], dq[q1]);
+    if constexpr (h1 + QD < 2 * W_SPI) load_half(it, it.s0 + (h1 + QD) / 2, H1{}, xq[q1], dq[q1]);
+    else load_half(nx, nx.s0 + (h1 + QD - 2 * W_SPI) / 2, H1{}, xq[q1], dq[q1]);
     __syncthreads();
     if constexpr (j + 1 < W_SPI) mfma_phase(buf, it, it.s0 + j + 1);
     else mfma_phase(buf, nx, nx.s0);
@@ -780,26 +834,28 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   Item it = item_of(item);
   load_half(it, it.s0, H0{}, xq[0], dq[0]);
   load_half(it, it.s0, H1{}, xq[1], dq[1]);
-  load_half(it, it.s0 + 1, H0{}, xq[2], dq[2]);
-  load_half(it, it.s0 + 1, H1{}, xq[3], dq[3]);
+  if constexpr (QD == 4) {
+    load_half(it, it.s0 + 1, H0{}, xq[2 % QD], dq[2 % QD]);
+    load_half(it, it.s0 + 1, H1{}, xq[3 % QD], dq[3 % QD]);
+  }
   load_pf(it, it.s0, 0, pfq[0]);
   load_pf(it, it.s0, 1, pfq[1]);
   // the partial sums this thread reduced for the previous item (pitem; -1: none):
   // pend[r][u] holds element tid + u * STHR of the item's token half r
-  float pend[2][NPH];
+  float pend[NR][NPH];
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int u = 0; u < NPH; ++u) pend[r][u] = 0.f;
   int pitem = -1;
   auto store_pending = [&]() __attribute__((always_inline)) {
     const uint32_t base = (uint32_t)pitem * (uint32_t)(PG::PART * 4);
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int u = 0; u < NPH; ++u) {
         const int o = tid + u * STHR;
-        const uint32_t off = pitem >= 0 && o < 32 * PG::PROW ? base + (uint32_t)(r * 32 * PG::PROW + o) * 4 : OOB;
+        const uint32_t off = pitem >= 0 && o < TPR * PG::PROW ? base + (uint32_t)(r * TPR * PG::PROW + o) * 4 : OOB;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend[r][u]), pres, off, 0, 0);
       }
   };
@@ -812,11 +868,11 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
       if constexpr (decltype(J)::value == 0) store_pending();
     });
     step += W_SPI;
-    // item end: the 8 waves' sums, 32 tokens (two token blocks) per round,
+    // item end: the 8 waves' sums, TPR tokens (TPR / 16 token blocks) per round,
     // through the buffer the last MFMA phase read
-    float* red = reinterpret_cast<float*>(lds + ((step - 1) & 1) * W_LBUF);  // [SWAVE][32][NCP + 1]
-    float* ssr = red + SWAVE * 32 * (NCP + 1);                                // [SWAVE][32]
-    float* dhr = ssr + SWAVE * 32;                                            // DH: [32][NS4]
+    float* red = reinterpret_cast<float*>(lds + ((step - 1) & 1) * W_LBUF);  // [SWAVE][TPR][RS]
+    float* ssr = red + SWAVE * TPR * RS;                                      // [SWAVE][TPR]
+    float* dhr = ssr + SWAVE * TPR;                                           // DH: [32][NS4]
     if constexpr (DH) {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -824,7 +880,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
         for (int i = 0; i < NS4; ++i) dh[r][i] = row16_sum(dh[r][i]);
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < NR; ++r) {
       __syncthreads();
       if constexpr (DH) {
         if ((tid & 15) == 0) {
@@ -833,31 +889,33 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
         }
       }
 #pragma unroll
-      for (int tbb = 0; tbb < 2; ++tbb) {
-        const int tb = 2 * r + tbb;
+      for (int tbb = 0; tbb < TPR / TOK; ++tbb) {
+        const int tb = (TPR / TOK) * r + tbb;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NA; ++b)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            red[(wave * 32 + tbb * TOK + q * 4 + e) * (NCP + 1) + b * 16 + tau] = acc[tb][b][e];
+            red[(wave * TPR + tbb * TOK + q * 4 + e) * RS + b * 16 + tau] = acc[tb][b][e];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (tau == q * 4 + e) ssr[wave * 32 + tbb * TOK + tau] = gram[tb][e];
+          if (tau == q * 4 + e) ssr[wave * TPR + tbb * TOK + tau] = gram[tb][e];
       }
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < NPH; ++u) {
         int o = tid + u * STHR;
-        o = o < 32 * PG::PROW ? o : tid;
+        o = o < TPR * PG::PROW ? o : tid;
         const int m = o / PG::PROW, col = o - m * PG::PROW;
         float sum = 0.f;
         if (col < PG::NCOLP) {
 #pragma unroll
-          for (int w = 0; w < SWAVE; ++w)
-            sum += red[(w * 32 + m) * (NCP + 1) + col] + red[(w * 32 + m) * (NCP + 1) + PG::NCOLP + col];
+          for (int w = 0; w < SWAVE; ++w) {
+            if constexpr (SH) sum += red[(w * TPR + m) * RS + col];
+            else sum += red[(w * TPR + m) * RS + col] + red[(w * TPR + m) * RS + PG::NCOLP + col];
+          }
         } else if (col == PG::NCOLP) {
 #pragma unroll
-          for (int w = 0; w < SWAVE; ++w) sum += ssr[w * 32 + m];
+          for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TPR + m];
         } else {
           sum = dhr[m * NS4 + (col - PG::NCOLP - 1)];
         }
@@ -872,7 +930,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     for (int tb = 0; tb < 4; ++tb) {
       gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < NA; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     }
     pitem = item;
     item = nitem_k;
@@ -1247,6 +1305,82 @@ __global__ __launch_bounds__(256) void xpre_finish_kernel(const float* __restric
   }
 }
 
+// xHC-Flash block entry ([xHC] xHC-Flash variant: the router once and every
+// sublayer's pre map from the block-entry state): the finish of the one
+// projection pass over columns [router N - m | pre map 0, N | ... | pre map L-1].
+// 32 lanes per token; lane c takes columns c, c + 32, c + 64 (each summed over
+// the token's items in order, as xpre_finish_kernel does), the router lanes c <
+// N - m run the same arg-max rounds.
+template <int NB>
+__global__ __launch_bounds__(256) void flash_entry_finish_kernel(const float* __restrict__ part, int64_t T,
+                                                                 int64_t C, int N, int per_tile, int L, int k, int m,
+                                                                 const float* __restrict__ b_pre, float a_pre,
+                                                                 float* __restrict__ h_pre, float* __restrict__ score,
+                                                                 int32_t* __restrict__ idx) {
+  using PG = PartGeom<NB, W_TOK>;
+  constexpr int NJ = (PG::NCOLP + 31) / 32;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tt = g >> 5;
+  const int c = (int)(g & 31);
+  const int64_t tc = tt < T ? tt : T - 1;
+  const int64_t tile = tc / W_TOK;
+  const int mrow = (int)(tc - tile * W_TOK);
+  const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
+  float ss = 0.f, pc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) pc[j] = 0.f;
+#pragma unroll 2
+  for (int it = 0; it < per_tile; ++it) {
+    const float* b = base + (int64_t)it * PG::PART;
+    ss += b[PG::NCOLP];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) pc[j] += b[c + 32 * j < PG::NCOLP ? c + 32 * j : 0];
+  }
+  const float r = sqrtf(ss / (float)((double)N * (double)C));
+  const float invr = (r > 0.f) ? 1.0f / r : 0.f;
+  const bool valid = tt < T;
+  const int nr = N - m;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int col = c + 32 * j - nr;
+    if (valid && col >= 0 && col < L * N) {
+      const int l = col / N, i = col - l * N;
+      h_pre[((int64_t)l * T + tt) * N + i] = sigmoid(a_pre * (pc[j] * invr) + b_pre[l * N + i]);
+    }
+  }
+  const bool is_rt = c < nr;
+  const float sc = sigmoid(pc[0] * invr);
+  if (valid && is_rt && score) score[tt * nr + c] = sc;
+  float key = is_rt ? sc : -1.f;
+  const int cand = is_rt ? c : 64;
+  uint64_t chosen = 0;
+  for (int round = 0; round < k - m; ++round) {
+    float bv = key;
+    int bl = cand;
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d, 32);
+      const int ol = __shfl_xor(bl, d, 32);
+      if (ov > bv || (ov == bv && ol < bl)) {
+        bv = ov;
+        bl = ol;
+      }
+    }
+    chosen |= 1ull << (m + bl);
+    if (cand == bl) key = -2.f;
+  }
+  if (valid && c < k) {
+    const uint64_t mask = chosen | ((m >= 64 ? ~0ull : (1ull << m) - 1));
+    int cnt = 0, v = 0;
+    for (int sidx = 0; sidx < N; ++sidx)
+      if ((mask >> sidx) & 1ull) {
+        if (cnt == c) v = sidx;
+        ++cnt;
+      }
+    idx[tt * k + c] = v;
+  }
+}
+
 // xHC active coefficients ([xHC] step 3, parameterisation) for k = 4: 16 lanes
 // per token. Columns [post k*K (a*K + j) | res 16 (a*4 + b)]. Each lane adds the
 // token's items in order, r_A = sqrt(ss / (4 C)); post lanes e < 4K: H_post =
@@ -1435,7 +1569,7 @@ __global__ __launch_bounds__(256) void pre_wide_kernel(const uint16_t* __restric
                               reinterpret_cast<u32x4_t*>(F_in + t * C + c0));
 }
 
-// xHC mix + scatter for k = 4 bfloat16 active streams and K <= 4 write-back
+// xHC mix + scatter for k = 4 bfloat16 active streams and K <= 8 write-back
 // components, in place ([xHC] step 3): X[t, idx[a]] = sum_b H_res[t, a, b]
 // X[t, idx[b]] + sum_j H_post[t, a, j] Wb[t, j], 8 channels per thread, all
 // 4 + K rows in flight at once, nontemporal loads and stores (each row is read
@@ -1777,27 +1911,24 @@ XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype) {
   return {(int64_t)k * C / 8 * (nb * 16) * 16, part_bytes(T, C, 1, nb)};
 }
 
-// Full-state projection and finish, on 64-token items (proj_wide_kernel, half
-// the phi traffic per byte of state) or 32-token items (mhc_split_kernel). The
-// item size follows from N and m alone, through the column count of the pass
-// with both maps (N + N - m): up to 24 columns the wide kernel, beyond it the
-// 32-token kernel, whose registers hold 32 columns (the wide kernel's 4 token
-// blocks of 4 accumulator sets do not fit, and measured slower at N = 16). So
-// the pre map, the router and both together add every column in one order
-// and give the same bits.
-template <int NB, int TT>
+// Full-state projection and finish, on 64-token items (proj_wide_kernel: each
+// phi fragment taken from L2 serves 64 tokens). Whether the hi and lo parts of
+// phi share accumulators follows from N and m alone, through the column count
+// of the pass with both maps (N + N - m): shared unless that pass has 24
+// columns (NB = 3, where hi and lo blocks do not pair up; 32 columns need the
+// shared form to fit the registers). So the pre map, the router and both
+// together add every column in one order and give the same bits.
+template <int NB, bool SH>
 static hipError_t xhc_full_nb(const void* X, int64_t T, int N, int64_t C, int k, int m, int npre, int nr,
                               const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
                               const void* packed, float* partial, hipStream_t st) {
-  const Geom g = geom(T, C, N / 4, TT);
+  const Geom g = geom(T, C, N / 4, W_TOK);
   const SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);
-  if constexpr (TT == W_TOK) hipLaunchKernelGGL((proj_wide_kernel<NB, ROWS_GROUPS>), dim3(grid_for(A.nitem)),
-                                                dim3(STHR), 0, st, A);
-  else hipLaunchKernelGGL((mhc_split_kernel<false, NB, ROWS_GROUPS>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
+  hipLaunchKernelGGL((proj_wide_kernel<NB, ROWS_GROUPS, false, SH>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t threads = T * 32;
-  hipLaunchKernelGGL((xpre_finish_kernel<NB, TT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL((xpre_finish_kernel<NB, W_TOK>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                      partial, T, C, N, g.NG * g.S, npre, nr, k, m, b_pre, a_pre, h_pre, score, idx);
   return hipGetLastError();
 }
@@ -1805,13 +1936,13 @@ static hipError_t xhc_full_nb(const void* X, int64_t T, int N, int64_t C, int k,
 static hipError_t xhc_full_proj(const void* X, int64_t T, int N, int64_t C, int k, int m, int npre, int nr, int nb,
                                  const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
                                  const void* packed, float* partial, hipStream_t st) {
-  const bool wide = nb_for(N + (N - m)) <= 3;
-#define HC_FULL(NB, TT) \
-  xhc_full_nb<NB, TT>(X, T, N, C, k, m, npre, nr, b_pre, a_pre, h_pre, score, idx, packed, partial, st)
+  const bool shared = nb_for(N + (N - m)) != 3;
+#define HC_FULL(NB, SH) \
+  xhc_full_nb<NB, SH>(X, T, N, C, k, m, npre, nr, b_pre, a_pre, h_pre, score, idx, packed, partial, st)
   switch (nb) {
-    case 2: return wide ? HC_FULL(2, W_TOK) : HC_FULL(2, TILE);
-    case 3: return wide ? HC_FULL(3, W_TOK) : HC_FULL(3, TILE);
-    default: return HC_FULL(4, TILE);
+    case 2: return shared ? HC_FULL(2, true) : HC_FULL(2, false);
+    case 3: return HC_FULL(3, false);
+    default: return HC_FULL(4, true);
   }
 #undef HC_FULL
 }
@@ -1827,6 +1958,67 @@ hipError_t launch_fast_xhc_full(const void* X, int64_t T, int N, int64_t C, int 
   e = xhc_full_proj(X, T, N, C, k, m, npre, nr, nb, b_pre, a_pre, h_pre, score, idx, packed, partial, st);
   if (e != hipSuccess || !F_in) return e;
   return launch_pre_wide(X, T, N, C, h_pre, F_in, st);
+}
+
+// xHC-Flash block entry in one projection pass: the router and the L pre maps
+// packed side by side (router first), 64-token items with shared hi/lo
+// accumulators, 2 * ceil(columns / 16) packed blocks (at most 80 columns).
+static int flash_entry_nb(int N, int m, int L) {
+  const int ncols = (N - m) + L * N;
+  const int nb = 2 * ((ncols + 15) / 16);
+  return nb < 2 ? 2 : nb;
+}
+
+XhcFastWs flash_entry_fast_ws(int64_t T, int N, int64_t C, int m, int L, int dtype) {
+  if (dtype != 1 || N % 4 != 0 || N > 16 || L < 2 || (N - m) > 32) return {0, 0};
+  const int nb = flash_entry_nb(N, m, L);
+  if (nb * 8 > PACK_MAXC || !shape_ok(T, C, N / 4, nb)) return {0, 0};
+  return {(int64_t)N * C / 8 * (nb * 16) * 16, part_bytes(T, C, N / 4, nb)};
+}
+
+template <int NB, int QD>
+static hipError_t flash_entry_nb_launch(const SplitArgs& A, const Geom& g, int64_t T, int N, int64_t C, int L, int k,
+                                        int m, const float* b_pre, float a_pre, float* h_pre, float* score,
+                                        int32_t* idx, const float* partial, hipStream_t st) {
+  hipLaunchKernelGGL((proj_wide_kernel<NB, ROWS_GROUPS, false, true, QD>), dim3(grid_for(A.nitem)), dim3(STHR), 0,
+                     st, A);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = T * 32;
+  hipLaunchKernelGGL((flash_entry_finish_kernel<NB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                     partial, T, C, N, g.NG * g.S, L, k, m, b_pre, a_pre, h_pre, score, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_flash_entry(const void* X, int64_t T, int N, int64_t C, int k, int m, int L,
+                                   const float* phi_pre, const float* b_pre, float a_pre, const float* w_router,
+                                   float* h_pre, float* score, int32_t* idx, void* packed, float* partial,
+                                   hipStream_t st) {
+  const int nb = flash_entry_nb(N, m, L);
+  const int64_t NC = (int64_t)N * C;
+  PackSrcs S{};
+  S.p[0] = w_router;
+  S.nc[0] = N - m;
+  for (int l = 0; l < L; ++l) {
+    S.p[1 + l] = phi_pre + (int64_t)l * NC * N;
+    S.nc[1 + l] = N;
+  }
+  S.ns = 1 + L;
+  hipLaunchKernelGGL(pack_phi_multi_kernel, dim3((unsigned)(NC / 64)), dim3(256), 0, st, S, nb * 8,
+                     (uint16_t*)packed);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const Geom g = geom(T, C, N / 4, W_TOK);
+  const SplitArgs A = args(X, T, C, NC, g, packed, partial);
+#define HC_FE(NB, QD) flash_entry_nb_launch<NB, QD>(A, g, T, N, C, L, k, m, b_pre, a_pre, h_pre, score, idx, partial, st)
+  switch (nb) {
+    case 2: return HC_FE(2, 4);
+    case 4: return HC_FE(4, 4);
+    case 6: return HC_FE(6, 4);
+    case 8: return HC_FE(8, 2);
+    default: return HC_FE(10, 2);
+  }
+#undef HC_FE
 }
 
 // Streaming copy of n16 16-byte words: 4 per thread, all loads issued before
@@ -1857,7 +2049,7 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, hipStrea
 }
 
 bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const void* Wb) {
-  return dtype == 1 && k == 4 && K >= 1 && K <= 4 && C % 8 == 0 && a16(X) && a16(Wb);
+  return dtype == 1 && k == 4 && K >= 1 && K <= 8 && C % 8 == 0 && a16(X) && a16(Wb);
 }
 
 hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* idx, const float* H_res,
@@ -1870,7 +2062,11 @@ hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* 
     case 1: hipLaunchKernelGGL(mix4_kernel<1>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
     case 2: hipLaunchKernelGGL(mix4_kernel<2>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
     case 3: hipLaunchKernelGGL(mix4_kernel<3>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    default: hipLaunchKernelGGL(mix4_kernel<4>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    case 4: hipLaunchKernelGGL(mix4_kernel<4>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    case 5: hipLaunchKernelGGL(mix4_kernel<5>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    case 6: hipLaunchKernelGGL(mix4_kernel<6>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    case 7: hipLaunchKernelGGL(mix4_kernel<7>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+    default: hipLaunchKernelGGL(mix4_kernel<8>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
   }
   return hipGetLastError();
 }

@@ -69,7 +69,7 @@ hipError_t launch_flash_input(int dtype, bool vec, int64_t T, int N, int64_t C, 
                               const void* F_pre, const float* h_pre, const int32_t* idx, const float* H_post,
                               const void* F_outs, void* F_in, hipStream_t st);
 // E [T, k, L]: the block end's write maps (H_res H_post[:, j] for j < L - 1, H_post[:, L - 1]).
-hipError_t launch_flash_post_maps(int64_t T, int k, int L, const float* H_post, const float* H_res, float* E,
+hipError_t launch_flash_post_maps(int64_t T, int k, int L, int Kb, const float* H_post, const float* H_res, float* E,
                                   hipStream_t st);
 
 }  // namespace hc

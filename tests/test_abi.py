@@ -358,9 +358,12 @@ def test_flash_validation(hc):
     assert L.xhc_flash_pre_workspace_bytes(T, N, C, m, Ls, 1) > 0
     assert L.xhc_flash_pre_workspace_bytes(T, N, C, m, 5, 1) == -1
     assert L.xhc_flash_pre_workspace_bytes(T, N, C, N, Ls, 1) == -1  # m = N leaves nothing to route
-    assert L.xhc_flash_maps_workspace_bytes(T, N, C, k, 0, 1) == -1
-    assert L.xhc_flash_post_workspace_bytes(T, k, Ls) >= T * k * Ls * 4
-    assert L.xhc_flash_post_workspace_bytes(T, k, 5) == -1
+    assert L.xhc_flash_maps_workspace_bytes(T, N, C, k, 0, 1, 1) == -1
+    assert L.xhc_flash_maps_workspace_bytes(T, N, C, k, Ls, 0, 1) == -1  # no component for the last sublayer
+    assert L.xhc_flash_maps_workspace_bytes(T, N, C, k, 4, 6, 1) == -1  # 9 components > HC_MAX_COMPONENTS
+    assert L.xhc_flash_post_workspace_bytes(T, k, Ls, 1) >= T * k * Ls * 4
+    assert L.xhc_flash_post_workspace_bytes(T, k, Ls, 4) >= T * k * (Ls + 3) * 4
+    assert L.xhc_flash_post_workspace_bytes(T, k, 5, 1) == -1
     P = lambda j: ctypes.c_void_p(0x1000000 * (j + 1))
     wsp = L.xhc_flash_pre_workspace_bytes(T, N, C, m, Ls, 1)
 
@@ -378,33 +381,37 @@ def test_flash_validation(hc):
     assert pre(F=ctypes.c_void_p(0x1000000)) == -5  # F_pre over X
     assert pre(idx=ctypes.c_void_p(0x7000000)) == -5  # idx over h_pre
 
-    wsm = L.xhc_flash_maps_workspace_bytes(T, N, C, k, Ls, 1)
+    wsm = L.xhc_flash_maps_workspace_bytes(T, N, C, k, Ls, 1, 1)
 
-    def maps(Lb=Ls, iters=20, wsb=wsm, **kw):
+    def maps(Lb=Ls, Kl=1, iters=20, wsb=wsm, **kw):
         p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["X", "idx", "phi", "b", "Hp", "Hr", "ws"])}
-        return L.xhc_flash_maps(p["X"], 1, T, N, C, k, Lb, p["idx"], p["phi"], p["b"], ctypes.c_float(0.01),
+        return L.xhc_flash_maps(p["X"], 1, T, N, C, k, Lb, Kl, p["idx"], p["phi"], p["b"], ctypes.c_float(0.01),
                                 ctypes.c_float(0.01), iters, p["Hp"], p["Hr"], p["ws"], wsb, None)
-    assert maps(Lb=5) == -2 and maps(iters=0) == -2
+    assert maps(Lb=5) == -2 and maps(iters=0) == -2 and maps(Kl=0) == -2 and maps(Kl=8) == -2
     for nm in ("X", "idx", "phi", "b", "Hp", "Hr"):
         assert maps(**{nm: None}) == -1, nm
     assert maps(wsb=wsm - 1) == -8
     assert maps(Hr=ctypes.c_void_p(0x5000000)) == -5  # H_res over H_post
 
-    def inp(l=1, Lb=Ls, **kw):
+    def inp(l=1, Lb=Ls, Kl=1, **kw):
         p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["Fp", "h", "idx", "Hp", "Fo", "Fi"])}
-        return L.xhc_flash_input(1, T, N, C, k, Lb, l, p["Fp"], p["h"], p["idx"], p["Hp"], p["Fo"], p["Fi"], None)
-    assert inp(l=2) == -2 and inp(l=-1) == -2 and inp(Lb=0) == -2
+        return L.xhc_flash_input(1, T, N, C, k, Lb, Kl, l, p["Fp"], p["h"], p["idx"], p["Hp"], p["Fo"], p["Fi"],
+                                 None)
+    assert inp(l=2) == -2 and inp(l=-1) == -2 and inp(Lb=0) == -2 and inp(Kl=0) == -2
+    assert inp(l=2, Kl=4) == -2  # l counts sublayers, not components
     for nm in ("Fp", "h", "idx", "Hp", "Fo", "Fi"):
         assert inp(**{nm: None}) == -1, nm
     assert inp(Fi=ctypes.c_void_p(0x6000001)) == -4
     assert inp(Fi=ctypes.c_void_p(0x5000000)) == -5  # F_in over F_outs
 
-    wsq = L.xhc_flash_post_workspace_bytes(T, k, Ls)
+    wsq = L.xhc_flash_post_workspace_bytes(T, k, Ls, 1)
 
-    def post(Lb=Ls, wsb=wsq, **kw):
+    def post(Lb=Ls, Kl=1, wsb=wsq, **kw):
         p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["X", "idx", "Hp", "Hr", "Fo", "ws"])}
-        return L.xhc_flash_post(p["X"], 1, T, N, C, k, Lb, p["idx"], p["Hp"], p["Hr"], p["Fo"], p["ws"], wsb, None)
-    assert post(Lb=5) == -2
+        return L.xhc_flash_post(p["X"], 1, T, N, C, k, Lb, Kl, p["idx"], p["Hp"], p["Hr"], p["Fo"], p["ws"], wsb,
+                                None)
+    assert post(Lb=5) == -2 and post(Kl=0) == -2
+    assert post(Kl=4) == -8  # the workspace holds T k (L - 1 + K_last) maps
     for nm in ("X", "idx", "Hp", "Hr", "Fo"):
         assert post(**{nm: None}) == -1, nm
     assert post(ws=None) == -8 and post(wsb=wsq - 1) == -8

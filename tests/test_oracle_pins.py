@@ -897,55 +897,72 @@ def test_conv_backward_adjoint_identities():
 
 # ------------------------------------------------------------------ xHC-Flash
 
-def _flash_case(seed, T=6, N=8, C=5, k=4, m=2, L=2):
+def _flash_case(seed, T=6, N=8, C=5, k=4, m=2, L=2, K_last=1):
     rng = np.random.default_rng(seed)
     X = rng.standard_normal((T, N, C))
     phis = [rng.standard_normal((N * C, N)) * 0.3 for _ in range(L)]
     bs = [rng.standard_normal(N) * 0.2 for _ in range(L)]
     w_r = rng.standard_normal((N * C, N - m)) * 0.3
-    phi_act = rng.standard_normal((k * C, k * L + k * k)) * 0.3
-    b_act = rng.standard_normal(k * L + k * k) * 0.2
+    Kb = L - 1 + K_last
+    phi_act = rng.standard_normal((k * C, k * Kb + k * k)) * 0.3
+    b_act = rng.standard_normal(k * Kb + k * k) * 0.2
     F_outs = rng.standard_normal((T, L, C))
     return X, phis, bs, w_r, phi_act, b_act, F_outs
 
 
-@pytest.mark.parametrize("L", [1, 2, 3, 4])
-def test_flash_matches_materialised_block(L):
+@pytest.mark.parametrize("L,K_last", [(1, 1), (2, 1), (3, 1), (4, 1), (2, 4), (3, 4), (1, 4)])
+def test_flash_matches_materialised_block(L, K_last):
     """The block run sublayer by sublayer with the state written out after each
     one (sublayers before the last add their post write to the active rows, the
     last mixes with H_res and adds its own, every sublayer's input is the dense
     read of the state as it then is) gives the inputs xhc_flash_input rebuilds
-    from the entry-state reads and the state xhc_flash_post writes."""
-    X0, phis, bs, w_r, phi_act, b_act, F_outs = _flash_case(700 + L, L=L)
+    from the entry-state reads and the state xhc_flash_post writes. With
+    K_last = 4 the last sublayer (the MLP) writes back its augmentation: the
+    Gram-Schmidt components of causal convs of its own output, each through its
+    own post-map column, as xhc_route adds K components."""
+    T, C = 8, 5
+    X0, phis, bs, w_r, phi_act, b_act, F_outs = _flash_case(700 + 10 * L + K_last, T=T, C=C, L=L, K_last=K_last)
     k, m = 4, 2
     pre = O.xhc_flash_pre(X0, phis, bs, 0.7, w_r, k, m)
     idx = pre["idx"]
-    H_post, H_res = O.xhc_flash_maps(X0, idx, phi_act, b_act, 0.6, 0.9, L, 20)
-    T = X0.shape[0]
+    H_post, H_res = O.xhc_flash_maps(X0, idx, phi_act, b_act, 0.6, 0.9, L, 20, K_last=K_last)
+    assert H_post.shape == (T, k, L - 1 + K_last)
+    if K_last == 1:
+        last = F_outs[:, L - 1:L]
+    else:  # 2 sequences of 4 tokens, kernels 2, 3, 4 (any sizes: the block end is linear in them)
+        rng = np.random.default_rng(33)
+        ws = [rng.standard_normal((C, kk)) / np.sqrt(kk) for kk in (2, 3, 4)[:K_last - 1]]
+        last = O.xhc_augment(F_outs[:, L - 1], ws, 2, T // 2)
+    W = np.concatenate([F_outs[:, :L - 1], last], axis=1)
     rows = np.arange(T)[:, None]
     Xs = X0.copy()
     for l in range(L):
         want = np.einsum("ti,tic->tc", pre["h_pre"][l], Xs)  # dense read of the current state
-        got = O.xhc_flash_input(l, pre["F_pre"][l], pre["h_pre"][l], idx, H_post, F_outs)
+        got = O.xhc_flash_input(l, pre["F_pre"][l], pre["h_pre"][l], idx, H_post, W)
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
         XA = Xs[rows, idx]
-        for a in range(k):
-            upd = H_post[:, a, l, None] * F_outs[:, l]
-            if l < L - 1:
-                XA[:, a] = XA[:, a] + upd
-        if l == L - 1:
+        if l < L - 1:
+            for a in range(k):
+                XA[:, a] = XA[:, a] + H_post[:, a, l, None] * F_outs[:, l]
+        else:
             mixed = np.zeros_like(XA)
             for a in range(k):
                 for b in range(k):
                     mixed[:, a] += H_res[:, a, b, None] * XA[:, b]
-                mixed[:, a] += H_post[:, a, l, None] * F_outs[:, l]
+                for r in range(K_last):
+                    mixed[:, a] += H_post[:, a, L - 1 + r, None] * last[:, r]
             XA = mixed
         Xs[rows, idx] = XA
-    np.testing.assert_allclose(O.xhc_flash_post(X0, idx, H_post, H_res, F_outs), Xs, rtol=1e-12, atol=1e-12)
+    got_X = O.xhc_flash_post(X0, idx, H_post, H_res, W, K_last=K_last)
+    np.testing.assert_allclose(got_X, Xs, rtol=1e-12, atol=1e-12)
     # rows outside the active set are the entry state's
     act = np.zeros((T, X0.shape[1]), bool)
     act[rows, idx] = True
-    np.testing.assert_array_equal(O.xhc_flash_post(X0, idx, H_post, H_res, F_outs)[~act], X0[~act])
+    np.testing.assert_array_equal(got_X[~act], X0[~act])
+    if L == 1:  # one augmented sublayer is xhc_route with the K_last components
+        X1, hp, hr = O.xhc_route(X0, idx, phi_act, b_act, 0.6, 0.9, last, 20)
+        np.testing.assert_allclose(got_X, X1, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(H_post, hp, rtol=1e-14)
 
 
 def test_flash_single_sublayer_is_xhc():
