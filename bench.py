@@ -326,35 +326,47 @@ def flash_bench(torch, hc, dev, reps: int = 10) -> dict:
     Xs = [rn(T, N, C).to(torch.bfloat16) for _ in range(3)]
     w_r = rn(N * C, N - m, std=(1.0 / (N * C)) ** 0.5)
     out = {}
-    for L in (2, 4):
+    B, S = 2, 4096
+    conv = torch.cat([rn(C, kk, std=(1.0 / kk) ** 0.5) for kk in (4, 8, 12)], 1).contiguous()
+    for L, K_last in ((2, 1), (4, 1), (2, 4)):
+        Kb = L - 1 + K_last
         phi_pre, b_pre = rn(L, N * C, N, std=0.02), torch.zeros(L, N, device=dev)
-        phi_act = rn(k * C, k * L + k * k, std=0.02)
-        b_act = torch.zeros(k * L + k * k, device=dev)
-        b_act[k * L:] = torch.eye(k, device=dev).flatten()
+        phi_act = rn(k * C, k * Kb + k * k, std=0.02)
+        b_act = torch.zeros(k * Kb + k * k, device=dev)
+        b_act[k * Kb:] = torch.eye(k, device=dev).flatten()
         F_outs = rn(T, L, C).to(torch.bfloat16)
+        W = F_outs if K_last == 1 else torch.cat([F_outs[:, :L - 1], F_outs[:, :1].expand(T, K_last, C)], 1).contiguous()
+        V = torch.empty(T, K_last, C, dtype=torch.bfloat16, device=dev)
+        F_last = F_outs[:, L - 1].contiguous()
+        wsa = (torch.empty(max(hc.xhc_augment_workspace_bytes(B, S, C, (4, 8, 12), torch.bfloat16), 1),
+                           dtype=torch.uint8, device=dev) if K_last > 1 else None)
         po = (torch.empty(T, k, dtype=torch.int32, device=dev), torch.empty(T, N - m, device=dev),
               torch.empty(L, T, N, device=dev), torch.empty(L, T, C, dtype=torch.bfloat16, device=dev))
-        mo = (torch.empty(T, k, L, device=dev), torch.empty(T, k, k, device=dev))
+        mo = (torch.empty(T, k, Kb, device=dev), torch.empty(T, k, k, device=dev))
         F_in = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
         wsp = torch.empty(hc.xhc_flash_pre_workspace_bytes(T, N, C, m, L, torch.bfloat16), dtype=torch.uint8,
                           device=dev)
-        wsm = torch.empty(hc.xhc_flash_maps_workspace_bytes(T, N, C, k, L, torch.bfloat16), dtype=torch.uint8,
+        wsm = torch.empty(hc.xhc_flash_maps_workspace_bytes(T, N, C, k, L, torch.bfloat16, K_last), dtype=torch.uint8,
                           device=dev)
-        wsq = torch.empty(hc.xhc_flash_post_workspace_bytes(T, k, L), dtype=torch.uint8, device=dev)
+        wsq = torch.empty(hc.xhc_flash_post_workspace_bytes(T, k, L, K_last), dtype=torch.uint8, device=dev)
 
         def block(i, ev=None):
             X = Xs[i % 3]
             idx, _, h_pre, F_pre = hc.xhc_flash_pre(X, phi_pre, b_pre, 0.01, w_r, k=k, m=m, out=po, workspace=wsp)
             if ev:
                 ev[1].record()
-            Hp, Hr = hc.xhc_flash_maps(X, idx, phi_act, b_act, 0.01, 0.01, L, out=mo, workspace=wsm)
+            Hp, Hr = hc.xhc_flash_maps(X, idx, phi_act, b_act, 0.01, 0.01, L, K_last=K_last, out=mo, workspace=wsm)
             if ev:
                 ev[2].record()
             for l in range(1, L):
-                hc.xhc_flash_input(l, F_pre[l], h_pre[l], idx, Hp, F_outs, out=F_in)
+                hc.xhc_flash_input(l, F_pre[l], h_pre[l], idx, Hp, W, K_last=K_last, out=F_in)
             if ev:
                 ev[3].record()
-            hc.xhc_flash_post(X, idx, Hp, Hr, F_outs, workspace=wsq)
+            if K_last > 1:  # the last sublayer's augmentation, read by the block end where it is written
+                hc.xhc_augment(F_last, conv, (4, 8, 12), B, S, out=V, workspace=wsa)
+                hc.xhc_flash_post(X, idx, Hp, Hr, W, K_last=K_last, W_last=V, workspace=wsq)
+            else:
+                hc.xhc_flash_post(X, idx, Hp, Hr, W, K_last=K_last, workspace=wsq)
 
         for i in range(3):
             block(i)
@@ -373,13 +385,18 @@ def flash_bench(torch, hc, dev, reps: int = 10) -> dict:
         e = 2
         alg = (T * N * C * e + L * T * C * e + T * k * C * e
                + sum((2 + l) * T * C * e for l in range(1, L))
-               + 2 * T * k * C * e + L * T * C * e)
-        out[f"L{L}"] = {"block_us": md[4] * 1e6, "per_sublayer_us": md[4] * 1e6 / L,
+               + 2 * T * k * C * e + Kb * T * C * e)
+        if K_last > 1:  # the augmentation reads the MLP output and writes its components
+            alg += T * C * e + K_last * T * C * e
+        out[f"L{L}" + ("_augmented_mlp" if K_last > 1 else "")] = {
+            "block_us": md[4] * 1e6, "per_sublayer_us": md[4] * 1e6 / L,
                         "xhc_flash_pre_us": md[0] * 1e6, "xhc_flash_maps_us": md[1] * 1e6,
                         "xhc_flash_input_us": md[2] * 1e6, "xhc_flash_post_us": md[3] * 1e6,
                         "algorithmic_bytes": alg, "achieved_GBps": alg / md[4] / 1e9,
                         "tokens_per_s_per_sublayer": T * L / md[4]}
-    return {"workload": "xHC-Flash N=16 k=4 m=2 C=4096 T=8192 bf16, blocks of L = 2 and 4 sublayers (K = 1 each)",
+    return {"workload": "xHC-Flash N=16 k=4 m=2 C=4096 T=8192 bf16, blocks of L = 2 and 4 sublayers (K = 1 each), "
+                        "and L = 2 with the MLP's K_r = 4 augmentation (2 sequences of 4096, kappa 4, 8, 12; the "
+                        "block end's time includes xhc_augment, whose output the block end reads as W_last)",
             **out}
 
 
@@ -654,6 +671,18 @@ def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0, single_se
                               "sample": f"{done1} tokens, {elapsed1:.1f} s, one BLAS thread"}}
 
 
+# The measurements besides the headline, by name (--only runs one of them alone).
+SECTIONS = {
+    "small_latency": lambda torch, hc, dev, args: small_latency_bench(torch, hc, dev),
+    "chain_C7168": lambda torch, hc, dev, args: chain_c7168_bench(torch, hc, dev),
+    "xhc": lambda torch, hc, dev, args: xhc_bench(torch, hc, dev, max(3, min(args.steps, 20)), 3),
+    "hc_baseline": lambda torch, hc, dev, args: hc_baseline_bench(torch, hc, dev),
+    "backward": lambda torch, hc, dev, args: backward_bench(torch, hc, dev),
+    "xhc_backward": lambda torch, hc, dev, args: xhc_backward_bench(torch, hc, dev),
+    "flash": lambda torch, hc, dev, args: flash_bench(torch, hc, dev),
+}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -661,6 +690,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-xhc", action="store_true", help="skip the xHC measurements")
+    ap.add_argument("--only", choices=sorted(SECTIONS) + ["mhc"], default=None,
+                    help="run one section only (for profiling one workload): mhc is the headline and its "
+                         "variants; the others print their own JSON object")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -673,6 +705,9 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only is not None and args.only != "mhc":
+        print(json.dumps({"section": args.only, args.only: SECTIONS[args.only](torch, hc, dev, args)}), flush=True)
+        return 0
     w = synth.WORKLOADS[WORKLOAD]
     T, n, C = w["T"], w["n"], w["C"]
     inp = synth.mhc_layer(w["seed"], 0, T, n, C, w["dtype"])
@@ -870,15 +905,11 @@ def main() -> int:
         "torch_copy_GBps": torch_copy_rate(torch, dev),
         "source_digest": digest,
     }
-    result["small_latency"] = small_latency_bench(torch, hc, dev)
-    if not args.no_xhc:
-        result["chain_C7168"] = chain_c7168_bench(torch, hc, dev)
-        result["xhc"] = xhc_bench(torch, hc, dev, max(3, min(args.steps, 20)), 3)
-        result["hc_baseline"] = hc_baseline_bench(torch, hc, dev)
-        result["backward"] = backward_bench(torch, hc, dev)
-        result["xhc_backward"] = xhc_backward_bench(torch, hc, dev)
-        result["flash"] = flash_bench(torch, hc, dev)
-    if not args.no_cpu_baseline:
+    if args.only is None:
+        for name in ("small_latency",) + (() if args.no_xhc else
+                                           ("chain_C7168", "xhc", "hc_baseline", "backward", "xhc_backward", "flash")):
+            result[name] = SECTIONS[name](torch, hc, dev, args)
+    if not args.no_cpu_baseline and args.only is None:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
     return 0

@@ -452,6 +452,9 @@ int xhc_augment_backward(const void* F_out, int dtype, int64_t B, int64_t S, int
  *   computed as one mix with the write maps E[:, j] = H_res H_post[:, j] (j < L-1)
  *   and E[:, j] = H_post[:, j] (j >= L-1) (kept in the workspace, T*k*Kb floats,
  *   xhc_flash_post_workspace_bytes); rows outside the active set untouched.
+ *   W_last: NULL, or the last sublayer's K_last components [T, K_last, C] kept
+ *   apart (e.g. xhc_augment's output as written): then they are read from W_last
+ *   and F_outs' rows L-1 .. Kb-1 are not read (F_outs keeps its [T, Kb, C] layout).
  * All: dtype HC_F32 or HC_BF16; float arrays 4-byte aligned, stream arrays aligned
  * to their element size, workspaces 256 bytes; outputs overlap no input, other
  * output or workspace (HC_ERR_ALIAS). Workspace queries: -1 for invalid sizes.
@@ -470,7 +473,7 @@ int xhc_flash_input(int dtype, int64_t T, int N, int64_t C, int k, int L, int K_
                     void* stream);
 int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L, int K_last);
 int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last, const int32_t* idx,
-                   const float* H_post, const float* H_res, const void* F_outs, void* workspace,
+                   const float* H_post, const float* H_res, const void* F_outs, const void* W_last, void* workspace,
                    int64_t workspace_bytes, void* stream);
 
 /* ----------------------------------------- HC baseline and gain diagnostic -- */

@@ -65,7 +65,7 @@ _SIGS = {
                                  _vp, _vp, _vp, _vp]),
     "xhc_flash_post_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_int, _c_int]),
     "xhc_flash_post": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
-                                _vp, _c_i64, _vp]),
+                                _vp, _vp, _c_i64, _vp]),
     "xhc_augment": (_c_int, [_vp, _c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_i64, _vp]),
     "xhc_backward_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_route_backward": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _vp, _vp, _vp, _c_float, _c_float,
@@ -610,10 +610,12 @@ def xhc_flash_post_workspace_bytes(T: int, k: int, L: int, K_last: int = 1) -> i
     return int(lib().xhc_flash_post_workspace_bytes(T, k, L, K_last))
 
 
-def xhc_flash_post(X, idx, H_post, H_res, F_outs, *, K_last=1, workspace=None, stream=None):
+def xhc_flash_post(X, idx, H_post, H_res, F_outs, *, K_last=1, W_last=None, workspace=None, stream=None):
     """Block end in place on X [T, N, C] from the entry state's active rows and the
     write-back components F_outs [T, Kb, C] (the earlier sublayers' outputs, then the
-    last sublayer's K_last components; Kb = H_post.shape[2]). Returns X."""
+    last sublayer's K_last components; Kb = H_post.shape[2]), or with the last
+    sublayer's components in W_last [T, K_last, C] (F_outs' last K_last rows then
+    unread). Returns X."""
     X = _state(X)
     T, N, C = X.shape
     dev = X.device
@@ -625,10 +627,11 @@ def xhc_flash_post(X, idx, H_post, H_res, F_outs, *, K_last=1, workspace=None, s
     idx = _i32(idx, "idx", (T, k), dev)
     H_res = _f32(H_res, "H_res", (T, k, k), dev)
     F_outs = _dev_tensor(F_outs, "F_outs", (X.dtype,), (T, Kb, C), dev)
+    W_last = None if W_last is None else _dev_tensor(W_last, "W_last", (X.dtype,), (T, K_last, C), dev)
     ws = _workspace(xhc_flash_post_workspace_bytes(T, k, L, K_last), dev, workspace)
     _check("xhc_flash_post", lib().xhc_flash_post(_ptr(X), _DT[X.dtype], T, N, C, k, L, K_last, _ptr(idx),
-                                                  _ptr(H_post), _ptr(H_res), _ptr(F_outs), _ptr(ws), _nbytes(ws),
-                                                  _stream(dev, stream)))
+                                                  _ptr(H_post), _ptr(H_res), _ptr(F_outs), _ptr(W_last), _ptr(ws),
+                                                  _nbytes(ws), _stream(dev, stream)))
     return X
 
 

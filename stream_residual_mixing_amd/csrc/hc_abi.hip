@@ -1023,7 +1023,7 @@ int64_t xhc_flash_post_workspace_bytes(int64_t T, int k, int L, int K_last) {
 }
 
 int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L, int K_last, const int32_t* idx,
-                   const float* H_post, const float* H_res, const void* F_outs, void* workspace,
+                   const float* H_post, const float* H_res, const void* F_outs, const void* W_last, void* workspace,
                    int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
   if (T < 0 || C < 1 || C > (1ll << 26) || N < 1 || N > HC_MAX_STREAMS || k < 1 || k > N || k > HC_MAX_ACTIVE ||
@@ -1034,26 +1034,29 @@ int xhc_flash_post(void* X, int dtype, int64_t T, int N, int64_t C, int k, int L
   if (T == 0) return HC_OK;
   if (!X || !idx || !H_post || !H_res || !F_outs) return HC_ERR_NULL;
   const size_t es = esize(dtype);
-  if (!aligned_to(X, es) || !aligned_to(F_outs, es) || !aligned_to(idx, 4) || !aligned_to(H_post, 4) ||
-      !aligned_to(H_res, 4))
+  if (!aligned_to(X, es) || !aligned_to(F_outs, es) || (W_last && !aligned_to(W_last, es)) || !aligned_to(idx, 4) ||
+      !aligned_to(H_post, 4) || !aligned_to(H_res, 4))
     return HC_ERR_ALIGN;
   const int64_t wsb = align256(T * k * L * 4);
   if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
   const void* outs[2] = {X, workspace};
   const int64_t ob[2] = {T * N * C * (int64_t)es, wsb};
-  const void* ins[4] = {idx, H_post, H_res, F_outs};
-  const int64_t ib[4] = {T * k * 4, T * k * L * 4, T * k * k * 4, T * L * C * (int64_t)es};
-  if (any_overlap(outs, ob, 2, ins, ib, 4)) return HC_ERR_ALIAS;
+  const void* ins[5] = {idx, H_post, H_res, F_outs, W_last};
+  const int64_t ib[5] = {T * k * 4, T * k * L * 4, T * k * k * 4, T * L * C * (int64_t)es,
+                         T * K_last * C * (int64_t)es};
+  if (any_overlap(outs, ob, 2, ins, ib, 5)) return HC_ERR_ALIAS;
   int s = device_status();
   if (s != HC_OK) return s;
   hipStream_t st = (hipStream_t)stream;
   float* E = (float*)workspace;
   hipError_t e = hc::launch_flash_post_maps(T, k, Lsub, L, H_post, H_res, E, st);
   if (e != hipSuccess) return HC_ERR_LAUNCH;
-  if (hc::fast_mix_supported(dtype, k, L, C, X, F_outs))
-    return launch_status(hc::launch_fast_mix(X, T, N, C, idx, H_res, E, F_outs, L, st));
-  return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, F_outs}), X, T, N, C, k, idx, H_res, E, F_outs, L,
-                                              st));
+  // the last sublayer's components from W_last when given (component rows Lsub - 1 ..)
+  const int j0 = W_last ? Lsub - 1 : L;
+  if (hc::fast_mix_supported(dtype, k, L, C, X, F_outs) && (!W_last || hc::fast_mix_supported(dtype, k, L, C, X, W_last)))
+    return launch_status(hc::launch_fast_mix(X, T, N, C, idx, H_res, E, F_outs, L, st, W_last, j0));
+  return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, F_outs, W_last}), X, T, N, C, k, idx, H_res, E,
+                                              F_outs, L, st, W_last, j0));
 }
 
 static int augment_spec(int64_t B, int64_t S, int64_t C, const int* kappa, int r, hc::ConvSpec& spec,

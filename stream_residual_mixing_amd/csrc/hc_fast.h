@@ -135,7 +135,8 @@ hipError_t launch_copy_probe(const void* src, void* dst, int64_t bytes, hipStrea
 // (C % 8 == 0, X and Wb 16-byte aligned).
 bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const void* Wb);
 hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* idx, const float* H_res,
-                           const float* H_post, const void* Wb, int K, hipStream_t st);
+                           const float* H_post, const void* Wb, int K, hipStream_t st,
+                           const void* Wb2 = nullptr, int j0 = 0);
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
                                   const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
                                   float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,

@@ -462,6 +462,8 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
   // once half h is in LDS its slot is refilled with half h + 4, which for the
   // last 4 halves is one of the next item's first 4.
   constexpr bool DEEP = !POST && !(MODE == ROWS_GATHER && NB >= 4);  // (the latter has no registers left)
+  constexpr bool RED2 = (SWAVE * TILE * (NCP + 1) + SWAVE * TILE) * 4 > LBUF;
+  static_assert((SWAVE * TILE * (NCP + 1) + SWAVE * TILE) * 4 <= 2 * LBUF, "reduction buffer");
   static_assert(2 * SPI % 4 == 0, "queue slots of the deep prefetch");
   uint4 xq[DEEP ? 4 : 1][NS4];
   // DEEP: the B fragments of the super-chunk being multiplied. Each stream's are
@@ -602,10 +604,11 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
     }
     step += SPI;
     // ---- item end: cross-wave reduction into this thread's partial sums,
-    // through the buffer the last super-chunk's MFMA phase read
+    // through the buffer the last super-chunk's MFMA phase read (through both
+    // buffers when the partials of more than 32 columns do not fit one)
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds + ((step - 1) & 1) * LBUF);  // [SWAVE][TILE][NCP + 1]
-    float* ssr = red + SWAVE * TILE * (NCP + 1);                           // [SWAVE][TILE]
+    float* red = reinterpret_cast<float*>(RED2 ? lds : lds + ((step - 1) & 1) * LBUF);  // [SWAVE][TILE][NCP + 1]
+    float* ssr = red + SWAVE * TILE * (NCP + 1);                                        // [SWAVE][TILE]
     // lane holds D[m = q*4 + e][n = tau] of each block b, for token block tb
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -650,6 +653,7 @@ __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
       const int o = tid + u * STHR;
       pend[u] = reduce(o < PG::PART ? o : tid);
     }
+    if constexpr (RED2) __syncthreads();  // the next item's first half is written into buffer 0
     pitem = item;
     item = nitem_k;
     it = nx;
@@ -1399,20 +1403,22 @@ __global__ __launch_bounds__(256) void xroute_finish_kernel(const float* __restr
   const int64_t tile = tc / TILE;
   const int mrow = (int)(tc - tile * TILE);
   const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
-  const int kK = 4 * K;
-  const int cpost = e < kK ? e : 0;
-  float ss = 0.f, pr = 0.f, pp = 0.f;
+  const int kK = 4 * K;  // post entries: lane e takes e and, for K > 4, e + 16
+  const int cpost = e < kK ? e : 0, cpost2 = e + 16 < kK ? e + 16 : 0;
+  float ss = 0.f, pr = 0.f, pp = 0.f, pp2 = 0.f;
 #pragma unroll 4
   for (int it = 0; it < per_tile; ++it) {
     const float* b = base + (int64_t)it * PG::PART;
     ss += b[PG::NCOLP];
     pr += b[kK + e];
     pp += b[cpost];
+    if (PG::NCOLP > 32) pp2 += b[cpost2];
   }
   const float r = sqrtf(ss / (float)(4.0 * (double)C));
   const float invr = (r > 0.f) ? 1.0f / r : 0.f;
   const bool valid = tt < T;
   if (valid && e < kK) Hp[tt * kK + e] = 2.0f * sigmoid(a_post * (pp * invr) + b_act[e]);
+  if (valid && e + 16 < kK) Hp[tt * kK + e + 16] = 2.0f * sigmoid(a_post * (pp2 * invr) + b_act[e + 16]);
   const float z = a_res * (pr * invr) + b_act[kK + e];
   float zm = fmaxf(z, dpp<DPP_QXOR1>(z));
   zm = fmaxf(zm, dpp<DPP_QXOR2>(zm));
@@ -1577,12 +1583,17 @@ __global__ __launch_bounds__(256) void pre_wide_kernel(const uint16_t* __restric
 // unchanged. Blocks take the tokens from the last to the first: the projection
 // pass before read the gathered rows from the first token on, so the rows it
 // read last are read first here.
-template <int K>
+//
+// Components j >= j0 may come from a second array Wb2 [T, K - j0, C] (an
+// xHC-Flash block whose last sublayer's components are kept apart); rows j <
+// j0 are read from Wb [T, K, C].
+template <int K, bool SPLIT = false>
 __global__ __launch_bounds__(256) void mix4_kernel(uint16_t* X, int64_t T, int N, int64_t C,
                                                    const int32_t* __restrict__ idx,
                                                    const float* __restrict__ H_res,
                                                    const float* __restrict__ H_post,
-                                                   const uint16_t* __restrict__ Wb) {
+                                                   const uint16_t* __restrict__ Wb,
+                                                   const uint16_t* __restrict__ Wb2, int j0) {
   const int64_t nch = C / 8;
   const int64_t g = (int64_t)((int)gridDim.x - 1 - (int)blockIdx.x) * blockDim.x + threadIdx.x;
   if (g >= T * nch) return;
@@ -1600,7 +1611,8 @@ __global__ __launch_bounds__(256) void mix4_kernel(uint16_t* X, int64_t T, int N
 #pragma unroll
   for (int a = 0; a < 4; ++a) xr[a] = ld_stream(X + (t * N + s[a]) * C + c0);
 #pragma unroll
-  for (int j = 0; j < K; ++j) wr[j] = ld_stream(Wb + (t * K + j) * C + c0);
+  for (int j = 0; j < K; ++j)
+    wr[j] = ld_stream(!SPLIT || j < j0 ? Wb + (t * K + j) * C + c0 : Wb2 + (t * (K - j0) + (j - j0)) * C + c0);
   const float* hr = H_res + t * 16;
   const float* hp = H_post + t * 4 * K;
   float x[4][8], y[4][8];
@@ -1702,7 +1714,9 @@ hipError_t launch_split_nb(int nb, const SplitArgs& A, hipStream_t st) {
   switch (nb) {
     case 2: return launch_split<false, 2, MODE>(A, st);
     case 3: return launch_split<false, 3, MODE>(A, st);
-    default: return launch_split<false, 4, MODE>(A, st);
+    case 4: return launch_split<false, 4, MODE>(A, st);
+    case 5: if constexpr (MODE == ROWS_GATHER) return launch_split<false, 5, MODE>(A, st); else return hipErrorInvalidValue;
+    default: if constexpr (MODE == ROWS_GATHER) return launch_split<false, 6, MODE>(A, st); else return hipErrorInvalidValue;
   }
 }
 
@@ -1904,10 +1918,13 @@ XhcFastWs xhc_router_fast_ws(int64_t T, int N, int64_t C, int m, int dtype) {
   return {(int64_t)N * C / 8 * (nb * 16) * 16, part_bytes(T, C, N / 4, nb)};
 }
 
+// packed column blocks of the active-set projection: up to 48 columns (k = 4, K <= 8)
+static int nb_for_act(int ncols) { return ncols <= 32 ? nb_for(ncols) : (ncols + 7) / 8; }
+
 XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype) {
   const int ncols = k * K + k * k;
-  if (dtype != 1 || k != 4 || ncols > 32 || !shape_ok(T, C, 1, nb_for(ncols))) return {0, 0};
-  const int nb = nb_for(ncols);
+  if (dtype != 1 || k != 4 || ncols > 48 || !shape_ok(T, C, 1, nb_for_act(ncols))) return {0, 0};
+  const int nb = nb_for_act(ncols);
   return {(int64_t)k * C / 8 * (nb * 16) * 16, part_bytes(T, C, 1, nb)};
 }
 
@@ -2053,20 +2070,35 @@ bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const
 }
 
 hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* idx, const float* H_res,
-                           const float* H_post, const void* Wb, int K, hipStream_t st) {
+                           const float* H_post, const void* Wb, int K, hipStream_t st, const void* Wb2, int j0) {
   if (T == 0) return hipSuccess;
   const dim3 grid((unsigned)((T * (C / 8) + 255) / 256)), blk(256);
   uint16_t* x = (uint16_t*)X;
   const uint16_t* w = (const uint16_t*)Wb;
-  switch (K) {
-    case 1: hipLaunchKernelGGL(mix4_kernel<1>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    case 2: hipLaunchKernelGGL(mix4_kernel<2>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    case 3: hipLaunchKernelGGL(mix4_kernel<3>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    case 4: hipLaunchKernelGGL(mix4_kernel<4>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    case 5: hipLaunchKernelGGL(mix4_kernel<5>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    case 6: hipLaunchKernelGGL(mix4_kernel<6>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    case 7: hipLaunchKernelGGL(mix4_kernel<7>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
-    default: hipLaunchKernelGGL(mix4_kernel<8>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w); break;
+  const uint16_t* w2 = (const uint16_t*)Wb2;
+  if (!Wb2) j0 = K;
+  if (Wb2) {
+    switch (K) {
+      case 1: hipLaunchKernelGGL((mix4_kernel<1, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 2: hipLaunchKernelGGL((mix4_kernel<2, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 3: hipLaunchKernelGGL((mix4_kernel<3, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 4: hipLaunchKernelGGL((mix4_kernel<4, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 5: hipLaunchKernelGGL((mix4_kernel<5, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 6: hipLaunchKernelGGL((mix4_kernel<6, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 7: hipLaunchKernelGGL((mix4_kernel<7, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      default: hipLaunchKernelGGL((mix4_kernel<8, true>), grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+    }
+  } else {
+    switch (K) {
+      case 1: hipLaunchKernelGGL(mix4_kernel<1>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 2: hipLaunchKernelGGL(mix4_kernel<2>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 3: hipLaunchKernelGGL(mix4_kernel<3>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 4: hipLaunchKernelGGL(mix4_kernel<4>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 5: hipLaunchKernelGGL(mix4_kernel<5>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 6: hipLaunchKernelGGL(mix4_kernel<6>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      case 7: hipLaunchKernelGGL(mix4_kernel<7>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+      default: hipLaunchKernelGGL(mix4_kernel<8>, grid, blk, 0, st, x, T, N, C, idx, H_res, H_post, w, w2, j0); break;
+    }
   }
   return hipGetLastError();
 }
@@ -2076,8 +2108,19 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
                                   float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,
                                   uint4* phi_rows) {
   const int ncols = 4 * K + 16;
-  const int nb = nb_for(ncols);
-  hipError_t e = launch_pack(phi_act, ncols, nullptr, 0, 4 * C, nb * 8, packed, st, phi_rows);
+  const int nb = nb_for_act(ncols);
+  hipError_t e;
+  if (ncols <= 32) {
+    e = launch_pack(phi_act, ncols, nullptr, 0, 4 * C, nb * 8, packed, st, phi_rows);
+  } else {  // more columns than the two-source pack holds (no row form: the backward takes K <= 4)
+    PackSrcs S{};
+    S.p[0] = phi_act;
+    S.nc[0] = ncols;
+    S.ns = 1;
+    hipLaunchKernelGGL(pack_phi_multi_kernel, dim3((unsigned)(4 * C / 64)), dim3(256), 0, st, S, nb * 8,
+                       (uint16_t*)packed);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const Geom g = geom(T, C, 1, TILE);
   SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);
@@ -2087,12 +2130,16 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
   if ((e = launch_split_nb<ROWS_GATHER>(nb, A, st)) != hipSuccess) return e;
   const int64_t threads = T * 16;
   const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
-  if (nb == 3)
-    hipLaunchKernelGGL(xroute_finish_kernel<3>, grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, iters,
-                       Hp, Hr);
-  else
-    hipLaunchKernelGGL(xroute_finish_kernel<4>, grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, iters,
-                       Hp, Hr);
+#define HC_XRF(NB) \
+  hipLaunchKernelGGL(xroute_finish_kernel<NB>, grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, iters, \
+                     Hp, Hr)
+  switch (nb) {
+    case 3: HC_XRF(3); break;
+    case 4: HC_XRF(4); break;
+    case 5: HC_XRF(5); break;
+    default: HC_XRF(6); break;
+  }
+#undef HC_XRF
   return hipGetLastError();
 }
 

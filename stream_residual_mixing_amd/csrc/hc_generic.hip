@@ -264,7 +264,7 @@ template <typename T, int KA, bool VEC>
 __global__ __launch_bounds__(256) void mix_generic_kernel(
     T* X, int64_t T_, int N, int64_t C, const int32_t* __restrict__ idx,
     const float* __restrict__ H_res, const float* __restrict__ H_post,
-    const T* __restrict__ Wb, int K) {
+    const T* __restrict__ Wb, int K, const T* __restrict__ Wb2, int j0) {  // rows j >= j0 from Wb2 [T_, K - j0, C]
   const int64_t nch = (C + 7) / 8;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= T_ * nch) return;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void mix_generic_kernel(
   }
   for (int j = 0; j < K; ++j) {
     float wv[8];
-    const T* p = Wb + (t * K + j) * C + c0;
+    const T* p = j < j0 ? Wb + (t * K + j) * C + c0 : Wb2 + (t * (K - j0) + (j - j0)) * C + c0;
     if (VEC) load8(p, wv); else load8_tail(p, cnt, wv);
 #pragma unroll
     for (int a = 0; a < KA; ++a) {
@@ -474,22 +474,24 @@ hipError_t launch_post_generic(int dtype, bool vec, const void* X, int64_t T_, i
 template <typename T, int KA>
 static void mix_dispatch_vec(bool vec, void* X, int64_t T_, int N, int64_t C, const int32_t* idx,
                              const float* H_res, const float* H_post, const void* Wb, int K,
-                             hipStream_t st) {
+                             hipStream_t st, const void* Wb2, int j0) {
   const int64_t work = T_ * ((C + 7) / 8);
   const dim3 g(grid1(work, 256)), b(256);
   if (vec)
-    hipLaunchKernelGGL((mix_generic_kernel<T, KA, true>), g, b, 0, st, (T*)X, T_, N, C, idx, H_res, H_post, (const T*)Wb, K);
+    hipLaunchKernelGGL((mix_generic_kernel<T, KA, true>), g, b, 0, st, (T*)X, T_, N, C, idx, H_res, H_post, (const T*)Wb, K,
+                       (const T*)Wb2, j0);
   else
-    hipLaunchKernelGGL((mix_generic_kernel<T, KA, false>), g, b, 0, st, (T*)X, T_, N, C, idx, H_res, H_post, (const T*)Wb, K);
+    hipLaunchKernelGGL((mix_generic_kernel<T, KA, false>), g, b, 0, st, (T*)X, T_, N, C, idx, H_res, H_post, (const T*)Wb, K,
+                       (const T*)Wb2, j0);
 }
 
 template <typename T>
 static void mix_dispatch_k(int k, bool vec, void* X, int64_t T_, int N, int64_t C,
                            const int32_t* idx, const float* H_res, const float* H_post,
-                           const void* Wb, int K, hipStream_t st) {
+                           const void* Wb, int K, hipStream_t st, const void* Wb2, int j0) {
   switch (k) {
 #define HC_MIX_CASE(KA) \
-  case KA: mix_dispatch_vec<T, KA>(vec, X, T_, N, C, idx, H_res, H_post, Wb, K, st); break;
+  case KA: mix_dispatch_vec<T, KA>(vec, X, T_, N, C, idx, H_res, H_post, Wb, K, st, Wb2, j0); break;
     HC_MIX_CASE(1) HC_MIX_CASE(2) HC_MIX_CASE(3) HC_MIX_CASE(4)
     HC_MIX_CASE(5) HC_MIX_CASE(6) HC_MIX_CASE(7) HC_MIX_CASE(8)
     HC_MIX_CASE(9) HC_MIX_CASE(10) HC_MIX_CASE(11) HC_MIX_CASE(12)
@@ -501,10 +503,11 @@ static void mix_dispatch_k(int k, bool vec, void* X, int64_t T_, int N, int64_t 
 
 hipError_t launch_mix_generic(int dtype, bool vec, void* X, int64_t T_, int N, int64_t C, int k,
                               const int32_t* idx, const float* H_res, const float* H_post,
-                              const void* Wb, int K, hipStream_t st) {
+                              const void* Wb, int K, hipStream_t st, const void* Wb2, int j0) {
   if (T_ == 0) return hipSuccess;
-  if (dtype == 0) mix_dispatch_k<float>(k, vec, X, T_, N, C, idx, H_res, H_post, Wb, K, st);
-  else mix_dispatch_k<bf16_t>(k, vec, X, T_, N, C, idx, H_res, H_post, Wb, K, st);
+  if (!Wb2) j0 = K;
+  if (dtype == 0) mix_dispatch_k<float>(k, vec, X, T_, N, C, idx, H_res, H_post, Wb, K, st, Wb2, j0);
+  else mix_dispatch_k<bf16_t>(k, vec, X, T_, N, C, idx, H_res, H_post, Wb, K, st, Wb2, j0);
   return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ hipError_t launch_post_generic(int dtype, bool vec, const void* X, int64_t T, in
                                hipStream_t st);
 hipError_t launch_mix_generic(int dtype, bool vec, void* X, int64_t T, int N, int64_t C, int k,
                               const int32_t* idx, const float* H_res, const float* H_post,
-                              const void* Wb, int K, hipStream_t st);
+                              const void* Wb, int K, hipStream_t st, const void* Wb2 = nullptr, int j0 = 0);
 int64_t augment_generic_lds_bytes(int r, int64_t C);
 hipError_t launch_augment_generic(int dtype, int vdtype, const void* F, int64_t B, int64_t S,
                                   int64_t C, const float* w, const ConvSpec& spec, void* V,

@@ -408,11 +408,13 @@ def test_flash_validation(hc):
 
     def post(Lb=Ls, Kl=1, wsb=wsq, **kw):
         p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(["X", "idx", "Hp", "Hr", "Fo", "ws"])}
-        return L.xhc_flash_post(p["X"], 1, T, N, C, k, Lb, Kl, p["idx"], p["Hp"], p["Hr"], p["Fo"], p["ws"], wsb,
-                                None)
+        return L.xhc_flash_post(p["X"], 1, T, N, C, k, Lb, Kl, p["idx"], p["Hp"], p["Hr"], p["Fo"],
+                                kw.get("Wl"), p["ws"], wsb, None)
     assert post(Lb=5) == -2 and post(Kl=0) == -2
     assert post(Kl=4) == -8  # the workspace holds T k (L - 1 + K_last) maps
     for nm in ("X", "idx", "Hp", "Hr", "Fo"):
         assert post(**{nm: None}) == -1, nm
     assert post(ws=None) == -8 and post(wsb=wsq - 1) == -8
     assert post(ws=ctypes.c_void_p(0x1000000)) == -5  # workspace inside X
+    assert post(Wl=ctypes.c_void_p(0x9000001)) == -4  # W_last misaligned
+    assert post(Wl=ctypes.c_void_p(0x1000000)) == -5  # W_last inside X

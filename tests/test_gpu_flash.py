@@ -85,6 +85,14 @@ def _run_and_check(inp, k, m, L, sample=None, K_last=1, seqs=1):
     if K_last > 1:
         refV = O.xhc_augment(inp["F_outs"].values[:, L - 1], inp["conv_w"], seqs, T // seqs)
         check_stream("V of the last sublayer", inp["X"].dtype, sl(host64(V)), sl(refV))
+        # the same block end with the last sublayer's components kept apart (W_last): the
+        # rows of W they replace are not read, and the state is bit-identical
+        Wz = W.clone()
+        Wz[:, L - 1:] = float("nan")
+        Xq = X.clone()
+        hc.xhc_flash_post(Xq, idx, Hp, Hr, Wz, K_last=K_last, W_last=V)
+        torch.cuda.synchronize()
+        assert torch.equal(Xq, Xp)
     dt = inp["X"].dtype
     Xv = sl(inp["X"].values)
     pre = O.xhc_flash_pre(Xv, list(inp["phi_pre"]), list(inp["b_pre"]), a, inp["w_router"], k, m)
