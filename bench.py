@@ -150,14 +150,14 @@ def backward_algorithmic_bytes(T: int, n: int, C: int, esize: int = 2) -> dict:
     dphi, float32 map gradients dh [T, n*n + 2n]): 'one_pass': read x, dX_next,
     F_out, dF_in and write dX, dF_out once, phi read and dphi written once;
     'by_design': what the launches move (post stage: x, dX_next, F_out read, dF_out
-    written; main stage: x read by the projection, the dH_pre sums, the dX pass
-    and the dphi pass, dF_in by the sums and the dX pass, dX_next by the dX pass,
-    dX written)."""
+    written; main stage: x read by the projection (which also forms the dH_pre
+    sums), the dX pass and the dphi pass, dF_in by the projection and the dX
+    pass, dX_next by the dX pass, dX written)."""
     s, f = n * C * esize, C * esize
     phi_b = n * C * (n * n + 2 * n) * 4
     dh_b = (n * n + 2 * n) * 4
     post = s + s + f + f + dh_b
-    main = 4 * s + 2 * f + s + s + dh_b
+    main = 3 * s + 2 * f + s + s + dh_b
     return {"one_pass": T * (3 * s + 3 * f) + 2 * phi_b,
             "by_design": T * (post + main) + 2 * phi_b,
             "post_stage": T * post, "main_stage": T * main + 2 * phi_b}

@@ -11,17 +11,18 @@
 //    token dh[4:24] = [dH_post | dH_res] (sums over the channels);
 //  main stage (once dF_in is known):
 //  1. phi packed in two forms (projection and dP phi^T operands) and the
-//     projection partials of X by the forward's kernel (hc_fused.hip);
-//  2. bwd_pre_sums_kernel: per token dh[0:4] = dH_pre (sums over the channels);
-//  3. bwd_coeff_kernel (hc_fused.hip, beside the forward finish whose floats it
-//     recomputes): gates and Sinkhorn backward -> dP, g2, sums over groups of
-//     16 tokens, and the forward's h_pre and h_res;
-//  4. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
+//     projection partials of X by the forward's kernel (hc_fused.hip), with
+//     the partial sums of dh[0:4] = dH_pre = <dF_in, x_i> formed from the same
+//     tiles of X (dF_in read beside them);
+//  2. bwd_coeff_kernel (hc_fused.hip, beside the forward finish whose floats it
+//     recomputes): dH_pre summed into dh, gates and Sinkhorn backward -> dP,
+//     g2, sums over groups of 16 tokens, and the forward's h_pre and h_res;
+//  3. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
 //     dP phi^T product on MFMA, and (xHC route and pre modes) from the same
 //     tiles of x the dphi partials vec(x)^T dP over groups of token tiles on
 //     MFMA (the tokens are the K dimension);
-//  5. bwd_dphi_kernel (n = 4 mHC): the same dphi partials in a pass of their own;
-//  6. bwd_sums_kernel: the group partials of dphi and the sums of db and dalpha
+//  4. bwd_dphi_kernel (n = 4 mHC): the same dphi partials in a pass of their own;
+//  5. bwd_sums_kernel: the group partials of dphi and the sums of db and dalpha
 //     added in a fixed order.
 #include "hc.h"
 #include "hc_device.h"
@@ -179,46 +180,6 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const uint16_t* __restric
   }
   __syncthreads();
   if (tid < NA) dh[t * dhs + off + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
-}
-
-// One 256-thread workgroup per token t (main stage): dh[i] = dH_pre[i] =
-// <dF_in, x_i> for the NS streams of the token's row (dh rows of dhs floats),
-// summed as in bwd_post_kernel.
-template <int NS>
-__global__ __launch_bounds__(256) void bwd_pre_sums_kernel(const uint16_t* __restrict__ X,
-                                                           const uint16_t* __restrict__ dFi, int64_t C,
-                                                           float* __restrict__ dh, int dhs) {
-  __shared__ float wsum[4][NS];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  float acc[NS];
-#pragma unroll
-  for (int i = 0; i < NS; ++i) acc[i] = 0.f;
-  const int64_t nch = C / 8;
-  const uint16_t* xr = X + t * NS * C;
-  for (int64_t j = tid; j < nch; j += 256) {
-    const int64_t c = j * 8;
-    uint4 xq[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) xq[i] = ld_nt16(xr + i * C + c);
-    const uint4 gq = ld_nt16(dFi + t * C + c);
-    float x[8], g[8];
-    unpack_bf8(gq, g);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      unpack_bf8(xq[i], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i] += g[e] * x[e];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NS; ++k) acc[k] = wave_sum(acc[k]);
-  if ((tid & 63) == 0) {
-#pragma unroll
-    for (int k = 0; k < NS; ++k) wsum[tid >> 6][k] = acc[k];
-  }
-  __syncthreads();
-  if (tid < NS) dh[t * dhs + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
 // ------------------------------------------------------------------- dX
@@ -1253,8 +1214,7 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pby
 }
 
 BwdWs carve_mhc(void* ws, int64_t T, int64_t C, int64_t* total) {
-  return carve(ws, T, C, BS * C, BCOL, fast_coeffs_packed_bytes(4, C, 1), fast_coeffs_partial_bytes(T, 4, C, 1), 4,
-               false, total);
+  return carve(ws, T, C, BS * C, BCOL, fast_bwd_packed_bytes(C), fast_bwd_partial_bytes(T, C), 4, false, total);
 }
 // route with K components: phi_act [4C, 4K + 16] packed as NB = 3 (K = 1) or 4
 // (K = 4) blocks of 16 columns, hi and lo (2 x 8 NB 16-byte chunks per 8 rows)
@@ -1304,11 +1264,9 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
                                 void* ws, hipStream_t st) {
   const BwdWs w = carve_mhc(ws, T, C, nullptr);
   const uint16_t* x = (const uint16_t*)X;
-  hipError_t e = launch_fast_bwd_front(X, T, C, phi, w.packed, w.phi_rows, w.partial, st);
+  // the projection recompute also forms dH_pre from the same read of x
+  hipError_t e = launch_fast_bwd_front(X, T, C, phi, w.packed, w.phi_rows, w.partial, dF_in, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_pre_sums_kernel<4>, dim3((unsigned)T), dim3(256), 0, st, x, (const uint16_t*)dF_in, C, dh,
-                     BCOL);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                   w.h_pre, w.h_res, st)) != hipSuccess)
     return e;

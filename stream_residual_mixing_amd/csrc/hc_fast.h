@@ -77,13 +77,18 @@ hipError_t launch_fast_augment_backward(const void* F_out, int dtype, int64_t B,
 // Pieces of the backward in hc_fused.hip, beside the partial layout they read:
 //  front: phi packed for the projection (packed) and in the row form of the
 //    dP phi^T operand (phi_rows, 4C x 128 bytes), then the projection partials
-//    of X on 64-token items;
-//  coeffs: gates' and Sinkhorn's backward from dh [T, 24]: dP [T, 32], g2 [T],
+//    of X on 64-token items, which also carry the partial sums of
+//    dH_pre = <dF_in, x_i> taken from the same read of X;
+//  coeffs: gates' and Sinkhorn's backward from dh [T, 24] (dH_pre, columns 0..3,
+//    written here from the front's partials; dH_post and dH_res read from the
+//    post stage): dP [T, 32], g2 [T],
 //    the sums red [ceil(T / 16), 36] over groups of 16 tokens, and the
 //    forward's h_pre [T, 4] and h_res [T, 16]; dynamic LDS of iters * 1 KB
 //    (iters <= 64).
+int64_t fast_bwd_packed_bytes(int64_t C);
+int64_t fast_bwd_partial_bytes(int64_t T, int64_t C);
 hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const float* phi, void* packed,
-                                 uint4* phi_rows, float* partial, hipStream_t st);
+                                 uint4* phi_rows, float* partial, const void* dF_in, hipStream_t st);
 // xHC routed-step backward pieces: the gathered active set's coefficient
 // backward for K = 1 or 4 (partials of launch_fast_xhc_active, dh [T, 4K + 16] =
 // [dH_post | dH_res], h_res out), and the pre map's: the full-state projection of
@@ -102,7 +107,7 @@ hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, i
 int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K);
 int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C);
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
-                                  float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
+                                  float a_post, float a_res, int iters, float* dh, float* dP, float* g2,
                                   float* red, float* h_pre, float* h_res, hipStream_t st);
 
 // xHC fast paths (bfloat16 streams, C % 32 == 0). Workspace needs of each (all zero

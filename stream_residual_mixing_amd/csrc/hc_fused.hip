@@ -1054,10 +1054,14 @@ __global__ __launch_bounds__(256) void coeffs_finish_kernel(const float* __restr
 // LAY = K (1 or 4): the xHC active set (k = 4) with K write-back components,
 // columns [post 4K (a*K + j) | res 16] and dh [T, 4K + 16] in that order: lanes
 // e < 4K carry post column e, no pre map (h_pre is not written).
-template <int TT, int LAY>
+//
+// DHP (mHC): the partials come from proj_wide_kernel with DH (32 padded columns,
+// then ss and the 4 sums <dF_in, x_i> per item): dH_pre = those sums added over
+// the token's items in order, also stored into dh[:, 0:4].
+template <int TT, int LAY, bool DHP = false>
 __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict__ part, int64_t T, int64_t C, int S,
                                                         const float* __restrict__ bias, Gate gate, int iters,
-                                                        const float* __restrict__ dh, float* __restrict__ dP,
+                                                        float* __restrict__ dh, float* __restrict__ dP,
                                                         float* __restrict__ g2, float* __restrict__ red,
                                                         float* __restrict__ h_pre, float* __restrict__ h_res) {
   constexpr bool ROUTE = LAY != 0;
@@ -1065,8 +1069,9 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   constexpr int NGC = RES0;                  // gate (pre/post) columns before it
   constexpr int DHS = RES0 + 16;             // dh row length
   static_assert(NGC == 4 || NGC == 8 || NGC == 16, "gate columns");
+  static_assert(!DHP || !ROUTE, "the fused dH_pre sums are the mHC pre map's");
   extern __shared__ float it_lds[];  // [iters][256]
-  using PG = PartGeom<(DHS > 24 ? 4 : 3), TT>;
+  using PG = PartGeom<(DHP || DHS > 24 ? 4 : 3), TT, DHP ? NS4 : 0>;
   const int tid = threadIdx.x;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
   const int64_t tt = g >> 4;
@@ -1076,13 +1081,17 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   const int64_t tile = tc / TT;
   const int m = (int)(tc - tile * TT);
   const float* base = part + tile * S * PG::PART + m * PG::PROW;
-  float ss = 0.f, pr = 0.f, pe = 0.f;
+  float ss = 0.f, pr = 0.f, pe = 0.f, pd = 0.f;
 #pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float* b = base + (int64_t)s * PG::PART;
     ss += b[PG::NCOLP];
     pr += b[RES0 + e];
     pe += b[e & (NGC - 1)];
+    if constexpr (DHP) pd += b[PG::NCOLP + 1 + (e & 3)];
+  }
+  if constexpr (DHP) {
+    if (valid && e < 4) dh[tt * DHS + e] = pd;
   }
   const float invr = inv_rms4(ss, C);
   const float a = (ROUTE || e >= 4) ? gate.a_post : gate.a_pre;
@@ -1132,7 +1141,7 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   const float dz_res = G * M0;
   float dz_pp = 0.f;
   if (e < NGC) {
-    const float d = dh[tc * DHS + e];
+    const float d = DHP && e < 4 ? pd : dh[tc * DHS + e];
     dz_pp = ((!ROUTE && e < 4) ? d : 2.0f * d) * sg * (1.0f - sg);
   }
   // sums over the 16 lanes: quads, then the four quads (every lane gets the total)
@@ -1848,11 +1857,20 @@ hipError_t launch_fast_pack(const float* phi, int64_t C, void* packed, hipStream
   return launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st);
 }
 
+// The mHC backward's recompute of the projection, with dH_pre = <dF_in, x_i>
+// from the same read of the state: phi's 24 columns padded to 32 (hi and lo
+// sharing accumulators), the 4 sums as the partials' extra columns.
+int64_t fast_bwd_packed_bytes(int64_t C) { return (int64_t)NS4 * C / 8 * 64 * 16; }
+int64_t fast_bwd_partial_bytes(int64_t T, int64_t C) { return part_bytes(T, C, 1, 4, NS4); }
+
 hipError_t launch_fast_bwd_front(const void* X, int64_t T, int64_t C, const float* phi, void* packed,
-                                 uint4* phi_rows, float* partial, hipStream_t st) {
-  hipError_t e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 24, packed, st, phi_rows);
+                                 uint4* phi_rows, float* partial, const void* dF_in, hipStream_t st) {
+  hipError_t e = launch_pack(phi, NCOL, nullptr, 0, 4 * C, 32, packed, st, phi_rows);
   if (e != hipSuccess) return e;
-  return launch_wide<3, ROWS_CONTIG>(args(X, T, C, 4 * C, geom(T, C, 1, W_TOK), packed, partial), st);
+  SplitArgs A = args(X, T, C, 4 * C, geom(T, C, 1, W_TOK), packed, partial);
+  A.dF = (const uint16_t*)dF_in;
+  hipLaunchKernelGGL((proj_wide_kernel<4, ROWS_CONTIG, true, true>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st, A);
+  return hipGetLastError();
 }
 
 hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_t C, int K, const float* b_act,
@@ -1861,12 +1879,13 @@ hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_
   const dim3 grid((unsigned)((T * 16 + 255) / 256)), blk(256);
   const size_t lds = (size_t)iters * 256 * sizeof(float);
   const Gate gt{0.f, a_post, a_res};
+  float* dhm = const_cast<float*>(dh);  // read only: the route layouts write no dh
   if (K == 4)
     hipLaunchKernelGGL((bwd_coeff_kernel<TILE, 4>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
-                       iters, dh, dP, g2, red, nullptr, h_res);
+                       iters, dhm, dP, g2, red, nullptr, h_res);
   else
     hipLaunchKernelGGL((bwd_coeff_kernel<TILE, 1>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
-                       iters, dh, dP, g2, red, nullptr, h_res);
+                       iters, dhm, dP, g2, red, nullptr, h_res);
   return hipGetLastError();
 }
 
@@ -1893,10 +1912,10 @@ int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K) { return part_byt
 int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C) { return part_bytes(T, C, N / 4, 2, NS4); }
 
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
-                                  float a_post, float a_res, int iters, const float* dh, float* dP, float* g2,
+                                  float a_post, float a_res, int iters, float* dh, float* dP, float* g2,
                                   float* red, float* h_pre, float* h_res, hipStream_t st) {
   const int64_t threads = T * 16;
-  hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, 0>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, 0, true>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
                      (size_t)iters * 256 * sizeof(float), st, partial, T, C, (int)slices(C), bias,
                      Gate{a_pre, a_post, a_res}, iters, dh, dP, g2, red, h_pre, h_res);
   return hipGetLastError();
