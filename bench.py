@@ -42,6 +42,7 @@ if ROOT not in sys.path:
 
 METRIC = "tokens/s + achieved HBM GB/s (% peak), fused mHC n=4 C=4096 sublayer, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "mhc_n4_C4096_T8192_bf16"
 SINKHORN_ITERS = 20
 
@@ -211,7 +212,10 @@ def backward_bench(torch, hc, dev, reps: int = 10) -> dict:
             "algorithmic_bytes": bb["one_pass"], "achieved_GBps": bb["one_pass"] / t / 1e9,
             "pct_hbm_peak": 100.0 * bb["one_pass"] / t / 1e9 / HBM_PEAK_GBPS,
             "by_design_bytes": bb["by_design"], "by_design_GBps": bb["by_design"] / t / 1e9,
-            "post_stage_GBps": bb["post_stage"] / t_post / 1e9, "main_stage_GBps": bb["main_stage"] / t_main / 1e9}
+            "post_stage_GBps": bb["post_stage"] / t_post / 1e9, "main_stage_GBps": bb["main_stage"] / t_main / 1e9,
+            "counters": {"hc_backward_post": counter_summary(load_counters("hc_backward_post", source_digest()),
+                                                             t_post),
+                         "hc_backward": counter_summary(load_counters("hc_backward", source_digest()), t_main)}}
 
 
 def xhc_backward_bench(torch, hc, dev, reps: int = 10) -> dict:
@@ -306,7 +310,10 @@ def xhc_backward_bench(torch, hc, dev, reps: int = 10) -> dict:
     return {"workload": "xHC backward N=16 k=4 m=2 C=4096 T=8192 bf16: routed step (K=1) and augmented step (K=4, "
                         "B=2 S=4096, kappa 4,8,12); 20 Sinkhorn iterations recomputed",
             "tokens_per_s": T / (t_r + t_p), "us": (t_r + t_p) * 1e6,
-            "xhc_route_backward": rate(alg_r, t_r), "xhc_pre_backward": rate(alg_p, t_p),
+            "xhc_route_backward": dict(rate(alg_r, t_r), counters=counter_summary(
+                load_counters("xhc_route_backward", source_digest()), t_r)),
+            "xhc_pre_backward": dict(rate(alg_p, t_p), counters=counter_summary(
+                load_counters("xhc_pre_backward", source_digest()), t_p)),
             "augmented_us": (t_4 + t_a + t_p) * 1e6,
             "xhc_route_backward_K4": rate(alg_4, t_4), "xhc_augment_backward": rate(alg_a, t_a)}
 
@@ -482,6 +489,9 @@ def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
             "calls": {c: {"us": kern[c] * 1e6, "algorithmic_bytes": ab[c], "achieved_GBps": ab[c] / kern[c] / 1e9,
                           "pct_hbm_peak": 100.0 * ab[c] / kern[c] / 1e9 / HBM_PEAK_GBPS} for c in calls},
         }
+        if name == "routed_K1":
+            for c in calls:
+                out[name]["calls"][c]["counters"] = counter_summary(load_counters(c, source_digest()), kern[c])
     out["workload"] = ("xHC N=16 k=4 m=2 C=4096 T=8192 bf16 (K=1: F_out written back; K=4: B=2 S=4096 "
                        "augmentation, kappa 4,8,12); seeded synthetic device data; durations from HIP events")
     return out
@@ -532,7 +542,8 @@ def chain_c7168_bench(torch, hc, dev, layers: int = 8, rounds: int = 3) -> dict:
             "per_layer_us": t * 1e6, "p10_us": float(np.percentile(per, 10)) * 1e6,
             "p90_us": float(np.percentile(per, 90)) * 1e6, "tokens_per_s_per_layer": T / t,
             "chain_us": t * layers * 1e6, "algorithmic_bytes_per_layer": nb, "achieved_GBps": nb / t / 1e9,
-            "pct_hbm_peak": 100.0 * nb / t / 1e9 / HBM_PEAK_GBPS}
+            "pct_hbm_peak": 100.0 * nb / t / 1e9 / HBM_PEAK_GBPS,
+            "counters": counter_summary(load_counters("hc_post_pre_C7168", source_digest()), t)}
 
 
 def small_latency_bench(torch, hc, dev, reps: int = 50) -> dict:
@@ -622,16 +633,32 @@ def torch_copy_rate(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2.0 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-def load_traffic(kernel: str, digest: str):
+def load_counters(entry: str, digest: str):
+    """The rocprofv3 counter figures of one entry point (profiles/traffic.json),
+    or None when they were taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    ent = data.get(kernel)
+    ent = data.get(entry)
     if not ent or ent.get("source_digest") != digest:
         return None
-    return ent.get("bytes_per_launch")
+    return ent
+
+
+def counter_summary(ent, launch_s: float):
+    """HBM bytes by the two counter pairs and MFMA figures of one call, the rate
+    of its MFMA work taken over the live duration `launch_s`."""
+    if ent is None:
+        return None
+    return {"fetch_write_bytes": ent["bytes_per_launch"], "dram_bytes": ent["dram_bytes_per_launch"],
+            "dram_read_bytes": ent["dram_read_bytes"], "dram_write_bytes": ent["dram_write_bytes"],
+            "dram_over_algorithmic": ent["dram_bytes_per_launch"] / ent["algorithmic_bytes"],
+            "mfma_flops": ent["mfma_flops"], "mfma_tflops": ent["mfma_flops"] / launch_s / 1e12,
+            "mfma_frac_bf16_peak": ent["mfma_flops"] / launch_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "mfma_busy_frac": ent["mfma_busy_frac"], "kernels": ent["kernels"],
+            "source": "profiles/traffic.json (rocprofv3 --pmc runs named there)"}
 
 
 def cpu_baseline(min_seconds: float = 10.0, max_seconds: float = 30.0, single_seconds: float = 3.0) -> dict:
@@ -856,7 +883,8 @@ def main() -> int:
     dom = "hc_post_pre"
     dom_gbps = ab[dom] / kern[dom] / 1e9
     digest = source_digest()
-    traffic = load_traffic(dom, digest)
+    cnt = load_counters(dom, digest)
+    traffic = cnt["bytes_per_launch"] if cnt else None
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -882,7 +910,7 @@ def main() -> int:
                      "bound": "hbm",
                      "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dom_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom],
-                     "launch_us": kern[dom] * 1e6},
+                     "launch_us": kern[dom] * 1e6, "counters": counter_summary(cnt, kern[dom])},
         "headline_one_pass": {
             "bytes_per_step": one_pass, "achieved_GBps": one_pass / (wall / args.steps) / 1e9,
             "pct_hbm_peak": 100.0 * one_pass / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS,
