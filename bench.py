@@ -492,6 +492,36 @@ def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
         if name == "routed_K1":
             for c in calls:
                 out[name]["calls"][c]["counters"] = counter_summary(load_counters(c, source_digest()), kern[c])
+    # The chained form of the routed step: one xhc_route_pre call per sublayer (route
+    # of sublayer l, maps and pre-read of sublayer l + 1, the carry of l + 2), each
+    # state set carrying its own active set and carry from its previous step.
+    ws_c = torch.empty(hc.xhc_chain_workspace_bytes(T, N, C, k, m, 1, torch.bfloat16), dtype=torch.uint8, device=dev)
+    chain = []
+    for i in range(3):
+        r = hc.xhc_pre_chain(Xs[i], phi_pre, b_pre, 0.01, w_r, phi_pre, w_r, k=k, m=m, workspace=ws_c)
+        chain.append([r["idx"], r["carry"]])
+    fin_c = (torch.empty(T, N, device=dev), torch.empty(T, C, dtype=torch.bfloat16, device=dev))
+
+    def chained(i, evs):
+        st = chain[i % 3]
+        if evs:
+            evs[0].record()
+        r = hc.xhc_route_pre(Xs[i % 3], Fs[i % 3], phi1, b1, 0.01, 0.01, st[0], st[1], b_pre, 0.01,
+                             phi_pre_next=phi_pre, w_router_next=w_r, carry_out=st[1], k=k, m=m, out=fin_c,
+                             workspace=ws_c)
+        if evs:
+            evs[1].record()
+        st[0] = r["idx"]
+
+    wall, kern = run(chained, ["xhc_route_pre"])
+    step_bytes = ab1["xhc_pre"] + ab1["xhc_route"]
+    total = kern["xhc_route_pre"]
+    out["routed_K1_chained"] = {
+        "tokens_per_s": T / total, "us_per_step": total * 1e6, "wall_us_per_step": wall * 1e6,
+        "algorithmic_bytes_per_step": step_bytes, "achieved_GBps": step_bytes / total / 1e9,
+        "pct_hbm_peak": 100.0 * step_bytes / total / 1e9 / HBM_PEAK_GBPS,
+        "note": "xhc_route_pre per step (the same work as xhc_pre + xhc_route, the full state read once)",
+        "counters": counter_summary(load_counters("xhc_route_pre", source_digest()), total)}
     out["workload"] = ("xHC N=16 k=4 m=2 C=4096 T=8192 bf16 (K=1: F_out written back; K=4: B=2 S=4096 "
                        "augmentation, kappa 4,8,12); seeded synthetic device data; durations from HIP events")
     return out

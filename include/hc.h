@@ -315,6 +315,59 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
               void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * xHC chained sublayers - the pair xhc_route (sublayer l) + xhc_pre (sublayer
+ * l + 1) with one read of the full state per sublayer ([xHC] steps 1-3). The
+ * maps of sublayer l + 1 are linear in the state up to the RMS factor, and
+ * route l rewrites only its k active rows, so their projection splits into the
+ * rows route l leaves unchanged, projected while the call before read the
+ * whole state for sublayer l's pre-read (the "carry"), and the k rewritten rows,
+ * projected right after the mix; the sum of squares splits the same way. The
+ * outputs are those of xhc_route + xhc_pre on the same inputs, with sums added
+ * in another order.
+ *   xhc_pre_chain(... maps of sublayer 0 ..., phi_pre_next, w_router_next,
+ *     carry_out): xhc_pre of the first sublayer (with the router: idx, score
+ *     required), whose pre-read also forms carry_out for sublayer 1's maps
+ *     (phi_pre_next [N*C, N], w_router_next [N*C, N - m]).
+ *   xhc_route_pre(X, ..., idx_in, route of sublayer l ..., b_pre, alpha_pre of
+ *     sublayer l + 1, carry_in, phi_pre_next, w_router_next, carry_out, outputs
+ *     of l + 1): xhc_route with idx_in, then xhc_pre of sublayer l + 1 on the
+ *     updated state: idx_out, score_out, h_pre_out (each may be NULL except
+ *     idx_out), F_in. carry_in is the carry written by the call that produced
+ *     idx_in (xhc_pre_chain or the previous xhc_route_pre), on this state
+ *     unchanged since; it holds sublayer l + 1's phi_pre and w_router (packed)
+ *     with their partial projection. With phi_pre_next and w_router_next (the
+ *     maps of sublayer l + 2) carry_out is written for the next call, else (the
+ *     last sublayer) phi_pre_next, w_router_next and carry_out are NULL.
+ *     carry_out may be carry_in (the carry is read before it is written);
+ *     idx_out may be idx_in.
+ *   carry: xhc_chain_carry_bytes(T, N, C, k, m, dtype) bytes, 256-byte aligned,
+ *     opaque (per-item partial projections, float32, and the maps in the
+ *     projection's packed bfloat16 form).
+ *   Covered: dtype HC_BF16 (HC_F32 -> HC_ERR_DTYPE), N = 16, k = 4, 1 <= m <= 4,
+ *   C a multiple of 512, K <= 8, 1 <= sinkhorn_iters <= HC_MAX_ITERS (else
+ *   HC_ERR_SHAPE; xhc_chain_carry_bytes returns -1). X, Wb, F_in 16-byte
+ *   aligned, idx arrays 16-byte aligned, float arrays 4 (else HC_ERR_ALIGN);
+ *   workspace 256-byte aligned, at least xhc_chain_workspace_bytes. The carries
+ *   and outputs overlap no input (but as stated above) and no other output
+ *   (HC_ERR_ALIAS). idx_in must be an active set these calls produced (k
+ *   distinct streams per token, as the carry left out).
+ */
+int64_t xhc_chain_carry_bytes(int64_t T, int N, int64_t C, int k, int m, int dtype);
+int64_t xhc_chain_workspace_bytes(int64_t T, int N, int64_t C, int k, int m, int K, int dtype);
+int xhc_pre_chain(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+                  const float* phi_pre, const float* b_pre, float alpha_pre, const float* w_router,
+                  const float* phi_pre_next, const float* w_router_next,
+                  float* h_pre, void* F_in, int32_t* idx, float* score, void* carry_out,
+                  void* workspace, int64_t workspace_bytes, void* stream);
+int xhc_route_pre(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+                  const int32_t* idx_in, const float* phi_act, const float* b_act, float alpha_post,
+                  float alpha_res, int sinkhorn_iters, const void* Wb, int K,
+                  const float* b_pre, float alpha_pre, const void* carry_in,
+                  const float* phi_pre_next, const float* w_router_next, void* carry_out,
+                  float* h_post_out, float* h_res_out, int32_t* idx_out, float* score_out, float* h_pre_out,
+                  void* F_in, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * xhc_route_backward, xhc_pre_backward - gradients of the routed xHC step
  * (xhc_pre, then xhc_route with K = 1 or 4 write-back components), the
  * backward of [xHC] steps 2 and 3 with the parameterisation: on the active rows

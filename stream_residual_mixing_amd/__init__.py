@@ -54,6 +54,13 @@ _SIGS = {
     "xhc_route": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp,
                            _c_float, _c_float, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_i64,
                            _vp]),
+    "xhc_chain_carry_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
+    "xhc_chain_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _c_int]),
+    "xhc_pre_chain": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _c_float, _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "xhc_route_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _c_float,
+                               _c_float, _c_int, _vp, _c_int, _vp, _c_float, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "xhc_augment_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _vp, _c_int, _c_int, _c_int]),
     "xhc_flash_pre_workspace_bytes": (_c_i64, [_c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int]),
     "xhc_flash_pre": (_c_int, [_vp, _c_int, _c_i64, _c_int, _c_i64, _c_int, _c_int, _c_int, _vp, _vp, _c_float,
@@ -514,6 +521,114 @@ def xhc_route(X, Wb, phi_act, b_act, alpha_post, alpha_res, *, k=4, m=2, idx=Non
     return res
 
 
+def xhc_chain_carry_bytes(T: int, N: int, C: int, k: int, m: int, dtype) -> int:
+    """Bytes of the carry of the chained xHC calls, or -1 for a shape they do not cover."""
+    return int(lib().xhc_chain_carry_bytes(T, N, C, k, m, _DT[dtype]))
+
+
+def xhc_chain_workspace_bytes(T: int, N: int, C: int, k: int, m: int, K: int, dtype) -> int:
+    return int(lib().xhc_chain_workspace_bytes(T, N, C, k, m, K, _DT[dtype]))
+
+
+def _carry(t, name, nbytes, dev):
+    if nbytes < 0:
+        raise ValueError("the chained xHC calls do not cover this shape (bfloat16, N = 16, k = 4, m <= 4, "
+                         "C a multiple of 512)")
+    if t is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    t = _dev_tensor(t, name, (torch.uint8,), device=dev)
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, needs {nbytes}")
+    return t
+
+
+def xhc_pre_chain(X, phi_pre, b_pre, alpha_pre, w_router, phi_pre_next, w_router_next, *, k=4, m=2,
+                  carry_out=None, out=None, workspace=None, stream=None):
+    """xhc_pre of the first sublayer of a chain, whose pre-read also forms the carry of
+    the next sublayer's maps (phi_pre_next, w_router_next). out = (h_pre or None, F_in).
+    Returns dict(h_pre, F_in, idx, score, carry)."""
+    X = _state(X, dtypes=(torch.bfloat16,))
+    T, N, C = X.shape
+    dev = X.device
+    if not 1 <= m <= k <= N:
+        raise ValueError(f"need 1 <= m <= k <= N, got m={m} k={k} N={N}")
+    phi_pre = _f32(phi_pre, "phi_pre", (N * C, N), dev)
+    b_pre = _f32(b_pre, "b_pre", (N,), dev)
+    w_router = _f32(w_router, "w_router", (N * C, N - m), dev)
+    phi_pre_next = _f32(phi_pre_next, "phi_pre_next", (N * C, N), dev)
+    w_router_next = _f32(w_router_next, "w_router_next", (N * C, N - m), dev)
+    if out is not None:
+        h_pre = None if out[0] is None else _f32(out[0], "h_pre out", (T, N), dev)
+        F_in = _stream_out(out[1], "F_in out", (T, C), X.dtype, dev)
+    else:
+        h_pre = torch.empty(T, N, device=dev)
+        F_in = torch.empty(T, C, dtype=X.dtype, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    score = torch.empty(T, N - m, device=dev)
+    carry_out = _carry(carry_out, "carry_out", xhc_chain_carry_bytes(T, N, C, k, m, X.dtype), dev)
+    ws = _workspace(xhc_chain_workspace_bytes(T, N, C, k, m, 1, X.dtype), dev, workspace)
+    _check("xhc_pre_chain", lib().xhc_pre_chain(_ptr(X), _DT[X.dtype], T, N, C, k, m, _ptr(phi_pre), _ptr(b_pre),
+                                                float(alpha_pre), _ptr(w_router), _ptr(phi_pre_next),
+                                                _ptr(w_router_next), _ptr(h_pre), _ptr(F_in), _ptr(idx), _ptr(score),
+                                                _ptr(carry_out), _ptr(ws), _nbytes(ws), _stream(dev, stream)))
+    return dict(h_pre=h_pre, F_in=F_in, idx=idx, score=score, carry=carry_out)
+
+
+def xhc_route_pre(X, Wb, phi_act, b_act, alpha_post, alpha_res, idx, carry, b_pre, alpha_pre,
+                  *, phi_pre_next=None, w_router_next=None, carry_out=None, k=4, m=2, sinkhorn_iters=20,
+                  want_coeffs=False, out=None, workspace=None, stream=None):
+    """One chained step: xhc_route of sublayer l in place on X (active set idx, the
+    carry written with it), then xhc_pre of sublayer l + 1 (b_pre, alpha_pre; its
+    phi_pre and w_router came with the carry); with phi_pre_next and w_router_next
+    (sublayer l + 2's maps) also the carry for the next call (carry_out may be `carry`
+    itself). out = (h_pre or None, F_in). Returns dict(idx, score, h_pre, F_in,
+    carry[, h_post, h_res])."""
+    X = _state(X, dtypes=(torch.bfloat16,))
+    T, N, C = X.shape
+    dev = X.device
+    if not 1 <= m <= k <= N:
+        raise ValueError(f"need 1 <= m <= k <= N, got m={m} k={k} N={N}")
+    Wb, K = _write_back(Wb, T, C, (X.dtype,), dev)
+    nc = k * K + k * k
+    phi_act = _f32(phi_act, "phi_act", (k * C, nc), dev)
+    b_act = _f32(b_act, "b_act", (nc,), dev)
+    idx = _i32(idx, "idx", (T, k), dev)
+    b_pre = _f32(b_pre, "b_pre", (N,), dev)
+    nbytes = xhc_chain_carry_bytes(T, N, C, k, m, X.dtype)
+    if carry is None:
+        raise ValueError("xhc_route_pre needs the carry written with idx (xhc_pre_chain or the previous call)")
+    carry = _carry(carry, "carry", nbytes, dev)
+    nxt = phi_pre_next is not None or w_router_next is not None
+    if nxt:
+        if phi_pre_next is None or w_router_next is None:
+            raise ValueError("phi_pre_next and w_router_next go together")
+        phi_pre_next = _f32(phi_pre_next, "phi_pre_next", (N * C, N), dev)
+        w_router_next = _f32(w_router_next, "w_router_next", (N * C, N - m), dev)
+        carry_out = _carry(carry_out, "carry_out", nbytes, dev)
+    elif carry_out is not None:
+        raise ValueError("carry_out needs the next sublayer's maps (phi_pre_next, w_router_next)")
+    if out is not None:
+        h_pre = None if out[0] is None else _f32(out[0], "h_pre out", (T, N), dev)
+        F_in = _stream_out(out[1], "F_in out", (T, C), X.dtype, dev)
+    else:
+        h_pre = torch.empty(T, N, device=dev)
+        F_in = torch.empty(T, C, dtype=X.dtype, device=dev)
+    idx_out = torch.empty(T, k, dtype=torch.int32, device=dev)
+    score = torch.empty(T, N - m, device=dev)
+    hp = torch.empty(T, k, K, device=dev) if want_coeffs else None
+    hr = torch.empty(T, k, k, device=dev) if want_coeffs else None
+    ws = _workspace(xhc_chain_workspace_bytes(T, N, C, k, m, K, X.dtype), dev, workspace)
+    _check("xhc_route_pre", lib().xhc_route_pre(
+        _ptr(X), _DT[X.dtype], T, N, C, k, m, _ptr(idx), _ptr(phi_act), _ptr(b_act), float(alpha_post),
+        float(alpha_res), int(sinkhorn_iters), _ptr(Wb), K, _ptr(b_pre), float(alpha_pre), _ptr(carry),
+        _ptr(phi_pre_next), _ptr(w_router_next), _ptr(carry_out), _ptr(hp), _ptr(hr),
+        _ptr(idx_out), _ptr(score), _ptr(h_pre), _ptr(F_in), _ptr(ws), _nbytes(ws), _stream(dev, stream)))
+    res = dict(idx=idx_out, score=score, h_pre=h_pre, F_in=F_in, carry=carry_out)
+    if want_coeffs:
+        res.update(h_post=hp, h_res=hr)
+    return res
+
+
 def xhc_flash_pre_workspace_bytes(T: int, N: int, C: int, m: int, L: int, dtype) -> int:
     return int(lib().xhc_flash_pre_workspace_bytes(T, N, C, m, L, _DT[dtype]))
 
@@ -858,7 +973,8 @@ __all__ = [
     "xhc_route_backward", "xhc_pre_backward", "xhc_augment_backward_workspace_bytes", "xhc_augment_backward", "hc_post_coeffs", "hc_phi_packed_bytes", "hc_phi_pack", "hc_post_pre",
     "hc_post_pre_noalloc", "HC_NOALLOC_SCRATCH_BYTES",
     "xhc_pre_workspace_bytes", "xhc_pre", "xhc_route_workspace_bytes",
-    "xhc_route", "xhc_augment_workspace_bytes", "xhc_augment", "xhc_flash_pre_workspace_bytes", "xhc_flash_pre",
+    "xhc_route", "xhc_chain_carry_bytes", "xhc_chain_workspace_bytes", "xhc_pre_chain", "xhc_route_pre",
+    "xhc_augment_workspace_bytes", "xhc_augment", "xhc_flash_pre_workspace_bytes", "xhc_flash_pre",
     "xhc_flash_maps_workspace_bytes", "xhc_flash_maps", "xhc_flash_input", "xhc_flash_post_workspace_bytes",
     "xhc_flash_post", "hc_tanh_coeffs", "hc_amax_gain",
     "hc_static_maps", "hc_static_pre", "hc_static_post", "hc_copy_probe",

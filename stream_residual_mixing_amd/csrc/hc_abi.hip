@@ -152,7 +152,7 @@ const char* hc_status_string(int status) {
   }
 }
 
-int hc_version(void) { return 101; }
+int hc_version(void) { return 102; }
 
 int64_t hc_coeffs_workspace_bytes(int64_t T, int n, int64_t C, int dtype) {
   if (T < 0 || n < 1 || n > HC_MAX_MHC_STREAMS || C < 1 || !dtype_ok(dtype)) return -1;
@@ -836,6 +836,181 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
     return launch_status(hc::launch_fast_mix(X, T, N, C, idx_out, Hr, Hp, Wb, K, st));
   return launch_status(hc::launch_mix_generic(dtype, vec_ok(C, {X, Wb}), X, T, N, C, k, idx_out, Hr, Hp,
                                               Wb, K, st));
+}
+
+// ------------------------------------------------------ xHC chained step
+
+// Workspace of the chained calls: the packed maps (route, and each sublayer's
+// full-state maps in turn), the partials (route, projection, pairs in turn),
+// H_post, H_res, h_pre and score scratch, and the pair tables.
+struct ChainWs {
+  void* packed;
+  float *partial, *Hp, *Hr, *hp, *sc;
+  int32_t *ptok, *pos, *toff, *sortw;
+};
+
+static int64_t chain_ws(int64_t T, int N, int64_t C, int k, int m, int K, void* base, ChainWs* w) {
+  const hc::XhcChainWs c = hc::xhc_chain_ws(T, N, C, k);
+  const hc::XhcFastWs r = hc::xhc_route_fast_ws(T, C, k, K, HC_BF16);
+  const hc::XhcFastWs f = hc::xhc_pre_fast_ws(T, N, C, m, true, HC_BF16);
+  int64_t pk = c.packed, pt = c.pair_part;
+  pk = r.packed > pk ? r.packed : pk;
+  pk = f.packed > pk ? f.packed : pk;
+  pt = r.partial > pt ? r.partial : pt;
+  pt = f.partial > pt ? f.partial : pt;
+  const int64_t sz[10] = {pk, pt, T * k * K * 4, T * k * k * 4, T * N * 4, T * (N - m) * 4, c.ptok, c.pos,
+                          c.tile_off, c.sort};
+  char* p = (char*)base;
+  int64_t off = 0;
+  void* ptrs[10];
+  for (int i = 0; i < 10; ++i) {
+    ptrs[i] = p ? p + off : nullptr;
+    off += align256(sz[i]);
+  }
+  if (w) {
+    w->packed = ptrs[0];
+    w->partial = (float*)ptrs[1];
+    w->Hp = (float*)ptrs[2];
+    w->Hr = (float*)ptrs[3];
+    w->hp = (float*)ptrs[4];
+    w->sc = (float*)ptrs[5];
+    w->ptok = (int32_t*)ptrs[6];
+    w->pos = (int32_t*)ptrs[7];
+    w->toff = (int32_t*)ptrs[8];
+    w->sortw = (int32_t*)ptrs[9];
+  }
+  return off;
+}
+
+int64_t xhc_chain_carry_bytes(int64_t T, int N, int64_t C, int k, int m, int dtype) {
+  if (!dtype_ok(dtype) || !hc::xhc_chain_supported(dtype, T < 1 ? 1 : T, N, C, k, m)) return -1;
+  return hc::xhc_chain_carry_bytes(T, N, C);
+}
+
+int64_t xhc_chain_workspace_bytes(int64_t T, int N, int64_t C, int k, int m, int K, int dtype) {
+  if (!dtype_ok(dtype) || K < 1 || K > HC_MAX_COMPONENTS || !hc::xhc_chain_supported(dtype, T < 1 ? 1 : T, N, C, k, m))
+    return -1;
+  return chain_ws(T, N, C, k, m, K, nullptr, nullptr);
+}
+
+int xhc_pre_chain(const void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+                  const float* phi_pre, const float* b_pre, float alpha_pre, const float* w_router,
+                  const float* phi_pre_next, const float* w_router_next,
+                  float* h_pre, void* F_in, int32_t* idx, float* score, void* carry_out,
+                  void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (dtype != HC_BF16) return HC_ERR_DTYPE;
+  if (T < 0 || !hc::xhc_chain_supported(dtype, T < 1 ? 1 : T, N, C, k, m)) return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  if (!X || !phi_pre || !b_pre || !w_router || !phi_pre_next || !w_router_next || !F_in || !idx || !carry_out)
+    return HC_ERR_NULL;
+  if (!aligned_to(X, 16) || !aligned_to(F_in, 16) || !aligned_to(idx, 16) || !aligned_to(carry_out, 256) ||
+      !aligned_to(phi_pre, 4) || !aligned_to(b_pre, 4) || !aligned_to(w_router, 4) || !aligned_to(phi_pre_next, 4) ||
+      !aligned_to(w_router_next, 4) || (h_pre && !aligned_to(h_pre, 16)) || (score && !aligned_to(score, 4)))
+    return HC_ERR_ALIGN;
+  const int64_t wsb = chain_ws(T, N, C, k, m, 1, nullptr, nullptr);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int64_t NC = (int64_t)N * C, xb = T * NC * 2, cb = hc::xhc_chain_carry_bytes(T, N, C);
+  const void* outs[5] = {F_in, h_pre, idx, score, carry_out};
+  const int64_t ob[5] = {T * C * 2, T * N * 4, T * k * 4, T * (N - m) * 4, cb};
+  const void* ins[7] = {X, phi_pre, b_pre, w_router, phi_pre_next, w_router_next, workspace};
+  const int64_t ib[7] = {xb, NC * N * 4, N * 4, NC * (N - m) * 4, NC * N * 4, NC * (N - m) * 4, wsb};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return HC_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  }
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  ChainWs w;
+  chain_ws(T, N, C, k, m, 1, workspace, &w);
+  float* hp = h_pre ? h_pre : w.hp;
+  float* sc = score ? score : w.sc;
+  hipError_t e = hc::launch_fast_xhc_full(X, T, N, C, k, m, phi_pre, b_pre, alpha_pre, w_router, hp, sc, idx,
+                                          nullptr, w.packed, w.partial, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  // the next sublayer's maps, packed into the carry beside the partials the pre-read forms
+  void* cpk = (char*)carry_out + hc::xhc_chain_carry_part_bytes(T, N, C);
+  if ((e = hc::launch_fast_xhc_pack_full(phi_pre_next, w_router_next, N, m, C, cpk, st)) != hipSuccess)
+    return HC_ERR_LAUNCH;
+  return launch_status(hc::launch_fast_xhc_dense(X, T, N, C, hp, idx, cpk, F_in, (float*)carry_out, st));
+}
+
+int xhc_route_pre(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
+                  const int32_t* idx_in, const float* phi_act, const float* b_act, float alpha_post,
+                  float alpha_res, int sinkhorn_iters, const void* Wb, int K,
+                  const float* b_pre, float alpha_pre, const void* carry_in,
+                  const float* phi_pre_next, const float* w_router_next, void* carry_out,
+                  float* h_post_out, float* h_res_out, int32_t* idx_out, float* score_out, float* h_pre_out,
+                  void* F_in, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
+  if (dtype != HC_BF16) return HC_ERR_DTYPE;
+  if (T < 0 || K < 1 || K > HC_MAX_COMPONENTS || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS ||
+      !hc::xhc_chain_supported(dtype, T < 1 ? 1 : T, N, C, k, m) || hc::xhc_route_fast_ws(T < 1 ? 1 : T, C, k, K, dtype).packed == 0)
+    return HC_ERR_SHAPE;
+  if (T == 0) return HC_OK;
+  const bool next = phi_pre_next || w_router_next || carry_out;
+  if (!X || !idx_in || !phi_act || !b_act || !Wb || !b_pre || !carry_in || !idx_out || !F_in ||
+      (next && (!phi_pre_next || !w_router_next || !carry_out)))
+    return HC_ERR_NULL;
+  if (!aligned_to(X, 16) || !aligned_to(Wb, 16) || !aligned_to(F_in, 16) || !aligned_to(idx_in, 16) ||
+      !aligned_to(idx_out, 16) || !aligned_to(carry_in, 256) || (carry_out && !aligned_to(carry_out, 256)) ||
+      !aligned_to(phi_act, 4) || !aligned_to(b_act, 4) || !aligned_to(b_pre, 4) ||
+      (phi_pre_next && !aligned_to(phi_pre_next, 4)) ||
+      (w_router_next && !aligned_to(w_router_next, 4)) || (h_post_out && !aligned_to(h_post_out, 4)) ||
+      (h_res_out && !aligned_to(h_res_out, 4)) || (score_out && !aligned_to(score_out, 4)) ||
+      (h_pre_out && !aligned_to(h_pre_out, 16)))
+    return HC_ERR_ALIGN;
+  const int64_t wsb = chain_ws(T, N, C, k, m, K, nullptr, nullptr);
+  if (!workspace || !aligned_to(workspace, 256) || workspace_bytes < wsb) return HC_ERR_WORKSPACE;
+  const int acols = k * K + k * k;
+  const int64_t NC = (int64_t)N * C, xb = T * NC * 2, cb = hc::xhc_chain_carry_bytes(T, N, C);
+  // X is updated in place; carry_out may be carry_in and idx_out may be idx_in.
+  const void* outs[8] = {X, carry_out, h_post_out, h_res_out, idx_out, score_out, h_pre_out, F_in};
+  const int64_t ob[8] = {xb, cb, T * k * K * 4, T * k * k * 4, T * k * 4, T * (N - m) * 4, T * N * 4, T * C * 2};
+  const void* ins[9] = {idx_in, phi_act, b_act, Wb, b_pre, carry_in, phi_pre_next, w_router_next, workspace};
+  const int64_t ib[9] = {T * k * 4, (int64_t)k * C * acols * 4, acols * 4, T * K * C * 2, N * 4, cb,
+                         NC * N * 4, NC * (N - m) * 4, wsb};
+  for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 9; ++j) {
+      if (i == 1 && j == 5 && outs[i] == ins[j]) continue;  // carry_out == carry_in
+      if (i == 4 && j == 0 && outs[i] == ins[j]) continue;  // idx_out == idx_in
+      if (overlaps(outs[i], ob[i], ins[j], ib[j])) return HC_ERR_ALIAS;
+    }
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], ob[i], outs[j], ob[j])) return HC_ERR_ALIAS;
+  }
+  int s = device_status();
+  if (s != HC_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  ChainWs w;
+  chain_ws(T, N, C, k, m, K, workspace, &w);
+  float* Hp = h_post_out ? h_post_out : w.Hp;
+  float* Hr = h_res_out ? h_res_out : w.Hr;
+  float* hp = h_pre_out ? h_pre_out : w.hp;
+  float* sc = score_out ? score_out : w.sc;
+  // route l: the active set's maps from its rows, then the mix in place
+  hipError_t e = hc::launch_fast_xhc_active(X, T, N, C, idx_in, K, phi_act, b_act, alpha_post, alpha_res,
+                                            sinkhorn_iters, Hp, Hr, w.packed, w.partial, st);
+  if (e != hipSuccess) return HC_ERR_LAUNCH;
+  if ((e = hc::launch_fast_mix(X, T, N, C, idx_in, Hr, Hp, Wb, K, st)) != hipSuccess) return HC_ERR_LAUNCH;
+  // sublayer l + 1's maps (packed in the carry): the carry's partials plus the rewritten rows
+  const int64_t cpb = hc::xhc_chain_carry_part_bytes(T, N, C);
+  const void* pk1 = (const char*)carry_in + cpb;
+  if ((e = hc::launch_fast_xhc_chain_maps(X, T, N, C, k, m, idx_in, pk1, (const float*)carry_in, b_pre,
+                                          alpha_pre, hp, sc, idx_out, w.ptok, w.toff, w.pos, w.sortw, w.partial,
+                                          st)) !=
+      hipSuccess)
+    return HC_ERR_LAUNCH;
+  if (!next) return launch_status(hc::launch_fast_pre_wide(X, T, N, C, hp, F_in, st));
+  // the pre-read of sublayer l + 1, which also forms the carry of sublayer l + 2 (its maps
+  // packed first; in place, after the rewritten rows' pass has read the carried ones)
+  void* pk2 = (char*)carry_out + cpb;
+  if ((e = hc::launch_fast_xhc_pack_full(phi_pre_next, w_router_next, N, m, C, pk2, st)) != hipSuccess)
+    return HC_ERR_LAUNCH;
+  return launch_status(hc::launch_fast_xhc_dense(X, T, N, C, hp, idx_out, pk2, F_in, (float*)carry_out, st));
 }
 
 // ---------------------------------------------------------------- xHC-Flash

@@ -147,6 +147,37 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
                                   float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,
                                   uint4* phi_rows = nullptr);
 
+// xHC chained step (the route of sublayer l, then sublayer l + 1's maps and dense
+// read with one read of the full state): bfloat16, N = 16, k = 4, m <= k, C %
+// 512 == 0, 16-byte aligned state, h_pre [T, 16] and idx [T, 4].
+//  carry: per-item partials [pre N | router N - m] of sublayer l + 1's maps over
+//    the rows outside route l's active set (the first xhc_chain_carry_part_bytes),
+//    then those maps packed (xhc_chain_carry_bytes in all);
+//  pack_full: [phi_pre | w_router] of one sublayer in the projection's packed form;
+//  dense: F_in = sum_i h_pre_i x_i and the carry of the packed maps over the rows
+//    not in idx, one pass over the state;
+//  chain_maps: the active rows (idx_prev) after the mix grouped by stream and
+//    projected, added to the carry, then h_pre, score and idx of the next sublayer.
+struct XhcChainWs {
+  int64_t packed, pair_part, ptok, pos, tile_off, sort;
+};
+bool xhc_chain_supported(int dtype, int64_t T, int N, int64_t C, int k, int m);
+int64_t xhc_chain_carry_part_bytes(int64_t T, int N, int64_t C);
+int64_t xhc_chain_carry_bytes(int64_t T, int N, int64_t C);
+XhcChainWs xhc_chain_ws(int64_t T, int N, int64_t C, int k);
+// the full-state pre-read alone (N % 4 == 0, N <= 16, C % 8 == 0, 16-byte aligned X, F_in)
+hipError_t launch_fast_pre_wide(const void* X, int64_t T, int N, int64_t C, const float* h_pre, void* F_in,
+                               hipStream_t st);
+hipError_t launch_fast_xhc_pack_full(const float* phi_pre, const float* w_router, int N, int m, int64_t C,
+                                     void* packed, hipStream_t st);
+hipError_t launch_fast_xhc_dense(const void* X, int64_t T, int N, int64_t C, const float* h_pre, const int32_t* idx,
+                                 const void* packed, void* F_in, float* carry, hipStream_t st);
+hipError_t launch_fast_xhc_chain_maps(const void* X, int64_t T, int N, int64_t C, int k, int m,
+                                      const int32_t* idx_prev, const void* packed, const float* carry,
+                                      const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
+                                      int32_t* ptok, int32_t* tile_off, int32_t* pos, int32_t* sortw,
+                                      float* pair_part, hipStream_t st);
+
 // Temporal augmentation for kappa = {4, 8, 12} (C % 4 == 0; F_out and V aligned to 4
 // elements): conv + Gram pass, then Gram-Schmidt from the Gram matrices.
 bool fast_augment_supported(int dtype, int vdtype, int64_t S, int64_t C, const int* kappa, int r, const void* F,

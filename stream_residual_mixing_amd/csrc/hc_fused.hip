@@ -211,9 +211,20 @@ __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
 //                N = 4 NG), with phi rows of those streams;
 //   ROWS_GATHER: the streams idx[t, 0..3] of a token row (xHC active set), with
 //                phi rows of slots 0..3.
+//
+// proj_wide_kernel (64-token items) has two more:
+//   ROWS_DENSE: all 16 streams of the xHC full state, item = 64 tokens x 256
+//                channels of every stream group (the groups are the inner
+//                steps); it also forms the dense read F_in = sum_i h_pre_i x_i
+//                of the rows it streams, and leaves the rows idx[t, 0..3] out
+//                of the projection;
+//   ROWS_PAIRS:  one stream row per item token: token m of pair tile p is the
+//                row (ptok[64 p + m], bucket stream of the tile), its 4 quarter
+//                rows taking the place of the 4 streams (phi rows of that
+//                stream); ptok < 0 marks padding.
 constexpr int SPI = 4;                   // super-chunks per item
 constexpr int NCOEF = TILE * 20;         // h_res (16) | h_post (4) per token of a tile
-enum : int { ROWS_CONTIG = 0, ROWS_GROUPS = 1, ROWS_GATHER = 2 };
+enum : int { ROWS_CONTIG = 0, ROWS_GROUPS = 1, ROWS_GATHER = 2, ROWS_DENSE = 3, ROWS_PAIRS = 4 };
 
 template <int NB, int TT = TILE, int EX = 0>  // TT: tokens per item; EX: extra columns after ss
 struct PartGeom {
@@ -253,11 +264,17 @@ struct SplitArgs {
   const uint16_t* phi_p;   // packed phi, NB * 16 columns
   float* part;             // [nitem][tokens per item][PROW]
   const uint16_t* dF;      // proj_wide_kernel with DH: dF_in [T, C]
+  const float* hd;         // ROWS_DENSE: h_pre [T, 16] of the dense read
+  uint16_t* Fd;            // ROWS_DENSE: the dense read's output F_in [T, C]
+  const int32_t* ptok;     // ROWS_PAIRS: token of each pair [ntile * 64] (< 0: padding)
+  const int32_t* tile_off; // ROWS_PAIRS: [nstreams + 1] first pair tile of each stream's bucket
+  int64_t sq;              // ROWS_PAIRS: elements between consecutive streams of a token row
 };
 
 template <bool POST, int NB, int MODE>
 __global__ __launch_bounds__(STHR) void mhc_split_kernel(SplitArgs A) {
   static_assert(!POST || MODE == ROWS_CONTIG, "the post/res write is for the mHC state");
+  static_assert(MODE <= ROWS_GATHER, "dense and pair rows use proj_wide_kernel");
   static_assert(SPI >= 3, "the next item's stream table is written after the second super-chunk");
   using PG = PartGeom<NB>;
   constexpr int NCP = PG::NCP;
@@ -701,6 +718,12 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   static_assert(MODE != ROWS_GATHER, "gathered rows use mhc_split_kernel");
   static_assert(!SH || NB % 2 == 0, "shared accumulators pair hi block b with lo block b + NB / 2");
   static_assert(QD == 2 || QD == 4, "token halves in flight");
+  constexpr bool DENSE = MODE == ROWS_DENSE, PAIRS = MODE == ROWS_PAIRS;
+  static_assert(!(DH && (DENSE || PAIRS)), "the dF_in sums are for the stream-group and contiguous rows");
+  // DENSE: the 4 stream groups of one 128-channel super-chunk are consecutive
+  // steps, so an item covers W_SPI / 4 super-chunks of every group
+  constexpr int NGD = DENSE ? 4 : 1;
+  static_assert(W_SPI % NGD == 0, "steps per item");
   constexpr int NA = SH ? NB / 2 : NB;   // accumulator sets per token block
   static_assert(NA <= 5, "4 token blocks x more accumulator sets exceed the registers");
   using PG = PartGeom<NB, W_TOK, DH ? NS4 : 0>;
@@ -711,10 +734,15 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   constexpr int NR = W_TOK / TPR;                            // rounds
   constexpr int NPH = (TPR * PG::PROW + STHR - 1) / STHR;   // partial floats per thread per round
   static_assert(SWAVE * TPR * RS * 4 + SWAVE * TPR * 4 + TPR * NS4 * 4 <= W_LBUF, "reduction buffer");
-  static_assert(!DH || TPR == 32, "the dF_in sums are kept per 32-token half");
+  static_assert(!(DH || DENSE) || TPR == 32, "the dF_in sums and DENSE's sums of squares are kept per 32-token half");
   const uint16_t* X = A.X;
   const int64_t T = A.T, C = A.C;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * W_LBUF];
+  // Per-token tables of the item being streamed and of the next item: PAIRS, the
+  // pair tokens; DENSE, the tokens' h_pre (htab) and the mask of their active
+  // streams (ptab)
+  __shared__ int ptab[PAIRS || DENSE ? 2 * W_TOK : 1];
+  __shared__ __attribute__((aligned(16))) float htab[DENSE ? 2 * W_TOK * 16 : 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -725,6 +753,8 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   const int cgw = wave & 3, sp = wave >> 2;
   const int G = (int)gridDim.x;
   const int nk = (A.nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
+  // items per tile (DENSE: 256-channel steps of all groups, as many as the
+  // group x 1024-channel items of the other modes)
   const int per_tile = A.NG * A.S;
 
   floatx4_t acc[4][NA], gram[4];
@@ -737,6 +767,8 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   const __amdgpu_buffer_rsrc_t pres =
       __builtin_amdgcn_make_buffer_rsrc(A.part, 0, (uint32_t)((int64_t)A.nitem * PG::PART * 4), BUF_DW3);
 
+  // g: the stream group (GROUPS; DENSE steps set their own), or the bucket's
+  // stream (PAIRS)
   struct Item {
     int tile, g;
     int64_t s0;
@@ -744,19 +776,58 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   auto item_of = [&](int item) __attribute__((always_inline)) {
     const int tile = item / per_tile;
     const int r = item - tile * per_tile;
+    if constexpr (DENSE) return Item{tile, 0, (int64_t)r * (W_SPI / NGD)};
+    if constexpr (PAIRS) {
+      // the bucket holding pair tile `tile` (tiles past the last bucket: the last
+      // stream, their pairs are all padding)
+      int b = 0;
+      for (int z = 1; z < A.nstreams; ++z) b = A.tile_off[z] <= tile ? z : b;
+      return Item{tile, b, (int64_t)r * W_SPI};
+    }
     const int g = r / A.S;
     return Item{tile, g, (int64_t)(r - g * A.S) * W_SPI};
   };
+  // first stream of an item's rows at stream group g (GROUPS, DENSE)
+  auto stream0 = [&](int g) __attribute__((always_inline)) { return MODE == ROWS_GROUPS || DENSE ? 4 * g : 0; };
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   // Loads are unconditional (clamped rows and channels), as in mhc_split_kernel.
-  auto load_half = [&](const Item& it, int64_t s, auto P, uint4 (&xv)[NS4], uint4& dv) __attribute__((always_inline)) {
+  // Step js of an item: super-chunk s0 + js / NGD, stream group js % NGD (DENSE);
+  // pt: the item's PAIRS table.
+  auto load_half = [&](const Item& it, int js, const int* pt, auto P, uint4 (&xv)[NS4], uint4& dv)
+                       __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
-    int64_t t = (int64_t)it.tile * W_TOK + st_tok + 32 * p;
-    t = t < T ? t : T - 1;
+    const int64_t s = it.s0 + js / NGD;
+    const int g = DENSE ? js % NGD : it.g;
+    if constexpr (DENSE) {
+      // Buffer loads over the item's tile of token rows: the per-thread offset is
+      // the same for every step (the stream and channel offsets go in the scalar
+      // offset), where 64-bit addresses per step and stream, kept across the
+      // unrolled steps, would not fit the registers; rows past T read as zeros.
+      const int64_t r0 = (int64_t)it.tile * W_TOK;
+      const int64_t nrow = T - r0 < W_TOK ? T - r0 : W_TOK;
+      const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(X) + r0 * A.rowstride, 0, (uint32_t)(nrow * A.rowstride * 2), BUF_DW3);
+      const uint32_t vo = (uint32_t)(((int64_t)(st_tok + 32 * p) * A.rowstride + st_c8) * 2);
+      const uint32_t so = (uint32_t)(((int64_t)stream0(g) * C + s * W_SC) * 2);
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xrs, vo, so + (uint32_t)(i * C * 2), 2);
+        xv[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+      return;
+    }
+    int64_t t;
+    if constexpr (PAIRS) {
+      const int v = pt[st_tok + 32 * p];
+      t = v < 0 ? 0 : (v >= T ? T - 1 : v);
+    } else {
+      t = (int64_t)it.tile * W_TOK + st_tok + 32 * p;
+      t = t < T ? t : T - 1;
+    }
     const int64_t c = s * W_SC + st_c8;
     const int64_t cc = c < C ? c : C - 8;
-    const uint16_t* xg = X + t * A.rowstride + cc + (int64_t)(MODE == ROWS_GROUPS ? 4 * it.g : 0) * C;
+    const uint16_t* xg = X + t * A.rowstride + cc + (PAIRS ? (int64_t)g * A.sq : (int64_t)stream0(g) * C);
 #pragma unroll
     for (int i = 0; i < NS4; ++i) xv[i] = ld_stream(xg + i * C);
     if constexpr (DH) dv = ld_stream(A.dF + t * C + cc);
@@ -766,12 +837,23 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int i = 0; i < NS4; ++i) dh[r][i] = 0.f;
-  // the tile in LDS holds zeros for rows past T and channels past C
-  auto stream_half = [&](const Item& it, int64_t s, auto P, const uint4 (&xc)[NS4], const uint4& dc,
+  // DENSE: the sum of squares of the rows kept in the projection, this thread's
+  // channels of its token in each half (taken with F_in instead of on MFMA)
+  float ssd[2] = {0.f, 0.f};
+  float fin[2][8];  // DENSE: this thread's F_in of the current super-chunk, per token half
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fin[r][e] = 0.f;
+  // the tile in LDS holds zeros for rows past T and channels past C (PAIRS: and
+  // for padding; pt is the item's table)
+  auto stream_half = [&](const Item& it, int js, const int* pt, auto P, const uint4 (&xc)[NS4], const uint4& dc,
                          unsigned char* buf) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     const int m = st_tok + 32 * p;
-    const bool ok = ((int64_t)it.tile * W_TOK + m < T) && (s * W_SC + st_c8 < C);
+    const int64_t s = it.s0 + js / NGD;
+    const bool row_ok = PAIRS ? pt[m] >= 0 : ((int64_t)it.tile * W_TOK + m < T);
+    const bool ok = row_ok && (s * W_SC + st_c8 < C);
     const uint4 dz = keep_or_zero(ok, dc);
 #pragma unroll
     for (int i = 0; i < NS4; ++i) {
@@ -787,63 +869,165 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
       }
     }
   };
+  // DENSE, once the step's tile is in LDS: this thread's F_in pieces (the rows
+  // it streamed, read back from the tile, every row in stream order as
+  // pre_wide_kernel adds them); after the last group of a super-chunk they are
+  // complete and stored. (Adding them from the loaded registers while the
+  // queue refills holds enough of them at once to spill.)
+  auto dense_read = [&](const Item& it, int js, const int* pt, const float* ht, const unsigned char* buf,
+                        __amdgpu_buffer_rsrc_t frs) __attribute__((always_inline)) {
+    const int64_t s = it.s0 + js / NGD;
+    const int g = js % NGD;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int m = st_tok + 32 * p;
+      const float4 hc = *reinterpret_cast<const float4*>(ht + m * 16 + 4 * g);
+      const float hw[4] = {hc.x, hc.y, hc.z, hc.w};
+      const int amask = pt[m] >> (4 * g);
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) {
+        const uint4 xr = *reinterpret_cast<const uint4*>(buf + (i * W_TOK + m) * W_LROW + st_c8 * 2);
+        float xv[8];
+        unpack8(xr, xv);
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          fin[p][e] += hw[i] * xv[e];
+          sq += xv[e] * xv[e];
+        }
+        ssd[p] += (amask >> i) & 1 ? 0.f : sq;
+      }
+      if (g == NGD - 1) {  // the last group of the super-chunk: these 8 channels are complete
+        const int64_t c = s * W_SC + st_c8;
+        const uint32_t off = c < C ? (uint32_t)(((int64_t)m * C + c) * 2) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pack_bf2_hw(fin[p][0], fin[p][1]), pack_bf2_hw(fin[p][2], fin[p][3]),
+                                                       pack_bf2_hw(fin[p][4], fin[p][5]), pack_bf2_hw(fin[p][6], fin[p][7])},
+                                               frs, off, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fin[p][e] = 0.f;
+      }
+    }
+  };
   uint4 xq[QD][NS4];
   uint4 dq[QD];  // DH: the dF_in pieces beside xq
   uint4 pfq[2][NB];
-  auto load_pf = [&](const Item& it2, int64_t s2, int si, uint4 (&dst)[NB]) __attribute__((always_inline)) {
+  // DENSE: the phi fragments through a buffer resource as well, the wave's row
+  // offset in the scalar offset (its stream and channel group are wave-uniform)
+  const int wu = __builtin_amdgcn_readfirstlane(wave);
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A.phi_p), 0, DENSE ? (uint32_t)(A.rowstride / 8 * NCP * 16) : 0u, BUF_DW3);
+  auto load_pf = [&](const Item& it2, int js2, int si, uint4 (&dst)[NB]) __attribute__((always_inline)) {
+    const int64_t s2 = it2.s0 + js2 / NGD;
+    const int g2 = DENSE ? js2 % NGD : it2.g;
+    if constexpr (DENSE) {
+      const int64_t cg = s2 * W_SC + (wu & 3) * 32;  // C % W_SC == 0: never past C
+      const int64_t prow0 = (int64_t)(stream0(g2) + 2 * (wu >> 2) + si) * C;
+      const uint32_t so = (uint32_t)((prow0 + cg) / 8 * NCP * 16);
+      const uint32_t vo = (uint32_t)((q * NCP + tau) * 16);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(prs, vo + (uint32_t)(b * 256), so, 0);
+        dst[b] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+      return;
+    }
     const int64_t cg = s2 * W_SC + cgw * 32;
     const int64_t cgc = cg < C ? cg : C - 32;
-    const int64_t prow0 = (int64_t)((MODE == ROWS_GROUPS ? 4 * it2.g : 0) + 2 * sp + si) * C;
+    const int64_t prow0 = PAIRS ? (int64_t)g2 * A.sq + (int64_t)(2 * sp + si) * C
+                                : (int64_t)(stream0(g2) + 2 * sp + si) * C;
     const uint4* pb = reinterpret_cast<const uint4*>(A.phi_p) + ((prow0 + cgc) / 8 + q) * NCP + tau;
 #pragma unroll
     for (int b = 0; b < NB; ++b) dst[b] = pb[b * 16];
   };
-  auto mfma_phase = [&](const unsigned char* buf, const Item& nit, int64_t ns) __attribute__((always_inline)) {
+  // DENSE: the tile holds every row; the rows of the active streams (bit of the
+  // token's mask in pt) enter the MFMAs as zeros
+  auto mfma_phase = [&](const unsigned char* buf, const Item& nit, int njs, int g, const int* pt)
+                        __attribute__((always_inline)) {
 #pragma unroll
     for (int si = 0; si < 2; ++si) {
       const int stream = 2 * sp + si;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const uint4 af = *reinterpret_cast<const uint4*>(buf + (stream * W_TOK + tb * TOK + tau) * W_LROW +
-                                                         (cgw * 32 + q * 8) * 2);
+        uint4 af = *reinterpret_cast<const uint4*>(buf + (stream * W_TOK + tb * TOK + tau) * W_LROW +
+                                                   (cgw * 32 + q * 8) * 2);
+        if constexpr (DENSE) af = keep_or_zero(!((pt[tb * TOK + tau] >> (4 * g + stream)) & 1), af);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           acc[tb][b % NA] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(pfq[si][b]), acc[tb][b % NA], 0, 0, 0);
-        gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
+        if constexpr (!DENSE)
+          gram[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af), as_bf16x8(af), gram[tb], 0, 0, 0);
       }
-      load_pf(nit, ns, si, pfq[si]);
+      load_pf(nit, njs, si, pfq[si]);
     }
   };
-  // Super-chunk j of item `it`: half h (= 2j + p) uses queue slot h mod QD and is
+  // Step j of item `it`: half h (= 2j + p) uses queue slot h mod QD and is
   // refilled with half h + QD (for the last QD halves: the next item's first QD).
   static_assert(2 * W_SPI % QD == 0, "queue slots");
-  auto body = [&](const Item& it, auto J, const Item& nx, unsigned char* buf) __attribute__((always_inline)) {
+  auto body = [&](const Item& it, auto J, const int* pt, const float* ht, const Item& nx, const int* npt,
+                  unsigned char* buf, __amdgpu_buffer_rsrc_t frs) __attribute__((always_inline)) {
     constexpr int j = decltype(J)::value;
     constexpr int h0 = 2 * j, h1 = 2 * j + 1;
     constexpr int q0 = h0 % QD, q1 = h1 % QD;
-    const int64_t s = it.s0 + j;
-    stream_half(it, s, H0{}, xq[q0], dq[q0], buf);
-    if constexpr (h0 + QD < 2 * W_SPI) load_half(it, it.s0 + (h0 + QD) / 2, H0{}, xq[q0], dq[q0]);
-    else load_half(nx, nx.s0 + (h0 + QD - 2 * W_SPI) / 2, H0{}, xq[q0], dq[q0]);
-    stream_half(it, s, H1{}, xq[q1], dq[q1], buf);
-    if constexpr (h1 + QD < 2 * W_SPI) load_half(it, it.s0 + (h1 + QD) / 2, H1{}, xq[q1], dq[q1]);
-    else load_half(nx, nx.s0 + (h1 + QD - 2 * W_SPI) / 2, H1{}, xq[q1], dq[q1]);
+    stream_half(it, j, pt, H0{}, xq[q0], dq[q0], buf);
+    if constexpr (h0 + QD < 2 * W_SPI) load_half(it, (h0 + QD) / 2, pt, H0{}, xq[q0], dq[q0]);
+    else load_half(nx, (h0 + QD - 2 * W_SPI) / 2, npt, H0{}, xq[q0], dq[q0]);
+    stream_half(it, j, pt, H1{}, xq[q1], dq[q1], buf);
+    if constexpr (h1 + QD < 2 * W_SPI) load_half(it, (h1 + QD) / 2, pt, H1{}, xq[q1], dq[q1]);
+    else load_half(nx, (h1 + QD - 2 * W_SPI) / 2, npt, H1{}, xq[q1], dq[q1]);
     __syncthreads();
-    if constexpr (j + 1 < W_SPI) mfma_phase(buf, it, it.s0 + j + 1);
-    else mfma_phase(buf, nx, nx.s0);
+    if constexpr (DENSE) dense_read(it, j, pt, ht, buf, frs);
+    if constexpr (j + 1 < W_SPI) mfma_phase(buf, it, j + 1, j % NGD, pt);
+    else mfma_phase(buf, nx, 0, j % NGD, pt);
+  };
+
+  // The tables of an item: loaded into registers (tab_load), then written to
+  // LDS buffer b (tab_store) once they have arrived.
+  int tv_i = 0;
+  float2 tv_h = make_float2(0.f, 0.f);
+  int4 tv_x = make_int4(0, 0, 0, 0);
+  auto tab_load = [&](const Item& it2) __attribute__((always_inline)) {
+    if constexpr (PAIRS) tv_i = tid < W_TOK ? A.ptok[(int64_t)it2.tile * W_TOK + tid] : 0;
+    if constexpr (DENSE) {
+      int64_t t = (int64_t)it2.tile * W_TOK + (tid >> 3);
+      t = t < T ? t : T - 1;
+      tv_h = *reinterpret_cast<const float2*>(A.hd + t * 16 + (tid & 7) * 2);
+      if (tid < W_TOK) {
+        int64_t t2 = (int64_t)it2.tile * W_TOK + tid;
+        t2 = t2 < T ? t2 : T - 1;
+        tv_x = *reinterpret_cast<const int4*>(A.idx + t2 * 4);
+      }
+    }
+  };
+  auto tab_store = [&](int b) __attribute__((always_inline)) {
+    if constexpr (PAIRS) {
+      if (tid < W_TOK) ptab[b * W_TOK + tid] = tv_i;
+    }
+    if constexpr (DENSE) {
+      *reinterpret_cast<float2*>(htab + b * W_TOK * 16 + (tid >> 3) * 16 + (tid & 7) * 2) = tv_h;
+      if (tid < W_TOK) {
+        // bit z: stream z is active (indices outside [0, 16) mark nothing)
+        auto bit = [](int z) { return z >= 0 && z < 16 ? 1 << z : 0; };
+        ptab[b * W_TOK + tid] = bit(tv_x.x) | bit(tv_x.y) | bit(tv_x.z) | bit(tv_x.w);
+      }
+    }
   };
 
   int item = (int)blockIdx.x;
   Item it = item_of(item);
-  load_half(it, it.s0, H0{}, xq[0], dq[0]);
-  load_half(it, it.s0, H1{}, xq[1], dq[1]);
-  if constexpr (QD == 4) {
-    load_half(it, it.s0 + 1, H0{}, xq[2 % QD], dq[2 % QD]);
-    load_half(it, it.s0 + 1, H1{}, xq[3 % QD], dq[3 % QD]);
+  if constexpr (PAIRS || DENSE) {
+    tab_load(it);
+    tab_store(0);
+    __syncthreads();
   }
-  load_pf(it, it.s0, 0, pfq[0]);
-  load_pf(it, it.s0, 1, pfq[1]);
+  load_half(it, 0, ptab, H0{}, xq[0], dq[0]);
+  load_half(it, 0, ptab, H1{}, xq[1], dq[1]);
+  if constexpr (QD == 4) {
+    load_half(it, 1, ptab, H0{}, xq[2 % QD], dq[2 % QD]);
+    load_half(it, 1, ptab, H1{}, xq[3 % QD], dq[3 % QD]);
+  }
+  load_pf(it, 0, 0, pfq[0]);
+  load_pf(it, 0, 1, pfq[1]);
   // the partial sums this thread reduced for the previous item (pitem; -1: none):
   // pend[r][u] holds element tid + u * STHR of the item's token half r
   float pend[NR][NPH];
@@ -867,9 +1051,25 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   for (int k = 0; k < nk; ++k) {
     const int nitem_k = k + 1 < nk ? item + G : item;
     const Item nx = item_of(nitem_k);
+    const int* pt = ptab + (PAIRS || DENSE ? (k & 1) * W_TOK : 0);
+    const int* npt = ptab + (PAIRS || DENSE ? ((k + 1) & 1) * W_TOK : 0);
+    const float* ht = htab + (DENSE ? (k & 1) * W_TOK * 16 : 0);
+    // The next item's tables: loaded now, written to the other buffer after the
+    // second step's barrier (that buffer's last reads, by the previous item, came
+    // before the first), so the next item's first prefetch (step W_SPI - QD / 2)
+    // and first streaming step find them.
+    if constexpr (PAIRS || DENSE) tab_load(nx);
+    // DENSE: F_in rows of this item's tile
+    __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0u, BUF_DW3);
+    if constexpr (DENSE) {
+      const int64_t r0 = (int64_t)it.tile * W_TOK;
+      const int64_t nrow = T - r0 < W_TOK ? T - r0 : W_TOK;
+      frs = __builtin_amdgcn_make_buffer_rsrc(A.Fd + r0 * C, 0, (uint32_t)(nrow * C * 2), BUF_DW3);
+    }
     static_for<W_SPI>([&](auto J) __attribute__((always_inline)) {
-      body(it, J, nx, lds + ((step + decltype(J)::value) & 1) * W_LBUF);
+      body(it, J, pt, ht, nx, npt, lds + ((step + decltype(J)::value) & 1) * W_LBUF, frs);
       if constexpr (decltype(J)::value == 0) store_pending();
+      if constexpr (decltype(J)::value == 1 && (PAIRS || DENSE)) tab_store((k + 1) & 1);
     });
     step += W_SPI;
     // item end: the 8 waves' sums, TPR tokens (TPR / 16 token blocks) per round,
@@ -883,6 +1083,10 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 #pragma unroll
         for (int i = 0; i < NS4; ++i) dh[r][i] = row16_sum(dh[r][i]);
     }
+    if constexpr (DENSE) {
+      ssd[0] = row16_sum(ssd[0]);
+      ssd[1] = row16_sum(ssd[1]);
+    }
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       __syncthreads();
@@ -891,6 +1095,9 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 #pragma unroll
           for (int i = 0; i < NS4; ++i) dhr[st_tok * NS4 + i] = dh[r][i];
         }
+      }
+      if constexpr (DENSE) {  // (TPR == 32: round r is token half r)
+        if ((tid & 15) == 0) dhr[st_tok] = ssd[r];
       }
 #pragma unroll
       for (int tbb = 0; tbb < TPR / TOK; ++tbb) {
@@ -918,8 +1125,12 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
             else sum += red[(w * TPR + m) * RS + col] + red[(w * TPR + m) * RS + PG::NCOLP + col];
           }
         } else if (col == PG::NCOLP) {
+          if constexpr (DENSE) {
+            sum = dhr[m];
+          } else {
 #pragma unroll
-          for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TPR + m];
+            for (int w = 0; w < SWAVE; ++w) sum += ssr[w * TPR + m];
+          }
         } else {
           sum = dhr[m * NS4 + (col - PG::NCOLP - 1)];
         }
@@ -930,6 +1141,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int i = 0; i < NS4; ++i) dh[r][i] = 0.f;
+    ssd[0] = ssd[1] = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       gram[tb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -1256,12 +1468,18 @@ __global__ __launch_bounds__(256) void bwd_xpre_coeff_kernel(const float* __rest
 // router lanes: score = sigmoid(P / r). Selection (when nr > 0): k - m rounds
 // of an arg-max over the candidate lanes (equal scores go to the lower stream),
 // then idx = the m fixed streams and the chosen ones in ascending order.
-template <int NB, int TT>
+// With PAIRP the projection is split in two: the partials `part` cover the
+// rows left out of the previous route's active set (the carry of the chained
+// step), and the pair partials pp (PAIRS items, ps slices per pair tile) the
+// active rows, pair pos[t, j] for slot j (< 0: none); both are added per token.
+template <int NB, int TT, bool PAIRP = false>
 __global__ __launch_bounds__(256) void xpre_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C, int N,
                                                           int per_tile, int npre, int nr, int k, int m,
                                                           const float* __restrict__ b_pre, float a_pre,
                                                           float* __restrict__ h_pre, float* __restrict__ score,
-                                                          int32_t* __restrict__ idx) {
+                                                          int32_t* __restrict__ idx, const float* __restrict__ pp = nullptr,
+                                                          const int32_t* __restrict__ ppos = nullptr, int pk = 0,
+                                                          int ps = 0) {
   using PG = PartGeom<NB, TT>;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tt = g >> 5;
@@ -1277,6 +1495,17 @@ __global__ __launch_bounds__(256) void xpre_finish_kernel(const float* __restric
     const float* b = base + (int64_t)it * PG::PART;
     ss += b[PG::NCOLP];
     pc += b[cc];
+  }
+  if constexpr (PAIRP) {
+    for (int j = 0; j < pk; ++j) {
+      const int pq = ppos[tc * pk + j];
+      if (pq < 0) continue;
+      const float* b = pp + (int64_t)(pq / TT) * ps * PG::PART + (pq % TT) * PG::PROW;
+      for (int sl = 0; sl < ps; ++sl) {
+        ss += b[(int64_t)sl * PG::PART + PG::NCOLP];
+        pc += b[(int64_t)sl * PG::PART + cc];
+      }
+    }
   }
   const float r = sqrtf(ss / (float)((double)N * (double)C));
   const float invr = (r > 0.f) ? 1.0f / r : 0.f;
@@ -1661,6 +1890,137 @@ __global__ __launch_bounds__(256) void mix4_kernel(uint16_t* X, int64_t T, int N
   }
 }
 
+// ------------------------------------------------------ active-row pairs
+
+// The pairs (t, j) of an active set idx [T, k] grouped by stream: bucket z holds
+// the pairs whose row is stream z, padded to whole tiles of W_TOK pairs. Three
+// launches over blocks of SORT_THR tokens: (1) each block's pairs per stream (a
+// wave counts its lanes with one ballot per stream, the waves' counts added in
+// order); (2) the buckets' first tiles (tile_off [N + 1], tile_off[N] the tiles
+// used), each block's first slot per stream, and the padding: ptok = -1 for the
+// tail of each bucket's last tile and every slot past the last bucket up to
+// ntile tiles; (3) each block places its pairs, slot order (block, slot j,
+// wave, lane): ptok (the token of each slot) and pos [T, k] (each pair's slot;
+// -1 for an index outside [0, N)).
+constexpr int SORT_THR = 256;
+constexpr int SORT_NW = SORT_THR / 64;
+constexpr int SORT_MAXN = 16;
+
+__global__ __launch_bounds__(SORT_THR) void pair_count_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int N,
+                                                              int32_t* __restrict__ cnt) {
+  __shared__ int wc[SORT_NW][SORT_MAXN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t = (int64_t)blockIdx.x * SORT_THR + tid;
+  int mine = 0;  // lane y: the wave's pairs of stream y
+  for (int j = 0; j < k; ++j) {
+    const int z = t < T ? idx[t * k + j] : -1;
+    for (int y = 0; y < N; ++y) {
+      const uint64_t mk = __ballot(z == y);
+      if (lane == y) mine += __popcll(mk);
+    }
+  }
+  if (lane < N) wc[wave][lane] = mine;
+  __syncthreads();
+  if (tid < N) {
+    int sum = 0;
+    for (int w = 0; w < SORT_NW; ++w) sum += wc[w][tid];
+    cnt[(int64_t)blockIdx.x * N + tid] = sum;
+  }
+}
+
+// (G * N counts, staged through LDS in chunks so the per-stream sums run on LDS)
+constexpr int SCAN_CHUNK = 4096;
+__global__ __launch_bounds__(SORT_THR) void pair_scan_kernel(const int32_t* __restrict__ cnt, int G, int N, int ntile,
+                                                             int32_t* __restrict__ tile_off,
+                                                             int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ ptok) {
+  __shared__ int total[SORT_MAXN], first[SORT_MAXN + 1];
+  __shared__ int stage[SCAN_CHUNK];
+  const int tid = threadIdx.x;
+  const int64_t nc = (int64_t)G * N;
+  const int bpc = SCAN_CHUNK / N;  // blocks per chunk
+  int run = 0;
+  for (int64_t c0 = 0; c0 < nc; c0 += (int64_t)bpc * N) {
+    const int64_t n = nc - c0 < (int64_t)bpc * N ? nc - c0 : (int64_t)bpc * N;
+    __syncthreads();
+    for (int i = tid; i < n; i += SORT_THR) stage[i] = cnt[c0 + i];
+    __syncthreads();
+    if (tid < N)
+      for (int b = 0; b < n / N; ++b) run += stage[b * N + tid];
+  }
+  if (tid < N) total[tid] = run;
+  __syncthreads();
+  if (tid == 0) {
+    int f = 0;
+    for (int z = 0; z < N; ++z) {
+      first[z] = f;
+      f += (total[z] + W_TOK - 1) / W_TOK;
+    }
+    first[N] = f;
+  }
+  __syncthreads();
+  if (tid <= N) tile_off[tid] = first[tid];
+  run = tid < N ? first[tid] * W_TOK : 0;
+  for (int64_t c0 = 0; c0 < nc; c0 += (int64_t)bpc * N) {
+    const int64_t n = nc - c0 < (int64_t)bpc * N ? nc - c0 : (int64_t)bpc * N;
+    __syncthreads();
+    for (int i = tid; i < n; i += SORT_THR) stage[i] = cnt[c0 + i];
+    __syncthreads();
+    if (tid < N)
+      for (int b = 0; b < n / N; ++b) {
+        const int v = stage[b * N + tid];
+        stage[b * N + tid] = run;
+        run += v;
+      }
+    __syncthreads();
+    for (int i = tid; i < n; i += SORT_THR) base[c0 + i] = stage[i];
+  }
+  for (int z = 0; z < N; ++z) {
+    const int a = first[z] * W_TOK + total[z], e = first[z + 1] * W_TOK;
+    for (int i = a + tid; i < e; i += SORT_THR) ptok[i] = -1;
+  }
+  for (int64_t i = (int64_t)first[N] * W_TOK + tid; i < (int64_t)ntile * W_TOK; i += SORT_THR) ptok[i] = -1;
+}
+
+__global__ __launch_bounds__(SORT_THR) void pair_place_kernel(const int32_t* __restrict__ idx, int64_t T, int k, int N,
+                                                              const int32_t* __restrict__ base,
+                                                              int32_t* __restrict__ ptok, int32_t* __restrict__ pos) {
+  __shared__ int wc[SORT_NW][SORT_MAXN], woff[SORT_NW][SORT_MAXN], run[SORT_MAXN];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int64_t t = (int64_t)blockIdx.x * SORT_THR + tid;
+  if (tid < N) run[tid] = base[(int64_t)blockIdx.x * N + tid];
+  for (int j = 0; j < k; ++j) {
+    const int z0 = t < T ? idx[t * k + j] : -1;
+    const int z = z0 >= 0 && z0 < N ? z0 : -1;
+    int rank = 0;
+    for (int y = 0; y < N; ++y) {
+      const uint64_t mk = __ballot(z == y);
+      if (z == y) rank = __popcll(mk & below);
+      if (lane == y) wc[wave][y] = __popcll(mk);
+    }
+    __syncthreads();  // (also orders the first slot after run's initialisation)
+    if (tid < N) {
+      int r = run[tid];
+      for (int w = 0; w < SORT_NW; ++w) {
+        woff[w][tid] = r;
+        r += wc[w][tid];
+      }
+      run[tid] = r;
+    }
+    __syncthreads();
+    if (t < T) {
+      int slot = -1;
+      if (z >= 0) {
+        slot = woff[wave][z] + rank;
+        ptok[slot] = (int32_t)t;
+      }
+      pos[t * k + j] = slot;
+    }
+    __syncthreads();  // wc and woff are rewritten for the next slot
+  }
+}
+
 // ----------------------------------------------------------------- hosts
 
 static inline bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -1695,6 +2055,14 @@ int grid_for(int nitem) {
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
     ncu = 256;
   return nitem < ncu ? nitem : ncu;
+}
+// The same number of item rounds with every workgroup taking one item per round
+// (528 items on 256 CUs: 176 workgroups of 3 items, not 16 of the 256 taking a
+// third round alone).
+int grid_balanced(int nitem) {
+  const int g = grid_for(nitem);
+  const int rounds = (nitem + g - 1) / g;
+  return (nitem + rounds - 1) / rounds;
 }
 
 SplitArgs args(const void* X, int64_t T, int64_t C, int64_t rowstride, const Geom& g, const void* phi_p,
@@ -2055,6 +2423,105 @@ hipError_t launch_fast_flash_entry(const void* X, int64_t T, int N, int64_t C, i
     default: return HC_FE(10, 2);
   }
 #undef HC_FE
+}
+
+// ------------------------------------------------------- xHC chained step
+// The full-state maps of sublayer l + 1 ([pre N | router N - m], packed as
+// NB = 4 blocks with shared hi/lo accumulators, 64-token items) over the state
+// route l has just written, from two parts: the carry, partials over the rows
+// route l left unchanged (formed by the dense read of the call before, which
+// leaves route l's active rows out), and the active rows themselves after the
+// mix, grouped by stream so that each pair tile multiplies one stream's phi
+// rows (ROWS_PAIRS). The state is then read once per sublayer: by the dense
+// read, which also forms the next carry.
+constexpr int CH_NB = 4;
+static int chain_ntile(int64_t T, int k, int N) { return (int)((T * k + W_TOK - 1) / W_TOK) + N; }
+
+bool xhc_chain_supported(int dtype, int64_t T, int N, int64_t C, int k, int m) {
+  const int nc = N + (N - m);
+  return dtype == 1 && N == 16 && k == 4 && m >= 1 && m <= k && nc > 24 && nc <= 32 && C % 512 == 0 && T >= 1 &&
+         T * k < (1ll << 30) && shape_ok(T, C, N / 4, CH_NB) && shape_ok(T * k, C / 4, 1, CH_NB);
+}
+
+static int sort_blocks(int64_t T) { return (int)((T + SORT_THR - 1) / SORT_THR); }
+
+// the carry: the partials, then the packed maps they were formed with
+int64_t xhc_chain_carry_part_bytes(int64_t T, int N, int64_t C) {
+  return (part_bytes(T, C, N / 4, CH_NB) + 255) / 256 * 256;
+}
+int64_t xhc_chain_carry_bytes(int64_t T, int N, int64_t C) {
+  return xhc_chain_carry_part_bytes(T, N, C) + (int64_t)N * C / 8 * (CH_NB * 16) * 16;
+}
+
+XhcChainWs xhc_chain_ws(int64_t T, int N, int64_t C, int k) {
+  const int ntile = chain_ntile(T, k, N);
+  XhcChainWs w;
+  w.packed = (int64_t)N * C / 8 * (CH_NB * 16) * 16;
+  w.pair_part = (int64_t)ntile * slices(C / 4) * W_TOK * (CH_NB * 8 + 1) * 4;
+  w.ptok = (int64_t)ntile * W_TOK * 4;
+  w.pos = T * k * 4;
+  w.tile_off = (int64_t)(N + 1) * 4;
+  w.sort = 2ll * sort_blocks(T) * N * 4;
+  return w;
+}
+
+hipError_t launch_fast_pre_wide(const void* X, int64_t T, int N, int64_t C, const float* h_pre, void* F_in,
+                               hipStream_t st) {
+  return launch_pre_wide(X, T, N, C, h_pre, F_in, st);
+}
+
+hipError_t launch_fast_xhc_pack_full(const float* phi_pre, const float* w_router, int N, int m, int64_t C,
+                                     void* packed, hipStream_t st) {
+  return launch_pack(phi_pre, N, w_router, N - m, (int64_t)N * C, CH_NB * 8, packed, st);
+}
+
+hipError_t launch_fast_xhc_dense(const void* X, int64_t T, int N, int64_t C, const float* h_pre, const int32_t* idx,
+                                 const void* packed, void* F_in, float* carry, hipStream_t st) {
+  const Geom g = geom(T, C, N / 4, W_TOK);
+  SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, carry);
+  A.hd = h_pre;
+  A.Fd = (uint16_t*)F_in;
+  A.idx = idx;
+  A.kidx = 4;
+  A.nstreams = N;
+  hipLaunchKernelGGL((proj_wide_kernel<CH_NB, ROWS_DENSE, false, true, 2>), dim3(grid_for(A.nitem)), dim3(STHR), 0,
+                     st, A);
+  return hipGetLastError();
+}
+
+hipError_t launch_fast_xhc_chain_maps(const void* X, int64_t T, int N, int64_t C, int k, int m,
+                                      const int32_t* idx_prev, const void* packed, const float* carry,
+                                      const float* b_pre, float a_pre, float* h_pre, float* score, int32_t* idx,
+                                      int32_t* ptok, int32_t* tile_off, int32_t* pos, int32_t* sortw,
+                                      float* pair_part, hipStream_t st) {
+  const int ntile = chain_ntile(T, k, N);
+  const int G = sort_blocks(T);
+  int32_t* cnt = sortw;
+  int32_t* base = sortw + (int64_t)G * N;
+  hipLaunchKernelGGL(pair_count_kernel, dim3(G), dim3(SORT_THR), 0, st, idx_prev, T, k, N, cnt);
+  hipLaunchKernelGGL(pair_scan_kernel, dim3(1), dim3(SORT_THR), 0, st, (const int32_t*)cnt, G, N, ntile, tile_off, base,
+                     ptok);
+  hipLaunchKernelGGL(pair_place_kernel, dim3(G), dim3(SORT_THR), 0, st, idx_prev, T, k, N, (const int32_t*)base, ptok,
+                     pos);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t Cq = C / 4;  // the quarter rows that stand in for a pair's 4 streams
+  const int ps = (int)slices(Cq);
+  const Geom gp{1, ps, ntile * ps};
+  SplitArgs A = args(X, T, Cq, (int64_t)N * C, gp, packed, pair_part);
+  A.ptok = ptok;
+  A.tile_off = tile_off;
+  A.nstreams = N;
+  A.sq = C;
+  hipLaunchKernelGGL((proj_wide_kernel<CH_NB, ROWS_PAIRS, false, true, 4>), dim3(grid_balanced(A.nitem)), dim3(STHR),
+                     0, st, A);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const Geom g = geom(T, C, N / 4, W_TOK);
+  const int64_t threads = T * 32;
+  hipLaunchKernelGGL((xpre_finish_kernel<CH_NB, W_TOK, true>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     st, carry, T, C, N, g.NG * g.S, N, N - m, k, m, b_pre, a_pre, h_pre, score, idx,
+                     (const float*)pair_part, (const int32_t*)pos, k, ps);
+  return hipGetLastError();
 }
 
 // Streaming copy of n16 16-byte words: 4 per thread, all loads issued before

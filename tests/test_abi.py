@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("hc_coeffs", "hc_pre", "hc_coeffs_pre", "hc_post", "hc_post_coeffs", "hc_post_pre",
                  "hc_phi_pack", "hc_phi_packed_bytes", "xhc_pre", "xhc_route", "xhc_augment",
+                 "xhc_pre_chain", "xhc_route_pre", "xhc_chain_carry_bytes", "xhc_chain_workspace_bytes",
                  "hc_status_string"):
         assert want in names
 
@@ -323,6 +324,64 @@ def test_xhc_backward_validation(hc):
     assert pre(ws=None) == -8
     assert pre(dX=ctypes.c_void_p(0x4000000)) == -5  # dX over dF_in
     assert pre(dphi=ctypes.c_void_p(0x5000040)) == -5  # dphi inside dX
+
+
+def test_xhc_chain_validation(hc):
+    """xhc_pre_chain / xhc_route_pre: the covered shapes, required pointers, alignment,
+    workspace and overlap rules, all rejected before any device work."""
+    L = hc.lib()
+    T, N, C = 8, 16, 512
+    cb = L.xhc_chain_carry_bytes(T, N, C, 4, 2, 1)
+    wsb = L.xhc_chain_workspace_bytes(T, N, C, 4, 2, 1, 1)
+    assert cb > 0 and wsb > 0
+    assert L.xhc_chain_carry_bytes(T, 8, C, 4, 2, 1) == -1       # N = 16 only
+    assert L.xhc_chain_carry_bytes(T, N, 256, 4, 2, 1) == -1     # C % 512
+    assert L.xhc_chain_carry_bytes(T, N, C, 3, 2, 1) == -1       # k = 4
+    assert L.xhc_chain_carry_bytes(T, N, C, 4, 5, 1) == -1       # m <= k
+    assert L.xhc_chain_carry_bytes(T, N, C, 4, 2, 0) == -1       # bfloat16
+    assert L.xhc_chain_workspace_bytes(T, N, C, 4, 2, 9, 1) == -1
+    P = lambda j: ctypes.c_void_p(0x1000000 * (j + 1))  # distinct, far apart, 256-byte aligned
+    pn = ["X", "phi", "b", "w", "phin", "wn", "hp", "Fin", "idx", "sc", "carry", "ws"]
+
+    def pre(dt=1, T=T, N=N, C=C, k=4, m=2, wsb=wsb, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(pn)}
+        return L.xhc_pre_chain(p["X"], dt, T, N, C, k, m, p["phi"], p["b"], 0.01, p["w"], p["phin"], p["wn"], p["hp"],
+                               p["Fin"], p["idx"], p["sc"], p["carry"], p["ws"], wsb, None)
+    assert pre(dt=0) == -3 and pre(dt=7) == -3
+    assert pre(N=8) == -2 and pre(C=1000) == -2 and pre(k=2) == -2 and pre(T=-1) == -2
+    assert pre(T=0, X=None) == 0
+    for nm in ["X", "phi", "b", "w", "phin", "wn", "Fin", "idx", "carry"]:
+        assert pre(**{nm: None}) == -1, nm
+    assert pre(idx=ctypes.c_void_p(0x9000004)) == -4    # idx rows are read 16 bytes at a time
+    assert pre(carry=ctypes.c_void_p(0xB000010)) == -4  # the carry is 256-byte aligned
+    assert pre(hp=ctypes.c_void_p(0x7000008)) == -4
+    assert pre(ws=None) == -8 and pre(wsb=wsb - 1) == -8
+    assert pre(Fin=ctypes.c_void_p(0x1000000)) == -5    # F_in over X
+    assert pre(carry=ctypes.c_void_p(0xC000000 - 256)) == -5  # carry runs into the workspace
+
+    rn = ["X", "idx", "pa", "ba", "Wb", "phi", "b", "w", "cin", "phin", "wn", "cout", "hpo", "hro", "idxo", "sc",
+          "hp", "Fin", "ws"]
+
+    def route(dt=1, T=T, N=N, C=C, k=4, m=2, K=1, iters=20, wsb=wsb, **kw):
+        p = {nm: kw.get(nm, P(j)) for j, nm in enumerate(rn)}
+        return L.xhc_route_pre(p["X"], dt, T, N, C, k, m, p["idx"], p["pa"], p["ba"], 0.01, 0.01, iters, p["Wb"], K,
+                               p["b"], 0.01, p["cin"], p["phin"], p["wn"], p["cout"], p["hpo"],
+                               p["hro"], p["idxo"], p["sc"], p["hp"], p["Fin"], p["ws"], wsb, None)
+    assert route(dt=0) == -3
+    assert route(N=12) == -2 and route(C=768) == -2 and route(K=0) == -2 and route(K=9) == -2
+    assert route(iters=0) == -2 and route(T=-2) == -2
+    assert route(T=0, X=None) == 0
+    for nm in ["X", "idx", "pa", "ba", "Wb", "b", "cin", "idxo", "Fin"]:
+        assert route(**{nm: None}) == -1, nm
+    # the next sublayer's maps and carry_out go together
+    assert route(cout=None) == -1 and route(phin=None) == -1
+    assert route(idx=ctypes.c_void_p(0x2000008)) == -4
+    assert route(idxo=ctypes.c_void_p(0xF000004)) == -4
+    assert route(cin=ctypes.c_void_p(0x9000080)) == -4
+    assert route(ws=None) == -8 and route(wsb=wsb - 1) == -8
+    assert route(Fin=ctypes.c_void_p(0x1000000)) == -5          # F_in over X
+    assert route(cout=ctypes.c_void_p(0x9000000 + 256)) == -5   # carry_out partly over carry_in
+    assert route(hp=ctypes.c_void_p(0x13000000 - 256)) == -5    # h_pre runs into the workspace
 
 
 def test_augment_backward_validation(hc):
