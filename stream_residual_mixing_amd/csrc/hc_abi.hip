@@ -898,7 +898,6 @@ int xhc_pre_chain(const void* X, int dtype, int64_t T, int N, int64_t C, int k, 
                   const float* phi_pre_next, const float* w_router_next,
                   float* h_pre, void* F_in, int32_t* idx, float* score, void* carry_out,
                   void* workspace, int64_t workspace_bytes, void* stream) {
-  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
   if (dtype != HC_BF16) return HC_ERR_DTYPE;
   if (T < 0 || !hc::xhc_chain_supported(dtype, T < 1 ? 1 : T, N, C, k, m)) return HC_ERR_SHAPE;
   if (T == 0) return HC_OK;
@@ -945,7 +944,6 @@ int xhc_route_pre(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
                   const float* phi_pre_next, const float* w_router_next, void* carry_out,
                   float* h_post_out, float* h_res_out, int32_t* idx_out, float* score_out, float* h_pre_out,
                   void* F_in, void* workspace, int64_t workspace_bytes, void* stream) {
-  if (!dtype_ok(dtype)) return HC_ERR_DTYPE;
   if (dtype != HC_BF16) return HC_ERR_DTYPE;
   if (T < 0 || K < 1 || K > HC_MAX_COMPONENTS || sinkhorn_iters < 1 || sinkhorn_iters > HC_MAX_ITERS ||
       !hc::xhc_chain_supported(dtype, T < 1 ? 1 : T, N, C, k, m) || hc::xhc_route_fast_ws(T < 1 ? 1 : T, C, k, K, dtype).packed == 0)

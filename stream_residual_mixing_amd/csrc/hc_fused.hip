@@ -752,7 +752,19 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   const int q = lane >> 4;
   const int cgw = wave & 3, sp = wave >> 2;
   const int G = (int)gridDim.x;
-  const int nk = (A.nitem - (int)blockIdx.x + G - 1) / G;  // items of this workgroup (>= 1)
+  // Items of this workgroup: blockIdx.x, + G, ... (>= 1); PAIRS: the items are
+  // split into 8 contiguous ranges, one per XCD (workgroups go to the XCDs in
+  // turn, workgroup b to XCD b mod 8), so each XCD's L2 holds the phi rows of the
+  // 2-3 buckets its range covers instead of every stream's
+  constexpr int NXCD = 8;
+  const bool xcd_map = PAIRS && G % NXCD == 0;
+  const int xs = (int)blockIdx.x % NXCD, xslot = (int)blockIdx.x / NXCD, GX = G / NXCD;
+  const int x_lo = xcd_map ? (int)((int64_t)xs * A.nitem / NXCD) : 0;
+  const int x_hi = xcd_map ? (int)((int64_t)(xs + 1) * A.nitem / NXCD) : A.nitem;
+  const int stride = xcd_map ? GX : G;
+  const int first_item = xcd_map ? x_lo + xslot : (int)blockIdx.x;
+  const int nk = first_item < x_hi ? (x_hi - first_item + stride - 1) / stride : 0;
+  if (nk == 0) return;  // (uniform over the workgroup, before any barrier)
   // items per tile (DENSE: 256-channel steps of all groups, as many as the
   // group x 1024-channel items of the other modes)
   const int per_tile = A.NG * A.S;
@@ -1013,7 +1025,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     }
   };
 
-  int item = (int)blockIdx.x;
+  int item = first_item;
   Item it = item_of(item);
   if constexpr (PAIRS || DENSE) {
     tab_load(it);
@@ -1049,7 +1061,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   };
   int step = 0;
   for (int k = 0; k < nk; ++k) {
-    const int nitem_k = k + 1 < nk ? item + G : item;
+    const int nitem_k = k + 1 < nk ? item + stride : item;
     const Item nx = item_of(nitem_k);
     const int* pt = ptab + (PAIRS || DENSE ? (k & 1) * W_TOK : 0);
     const int* npt = ptab + (PAIRS || DENSE ? ((k + 1) & 1) * W_TOK : 0);
@@ -2440,7 +2452,8 @@ static int chain_ntile(int64_t T, int k, int N) { return (int)((T * k + W_TOK - 
 bool xhc_chain_supported(int dtype, int64_t T, int N, int64_t C, int k, int m) {
   const int nc = N + (N - m);
   return dtype == 1 && N == 16 && k == 4 && m >= 1 && m <= k && nc > 24 && nc <= 32 && C % 512 == 0 && T >= 1 &&
-         T * k < (1ll << 30) && shape_ok(T, C, N / 4, CH_NB) && shape_ok(T * k, C / 4, 1, CH_NB);
+         T * k < (1ll << 30) && shape_ok(T, C, N / 4, CH_NB) &&
+         (int64_t)chain_ntile(T, k, N) * slices(C / 4) * W_TOK * (CH_NB * 8 + 1) * 4 < (1ll << 31);
 }
 
 static int sort_blocks(int64_t T) { return (int)((T + SORT_THR - 1) / SORT_THR); }
