@@ -796,8 +796,27 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
       for (int z = 1; z < A.nstreams; ++z) b = A.tile_off[z] <= tile ? z : b;
       return Item{tile, b, (int64_t)r * W_SPI};
     }
+    if constexpr (MODE == ROWS_GROUPS && DH) {
+      // Blocks of 2 tiles with the stream group as the stride-2S digit: with S = 4
+      // slices the 4 groups of one (tile, slice) are 8 items apart, so they run on
+      // one XCD in the same round and read that slice of dF_in through one L2
+      // (the last block of an odd tile count keeps the tile-major order)
+      const int blk = 2 * per_tile;
+      const int pb = item / blk, rb = item - pb * blk;
+      if (2 * pb + 1 < (A.nitem / per_tile)) {
+        const int g = rb / (2 * A.S), rest = rb - g * 2 * A.S;
+        const int half = rest / A.S;
+        return Item{2 * pb + half, g, (int64_t)(rest - half * A.S) * W_SPI};
+      }
+    }
     const int g = r / A.S;
     return Item{tile, g, (int64_t)(r - g * A.S) * W_SPI};
+  };
+  // where an item's partials go: its tile-major index, the order the finish
+  // kernels add them in (the schedule order differs for the dF_in-sum mode)
+  auto part_index = [&](int item, const Item& it) __attribute__((always_inline)) {
+    if constexpr (MODE == ROWS_GROUPS && DH) return it.tile * per_tile + it.g * A.S + (int)(it.s0 / W_SPI);
+    return item;
   };
   // first stream of an item's rows at stream group g (GROUPS, DENSE)
   auto stream0 = [&](int g) __attribute__((always_inline)) { return MODE == ROWS_GROUPS || DENSE ? 4 * g : 0; };
@@ -1160,7 +1179,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 #pragma unroll
       for (int b = 0; b < NA; ++b) acc[tb][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     }
-    pitem = item;
+    pitem = part_index(item, it);
     item = nitem_k;
     it = nx;
   }
