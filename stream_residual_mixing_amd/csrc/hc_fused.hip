@@ -724,6 +724,12 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   // steps, so an item covers W_SPI / 4 super-chunks of every group
   constexpr int NGD = DENSE ? 4 : 1;
   static_assert(W_SPI % NGD == 0, "steps per item");
+  // The state and phi read through buffer resources with per-step scalar
+  // offsets (one per-thread offset for every step), where 64-bit addresses per
+  // step and stream would not fit the registers: the dense rows, whose steps
+  // change stream group, and the widest stream-group passes (NB >= 6, the
+  // xHC-Flash block entry). The host keeps a tile's rows under 4 GiB.
+  constexpr bool BUFL = DENSE || (MODE == ROWS_GROUPS && !DH && NB >= 6);
   constexpr int NA = SH ? NB / 2 : NB;   // accumulator sets per token block
   static_assert(NA <= 5, "4 token blocks x more accumulator sets exceed the registers");
   using PG = PartGeom<NB, W_TOK, DH ? NS4 : 0>;
@@ -830,11 +836,9 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     constexpr int p = decltype(P)::value;
     const int64_t s = it.s0 + js / NGD;
     const int g = DENSE ? js % NGD : it.g;
-    if constexpr (DENSE) {
-      // Buffer loads over the item's tile of token rows: the per-thread offset is
-      // the same for every step (the stream and channel offsets go in the scalar
-      // offset), where 64-bit addresses per step and stream, kept across the
-      // unrolled steps, would not fit the registers; rows past T read as zeros.
+    if constexpr (BUFL) {
+      // Buffer loads over the item's tile of token rows (rows past T read as
+      // zeros; channels past C, the next row's, are zeroed when streamed).
       const int64_t r0 = (int64_t)it.tile * W_TOK;
       const int64_t nrow = T - r0 < W_TOK ? T - r0 : W_TOK;
       const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -942,16 +946,18 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   uint4 xq[QD][NS4];
   uint4 dq[QD];  // DH: the dF_in pieces beside xq
   uint4 pfq[2][NB];
-  // DENSE: the phi fragments through a buffer resource as well, the wave's row
+  // BUFL: the phi fragments through a buffer resource as well, the wave's row
   // offset in the scalar offset (its stream and channel group are wave-uniform)
   const int wu = __builtin_amdgcn_readfirstlane(wave);
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A.phi_p), 0, DENSE ? (uint32_t)(A.rowstride / 8 * NCP * 16) : 0u, BUF_DW3);
+      const_cast<uint16_t*>(A.phi_p), 0, BUFL ? (uint32_t)(A.rowstride / 8 * NCP * 16) : 0u, BUF_DW3);
   auto load_pf = [&](const Item& it2, int js2, int si, uint4 (&dst)[NB]) __attribute__((always_inline)) {
     const int64_t s2 = it2.s0 + js2 / NGD;
     const int g2 = DENSE ? js2 % NGD : it2.g;
-    if constexpr (DENSE) {
-      const int64_t cg = s2 * W_SC + (wu & 3) * 32;  // C % W_SC == 0: never past C
+    if constexpr (BUFL) {
+      // (a group past C reads the next stream's rows, or zeros past the end, and
+      // meets zero A fragments)
+      const int64_t cg = s2 * W_SC + (wu & 3) * 32;
       const int64_t prow0 = (int64_t)(stream0(g2) + 2 * (wu >> 2) + si) * C;
       const uint32_t so = (uint32_t)((prow0 + cg) / 8 * NCP * 16);
       const uint32_t vo = (uint32_t)((q * NCP + tau) * 16);
@@ -2406,6 +2412,7 @@ static int flash_entry_nb(int N, int m, int L) {
 
 XhcFastWs flash_entry_fast_ws(int64_t T, int N, int64_t C, int m, int L, int dtype) {
   if (dtype != 1 || N % 4 != 0 || N > 16 || L < 2 || (N - m) > 32) return {0, 0};
+  if ((int64_t)W_TOK * N * C * 2 >= (1ll << 32)) return {0, 0};  // buffer-resource range of a tile
   const int nb = flash_entry_nb(N, m, L);
   if (nb * 8 > PACK_MAXC || !shape_ok(T, C, N / 4, nb)) return {0, 0};
   return {(int64_t)N * C / 8 * (nb * 16) * 16, part_bytes(T, C, N / 4, nb)};
@@ -2471,7 +2478,7 @@ static int chain_ntile(int64_t T, int k, int N) { return (int)((T * k + W_TOK - 
 bool xhc_chain_supported(int dtype, int64_t T, int N, int64_t C, int k, int m) {
   const int nc = N + (N - m);
   return dtype == 1 && N == 16 && k == 4 && m >= 1 && m <= k && nc > 24 && nc <= 32 && C % 512 == 0 && T >= 1 &&
-         T * k < (1ll << 30) && shape_ok(T, C, N / 4, CH_NB) &&
+         T * k < (1ll << 30) && shape_ok(T, C, N / 4, CH_NB) && (int64_t)W_TOK * N * C * 2 < (1ll << 32) &&
          (int64_t)chain_ntile(T, k, N) * slices(C / 4) * W_TOK * (CH_NB * 8 + 1) * 4 < (1ll << 31);
 }
 

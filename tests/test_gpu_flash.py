@@ -128,6 +128,8 @@ def _run_and_check(inp, k, m, L, sample=None, K_last=1, seqs=1):
     (2, 6, 40, 29, 3, 1, synth.F32),      # float32 and shapes only the generic kernels take
     (4, 12, 64, 1, 4, 2, synth.BF16),     # one token
     (2, 16, 40, 20, 4, 2, synth.BF16),    # C % 32 != 0: generic projections beside the 16-byte kernels
+    (2, 16, 96, 50, 4, 2, synth.BF16),    # the 46-column entry pass with a partial 128-channel step
+    (4, 16, 160, 20, 4, 2, synth.BF16),   # the 78-column entry pass with a partial 128-channel step
 ])
 def test_flash_block(L, N, C, T, k, m, dtype):
     note(f"xhc_flash L={L} N={N} C={C} T={T} k={k} m={m} {dtype}")
