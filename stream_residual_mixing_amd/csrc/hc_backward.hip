@@ -198,6 +198,8 @@ __device__ __forceinline__ int xoff(int i, int m, int c) {
 }
 
 
+constexpr unsigned BUFW3 = 0x00020000u;  // buffer-resource word 3 (raw, 32-bit data)
+constexpr uint32_t OOBW = 0x80000000u;   // an offset no range reaches: the access is dropped
 constexpr int XT = 32;        // tokens per item
 constexpr int XCH = 128;      // channels per item
 constexpr int PRJ = XCH + 4;  // floats per (stream, token) row of the product tile in LDS
@@ -294,12 +296,37 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
     const int64_t t = tl * XT + m;
     const int64_t tc = t < T ? t : T - 1;
     slot_streams<BM>(idx, tc, N, in.sl);
+    // Buffer loads over the tile's token rows (rows past T read as zeros): a
+    // 32-bit offset per thread and, for the fixed slots of the mHC and pre
+    // modes, each slot's offset in a scalar register, where 64-bit addresses per
+    // row held registers the fused dphi products need.
+    const int64_t r0 = tl * XT;
+    const int64_t nrow = T - r0 < XT ? T - r0 : XT;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(X) + r0 * N * C, 0, (uint32_t)(nrow * N * C * 2), BUFW3);
+    const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(dXn) + r0 * N * C, 0, (uint32_t)(nrow * N * C * 2), BUFW3);
 #pragma unroll
     for (int i = 0; i < BS; ++i) {
-      in.xq[i] = ld_nt16(X + (tc * N + in.sl[i]) * C + cl);
-      in.dq[i] = ld_nt16(dXn + (tc * N + in.sl[i]) * C + cl);
+      uint32_t vo, so;
+      if constexpr (BM == BM_ROUTE) {
+        vo = (uint32_t)((((int64_t)m * N + in.sl[i]) * C + cl) * 2);
+        so = 0;
+      } else {
+        vo = (uint32_t)(((int64_t)m * N * C + cl) * 2);
+        so = (uint32_t)((int64_t)(g0 + i) * C * 2);
+      }
+      const u4_t a = __builtin_amdgcn_raw_buffer_load_b128(xr, vo, so, 2);
+      const u4_t b = __builtin_amdgcn_raw_buffer_load_b128(dr, vo, so, 2);
+      in.xq[i] = make_uint4(a.x, a.y, a.z, a.w);
+      in.dq[i] = make_uint4(b.x, b.y, b.z, b.w);
     }
-    if constexpr (BM != BM_ROUTE) in.fq = ld_nt16(dFi + tc * C + cl);
+    if constexpr (BM != BM_ROUTE) {
+      const __amdgpu_buffer_rsrc_t fr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(dFi) + r0 * C, 0, (uint32_t)(nrow * C * 2), BUFW3);
+      const u4_t f = __builtin_amdgcn_raw_buffer_load_b128(fr, (uint32_t)(((int64_t)m * C + cl) * 2), 0, 2);
+      in.fq = make_uint4(f.x, f.y, f.z, f.w);
+    }
     int64_t t1 = tl * XT + ctok;
     t1 = t1 < T ? t1 : T - 1;
     if (cpc < 4) {
@@ -392,6 +419,9 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
     if constexpr (BM != BM_ROUTE) unpack_bf8(cur.fq, f);
     const int64_t t = tl * XT + m;
     const bool ok = t < T && cok;
+    const int64_t nrw = T - tl * XT < XT ? T - tl * XT : XT;
+    const __amdgpu_buffer_rsrc_t xw =
+        __builtin_amdgcn_make_buffer_rsrc(dX + tl * XT * N * C, 0, (uint32_t)(nrw * N * C * 2), BUFW3);
 #pragma unroll
     for (int j = 0; j < BS; ++j) {
       const float4* pj = reinterpret_cast<const float4*>(prj + (j * XT + m) * PRJ + c8);
@@ -408,10 +438,16 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
         if constexpr (BM == BM_MHC) v += hp[j] * f[e];
         o[e] = v + p[e] + g4.x * xj[e];
       }
-      if (ok)
-        __builtin_nontemporal_store(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]),
-                                         pack_bf2_hw(o[4], o[5]), pack_bf2_hw(o[6], o[7])},
-                                    reinterpret_cast<u4_t*>(dX + (t * N + cur.sl[j]) * C + c));
+      // through a buffer resource over the tile's rows: past T or C the offset is
+      // out of range and the store is dropped (nontemporal)
+      uint32_t off = OOBW;
+      if (ok) {
+        if constexpr (BM == BM_ROUTE) off = (uint32_t)((((int64_t)m * N + cur.sl[j]) * C + c) * 2);
+        else off = (uint32_t)((((int64_t)m * N + g0 + j) * C + c) * 2);
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(u4_t{pack_bf2_hw(o[0], o[1]), pack_bf2_hw(o[2], o[3]),
+                                                  pack_bf2_hw(o[4], o[5]), pack_bf2_hw(o[6], o[7])},
+                                             xw, off, 0, 2);
     }
     __syncthreads();  // the LDS tiles are rewritten by the next tile
     tl = nt;
@@ -1241,7 +1277,8 @@ hipError_t launch_sums(const BwdWs& w, int64_t T, int64_t nrows, int ncol, float
 
 bool fast_backward_supported(int dtype, int n, int64_t T, int64_t C, int iters) {
   return dtype == 1 && n == 4 && T >= 1 && iters >= 1 && iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 &&
-         fast_coeffs_partial_bytes(T, 4, C, 1) > 0 && (C + FCH - 1) / FCH <= 65535;
+         fast_coeffs_partial_bytes(T, 4, C, 1) > 0 && (C + FCH - 1) / FCH <= 65535 &&
+         (int64_t)XT * 4 * C * 2 < (1ll << 32);  // a dX tile's rows in one buffer resource
 }
 
 int64_t fast_backward_ws_bytes(int64_t T, int64_t C) {
@@ -1288,7 +1325,8 @@ bool fast_xhc_backward_supported(int dtype, int N, int k, int K, int64_t T, int6
          iters <= HC_MAX_BWD_ITERS && C % 32 == 0 && C >= 32 && C < (1ll << 24) &&
          // the projection partials are addressed with 32-bit buffer offsets
          fast_xroute_partial_bytes(T, C, K) < (1ll << 31) && fast_xpre_partial_bytes(T, N, C) < (1ll << 31) &&
-         (C + FCH - 1) / FCH <= 65535 && T * (int64_t)N * C < (1ll << 40);
+         (C + FCH - 1) / FCH <= 65535 && T * (int64_t)N * C < (1ll << 40) &&
+         (int64_t)XT * N * C * 2 < (1ll << 32);  // a dX tile's rows in one buffer resource
 }
 
 int64_t fast_xhc_backward_ws_bytes(int64_t T, int N, int64_t C) {
