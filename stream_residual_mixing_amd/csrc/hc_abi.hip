@@ -823,7 +823,7 @@ int xhc_route(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m, con
   }
   if (x16 && hc::xhc_route_fast_ws(T, C, k, K, dtype).packed > 0) {
     e = hc::launch_fast_xhc_active(X, T, N, C, idx_out, K, phi_act, b_act, alpha_post, alpha_res, sinkhorn_iters,
-                                   Hp, Hr, packed, partial, st);
+                                   Hp, Hr, packed, partial, st, nullptr, K > 1);
   } else {
     e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, k, idx_out, N, phi_act, acols, nullptr, 0,
                                 P, ss, st);
@@ -991,7 +991,7 @@ int xhc_route_pre(void* X, int dtype, int64_t T, int N, int64_t C, int k, int m,
   float* sc = score_out ? score_out : w.sc;
   // route l: the active set's maps from its rows, then the mix in place
   hipError_t e = hc::launch_fast_xhc_active(X, T, N, C, idx_in, K, phi_act, b_act, alpha_post, alpha_res,
-                                            sinkhorn_iters, Hp, Hr, w.packed, w.partial, st);
+                                            sinkhorn_iters, Hp, Hr, w.packed, w.partial, st, nullptr, K > 1);
   if (e != hipSuccess) return HC_ERR_LAUNCH;
   if ((e = hc::launch_fast_mix(X, T, N, C, idx_in, Hr, Hp, Wb, K, st)) != hipSuccess) return HC_ERR_LAUNCH;
   // sublayer l + 1's maps (packed in the carry): the carry's partials plus the rewritten rows
@@ -1153,7 +1153,7 @@ int xhc_flash_maps(const void* X, int dtype, int64_t T, int N, int64_t C, int k,
   hipError_t e;
   if (aligned_to(X, 16) && f.packed > 0) {
     e = hc::launch_fast_xhc_active(X, T, N, C, idx, L, phi_act, b_act, alpha_post, alpha_res, sinkhorn_iters,
-                                   H_post, H_res, packed, partial, st);
+                                   H_post, H_res, packed, partial, st, nullptr, L > 1);
   } else {
     e = hc::launch_proj_generic(dtype, X, (int64_t)N * C, T, C, k, idx, N, phi_act, acols, nullptr, 0, P, ss, st);
     if (e != hipSuccess) return HC_ERR_LAUNCH;

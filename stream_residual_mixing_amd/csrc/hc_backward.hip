@@ -1252,10 +1252,10 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pby
 BwdWs carve_mhc(void* ws, int64_t T, int64_t C, int64_t* total) {
   return carve(ws, T, C, BS * C, BCOL, fast_bwd_packed_bytes(C), fast_bwd_partial_bytes(T, C), 4, false, total);
 }
-// route with K components: phi_act [4C, 4K + 16] packed as NB = 3 (K = 1) or 4
-// (K = 4) blocks of 16 columns, hi and lo (2 x 8 NB 16-byte chunks per 8 rows)
+// route with K components: phi_act [4C, 4K + 16] packed as NB = 4 blocks of 16
+// columns, 2 hi and 2 lo (2 x 8 NB 16-byte chunks per 8 rows)
 BwdWs carve_route(void* ws, int64_t T, int64_t C, int K, int64_t* total) {
-  const int nb = K == 4 ? 4 : 3;
+  const int nb = 4;
   return carve(ws, T, C, BS * C, 4 * K + 16, BS * C / 8 * (16 * nb) * 16, fast_xroute_partial_bytes(T, C, K), 4,
                true, total);
 }

@@ -145,7 +145,7 @@ hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* 
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
                                   const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
                                   float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,
-                                  uint4* phi_rows = nullptr);
+                                  uint4* phi_rows = nullptr, bool nt_rows = false);
 
 // xHC chained step (the route of sublayer l, then sublayer l + 1's maps and dense
 // read with one read of the full state): bfloat16, N = 16, k = 4, m <= k, C %

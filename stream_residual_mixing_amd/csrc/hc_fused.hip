@@ -212,7 +212,7 @@ __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
 //   ROWS_GATHER: the streams idx[t, 0..3] of a token row (xHC active set), with
 //                phi rows of slots 0..3.
 //
-// proj_wide_kernel (64-token items) has two more:
+// proj_wide_kernel (64-token items) takes ROWS_GATHER (with up to 32 columns) and two more:
 //   ROWS_DENSE: all 16 streams of the xHC full state, item = 64 tokens x 256
 //                channels of every stream group (the groups are the inner
 //                steps); it also forms the dense read F_in = sum_i h_pre_i x_i
@@ -713,13 +713,14 @@ constexpr int W_LBUF = NS4 * W_TOK * W_LROW;  // bytes per LDS buffer
 //
 // QD token halves are in flight (4: two super-chunks ahead; 2: one, for the
 // widest column counts, whose accumulators and phi fragments need the registers).
-template <int NB, int MODE, bool DH = false, bool SH = false, int QD = 4>  // SH: hi and lo share accumulators
+// NTG (ROWS_GATHER): nontemporal loads of the gathered rows.
+template <int NB, int MODE, bool DH = false, bool SH = false, int QD = 4,
+          bool NTG = false>  // SH: hi and lo share accumulators
 __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
-  static_assert(MODE != ROWS_GATHER, "gathered rows use mhc_split_kernel");
   static_assert(!SH || NB % 2 == 0, "shared accumulators pair hi block b with lo block b + NB / 2");
   static_assert(QD == 2 || QD == 4, "token halves in flight");
-  constexpr bool DENSE = MODE == ROWS_DENSE, PAIRS = MODE == ROWS_PAIRS;
-  static_assert(!(DH && (DENSE || PAIRS)), "the dF_in sums are for the stream-group and contiguous rows");
+  constexpr bool DENSE = MODE == ROWS_DENSE, PAIRS = MODE == ROWS_PAIRS, GATH = MODE == ROWS_GATHER;
+  static_assert(!(DH && (DENSE || PAIRS || GATH)), "the dF_in sums are for the stream-group and contiguous rows");
   // DENSE: the 4 stream groups of one 128-channel super-chunk are consecutive
   // steps, so an item covers W_SPI / 4 super-chunks of every group
   constexpr int NGD = DENSE ? 4 : 1;
@@ -746,8 +747,10 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * W_LBUF];
   // Per-token tables of the item being streamed and of the next item: PAIRS, the
   // pair tokens; DENSE, the tokens' h_pre (htab) and the mask of their active
-  // streams (ptab)
-  __shared__ int ptab[PAIRS || DENSE ? 2 * W_TOK : 1];
+  // streams (ptab); GATH, the tokens' 4 stream indices (ptab, 4 per token)
+  constexpr bool TAB = PAIRS || DENSE || GATH;
+  constexpr int TABW = GATH ? 4 * W_TOK : W_TOK;  // ints per table
+  __shared__ __attribute__((aligned(16))) int ptab[TAB ? 2 * TABW : 1];
   __shared__ __attribute__((aligned(16))) float htab[DENSE ? 2 * W_TOK * 16 : 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -862,6 +865,22 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     }
     const int64_t c = s * W_SC + st_c8;
     const int64_t cc = c < C ? c : C - 8;
+    if constexpr (GATH) {
+      // the token's 4 streams from the table (clamped into the row); ordinary
+      // (cache-allocating) loads unless NTG: the mix pass that follows reads
+      // these rows again, newest first, and finds part of them in the
+      // last-level cache, which pays where it reads little else (K = 1)
+      const int4 z4 = *reinterpret_cast<const int4*>(pt + (st_tok + 32 * p) * 4);
+      const int zs[NS4] = {z4.x, z4.y, z4.z, z4.w};
+      const uint16_t* xr = X + t * A.rowstride + cc;
+#pragma unroll
+      for (int i = 0; i < NS4; ++i) {
+        const int z = zs[i] < 0 ? 0 : (zs[i] >= A.nstreams ? A.nstreams - 1 : zs[i]);
+        if constexpr (NTG) xv[i] = ld_stream(xr + (int64_t)z * C);
+        else xv[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)z * C);
+      }
+      return;
+    }
     const uint16_t* xg = X + t * A.rowstride + cc + (PAIRS ? (int64_t)g * A.sq : (int64_t)stream0(g) * C);
 #pragma unroll
     for (int i = 0; i < NS4; ++i) xv[i] = ld_stream(xg + i * C);
@@ -1025,6 +1044,13 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   int4 tv_x = make_int4(0, 0, 0, 0);
   auto tab_load = [&](const Item& it2) __attribute__((always_inline)) {
     if constexpr (PAIRS) tv_i = tid < W_TOK ? A.ptok[(int64_t)it2.tile * W_TOK + tid] : 0;
+    if constexpr (GATH) {
+      if (tid < 4 * W_TOK) {
+        int64_t t2 = (int64_t)it2.tile * W_TOK + (tid >> 2);
+        t2 = t2 < T ? t2 : T - 1;
+        tv_i = A.idx[t2 * A.kidx + (tid & 3)];
+      }
+    }
     if constexpr (DENSE) {
       int64_t t = (int64_t)it2.tile * W_TOK + (tid >> 3);
       t = t < T ? t : T - 1;
@@ -1040,6 +1066,9 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     if constexpr (PAIRS) {
       if (tid < W_TOK) ptab[b * W_TOK + tid] = tv_i;
     }
+    if constexpr (GATH) {
+      if (tid < 4 * W_TOK) ptab[b * TABW + tid] = tv_i;
+    }
     if constexpr (DENSE) {
       *reinterpret_cast<float2*>(htab + b * W_TOK * 16 + (tid >> 3) * 16 + (tid & 7) * 2) = tv_h;
       if (tid < W_TOK) {
@@ -1052,7 +1081,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
 
   int item = first_item;
   Item it = item_of(item);
-  if constexpr (PAIRS || DENSE) {
+  if constexpr (TAB) {
     tab_load(it);
     tab_store(0);
     __syncthreads();
@@ -1088,14 +1117,14 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
   for (int k = 0; k < nk; ++k) {
     const int nitem_k = k + 1 < nk ? item + stride : item;
     const Item nx = item_of(nitem_k);
-    const int* pt = ptab + (PAIRS || DENSE ? (k & 1) * W_TOK : 0);
-    const int* npt = ptab + (PAIRS || DENSE ? ((k + 1) & 1) * W_TOK : 0);
+    const int* pt = ptab + (TAB ? (k & 1) * TABW : 0);
+    const int* npt = ptab + (TAB ? ((k + 1) & 1) * TABW : 0);
     const float* ht = htab + (DENSE ? (k & 1) * W_TOK * 16 : 0);
     // The next item's tables: loaded now, written to the other buffer after the
     // second step's barrier (that buffer's last reads, by the previous item, came
     // before the first), so the next item's first prefetch (step W_SPI - QD / 2)
     // and first streaming step find them.
-    if constexpr (PAIRS || DENSE) tab_load(nx);
+    if constexpr (TAB) tab_load(nx);
     // DENSE: F_in rows of this item's tile
     __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(nullptr, 0, 0u, BUF_DW3);
     if constexpr (DENSE) {
@@ -1106,7 +1135,7 @@ __global__ __launch_bounds__(STHR) void proj_wide_kernel(SplitArgs A) {
     static_for<W_SPI>([&](auto J) __attribute__((always_inline)) {
       body(it, J, pt, ht, nx, npt, lds + ((step + decltype(J)::value) & 1) * W_LBUF, frs);
       if constexpr (decltype(J)::value == 0) store_pending();
-      if constexpr (decltype(J)::value == 1 && (PAIRS || DENSE)) tab_store((k + 1) & 1);
+      if constexpr (decltype(J)::value == 1 && TAB) tab_store((k + 1) & 1);
     });
     step += W_SPI;
     // item end: the 8 waves' sums, TPR tokens (TPR / 16 token blocks) per round,
@@ -1320,7 +1349,7 @@ __global__ __launch_bounds__(256) void bwd_coeff_kernel(const float* __restrict_
   static_assert(NGC == 4 || NGC == 8 || NGC == 16, "gate columns");
   static_assert(!DHP || !ROUTE, "the fused dH_pre sums are the mHC pre map's");
   extern __shared__ float it_lds[];  // [iters][256]
-  using PG = PartGeom<(DHP || DHS > 24 ? 4 : 3), TT, DHP ? NS4 : 0>;
+  using PG = PartGeom<(DHP || ROUTE ? 4 : 3), TT, DHP ? NS4 : 0>;
   const int tid = threadIdx.x;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + tid;
   const int64_t tt = g >> 4;
@@ -1665,18 +1694,19 @@ __global__ __launch_bounds__(256) void flash_entry_finish_kernel(const float* __
 // token's items in order, r_A = sqrt(ss / (4 C)); post lanes e < 4K: H_post =
 // 2 sigmoid(alpha_post P / r + b); H_res = Sinkhorn-Knopp(exp(alpha_res P / r +
 // b)) on the 4x4 block held by the 16 lanes (DPP exchanges as in mHC).
-template <int NB>
+// TT: tokens per item of the partials.
+template <int NB, int TT = TILE>
 __global__ __launch_bounds__(256) void xroute_finish_kernel(const float* __restrict__ part, int64_t T, int64_t C,
                                                             int per_tile, int K, const float* __restrict__ b_act,
                                                             float a_post, float a_res, int iters,
                                                             float* __restrict__ Hp, float* __restrict__ Hr) {
-  using PG = PartGeom<NB>;
+  using PG = PartGeom<NB, TT>;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t tt = g >> 4;
   const int e = (int)(g & 15);
   const int64_t tc = tt < T ? tt : T - 1;
-  const int64_t tile = tc / TILE;
-  const int mrow = (int)(tc - tile * TILE);
+  const int64_t tile = tc / TT;
+  const int mrow = (int)(tc - tile * TT);
   const float* base = part + tile * per_tile * PG::PART + mrow * PG::PROW;
   const int kK = 4 * K;  // post entries: lane e takes e and, for K > 4, e + 16
   const int cpost = e < kK ? e : 0, cpost2 = e + 16 < kK ? e + 16 : 0;
@@ -2286,10 +2316,10 @@ hipError_t launch_fast_xroute_bwd_coeffs(const float* partial, int64_t T, int64_
   const Gate gt{0.f, a_post, a_res};
   float* dhm = const_cast<float*>(dh);  // read only: the route layouts write no dh
   if (K == 4)
-    hipLaunchKernelGGL((bwd_coeff_kernel<TILE, 4>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
+    hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, 4>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
                        iters, dhm, dP, g2, red, nullptr, h_res);
   else
-    hipLaunchKernelGGL((bwd_coeff_kernel<TILE, 1>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
+    hipLaunchKernelGGL((bwd_coeff_kernel<W_TOK, 1>), grid, blk, lds, st, partial, T, C, (int)slices(C), b_act, gt,
                        iters, dhm, dP, g2, red, nullptr, h_res);
   return hipGetLastError();
 }
@@ -2313,7 +2343,7 @@ hipError_t launch_fast_xpre_bwd_coeffs(const float* partial, int64_t T, int N, i
   return hipGetLastError();
 }
 
-int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K) { return part_bytes(T, C, 1, K == 4 ? 4 : 3); }
+int64_t fast_xroute_partial_bytes(int64_t T, int64_t C, int K) { return part_bytes(T, C, 1, 4); }
 int64_t fast_xpre_partial_bytes(int64_t T, int N, int64_t C) { return part_bytes(T, C, N / 4, 2, NS4); }
 
 hipError_t launch_fast_bwd_coeffs(const float* partial, int64_t T, int64_t C, const float* bias, float a_pre,
@@ -2342,8 +2372,10 @@ XhcFastWs xhc_router_fast_ws(int64_t T, int N, int64_t C, int m, int dtype) {
   return {(int64_t)N * C / 8 * (nb * 16) * 16, part_bytes(T, C, N / 4, nb)};
 }
 
-// packed column blocks of the active-set projection: up to 48 columns (k = 4, K <= 8)
-static int nb_for_act(int ncols) { return ncols <= 32 ? nb_for(ncols) : (ncols + 7) / 8; }
+// packed column blocks of the active-set projection: up to 32 columns (K <= 4)
+// as 4 blocks (2 hi, 2 lo) for the 64-token gathered pass, whose hi and lo
+// blocks share accumulators; up to 48 (K <= 8) on 32-token items
+static int nb_for_act(int ncols) { return ncols <= 32 ? 4 : (ncols + 7) / 8; }
 
 XhcFastWs xhc_route_fast_ws(int64_t T, int64_t C, int k, int K, int dtype) {
   const int ncols = k * K + k * k;
@@ -2631,7 +2663,7 @@ hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* 
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
                                   const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
                                   float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,
-                                  uint4* phi_rows) {
+                                  uint4* phi_rows, bool nt_rows) {
   const int ncols = 4 * K + 16;
   const int nb = nb_for_act(ncols);
   hipError_t e;
@@ -2647,22 +2679,40 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  const Geom g = geom(T, C, 1, TILE);
+  // up to 32 columns: 64-token items (each phi fragment from L2 serves 64
+  // tokens); wider: 32-token items
+  const bool wide = ncols <= 32;
+  const Geom g = geom(T, C, 1, wide ? W_TOK : TILE);
   SplitArgs A = args(X, T, C, (int64_t)N * C, g, packed, partial);
   A.idx = idx;
   A.kidx = 4;
   A.nstreams = N;
-  if ((e = launch_split_nb<ROWS_GATHER>(nb, A, st)) != hipSuccess) return e;
+  // nt_rows: nontemporal loads of the gathered rows, for a caller whose next
+  // pass gains less from finding them in the last-level cache than those loads
+  // gain here (the forward mix with K > 1 components, which reads as many bytes
+  // of them as of the rows: projection + mix 195 against 202 us at K = 4, N =
+  // 16, C = 4096, T = 8192; at K = 1, 158 against 168 us the other way).
+  if (wide && nt_rows) {
+    hipLaunchKernelGGL((proj_wide_kernel<4, ROWS_GATHER, false, true, 4, true>), dim3(grid_for(A.nitem)), dim3(STHR), 0,
+                       st, A);
+    e = hipGetLastError();
+  } else if (wide) {
+    hipLaunchKernelGGL((proj_wide_kernel<4, ROWS_GATHER, false, true, 4>), dim3(grid_for(A.nitem)), dim3(STHR), 0, st,
+                       A);
+    e = hipGetLastError();
+  } else {
+    e = launch_split_nb<ROWS_GATHER>(nb, A, st);
+  }
+  if (e != hipSuccess) return e;
   const int64_t threads = T * 16;
   const dim3 grid((unsigned)((threads + 255) / 256)), blk(256);
-#define HC_XRF(NB) \
-  hipLaunchKernelGGL(xroute_finish_kernel<NB>, grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, iters, \
-                     Hp, Hr)
+#define HC_XRF(NB, TT) \
+  hipLaunchKernelGGL((xroute_finish_kernel<NB, TT>), grid, blk, 0, st, partial, T, C, g.S, K, b_act, a_post, a_res, \
+                     iters, Hp, Hr)
   switch (nb) {
-    case 3: HC_XRF(3); break;
-    case 4: HC_XRF(4); break;
-    case 5: HC_XRF(5); break;
-    default: HC_XRF(6); break;
+    case 4: HC_XRF(4, W_TOK); break;
+    case 5: HC_XRF(5, TILE); break;
+    default: HC_XRF(6, TILE); break;
   }
 #undef HC_XRF
   return hipGetLastError();
