@@ -277,13 +277,20 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
     for (int nb = 0; nb < PNB; ++nb) pacc[cb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 bh[4], bl[4];
+  // The phi fragments of the dP phi^T product (this wave's stream and channel
+  // blocks, hi and lo) stay for the whole kernel: in registers, except the hi
+  // parts of the route mode, which go to LDS (each wave its own 4 KB) to make
+  // room for that mode's dphi accumulators and gathered row offsets.
+  constexpr bool PHL = BM == BM_ROUTE;
+  __shared__ __attribute__((aligned(16))) uint4 phl[PHL ? 8 * 4 * 64 : 1];
+  uint4 bh[PHL ? 1 : 4], bl[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     int64_t ch = chunk * XCH + (cb0 + cb) * 16 + tau;
     ch = ch < C ? ch : C - 1;
     const uint4* pr = phi_rows + ((int64_t)(g0 + si) * C + ch) * 8;
-    bh[cb] = pr[q];
+    if constexpr (PHL) phl[(wave * 4 + cb) * 64 + lane] = pr[q];
+    else bh[cb] = pr[q];
     bl[cb] = pr[4 + q];
   }
 
@@ -372,10 +379,13 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
       split_bf8(v, ah, al);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
+        uint4 bhc;
+        if constexpr (PHL) bhc = phl[(wave * 4 + cb) * 64 + lane];
+        else bhc = bh[cb];
         f4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah), bf8(bh[cb]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah), bf8(bhc), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(ah), bf8(bl[cb]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(al), bf8(bh[cb]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(al), bf8(bhc), acc, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) prj[(si * XT + tb * 16 + q * 4 + e) * PRJ + (cb0 + cb) * 16 + tau] = acc[e];
       }
