@@ -18,11 +18,10 @@
 //     recomputes): dH_pre summed into dh, gates and Sinkhorn backward -> dP,
 //     g2, sums over groups of 16 tokens, and the forward's h_pre and h_res;
 //  3. bwd_dx_kernel: dX = H_res^T dX_next + H_pre dF_in + dP phi^T + g2 x, the
-//     dP phi^T product on MFMA, and (xHC route and pre modes) from the same
-//     tiles of x the dphi partials vec(x)^T dP over groups of token tiles on
-//     MFMA (the tokens are the K dimension);
-//  4. bwd_dphi_kernel (n = 4 mHC): the same dphi partials in a pass of their own;
-//  5. bwd_sums_kernel: the group partials of dphi and the sums of db and dalpha
+//     dP phi^T product on MFMA, and from the same tiles of x the dphi partials
+//     vec(x)^T dP over groups of token tiles on MFMA (the tokens are the K
+//     dimension);
+//  4. bwd_sums_kernel: the group partials of dphi and the sums of db and dalpha
 //     added in a fixed order.
 #include "hc.h"
 #include "hc_device.h"
@@ -220,7 +219,7 @@ static_assert(XT == FT && XCH == FCH, "the dphi MFMAs take the dX tile's state r
 //    (v_mfma_f32_16x16x32_bf16; A = the tokens' dP rows split hi/lo, B = the
 //    channels' phi rows hi/lo; hi*hi + hi*lo + lo*hi into one float32
 //    accumulator) into the LDS product tile; then the next tile's loads are
-//    issued, and (route and pre modes) the same wave adds the tile's x^T dP to its dphi
+//    issued, and the same wave adds the tile's x^T dP to its dphi
 //    accumulators for the same slot and channel blocks and both 16-column
 //    blocks of dP, with the tokens as K (A = x^T, one channel and 8 tokens a
 //    lane, read from the state tile the threads also stage in LDS; B = dP
@@ -232,7 +231,7 @@ static_assert(XT == FT && XCH == FCH, "the dphi MFMAs take the dX tile's state r
 //      BM_PRE:   dX_j += H_pre[j] dF_in + (dP phi^T)_j + g2 x_j (dX_next is dX)
 //    rounded once to bfloat16 and stored.
 // Rows past T and channels past C are computed on clamped addresses and not
-// stored. After the last tile (route and pre modes) each workgroup writes its dphi partials,
+// stored. After the last tile each workgroup writes its dphi partials,
 //   part[blockIdx.y][R][k] = sum over its tiles of x[t, slot, c] dP[t, k]   (k < ncol)
 // with R the phi row of the slot's channel c, added over the groups later in a
 // fixed order. In place is safe: a thread reads its (token, channels) of dX_next one
@@ -251,11 +250,9 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) float prj[BS * XT * PRJ];
   __shared__ __attribute__((aligned(16))) float cf[XT * CFR];
   __shared__ __attribute__((aligned(16))) float dpt[XT * DPR];
-  // the dphi MFMAs ride along in the route and pre modes; the mHC mode's
-  // H_res product holds too many registers for them, so it keeps its own pass
-  constexpr bool FUSE = BM != BM_MHC;
-  __shared__ __attribute__((aligned(16))) unsigned char xt[FUSE ? BS * FT * FROW : 16];
-  __shared__ __attribute__((aligned(16))) uint16_t dph[FUSE ? 2 * DPS * DPT : 8];  // [hi | lo][column][token]
+  // the dphi MFMAs' tiles: the state (swizzled) and dP transposed, hi and lo
+  __shared__ __attribute__((aligned(16))) unsigned char xt[BS * FT * FROW];
+  __shared__ __attribute__((aligned(16))) uint16_t dph[2 * DPS * DPT];  // [hi | lo][column][token]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t chunk = blockIdx.x;
   const int64_t J = gridDim.y, ntile = (T + XT - 1) / XT;
@@ -279,9 +276,9 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
     for (int nb = 0; nb < PNB; ++nb) pacc[cb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
   // The phi fragments of the dP phi^T product (this wave's stream and channel
   // blocks, hi and lo) stay for the whole kernel: in registers, except the hi
-  // parts of the route mode, which go to LDS (each wave its own 4 KB) to make
-  // room for that mode's dphi accumulators and gathered row offsets.
-  constexpr bool PHL = BM == BM_ROUTE;
+  // parts of the mHC and route modes, which go to LDS (each wave its own 4 KB)
+  // to make room for their H_res product beside the dphi accumulators.
+  constexpr bool PHL = BM != BM_PRE;
   __shared__ __attribute__((aligned(16))) uint4 phl[PHL ? 8 * 4 * 64 : 1];
   uint4 bh[PHL ? 1 : 4], bl[4];
 #pragma unroll
@@ -352,12 +349,10 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   // one tile: returns false after the last
   auto step = [&](int64_t& tl, In& cur, In& nxt) __attribute__((always_inline)) {
     if (tid < 192) *reinterpret_cast<float4*>(cf + ctok * CFR + cpc * 4) = cur.cv;
-    if constexpr (FUSE) {
 #pragma unroll
-      for (int i = 0; i < BS; ++i) *reinterpret_cast<uint4*>(xt + xoff(i, m, c8)) = cur.xq[i];
-    }
+    for (int i = 0; i < BS; ++i) *reinterpret_cast<uint4*>(xt + xoff(i, m, c8)) = cur.xq[i];
     if (tid < 256) *reinterpret_cast<float4*>(dpt + dtok * DPR + dpc * 4) = cur.dv;
-    if (FUSE && tid < 256) {
+    if (tid < 256) {
       const bool pok = tl * XT + dtok < T;
       const float v[4] = {cur.dv.x, cur.dv.y, cur.dv.z, cur.dv.w};
 #pragma unroll
@@ -392,7 +387,7 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
     }
     const int64_t nt = tl + J;
     if (nt < ntile) load(nt, nxt);
-    if constexpr (FUSE) {
+    {
       uint4 ph[PNB], pl[PNB];
 #pragma unroll
       for (int nb = 0; nb < PNB; ++nb) {
@@ -438,8 +433,7 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
       const float4 p0 = pj[0], p1 = pj[1];
       const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
       float xj[8], o[8];
-      if constexpr (FUSE) unpack_bf8(*reinterpret_cast<const uint4*>(xt + xoff(j, m, c8)), xj);
-      else unpack_bf8(cur.xq[j], xj);
+      unpack_bf8(*reinterpret_cast<const uint4*>(xt + xoff(j, m, c8)), xj);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v;
@@ -468,7 +462,6 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
   load(tl, a);
   while (step(tl, a, b) && step(tl, b, a)) {
   }
-  if constexpr (!FUSE) return;
   float* out = part + (int64_t)blockIdx.y * nrows * ncol;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
@@ -479,114 +472,6 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
         const int64_t ch = chunk * XCH + (cb0 + cb) * 16 + q * 4 + e;
         const int col = nb * 16 + tau;
         if (ch < C && col < ncol) out[((int64_t)(g0 + si) * C + ch) * ncol + col] = pacc[cb][nb][e];
-      }
-}
-
-// Partial dphi of a chunk of 128 channels x the 4 slots of the n = 4 mHC mode over
-// the token tiles g, g + G, ... (g = blockIdx.y, G = gridDim.y <= the tile
-// count), with R = the phi row of the slot's channel c:
-//   part[g][R][k] = sum_t x[t, slot, c] dP[t, k]   (k < ncol)
-// on MFMA with the tokens as K: A = x^T (lane: one channel, 8 tokens, read from
-// the LDS state tile one element at a time), B = dP (lane: one column, 8 tokens,
-// from the transposed hi/lo tile in LDS), D += A B_hi + A B_lo. Wave w owns
-// stream w >> 1, channel blocks (w & 1) * 4 .. + 3 and both 16-column blocks;
-// its accumulators stay in registers over the workgroup's tiles. The next
-// tile's state and dP are loaded while the MFMAs of the current one run.
-template <int BM>
-__global__ __launch_bounds__(512) void bwd_dphi_kernel(const uint16_t* __restrict__ X, const float* __restrict__ dP,
-                                                       int64_t T, int64_t C, int N, const int32_t* __restrict__ idx,
-                                                       int ncol, int64_t nrows, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) unsigned char xt[BS * FT * FROW];
-  __shared__ __attribute__((aligned(16))) uint16_t dpt[2 * DPS * DPT];  // [hi | lo][column][token]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t chunk = blockIdx.x;
-  const int grp = blockIdx.y, G = gridDim.y;
-  const int64_t ntile = (T + FT - 1) / FT;
-  const int m = tid >> 4, c8 = (tid & 15) * 8;
-  const int64_t c = chunk * FCH + c8;
-  const bool cok = c < C;
-  const int64_t cl = cok ? c : C - 8;
-  // dP staging: threads tid < 256 take token tid >> 3, columns (tid & 7) * 4 .. + 3
-  const int pm = (tid & 255) >> 3, pc = (tid & 7) * 4;
-  const int si = wave >> 1, cb0 = (wave & 1) * 4;
-  const int tau = lane & 15, q = lane >> 4;
-  const int g0 = BM == BM_PRE ? 4 * (int)blockIdx.z : 0;
-
-  f4_t acc[4][2];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[cb][nb] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 xq[BS];
-  float4 pv;
-  auto load_tile = [&](int64_t tl) __attribute__((always_inline)) {
-    const int64_t t = tl * FT + m;
-    const bool ok = t < T && cok;
-    const int64_t tc = t < T ? t : T - 1;
-    int sl[4];
-    slot_streams<BM>(idx, tc, N, sl);
-#pragma unroll
-    for (int i = 0; i < BS; ++i) {
-      const uint4 v = ld_nt16(X + (tc * N + sl[i]) * C + cl);
-      xq[i] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
-    const int64_t t2 = tl * FT + pm;
-    const float4 w = *reinterpret_cast<const float4*>(dP + (t2 < T ? t2 : T - 1) * DPS + pc);
-    pv = t2 < T ? w : make_float4(0.f, 0.f, 0.f, 0.f);
-  };
-  int64_t tl = grp;
-  load_tile(tl);
-  for (; tl < ntile; tl += G) {
-#pragma unroll
-    for (int i = 0; i < BS; ++i) *reinterpret_cast<uint4*>(xt + xoff(i, m, c8)) = xq[i];
-    if (tid < 256) {
-      const float v[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t h = f2bf(v[k]);
-        const uint32_t l = f2bf(v[k] - bf2f(h));
-        dpt[(pc + k) * DPT + pm] = (uint16_t)h;
-        dpt[(DPS + pc + k) * DPT + pm] = (uint16_t)l;
-      }
-    }
-    __syncthreads();
-    if (tl + G < ntile) load_tile(tl + G);
-    uint4 bh[2], bl[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      bh[nb] = *reinterpret_cast<const uint4*>(dpt + (nb * 16 + tau) * DPT + q * 8);
-      bl[nb] = *reinterpret_cast<const uint4*>(dpt + (DPS + nb * 16 + tau) * DPT + q * 8);
-    }
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      const int chl = (cb0 + cb) * 16 + tau;
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(xt + xoff(si, q * 8 + 2 * k, chl));
-        const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(xt + xoff(si, q * 8 + 2 * k + 1, chl));
-        w[k] = lo16 | (hi16 << 16);
-      }
-      const uint4 a = make_uint4(w[0], w[1], w[2], w[3]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(a), bf8(bh[nb]), acc[cb][nb], 0, 0, 0);
-        acc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf8(a), bf8(bl[nb]), acc[cb][nb], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-  }
-  float* out = part + (int64_t)grp * nrows * ncol;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t ch = chunk * FCH + (cb0 + cb) * 16 + q * 4 + e;
-        const int col = nb * 16 + tau;
-        if (ch < C && col < ncol) out[((int64_t)(g0 + si) * C + ch) * ncol + col] = acc[cb][nb][e];
       }
 }
 
@@ -1202,15 +1087,6 @@ int ncu_of_device() {
 
 int64_t al256(int64_t b) { return (b + 255) / 256 * 256; }
 
-// token groups of the dphi pass: about two workgroups per CU over the chunks and
-// the nz stream groups (grid z), at most the tile count
-int dphi_groups(int64_t T, int64_t C, int nz) {
-  const int64_t nchunk = (C + FCH - 1) / FCH * nz, ntile = (T + FT - 1) / FT;
-  int64_t g = (2 * (int64_t)ncu_of_device() + nchunk - 1) / nchunk;
-  g = g < 1 ? 1 : g;
-  return (int)(g < ntile ? g : ntile);
-}
-
 // token-tile groups of the dX pass (and of its dphi partials): about one
 // workgroup per CU over the chunks and the nz stream groups (grid z), at most
 // the tile count
@@ -1251,9 +1127,8 @@ BwdWs carve(void* ws, int64_t T, int64_t C, int64_t nrows, int ncol, int64_t pby
   w.dP = (float*)take(T * DPS * 4);
   w.g2 = (float*)take(T * 4);
   w.red = (float*)take((T + 15) / 16 * RED * 4);
-  // dphi partials: the dX pass's groups where it forms them (route, pre: N / 4
-  // stream groups), else the separate pass's (n = 4 mHC)
-  w.G = route || hp > 4 ? dx_groups(T, C, hp > 4 ? hp / 4 : 1) : dphi_groups(T, C, 1);
+  // dphi partials: one per group of the dX pass (pre: over the N / 4 stream groups)
+  w.G = dx_groups(T, C, hp > 4 ? hp / 4 : 1);
   w.dphi_part = (float*)take((int64_t)w.G * nrows * ncol * 4);
   if (total) *total = off;
   return w;
@@ -1317,13 +1192,9 @@ hipError_t launch_fast_backward(const void* X, int64_t T, int64_t C, const float
   if ((e = launch_fast_bwd_coeffs(w.partial, T, C, bias, a_pre, a_post, a_res, iters, dh, w.dP, w.g2, w.red,
                                   w.h_pre, w.h_res, st)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(bwd_dx_kernel<BM_MHC>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)dx_groups(T, C, 1)),
-                     dim3(512), 0, st, x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, 4,
-                     (const int32_t*)nullptr, w.h_pre, w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX, 0, (int64_t)0,
-                     (float*)nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dphi_kernel<BM_MHC>, dim3((unsigned)((C + FCH - 1) / FCH), (unsigned)w.G), dim3(512), 0, st,
-                     x, w.dP, T, C, 4, (const int32_t*)nullptr, BCOL, (int64_t)BS * C, w.dphi_part);
+  hipLaunchKernelGGL(bwd_dx_kernel<BM_MHC>, dim3((unsigned)((C + XCH - 1) / XCH), (unsigned)w.G), dim3(512), 0, st,
+                     x, (const uint16_t*)dX_next, (const uint16_t*)dF_in, T, C, 4, (const int32_t*)nullptr, w.h_pre,
+                     w.h_res, w.dP, w.g2, w.phi_rows, (uint16_t*)dX, BCOL, (int64_t)BS * C, w.dphi_part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return launch_sums(w, T, (int64_t)BS * C, BCOL, dphi, dbias, 32, 3, dalpha, st);
 }
