@@ -405,10 +405,14 @@ def test_fast_full_state_pre_read_h_pre_alignment(N):
     check_bf16("F_in", host64(b["F_in"]), ref["F_in"])
 
 
-@pytest.mark.parametrize("K,C,T", [(1, 96, 29), (2, 64, 40), (3, 320, 17), (4, 4096, 33)])
+@pytest.mark.parametrize("K,C,T", [(1, 96, 29), (2, 64, 40), (3, 320, 17), (4, 4096, 33),
+                                   (1, 96, 64 * 600 + 17), (4, 1024, 64 * 520 + 33)])
 def test_fast_route_shapes(K, C, T):
     """xhc_route with k = 4 gathered streams for K = 1..4 write-back components, with
-    supplied indices and with the router inside."""
+    supplied indices and with the router inside. The last two shapes give the
+    gathered 64-token pass 601 and 521 items, so a workgroup streams up to 3 of them
+    (each next item's index table prefetched while the current one runs) and the
+    last tile is ragged."""
     N, k, m = 8, 4, 1
     note(f"xHC xhc_route N={N} k=4 K={K} C={C} T={T} bf16")
     inp = _xhc_inputs(60 + K, T, N, k, m, C, 1)
