@@ -87,10 +87,12 @@ def _compare(got, ref, rows=None):
     note(f"relative L2: {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
 
 
-@pytest.mark.parametrize("T,C", [(70, 256), (33, 96), (64, 4096), (1, 32), (129, 160)])
+@pytest.mark.parametrize("T,C", [(70, 256), (33, 96), (64, 4096), (1, 32), (129, 160), (32 * 700 + 5, 256)])
 def test_backward_shapes(T, C):
     """Ragged T (not a multiple of the 32-token tiles and 64-token items), C not a
-    multiple of the 128-channel chunks, one token, the workload's C."""
+    multiple of the 128-channel chunks, one token, the workload's C; at 22,405
+    tokens each workgroup of the dX pass walks several tiles (its dphi partial
+    summing them) and ends on the ragged one."""
     note(f"hc_backward n=4 C={C} T={T} bf16")
     inp, g = _inputs(400 + T, T, C)
     _compare(_gpu(inp, g), _oracle(inp, g))

@@ -115,14 +115,17 @@ def _compare(route, pre, ref, g, idx, rows=None):
     note(f"relative L2: {', '.join(f'{k} {v:.2e}' for k, v in errs.items())}")
 
 
-@pytest.mark.parametrize("N,C,T,m", [(16, 256, 70, 2), (8, 96, 33, 1), (4, 128, 40, 1), (12, 4096, 20, 2)])
+@pytest.mark.parametrize("N,C,T,m", [(16, 256, 70, 2), (8, 96, 33, 1), (4, 128, 40, 1), (12, 4096, 20, 2),
+                                     (16, 256, 64 * 300 + 9, 2)])
 def test_xhc_backward_shapes(N, C, T, m):
     """Several N (k = 4 active), ragged T, C not a multiple of the 128-channel
-    chunks, the workload's C; N = 4 is the dense case (every stream active)."""
+    chunks, the workload's C; N = 4 is the dense case (every stream active). At
+    19,209 tokens the gathered projection's workgroups take 2 items and the dX
+    passes' workgroups several tiles each, ending on a ragged one."""
     note(f"xHC backward N={N} C={C} T={T} m={m} bf16")
     inp, g, idx = _inputs(500 + N + T, T, N, C, m)
     route, pre = _gpu(inp, g, idx)
-    _compare(route, pre, _oracle(inp, g, idx), g, idx)
+    _compare(route, pre, _oracle(inp, g, idx, chunk=4096), g, idx)
 
 
 def test_xhc_backward_strong_gates():
