@@ -411,7 +411,8 @@ def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
     """Throughput of the xHC sublayer (N=16, k=4, m=2, C=4096, T=8192, bf16) on
     seeded synthetic device data: the routed step xhc_pre + xhc_route (K=1, F_out
     written back) and the augmented step xhc_pre + xhc_augment + xhc_route (K=4,
-    B=2 S=4096), three rotating state sets, HIP events around every call."""
+    B=2 S=4096), each also chained (xhc_route_pre per step), three rotating state
+    sets, HIP events around every call."""
     N, k, m, C, T = 16, 4, 2, 4096, 8192
     B, S = 2, 4096
     g = torch.Generator(device=dev)
@@ -522,6 +523,38 @@ def xhc_bench(torch, hc, dev, steps: int, warmup: int) -> dict:
         "pct_hbm_peak": 100.0 * step_bytes / total / 1e9 / HBM_PEAK_GBPS,
         "note": "xhc_route_pre per step (the same work as xhc_pre + xhc_route, the full state read once)",
         "counters": counter_summary(load_counters("xhc_route_pre", source_digest()), total)}
+
+    # The augmented step chained: xhc_augment of the sublayer's F_out, then
+    # xhc_route_pre with its K = 4 components (route l, pre-read of l + 1).
+    ws_c4 = torch.empty(hc.xhc_chain_workspace_bytes(T, N, C, k, m, 4, torch.bfloat16), dtype=torch.uint8,
+                        device=dev)
+    for i in range(3):
+        r = hc.xhc_pre_chain(Xs[i], phi_pre, b_pre, 0.01, w_r, phi_pre, w_r, k=k, m=m, workspace=ws_c4)
+        chain[i] = [r["idx"], r["carry"]]
+
+    def chained_aug(i, evs):
+        st = chain[i % 3]
+        if evs:
+            evs[0].record()
+        V = hc.xhc_augment(Fs[i % 3], conv, (4, 8, 12), B, S, workspace=ws_a)
+        if evs:
+            evs[1].record()
+        r = hc.xhc_route_pre(Xs[i % 3], V, phi4, b4, 0.01, 0.01, st[0], st[1], b_pre, 0.01,
+                             phi_pre_next=phi_pre, w_router_next=w_r, carry_out=st[1], k=k, m=m, out=fin_c,
+                             workspace=ws_c4)
+        if evs:
+            evs[2].record()
+        st[0] = r["idx"]
+
+    wall, kern = run(chained_aug, ["xhc_augment", "xhc_route_pre"])
+    step_bytes = ab4["xhc_pre"] + ab4["xhc_augment"] + ab4["xhc_route"]
+    total = sum(kern.values())
+    out["augmented_K4_chained"] = {
+        "tokens_per_s": T / total, "us_per_step": total * 1e6, "wall_us_per_step": wall * 1e6,
+        "algorithmic_bytes_per_step": step_bytes, "achieved_GBps": step_bytes / total / 1e9,
+        "pct_hbm_peak": 100.0 * step_bytes / total / 1e9 / HBM_PEAK_GBPS,
+        "calls_us": {c: v * 1e6 for c, v in kern.items()},
+        "note": "xhc_augment + xhc_route_pre (K = 4) per step: the augmented step with the full state read once"}
     out["workload"] = ("xHC N=16 k=4 m=2 C=4096 T=8192 bf16 (K=1: F_out written back; K=4: B=2 S=4096 "
                        "augmentation, kappa 4,8,12); seeded synthetic device data; durations from HIP events")
     return out

@@ -92,11 +92,22 @@ def _check_inactive_unchanged(name, X_before, X_after, idx):
     assert bool(same[~act].all().item()), f"{name}: {int((~same[~act]).sum().item())} inactive rows changed"
 
 
-def _run_chain(seed, T, C, L, carry_in_place, sample=None):
+def _write_back(layer, seed, l, K):
+    """The route's write-back components: F_out (K = 1), else K seeded N(0, 1)
+    components [T, K, C] standing in for the augmentation's output."""
+    if K == 1:
+        return layer["F_out"]
+    T, C = layer["F_out"].values.shape
+    return synth.Tensor(synth.normal(synth.make_rng(seed, l, stream=2), (T, K, C)), synth.BF16)
+
+
+def _run_chain(seed, T, C, L, carry_in_place, sample=None, K=1):
     """L sublayers: xhc_pre_chain, L - 1 calls of xhc_route_pre, the last route by
-    xhc_route; every call checked against the oracle on the GPU's state."""
+    xhc_route; every call checked against the oracle on the GPU's state. K: the
+    routes' write-back components."""
     k, m = K_ACT, M_FIX
-    layers = [synth.xhc_layer(seed, l, T, N, C, k, m, 1, synth.BF16) for l in range(L)]
+    layers = [synth.xhc_layer(seed, l, T, N, C, k, m, K, synth.BF16) for l in range(L)]
+    wbs = [_write_back(layers[l], seed, l, K) for l in range(L)]
     X = dev(layers[0]["X"])
     note(f"xhc_pre_chain T={T} C={C} seed={seed}")
     res = hc.xhc_pre_chain(X, *_maps(layers[0]), dev(layers[1]["phi_pre"]), dev(layers[1]["w_router"]), k=k, m=m)
@@ -111,7 +122,7 @@ def _run_chain(seed, T, C, L, carry_in_place, sample=None):
         idx_host = idx.cpu().numpy().astype(np.int64)
         note(f"xhc_route_pre sublayer {l} -> {l + 1} T={T} C={C} next={nxt is not None}")
         out = hc.xhc_route_pre(
-            X, dev(layers[l]["F_out"]), dev(layers[l]["phi_act"]), dev(layers[l]["b_act"]), layers[l]["alpha_post"],
+            X, dev(wbs[l]), dev(layers[l]["phi_act"]), dev(layers[l]["b_act"]), layers[l]["alpha_post"],
             layers[l]["alpha_res"], idx, carry, dev(layers[l + 1]["b_pre"]), layers[l + 1]["alpha_pre"],
             phi_pre_next=None if nxt is None else dev(nxt["phi_pre"]),
             w_router_next=None if nxt is None else dev(nxt["w_router"]),
@@ -122,7 +133,7 @@ def _run_chain(seed, T, C, L, carry_in_place, sample=None):
         Xb = _rows(X_before, sample)
         ref_X, ref_hp, ref_hr = O.xhc_route(Xb, sl(idx_host), layers[l]["phi_act"], layers[l]["b_act"],
                                             layers[l]["alpha_post"], layers[l]["alpha_res"],
-                                            sl(layers[l]["F_out"].values.astype(np.float64)))
+                                            sl(wbs[l].values.astype(np.float64)))
         check_fp32(f"route {l} H_post", sl(host64(out["h_post"])), ref_hp)
         check_fp32(f"route {l} H_res", sl(host64(out["h_res"])), ref_hr)
         _check_inactive_unchanged(f"route {l}", X_before, X, idx)
@@ -138,7 +149,7 @@ def _run_chain(seed, T, C, L, carry_in_place, sample=None):
             carry = out["carry"]
     # the chain's last route, unchained
     last = layers[L - 1]
-    hc.xhc_route(X, dev(last["F_out"]), dev(last["phi_act"]), dev(last["b_act"]), last["alpha_post"],
+    hc.xhc_route(X, dev(wbs[L - 1]), dev(last["phi_act"]), dev(last["b_act"]), last["alpha_post"],
                  last["alpha_res"], k=k, m=m, idx=idx)
     torch.cuda.synchronize()
 
@@ -151,6 +162,20 @@ def test_chain_small(T):
 
 def test_chain_separate_carries_C2048():
     _run_chain(12, 200, 2048, 4, carry_in_place=False)
+
+
+@pytest.mark.parametrize("T", [45, 300])
+def test_chain_augmented_K4(T):
+    """The routes write back K = 4 components (the augmented step's route)."""
+    _run_chain(14, T, 1024, 3, carry_in_place=True, K=4)
+
+
+def test_chain_augmented_K4_full_size_N16_C4096_T8192():
+    """The benchmarked augmented shape (2 sequences of 4096 tokens): oracle on 256
+    sampled tokens per call, the unchained calls on every token."""
+    rng = np.random.default_rng(6)
+    sample = np.sort(rng.choice(8192, 256, replace=False))
+    _run_chain(15, 8192, 4096, 3, carry_in_place=True, sample=sample, K=4)
 
 
 def test_chain_full_size_N16_C4096_T8192():
