@@ -142,6 +142,11 @@ bool fast_mix_supported(int dtype, int k, int K, int64_t C, const void* X, const
 hipError_t launch_fast_mix(void* X, int64_t T, int N, int64_t C, const int32_t* idx, const float* H_res,
                            const float* H_post, const void* Wb, int K, hipStream_t st,
                            const void* Wb2 = nullptr, int j0 = 0);
+// The active set's coefficients (H_post [T, 4, K], H_res [T, 4, 4]) for k = 4:
+// phi_act packed (and, with phi_rows, also in the backward's row form), the
+// gathered projection (64-token items up to K = 4, 32-token ones beyond) and
+// the finish. nt_rows: the gathered rows with nontemporal loads, for a caller
+// whose next pass gains less from finding them in the last-level cache.
 hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, const int32_t* idx, int K,
                                   const float* phi_act, const float* b_act, float a_post, float a_res, int iters,
                                   float* Hp, float* Hr, void* packed, float* partial, hipStream_t st,
