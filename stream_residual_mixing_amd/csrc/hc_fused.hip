@@ -2154,15 +2154,9 @@ hipError_t launch_split(const SplitArgs& A, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_split_nb(int nb, const SplitArgs& A, hipStream_t st) {
-  switch (nb) {
-    case 2: return launch_split<false, 2, MODE>(A, st);
-    case 3: return launch_split<false, 3, MODE>(A, st);
-    case 4: return launch_split<false, 4, MODE>(A, st);
-    case 5: if constexpr (MODE == ROWS_GATHER) return launch_split<false, 5, MODE>(A, st); else return hipErrorInvalidValue;
-    default: if constexpr (MODE == ROWS_GATHER) return launch_split<false, 6, MODE>(A, st); else return hipErrorInvalidValue;
-  }
+// the gathered active set beyond 32 columns (K > 4): NB = 5 or 6 blocks
+hipError_t launch_split_gather(int nb, const SplitArgs& A, hipStream_t st) {
+  return nb == 5 ? launch_split<false, 5, ROWS_GATHER>(A, st) : launch_split<false, 6, ROWS_GATHER>(A, st);
 }
 
 // projection only, W_TOK-token items (A from geom(..., W_TOK)); DH: with the
@@ -2702,7 +2696,7 @@ hipError_t launch_fast_xhc_active(const void* X, int64_t T, int N, int64_t C, co
                        A);
     e = hipGetLastError();
   } else {
-    e = launch_split_nb<ROWS_GATHER>(nb, A, st);
+    e = launch_split_gather(nb, A, st);
   }
   if (e != hipSuccess) return e;
   const int64_t threads = T * 16;
