@@ -838,9 +838,15 @@ def main() -> int:
         dist[label] = {
             nm: {q: float(np.percentile([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs], p))
                  for q, p in (("p10_us", 10), ("median_us", 50), ("p90_us", 90))} for j, nm in enumerate(names)}
+        # the median step period of the evented run: first event of step i to that
+        # of step i + 1, the gaps between the steps' launches included
+        period = (float(np.median([evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(steps - 1)])) * 1e-3
+                  if steps > 1 else gpu / steps)
+        periods[label] = period
         return wall, gpu, kern
 
     dist = {}
+    periods = {}
 
     Fs = [F0] + [F0.clone() for _ in range(2)]
     phi_packed = hc.hc_phi_pack(phi, n, C, torch.bfloat16)
@@ -934,15 +940,17 @@ def main() -> int:
     del flush
     t_cold = float(np.median(cold))
 
-    def rate(gpu_s, wall_s, nbytes):
-        # The variants' rates come from the bare run's HIP events (GPU time from the
-        # first launch to the last): a host-side stall while Python issues the steps
-        # (seen now and then right after another GPU process) would otherwise be
-        # charged to the kernels. The host's wall clock is reported beside it.
-        per = gpu_s / args.steps
+    def rate(label, gpu_s, wall_s, nbytes):
+        # The variants' rates come from the median step period of the evented run:
+        # in some runs right after another GPU process, the bare run of the two-call
+        # chain held one long stall in issuing (about 35 ms over 50 steps, on the
+        # host's clock and the GPU's alike) that the per-step periods do not
+        # show. The bare run's wall clock and GPU time per step are reported beside.
+        per = periods[label]
         return {"tokens_per_s": T / per, "ms_per_step": per * 1e3, "achieved_GBps": nbytes / per / 1e9,
                 "pct_hbm_peak": 100.0 * nbytes / per / 1e9 / HBM_PEAK_GBPS,
-                "wall_ms_per_step": wall_s / args.steps * 1e3}
+                "bare_wall_ms_per_step": wall_s / args.steps * 1e3,
+                "bare_gpu_ms_per_step": gpu_s / args.steps * 1e3}
 
     one_pass = T * (n * C * 2 + C * 2 + n * C * 2 + C * 2 + (n + n * n) * 4 * 2)
     ms_per_step = wall / args.steps * 1e3
@@ -990,12 +998,12 @@ def main() -> int:
             "pct_hbm_peak": 100.0 * step_bytes / t_cold / 1e9 / HBM_PEAK_GBPS,
             "note": "hc_post_pre timed alone after 1 GiB of unrelated streaming (hc_copy_probe over 512 MiB) before "
                     "every call, so nothing of its inputs is left in the caches when it starts"},
-        "chain_phi_packed_each_step": dict(rate(gpu_pk, wall_pk, step_bytes),
+        "chain_phi_packed_each_step": dict(rate("chain_phi_packed_each_step", gpu_pk, wall_pk, step_bytes),
                                            call_us=dist["chain_phi_packed_each_step"][dom]["median_us"]),
-        "chain_two_calls": dict(rate(gpu2, wall2, ab["hc_pre"] + ab["hc_post_coeffs"]),
+        "chain_two_calls": dict(rate("chain_two_calls", gpu2, wall2, ab["hc_pre"] + ab["hc_post_coeffs"]),
                                 calls_us={k: v * 1e6 for k, v in kern2.items()},
                                 calls_GBps={k: ab[k] / v / 1e9 for k, v in kern2.items()}),
-        "isolated_sublayer": dict(rate(iso_gpu, iso_wall, iso_bytes), calls_us={k: v * 1e6 for k, v in iso_kern.items()},
+        "isolated_sublayer": dict(rate("isolated_sublayer", iso_gpu, iso_wall, iso_bytes), calls_us={k: v * 1e6 for k, v in iso_kern.items()},
                                   algorithmic_bytes_per_step=iso_bytes),
         "call_durations": dist,
         "device_copy_ceiling_GBps": device_copy_rate(torch, hc, dev),
