@@ -167,25 +167,6 @@ __device__ __forceinline__ uint4 ld_stream(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Lane exchange within rows of 16 lanes (DPP): quad permutations and row rotations.
-constexpr int DPP_QXOR1 = 0xB1;  // quad_perm [1, 0, 3, 2]
-constexpr int DPP_QXOR2 = 0x4E;  // quad_perm [2, 3, 0, 1]
-constexpr int DPP_ROR4 = 0x124;  // row_ror:4
-constexpr int DPP_ROR8 = 0x128;  // row_ror:8
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// the sum over a row of 16 lanes, in every lane of the row
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp<DPP_QXOR1>(x);
-  x += dpp<DPP_QXOR2>(x);
-  x += dpp<DPP_ROR8>(x);
-  x += dpp<DPP_ROR4>(x);
-  return x;
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 
