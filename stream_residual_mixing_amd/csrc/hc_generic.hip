@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(
   sq = wave_sum(sq);
   if (lane == 0) redsq[wid] = sq;
   __syncthreads();
-  if (threadIdx.x < nc) {
+  if ((int)threadIdx.x < nc) {
     float s = 0.f;
     for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += red[w][threadIdx.x];
     P[t * ncols + col0 + threadIdx.x] = s;
