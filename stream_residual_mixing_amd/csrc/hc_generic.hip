@@ -79,15 +79,15 @@ __global__ __launch_bounds__(256) void proj_generic_kernel(
 // waves stages phi once, row-major with a row stride of ncols + 1 floats, and
 // each wave takes tok_per_wave tokens, one at a time: it copies vec(x_t) to its
 // own LDS row buffer (and forms ss), then lane (g, j) = (lane >> 5, lane & 31)
-// adds x[r] phi[r, j] over the rows r = g, g + 2, ..., and the two halves of the
-// wave are added. One accumulator per lane keeps the code small. At 512 tokens
-// of 4 x 256 floats it takes 28 us against 34 us for proj_generic_kernel (of
-// which the staging is about 10 us and the products about 8 us); forms with 32
-// accumulators per lane, fully unrolled, took 37-57 us.
+// adds x[r] phi[r, j] over half g of the rows, and the two halves of the wave
+// are added. One accumulator per lane keeps the code small. At 512 tokens
+// of 4 x 256 floats it takes 27 us against 34 us for proj_generic_kernel (the
+// staging about 10 us of it, the products about 8); forms with 32 accumulators
+// per lane, fully unrolled, took 37-57 us.
 constexpr int PROJ_LDS_FLOATS = 25 * 1024;  // 100 KB (4 x 256 rows x 24 columns fit)
 constexpr int PROJ_THREADS = 256;
 constexpr int PROJ_XMAX = 1024;             // vec(x_t) floats per wave buffer (4 KB)
-constexpr int PROJ_SB = 50;                 // phi elements per thread per staging batch
+constexpr int PROJ_SB = 100;                // phi elements per thread per staging batch
 constexpr int PROJ_XB = 16;                 // rows of vec(x_t) per lane per batch
 template <typename T>
 __global__ __launch_bounds__(PROJ_THREADS) void proj_lds_kernel(
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(PROJ_THREADS) void proj_lds_kernel(
     const float* __restrict__ phiA, int colsA, const float* __restrict__ phiB, int colsB,
     float* __restrict__ P, float* __restrict__ ss, int tok_per_wave) {
   __shared__ float phs[PROJ_LDS_FLOATS];                    // [R][ncols + 1]
-  __shared__ float xs[PROJ_THREADS / 64][PROJ_XMAX];        // vec(x_t) per wave
+  __shared__ __attribute__((aligned(16))) float xs[PROJ_THREADS / 64][PROJ_XMAX];  // vec(x_t) per wave
   const int ncols = colsA + colsB, RS = ncols + 1;
   const int Ci = (int)C;
   const int R = nvec * Ci;  // (R <= PROJ_XMAX, R * RS <= PROJ_LDS_FLOATS: 32-bit indices)
@@ -157,17 +157,21 @@ __global__ __launch_bounds__(PROJ_THREADS) void proj_lds_kernel(
     }
     __builtin_amdgcn_wave_barrier();  // (one wave's LDS accesses run in order)
     float acc = 0.f;
-    if (jok) {  // four partial sums, so the adds do not form one chain
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      int r = g;
+    if (jok) {  // half g of the rows, 4 at a time (x as one float4, read by the half's lanes alike)
+      const int Rh = ((R + 7) >> 3) << 2;  // rows per half, a multiple of 4
+      const int rb = g * Rh, re = R < rb + Rh ? R : rb + Rh;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;  // four partial sums: no single chain of adds
+      int r = rb;
 #pragma unroll 2
-      for (; r + 6 < R; r += 8) {
-        a0 += xw[r] * phs[r * RS + j];
-        a1 += xw[r + 2] * phs[(r + 2) * RS + j];
-        a2 += xw[r + 4] * phs[(r + 4) * RS + j];
-        a3 += xw[r + 6] * phs[(r + 6) * RS + j];
+      for (; r + 3 < re; r += 4) {
+        const float4 x4 = *reinterpret_cast<const float4*>(xw + r);
+        const float* ph = phs + r * RS + j;
+        a0 += x4.x * ph[0];
+        a1 += x4.y * ph[RS];
+        a2 += x4.z * ph[2 * RS];
+        a3 += x4.w * ph[3 * RS];
       }
-      for (; r < R; r += 2) a0 += xw[r] * phs[r * RS + j];
+      for (; r < re; ++r) a0 += xw[r] * phs[r * RS + j];
       acc = (a0 + a1) + (a2 + a3);
     }
     acc += __shfl_xor(acc, 32, 64);
