@@ -413,15 +413,22 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
       }
     }
     __syncthreads();
-    const float4* c4 = reinterpret_cast<const float4*>(cf + m * CFR);
-    const float4 r0 = c4[0], r1 = c4[1], r2 = c4[2], r3 = c4[3], hp4 = c4[4], g4 = c4[5];
-    const float H[4][4] = {{r0.x, r0.y, r0.z, r0.w}, {r1.x, r1.y, r1.z, r1.w}, {r2.x, r2.y, r2.z, r2.w},
-                           {r3.x, r3.y, r3.z, r3.w}};  // H[i][j] = h_res[t, i, j]
+    // the token's staged coefficients [h_res 16 | h_pre 4 | g2 ...]: H[i][j] =
+    // h_res[t, i, j], read from LDS where each output slot j uses them
+    const float* cft = cf + m * CFR;
+    const float4 hp4 = reinterpret_cast<const float4*>(cft)[4], g4 = reinterpret_cast<const float4*>(cft)[5];
     const float hp[4] = {hp4.x, hp4.y, hp4.z, hp4.w};
-    float d[BS][8], f[8];
-#pragma unroll
-    for (int i = 0; i < BS; ++i) unpack_bf8(cur.dq[i], d[i]);
-    if constexpr (BM != BM_ROUTE) unpack_bf8(cur.fq, f);
+    // dX_next and dF_in stay packed (bfloat16 pairs) and each value is widened
+    // where it is used, rather than all 40 at once; likewise h_res is read from
+    // LDS a column at a time (these registers are what the dphi accumulators need)
+    auto dn = [&](int i, int e) __attribute__((always_inline)) {
+      const uint32_t w = e < 2 ? cur.dq[i].x : (e < 4 ? cur.dq[i].y : (e < 6 ? cur.dq[i].z : cur.dq[i].w));
+      return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    };
+    auto fn = [&](int e) __attribute__((always_inline)) {
+      const uint32_t w = e < 2 ? cur.fq.x : (e < 4 ? cur.fq.y : (e < 6 ? cur.fq.z : cur.fq.w));
+      return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    };
     const int64_t t = tl * XT + m;
     const bool ok = t < T && cok;
     const int64_t nrw = T - tl * XT < XT ? T - tl * XT : XT;
@@ -434,12 +441,13 @@ __global__ __launch_bounds__(512) void bwd_dx_kernel(const uint16_t* __restrict_
       const float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
       float xj[8], o[8];
       unpack_bf8(*reinterpret_cast<const uint4*>(xt + xoff(j, m, c8)), xj);
+      const float H0 = cft[j], H1 = cft[4 + j], H2 = cft[8 + j], H3 = cft[12 + j];  // column j
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v;
-        if constexpr (BM == BM_PRE) v = d[j][e] + hp[j] * f[e];
-        else v = H[0][j] * d[0][e] + H[1][j] * d[1][e] + H[2][j] * d[2][e] + H[3][j] * d[3][e];
-        if constexpr (BM == BM_MHC) v += hp[j] * f[e];
+        if constexpr (BM == BM_PRE) v = dn(j, e) + hp[j] * fn(e);
+        else v = H0 * dn(0, e) + H1 * dn(1, e) + H2 * dn(2, e) + H3 * dn(3, e);
+        if constexpr (BM == BM_MHC) v += hp[j] * fn(e);
         o[e] = v + p[e] + g4.x * xj[e];
       }
       // through a buffer resource over the tile's rows: past T or C the offset is
